@@ -1,0 +1,192 @@
+/*
+ * gpt2.h -- C ABI of the MI355X (gfx950) GPT-2 training-step library.
+ *
+ * The library follows the problem statement of the llm.c articles:
+ *   - all memory is allocated once, up front, as flat 1-D arenas (parameters,
+ *     gradients, optimizer moments, activations) and never allocated or freed
+ *     while training (yinghuohong.cn article "OpenAI创始大神手搓千行C代码训练GPT",
+ *     section "脚动完成每一个层前向/反向流传"; ujoy.net article "徒手用 1000 行
+ *     C 语言实现", section "用C语言实现LLM");
+ *   - one training step is forward, zero-grad, backward and an Adam(W) update
+ *     at lr 1e-4 (ujoy.net, section "训练过程");
+ *   - the model is GPT-2 with the config fields that page prints (max_seq_len,
+ *     vocab_size, num_layers, num_heads, channels).
+ *
+ * Conventions.  Every entry point returns 0 (GPT2_OK) or a negative status;
+ * gpt2_last_error() then gives a message (thread-local, valid until the next
+ * call on the same thread).  All device work is queued on the one HIP stream
+ * given at create, in call order.  Host buffers are owned by the caller and
+ * may be reused as soon as a call returns.  Device memory is owned by the
+ * library: allocated in gpt2_create only, released in gpt2_destroy only.
+ *
+ * Layouts.  Parameters live in one fp32 arena of 16 tensors in this order:
+ * wte (V,C), wpe (maxT,C), ln1w (L,C), ln1b (L,C), qkvw (L,3C,C), qkvb (L,3C),
+ * attprojw (L,C,C), attprojb (L,C), ln2w (L,C), ln2b (L,C), fcw (L,4C,C),
+ * fcb (L,4C), fcprojw (L,C,4C), fcprojb (L,C), lnfw (C), lnfb (C); linear
+ * weights are (out, in) row-major and the LM head is wte itself (tied, no
+ * bias).  Gradients and the two Adam moments use the same layout.  Token ids
+ * are int32, row-major (B,T); targets likewise.
+ */
+#ifndef GPT2_H
+#define GPT2_H
+
+#include <stddef.h>
+#include <stdint.h>
+
+#ifdef __cplusplus
+extern "C" {
+#endif
+
+#define GPT2_API __attribute__((visibility("default")))
+
+/* ---- status codes ------------------------------------------------------ */
+#define GPT2_OK 0
+#define GPT2_EINVAL (-1)  /* bad config, size, name or argument            */
+#define GPT2_ERANGE (-2)  /* a token or target id outside [0, vocab_size)   */
+#define GPT2_ESTATE (-3)  /* call out of order (backward before a forward
+                             with targets)                                  */
+#define GPT2_ENOMEM (-4)  /* the allocator returned NULL                    */
+#define GPT2_EDEVICE (-5) /* a HIP runtime error (message has its string)   */
+
+/* ---- precision --------------------------------------------------------- */
+#define GPT2_FP32 0       /* everything fp32, fp32 matrix cores            */
+#define GPT2_BF16_MIXED 1 /* bf16 activations and matmul inputs (fp32
+                             accumulate); fp32 master weights, gradients,
+                             Adam state, loss and softmax statistics      */
+
+typedef struct gpt2_model gpt2_model; /* opaque */
+
+/* Model shape plus the largest batch the arenas are sized for.  Limits:
+ * channels % num_heads == 0 with head size 16, 32 or 64; channels <= 1024;
+ * seq_len <= max_seq_len; batch_size*seq_len <= 32768; vocab_size <= 65536. */
+typedef struct {
+    int32_t max_seq_len, vocab_size, num_layers, num_heads, channels;
+    int32_t batch_size, seq_len; /* arena sizing, fixed at create */
+    int32_t precision;           /* GPT2_FP32 or GPT2_BF16_MIXED */
+} gpt2_config;
+
+/* Optional device allocator.  alloc returns device memory of at least
+ * `bytes` bytes, aligned to 256 bytes, or NULL; it is called exactly once,
+ * from gpt2_create; free is called once from gpt2_destroy. */
+typedef struct {
+    void* (*alloc)(size_t bytes, void* ctx);
+    void (*free)(void* ptr, void* ctx);
+    void* ctx;
+} gpt2_allocator;
+
+/* ---- host-only queries (no device needed) -------------------------------*/
+
+/* GPT2_OK if the config is within the limits above, else GPT2_EINVAL. */
+GPT2_API int gpt2_validate_config(const gpt2_config* cfg);
+
+/* Number of parameters (124,439,808 for the 124M shape), or -1 if invalid.
+ * The count is printed by the C trainer (ujoy.net, section "训练过程"). */
+GPT2_API int64_t gpt2_config_num_parameters(const gpt2_config* cfg);
+
+/* Name, element offset and element count of parameter tensor i (0..15). */
+GPT2_API int gpt2_config_param_tensor(const gpt2_config* cfg, int i, const char** name,
+                             int64_t* offset, int64_t* numel);
+
+/* Bytes of device memory gpt2_create will request for this config. */
+GPT2_API int64_t gpt2_config_device_bytes(const gpt2_config* cfg);
+
+/* ---- lifetime ---------------------------------------------------------- */
+
+/* Validates cfg, allocates every arena in one allocation (through alloc, or
+ * hipMalloc when alloc is NULL), zeroes parameters, gradients and moments,
+ * and binds the model to hip_stream (a hipStream_t; NULL = the null stream).
+ * On failure nothing is leaked and *out is NULL. */
+GPT2_API int gpt2_create(const gpt2_config* cfg, const gpt2_allocator* alloc,
+                void* hip_stream, gpt2_model** out);
+GPT2_API void gpt2_destroy(gpt2_model* model);
+
+GPT2_API int64_t gpt2_num_parameters(const gpt2_model* model);
+GPT2_API int gpt2_param_tensor(const gpt2_model* model, int i, const char** name,
+                      int64_t* offset, int64_t* numel);
+
+/* ---- host <-> device copies (synchronous) -------------------------------*/
+
+/* Exactly one of host_dst / host_src is non-NULL: read or write all
+ * parameters (fp32, arena layout).  Writing also refreshes the bf16 weight
+ * copies of the mixed-precision model. */
+GPT2_API int gpt2_copy_params(gpt2_model* model, float* host_dst, const float* host_src);
+GPT2_API int gpt2_copy_grads(gpt2_model* model, float* host_dst);
+/* Either pointer may be NULL. */
+GPT2_API int gpt2_copy_opt_state(gpt2_model* model, float* host_m, float* host_v);
+
+/* Copy one activation of the last forward to the host as fp32 (converted from
+ * bf16 in the mixed-precision model).  Names: "encoded", "ln1", "ln1_mean",
+ * "ln1_rstd", "qkv", "atty", "att_lse", "residual2", "ln2", "ln2_mean",
+ * "ln2_rstd", "fch", "fch_gelu", "residual3", "lnf", "lnf_mean", "lnf_rstd",
+ * "logits", "losses".  layer is used by the per-layer names and ignored by
+ * the others.  Sizes are those of the last forward's (B,T): (B*T, width),
+ * except att_lse (B, num_heads, T) and logits (B*T, vocab_size).  After a
+ * forward with targets, "logits" holds d(mean loss)/d(logits) instead of the
+ * logits (the loss kernel overwrites them in place).  With host_dst NULL only
+ * *numel is set. */
+GPT2_API int gpt2_copy_activation(gpt2_model* model, const char* name, int layer,
+                         float* host_dst, int64_t* numel);
+
+/* ---- the training step ------------------------------------------------- */
+
+/* Forward pass on B <= batch_size sequences of T <= seq_len tokens.
+ * tokens: host int32 (B,T), each in [0, vocab_size).  targets: host int32
+ * (B,T) or NULL.  With targets, *mean_loss (if mean_loss is non-NULL) gets the
+ * mean cross-entropy over the B*T positions (this waits for the stream) and
+ * the state needed by gpt2_backward is kept; without targets the logits are
+ * kept and *mean_loss is NaN.  Ids are checked on the host: GPT2_ERANGE. */
+GPT2_API int gpt2_forward(gpt2_model* model, const int32_t* tokens,
+                 const int32_t* targets, int B, int T, float* mean_loss);
+
+/* As gpt2_forward, with tokens / targets already in device memory (the
+ * caller keeps them alive until the stream has consumed them).  Ids are
+ * checked on the device; a bad id zeroes its row, and the next call that
+ * reads the loss (this one, if mean_loss is non-NULL) returns GPT2_ERANGE. */
+GPT2_API int gpt2_forward_device(gpt2_model* model, const int32_t* tokens,
+                        const int32_t* targets, int B, int T,
+                        float* mean_loss);
+
+/* Clears the parameter gradients (backward accumulates into them). */
+GPT2_API int gpt2_zero_grad(gpt2_model* model);
+
+/* Gradient of the mean loss of the last forward, added (+=) into the
+ * parameter gradients.  GPT2_ESTATE if the last forward had no targets. */
+GPT2_API int gpt2_backward(gpt2_model* model);
+
+/* One AdamW step over the whole flat arena (1-based step, decoupled weight
+ * decay applied to every parameter):
+ *   m = b1 m + (1-b1) g;  v = b2 v + (1-b2) g^2;
+ *   p -= lr (m/(1-b1^step) / (sqrt(v/(1-b2^step)) + eps) + weight_decay p). */
+GPT2_API int gpt2_update(gpt2_model* model, float lr, float beta1, float beta2,
+                float eps, float weight_decay, int step);
+
+/* Waits for the model's stream; reports a pending device-side id error. */
+GPT2_API int gpt2_synchronize(gpt2_model* model);
+
+GPT2_API const char* gpt2_last_error(void);
+
+/* ---- per-kernel timing (HIP events on the model's stream) ---------------*/
+
+/* Kernel classes timed when profiling is on. */
+#define GPT2_KC_GEMM 0      /* every matmul (forward, dX, dW, split-K sum) */
+#define GPT2_KC_ATTENTION 1 /* attention forward and backward             */
+#define GPT2_KC_LAYERNORM 2 /* layernorm forward and backward             */
+#define GPT2_KC_SOFTMAX_CE 3
+#define GPT2_KC_ADAMW 4
+#define GPT2_KC_OTHER 5     /* encoder, bias sums, zero-grad, loss mean   */
+#define GPT2_KC_COUNT 6
+
+/* enable != 0 records an event pair around every launch from now on and
+ * clears the counters; enable == 0 stops recording. */
+GPT2_API int gpt2_profile(gpt2_model* model, int enable);
+
+/* Totals since profiling was enabled for one kernel class: summed kernel
+ * time (ms, waits for the stream), number of launches, and the algorithmic
+ * work of those launches: floating-point operations and HBM bytes. */
+GPT2_API int gpt2_profile_read(gpt2_model* model, int kernel_class, double* total_ms,
+                      int64_t* launches, double* flops, double* bytes);
+
+#ifdef __cplusplus
+}
+#endif
+#endif /* GPT2_H */

@@ -1,0 +1,328 @@
+// Bandwidth-bound kernels: token+position embedding (forward, and its
+// deterministic scatter-add backward), bias-gradient column sums, zeroing of
+// the gradient arena and the AdamW sweep over the flat parameter arena.
+//
+// Embedding (ujoy.net article "徒手用 1000 行 C 语言实现", section "用C语言实现
+// LLM": the encoder layer):  x[b,t] = wte[tok[b,t]] + wpe[t];  the backward
+// adds each position's gradient into its token row and its position row.
+// Rows of wte hit by several positions are summed in position order after a
+// sort of (token, position) keys, so the result does not depend on timing.
+//
+// AdamW (section "训练过程" runs Adam at lr 1e-4; decoupled weight decay as in
+// Loshchilov & Hutter): per element, with bias corrections c1 = 1 - b1^step
+// and c2 = 1 - b2^step computed once on the host,
+//   m = b1 m + (1-b1) g;  v = b2 v + (1-b2) g^2;
+//   p -= lr ((m/c1) / (sqrt(v/c2) + eps) + wd p).
+#include "common.h"
+#include "kernels.h"
+
+namespace gk {
+namespace {
+
+__global__ __launch_bounds__(256) void encoder_fwd_kernel(float* __restrict__ out,
+                                                          const int32_t* __restrict__ tok,
+                                                          const float* __restrict__ wte,
+                                                          const float* __restrict__ wpe,
+                                                          int B, int T, int C, int V,
+                                                          int* __restrict__ flag) {
+    const int C4 = C >> 2;
+    const int64_t n = (int64_t)B * T * C4;
+    for (int64_t i = blockIdx.x * (int64_t)blockDim.x + threadIdx.x; i < n;
+         i += (int64_t)gridDim.x * blockDim.x) {
+        const int64_t bt = i / C4;
+        const int c = (int)(i - bt * C4) * 4;
+        const int t = (int)(bt % T);
+        const int id = tok[bt];
+        float4 r = make_float4(0.f, 0.f, 0.f, 0.f);
+        if (id >= 0 && id < V) {
+            const float4 a = ld4(wte + (int64_t)id * C + c);
+            const float4 p = ld4(wpe + (int64_t)t * C + c);
+            r = make_float4(a.x + p.x, a.y + p.y, a.z + p.z, a.w + p.w);
+        } else if (c == 0) {
+            atomicOr(flag, 1);
+        }
+        st4(out + bt * C + c, r);
+    }
+}
+
+// Bitonic sort of (token << pos_bits | position) keys in LDS, one workgroup.
+// Ids outside [0, V) get the token field V so the backward skips them.
+__global__ __launch_bounds__(1024) void encoder_sort_kernel(uint32_t* __restrict__ keys,
+                                                            const int32_t* __restrict__ tok,
+                                                            int n, int V, int pos_bits,
+                                                            int n_pow2) {
+    extern __shared__ uint32_t sk[];
+    for (int i = threadIdx.x; i < n_pow2; i += blockDim.x) {
+        uint32_t k = 0xFFFFFFFFu;
+        if (i < n) {
+            const int id = tok[i];
+            const uint32_t tf = (id >= 0 && id < V) ? (uint32_t)id : (uint32_t)V;
+            k = (tf << pos_bits) | (uint32_t)i;
+        }
+        sk[i] = k;
+    }
+    __syncthreads();
+    for (int k = 2; k <= n_pow2; k <<= 1) {
+        for (int j = k >> 1; j > 0; j >>= 1) {
+            for (int i = threadIdx.x; i < n_pow2; i += blockDim.x) {
+                const int p = i ^ j;
+                if (p > i) {
+                    const uint32_t a = sk[i], b = sk[p];
+                    const bool up = (i & k) == 0;
+                    if ((a > b) == up) {
+                        sk[i] = b;
+                        sk[p] = a;
+                    }
+                }
+            }
+            __syncthreads();
+        }
+    }
+    for (int i = threadIdx.x; i < n_pow2; i += blockDim.x) keys[i] = sk[i];
+}
+
+// One wave per sorted position; the first position of each run of equal
+// tokens sums the run's gradient rows in position order into wte's row.
+template <int NCH>
+__global__ __launch_bounds__(256) void encoder_bwd_wte_kernel(float* __restrict__ dwte,
+                                                              const float* __restrict__ dx,
+                                                              const uint32_t* __restrict__ keys,
+                                                              int n, int C, int V,
+                                                              int pos_bits) {
+    const int i = blockIdx.x * 4 + (threadIdx.x >> 6);
+    const int lane = threadIdx.x & 63;
+    if (i >= n) return;
+    const uint32_t tok = keys[i] >> pos_bits;
+    if (tok >= (uint32_t)V) return;
+    if (i > 0 && (keys[i - 1] >> pos_bits) == tok) return;
+    const uint32_t pmask = (1u << pos_bits) - 1u;
+    const int C4 = C >> 2;
+    float4 acc[NCH];
+#pragma unroll
+    for (int c = 0; c < NCH; c++) acc[c] = make_float4(0.f, 0.f, 0.f, 0.f);
+    for (int j = i; j < n && (keys[j] >> pos_bits) == tok; j++) {
+        const float* row = dx + (int64_t)(keys[j] & pmask) * C;
+#pragma unroll
+        for (int c = 0; c < NCH; c++) {
+            const int c4 = lane + 64 * c;
+            if (c4 < C4) {
+                const float4 d = ld4(row + 4 * c4);
+                acc[c].x += d.x;
+                acc[c].y += d.y;
+                acc[c].z += d.z;
+                acc[c].w += d.w;
+            }
+        }
+    }
+    float* out = dwte + (int64_t)tok * C;
+#pragma unroll
+    for (int c = 0; c < NCH; c++) {
+        const int c4 = lane + 64 * c;
+        if (c4 < C4) {
+            float4 o = ld4(out + 4 * c4);
+            o.x += acc[c].x;
+            o.y += acc[c].y;
+            o.z += acc[c].z;
+            o.w += acc[c].w;
+            st4(out + 4 * c4, o);
+        }
+    }
+}
+
+// dwpe[t] += sum over b of dx[b,t], b in order.
+__global__ __launch_bounds__(256) void encoder_bwd_wpe_kernel(float* __restrict__ dwpe,
+                                                              const float* __restrict__ dx,
+                                                              int B, int T, int C) {
+    const int C4 = C >> 2;
+    const int64_t i = blockIdx.x * (int64_t)blockDim.x + threadIdx.x;
+    if (i >= (int64_t)T * C4) return;
+    const int t = (int)(i / C4), c = (int)(i - (int64_t)t * C4) * 4;
+    float4 s = make_float4(0.f, 0.f, 0.f, 0.f);
+    for (int b = 0; b < B; b++) {
+        const float4 d = ld4(dx + ((int64_t)b * T + t) * C + c);
+        s.x += d.x;
+        s.y += d.y;
+        s.z += d.z;
+        s.w += d.w;
+    }
+    float* o = dwpe + (int64_t)t * C + c;
+    float4 r = ld4(o);
+    r.x += s.x;
+    r.y += s.y;
+    r.z += s.z;
+    r.w += s.w;
+    st4(o, r);
+}
+
+// Column sums of dy (M rows, N % 4 == 0 columns, leading dim ld): each
+// workgroup sums a chunk of rows for 256 columns (four waves, rows strided by
+// four), then a second kernel adds the chunk partials in chunk order.
+constexpr int BIAS_ROWS = 64;
+
+__global__ __launch_bounds__(256) void bias_partial_kernel(float* __restrict__ part,
+                                                           const float* __restrict__ dy, int M,
+                                                           int N, int64_t ld) {
+    __shared__ float4 sh[4][64];
+    const int lane = threadIdx.x & 63, wave = threadIdx.x >> 6;
+    const int col = (blockIdx.x * 64 + lane) * 4;
+    const int r0 = blockIdx.y * BIAS_ROWS;
+    const int r1 = min(M, r0 + BIAS_ROWS);
+    float4 s = make_float4(0.f, 0.f, 0.f, 0.f);
+    if (col < N) {
+        for (int r = r0 + wave; r < r1; r += 4) {
+            const float4 d = ld4(dy + (int64_t)r * ld + col);
+            s.x += d.x;
+            s.y += d.y;
+            s.z += d.z;
+            s.w += d.w;
+        }
+    }
+    sh[wave][lane] = s;
+    __syncthreads();
+    if (wave == 0 && col < N) {
+        float4 t = sh[0][lane];
+        for (int w = 1; w < 4; w++) {
+            t.x += sh[w][lane].x;
+            t.y += sh[w][lane].y;
+            t.z += sh[w][lane].z;
+            t.w += sh[w][lane].w;
+        }
+        st4(part + (int64_t)blockIdx.y * N + col, t);
+    }
+}
+
+__global__ __launch_bounds__(256) void bias_finish_kernel(float* __restrict__ db,
+                                                          const float* __restrict__ part,
+                                                          int nchunks, int N) {
+    const int c = blockIdx.x * blockDim.x + threadIdx.x;
+    if (c >= N) return;
+    float s = 0.f;
+    for (int k = 0; k < nchunks; k++) s += part[(int64_t)k * N + c];
+    db[c] += s;
+}
+
+__global__ __launch_bounds__(256) void fill_zero_kernel(float* __restrict__ p, int64_t n) {
+    const int64_t n4 = n >> 2;
+    const int64_t stride = (int64_t)gridDim.x * blockDim.x;
+    for (int64_t i = blockIdx.x * (int64_t)blockDim.x + threadIdx.x; i < n4; i += stride)
+        st4(p + 4 * i, make_float4(0.f, 0.f, 0.f, 0.f));
+    for (int64_t i = 4 * n4 + blockIdx.x * (int64_t)blockDim.x + threadIdx.x; i < n; i += stride)
+        p[i] = 0.f;
+}
+
+__device__ __forceinline__ float adamw_one(float& p, float g, float& m, float& v, float lr,
+                                           float b1, float b2, float eps, float wd, float bc1,
+                                           float bc2) {
+    m = b1 * m + (1.f - b1) * g;
+    v = b2 * v + (1.f - b2) * g * g;
+    const float mhat = m / bc1;
+    const float vhat = v / bc2;
+    p -= lr * (mhat / (sqrtf(vhat) + eps) + wd * p);
+    return p;
+}
+
+__global__ __launch_bounds__(256) void adamw_kernel(float* __restrict__ p,
+                                                    const float* __restrict__ g,
+                                                    float* __restrict__ m, float* __restrict__ v,
+                                                    int64_t n, float lr, float b1, float b2,
+                                                    float eps, float wd, float bc1, float bc2) {
+    const int64_t n4 = n >> 2;
+    const int64_t stride = (int64_t)gridDim.x * blockDim.x;
+    for (int64_t i = blockIdx.x * (int64_t)blockDim.x + threadIdx.x; i < n4; i += stride) {
+        float4 pp = ld4(p + 4 * i), gg = ld4(g + 4 * i), mm = ld4(m + 4 * i), vv = ld4(v + 4 * i);
+        adamw_one(pp.x, gg.x, mm.x, vv.x, lr, b1, b2, eps, wd, bc1, bc2);
+        adamw_one(pp.y, gg.y, mm.y, vv.y, lr, b1, b2, eps, wd, bc1, bc2);
+        adamw_one(pp.z, gg.z, mm.z, vv.z, lr, b1, b2, eps, wd, bc1, bc2);
+        adamw_one(pp.w, gg.w, mm.w, vv.w, lr, b1, b2, eps, wd, bc1, bc2);
+        st4(p + 4 * i, pp);
+        st4(m + 4 * i, mm);
+        st4(v + 4 * i, vv);
+    }
+    for (int64_t i = 4 * n4 + blockIdx.x * (int64_t)blockDim.x + threadIdx.x; i < n; i += stride)
+        adamw_one(p[i], g[i], m[i], v[i], lr, b1, b2, eps, wd, bc1, bc2);
+}
+
+inline unsigned grid_for(int64_t work, int per_block, unsigned cap) {
+    int64_t g = (work + per_block - 1) / per_block;
+    if (g < 1) g = 1;
+    return (unsigned)(g > cap ? cap : g);
+}
+
+}  // namespace
+
+hipError_t encoder_forward(hipStream_t s, float* out, const int32_t* tok, const float* wte,
+                           const float* wpe, int B, int T, int C, int V, int* flag) {
+    const int64_t n = (int64_t)B * T * (C / 4);
+    if (n <= 0) return hipSuccess;
+    hipLaunchKernelGGL(encoder_fwd_kernel, dim3(grid_for(n, 256, 65535)), dim3(256), 0, s, out,
+                       tok, wte, wpe, B, T, C, V, flag);
+    return hipGetLastError();
+}
+
+hipError_t encoder_sort_prepare(int n_pow2) {
+    return hipFuncSetAttribute((const void*)encoder_sort_kernel,
+                               hipFuncAttributeMaxDynamicSharedMemorySize, n_pow2 * 4);
+}
+
+hipError_t encoder_sort(hipStream_t s, uint32_t* keys, const int32_t* tok, int n, int V,
+                        int pos_bits, int n_pow2) {
+    if (n <= 0) return hipSuccess;
+    hipLaunchKernelGGL(encoder_sort_kernel, dim3(1), dim3(1024), (size_t)n_pow2 * 4, s, keys,
+                       tok, n, V, pos_bits, n_pow2);
+    return hipGetLastError();
+}
+
+hipError_t encoder_backward(hipStream_t s, float* dwte, float* dwpe, const float* dx,
+                            const uint32_t* keys, int B, int T, int C, int V, int pos_bits) {
+    const int n = B * T;
+    if (n <= 0) return hipSuccess;
+    const int nch = (C + 255) / 256;
+    dim3 grid((n + 3) / 4), block(256);
+    switch (nch) {
+        case 1: hipLaunchKernelGGL(encoder_bwd_wte_kernel<1>, grid, block, 0, s, dwte, dx, keys, n, C, V, pos_bits); break;
+        case 2: hipLaunchKernelGGL(encoder_bwd_wte_kernel<2>, grid, block, 0, s, dwte, dx, keys, n, C, V, pos_bits); break;
+        case 3: hipLaunchKernelGGL(encoder_bwd_wte_kernel<3>, grid, block, 0, s, dwte, dx, keys, n, C, V, pos_bits); break;
+        case 4: hipLaunchKernelGGL(encoder_bwd_wte_kernel<4>, grid, block, 0, s, dwte, dx, keys, n, C, V, pos_bits); break;
+        default: return hipErrorInvalidValue;
+    }
+    hipError_t e = hipGetLastError();
+    if (e != hipSuccess) return e;
+    const int64_t nw = (int64_t)T * (C / 4);
+    hipLaunchKernelGGL(encoder_bwd_wpe_kernel, dim3(grid_for(nw, 256, 1u << 30)), dim3(256), 0,
+                       s, dwpe, dx, B, T, C);
+    return hipGetLastError();
+}
+
+size_t bias_partials_floats(int M, int N) {
+    return (size_t)((M + BIAS_ROWS - 1) / BIAS_ROWS) * N;
+}
+
+hipError_t bias_grad(hipStream_t s, float* db, float* part, const float* dy, int M, int N,
+                     int64_t ld) {
+    if (M <= 0 || N <= 0) return hipSuccess;
+    const int nchunks = (M + BIAS_ROWS - 1) / BIAS_ROWS;
+    dim3 grid((N / 4 + 63) / 64, nchunks);
+    hipLaunchKernelGGL(bias_partial_kernel, grid, dim3(256), 0, s, part, dy, M, N, ld);
+    hipError_t e = hipGetLastError();
+    if (e != hipSuccess) return e;
+    hipLaunchKernelGGL(bias_finish_kernel, dim3((N + 255) / 256), dim3(256), 0, s, db, part,
+                       nchunks, N);
+    return hipGetLastError();
+}
+
+hipError_t fill_zero(hipStream_t s, float* p, int64_t n) {
+    if (n <= 0) return hipSuccess;
+    hipLaunchKernelGGL(fill_zero_kernel, dim3(grid_for(n / 4 + 1, 256, 8192)), dim3(256), 0, s,
+                       p, n);
+    return hipGetLastError();
+}
+
+hipError_t adamw(hipStream_t s, float* p, const float* g, float* m, float* v, int64_t n,
+                 float lr, float b1, float b2, float eps, float wd, float bc1, float bc2) {
+    if (n <= 0) return hipSuccess;
+    hipLaunchKernelGGL(adamw_kernel, dim3(grid_for(n / 4 + 1, 256, 8192)), dim3(256), 0, s, p,
+                       g, m, v, n, lr, b1, b2, eps, wd, bc1, bc2);
+    return hipGetLastError();
+}
+
+}  // namespace gk

@@ -1,0 +1,233 @@
+// LayerNorm forward and backward (the layer the llm.c articles walk through
+// as the worked example: yinghuohong.cn article "OpenAI创始大神手搓千行C代码
+// 训练GPT", section "脚动完成每一个层前向/反向流传"; ujoy.net article "徒手用
+// 1000 行 C 语言实现", section "用C语言实现LLM").
+//
+//   forward:  y = (x - mean) * rstd * w + b,  rstd = 1/sqrt(var + 1e-5),
+//             biased variance, mean taken first and variance second;
+//   backward: with xhat = (x - mean) rstd and g = dy w,
+//             dx = rstd (g - mean(g) - xhat mean(g xhat)),
+//             dw += sum_rows dy xhat,  db += sum_rows dy.
+//
+// One wave per row; the row stays in registers between the two reductions,
+// so x is read once.  The backward's column sums are deterministic: each
+// workgroup reduces its rows to one partial row, a second kernel adds the
+// partial rows in order.
+#include <algorithm>
+
+#include "common.h"
+#include "kernels.h"
+
+namespace gk {
+namespace {
+
+constexpr float LN_EPS = 1e-5f;
+
+template <int NCH>  // float4 chunks per lane: C <= 256 * NCH
+__global__ __launch_bounds__(256) void ln_fwd_kernel(float* __restrict__ out,
+                                                     float* __restrict__ mean,
+                                                     float* __restrict__ rstd,
+                                                     const float* __restrict__ inp,
+                                                     const float* __restrict__ w,
+                                                     const float* __restrict__ b, int N,
+                                                     int C) {
+    const int row = blockIdx.x * 4 + (threadIdx.x >> 6);
+    const int lane = threadIdx.x & 63;
+    if (row >= N) return;
+    const int C4 = C >> 2;
+    const float* x = inp + (int64_t)row * C;
+    float4 v[NCH];
+    float s = 0.f;
+#pragma unroll
+    for (int i = 0; i < NCH; i++) {
+        const int c4 = lane + 64 * i;
+        v[i] = c4 < C4 ? ld4(x + 4 * c4) : make_float4(0.f, 0.f, 0.f, 0.f);
+        s += (v[i].x + v[i].y) + (v[i].z + v[i].w);
+    }
+    const float m = wave_sum(s) / C;
+    float ss = 0.f;
+#pragma unroll
+    for (int i = 0; i < NCH; i++) {
+        const int c4 = lane + 64 * i;
+        if (c4 < C4) {
+            const float a = v[i].x - m, bb = v[i].y - m, c = v[i].z - m, d = v[i].w - m;
+            ss += (a * a + bb * bb) + (c * c + d * d);
+        }
+    }
+    const float var = wave_sum(ss) / C;
+    const float r = 1.0f / sqrtf(var + LN_EPS);
+    float* y = out + (int64_t)row * C;
+#pragma unroll
+    for (int i = 0; i < NCH; i++) {
+        const int c4 = lane + 64 * i;
+        if (c4 < C4) {
+            const float4 ww = ld4(w + 4 * c4), bb = ld4(b + 4 * c4);
+            st4(y + 4 * c4, make_float4((v[i].x - m) * r * ww.x + bb.x,
+                                        (v[i].y - m) * r * ww.y + bb.y,
+                                        (v[i].z - m) * r * ww.z + bb.z,
+                                        (v[i].w - m) * r * ww.w + bb.w));
+        }
+    }
+    if (lane == 0) {
+        mean[row] = m;
+        rstd[row] = r;
+    }
+}
+
+// Rows per backward workgroup: enough workgroups to fill the chip, few
+// enough partial rows to keep the second stage small.
+inline int ln_rows_per_block(int N) {
+    int r = (N + 511) / 512;
+    r = (r + 3) & ~3;
+    return r < 4 ? 4 : r;
+}
+
+template <int NCH>
+__global__ __launch_bounds__(256) void ln_bwd_kernel(
+    float* __restrict__ dres, int accumulate, float* __restrict__ partials,
+    const float* __restrict__ dout, const float* __restrict__ inp, const float* __restrict__ w,
+    const float* __restrict__ mean, const float* __restrict__ rstd, int N, int C, int rpb) {
+    extern __shared__ float red[];  // [4 waves][2][C]
+    const int lane = threadIdx.x & 63, wave = threadIdx.x >> 6;
+    const int C4 = C >> 2;
+    float4 pw[NCH], pb[NCH], wv[NCH];
+#pragma unroll
+    for (int i = 0; i < NCH; i++) {
+        pw[i] = pb[i] = make_float4(0.f, 0.f, 0.f, 0.f);
+        const int c4 = lane + 64 * i;
+        wv[i] = c4 < C4 ? ld4(w + 4 * c4) : make_float4(0.f, 0.f, 0.f, 0.f);
+    }
+    const int r0 = blockIdx.x * rpb;
+    const int r1 = min(N, r0 + rpb);
+    for (int row = r0 + wave; row < r1; row += 4) {
+        const float m = mean[row], rs = rstd[row];
+        const float* dy = dout + (int64_t)row * C;
+        const float* x = inp + (int64_t)row * C;
+        float4 g[NCH], xh[NCH];
+        float sg = 0.f, sgx = 0.f;
+#pragma unroll
+        for (int i = 0; i < NCH; i++) {
+            const int c4 = lane + 64 * i;
+            float4 d = make_float4(0.f, 0.f, 0.f, 0.f), xx = d;
+            if (c4 < C4) {
+                d = ld4(dy + 4 * c4);
+                xx = ld4(x + 4 * c4);
+            }
+            xh[i] = make_float4((xx.x - m) * rs, (xx.y - m) * rs, (xx.z - m) * rs,
+                                (xx.w - m) * rs);
+            g[i] = make_float4(d.x * wv[i].x, d.y * wv[i].y, d.z * wv[i].z, d.w * wv[i].w);
+            sg += (g[i].x + g[i].y) + (g[i].z + g[i].w);
+            sgx += (g[i].x * xh[i].x + g[i].y * xh[i].y) + (g[i].z * xh[i].z + g[i].w * xh[i].w);
+            pw[i].x += d.x * xh[i].x;
+            pw[i].y += d.y * xh[i].y;
+            pw[i].z += d.z * xh[i].z;
+            pw[i].w += d.w * xh[i].w;
+            pb[i].x += d.x;
+            pb[i].y += d.y;
+            pb[i].z += d.z;
+            pb[i].w += d.w;
+        }
+        const float mg = wave_sum(sg) / C, mgx = wave_sum(sgx) / C;
+        float* dx = dres + (int64_t)row * C;
+#pragma unroll
+        for (int i = 0; i < NCH; i++) {
+            const int c4 = lane + 64 * i;
+            if (c4 < C4) {
+                float4 o = make_float4(rs * (g[i].x - mg - xh[i].x * mgx),
+                                       rs * (g[i].y - mg - xh[i].y * mgx),
+                                       rs * (g[i].z - mg - xh[i].z * mgx),
+                                       rs * (g[i].w - mg - xh[i].w * mgx));
+                if (accumulate) {
+                    const float4 p = ld4(dx + 4 * c4);
+                    o.x += p.x;
+                    o.y += p.y;
+                    o.z += p.z;
+                    o.w += p.w;
+                }
+                st4(dx + 4 * c4, o);
+            }
+        }
+    }
+    // reduce the four waves' column partials, in wave order
+#pragma unroll
+    for (int i = 0; i < NCH; i++) {
+        const int c4 = lane + 64 * i;
+        if (c4 < C4) {
+            st4(red + (wave * 2) * C + 4 * c4, pw[i]);
+            st4(red + (wave * 2 + 1) * C + 4 * c4, pb[i]);
+        }
+    }
+    __syncthreads();
+    for (int c = threadIdx.x; c < 2 * C; c += blockDim.x) {
+        const int k = c / C, cc = c - k * C;
+        float s = red[(0 * 2 + k) * C + cc];
+        s += red[(1 * 2 + k) * C + cc];
+        s += red[(2 * 2 + k) * C + cc];
+        s += red[(3 * 2 + k) * C + cc];
+        partials[(int64_t)blockIdx.x * 2 * C + c] = s;
+    }
+}
+
+__global__ __launch_bounds__(256) void ln_bwd_finish_kernel(float* __restrict__ dw,
+                                                            float* __restrict__ db,
+                                                            const float* __restrict__ partials,
+                                                            int nblocks, int C) {
+    const int c = blockIdx.x * blockDim.x + threadIdx.x;
+    if (c >= 2 * C) return;
+    float s = 0.f;
+    for (int k = 0; k < nblocks; k++) s += partials[(int64_t)k * 2 * C + c];
+    if (c < C)
+        dw[c] += s;
+    else
+        db[c - C] += s;
+}
+
+}  // namespace
+
+hipError_t layernorm_forward(hipStream_t s, float* out, float* mean, float* rstd,
+                             const float* inp, const float* w, const float* b, int N, int C) {
+    if (N <= 0) return hipSuccess;
+    dim3 grid((N + 3) / 4), block(256);
+    const int nch = (C + 255) / 256;
+    switch (nch) {
+        case 1: hipLaunchKernelGGL(ln_fwd_kernel<1>, grid, block, 0, s, out, mean, rstd, inp, w, b, N, C); break;
+        case 2: hipLaunchKernelGGL(ln_fwd_kernel<2>, grid, block, 0, s, out, mean, rstd, inp, w, b, N, C); break;
+        case 3: hipLaunchKernelGGL(ln_fwd_kernel<3>, grid, block, 0, s, out, mean, rstd, inp, w, b, N, C); break;
+        case 4: hipLaunchKernelGGL(ln_fwd_kernel<4>, grid, block, 0, s, out, mean, rstd, inp, w, b, N, C); break;
+        default: return hipErrorInvalidValue;
+    }
+    return hipGetLastError();
+}
+
+// Upper bound of the workgroup count over every row count up to N: at most
+// 512 (rows per workgroup grow past 2048 rows) and at most ceil(N/4).
+size_t layernorm_partials_floats(int N, int C) {
+    const int nb = std::min(512, (N + 3) / 4);
+    return (size_t)nb * 2 * C;
+}
+
+hipError_t layernorm_backward(hipStream_t s, float* dres, int accumulate, float* dw, float* db,
+                              float* partials, const float* dout, const float* inp,
+                              const float* w, const float* mean, const float* rstd, int N,
+                              int C) {
+    if (N <= 0) return hipSuccess;
+    const int rpb = ln_rows_per_block(N);
+    const int nb = (N + rpb - 1) / rpb;
+    const size_t shm = (size_t)8 * C * sizeof(float);
+    const int nch = (C + 255) / 256;
+    dim3 grid(nb), block(256);
+    switch (nch) {
+        case 1: hipLaunchKernelGGL(ln_bwd_kernel<1>, grid, block, shm, s, dres, accumulate, partials, dout, inp, w, mean, rstd, N, C, rpb); break;
+        case 2: hipLaunchKernelGGL(ln_bwd_kernel<2>, grid, block, shm, s, dres, accumulate, partials, dout, inp, w, mean, rstd, N, C, rpb); break;
+        case 3: hipLaunchKernelGGL(ln_bwd_kernel<3>, grid, block, shm, s, dres, accumulate, partials, dout, inp, w, mean, rstd, N, C, rpb); break;
+        case 4: hipLaunchKernelGGL(ln_bwd_kernel<4>, grid, block, shm, s, dres, accumulate, partials, dout, inp, w, mean, rstd, N, C, rpb); break;
+        default: return hipErrorInvalidValue;
+    }
+    hipError_t e = hipGetLastError();
+    if (e != hipSuccess) return e;
+    hipLaunchKernelGGL(ln_bwd_finish_kernel, dim3((2 * C + 255) / 256), dim3(256), 0, s, dw, db,
+                       partials, nb, C);
+    return hipGetLastError();
+}
+
+}  // namespace gk

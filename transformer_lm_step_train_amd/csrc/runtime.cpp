@@ -1,0 +1,808 @@
+// Host runtime behind the C ABI (include/gpt2.h): config checks, the arena
+// layout, one device allocation, and the launch sequence of one training
+// step on one HIP stream.
+//
+// The arenas follow the llm.c design of allocating everything once as flat
+// 1-D memory and pointing every tensor into it (yinghuohong.cn article
+// "OpenAI创始大神手搓千行C代码训练GPT", section "脚动完成每一个层前向/反向流传";
+// ujoy.net article "徒手用 1000 行 C 语言实现", section "用C语言实现LLM").  The
+// activation arena differs from a CPU layout: attention keeps one
+// log-sum-exp per query row instead of the (T, T) probabilities, the residual
+// adds and GELU are produced by the matmul epilogues, and the LM-head logits
+// are overwritten in place by their gradient.
+#include <hip/hip_runtime.h>
+
+#include <algorithm>
+#include <cmath>
+#include <cstdarg>
+#include <cstdio>
+#include <cstring>
+#include <string>
+#include <vector>
+
+#include "../../include/gpt2.h"
+#include "kernels.h"
+
+namespace {
+
+thread_local std::string g_err;
+
+int fail(int code, const char* fmt, ...) {
+    char buf[512];
+    va_list ap;
+    va_start(ap, fmt);
+    vsnprintf(buf, sizeof buf, fmt, ap);
+    va_end(ap);
+    g_err = buf;
+    return code;
+}
+
+const char* kParamNames[16] = {"wte",      "wpe",      "ln1w", "ln1b", "qkvw",    "qkvb",
+                               "attprojw", "attprojb", "ln2w", "ln2b", "fcw",     "fcb",
+                               "fcprojw",  "fcprojb",  "lnfw", "lnfb"};
+enum { P_WTE, P_WPE, P_LN1W, P_LN1B, P_QKVW, P_QKVB, P_ATTPROJW, P_ATTPROJB,
+       P_LN2W, P_LN2B, P_FCW, P_FCB, P_FCPROJW, P_FCPROJB, P_LNFW, P_LNFB };
+
+void param_sizes(const gpt2_config* c, int64_t* s) {
+    const int64_t L = c->num_layers, C = c->channels, V = c->vocab_size, T = c->max_seq_len;
+    const int64_t v[16] = {V * C, T * C, L * C, L * C, L * 3 * C * C, L * 3 * C, L * C * C,
+                           L * C, L * C, L * C, L * 4 * C * C, L * 4 * C, L * C * 4 * C,
+                           L * C, C, C};
+    for (int i = 0; i < 16; i++) s[i] = v[i];
+}
+
+int ceil_log2(int64_t n) {
+    int b = 0;
+    while ((int64_t(1) << b) < n) b++;
+    return b;
+}
+
+int check_config(const gpt2_config* c) {
+    if (!c) return fail(GPT2_EINVAL, "config is NULL");
+    if (c->num_layers <= 0 || c->channels <= 0 || c->num_heads <= 0 || c->vocab_size <= 0 ||
+        c->max_seq_len <= 0 || c->batch_size <= 0 || c->seq_len <= 0)
+        return fail(GPT2_EINVAL, "every config field must be positive");
+    if (c->channels % c->num_heads)
+        return fail(GPT2_EINVAL, "channels (%d) must be a multiple of num_heads (%d)",
+                    c->channels, c->num_heads);
+    const int hs = c->channels / c->num_heads;
+    if (hs != 16 && hs != 32 && hs != 64)
+        return fail(GPT2_EINVAL, "head size %d not supported (16, 32 or 64)", hs);
+    if (c->channels > 1024) return fail(GPT2_EINVAL, "channels > 1024 not supported");
+    if (c->seq_len > c->max_seq_len)
+        return fail(GPT2_EINVAL, "seq_len %d > max_seq_len %d", c->seq_len, c->max_seq_len);
+    if ((int64_t)c->batch_size * c->seq_len > 32768)
+        return fail(GPT2_EINVAL, "batch_size*seq_len > 32768 not supported");
+    if (c->vocab_size > 65536) return fail(GPT2_EINVAL, "vocab_size > 65536 not supported");
+    if (c->precision != GPT2_FP32 && c->precision != GPT2_BF16_MIXED)
+        return fail(GPT2_EINVAL, "unknown precision %d", c->precision);
+    if (c->precision == GPT2_BF16_MIXED)
+        return fail(GPT2_EINVAL, "GPT2_BF16_MIXED is not built into this library");
+    return GPT2_OK;
+}
+
+inline size_t align256(size_t x) { return (x + 255) & ~size_t(255); }
+
+// Byte offsets of every sub-buffer inside the one device allocation.
+struct Layout {
+    int L, C, NH, V, Vp, maxT, Bmax, Tmax, M, pos_bits, n_pow2;
+    int64_t nparams, poff[16], psize[16];
+    size_t params, grads, m, v;
+    size_t encoded, ln1, ln1_mean, ln1_rstd, qkv, atty, lse, res2, ln2, ln2_mean, ln2_rstd, fch,
+        fch_gelu, res3, lnf, lnf_mean, lnf_rstd, logits, losses;
+    size_t dres, dtmp, dqkv, dfch, attn_d, ln_part, bias_part, gemm_ws, keys, tokens, targets,
+        scalars;
+    size_t gemm_ws_bytes, total;
+
+    void build(const gpt2_config* c) {
+        L = c->num_layers;
+        C = c->channels;
+        NH = c->num_heads;
+        V = c->vocab_size;
+        Vp = (V + 63) / 64 * 64;
+        maxT = c->max_seq_len;
+        Bmax = c->batch_size;
+        Tmax = c->seq_len;
+        M = Bmax * Tmax;
+        pos_bits = std::max(1, ceil_log2(M));
+        n_pow2 = 1 << ceil_log2(M);
+        param_sizes(c, psize);
+        nparams = 0;
+        for (int i = 0; i < 16; i++) {
+            poff[i] = nparams;
+            nparams += psize[i];
+        }
+        size_t off = 0;
+        auto take = [&](size_t bytes) {
+            size_t o = off;
+            off = align256(off + bytes);
+            return o;
+        };
+        const size_t f = sizeof(float);
+        const size_t MC = (size_t)M * C;
+        params = take(nparams * f);
+        grads = take(nparams * f);
+        m = take(nparams * f);
+        v = take(nparams * f);
+        encoded = take(MC * f);
+        ln1 = take(L * MC * f);
+        ln1_mean = take((size_t)L * M * f);
+        ln1_rstd = take((size_t)L * M * f);
+        qkv = take(L * 3 * MC * f);
+        atty = take(L * MC * f);
+        lse = take((size_t)L * M * NH * f);
+        res2 = take(L * MC * f);
+        ln2 = take(L * MC * f);
+        ln2_mean = take((size_t)L * M * f);
+        ln2_rstd = take((size_t)L * M * f);
+        fch = take(L * 4 * MC * f);
+        fch_gelu = take(L * 4 * MC * f);
+        res3 = take(L * MC * f);
+        lnf = take(MC * f);
+        lnf_mean = take((size_t)M * f);
+        lnf_rstd = take((size_t)M * f);
+        logits = take((size_t)M * Vp * f);
+        losses = take((size_t)M * f);
+        dres = take(MC * f);
+        dtmp = take(MC * f);
+        dqkv = take(3 * MC * f);
+        dfch = take(4 * MC * f);
+        attn_d = take((size_t)M * NH * f);
+        ln_part = take(gk::layernorm_partials_floats(M, C) * f);
+        bias_part = take(gk::bias_partials_floats(M, 4 * C) * f);
+        gemm_ws_bytes = 0;
+        const int outs[4][2] = {{3 * C, C}, {C, C}, {4 * C, C}, {C, 4 * C}};
+        for (auto& o : outs)
+            gemm_ws_bytes = std::max(gemm_ws_bytes, gk::gemm_workspace_bytes(gk::GEMM_TN, o[0], o[1], M));
+        gemm_ws_bytes = std::max(gemm_ws_bytes, gk::gemm_workspace_bytes(gk::GEMM_TN, V, C, M));
+        gemm_ws = take(gemm_ws_bytes);
+        keys = take((size_t)n_pow2 * sizeof(uint32_t));
+        tokens = take((size_t)M * sizeof(int32_t));
+        targets = take((size_t)M * sizeof(int32_t));
+        scalars = take(256);
+        total = off;
+    }
+};
+
+constexpr int kEventPool = 4096;
+
+struct Prof {
+    bool on = false;
+    std::vector<hipEvent_t> ev;
+    struct Rec {
+        int kc;
+        double flops, bytes;
+    };
+    std::vector<Rec> recs;
+    double ms[GPT2_KC_COUNT] = {}, fl[GPT2_KC_COUNT] = {}, by[GPT2_KC_COUNT] = {};
+    int64_t n[GPT2_KC_COUNT] = {};
+};
+
+}  // namespace
+
+struct gpt2_model {
+    gpt2_config cfg;
+    Layout lay;
+    hipStream_t stream = nullptr;
+    gpt2_allocator alloc{};
+    bool custom_alloc = false;
+    char* base = nullptr;
+    int32_t* h_stage = nullptr;  // pinned: tokens then targets
+    float* h_scal = nullptr;     // pinned: loss, flag
+    hipEvent_t stage_done = nullptr;
+    bool stage_pending = false;
+    int B = 0, T = 0;
+    bool have_fwd = false, have_targets = false;
+    Prof prof;
+
+    template <class X>
+    X* at(size_t off) const {
+        return reinterpret_cast<X*>(base + off);
+    }
+    float* P(int i) const { return at<float>(lay.params) + lay.poff[i]; }
+    float* G(int i) const { return at<float>(lay.grads) + lay.poff[i]; }
+    int* flag() const { return at<int>(lay.scalars + 4); }
+    float* dloss() const { return at<float>(lay.scalars); }
+};
+
+namespace {
+
+// ---- per-launch timing ------------------------------------------------------
+
+void prof_flush(gpt2_model* md) {
+    Prof& p = md->prof;
+    if (p.recs.empty()) return;
+    hipEventSynchronize(p.ev[2 * p.recs.size() - 1]);
+    for (size_t i = 0; i < p.recs.size(); i++) {
+        float ms = 0.f;
+        hipEventElapsedTime(&ms, p.ev[2 * i], p.ev[2 * i + 1]);
+        const int kc = p.recs[i].kc;
+        p.ms[kc] += ms;
+        p.n[kc] += 1;
+        p.fl[kc] += p.recs[i].flops;
+        p.by[kc] += p.recs[i].bytes;
+    }
+    p.recs.clear();
+}
+
+struct Scope {
+    gpt2_model* md;
+    int kc;
+    double flops, bytes;
+    bool on;
+    Scope(gpt2_model* m, int k, double f, double b) : md(m), kc(k), flops(f), bytes(b) {
+        on = md->prof.on;
+        if (!on) return;
+        if (2 * (md->prof.recs.size() + 1) > md->prof.ev.size()) prof_flush(md);
+        hipEventRecord(md->prof.ev[2 * md->prof.recs.size()], md->stream);
+    }
+    ~Scope() {
+        if (!on) return;
+        hipEventRecord(md->prof.ev[2 * md->prof.recs.size() + 1], md->stream);
+        md->prof.recs.push_back({kc, flops, bytes});
+    }
+};
+
+#define LAUNCH(md, kc, flops, bytes, call)                                                \
+    do {                                                                                  \
+        hipError_t e_;                                                                    \
+        {                                                                                 \
+            Scope sc_(md, kc, (double)(flops), (double)(bytes));                          \
+            e_ = (call);                                                                  \
+        }                                                                                 \
+        if (e_ != hipSuccess)                                                             \
+            return fail(GPT2_EDEVICE, "%s: %s", #call, hipGetErrorString(e_));            \
+    } while (0)
+
+int hip_check(hipError_t e, const char* what) {
+    if (e != hipSuccess) return fail(GPT2_EDEVICE, "%s: %s", what, hipGetErrorString(e));
+    return GPT2_OK;
+}
+
+gk::GemmArgs gemm_args(int op, int epi, int M, int N, int K, const float* A, int64_t lda,
+                       const float* B, int64_t ldb, float* C, int64_t ldc) {
+    gk::GemmArgs a{};
+    a.op = op;
+    a.epi = epi;
+    a.M = M;
+    a.N = N;
+    a.K = K;
+    a.A = A;
+    a.lda = lda;
+    a.B = B;
+    a.ldb = ldb;
+    a.C = C;
+    a.ldc = ldc;
+    return a;
+}
+
+int run_gemm(gpt2_model* md, const gk::GemmArgs& a) {
+    const double flops = 2.0 * a.M * a.N * (double)a.K;
+    const double bytes = 4.0 * ((double)a.M * a.K + (double)a.K * a.N + (double)a.M * a.N);
+    LAUNCH(md, GPT2_KC_GEMM, flops, bytes,
+           gk::gemm(md->stream, a, md->at<float>(md->lay.gemm_ws), md->lay.gemm_ws_bytes));
+    return GPT2_OK;
+}
+
+#define TRY(x)                      \
+    do {                            \
+        int r_ = (x);               \
+        if (r_ != GPT2_OK) return r_; \
+    } while (0)
+
+// ---- forward ---------------------------------------------------------------
+
+int forward_impl(gpt2_model* md, const int32_t* tok, const int32_t* tgt, int B, int T) {
+    const Layout& y = md->lay;
+    const int L = y.L, C = y.C, NH = y.NH, V = y.V, M = B * T;
+    const size_t MC = (size_t)y.M * C;  // per-layer capacity stride
+    const double f4 = 4.0;
+    hipStream_t s = md->stream;
+    float* enc = md->at<float>(y.encoded);
+
+    LAUNCH(md, GPT2_KC_OTHER, 0, 4.0, gk::fill_zero(s, (float*)md->flag(), 1));
+    LAUNCH(md, GPT2_KC_OTHER, 0, f4 * (3.0 * M * C) + 4.0 * M,
+           gk::encoder_forward(s, enc, tok, md->P(P_WTE), md->P(P_WPE), B, T, C, V, md->flag()));
+    for (int l = 0; l < L; l++) {
+        const float* resid = l == 0 ? enc : md->at<float>(y.res3) + (l - 1) * MC;
+        float* ln1 = md->at<float>(y.ln1) + l * MC;
+        float* ln1m = md->at<float>(y.ln1_mean) + (size_t)l * y.M;
+        float* ln1r = md->at<float>(y.ln1_rstd) + (size_t)l * y.M;
+        float* qkv = md->at<float>(y.qkv) + l * 3 * MC;
+        float* atty = md->at<float>(y.atty) + l * MC;
+        float* lse = md->at<float>(y.lse) + (size_t)l * y.M * NH;
+        float* res2 = md->at<float>(y.res2) + l * MC;
+        float* ln2 = md->at<float>(y.ln2) + l * MC;
+        float* ln2m = md->at<float>(y.ln2_mean) + (size_t)l * y.M;
+        float* ln2r = md->at<float>(y.ln2_rstd) + (size_t)l * y.M;
+        float* fch = md->at<float>(y.fch) + l * 4 * MC;
+        float* fchg = md->at<float>(y.fch_gelu) + l * 4 * MC;
+        float* res3 = md->at<float>(y.res3) + l * MC;
+
+        LAUNCH(md, GPT2_KC_LAYERNORM, 0, f4 * (2.0 * M * C + 2.0 * M),
+               gk::layernorm_forward(s, ln1, ln1m, ln1r, resid, md->P(P_LN1W) + l * C,
+                                     md->P(P_LN1B) + l * C, M, C));
+        gk::GemmArgs a = gemm_args(gk::GEMM_NT, gk::EPI_STORE, M, 3 * C, C, ln1, C,
+                                   md->P(P_QKVW) + (size_t)l * 3 * C * C, C, qkv, 3 * C);
+        a.bias = md->P(P_QKVB) + l * 3 * C;
+        TRY(run_gemm(md, a));
+        {
+            const double hs = C / NH;
+            const double flops = 4.0 * B * NH * hs * (double)T * (T + 1) / 2.0;
+            LAUNCH(md, GPT2_KC_ATTENTION, flops, f4 * (4.0 * M * C + (double)M * NH),
+                   gk::attention_forward(s, atty, lse, qkv, B, T, C, NH));
+        }
+        a = gemm_args(gk::GEMM_NT, gk::EPI_RESID, M, C, C, atty, C,
+                      md->P(P_ATTPROJW) + (size_t)l * C * C, C, res2, C);
+        a.bias = md->P(P_ATTPROJB) + l * C;
+        a.aux = resid;
+        a.ldaux = C;
+        TRY(run_gemm(md, a));
+        LAUNCH(md, GPT2_KC_LAYERNORM, 0, f4 * (2.0 * M * C + 2.0 * M),
+               gk::layernorm_forward(s, ln2, ln2m, ln2r, res2, md->P(P_LN2W) + l * C,
+                                     md->P(P_LN2B) + l * C, M, C));
+        a = gemm_args(gk::GEMM_NT, gk::EPI_GELU, M, 4 * C, C, ln2, C,
+                      md->P(P_FCW) + (size_t)l * 4 * C * C, C, fch, 4 * C);
+        a.bias = md->P(P_FCB) + l * 4 * C;
+        a.out2 = fchg;
+        TRY(run_gemm(md, a));
+        a = gemm_args(gk::GEMM_NT, gk::EPI_RESID, M, C, 4 * C, fchg, 4 * C,
+                      md->P(P_FCPROJW) + (size_t)l * C * 4 * C, 4 * C, res3, C);
+        a.bias = md->P(P_FCPROJB) + l * C;
+        a.aux = res2;
+        a.ldaux = C;
+        TRY(run_gemm(md, a));
+    }
+    const float* last = md->at<float>(y.res3) + (L - 1) * MC;
+    float* lnf = md->at<float>(y.lnf);
+    LAUNCH(md, GPT2_KC_LAYERNORM, 0, f4 * (2.0 * M * C + 2.0 * M),
+           gk::layernorm_forward(s, lnf, md->at<float>(y.lnf_mean), md->at<float>(y.lnf_rstd),
+                                 last, md->P(P_LNFW), md->P(P_LNFB), M, C));
+    float* logits = md->at<float>(y.logits);
+    TRY(run_gemm(md, gemm_args(gk::GEMM_NT, gk::EPI_STORE, M, V, C, lnf, C, md->P(P_WTE), C,
+                               logits, y.Vp)));
+    if (tgt) {
+        float* losses = md->at<float>(y.losses);
+        LAUNCH(md, GPT2_KC_SOFTMAX_CE, 0, f4 * 2.0 * M * (double)V + 8.0 * M,
+               gk::softmax_ce(s, logits, losses, tgt, M, V, y.Vp, 1.0f / M, md->flag()));
+        LAUNCH(md, GPT2_KC_OTHER, 0, 4.0 * M, gk::mean_reduce(s, md->dloss(), losses, M));
+        const int np2 = 1 << ceil_log2(M);
+        LAUNCH(md, GPT2_KC_OTHER, 0, 4.0 * M + 4.0 * np2,
+               gk::encoder_sort(s, md->at<uint32_t>(y.keys), tok, M, V, y.pos_bits, np2));
+    }
+    md->B = B;
+    md->T = T;
+    md->have_fwd = true;
+    md->have_targets = tgt != nullptr;
+    return GPT2_OK;
+}
+
+int read_loss(gpt2_model* md, float* mean_loss) {
+    TRY(hip_check(hipMemcpyAsync(md->h_scal, md->at<char>(md->lay.scalars), 8,
+                                 hipMemcpyDeviceToHost, md->stream),
+                  "loss readback"));
+    TRY(hip_check(hipStreamSynchronize(md->stream), "stream synchronize"));
+    int flag;
+    std::memcpy(&flag, md->h_scal + 1, 4);
+    if (mean_loss) *mean_loss = md->have_targets ? md->h_scal[0] : NAN;
+    if (flag & 1) return fail(GPT2_ERANGE, "a token id is outside [0, vocab_size)");
+    if (flag & 2) return fail(GPT2_ERANGE, "a target id is outside [0, vocab_size)");
+    return GPT2_OK;
+}
+
+int check_bt(gpt2_model* md, int B, int T) {
+    if (B <= 0 || T <= 0 || B > md->lay.Bmax || T > md->lay.Tmax)
+        return fail(GPT2_EINVAL, "B=%d T=%d outside the allocated 1..%d x 1..%d", B, T,
+                    md->lay.Bmax, md->lay.Tmax);
+    return GPT2_OK;
+}
+
+// ---- backward --------------------------------------------------------------
+
+int backward_impl(gpt2_model* md) {
+    const Layout& y = md->lay;
+    const int L = y.L, C = y.C, NH = y.NH, V = y.V, B = md->B, T = md->T, M = B * T;
+    const size_t MC = (size_t)y.M * C;
+    const double f4 = 4.0;
+    hipStream_t s = md->stream;
+    float* dres = md->at<float>(y.dres);
+    float* dtmp = md->at<float>(y.dtmp);
+    float* dqkv = md->at<float>(y.dqkv);
+    float* dfch = md->at<float>(y.dfch);
+    float* lnpart = md->at<float>(y.ln_part);
+    float* bpart = md->at<float>(y.bias_part);
+    float* dlogits = md->at<float>(y.logits);
+    float* lnf = md->at<float>(y.lnf);
+
+    // LM head (tied): dlnf = dlogits wte;  dwte += dlogits^T lnf
+    TRY(run_gemm(md, gemm_args(gk::GEMM_NN, gk::EPI_STORE, M, C, V, dlogits, y.Vp,
+                               md->P(P_WTE), C, dtmp, C)));
+    TRY(run_gemm(md, gemm_args(gk::GEMM_TN, gk::EPI_ACCUM, V, C, M, dlogits, y.Vp, lnf, C,
+                               md->G(P_WTE), C)));
+    const float* last = md->at<float>(y.res3) + (L - 1) * MC;
+    LAUNCH(md, GPT2_KC_LAYERNORM, 0, f4 * (3.0 * M * C + 2.0 * M),
+           gk::layernorm_backward(s, dres, 0, md->G(P_LNFW), md->G(P_LNFB), lnpart, dtmp, last,
+                                  md->P(P_LNFW), md->at<float>(y.lnf_mean),
+                                  md->at<float>(y.lnf_rstd), M, C));
+    for (int l = L - 1; l >= 0; l--) {
+        const float* resid = l == 0 ? md->at<float>(y.encoded) : md->at<float>(y.res3) + (l - 1) * MC;
+        const float* ln1 = md->at<float>(y.ln1) + l * MC;
+        const float* ln1m = md->at<float>(y.ln1_mean) + (size_t)l * y.M;
+        const float* ln1r = md->at<float>(y.ln1_rstd) + (size_t)l * y.M;
+        const float* qkv = md->at<float>(y.qkv) + l * 3 * MC;
+        const float* atty = md->at<float>(y.atty) + l * MC;
+        const float* lse = md->at<float>(y.lse) + (size_t)l * y.M * NH;
+        const float* res2 = md->at<float>(y.res2) + l * MC;
+        const float* ln2 = md->at<float>(y.ln2) + l * MC;
+        const float* ln2m = md->at<float>(y.ln2_mean) + (size_t)l * y.M;
+        const float* ln2r = md->at<float>(y.ln2_rstd) + (size_t)l * y.M;
+        const float* fch = md->at<float>(y.fch) + l * 4 * MC;
+        const float* fchg = md->at<float>(y.fch_gelu) + l * 4 * MC;
+
+        // MLP projection: dfch = (dres W) * gelu'(fch);  dW += dres^T gelu(fch)
+        gk::GemmArgs a = gemm_args(gk::GEMM_NN, gk::EPI_GELU_BWD, M, 4 * C, C, dres, C,
+                                   md->P(P_FCPROJW) + (size_t)l * C * 4 * C, 4 * C, dfch, 4 * C);
+        a.aux = fch;
+        a.ldaux = 4 * C;
+        TRY(run_gemm(md, a));
+        TRY(run_gemm(md, gemm_args(gk::GEMM_TN, gk::EPI_ACCUM, C, 4 * C, M, dres, C, fchg,
+                                   4 * C, md->G(P_FCPROJW) + (size_t)l * C * 4 * C, 4 * C)));
+        LAUNCH(md, GPT2_KC_OTHER, 0, f4 * M * C,
+               gk::bias_grad(s, md->G(P_FCPROJB) + l * C, bpart, dres, M, C, C));
+        // MLP fc: dln2 = dfch W;  dW += dfch^T ln2
+        TRY(run_gemm(md, gemm_args(gk::GEMM_NN, gk::EPI_STORE, M, C, 4 * C, dfch, 4 * C,
+                                   md->P(P_FCW) + (size_t)l * 4 * C * C, C, dtmp, C)));
+        TRY(run_gemm(md, gemm_args(gk::GEMM_TN, gk::EPI_ACCUM, 4 * C, C, M, dfch, 4 * C, ln2,
+                                   C, md->G(P_FCW) + (size_t)l * 4 * C * C, C)));
+        LAUNCH(md, GPT2_KC_OTHER, 0, f4 * 4.0 * M * C,
+               gk::bias_grad(s, md->G(P_FCB) + l * 4 * C, bpart, dfch, M, 4 * C, 4 * C));
+        LAUNCH(md, GPT2_KC_LAYERNORM, 0, f4 * (4.0 * M * C + 2.0 * M),
+               gk::layernorm_backward(s, dres, 1, md->G(P_LN2W) + l * C, md->G(P_LN2B) + l * C,
+                                      lnpart, dtmp, res2, md->P(P_LN2W) + l * C, ln2m, ln2r, M, C));
+        // attention projection: datty = dres W;  dW += dres^T atty
+        TRY(run_gemm(md, gemm_args(gk::GEMM_NN, gk::EPI_STORE, M, C, C, dres, C,
+                                   md->P(P_ATTPROJW) + (size_t)l * C * C, C, dtmp, C)));
+        TRY(run_gemm(md, gemm_args(gk::GEMM_TN, gk::EPI_ACCUM, C, C, M, dres, C, atty, C,
+                                   md->G(P_ATTPROJW) + (size_t)l * C * C, C)));
+        LAUNCH(md, GPT2_KC_OTHER, 0, f4 * M * C,
+               gk::bias_grad(s, md->G(P_ATTPROJB) + l * C, bpart, dres, M, C, C));
+        {
+            const double hs = C / NH;
+            const double flops = 8.0 * B * NH * hs * (double)T * (T + 1) / 2.0;
+            LAUNCH(md, GPT2_KC_ATTENTION, flops, f4 * (7.0 * M * C + 2.0 * M * NH),
+                   gk::attention_backward(s, dqkv, md->at<float>(y.attn_d), dtmp, qkv, atty, lse,
+                                          B, T, C, NH));
+        }
+        // QKV: dln1 = dqkv W;  dW += dqkv^T ln1
+        TRY(run_gemm(md, gemm_args(gk::GEMM_NN, gk::EPI_STORE, M, C, 3 * C, dqkv, 3 * C,
+                                   md->P(P_QKVW) + (size_t)l * 3 * C * C, C, dtmp, C)));
+        TRY(run_gemm(md, gemm_args(gk::GEMM_TN, gk::EPI_ACCUM, 3 * C, C, M, dqkv, 3 * C, ln1, C,
+                                   md->G(P_QKVW) + (size_t)l * 3 * C * C, C)));
+        LAUNCH(md, GPT2_KC_OTHER, 0, f4 * 3.0 * M * C,
+               gk::bias_grad(s, md->G(P_QKVB) + l * 3 * C, bpart, dqkv, M, 3 * C, 3 * C));
+        LAUNCH(md, GPT2_KC_LAYERNORM, 0, f4 * (4.0 * M * C + 2.0 * M),
+               gk::layernorm_backward(s, dres, 1, md->G(P_LN1W) + l * C, md->G(P_LN1B) + l * C,
+                                      lnpart, dtmp, resid, md->P(P_LN1W) + l * C, ln1m, ln1r, M, C));
+    }
+    LAUNCH(md, GPT2_KC_OTHER, 0, f4 * (2.0 * M * C + 2.0 * T * C) + 4.0 * M,
+           gk::encoder_backward(s, md->G(P_WTE), md->G(P_WPE), dres, md->at<uint32_t>(y.keys), B,
+                                T, C, V, y.pos_bits));
+    return GPT2_OK;
+}
+
+bool valid_model(gpt2_model* md) { return md != nullptr && md->base != nullptr; }
+
+}  // namespace
+
+// ============================================================================
+// C ABI
+// ============================================================================
+
+extern "C" {
+
+const char* gpt2_last_error(void) { return g_err.c_str(); }
+
+int gpt2_validate_config(const gpt2_config* cfg) { return check_config(cfg); }
+
+int64_t gpt2_config_num_parameters(const gpt2_config* cfg) {
+    if (check_config(cfg) != GPT2_OK) return -1;
+    int64_t s[16], n = 0;
+    param_sizes(cfg, s);
+    for (int i = 0; i < 16; i++) n += s[i];
+    return n;
+}
+
+int gpt2_config_param_tensor(const gpt2_config* cfg, int i, const char** name, int64_t* offset,
+                             int64_t* numel) {
+    TRY(check_config(cfg));
+    if (i < 0 || i >= 16) return fail(GPT2_EINVAL, "parameter index %d outside 0..15", i);
+    int64_t s[16], off = 0;
+    param_sizes(cfg, s);
+    for (int k = 0; k < i; k++) off += s[k];
+    if (name) *name = kParamNames[i];
+    if (offset) *offset = off;
+    if (numel) *numel = s[i];
+    return GPT2_OK;
+}
+
+int64_t gpt2_config_device_bytes(const gpt2_config* cfg) {
+    if (check_config(cfg) != GPT2_OK) return -1;
+    Layout y;
+    y.build(cfg);
+    return (int64_t)y.total;
+}
+
+void gpt2_destroy(gpt2_model* md) {
+    if (!md) return;
+    if (md->stream != nullptr || md->base) hipStreamSynchronize(md->stream);
+    for (hipEvent_t e : md->prof.ev) hipEventDestroy(e);
+    if (md->stage_done) hipEventDestroy(md->stage_done);
+    if (md->h_stage) hipHostFree(md->h_stage);
+    if (md->h_scal) hipHostFree(md->h_scal);
+    if (md->base) {
+        if (md->custom_alloc)
+            md->alloc.free(md->base, md->alloc.ctx);
+        else
+            hipFree(md->base);
+    }
+    delete md;
+}
+
+int gpt2_create(const gpt2_config* cfg, const gpt2_allocator* alloc, void* hip_stream,
+                gpt2_model** out) {
+    if (!out) return fail(GPT2_EINVAL, "out is NULL");
+    *out = nullptr;
+    TRY(check_config(cfg));
+    if (alloc && (!alloc->alloc || !alloc->free))
+        return fail(GPT2_EINVAL, "allocator needs both alloc and free");
+    gpt2_model* md = new gpt2_model();
+    md->cfg = *cfg;
+    md->lay.build(cfg);
+    md->stream = (hipStream_t)hip_stream;
+    int rc = GPT2_OK;
+    if (alloc) {
+        md->alloc = *alloc;
+        md->custom_alloc = true;
+        md->base = (char*)alloc->alloc(md->lay.total, alloc->ctx);
+        if (!md->base) rc = fail(GPT2_ENOMEM, "allocator returned NULL for %zu bytes", md->lay.total);
+    } else {
+        hipError_t e = hipMalloc((void**)&md->base, md->lay.total);
+        if (e != hipSuccess) {
+            md->base = nullptr;
+            rc = fail(e == hipErrorOutOfMemory ? GPT2_ENOMEM : GPT2_EDEVICE,
+                      "hipMalloc(%zu): %s", md->lay.total, hipGetErrorString(e));
+        }
+    }
+    if (rc == GPT2_OK && ((uintptr_t)md->base & 255))
+        rc = fail(GPT2_EINVAL, "allocator returned memory not aligned to 256 bytes");
+    if (rc == GPT2_OK)
+        rc = hip_check(hipHostMalloc((void**)&md->h_stage, 2 * (size_t)md->lay.M * sizeof(int32_t)),
+                       "hipHostMalloc");
+    if (rc == GPT2_OK) rc = hip_check(hipHostMalloc((void**)&md->h_scal, 64), "hipHostMalloc");
+    if (rc == GPT2_OK)
+        rc = hip_check(hipEventCreateWithFlags(&md->stage_done, hipEventDisableTiming),
+                       "hipEventCreate");
+    if (rc == GPT2_OK) {
+        const hipError_t e = gk::encoder_sort_prepare(md->lay.n_pow2);
+        rc = hip_check(e, "encoder sort setup");
+    }
+    if (rc == GPT2_OK) {
+        // parameters, gradients and both moments start at zero
+        const hipError_t e = gk::fill_zero(md->stream, md->at<float>(0),
+                                           (int64_t)(md->lay.encoded / sizeof(float)));
+        rc = hip_check(e, "zero arenas");
+        if (rc == GPT2_OK) rc = hip_check(hipStreamSynchronize(md->stream), "synchronize");
+    }
+    if (rc != GPT2_OK) {
+        std::string msg = g_err;
+        gpt2_destroy(md);
+        g_err = msg;
+        return rc;
+    }
+    *out = md;
+    return GPT2_OK;
+}
+
+int64_t gpt2_num_parameters(const gpt2_model* md) { return md ? md->lay.nparams : -1; }
+
+int gpt2_param_tensor(const gpt2_model* md, int i, const char** name, int64_t* offset,
+                      int64_t* numel) {
+    if (!md) return fail(GPT2_EINVAL, "model is NULL");
+    return gpt2_config_param_tensor(&md->cfg, i, name, offset, numel);
+}
+
+int gpt2_copy_params(gpt2_model* md, float* dst, const float* src) {
+    if (!valid_model(md)) return fail(GPT2_EINVAL, "model is NULL");
+    if ((dst == nullptr) == (src == nullptr))
+        return fail(GPT2_EINVAL, "exactly one of host_dst and host_src must be non-NULL");
+    const size_t bytes = md->lay.nparams * sizeof(float);
+    TRY(hip_check(hipStreamSynchronize(md->stream), "synchronize"));
+    if (dst)
+        return hip_check(hipMemcpy(dst, md->P(0), bytes, hipMemcpyDeviceToHost), "copy params");
+    return hip_check(hipMemcpy(md->P(0), src, bytes, hipMemcpyHostToDevice), "copy params");
+}
+
+int gpt2_copy_grads(gpt2_model* md, float* dst) {
+    if (!valid_model(md) || !dst) return fail(GPT2_EINVAL, "NULL argument");
+    TRY(hip_check(hipStreamSynchronize(md->stream), "synchronize"));
+    return hip_check(hipMemcpy(dst, md->G(0), md->lay.nparams * sizeof(float),
+                               hipMemcpyDeviceToHost),
+                     "copy grads");
+}
+
+int gpt2_copy_opt_state(gpt2_model* md, float* hm, float* hv) {
+    if (!valid_model(md)) return fail(GPT2_EINVAL, "model is NULL");
+    TRY(hip_check(hipStreamSynchronize(md->stream), "synchronize"));
+    const size_t bytes = md->lay.nparams * sizeof(float);
+    if (hm) TRY(hip_check(hipMemcpy(hm, md->at<float>(md->lay.m), bytes, hipMemcpyDeviceToHost), "copy m"));
+    if (hv) TRY(hip_check(hipMemcpy(hv, md->at<float>(md->lay.v), bytes, hipMemcpyDeviceToHost), "copy v"));
+    return GPT2_OK;
+}
+
+int gpt2_copy_activation(gpt2_model* md, const char* name, int layer, float* dst,
+                         int64_t* numel) {
+    if (!valid_model(md) || !name) return fail(GPT2_EINVAL, "NULL argument");
+    if (!md->have_fwd) return fail(GPT2_ESTATE, "no forward has run");
+    const Layout& y = md->lay;
+    const int64_t M = (int64_t)md->B * md->T, C = y.C;
+    const size_t MC = (size_t)y.M * C;
+    struct Item {
+        const char* n;
+        size_t off;
+        size_t layer_stride;  // elements; 0 = not per layer
+        int64_t width;        // per row of B*T
+    };
+    const Item items[] = {
+        {"encoded", y.encoded, 0, C},
+        {"ln1", y.ln1, MC, C},
+        {"ln1_mean", y.ln1_mean, (size_t)y.M, 1},
+        {"ln1_rstd", y.ln1_rstd, (size_t)y.M, 1},
+        {"qkv", y.qkv, 3 * MC, 3 * C},
+        {"atty", y.atty, MC, C},
+        {"att_lse", y.lse, (size_t)y.M * y.NH, y.NH},
+        {"residual2", y.res2, MC, C},
+        {"ln2", y.ln2, MC, C},
+        {"ln2_mean", y.ln2_mean, (size_t)y.M, 1},
+        {"ln2_rstd", y.ln2_rstd, (size_t)y.M, 1},
+        {"fch", y.fch, 4 * MC, 4 * C},
+        {"fch_gelu", y.fch_gelu, 4 * MC, 4 * C},
+        {"residual3", y.res3, MC, C},
+        {"lnf", y.lnf, 0, C},
+        {"lnf_mean", y.lnf_mean, 0, 1},
+        {"lnf_rstd", y.lnf_rstd, 0, 1},
+        {"logits", y.logits, 0, y.V},
+        {"losses", y.losses, 0, 1},
+    };
+    for (const Item& it : items) {
+        if (std::strcmp(it.n, name)) continue;
+        if (it.layer_stride && (layer < 0 || layer >= y.L))
+            return fail(GPT2_EINVAL, "layer %d outside 0..%d", layer, y.L - 1);
+        const int64_t n = M * it.width;
+        if (numel) *numel = n;
+        if (!dst) return GPT2_OK;
+        TRY(hip_check(hipStreamSynchronize(md->stream), "synchronize"));
+        const float* src = md->at<float>(it.off) + (it.layer_stride ? layer * it.layer_stride : 0);
+        if (std::strcmp(name, "logits") == 0)
+            return hip_check(hipMemcpy2D(dst, y.V * sizeof(float), src, y.Vp * sizeof(float),
+                                         y.V * sizeof(float), M, hipMemcpyDeviceToHost),
+                             "copy logits");
+        return hip_check(hipMemcpy(dst, src, n * sizeof(float), hipMemcpyDeviceToHost),
+                         "copy activation");
+    }
+    return fail(GPT2_EINVAL, "unknown activation name '%s'", name);
+}
+
+int gpt2_forward(gpt2_model* md, const int32_t* tokens, const int32_t* targets, int B, int T,
+                 float* mean_loss) {
+    if (!valid_model(md) || !tokens) return fail(GPT2_EINVAL, "NULL argument");
+    TRY(check_bt(md, B, T));
+    const int M = B * T, V = md->lay.V;
+    for (int i = 0; i < M; i++)
+        if (tokens[i] < 0 || tokens[i] >= V)
+            return fail(GPT2_ERANGE, "token %d at position %d outside [0, %d)", tokens[i], i, V);
+    if (targets)
+        for (int i = 0; i < M; i++)
+            if (targets[i] < 0 || targets[i] >= V)
+                return fail(GPT2_ERANGE, "target %d at position %d outside [0, %d)", targets[i],
+                            i, V);
+    // stage through pinned memory; wait until the previous upload has left it
+    if (md->stage_pending) TRY(hip_check(hipEventSynchronize(md->stage_done), "stage wait"));
+    std::memcpy(md->h_stage, tokens, M * sizeof(int32_t));
+    if (targets) std::memcpy(md->h_stage + md->lay.M, targets, M * sizeof(int32_t));
+    int32_t* dtok = md->at<int32_t>(md->lay.tokens);
+    int32_t* dtgt = md->at<int32_t>(md->lay.targets);
+    TRY(hip_check(hipMemcpyAsync(dtok, md->h_stage, M * sizeof(int32_t), hipMemcpyHostToDevice,
+                                 md->stream),
+                  "token upload"));
+    if (targets)
+        TRY(hip_check(hipMemcpyAsync(dtgt, md->h_stage + md->lay.M, M * sizeof(int32_t),
+                                     hipMemcpyHostToDevice, md->stream),
+                      "target upload"));
+    TRY(hip_check(hipEventRecord(md->stage_done, md->stream), "event record"));
+    md->stage_pending = true;
+    TRY(forward_impl(md, dtok, targets ? dtgt : nullptr, B, T));
+    if (mean_loss) return read_loss(md, mean_loss);
+    return GPT2_OK;
+}
+
+int gpt2_forward_device(gpt2_model* md, const int32_t* tokens, const int32_t* targets, int B,
+                        int T, float* mean_loss) {
+    if (!valid_model(md) || !tokens) return fail(GPT2_EINVAL, "NULL argument");
+    TRY(check_bt(md, B, T));
+    TRY(forward_impl(md, tokens, targets, B, T));
+    if (mean_loss) return read_loss(md, mean_loss);
+    return GPT2_OK;
+}
+
+int gpt2_zero_grad(gpt2_model* md) {
+    if (!valid_model(md)) return fail(GPT2_EINVAL, "model is NULL");
+    LAUNCH(md, GPT2_KC_OTHER, 0, 4.0 * md->lay.nparams,
+           gk::fill_zero(md->stream, md->G(0), md->lay.nparams));
+    return GPT2_OK;
+}
+
+int gpt2_backward(gpt2_model* md) {
+    if (!valid_model(md)) return fail(GPT2_EINVAL, "model is NULL");
+    if (!md->have_fwd || !md->have_targets)
+        return fail(GPT2_ESTATE, "backward needs a preceding forward with targets");
+    TRY(backward_impl(md));
+    md->have_targets = false;  // the logits gradient has been consumed
+    return GPT2_OK;
+}
+
+int gpt2_update(gpt2_model* md, float lr, float beta1, float beta2, float eps,
+                float weight_decay, int step) {
+    if (!valid_model(md)) return fail(GPT2_EINVAL, "model is NULL");
+    if (step < 1) return fail(GPT2_EINVAL, "step must be >= 1 (got %d)", step);
+    if (!(beta1 >= 0.f && beta1 < 1.f) || !(beta2 >= 0.f && beta2 < 1.f))
+        return fail(GPT2_EINVAL, "betas must be in [0, 1)");
+    const float bc1 = (float)(1.0 - std::pow((double)beta1, (double)step));
+    const float bc2 = (float)(1.0 - std::pow((double)beta2, (double)step));
+    const int64_t n = md->lay.nparams;
+    LAUNCH(md, GPT2_KC_ADAMW, 0, 28.0 * n,
+           gk::adamw(md->stream, md->P(0), md->G(0), md->at<float>(md->lay.m),
+                     md->at<float>(md->lay.v), n, lr, beta1, beta2, eps, weight_decay, bc1, bc2));
+    return GPT2_OK;
+}
+
+int gpt2_synchronize(gpt2_model* md) {
+    if (!valid_model(md)) return fail(GPT2_EINVAL, "model is NULL");
+    TRY(hip_check(hipStreamSynchronize(md->stream), "synchronize"));
+    int flag = 0;
+    TRY(hip_check(hipMemcpy(&flag, md->flag(), 4, hipMemcpyDeviceToHost), "flag readback"));
+    if (flag & 1) return fail(GPT2_ERANGE, "a token id is outside [0, vocab_size)");
+    if (flag & 2) return fail(GPT2_ERANGE, "a target id is outside [0, vocab_size)");
+    return GPT2_OK;
+}
+
+int gpt2_profile(gpt2_model* md, int enable) {
+    if (!valid_model(md)) return fail(GPT2_EINVAL, "model is NULL");
+    Prof& p = md->prof;
+    if (enable) {
+        if (p.ev.empty()) {
+            p.ev.resize(kEventPool);
+            for (auto& e : p.ev) TRY(hip_check(hipEventCreate(&e), "hipEventCreate"));
+        }
+        prof_flush(md);
+        for (int k = 0; k < GPT2_KC_COUNT; k++) p.ms[k] = p.fl[k] = p.by[k] = 0, p.n[k] = 0;
+        p.on = true;
+    } else {
+        prof_flush(md);
+        p.on = false;
+    }
+    return GPT2_OK;
+}
+
+int gpt2_profile_read(gpt2_model* md, int kc, double* total_ms, int64_t* launches,
+                      double* flops, double* bytes) {
+    if (!valid_model(md)) return fail(GPT2_EINVAL, "model is NULL");
+    if (kc < 0 || kc >= GPT2_KC_COUNT) return fail(GPT2_EINVAL, "kernel class %d", kc);
+    prof_flush(md);
+    if (total_ms) *total_ms = md->prof.ms[kc];
+    if (launches) *launches = md->prof.n[kc];
+    if (flops) *flops = md->prof.fl[kc];
+    if (bytes) *bytes = md->prof.by[kc];
+    return GPT2_OK;
+}
+
+}  // extern "C"

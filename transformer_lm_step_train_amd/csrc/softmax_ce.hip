@@ -1,0 +1,147 @@
+// Fused softmax + cross-entropy over the vocabulary, forward and backward in
+// one pass (ujoy.net article "徒手用 1000 行 C 语言实现", section "用C语言实现
+// LLM": the softmax and cross-entropy layers; section "训练过程": the mean
+// "train loss" printed each step).
+//
+// Per position n with logits z (V values) and target y:
+//   lse = max z + log sum_v exp(z_v - max z),  loss_n = lse - z_y,
+//   d(mean loss)/dz_v = (exp(z_v - lse) - [v == y]) / N.
+// This equals the materialized softmax followed by -log p_y.  One workgroup
+// holds a whole row in registers (one HBM read), and writes the gradient over
+// the logits (one HBM write).
+#include "common.h"
+#include "kernels.h"
+
+namespace gk {
+namespace {
+
+template <int NT>
+__device__ __forceinline__ float block_max(float v, float* sh) {
+    v = wave_max(v);
+    const int lane = threadIdx.x & 63, wave = threadIdx.x >> 6;
+    __syncthreads();
+    if (lane == 0) sh[wave] = v;
+    __syncthreads();
+    float r = sh[0];
+#pragma unroll
+    for (int i = 1; i < NT / 64; i++) r = fmaxf(r, sh[i]);
+    return r;
+}
+
+template <int NT>
+__device__ __forceinline__ float block_sum(float v, float* sh) {
+    v = wave_sum(v);
+    const int lane = threadIdx.x & 63, wave = threadIdx.x >> 6;
+    __syncthreads();
+    if (lane == 0) sh[wave] = v;
+    __syncthreads();
+    float r = sh[0];
+#pragma unroll
+    for (int i = 1; i < NT / 64; i++) r += sh[i];
+    return r;
+}
+
+template <int NT, int NJ>
+__global__ __launch_bounds__(NT) void softmax_ce_kernel(float* __restrict__ logits,
+                                                        float* __restrict__ losses,
+                                                        const int32_t* __restrict__ targets,
+                                                        int V, int ldv, float dscale,
+                                                        int* __restrict__ flag) {
+    __shared__ float sh[NT / 64];
+    const int64_t row = blockIdx.x;
+    float* z = logits + row * ldv;
+    const int V4 = ldv >> 2;
+    const int tgt = targets[row];
+    const bool bad = tgt < 0 || tgt >= V;
+    float4 v[NJ];
+    float mx = -INFINITY;
+#pragma unroll
+    for (int j = 0; j < NJ; j++) {
+        const int c4 = threadIdx.x + NT * j;
+        float4 x = make_float4(-INFINITY, -INFINITY, -INFINITY, -INFINITY);
+        if (c4 < V4) {
+            x = ld4(z + 4 * c4);
+            const int c = 4 * c4;
+            if (c >= V) x.x = -INFINITY;
+            if (c + 1 >= V) x.y = -INFINITY;
+            if (c + 2 >= V) x.z = -INFINITY;
+            if (c + 3 >= V) x.w = -INFINITY;
+        }
+        v[j] = x;
+        mx = fmaxf(mx, fmaxf(fmaxf(x.x, x.y), fmaxf(x.z, x.w)));
+    }
+    float zt = 0.f;
+    if (threadIdx.x == 0 && !bad) zt = z[tgt];
+    mx = block_max<NT>(mx, sh);
+    float s = 0.f;
+#pragma unroll
+    for (int j = 0; j < NJ; j++)
+        s += (expf(v[j].x - mx) + expf(v[j].y - mx)) + (expf(v[j].z - mx) + expf(v[j].w - mx));
+    s = block_sum<NT>(s, sh);
+    const float lse = mx + logf(s);
+    if (threadIdx.x == 0) {
+        losses[row] = bad ? 0.f : lse - zt;
+        if (bad) atomicOr(flag, 2);
+    }
+#pragma unroll
+    for (int j = 0; j < NJ; j++) {
+        const int c4 = threadIdx.x + NT * j;
+        if (c4 < V4) {
+            const int c = 4 * c4;
+            float4 d;
+            d.x = (expf(v[j].x - lse) - (c == tgt ? 1.f : 0.f)) * dscale;
+            d.y = (expf(v[j].y - lse) - (c + 1 == tgt ? 1.f : 0.f)) * dscale;
+            d.z = (expf(v[j].z - lse) - (c + 2 == tgt ? 1.f : 0.f)) * dscale;
+            d.w = (expf(v[j].w - lse) - (c + 3 == tgt ? 1.f : 0.f)) * dscale;
+            if (bad) d = make_float4(0.f, 0.f, 0.f, 0.f);
+            st4(z + c, d);  // exp(-inf) = 0 in the padding columns
+        }
+    }
+}
+
+template <int NT, int NJ>
+hipError_t launch_ce(hipStream_t s, float* logits, float* losses, const int32_t* targets,
+                     int N, int V, int ldv, float dscale, int* flag) {
+    hipLaunchKernelGGL((softmax_ce_kernel<NT, NJ>), dim3(N), dim3(NT), 0, s, logits, losses,
+                       targets, V, ldv, dscale, flag);
+    return hipGetLastError();
+}
+
+__global__ __launch_bounds__(1024) void mean_kernel(float* __restrict__ out,
+                                                    const float* __restrict__ x, int n) {
+    __shared__ double sh[16];
+    double s = 0.0;
+    for (int i = threadIdx.x; i < n; i += 1024) s += (double)x[i];
+    s = wave_sum_d(s);
+    if ((threadIdx.x & 63) == 0) sh[threadIdx.x >> 6] = s;
+    __syncthreads();
+    if (threadIdx.x == 0) {
+        double t = 0.0;
+        for (int i = 0; i < 16; i++) t += sh[i];
+        out[0] = (float)(t / n);
+    }
+}
+
+}  // namespace
+
+hipError_t softmax_ce(hipStream_t s, float* logits, float* losses, const int32_t* targets,
+                      int N, int V, int ldv, float dscale, int* flag) {
+    if (N <= 0) return hipSuccess;
+    const int V4 = ldv / 4;
+    if (V4 <= 256) return launch_ce<256, 1>(s, logits, losses, targets, N, V, ldv, dscale, flag);
+    const int nj = (V4 + 1023) / 1024;
+    if (nj <= 1) return launch_ce<1024, 1>(s, logits, losses, targets, N, V, ldv, dscale, flag);
+    if (nj <= 2) return launch_ce<1024, 2>(s, logits, losses, targets, N, V, ldv, dscale, flag);
+    if (nj <= 4) return launch_ce<1024, 4>(s, logits, losses, targets, N, V, ldv, dscale, flag);
+    if (nj <= 8) return launch_ce<1024, 8>(s, logits, losses, targets, N, V, ldv, dscale, flag);
+    if (nj <= 13) return launch_ce<1024, 13>(s, logits, losses, targets, N, V, ldv, dscale, flag);
+    if (nj <= 16) return launch_ce<1024, 16>(s, logits, losses, targets, N, V, ldv, dscale, flag);
+    return hipErrorInvalidValue;
+}
+
+hipError_t mean_reduce(hipStream_t s, float* out, const float* x, int n) {
+    hipLaunchKernelGGL(mean_kernel, dim3(1), dim3(1024), 0, s, out, x, n);
+    return hipGetLastError();
+}
+
+}  // namespace gk
