@@ -5,9 +5,11 @@ Tolerances (max |a - r| / max |r| per tensor unless noted):
   loss rel 1e-5; logits, their gradient and every parameter gradient 1e-3;
   parameters after the AdamW step 1e-4; forward activations 1e-4.
 The AdamW step is sign-like on step 1 (dp = -lr g/(|g| + eps)); an element
-whose gradient is at rounding-noise level can flip sign between two correct
-fp32 implementations.  Such elements (|g_gpu - g_ref| >= |g_ref|) are
-counted and excluded from the parameter check, and the update itself is
+whose gradient is at rounding-noise level gets an undetermined update from
+two correct fp32 implementations.  Such elements (|g_gpu - g_ref| >
+1e-3 |g_ref|, or |g_ref| so close to eps that a 1e-3 gradient error moves the
+update past the parameter tolerance) are counted and excluded from the
+parameter check (at most 0.5% of the arena), and the update itself is
 checked exactly by applying the oracle's AdamW to the GPU's own gradients.
 """
 import math
@@ -143,16 +145,30 @@ def check_step(P, tok, tgt, lr=1e-4, wd=0.0):
         assert rel(a, b) < 1e-6, n
     mg, vg = P.gpu.opt_state()
     assert rel(mg, m0) < 1e-6 and rel(vg, v0) < 1e-6
-    # the whole step against the oracle's own step
-    flips = 0
+    # the whole step against the oracle's own step.  Step-1 Adam moves an
+    # element by ~lr whatever the size of its gradient, so an element whose
+    # own gradient is not determined to 1e-3 (rounding noise: e.g. the key
+    # bias, whose exact gradient is 0 because softmax ignores a constant
+    # shift of a row) has no determined update; such elements are counted
+    # and excluded, and must stay a small fraction of the arena.
+    excluded = 0
     PG, PO = split(pg, P.sizes), split(P.orc.params.copy(), P.sizes)
     for n in oracle.PARAM_NAMES:
         scale = max(np.max(np.abs(PO[n])), 1e-30)
         bad = np.abs(PG[n].astype(np.float64) - PO[n]) > 1e-4 * scale
-        noise = np.abs(G[n].astype(np.float64) - R[n]) >= np.abs(R[n])
-        flips += int(np.sum(bad & noise))
-        assert not np.any(bad & ~noise), (n, int(np.sum(bad & ~noise)))
-    print(f"[parity] params: {flips} noise-level gradient sign flips excluded", flush=True)
+        r = np.abs(R[n].astype(np.float64))
+        # d(update)/d(g) of step-1 Adam is lr*eps/(|g|+eps)^2: a gradient error
+        # at the 1e-3 tolerance moves the update by more than the parameter
+        # tolerance when the gradient sits within a few eps of zero
+        sensitive = lr * 1e-8 * 1e-3 * r / (r + 1e-8) ** 2 > 1e-4 * scale
+        ill = (np.abs(G[n].astype(np.float64) - R[n]) > 1e-3 * r) | sensitive
+        excluded += int(np.sum(bad & ill))
+        idx = np.flatnonzero(bad & ~ill)[:5]
+        assert idx.size == 0, (n, [(int(i), float(G[n][i]), float(R[n][i]),
+                                    float(PG[n][i]), float(PO[n][i])) for i in idx])
+    print(f"[parity] params: {excluded} elements with undetermined gradients excluded",
+          flush=True)
+    assert excluded <= 0.005 * pg.size
     return loss_g
 
 

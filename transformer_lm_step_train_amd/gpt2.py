@@ -11,6 +11,10 @@ import ctypes
 import os
 
 import numpy as np
+# torch ships its own HIP runtime under the same soname (libamdhip64.so.7).
+# Loading torch first makes the library bind to that one runtime instead of
+# pulling a second copy from /opt/rocm into the process.
+import torch  # noqa: F401
 
 HERE = os.path.dirname(os.path.abspath(__file__))
 LIB_PATH = os.path.join(HERE, "libgpt2_hip.so")
