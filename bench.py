@@ -1,0 +1,166 @@
+"""Training throughput of one GPT-2 124M step (forward, backward, AdamW) on
+one MI355X, B=16 sequences of T=1024 tokens, fp32.
+
+Usage: python bench.py [--gpus 1] [--steps K] [--warmup W]
+
+Prints one JSON line.  The timed region covers exactly K training steps,
+each = forward with the loss read back to the host + zero-grad + backward +
+AdamW update, with token ids already resident in device memory; it is
+bracketed by device synchronizations.  Per-kernel-class times come from HIP
+events the library records around its own launches on its stream during the
+timed steps.  The CPU-oracle baseline is timed afterwards on a bounded sample
+(one sequence of the same batch shape) on the host cores.
+"""
+import argparse
+import json
+import os
+import sys
+import time
+
+import numpy as np
+
+ROOT = os.path.dirname(os.path.abspath(__file__))
+sys.path.insert(0, ROOT)
+
+WORKLOAD = "gpt2_124m_b16t1024"
+MFMA_FP32_PEAK_TFLOPS = 157.3
+HBM_PEAK_GBS = 8000.0
+
+
+def parse():
+    ap = argparse.ArgumentParser()
+    ap.add_argument("--gpus", type=int, default=1)
+    ap.add_argument("--steps", type=int, default=20)
+    ap.add_argument("--warmup", type=int, default=3)
+    ap.add_argument("--no-cpu-baseline", action="store_true")
+    ap.add_argument("--no-kernel-timing", action="store_true",
+                    help="do not record per-launch HIP events in the timed steps")
+    return ap.parse_args()
+
+
+def cpu_baseline(c, params, tok, tgt):
+    """The oracle (plain C, OpenMP) on one sequence of the batch: one full
+    training step at B=1, T=1024, i.e. 1/16 of the GPU step's tokens."""
+    from oracle import OracleModel
+    cores = int(os.environ.get("OMP_NUM_THREADS") or len(os.sched_getaffinity(0)))
+    o = OracleModel(c["L"], c["C"], c["NH"], c["V"], c["maxT"], 1, c["T"])
+    o.params[:] = params
+    t0 = time.perf_counter()
+    o.forward(tok[:1], tgt[:1])
+    o.zero_grad()
+    o.backward()
+    o.update(step=1, lr=1e-4)
+    dt = time.perf_counter() - t0
+    o.close()
+    return {"value": round(c["T"] / dt, 2), "unit": "tokens/s", "cores": cores,
+            "kind": "oracle",
+            "sample": f"1 training step (fwd+bwd+AdamW) on 1 sequence of T={c['T']} "
+                      f"(1/{c['B']} of the batch), {dt:.2f} s"}
+
+
+def main():
+    args = parse()
+    if args.gpus != 1:
+        print(f"bench.py: --gpus {args.gpus} is not supported: this build runs on one GPU "
+              f"only (no collectives); run with --gpus 1", file=sys.stderr)
+        sys.exit(2)
+    import torch
+    from transformer_lm_step_train_amd import gpt2, synth
+
+    assert torch.cuda.is_available(), "bench.py needs a GPU"
+    torch.cuda.set_device(0)
+    c = synth.CONFIGS[WORKLOAD]
+    B, T = c["B"], c["T"]
+    params = synth.init_params(c["L"], c["C"], c["V"], c["maxT"])
+    tok, tgt = synth.token_stream(B, T, c["V"])
+    m = gpt2.Model(c["L"], c["C"], c["NH"], c["V"], c["maxT"], B, T)
+    m.set_params(params)
+    dtok = torch.tensor(tok, dtype=torch.int32, device="cuda")
+    dtgt = torch.tensor(tgt, dtype=torch.int32, device="cuda")
+    adamw = dict(synth.ADAMW)
+
+    step = 0
+    losses = []
+
+    def train_step():
+        nonlocal step
+        step += 1
+        losses.append(m.forward_device(dtok, dtgt))
+        m.zero_grad()
+        m.backward()
+        m.update(step=step, **adamw)
+
+    for _ in range(args.warmup):
+        train_step()
+    m.synchronize()
+    if not args.no_kernel_timing:
+        gpt2.gpt2_profile(m.h, True)
+    torch.cuda.synchronize()
+    t0 = time.perf_counter()
+    for _ in range(args.steps):
+        train_step()
+    m.synchronize()
+    torch.cuda.synchronize()
+    dt = time.perf_counter() - t0
+    ms = 1000.0 * dt / args.steps
+    tokens_per_s = B * T * args.steps / dt
+
+    kc = {}
+    if not args.no_kernel_timing:
+        for i, name in enumerate(gpt2.KC_NAMES):
+            kc[name] = gpt2.gpt2_profile_read(m.h, i)
+        gpt2.gpt2_profile(m.h, False)
+    assert all(np.isfinite(losses)), losses
+    m.close()
+
+    roofline = None
+    if kc:
+        g = kc["gemm"]
+        n = max(g["launches"], 1)
+        avg_s = g["ms"] / n / 1000.0
+        achieved = (g["flops"] / n) / avg_s / 1e12 if avg_s > 0 else 0.0
+        roofline = {"bound": "mfma", "achieved": round(achieved, 2),
+                    "peak": MFMA_FP32_PEAK_TFLOPS, "unit": "TFLOP/s",
+                    "frac": round(achieved / MFMA_FP32_PEAK_TFLOPS, 4), "traffic": None,
+                    "kernel": "gemm (all fp32 MFMA matmul launches of the step)",
+                    "launches_per_step": n // args.steps,
+                    "avg_launch_ms": round(g["ms"] / n, 4)}
+        print("per-class kernel time per step:", file=sys.stderr)
+        total = 0.0
+        for name, r in kc.items():
+            per = r["ms"] / args.steps
+            total += per
+            gbs = r["bytes"] / (r["ms"] / 1e3) / 1e9 if r["ms"] > 0 else 0.0
+            tf = r["flops"] / (r["ms"] / 1e3) / 1e12 if r["ms"] > 0 else 0.0
+            print(f"  {name:11s} {per:9.3f} ms  launches/step {r['launches'] // args.steps:4d}"
+                  f"  {tf:7.2f} TFLOP/s  {gbs:8.1f} GB/s", file=sys.stderr)
+        print(f"  {'sum':11s} {total:9.3f} ms of {ms:.3f} ms per step", file=sys.stderr)
+
+    out = {
+        "metric": "training tokens/sec (fwd+bwd+AdamW), GPT-2 124M B16 T1024 at 1 GPU",
+        "value": round(tokens_per_s, 1),
+        "unit": "tokens/s",
+        "n_gpus": 1,
+        "steps": args.steps,
+        "warmup": args.warmup,
+        "ms_per_step": round(ms, 3),
+        "higher_is_better": True,
+        "scaling": "weak",
+        "vs_baseline": None,
+        "dtype": "f32",
+        "data": "synthetic (seeded uniform int32 token ids, GPT-2 init N(0,0.02))",
+        "config": {"workload": "GPT-2 124M training step, B=16 T=1024 fp32",
+                   "global_batch": B, "seq_len": T, "layers": c["L"], "channels": c["C"],
+                   "heads": c["NH"], "vocab": c["V"], "parallelism": "single GPU"},
+        "roofline": roofline,
+        "cpu_baseline": None,
+        "kernel_ms_per_step": {k: round(v["ms"] / args.steps, 3) for k, v in kc.items()},
+        "loss_first_last": [round(losses[0], 5), round(losses[-1], 5)],
+    }
+    if not args.no_cpu_baseline:
+        out["cpu_baseline"] = cpu_baseline(c, params, tok, tgt)
+    print(json.dumps(out), flush=True)
+
+
+if __name__ == "__main__":
+    main()
