@@ -15,53 +15,94 @@
 // 32 keys in registers.  The row statistics are then per-lane scalars, and
 // the same registers are directly the B operand of O^T = V^T P^T.  The
 // key/value kernel of the backward uses the mirror image (lane owns a key).
+// Scores are kept in base 2 (log2(e) is folded into the query scale), so the
+// exponentials are single v_exp_f32 instructions.
 //
 // Backward: D_t = dout_t . out_t;  P = exp(s - lse);  dS = P (dP - D) with
 // dP = dout V^T;  dQ = dS K / sqrt(hs);  dK = dS^T Q / sqrt(hs);  dV = P^T dout.
-// dQ and (dK, dV) come from two kernels that each own their output rows, so
-// no output is accumulated with atomics and results are deterministic.
+// dQ (with D) and (dK, dV) come from two kernels that each own their output
+// rows, so no output is accumulated with atomics and results are
+// deterministic.
+//
+// Each workgroup is four waves owning 128 consecutive rows; the other operand
+// streams through LDS in 64-row tiles, double-buffered with a register
+// prefetch of the next tile (one barrier per tile).  32-row blocks that the
+// causal mask empties completely are skipped.
 #include "common.h"
 #include "kernels.h"
 
 namespace gk {
 namespace {
 
-constexpr int QB = 64;  // rows owned per workgroup (two waves of 32)
-constexpr int KT = 64;  // rows per staged tile
+constexpr int AQ = 128;  // rows owned per workgroup (four waves of 32)
+constexpr int AT = 64;   // rows per staged tile
+constexpr float LOG2E = 1.4426950408889634f;
+constexpr float LN2 = 0.6931471805599453f;
 
 __device__ __forceinline__ floatx16 mfma(float a, float b, floatx16 c) {
     return __builtin_amdgcn_mfma_f32_32x32x2f32(a, b, c, 0, 0, 0);
 }
+
+__device__ __forceinline__ float exp2_fast(float x) { return __builtin_amdgcn_exp2f(x); }
 
 __device__ __forceinline__ void zero16(floatx16& x) {
 #pragma unroll
     for (int e = 0; e < 16; e++) x[e] = 0.f;
 }
 
-// Copy rows r0..r0+63 (row r at base + r*ld, HS floats each) into LDS with
-// row stride HS+4; rows at or past T are zero.
+// One 64-row tile of one head (HS floats per row), held in registers between
+// its global load and its LDS store.  Rows at or past T are zero.
 template <int HS>
-__device__ __forceinline__ void stage_rows(float* sm, const float* __restrict__ base,
-                                           int64_t ld, int r0, int T) {
-    constexpr int C4 = HS / 4;
-    for (int i = threadIdx.x; i < KT * C4; i += blockDim.x) {
-        const int r = i / C4, c = (i - r * C4) * 4;
-        float4 x = make_float4(0.f, 0.f, 0.f, 0.f);
-        if (r0 + r < T) x = ld4(base + (int64_t)(r0 + r) * ld + c);
-        st4(sm + r * (HS + 4) + c, x);
+struct TileRegs {
+    static constexpr int C4 = HS / 4;
+    static constexpr int PER = AT * C4 / 256;  // float4 per thread
+    float4 v[PER];
+    __device__ __forceinline__ void load(const float* __restrict__ base, int64_t ld, int r0,
+                                         int T) {
+#pragma unroll
+        for (int i = 0; i < PER; i++) {
+            const int idx = threadIdx.x + 256 * i;
+            const int r = idx / C4, c = (idx - r * C4) * 4;
+            v[i] = r0 + r < T ? ld4(base + (int64_t)(r0 + r) * ld + c)
+                              : make_float4(0.f, 0.f, 0.f, 0.f);
+        }
     }
+    __device__ __forceinline__ void store(float* sm) const {
+#pragma unroll
+        for (int i = 0; i < PER; i++) {
+            const int idx = threadIdx.x + 256 * i;
+            const int r = idx / C4, c = (idx - r * C4) * 4;
+            st4(sm + r * (HS + 4) + c, v[i]);
+        }
+    }
+};
+
+// Write a lane's 32-row accumulator block(s) of one row: the lane holds
+// columns d*32 + 8*(e/4) + 4*g + e%4 of its row, i.e. float4 runs.
+template <int HS, int NDB>
+__device__ __forceinline__ void store_row(float* row, const floatx16 (&acc)[NDB], int g,
+                                          float mul) {
+#pragma unroll
+    for (int d = 0; d < NDB; d++)
+#pragma unroll
+        for (int c = 0; c < 4; c++) {
+            const int dim0 = d * 32 + 8 * c + 4 * g;
+            if (dim0 < HS)
+                st4(row + dim0, make_float4(acc[d][4 * c] * mul, acc[d][4 * c + 1] * mul,
+                                            acc[d][4 * c + 2] * mul, acc[d][4 * c + 3] * mul));
+        }
 }
 
 template <int HS>
-__global__ __launch_bounds__(128) void attn_fwd_kernel(float* __restrict__ out,
-                                                       float* __restrict__ lse,
-                                                       const float* __restrict__ qkv,
-                                                       int T, int C, int NH, float scale) {
+__global__ __launch_bounds__(256, 2) void attn_fwd_kernel(float* __restrict__ out,
+                                                          float* __restrict__ lse,
+                                                          const float* __restrict__ qkv, int T,
+                                                          int C, int NH, float qscale) {
     constexpr int LD = HS + 4, HALF = HS / 2, NDB = (HS + 31) / 32;
-    __shared__ __attribute__((aligned(16))) float ks[KT * LD];
-    __shared__ __attribute__((aligned(16))) float vs[KT * LD];
+    __shared__ __attribute__((aligned(16))) float ks[2][AT * LD];
+    __shared__ __attribute__((aligned(16))) float vs[2][AT * LD];
 
-    const int nqb = (T + QB - 1) / QB;
+    const int nqb = (T + AQ - 1) / AQ;
     const int id = xcd_remap(blockIdx.x, gridDim.x);
     const int bh = id / nqb;
     const int qb = nqb - 1 - (id - bh * nqb);  // longest rows first
@@ -70,130 +111,128 @@ __global__ __launch_bounds__(128) void attn_fwd_kernel(float* __restrict__ out,
     const int li = lane & 31, g = lane >> 5;
     const int64_t ld = 3 * (int64_t)C;
     const float* qbase = qkv + (int64_t)b * T * ld + h * HS;
-    const int q = qb * QB + wave * 32 + li;
+    const int q0 = qb * AQ;
+    const int qw = q0 + wave * 32;
+    const int q = qw + li;
+    const int qmax = qw < T ? min(qw + 31, T - 1) : -1;  // last query of this wave
+    const int nkt = (min(q0 + AQ, T) - 1) / AT + 1;
 
     float qr[HALF];
 #pragma unroll
     for (int s = 0; s < HALF; s += 4) {
         float4 x = make_float4(0.f, 0.f, 0.f, 0.f);
         if (q < T) x = ld4(qbase + (int64_t)q * ld + g * HALF + s);
-        qr[s] = x.x * scale;
-        qr[s + 1] = x.y * scale;
-        qr[s + 2] = x.z * scale;
-        qr[s + 3] = x.w * scale;
+        qr[s] = x.x * qscale;
+        qr[s + 1] = x.y * qscale;
+        qr[s + 2] = x.z * qscale;
+        qr[s + 3] = x.w * qscale;
     }
     floatx16 o[NDB];
 #pragma unroll
     for (int d = 0; d < NDB; d++) zero16(o[d]);
     float m = -INFINITY, l = 0.f;
 
-    for (int kt = 0; kt <= qb; kt++) {
-        __syncthreads();
-        stage_rows<HS>(ks, qbase + C, ld, kt * KT, T);
-        stage_rows<HS>(vs, qbase + 2 * C, ld, kt * KT, T);
-        __syncthreads();
-        floatx16 sc[2];
-#pragma unroll
-        for (int kb = 0; kb < 2; kb++) {
-            zero16(sc[kb]);
-            const float* kr = ks + (kb * 32 + li) * LD + g * HALF;
-#pragma unroll
-            for (int s = 0; s < HALF; s += 4) {
-                const float4 kf = ld4(kr + s);
-                sc[kb] = mfma(kf.x, qr[s], sc[kb]);
-                sc[kb] = mfma(kf.y, qr[s + 1], sc[kb]);
-                sc[kb] = mfma(kf.z, qr[s + 2], sc[kb]);
-                sc[kb] = mfma(kf.w, qr[s + 3], sc[kb]);
-            }
+    TileRegs<HS> kreg, vreg;
+    kreg.load(qbase + C, ld, 0, T);
+    vreg.load(qbase + 2 * C, ld, 0, T);
+    kreg.store(ks[0]);
+    vreg.store(vs[0]);
+    __syncthreads();
+    for (int kt = 0; kt < nkt; kt++) {
+        const int cur = kt & 1;
+        if (kt + 1 < nkt) {
+            kreg.load(qbase + C, ld, (kt + 1) * AT, T);
+            vreg.load(qbase + 2 * C, ld, (kt + 1) * AT, T);
         }
-        float mt = -INFINITY;
+        const int k0 = kt * AT;
+        if (k0 <= qmax) {
+            const bool kb1 = k0 + 32 <= qmax;
+            const float* ksm = ks[cur];
+            const float* vsm = vs[cur];
+            floatx16 sc[2];
+            zero16(sc[0]);
+            zero16(sc[1]);
 #pragma unroll
-        for (int kb = 0; kb < 2; kb++)
+            for (int kb = 0; kb < 2; kb++) {
+                if (kb == 1 && !kb1) break;
+                const float* kr = ksm + (kb * 32 + li) * LD + g * HALF;
 #pragma unroll
-            for (int e = 0; e < 16; e++) {
-                const int key = kt * KT + kb * 32 + 8 * (e >> 2) + 4 * g + (e & 3);
-                if (key > q || key >= T) sc[kb][e] = -INFINITY;
-                mt = fmaxf(mt, sc[kb][e]);
-            }
-        mt = fmaxf(mt, __shfl_xor(mt, 32, WAVE));
-        const float mn = fmaxf(m, mt);
-        const float corr = expf(m - mn);
-        float ls = 0.f;
-#pragma unroll
-        for (int kb = 0; kb < 2; kb++)
-#pragma unroll
-            for (int e = 0; e < 16; e++) {
-                const float p = expf(sc[kb][e] - mn);
-                sc[kb][e] = p;
-                ls += p;
-            }
-        ls += __shfl_xor(ls, 32, WAVE);
-        l = l * corr + ls;
-        m = mn;
-#pragma unroll
-        for (int d = 0; d < NDB; d++)
-#pragma unroll
-            for (int e = 0; e < 16; e++) o[d][e] *= corr;
-#pragma unroll
-        for (int kb = 0; kb < 2; kb++)
-#pragma unroll
-            for (int e = 0; e < 16; e++) {
-                const int kl = kb * 32 + 8 * (e >> 2) + 4 * g + (e & 3);
-#pragma unroll
-                for (int d = 0; d < NDB; d++) {
-                    const int dim = d * 32 + li;
-                    const float va = dim < HS ? vs[kl * LD + dim] : 0.f;
-                    o[d] = mfma(va, sc[kb][e], o[d]);
+                for (int s = 0; s < HALF; s += 4) {
+                    const float4 kf = ld4(kr + s);
+                    sc[kb] = mfma(kf.x, qr[s], sc[kb]);
+                    sc[kb] = mfma(kf.y, qr[s + 1], sc[kb]);
+                    sc[kb] = mfma(kf.z, qr[s + 2], sc[kb]);
+                    sc[kb] = mfma(kf.w, qr[s + 3], sc[kb]);
                 }
             }
+            const bool need_mask = (k0 + AT - 1 > qw) || (k0 + AT > T);
+            float mt = -INFINITY;
+#pragma unroll
+            for (int kb = 0; kb < 2; kb++)
+#pragma unroll
+                for (int e = 0; e < 16; e++) {
+                    const int key = k0 + kb * 32 + 8 * (e >> 2) + 4 * g + (e & 3);
+                    if ((kb == 1 && !kb1) || (need_mask && (key > q || key >= T)))
+                        sc[kb][e] = -INFINITY;
+                    mt = fmaxf(mt, sc[kb][e]);
+                }
+            mt = fmaxf(mt, __shfl_xor(mt, 32, WAVE));
+            const float mn = fmaxf(m, mt);
+            const float corr = exp2_fast(m - mn);
+            float ls = 0.f;
+#pragma unroll
+            for (int kb = 0; kb < 2; kb++)
+#pragma unroll
+                for (int e = 0; e < 16; e++) {
+                    const float p = exp2_fast(sc[kb][e] - mn);
+                    sc[kb][e] = p;
+                    ls += p;
+                }
+            ls += __shfl_xor(ls, 32, WAVE);
+            l = l * corr + ls;
+            m = mn;
+#pragma unroll
+            for (int d = 0; d < NDB; d++)
+#pragma unroll
+                for (int e = 0; e < 16; e++) o[d][e] *= corr;
+#pragma unroll
+            for (int kb = 0; kb < 2; kb++) {
+                if (kb == 1 && !kb1) break;
+#pragma unroll
+                for (int e = 0; e < 16; e++) {
+                    const int kl = kb * 32 + 8 * (e >> 2) + 4 * g + (e & 3);
+#pragma unroll
+                    for (int d = 0; d < NDB; d++) {
+                        const int dim = d * 32 + li;
+                        const float va = dim < HS ? vsm[kl * LD + dim] : 0.f;
+                        o[d] = mfma(va, sc[kb][e], o[d]);
+                    }
+                }
+            }
+        }
+        if (kt + 1 < nkt) {
+            kreg.store(ks[cur ^ 1]);
+            vreg.store(vs[cur ^ 1]);
+        }
+        __syncthreads();
     }
     if (q < T) {
-        const float inv = 1.f / l;
-        float* orow = out + ((int64_t)b * T + q) * C + h * HS;
-#pragma unroll
-        for (int d = 0; d < NDB; d++)
-#pragma unroll
-            for (int c = 0; c < 4; c++) {
-                const int dim0 = d * 32 + 8 * c + 4 * g;
-                if (dim0 < HS)
-                    st4(orow + dim0, make_float4(o[d][4 * c] * inv, o[d][4 * c + 1] * inv,
-                                                 o[d][4 * c + 2] * inv, o[d][4 * c + 3] * inv));
-            }
-        if (g == 0) lse[((int64_t)b * NH + h) * T + q] = m + logf(l);
+        store_row<HS, NDB>(out + ((int64_t)b * T + q) * C + h * HS, o, g, 1.f / l);
+        if (g == 0) lse[((int64_t)b * NH + h) * T + q] = (m + log2f(l)) * LN2;
     }
 }
 
-// D[b,h,t] = dout[b,t,h-slice] . out[b,t,h-slice]
-__global__ __launch_bounds__(256) void attn_rowdot_kernel(float* __restrict__ D,
-                                                          const float* __restrict__ dout,
-                                                          const float* __restrict__ out,
-                                                          int B, int T, int C, int NH,
-                                                          int HS) {
-    const int64_t i = blockIdx.x * (int64_t)blockDim.x + threadIdx.x;
-    if (i >= (int64_t)B * T * NH) return;
-    const int h = (int)(i % NH);
-    const int64_t bt = i / NH;
-    const int b = (int)(bt / T), t = (int)(bt - (int64_t)b * T);
-    const float* x = dout + bt * C + h * HS;
-    const float* y = out + bt * C + h * HS;
-    float s = 0.f;
-    for (int d = 0; d < HS; d += 4) {
-        const float4 a = ld4(x + d), c = ld4(y + d);
-        s += a.x * c.x + a.y * c.y + a.z * c.z + a.w * c.w;
-    }
-    D[((int64_t)b * NH + h) * T + t] = s;
-}
-
+// dQ, and D = rowsum(dout * out) for the key/value kernel.
 template <int HS>
-__global__ __launch_bounds__(128) void attn_bwd_dq_kernel(
-    float* __restrict__ dqkv, const float* __restrict__ dout, const float* __restrict__ qkv,
-    const float* __restrict__ lse, const float* __restrict__ D, int T, int C, int NH,
-    float scale) {
+__global__ __launch_bounds__(256, 2) void attn_bwd_dq_kernel(
+    float* __restrict__ dqkv, float* __restrict__ Dout, const float* __restrict__ dout,
+    const float* __restrict__ out, const float* __restrict__ qkv, const float* __restrict__ lse,
+    int T, int C, int NH, float qscale, float scale) {
     constexpr int LD = HS + 4, HALF = HS / 2, NDB = (HS + 31) / 32;
-    __shared__ __attribute__((aligned(16))) float ks[KT * LD];
-    __shared__ __attribute__((aligned(16))) float vs[KT * LD];
+    __shared__ __attribute__((aligned(16))) float ks[2][AT * LD];
+    __shared__ __attribute__((aligned(16))) float vs[2][AT * LD];
 
-    const int nqb = (T + QB - 1) / QB;
+    const int nqb = (T + AQ - 1) / AQ;
     const int id = xcd_remap(blockIdx.x, gridDim.x);
     const int bh = id / nqb;
     const int qb = nqb - 1 - (id - bh * nqb);
@@ -203,108 +242,127 @@ __global__ __launch_bounds__(128) void attn_bwd_dq_kernel(
     const int64_t ld = 3 * (int64_t)C;
     const float* qbase = qkv + (int64_t)b * T * ld + h * HS;
     const float* dobase = dout + (int64_t)b * T * C + h * HS;
-    const int q = qb * QB + wave * 32 + li;
+    const float* obase = out + (int64_t)b * T * C + h * HS;
+    const int q0 = qb * AQ;
+    const int qw = q0 + wave * 32;
+    const int q = qw + li;
+    const int qmax = qw < T ? min(qw + 31, T - 1) : -1;
+    const int nkt = (min(q0 + AQ, T) - 1) / AT + 1;
 
     float qr[HALF], dr[HALF];
+    float dsum = 0.f;
 #pragma unroll
     for (int s = 0; s < HALF; s += 4) {
-        float4 x = make_float4(0.f, 0.f, 0.f, 0.f), y = x;
+        float4 x = make_float4(0.f, 0.f, 0.f, 0.f), y = x, z = x;
         if (q < T) {
             x = ld4(qbase + (int64_t)q * ld + g * HALF + s);
             y = ld4(dobase + (int64_t)q * C + g * HALF + s);
+            z = ld4(obase + (int64_t)q * C + g * HALF + s);
         }
-        qr[s] = x.x * scale;
-        qr[s + 1] = x.y * scale;
-        qr[s + 2] = x.z * scale;
-        qr[s + 3] = x.w * scale;
+        qr[s] = x.x * qscale;
+        qr[s + 1] = x.y * qscale;
+        qr[s + 2] = x.z * qscale;
+        qr[s + 3] = x.w * qscale;
         dr[s] = y.x;
         dr[s + 1] = y.y;
         dr[s + 2] = y.z;
         dr[s + 3] = y.w;
+        dsum += (y.x * z.x + y.y * z.y) + (y.z * z.z + y.w * z.w);
     }
+    const float Dq = dsum + __shfl_xor(dsum, 32, WAVE);
     const int64_t srow = ((int64_t)b * NH + h) * T;
-    const float lq = q < T ? lse[srow + q] : 0.f;
-    const float Dq = q < T ? D[srow + q] : 0.f;
+    if (q < T && g == 0) Dout[srow + q] = Dq;
+    const float lq = q < T ? lse[srow + q] * LOG2E : 0.f;
     floatx16 dq[NDB];
 #pragma unroll
     for (int d = 0; d < NDB; d++) zero16(dq[d]);
 
-    for (int kt = 0; kt <= qb; kt++) {
-        __syncthreads();
-        stage_rows<HS>(ks, qbase + C, ld, kt * KT, T);
-        stage_rows<HS>(vs, qbase + 2 * C, ld, kt * KT, T);
-        __syncthreads();
-        floatx16 sc[2], dp[2];
-#pragma unroll
-        for (int kb = 0; kb < 2; kb++) {
-            zero16(sc[kb]);
-            zero16(dp[kb]);
-            const float* kr = ks + (kb * 32 + li) * LD + g * HALF;
-            const float* vr = vs + (kb * 32 + li) * LD + g * HALF;
-#pragma unroll
-            for (int s = 0; s < HALF; s += 4) {
-                const float4 kf = ld4(kr + s);
-                const float4 vf = ld4(vr + s);
-                sc[kb] = mfma(kf.x, qr[s], sc[kb]);
-                sc[kb] = mfma(kf.y, qr[s + 1], sc[kb]);
-                sc[kb] = mfma(kf.z, qr[s + 2], sc[kb]);
-                sc[kb] = mfma(kf.w, qr[s + 3], sc[kb]);
-                dp[kb] = mfma(vf.x, dr[s], dp[kb]);
-                dp[kb] = mfma(vf.y, dr[s + 1], dp[kb]);
-                dp[kb] = mfma(vf.z, dr[s + 2], dp[kb]);
-                dp[kb] = mfma(vf.w, dr[s + 3], dp[kb]);
-            }
+    TileRegs<HS> kreg, vreg;
+    kreg.load(qbase + C, ld, 0, T);
+    vreg.load(qbase + 2 * C, ld, 0, T);
+    kreg.store(ks[0]);
+    vreg.store(vs[0]);
+    __syncthreads();
+    for (int kt = 0; kt < nkt; kt++) {
+        const int cur = kt & 1;
+        if (kt + 1 < nkt) {
+            kreg.load(qbase + C, ld, (kt + 1) * AT, T);
+            vreg.load(qbase + 2 * C, ld, (kt + 1) * AT, T);
         }
+        const int k0 = kt * AT;
+        if (k0 <= qmax) {
+            const bool kb1 = k0 + 32 <= qmax;
+            const float* ksm = ks[cur];
+            const float* vsm = vs[cur];
+            floatx16 sc[2], dp[2];
 #pragma unroll
-        for (int kb = 0; kb < 2; kb++)
+            for (int kb = 0; kb < 2; kb++) {
+                zero16(sc[kb]);
+                zero16(dp[kb]);
+                if (kb == 1 && !kb1) break;
+                const float* kr = ksm + (kb * 32 + li) * LD + g * HALF;
+                const float* vr = vsm + (kb * 32 + li) * LD + g * HALF;
 #pragma unroll
-            for (int e = 0; e < 16; e++) {
-                const int key = kt * KT + kb * 32 + 8 * (e >> 2) + 4 * g + (e & 3);
-                const float p = (key <= q && key < T) ? expf(sc[kb][e] - lq) : 0.f;
-                sc[kb][e] = p * (dp[kb][e] - Dq);
-            }
-#pragma unroll
-        for (int kb = 0; kb < 2; kb++)
-#pragma unroll
-            for (int e = 0; e < 16; e++) {
-                const int kl = kb * 32 + 8 * (e >> 2) + 4 * g + (e & 3);
-#pragma unroll
-                for (int d = 0; d < NDB; d++) {
-                    const int dim = d * 32 + li;
-                    const float ka = dim < HS ? ks[kl * LD + dim] : 0.f;
-                    dq[d] = mfma(ka, sc[kb][e], dq[d]);
+                for (int s = 0; s < HALF; s += 4) {
+                    const float4 kf = ld4(kr + s);
+                    const float4 vf = ld4(vr + s);
+                    sc[kb] = mfma(kf.x, qr[s], sc[kb]);
+                    sc[kb] = mfma(kf.y, qr[s + 1], sc[kb]);
+                    sc[kb] = mfma(kf.z, qr[s + 2], sc[kb]);
+                    sc[kb] = mfma(kf.w, qr[s + 3], sc[kb]);
+                    dp[kb] = mfma(vf.x, dr[s], dp[kb]);
+                    dp[kb] = mfma(vf.y, dr[s + 1], dp[kb]);
+                    dp[kb] = mfma(vf.z, dr[s + 2], dp[kb]);
+                    dp[kb] = mfma(vf.w, dr[s + 3], dp[kb]);
                 }
             }
-    }
-    if (q < T) {
-        float* row = dqkv + ((int64_t)b * T + q) * ld + h * HS;
 #pragma unroll
-        for (int d = 0; d < NDB; d++)
+            for (int kb = 0; kb < 2; kb++)
 #pragma unroll
-            for (int c = 0; c < 4; c++) {
-                const int dim0 = d * 32 + 8 * c + 4 * g;
-                if (dim0 < HS)
-                    st4(row + dim0,
-                        make_float4(dq[d][4 * c] * scale, dq[d][4 * c + 1] * scale,
-                                    dq[d][4 * c + 2] * scale, dq[d][4 * c + 3] * scale));
+                for (int e = 0; e < 16; e++) {
+                    const int key = k0 + kb * 32 + 8 * (e >> 2) + 4 * g + (e & 3);
+                    const bool live = (kb == 0 || kb1) && key <= q && key < T;
+                    const float p = live ? exp2_fast(sc[kb][e] - lq) : 0.f;
+                    sc[kb][e] = p * (dp[kb][e] - Dq);
+                }
+#pragma unroll
+            for (int kb = 0; kb < 2; kb++) {
+                if (kb == 1 && !kb1) break;
+#pragma unroll
+                for (int e = 0; e < 16; e++) {
+                    const int kl = kb * 32 + 8 * (e >> 2) + 4 * g + (e & 3);
+#pragma unroll
+                    for (int d = 0; d < NDB; d++) {
+                        const int dim = d * 32 + li;
+                        const float ka = dim < HS ? ksm[kl * LD + dim] : 0.f;
+                        dq[d] = mfma(ka, sc[kb][e], dq[d]);
+                    }
+                }
             }
+        }
+        if (kt + 1 < nkt) {
+            kreg.store(ks[cur ^ 1]);
+            vreg.store(vs[cur ^ 1]);
+        }
+        __syncthreads();
     }
+    if (q < T) store_row<HS, NDB>(dqkv + ((int64_t)b * T + q) * ld + h * HS, dq, g, scale);
 }
 
 template <int HS>
-__global__ __launch_bounds__(128) void attn_bwd_dkdv_kernel(
+__global__ __launch_bounds__(256, 2) void attn_bwd_dkdv_kernel(
     float* __restrict__ dqkv, const float* __restrict__ dout, const float* __restrict__ qkv,
     const float* __restrict__ lse, const float* __restrict__ D, int T, int C, int NH,
-    float scale) {
+    float qscale, float scale) {
     constexpr int LD = HS + 4, HALF = HS / 2, NDB = (HS + 31) / 32;
-    __shared__ __attribute__((aligned(16))) float qs[KT * LD];
-    __shared__ __attribute__((aligned(16))) float dos[KT * LD];
-    __shared__ float lsm[KT], dsm[KT];
+    __shared__ __attribute__((aligned(16))) float qs[2][AT * LD];
+    __shared__ __attribute__((aligned(16))) float dos[2][AT * LD];
+    __shared__ float lsm[2][AT], dsm[2][AT];
 
-    const int nkb = (T + QB - 1) / QB;
+    const int nkb = (T + AQ - 1) / AQ;
     const int id = xcd_remap(blockIdx.x, gridDim.x);
     const int bh = id / nkb;
-    const int kb0 = id - bh * nkb;  // lowest key block = most query tiles: first
+    const int kb0 = id - bh * nkb;  // lowest keys = most query tiles: first
     const int b = bh / NH, h = bh - b * NH;
     const int lane = threadIdx.x & 63, wave = threadIdx.x >> 6;
     const int li = lane & 31, g = lane >> 5;
@@ -312,7 +370,8 @@ __global__ __launch_bounds__(128) void attn_bwd_dkdv_kernel(
     const float* qbase = qkv + (int64_t)b * T * ld + h * HS;
     const float* dobase = dout + (int64_t)b * T * C + h * HS;
     const int64_t srow = ((int64_t)b * NH + h) * T;
-    const int key = kb0 * QB + wave * 32 + li;
+    const int kw = kb0 * AQ + wave * 32;  // first key of this wave
+    const int key = kw + li;
 
     float kr[HALF], vr[HALF];
 #pragma unroll
@@ -337,32 +396,52 @@ __global__ __launch_bounds__(128) void attn_bwd_dkdv_kernel(
         zero16(dk[d]);
         zero16(dv[d]);
     }
-    const int nqt = (T + KT - 1) / KT;
-    for (int qt = kb0; qt < nqt; qt++) {
-        __syncthreads();
-        stage_rows<HS>(qs, qbase, ld, qt * KT, T);
-        stage_rows<HS>(dos, dobase, C, qt * KT, T);
-        for (int i = threadIdx.x; i < KT; i += blockDim.x) {
-            const int t = qt * KT + i;
-            lsm[i] = t < T ? lse[srow + t] : 0.f;
-            dsm[i] = t < T ? D[srow + t] : 0.f;
+    const int qt0 = (kb0 * AQ) / AT;
+    const int nqt = (T + AT - 1) / AT;
+    TileRegs<HS> qreg, dreg;
+    float sreg = 0.f;  // one lse (threads 0..63) or D (64..127) value per thread
+    auto load_stats = [&](int qt) {
+        const int i = threadIdx.x & 63, t = qt * AT + i;
+        if (threadIdx.x < 64) sreg = t < T ? lse[srow + t] * LOG2E : 0.f;
+        else if (threadIdx.x < 128) sreg = t < T ? D[srow + t] : 0.f;
+    };
+    auto store_stats = [&](int buf) {
+        if (threadIdx.x < 64) lsm[buf][threadIdx.x] = sreg;
+        else if (threadIdx.x < 128) dsm[buf][threadIdx.x - 64] = sreg;
+    };
+    qreg.load(qbase, ld, qt0 * AT, T);
+    dreg.load(dobase, C, qt0 * AT, T);
+    load_stats(qt0);
+    qreg.store(qs[0]);
+    dreg.store(dos[0]);
+    store_stats(0);
+    __syncthreads();
+    for (int qt = qt0; qt < nqt; qt++) {
+        const int cur = (qt - qt0) & 1;
+        if (qt + 1 < nqt) {
+            qreg.load(qbase, ld, (qt + 1) * AT, T);
+            dreg.load(dobase, C, (qt + 1) * AT, T);
+            load_stats(qt + 1);
         }
-        __syncthreads();
+        const float* qsm = qs[cur];
+        const float* dsmem = dos[cur];
 #pragma unroll
         for (int qh = 0; qh < 2; qh++) {
+            const int qlo = qt * AT + qh * 32;
+            if (kw >= T || qlo + 31 < kw || qlo >= T) continue;  // empty under the mask
             floatx16 sc, dp;
             zero16(sc);
             zero16(dp);
-            const float* qrow = qs + (qh * 32 + li) * LD + g * HALF;
-            const float* drow = dos + (qh * 32 + li) * LD + g * HALF;
+            const float* qrow = qsm + (qh * 32 + li) * LD + g * HALF;
+            const float* drow = dsmem + (qh * 32 + li) * LD + g * HALF;
 #pragma unroll
             for (int s = 0; s < HALF; s += 4) {
                 const float4 qf = ld4(qrow + s);
                 const float4 df = ld4(drow + s);
-                sc = mfma(qf.x * scale, kr[s], sc);
-                sc = mfma(qf.y * scale, kr[s + 1], sc);
-                sc = mfma(qf.z * scale, kr[s + 2], sc);
-                sc = mfma(qf.w * scale, kr[s + 3], sc);
+                sc = mfma(qf.x * qscale, kr[s], sc);
+                sc = mfma(qf.y * qscale, kr[s + 1], sc);
+                sc = mfma(qf.z * qscale, kr[s + 2], sc);
+                sc = mfma(qf.w * qscale, kr[s + 3], sc);
                 dp = mfma(df.x, vr[s], dp);
                 dp = mfma(df.y, vr[s + 1], dp);
                 dp = mfma(df.z, vr[s + 2], dp);
@@ -371,10 +450,10 @@ __global__ __launch_bounds__(128) void attn_bwd_dkdv_kernel(
 #pragma unroll
             for (int e = 0; e < 16; e++) {
                 const int ql = qh * 32 + 8 * (e >> 2) + 4 * g + (e & 3);
-                const int qa = qt * KT + ql;
-                const float p = (qa < T && key <= qa) ? expf(sc[e] - lsm[ql]) : 0.f;
+                const int qa = qt * AT + ql;
+                const float p = (qa < T && key <= qa) ? exp2_fast(sc[e] - lsm[cur][ql]) : 0.f;
                 sc[e] = p;
-                dp[e] = p * (dp[e] - dsm[ql]);
+                dp[e] = p * (dp[e] - dsm[cur][ql]);
             }
 #pragma unroll
             for (int e = 0; e < 16; e++) {
@@ -382,54 +461,47 @@ __global__ __launch_bounds__(128) void attn_bwd_dkdv_kernel(
 #pragma unroll
                 for (int d = 0; d < NDB; d++) {
                     const int dim = d * 32 + li;
-                    const float da = dim < HS ? dos[ql * LD + dim] : 0.f;
-                    const float qa = dim < HS ? qs[ql * LD + dim] : 0.f;
+                    const float da = dim < HS ? dsmem[ql * LD + dim] : 0.f;
+                    const float qa = dim < HS ? qsm[ql * LD + dim] : 0.f;
                     dv[d] = mfma(da, sc[e], dv[d]);
                     dk[d] = mfma(qa, dp[e], dk[d]);
                 }
             }
         }
+        if (qt + 1 < nqt) {
+            qreg.store(qs[cur ^ 1]);
+            dreg.store(dos[cur ^ 1]);
+            store_stats(cur ^ 1);
+        }
+        __syncthreads();
     }
     if (key < T) {
         float* row = dqkv + ((int64_t)b * T + key) * ld + h * HS;
-#pragma unroll
-        for (int d = 0; d < NDB; d++)
-#pragma unroll
-            for (int c = 0; c < 4; c++) {
-                const int dim0 = d * 32 + 8 * c + 4 * g;
-                if (dim0 < HS) {
-                    st4(row + C + dim0,
-                        make_float4(dk[d][4 * c] * scale, dk[d][4 * c + 1] * scale,
-                                    dk[d][4 * c + 2] * scale, dk[d][4 * c + 3] * scale));
-                    st4(row + 2 * C + dim0, make_float4(dv[d][4 * c], dv[d][4 * c + 1],
-                                                        dv[d][4 * c + 2], dv[d][4 * c + 3]));
-                }
-            }
+        store_row<HS, NDB>(row + C, dk, g, scale);
+        store_row<HS, NDB>(row + 2 * C, dv, g, 1.f);
     }
 }
 
 template <int HS>
 hipError_t fwd_hs(hipStream_t s, float* out, float* lse, const float* qkv, int B, int T,
                   int C, int NH) {
-    const int nqb = (T + QB - 1) / QB;
-    const float scale = 1.0f / sqrtf((float)HS);
-    hipLaunchKernelGGL((attn_fwd_kernel<HS>), dim3(B * NH * nqb), dim3(128), 0, s, out, lse,
-                       qkv, T, C, NH, scale);
+    const int nqb = (T + AQ - 1) / AQ;
+    const float qscale = LOG2E / sqrtf((float)HS);
+    hipLaunchKernelGGL((attn_fwd_kernel<HS>), dim3(B * NH * nqb), dim3(256), 0, s, out, lse,
+                       qkv, T, C, NH, qscale);
     return hipGetLastError();
 }
 
 template <int HS>
 hipError_t bwd_hs(hipStream_t s, float* dqkv, float* D, const float* dout, const float* qkv,
                   const float* out, const float* lse, int B, int T, int C, int NH) {
-    const int nb = (T + QB - 1) / QB;
+    const int nb = (T + AQ - 1) / AQ;
     const float scale = 1.0f / sqrtf((float)HS);
-    const int64_t rows = (int64_t)B * T * NH;
-    hipLaunchKernelGGL(attn_rowdot_kernel, dim3((unsigned)((rows + 255) / 256)), dim3(256), 0,
-                       s, D, dout, out, B, T, C, NH, HS);
-    hipLaunchKernelGGL((attn_bwd_dq_kernel<HS>), dim3(B * NH * nb), dim3(128), 0, s, dqkv,
-                       dout, qkv, lse, D, T, C, NH, scale);
-    hipLaunchKernelGGL((attn_bwd_dkdv_kernel<HS>), dim3(B * NH * nb), dim3(128), 0, s, dqkv,
-                       dout, qkv, lse, D, T, C, NH, scale);
+    const float qscale = LOG2E * scale;
+    hipLaunchKernelGGL((attn_bwd_dq_kernel<HS>), dim3(B * NH * nb), dim3(256), 0, s, dqkv, D,
+                       dout, out, qkv, lse, T, C, NH, qscale, scale);
+    hipLaunchKernelGGL((attn_bwd_dkdv_kernel<HS>), dim3(B * NH * nb), dim3(256), 0, s, dqkv,
+                       dout, qkv, lse, D, T, C, NH, qscale, scale);
     return hipGetLastError();
 }
 

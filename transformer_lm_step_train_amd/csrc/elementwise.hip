@@ -191,14 +191,39 @@ __global__ __launch_bounds__(256) void bias_partial_kernel(float* __restrict__ p
     }
 }
 
-__global__ __launch_bounds__(256) void bias_finish_kernel(float* __restrict__ db,
-                                                          const float* __restrict__ part,
-                                                          int nchunks, int N) {
-    const int c = blockIdx.x * blockDim.x + threadIdx.x;
-    if (c >= N) return;
-    float s = 0.f;
-    for (int k = 0; k < nchunks; k++) s += part[(int64_t)k * N + c];
-    db[c] += s;
+// out[c] += sum over rows r of part[r*ncols + c], for c < split into out0 and
+// c >= split into out1[c - split].  One workgroup per 64 columns; its 16
+// waves sum interleaved rows (wave w takes rows w, w+16, ...) and are then
+// added in wave order, so the result is the same on every run.
+__global__ __launch_bounds__(1024) void colsum_finish_kernel(float* __restrict__ out0,
+                                                             float* __restrict__ out1,
+                                                             int split,
+                                                             const float* __restrict__ part,
+                                                             int nrows, int ncols) {
+    __shared__ float sh[16][64];
+    const int lane = threadIdx.x & 63, wave = threadIdx.x >> 6;
+    const int c = blockIdx.x * 64 + lane;
+    float s0 = 0.f, s1 = 0.f, s2 = 0.f, s3 = 0.f;
+    if (c < ncols) {
+        int r = wave;
+        for (; r + 48 < nrows; r += 64) {
+            s0 += part[(int64_t)r * ncols + c];
+            s1 += part[(int64_t)(r + 16) * ncols + c];
+            s2 += part[(int64_t)(r + 32) * ncols + c];
+            s3 += part[(int64_t)(r + 48) * ncols + c];
+        }
+        for (; r < nrows; r += 16) s0 += part[(int64_t)r * ncols + c];
+    }
+    sh[wave][lane] = (s0 + s1) + (s2 + s3);
+    __syncthreads();
+    if (wave == 0 && c < ncols) {
+        float t = sh[0][lane];
+        for (int w = 1; w < 16; w++) t += sh[w][lane];
+        if (c < split)
+            out0[c] += t;
+        else
+            out1[c - split] += t;
+    }
 }
 
 __global__ __launch_bounds__(256) void fill_zero_kernel(float* __restrict__ p, int64_t n) {
@@ -305,8 +330,14 @@ hipError_t bias_grad(hipStream_t s, float* db, float* part, const float* dy, int
     hipLaunchKernelGGL(bias_partial_kernel, grid, dim3(256), 0, s, part, dy, M, N, ld);
     hipError_t e = hipGetLastError();
     if (e != hipSuccess) return e;
-    hipLaunchKernelGGL(bias_finish_kernel, dim3((N + 255) / 256), dim3(256), 0, s, db, part,
-                       nchunks, N);
+    return colsum_add(s, db, db, N, part, nchunks, N);
+}
+
+hipError_t colsum_add(hipStream_t s, float* out0, float* out1, int split, const float* part,
+                      int nrows, int ncols) {
+    if (nrows <= 0 || ncols <= 0) return hipSuccess;
+    hipLaunchKernelGGL(colsum_finish_kernel, dim3((ncols + 63) / 64), dim3(1024), 0, s, out0,
+                       out1, split, part, nrows, ncols);
     return hipGetLastError();
 }
 

@@ -99,6 +99,10 @@ hipError_t encoder_backward(hipStream_t s, float* dwte, float* dwpe,
 size_t bias_partials_floats(int M, int N);
 hipError_t bias_grad(hipStream_t s, float* db, float* partials,
                      const float* dy, int M, int N, int64_t ld);
+// out0[c] += sum_r part[r*ncols + c] for c < split, out1[c-split] likewise
+// for c >= split; rows summed in a fixed order.
+hipError_t colsum_add(hipStream_t s, float* out0, float* out1, int split, const float* part,
+                      int nrows, int ncols);
 hipError_t fill_zero(hipStream_t s, float* p, int64_t n);
 hipError_t adamw(hipStream_t s, float* p, const float* g, float* m, float* v,
                  int64_t n, float lr, float b1, float b2, float eps, float wd,

@@ -168,20 +168,6 @@ __global__ __launch_bounds__(256) void ln_bwd_kernel(
     }
 }
 
-__global__ __launch_bounds__(256) void ln_bwd_finish_kernel(float* __restrict__ dw,
-                                                            float* __restrict__ db,
-                                                            const float* __restrict__ partials,
-                                                            int nblocks, int C) {
-    const int c = blockIdx.x * blockDim.x + threadIdx.x;
-    if (c >= 2 * C) return;
-    float s = 0.f;
-    for (int k = 0; k < nblocks; k++) s += partials[(int64_t)k * 2 * C + c];
-    if (c < C)
-        dw[c] += s;
-    else
-        db[c - C] += s;
-}
-
 }  // namespace
 
 hipError_t layernorm_forward(hipStream_t s, float* out, float* mean, float* rstd,
@@ -225,9 +211,7 @@ hipError_t layernorm_backward(hipStream_t s, float* dres, int accumulate, float*
     }
     hipError_t e = hipGetLastError();
     if (e != hipSuccess) return e;
-    hipLaunchKernelGGL(ln_bwd_finish_kernel, dim3((2 * C + 255) / 256), dim3(256), 0, s, dw, db,
-                       partials, nb, C);
-    return hipGetLastError();
+    return colsum_add(s, dw, db, C, partials, nb, 2 * C);
 }
 
 }  // namespace gk
