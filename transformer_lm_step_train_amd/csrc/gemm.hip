@@ -7,21 +7,25 @@
 //
 // Tiling: a 256-thread workgroup owns a 128x128 output tile; its four waves
 // each own 64x64 (2x2 blocks of the 32x32 MFMA).  The reduction runs in
-// steps of 32, staged through LDS with a register prefetch of the next step
-// (two LDS stages, one barrier per step).  Within a step the two 32-lane
-// halves of a wave own k = 0..15 and k = 16..31, so an operand stored
-// k-contiguous is read from LDS as float4 (four MFMA steps per read).
+// steps of 32 staged through two LDS buffers (one barrier per step) while
+// the global loads of the step after next are in flight in registers, so
+// each load has two steps of MFMA work to arrive.  Within a step the two
+// 32-lane halves of a wave own k = 0..15 and k = 16..31, so an operand
+// stored k-contiguous is read from LDS as float4 (four MFMA steps per read).
+// Tiles wholly inside the matrices load without bounds checks.
 //
 // Operands whose reduction index is contiguous in HBM are stored in LDS as
 // [row][k] (36-float rows); operands whose free index is contiguous are
 // stored as [k][row] (132-float rows).  Both are written with float4.
 //
-// Epilogues fuse what the layer does next: bias, residual add, GELU (writing
-// both pre- and post-activation), the GELU derivative of the backward, or +=
-// into a gradient.  Large reductions over few output tiles are split over K
-// into a workspace and summed in a fixed order by a second kernel, so results
-// are deterministic.
+// The epilogue stages each wave's 64x64 block through LDS and then works
+// along rows with float4 loads and stores, fusing what the layer does next:
+// bias, residual add, GELU (writing both pre- and post-activation), the
+// GELU derivative of the backward, or += into a gradient.  Large reductions
+// over few output tiles are split over K into a workspace and summed in a
+// fixed order by a second kernel, so results are deterministic.
 #include <algorithm>
+#include <type_traits>
 
 #include "common.h"
 #include "kernels.h"
@@ -30,103 +34,167 @@ namespace gk {
 namespace {
 
 constexpr int BM = 128, BN = 128, BK = 32, NTHR = 256;
+constexpr int PF = 2;            // register prefetch depth (tiles in flight)
 constexpr int FM_LD = BK + 4;    // [row][k] tile row stride
-constexpr int KM_LD = 128 + 4;   // [k][row] tile row stride
 constexpr int EPI_PARTIAL = 100; // internal: write split-K partial sums
 
 __device__ __forceinline__ floatx16 mfma(float a, float b, floatx16 c) {
     return __builtin_amdgcn_mfma_f32_32x32x2f32(a, b, c, 0, 0, 0);
 }
 
-template <bool KC>
+template <bool KC, int R, int NT>
 struct Tile;
 
-// Reduction index contiguous: element (r, k) at g[r*ld + k].
-template <>
-struct Tile<true> {
-    static constexpr int FLOATS = 128 * FM_LD;
-    float4 v[4];
-    __device__ __forceinline__ void load(const float* __restrict__ g, int64_t ld,
-                                         int r0, int R, int k0, int K) {
-        const int t = threadIdx.x;
-        const int k = k0 + (t & 7) * 4;
+template <int R, int NT>
+struct Tile<true, R, NT> {
+    static constexpr int FLOATS = R * FM_LD;
+    static constexpr int PER = R * 8 / NT;
+    float4 v[PER];
+    template <bool CHECK>
+    __device__ __forceinline__ void load(const float* __restrict__ g, int64_t ld, int r0, int Rn,
+                                         int k0, int K) {
 #pragma unroll
-        for (int i = 0; i < 4; i++) {
-            const int r = r0 + (t >> 3) + 32 * i;
-            float4 x = make_float4(0.f, 0.f, 0.f, 0.f);
-            if (r < R) {
-                const float* p = g + (int64_t)r * ld + k;
-                if (k + 3 < K) {
-                    x = ld4(p);
-                } else {
-                    if (k < K) x.x = p[0];
-                    if (k + 1 < K) x.y = p[1];
-                    if (k + 2 < K) x.z = p[2];
+        for (int i = 0; i < PER; i++) {
+            const int idx = threadIdx.x + NT * i;
+            const int r = r0 + (idx >> 3);
+            const int k = k0 + (idx & 7) * 4;
+            const float* p = g + (int64_t)r * ld + k;
+            if (!CHECK) {
+                v[i] = ld4(p);
+            } else {
+                float4 x = make_float4(0.f, 0.f, 0.f, 0.f);
+                if (r < Rn) {
+                    if (k + 3 < K) x = ld4(p);
+                    else {
+                        if (k < K) x.x = p[0];
+                        if (k + 1 < K) x.y = p[1];
+                        if (k + 2 < K) x.z = p[2];
+                    }
                 }
+                v[i] = x;
             }
-            v[i] = x;
         }
     }
     __device__ __forceinline__ void store(float* s) const {
-        const int t = threadIdx.x;
 #pragma unroll
-        for (int i = 0; i < 4; i++)
-            st4(s + ((t >> 3) + 32 * i) * FM_LD + (t & 7) * 4, v[i]);
+        for (int i = 0; i < PER; i++) {
+            const int idx = threadIdx.x + NT * i;
+            st4(s + (idx >> 3) * FM_LD + (idx & 7) * 4, v[i]);
+        }
     }
-    // k = 16*g + 4*q + (0..3) at tile row r
     __device__ static __forceinline__ float4 frag(const float* s, int r, int g, int q) {
         return ld4(s + r * FM_LD + 16 * g + 4 * q);
     }
 };
 
-// Free index contiguous: element (r, k) at g[k*ld + r].
-template <>
-struct Tile<false> {
-    static constexpr int FLOATS = BK * KM_LD;
-    float4 v[4];
-    __device__ __forceinline__ void load(const float* __restrict__ g, int64_t ld,
-                                         int r0, int R, int k0, int K) {
-        const int t = threadIdx.x;
-        const int r = r0 + (t & 31) * 4;
+template <int R, int NT>
+struct Tile<false, R, NT> {
+    static constexpr int LDK = R + 4;
+    static constexpr int FLOATS = BK * LDK;
+    static constexpr int PER = BK * R / 4 / NT;
+    static constexpr int R4 = R / 4;
+    float4 v[PER];
+    template <bool CHECK>
+    __device__ __forceinline__ void load(const float* __restrict__ g, int64_t ld, int r0, int Rn,
+                                         int k0, int K) {
 #pragma unroll
-        for (int i = 0; i < 4; i++) {
-            const int k = k0 + (t >> 5) + 8 * i;
-            float4 x = make_float4(0.f, 0.f, 0.f, 0.f);
-            if (k < K) {
-                const float* p = g + (int64_t)k * ld + r;
-                if (r + 3 < R) {
-                    x = ld4(p);
-                } else {
-                    if (r < R) x.x = p[0];
-                    if (r + 1 < R) x.y = p[1];
-                    if (r + 2 < R) x.z = p[2];
+        for (int i = 0; i < PER; i++) {
+            const int idx = threadIdx.x + NT * i;
+            const int k = k0 + idx / R4;
+            const int r = r0 + (idx % R4) * 4;
+            const float* p = g + (int64_t)k * ld + r;
+            if (!CHECK) {
+                v[i] = ld4(p);
+            } else {
+                float4 x = make_float4(0.f, 0.f, 0.f, 0.f);
+                if (k < K) {
+                    if (r + 3 < Rn) x = ld4(p);
+                    else {
+                        if (r < Rn) x.x = p[0];
+                        if (r + 1 < Rn) x.y = p[1];
+                        if (r + 2 < Rn) x.z = p[2];
+                    }
                 }
+                v[i] = x;
             }
-            v[i] = x;
         }
     }
     __device__ __forceinline__ void store(float* s) const {
-        const int t = threadIdx.x;
 #pragma unroll
-        for (int i = 0; i < 4; i++)
-            st4(s + ((t >> 5) + 8 * i) * KM_LD + (t & 31) * 4, v[i]);
+        for (int i = 0; i < PER; i++) {
+            const int idx = threadIdx.x + NT * i;
+            st4(s + (idx / R4) * LDK + (idx % R4) * 4, v[i]);
+        }
     }
     __device__ static __forceinline__ float4 frag(const float* s, int r, int g, int q) {
-        const float* p = s + (16 * g + 4 * q) * KM_LD + r;
-        return make_float4(p[0], p[KM_LD], p[2 * KM_LD], p[3 * KM_LD]);
+        const float* p = s + (16 * g + 4 * q) * LDK + r;
+        return make_float4(p[0], p[LDK], p[2 * LDK], p[3 * LDK]);
     }
 };
 
+template <int EPI>
+__device__ __forceinline__ void epi_store(const GemmArgs& a, float* __restrict__ partial,
+                                          int row, int col, float4 v) {
+    if (EPI == EPI_PARTIAL) {
+        st4(partial + (int64_t)blockIdx.z * a.M * a.N + (int64_t)row * a.N + col, v);
+        return;
+    }
+    float* c = a.C + (int64_t)row * a.ldc + col;
+    if (EPI == EPI_ACCUM) {
+        const float4 o = ld4(c);
+        st4(c, make_float4(o.x + v.x, o.y + v.y, o.z + v.z, o.w + v.w));
+        return;
+    }
+    if (EPI == EPI_GELU_BWD) {
+        const float4 x = ld4(a.aux + (int64_t)row * a.ldaux + col);
+        st4(c, make_float4(v.x * gelu_grad_f(x.x), v.y * gelu_grad_f(x.y), v.z * gelu_grad_f(x.z),
+                           v.w * gelu_grad_f(x.w)));
+        return;
+    }
+    float4 bb = make_float4(0.f, 0.f, 0.f, 0.f);
+    if (EPI != EPI_STORE || a.bias) bb = ld4(a.bias + col);
+    v = make_float4(v.x + bb.x, v.y + bb.y, v.z + bb.z, v.w + bb.w);
+    if (EPI == EPI_RESID) {
+        const float4 x = ld4(a.aux + (int64_t)row * a.ldaux + col);
+        v = make_float4(v.x + x.x, v.y + x.y, v.z + x.z, v.w + x.w);
+    }
+    st4(c, v);
+    if (EPI == EPI_GELU)
+        st4(a.out2 + (int64_t)row * a.ldc + col,
+            make_float4(gelu_f(v.x), gelu_f(v.y), gelu_f(v.z), gelu_f(v.w)));
+}
+
+template <int EPI>
+__device__ __forceinline__ void epi_scalar(const GemmArgs& a, float* __restrict__ partial,
+                                           int row, int col, float v) {
+    if (EPI == EPI_PARTIAL) {
+        partial[(int64_t)blockIdx.z * a.M * a.N + (int64_t)row * a.N + col] = v;
+        return;
+    }
+    const int64_t idx = (int64_t)row * a.ldc + col;
+    if (EPI == EPI_ACCUM) { a.C[idx] += v; return; }
+    if (EPI == EPI_GELU_BWD) { a.C[idx] = v * gelu_grad_f(a.aux[(int64_t)row * a.ldaux + col]); return; }
+    float bb = 0.f;
+    if (EPI != EPI_STORE || a.bias) bb = a.bias[col];
+    v += bb;
+    if (EPI == EPI_RESID) v += a.aux[(int64_t)row * a.ldaux + col];
+    a.C[idx] = v;
+    if (EPI == EPI_GELU) a.out2[idx] = gelu_f(v);
+}
+
 template <int OP, int EPI>
-__global__ __launch_bounds__(NTHR, 2) void gemm_kernel(const GemmArgs a, int tiles_m,
-                                                       int tiles_n, int kchunk,
-                                                       float* __restrict__ partial) {
+__global__ __launch_bounds__(NTHR, 2) void gemm_kernel(
+    const GemmArgs a, int tiles_m, int tiles_n, int kchunk, float* __restrict__ partial) {
+    constexpr int NT = NTHR;
     constexpr bool AKC = (OP != GEMM_TN);
     constexpr bool BKC = (OP == GEMM_NT);
-    __shared__ __attribute__((aligned(16))) float smA[2][Tile<AKC>::FLOATS];
-    __shared__ __attribute__((aligned(16))) float smB[2][Tile<BKC>::FLOATS];
+    using TA = Tile<AKC, BM, NT>;
+    using TB = Tile<BKC, BN, NT>;
+    constexpr int MAIN = 2 * (TA::FLOATS + TB::FLOATS);
+    constexpr int EPIF = (NT / 64) * 64 * 68;  // epilogue staging, one 64x68 block per wave
+    constexpr int SMEM = MAIN > EPIF ? MAIN : EPIF;
+    __shared__ __attribute__((aligned(16))) float sm[SMEM];
 
-    // tile order: XCD-contiguous ranges, then groups of 8 tile-rows
     const int tile = xcd_remap(blockIdx.x, tiles_m * tiles_n);
     constexpr int GM = 8;
     const int per_group = GM * tiles_n;
@@ -140,6 +208,7 @@ __global__ __launch_bounds__(NTHR, 2) void gemm_kernel(const GemmArgs a, int til
     const int k_begin = blockIdx.z * kchunk;
     const int k_end = min(a.K, k_begin + kchunk);
     const int nk = k_end > k_begin ? (k_end - k_begin + BK - 1) / BK : 0;
+    const bool interior = (m0 + BM <= a.M) && (n0 + BN <= a.N);
 
     const int lane = threadIdx.x & 63, wave = threadIdx.x >> 6;
     const int wm = (wave >> 1) * 64, wn = (wave & 1) * 64;
@@ -153,30 +222,43 @@ __global__ __launch_bounds__(NTHR, 2) void gemm_kernel(const GemmArgs a, int til
 #pragma unroll
             for (int e = 0; e < 16; e++) acc[i][j][e] = 0.f;
 
-    Tile<AKC> ta;
-    Tile<BKC> tb;
+    TA ta[PF];
+    TB tb[PF];
+    auto issue = [&](auto slotc, int kt) {
+        constexpr int S = decltype(slotc)::value;
+        const int kk = k_begin + kt * BK;
+        if (interior && kk + BK <= k_end) {
+            ta[S].template load<false>(a.A, a.lda, m0, a.M, kk, k_end);
+            tb[S].template load<false>(a.B, a.ldb, n0, a.N, kk, k_end);
+        } else {
+            ta[S].template load<true>(a.A, a.lda, m0, a.M, kk, k_end);
+            tb[S].template load<true>(a.B, a.ldb, n0, a.N, kk, k_end);
+        }
+    };
+    using I0 = std::integral_constant<int, 0>;
+    using I1 = std::integral_constant<int, 1>;
     if (nk > 0) {
-        ta.load(a.A, a.lda, m0, a.M, k_begin, k_end);
-        tb.load(a.B, a.ldb, n0, a.N, k_begin, k_end);
-        ta.store(smA[0]);
-        tb.store(smB[0]);
+        issue(I0{}, 0);
+        ta[0].store(sm);
+        tb[0].store(sm + 2 * TA::FLOATS);
+        if (nk > 1) issue(I1{}, 1);
     }
     __syncthreads();
-    for (int kt = 0; kt < nk; kt++) {
+    // Tile j's registers live in slot j & 1: while step j computes from LDS,
+    // tile j+2 is loading into the slot step j-1 just emptied into LDS.
+    auto step = [&](int kt, auto slotc) {
+        constexpr int S = decltype(slotc)::value;
+        constexpr int NS = S ^ 1;
         const int cur = kt & 1;
-        if (kt + 1 < nk) {
-            const int kn = k_begin + (kt + 1) * BK;
-            ta.load(a.A, a.lda, m0, a.M, kn, k_end);
-            tb.load(a.B, a.ldb, n0, a.N, kn, k_end);
-        }
-        const float* sa = smA[cur];
-        const float* sb = smB[cur];
+        if (kt + 2 < nk) issue(slotc, kt + 2);
+        const float* sa = sm + cur * TA::FLOATS;
+        const float* sb = sm + 2 * TA::FLOATS + cur * TB::FLOATS;
 #pragma unroll
         for (int q = 0; q < 4; q++) {
-            const float4 a0 = Tile<AKC>::frag(sa, wm + li, g, q);
-            const float4 a1 = Tile<AKC>::frag(sa, wm + 32 + li, g, q);
-            const float4 b0 = Tile<BKC>::frag(sb, wn + li, g, q);
-            const float4 b1 = Tile<BKC>::frag(sb, wn + 32 + li, g, q);
+            const float4 a0 = TA::frag(sa, wm + li, g, q);
+            const float4 a1 = TA::frag(sa, wm + 32 + li, g, q);
+            const float4 b0 = TB::frag(sb, wn + li, g, q);
+            const float4 b1 = TB::frag(sb, wn + 32 + li, g, q);
             acc[0][0] = mfma(a0.x, b0.x, acc[0][0]);
             acc[0][1] = mfma(a0.x, b1.x, acc[0][1]);
             acc[1][0] = mfma(a1.x, b0.x, acc[1][0]);
@@ -195,46 +277,40 @@ __global__ __launch_bounds__(NTHR, 2) void gemm_kernel(const GemmArgs a, int til
             acc[1][1] = mfma(a1.w, b1.w, acc[1][1]);
         }
         if (kt + 1 < nk) {
-            ta.store(smA[cur ^ 1]);
-            tb.store(smB[cur ^ 1]);
+            ta[NS].store(sm + (cur ^ 1) * TA::FLOATS);
+            tb[NS].store(sm + 2 * TA::FLOATS + (cur ^ 1) * TB::FLOATS);
         }
         __syncthreads();
+    };
+    for (int kt = 0; kt < nk; kt += 2) {
+        step(kt, I0{});
+        if (kt + 1 < nk) step(kt + 1, I1{});
     }
 
-    // 32x32 accumulator layout: lane holds column li, rows 8*(e/4) + 4*g + e%4
+    // Stage this wave's 64x64 block in LDS (the main loop's buffers are free
+    // after the last barrier), then apply the epilogue along rows with float4.
+    float* ws = sm + wave * 64 * 68;
 #pragma unroll
-    for (int bn = 0; bn < 2; bn++) {
-        const int col = n0 + wn + 32 * bn + li;
-        if (col >= a.N) continue;
-        float bcol = 0.f;
-        if (EPI == EPI_RESID || EPI == EPI_GELU || (EPI == EPI_STORE && a.bias))
-            bcol = a.bias[col];
+    for (int bm = 0; bm < 2; bm++)
 #pragma unroll
-        for (int bm = 0; bm < 2; bm++) {
+        for (int bn = 0; bn < 2; bn++)
 #pragma unroll
-            for (int e = 0; e < 16; e++) {
-                const int row = m0 + wm + 32 * bm + 8 * (e >> 2) + 4 * g + (e & 3);
-                if (row >= a.M) continue;
-                const float v = acc[bm][bn][e];
-                if (EPI == EPI_PARTIAL) {
-                    partial[(int64_t)blockIdx.z * a.M * a.N + (int64_t)row * a.N + col] = v;
-                } else {
-                    const int64_t idx = (int64_t)row * a.ldc + col;
-                    if (EPI == EPI_STORE) {
-                        a.C[idx] = v + bcol;
-                    } else if (EPI == EPI_RESID) {
-                        a.C[idx] = v + bcol + a.aux[(int64_t)row * a.ldaux + col];
-                    } else if (EPI == EPI_GELU) {
-                        const float pre = v + bcol;
-                        a.C[idx] = pre;
-                        a.out2[idx] = gelu_f(pre);
-                    } else if (EPI == EPI_GELU_BWD) {
-                        a.C[idx] = v * gelu_grad_f(a.aux[(int64_t)row * a.ldaux + col]);
-                    } else if (EPI == EPI_ACCUM) {
-                        a.C[idx] += v;
-                    }
-                }
-            }
+            for (int e = 0; e < 16; e++)
+                ws[(32 * bm + 8 * (e >> 2) + 4 * g + (e & 3)) * 68 + 32 * bn + li] = acc[bm][bn][e];
+    __syncthreads();
+#pragma unroll 4
+    for (int j = 0; j < 16; j++) {
+        const int idx = lane + 64 * j;
+        const int r = idx >> 4, c4 = (idx & 15) * 4;
+        const float4 v = ld4(ws + r * 68 + c4);
+        const int row = m0 + wm + r, col = n0 + wn + c4;
+        if (row >= a.M) continue;
+        if (col + 3 < a.N) {
+            epi_store<EPI>(a, partial, row, col, v);
+        } else {
+            if (col < a.N) epi_scalar<EPI>(a, partial, row, col, v.x);
+            if (col + 1 < a.N) epi_scalar<EPI>(a, partial, row, col + 1, v.y);
+            if (col + 2 < a.N) epi_scalar<EPI>(a, partial, row, col + 2, v.z);
         }
     }
 }
