@@ -25,9 +25,11 @@
 // deterministic.
 //
 // Each workgroup is four waves owning 128 consecutive rows; the other operand
-// streams through LDS in 64-row tiles, double-buffered with a register
-// prefetch of the next tile (one barrier per tile).  32-row blocks that the
-// causal mask empties completely are skipped.
+// streams through LDS in 64-row tiles (V transposed in the forward, so one
+// float4 read feeds four MFMA steps), double-buffered with a register
+// prefetch of the next tile (one barrier per tile).  Tiles (and, in the
+// key/value kernel, 32-query blocks) that the causal mask empties completely
+// are skipped.
 #include "common.h"
 #include "kernels.h"
 
@@ -75,6 +77,18 @@ struct TileRegs {
             st4(sm + r * (HS + 4) + c, v[i]);
         }
     }
+    // transposed: element (row r, column c) at sm[c * (AT + 4) + r]
+    __device__ __forceinline__ void store_t(float* sm) const {
+#pragma unroll
+        for (int i = 0; i < PER; i++) {
+            const int idx = threadIdx.x + 256 * i;
+            const int r = idx / C4, c = (idx - r * C4) * 4;
+            sm[(c + 0) * (AT + 4) + r] = v[i].x;
+            sm[(c + 1) * (AT + 4) + r] = v[i].y;
+            sm[(c + 2) * (AT + 4) + r] = v[i].z;
+            sm[(c + 3) * (AT + 4) + r] = v[i].w;
+        }
+    }
 };
 
 // Write a lane's 32-row accumulator block(s) of one row: the lane holds
@@ -99,13 +113,24 @@ __global__ __launch_bounds__(256, 2) void attn_fwd_kernel(float* __restrict__ ou
                                                           const float* __restrict__ qkv, int T,
                                                           int C, int NH, float qscale) {
     constexpr int LD = HS + 4, HALF = HS / 2, NDB = (HS + 31) / 32;
+    constexpr int LDT = AT + 4;        // V^T row stride (keys)
+    constexpr int VROWS = NDB * 32;    // V^T rows (head dims, padded to 32)
     __shared__ __attribute__((aligned(16))) float ks[2][AT * LD];
-    __shared__ __attribute__((aligned(16))) float vs[2][AT * LD];
+    __shared__ __attribute__((aligned(16))) float vs[2][VROWS * LDT];
 
+    // Longest-first over the whole grid: all heads' last query blocks (the
+    // most key tiles) are dispatched first, the first blocks fill the tail.
+    // Plain round-robin dispatch then gives every XCD the same mix.
     const int nqb = (T + AQ - 1) / AQ;
-    const int id = xcd_remap(blockIdx.x, gridDim.x);
-    const int bh = id / nqb;
-    const int qb = nqb - 1 - (id - bh * nqb);  // longest rows first
+    const int nbh = gridDim.x / nqb;
+    const int bh = blockIdx.x % nbh;
+    const int qb = nqb - 1 - blockIdx.x / nbh;
+    if (VROWS > HS) {  // padding rows of V^T stay zero
+        for (int i = threadIdx.x; i < (VROWS - HS) * LDT; i += blockDim.x) {
+            vs[0][HS * LDT + i] = 0.f;
+            vs[1][HS * LDT + i] = 0.f;
+        }
+    }
     const int b = bh / NH, h = bh - b * NH;
     const int lane = threadIdx.x & 63, wave = threadIdx.x >> 6;
     const int li = lane & 31, g = lane >> 5;
@@ -136,7 +161,7 @@ __global__ __launch_bounds__(256, 2) void attn_fwd_kernel(float* __restrict__ ou
     kreg.load(qbase + C, ld, 0, T);
     vreg.load(qbase + 2 * C, ld, 0, T);
     kreg.store(ks[0]);
-    vreg.store(vs[0]);
+    vreg.store_t(vs[0]);
     __syncthreads();
     for (int kt = 0; kt < nkt; kt++) {
         const int cur = kt & 1;
@@ -146,36 +171,42 @@ __global__ __launch_bounds__(256, 2) void attn_fwd_kernel(float* __restrict__ ou
         }
         const int k0 = kt * AT;
         if (k0 <= qmax) {
-            const bool kb1 = k0 + 32 <= qmax;
             const float* ksm = ks[cur];
             const float* vsm = vs[cur];
+            // S^T for both 32-key blocks as two interleaved MFMA chains
             floatx16 sc[2];
             zero16(sc[0]);
             zero16(sc[1]);
+            const float* kr0 = ksm + li * LD + g * HALF;
+            const float* kr1 = kr0 + 32 * LD;
 #pragma unroll
-            for (int kb = 0; kb < 2; kb++) {
-                if (kb == 1 && !kb1) break;
-                const float* kr = ksm + (kb * 32 + li) * LD + g * HALF;
-#pragma unroll
-                for (int s = 0; s < HALF; s += 4) {
-                    const float4 kf = ld4(kr + s);
-                    sc[kb] = mfma(kf.x, qr[s], sc[kb]);
-                    sc[kb] = mfma(kf.y, qr[s + 1], sc[kb]);
-                    sc[kb] = mfma(kf.z, qr[s + 2], sc[kb]);
-                    sc[kb] = mfma(kf.w, qr[s + 3], sc[kb]);
-                }
+            for (int s = 0; s < HALF; s += 4) {
+                const float4 k0f = ld4(kr0 + s);
+                const float4 k1f = ld4(kr1 + s);
+                sc[0] = mfma(k0f.x, qr[s], sc[0]);
+                sc[1] = mfma(k1f.x, qr[s], sc[1]);
+                sc[0] = mfma(k0f.y, qr[s + 1], sc[0]);
+                sc[1] = mfma(k1f.y, qr[s + 1], sc[1]);
+                sc[0] = mfma(k0f.z, qr[s + 2], sc[0]);
+                sc[1] = mfma(k1f.z, qr[s + 2], sc[1]);
+                sc[0] = mfma(k0f.w, qr[s + 3], sc[0]);
+                sc[1] = mfma(k1f.w, qr[s + 3], sc[1]);
             }
-            const bool need_mask = (k0 + AT - 1 > qw) || (k0 + AT > T);
+            if ((k0 + AT - 1 > qw) || (k0 + AT > T)) {  // tile touches the mask
+#pragma unroll
+                for (int kb = 0; kb < 2; kb++)
+#pragma unroll
+                    for (int e = 0; e < 16; e++) {
+                        const int key = k0 + kb * 32 + 8 * (e >> 2) + 4 * g + (e & 3);
+                        const bool dead = (key > q) | (key >= T);
+                        sc[kb][e] = dead ? -INFINITY : sc[kb][e];
+                    }
+            }
             float mt = -INFINITY;
 #pragma unroll
             for (int kb = 0; kb < 2; kb++)
 #pragma unroll
-                for (int e = 0; e < 16; e++) {
-                    const int key = k0 + kb * 32 + 8 * (e >> 2) + 4 * g + (e & 3);
-                    if ((kb == 1 && !kb1) || (need_mask && (key > q || key >= T)))
-                        sc[kb][e] = -INFINITY;
-                    mt = fmaxf(mt, sc[kb][e]);
-                }
+                for (int e = 0; e < 16; e++) mt = fmaxf(mt, sc[kb][e]);
             mt = fmaxf(mt, __shfl_xor(mt, 32, WAVE));
             const float mn = fmaxf(m, mt);
             const float corr = exp2_fast(m - mn);
@@ -195,24 +226,25 @@ __global__ __launch_bounds__(256, 2) void attn_fwd_kernel(float* __restrict__ ou
             for (int d = 0; d < NDB; d++)
 #pragma unroll
                 for (int e = 0; e < 16; e++) o[d][e] *= corr;
+            // O^T += V^T P^T: steps e = 4c..4c+3 use keys 8c+4g+(0..3) of a
+            // block, one float4 of a V^T row
 #pragma unroll
-            for (int kb = 0; kb < 2; kb++) {
-                if (kb == 1 && !kb1) break;
+            for (int kb = 0; kb < 2; kb++)
 #pragma unroll
-                for (int e = 0; e < 16; e++) {
-                    const int kl = kb * 32 + 8 * (e >> 2) + 4 * g + (e & 3);
+                for (int c = 0; c < 4; c++)
 #pragma unroll
                     for (int d = 0; d < NDB; d++) {
-                        const int dim = d * 32 + li;
-                        const float va = dim < HS ? vsm[kl * LD + dim] : 0.f;
-                        o[d] = mfma(va, sc[kb][e], o[d]);
+                        const float4 va =
+                            ld4(vsm + (d * 32 + li) * LDT + kb * 32 + 8 * c + 4 * g);
+                        o[d] = mfma(va.x, sc[kb][4 * c], o[d]);
+                        o[d] = mfma(va.y, sc[kb][4 * c + 1], o[d]);
+                        o[d] = mfma(va.z, sc[kb][4 * c + 2], o[d]);
+                        o[d] = mfma(va.w, sc[kb][4 * c + 3], o[d]);
                     }
-                }
-            }
         }
         if (kt + 1 < nkt) {
             kreg.store(ks[cur ^ 1]);
-            vreg.store(vs[cur ^ 1]);
+            vreg.store_t(vs[cur ^ 1]);
         }
         __syncthreads();
     }
@@ -233,9 +265,9 @@ __global__ __launch_bounds__(256, 2) void attn_bwd_dq_kernel(
     __shared__ __attribute__((aligned(16))) float vs[2][AT * LD];
 
     const int nqb = (T + AQ - 1) / AQ;
-    const int id = xcd_remap(blockIdx.x, gridDim.x);
-    const int bh = id / nqb;
-    const int qb = nqb - 1 - (id - bh * nqb);
+    const int nbh = gridDim.x / nqb;
+    const int bh = blockIdx.x % nbh;
+    const int qb = nqb - 1 - blockIdx.x / nbh;  // longest first
     const int b = bh / NH, h = bh - b * NH;
     const int lane = threadIdx.x & 63, wave = threadIdx.x >> 6;
     const int li = lane & 31, g = lane >> 5;
@@ -291,7 +323,6 @@ __global__ __launch_bounds__(256, 2) void attn_bwd_dq_kernel(
         }
         const int k0 = kt * AT;
         if (k0 <= qmax) {
-            const bool kb1 = k0 + 32 <= qmax;
             const float* ksm = ks[cur];
             const float* vsm = vs[cur];
             floatx16 sc[2], dp[2];
@@ -299,20 +330,22 @@ __global__ __launch_bounds__(256, 2) void attn_bwd_dq_kernel(
             for (int kb = 0; kb < 2; kb++) {
                 zero16(sc[kb]);
                 zero16(dp[kb]);
-                if (kb == 1 && !kb1) break;
-                const float* kr = ksm + (kb * 32 + li) * LD + g * HALF;
-                const float* vr = vsm + (kb * 32 + li) * LD + g * HALF;
+            }
+            const float* kr0 = ksm + li * LD + g * HALF;
+            const float* vr0 = vsm + li * LD + g * HALF;
 #pragma unroll
-                for (int s = 0; s < HALF; s += 4) {
-                    const float4 kf = ld4(kr + s);
-                    const float4 vf = ld4(vr + s);
+            for (int s = 0; s < HALF; s += 4) {
+#pragma unroll
+                for (int kb = 0; kb < 2; kb++) {
+                    const float4 kf = ld4(kr0 + kb * 32 * LD + s);
+                    const float4 vf = ld4(vr0 + kb * 32 * LD + s);
                     sc[kb] = mfma(kf.x, qr[s], sc[kb]);
-                    sc[kb] = mfma(kf.y, qr[s + 1], sc[kb]);
-                    sc[kb] = mfma(kf.z, qr[s + 2], sc[kb]);
-                    sc[kb] = mfma(kf.w, qr[s + 3], sc[kb]);
                     dp[kb] = mfma(vf.x, dr[s], dp[kb]);
+                    sc[kb] = mfma(kf.y, qr[s + 1], sc[kb]);
                     dp[kb] = mfma(vf.y, dr[s + 1], dp[kb]);
+                    sc[kb] = mfma(kf.z, qr[s + 2], sc[kb]);
                     dp[kb] = mfma(vf.z, dr[s + 2], dp[kb]);
+                    sc[kb] = mfma(kf.w, qr[s + 3], sc[kb]);
                     dp[kb] = mfma(vf.w, dr[s + 3], dp[kb]);
                 }
             }
@@ -321,23 +354,26 @@ __global__ __launch_bounds__(256, 2) void attn_bwd_dq_kernel(
 #pragma unroll
                 for (int e = 0; e < 16; e++) {
                     const int key = k0 + kb * 32 + 8 * (e >> 2) + 4 * g + (e & 3);
-                    const bool live = (kb == 0 || kb1) && key <= q && key < T;
-                    const float p = live ? exp2_fast(sc[kb][e] - lq) : 0.f;
-                    sc[kb][e] = p * (dp[kb][e] - Dq);
+                    const bool live = (key <= q) & (key < T);
+                    const float p = exp2_fast(sc[kb][e] - lq);
+                    sc[kb][e] = live ? p * (dp[kb][e] - Dq) : 0.f;
                 }
 #pragma unroll
             for (int kb = 0; kb < 2; kb++) {
-                if (kb == 1 && !kb1) break;
+                float ka[16][NDB];  // all reads of the block issued before its MFMAs
 #pragma unroll
                 for (int e = 0; e < 16; e++) {
                     const int kl = kb * 32 + 8 * (e >> 2) + 4 * g + (e & 3);
 #pragma unroll
                     for (int d = 0; d < NDB; d++) {
                         const int dim = d * 32 + li;
-                        const float ka = dim < HS ? ksm[kl * LD + dim] : 0.f;
-                        dq[d] = mfma(ka, sc[kb][e], dq[d]);
+                        ka[e][d] = dim < HS ? ksm[kl * LD + dim] : 0.f;
                     }
                 }
+#pragma unroll
+                for (int e = 0; e < 16; e++)
+#pragma unroll
+                    for (int d = 0; d < NDB; d++) dq[d] = mfma(ka[e][d], sc[kb][e], dq[d]);
             }
         }
         if (kt + 1 < nkt) {
@@ -360,9 +396,9 @@ __global__ __launch_bounds__(256, 2) void attn_bwd_dkdv_kernel(
     __shared__ float lsm[2][AT], dsm[2][AT];
 
     const int nkb = (T + AQ - 1) / AQ;
-    const int id = xcd_remap(blockIdx.x, gridDim.x);
-    const int bh = id / nkb;
-    const int kb0 = id - bh * nkb;  // lowest keys = most query tiles: first
+    const int nbh = gridDim.x / nkb;
+    const int bh = blockIdx.x % nbh;
+    const int kb0 = blockIdx.x / nbh;  // lowest keys = most query tiles: first
     const int b = bh / NH, h = bh - b * NH;
     const int lane = threadIdx.x & 63, wave = threadIdx.x >> 6;
     const int li = lane & 31, g = lane >> 5;
@@ -451,21 +487,32 @@ __global__ __launch_bounds__(256, 2) void attn_bwd_dkdv_kernel(
             for (int e = 0; e < 16; e++) {
                 const int ql = qh * 32 + 8 * (e >> 2) + 4 * g + (e & 3);
                 const int qa = qt * AT + ql;
-                const float p = (qa < T && key <= qa) ? exp2_fast(sc[e] - lsm[cur][ql]) : 0.f;
+                const bool live = (qa < T) & (key <= qa);
+                const float p = live ? exp2_fast(sc[e] - lsm[cur][ql]) : 0.f;
                 sc[e] = p;
                 dp[e] = p * (dp[e] - dsm[cur][ql]);
             }
 #pragma unroll
-            for (int e = 0; e < 16; e++) {
-                const int ql = qh * 32 + 8 * (e >> 2) + 4 * g + (e & 3);
+            for (int half = 0; half < 2; half++) {
+                float da[8][NDB], qa[8][NDB];  // reads issued before the MFMAs
 #pragma unroll
-                for (int d = 0; d < NDB; d++) {
-                    const int dim = d * 32 + li;
-                    const float da = dim < HS ? dsmem[ql * LD + dim] : 0.f;
-                    const float qa = dim < HS ? qsm[ql * LD + dim] : 0.f;
-                    dv[d] = mfma(da, sc[e], dv[d]);
-                    dk[d] = mfma(qa, dp[e], dk[d]);
+                for (int i = 0; i < 8; i++) {
+                    const int e = half * 8 + i;
+                    const int ql = qh * 32 + 8 * (e >> 2) + 4 * g + (e & 3);
+#pragma unroll
+                    for (int d = 0; d < NDB; d++) {
+                        const int dim = d * 32 + li;
+                        da[i][d] = dim < HS ? dsmem[ql * LD + dim] : 0.f;
+                        qa[i][d] = dim < HS ? qsm[ql * LD + dim] : 0.f;
+                    }
                 }
+#pragma unroll
+                for (int i = 0; i < 8; i++)
+#pragma unroll
+                    for (int d = 0; d < NDB; d++) {
+                        dv[d] = mfma(da[i][d], sc[half * 8 + i], dv[d]);
+                        dk[d] = mfma(qa[i][d], dp[half * 8 + i], dk[d]);
+                    }
             }
         }
         if (qt + 1 < nqt) {
