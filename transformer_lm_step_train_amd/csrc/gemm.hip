@@ -315,10 +315,14 @@ __global__ __launch_bounds__(NTHR, 2) void gemm_kernel(
     }
 }
 
-// C (+)= sum over splits of partial, in split order.  N % 4 == 0.
-__global__ __launch_bounds__(256) void splitk_reduce_kernel(
-    float* __restrict__ C, int64_t ldc, const float* __restrict__ partial, int splits,
-    int M, int N, int accumulate) {
+// Sum of the split-K partials in split order, then the epilogue of the
+// matmul (store with optional bias, residual add, or += into a gradient).
+// N % 4 == 0.
+template <int EPI>
+__global__ __launch_bounds__(256) void splitk_reduce_kernel(const GemmArgs a,
+                                                            const float* __restrict__ partial,
+                                                            int splits) {
+    const int M = a.M, N = a.N;
     const int64_t n4 = (int64_t)M * (N / 4);
     for (int64_t i = blockIdx.x * (int64_t)blockDim.x + threadIdx.x; i < n4;
          i += (int64_t)gridDim.x * blockDim.x) {
@@ -332,32 +336,49 @@ __global__ __launch_bounds__(256) void splitk_reduce_kernel(
             s.z += p.z;
             s.w += p.w;
         }
-        float* c = C + row * ldc + col;
-        if (accumulate) {
-            const float4 o = ld4(c);
-            s.x += o.x;
-            s.y += o.y;
-            s.z += o.z;
-            s.w += o.w;
-        }
-        st4(c, s);
+        epi_store<EPI>(a, nullptr, (int)row, col, s);
     }
 }
 
 inline int cdiv(int64_t a, int64_t b) { return (int)((a + b - 1) / b); }
 
-// Split the reduction when there are too few output tiles to fill the chip
-// (weight gradients of the C x C and 4C x C layers, whose K is B*T).
-int choose_splits(int op, int M, int N, int K) {
-    if (op != GEMM_TN || (N % 4) != 0) return 1;
+// Workgroups resident at once (two per compute unit).
+int resident_slots() {
+    static int slots = 0;
+    if (!slots) {
+        int dev = 0, cus = 0;
+        if (hipGetDevice(&dev) != hipSuccess ||
+            hipDeviceGetAttribute(&cus, hipDeviceAttributeMultiprocessorCount, dev) != hipSuccess ||
+            cus <= 0)
+            cus = 256;
+        slots = 2 * cus;
+    }
+    return slots;
+}
+
+// Split the reduction over K when the output tiles alone leave the chip
+// idle: weight gradients of the C x C and 4C x C layers (K = B*T, few tiles),
+// and long-K forward / input-gradient products whose tile count falls
+// between one and two rounds of resident workgroups (two splits make whole
+// rounds).
+int choose_splits(int op, int epi, int M, int N, int K) {
+    if ((N % 4) != 0) return 1;
     const int tiles = cdiv(M, BM) * cdiv(N, BN);
-    const int target = 768;
-    if (tiles >= target / 2) return 1;
-    int splits = cdiv(target, tiles);
-    const int max_splits = K / (BK * 4);  // at least 4 reduction steps each
-    if (splits > max_splits) splits = max_splits;
-    if (splits < 1) splits = 1;
-    return splits;
+    if (op == GEMM_TN) {
+        if (epi != EPI_ACCUM && epi != EPI_STORE) return 1;
+        const int target = 768;
+        if (tiles >= target / 2) return 1;
+        int splits = cdiv(target, tiles);
+        const int max_splits = K / (BK * 4);  // at least 4 reduction steps each
+        if (splits > max_splits) splits = max_splits;
+        return splits < 1 ? 1 : splits;
+    }
+    if (epi != EPI_STORE && epi != EPI_RESID) return 1;
+    const int slots = resident_slots();
+    const bool whole_rounds = tiles > slots && tiles < 2 * slots && (2 * tiles) % slots == 0;
+    // measured: pays for the long-K forward products and the LM-head dX only
+    const int min_k = op == GEMM_NT ? 2048 : 8192;
+    return whole_rounds && K >= min_k ? 2 : 1;
 }
 
 int split_chunk(int K, int splits) {
@@ -378,30 +399,50 @@ hipError_t launch(hipStream_t s, const GemmArgs& a, int splits, float* ws) {
 
 }  // namespace
 
-size_t gemm_workspace_bytes(int op, int M, int N, int K) {
-    const int splits = choose_splits(op, M, N, K);
+size_t gemm_workspace_bytes(int op, int epi, int M, int N, int K) {
+    const int splits = choose_splits(op, epi, M, N, K);
     if (splits <= 1) return 0;
     const int chunk = split_chunk(K, splits);
     const int nz = cdiv(K, chunk);
     return (size_t)nz * M * N * sizeof(float);
 }
 
+template <int OP>
+hipError_t launch_split(hipStream_t s, const GemmArgs& a, int splits, float* ws) {
+    hipError_t e = launch<OP, EPI_PARTIAL>(s, a, splits, ws);
+    if (e != hipSuccess) return e;
+    const int nz = cdiv(a.K, split_chunk(a.K, splits));
+    const int64_t n4 = (int64_t)a.M * (a.N / 4);
+    const int blocks = (int)std::min<int64_t>((n4 + 255) / 256, 4096);
+    switch (a.epi) {
+        case EPI_STORE:
+            hipLaunchKernelGGL(splitk_reduce_kernel<EPI_STORE>, dim3(blocks), dim3(256), 0, s, a,
+                               ws, nz);
+            break;
+        case EPI_RESID:
+            hipLaunchKernelGGL(splitk_reduce_kernel<EPI_RESID>, dim3(blocks), dim3(256), 0, s, a,
+                               ws, nz);
+            break;
+        case EPI_ACCUM:
+            hipLaunchKernelGGL(splitk_reduce_kernel<EPI_ACCUM>, dim3(blocks), dim3(256), 0, s, a,
+                               ws, nz);
+            break;
+        default: return hipErrorInvalidValue;
+    }
+    return hipGetLastError();
+}
+
 hipError_t gemm(hipStream_t s, const GemmArgs& a, float* ws, size_t ws_bytes) {
     if (a.M <= 0 || a.N <= 0) return hipSuccess;
-    int splits = choose_splits(a.op, a.M, a.N, a.K);
-    if (splits > 1 && gemm_workspace_bytes(a.op, a.M, a.N, a.K) > ws_bytes) splits = 1;
+    int splits = choose_splits(a.op, a.epi, a.M, a.N, a.K);
+    if (splits > 1 && gemm_workspace_bytes(a.op, a.epi, a.M, a.N, a.K) > ws_bytes) splits = 1;
     if (splits > 1) {
-        // only weight gradients are split; they store or accumulate
-        if (a.epi != EPI_ACCUM && a.epi != EPI_STORE) return hipErrorInvalidValue;
-        hipError_t e = launch<GEMM_TN, EPI_PARTIAL>(s, a, splits, ws);
-        if (e != hipSuccess) return e;
-        const int chunk = split_chunk(a.K, splits);
-        const int nz = cdiv(a.K, chunk);
-        const int64_t n4 = (int64_t)a.M * (a.N / 4);
-        int blocks = (int)std::min<int64_t>((n4 + 255) / 256, 4096);
-        hipLaunchKernelGGL(splitk_reduce_kernel, dim3(blocks), dim3(256), 0, s, a.C, a.ldc,
-                           ws, nz, a.M, a.N, a.epi == EPI_ACCUM ? 1 : 0);
-        return hipGetLastError();
+        switch (a.op) {
+            case GEMM_NT: return launch_split<GEMM_NT>(s, a, splits, ws);
+            case GEMM_NN: return launch_split<GEMM_NN>(s, a, splits, ws);
+            case GEMM_TN: return launch_split<GEMM_TN>(s, a, splits, ws);
+            default: return hipErrorInvalidValue;
+        }
     }
     switch (a.op) {
         case GEMM_NT:

@@ -38,7 +38,7 @@ struct GemmArgs {
 };
 
 // Workspace bytes a call may need for split-K partial sums.
-size_t gemm_workspace_bytes(int op, int M, int N, int K);
+size_t gemm_workspace_bytes(int op, int epi, int M, int N, int K);
 hipError_t gemm(hipStream_t s, const GemmArgs& a, float* workspace,
                 size_t workspace_bytes);
 

@@ -150,11 +150,20 @@ struct Layout {
         attn_d = take((size_t)M * NH * f);
         ln_part = take(gk::layernorm_partials_floats(M, C) * f);
         bias_part = take(gk::bias_partials_floats(M, 4 * C) * f);
+        // the largest split-K workspace over every matmul of the step
         gemm_ws_bytes = 0;
+        auto need = [&](int op, int epi, int m, int n, int k) {
+            gemm_ws_bytes = std::max(gemm_ws_bytes, gk::gemm_workspace_bytes(op, epi, m, n, k));
+        };
         const int outs[4][2] = {{3 * C, C}, {C, C}, {4 * C, C}, {C, 4 * C}};
-        for (auto& o : outs)
-            gemm_ws_bytes = std::max(gemm_ws_bytes, gk::gemm_workspace_bytes(gk::GEMM_TN, o[0], o[1], M));
-        gemm_ws_bytes = std::max(gemm_ws_bytes, gk::gemm_workspace_bytes(gk::GEMM_TN, V, C, M));
+        for (auto& o : outs) need(gk::GEMM_TN, gk::EPI_ACCUM, o[0], o[1], M);
+        need(gk::GEMM_TN, gk::EPI_ACCUM, V, C, M);
+        for (int k : {C, 3 * C, 4 * C}) {
+            need(gk::GEMM_NT, gk::EPI_RESID, M, C, k);
+            need(gk::GEMM_NN, gk::EPI_STORE, M, C, k);
+        }
+        need(gk::GEMM_NT, gk::EPI_STORE, M, 3 * C, C);
+        need(gk::GEMM_NN, gk::EPI_STORE, M, C, V);
         gemm_ws = take(gemm_ws_bytes);
         keys = take((size_t)n_pow2 * sizeof(uint32_t));
         tokens = take((size_t)M * sizeof(int32_t));
