@@ -24,6 +24,7 @@ sys.path.insert(0, ROOT)
 
 WORKLOAD = "gpt2_124m_b16t1024"
 MFMA_FP32_PEAK_TFLOPS = 157.3
+MFMA_BF16_PEAK_TFLOPS = 2500.0
 HBM_PEAK_GBS = 8000.0
 
 
@@ -33,6 +34,8 @@ def parse():
     ap.add_argument("--steps", type=int, default=20)
     ap.add_argument("--warmup", type=int, default=3)
     ap.add_argument("--no-cpu-baseline", action="store_true")
+    ap.add_argument("--precision", choices=["fp32", "bf16"], default="fp32",
+                    help="fp32 (the headline workload) or the bf16 mixed-precision model")
     ap.add_argument("--no-kernel-timing", action="store_true",
                     help="do not record per-launch HIP events in the timed steps")
     return ap.parse_args()
@@ -73,7 +76,9 @@ def main():
     B, T = c["B"], c["T"]
     params = synth.init_params(c["L"], c["C"], c["V"], c["maxT"])
     tok, tgt = synth.token_stream(B, T, c["V"])
-    m = gpt2.Model(c["L"], c["C"], c["NH"], c["V"], c["maxT"], B, T)
+    bf16 = args.precision == "bf16"
+    m = gpt2.Model(c["L"], c["C"], c["NH"], c["V"], c["maxT"], B, T,
+                   precision=gpt2.GPT2_BF16_MIXED if bf16 else gpt2.GPT2_FP32)
     m.set_params(params)
     dtok = torch.tensor(tok, dtype=torch.int32, device="cuda")
     dtgt = torch.tensor(tgt, dtype=torch.int32, device="cuda")
@@ -114,15 +119,17 @@ def main():
     m.close()
 
     roofline = None
+    peak = MFMA_BF16_PEAK_TFLOPS if bf16 else MFMA_FP32_PEAK_TFLOPS
     if kc:
         g = kc["gemm"]
         n = max(g["launches"], 1)
         avg_s = g["ms"] / n / 1000.0
         achieved = (g["flops"] / n) / avg_s / 1e12 if avg_s > 0 else 0.0
         roofline = {"bound": "mfma", "achieved": round(achieved, 2),
-                    "peak": MFMA_FP32_PEAK_TFLOPS, "unit": "TFLOP/s",
-                    "frac": round(achieved / MFMA_FP32_PEAK_TFLOPS, 4), "traffic": None,
-                    "kernel": "gemm (all fp32 MFMA matmul launches of the step)",
+                    "peak": peak, "unit": "TFLOP/s",
+                    "frac": round(achieved / peak, 4), "traffic": None,
+                    "kernel": "gemm (all %s MFMA matmul launches of the step)"
+                              % ("bf16" if bf16 else "fp32"),
                     "launches_per_step": n // args.steps,
                     "avg_launch_ms": round(g["ms"] / n, 4)}
         print("per-class kernel time per step:", file=sys.stderr)
@@ -137,7 +144,8 @@ def main():
         print(f"  {'sum':11s} {total:9.3f} ms of {ms:.3f} ms per step", file=sys.stderr)
 
     out = {
-        "metric": "training tokens/sec (fwd+bwd+AdamW), GPT-2 124M B16 T1024 at 1 GPU",
+        "metric": "training tokens/sec (fwd+bwd+AdamW), GPT-2 124M B16 T1024 at 1 GPU"
+                  + ("" if not bf16 else " (bf16 mixed precision)"),
         "value": round(tokens_per_s, 1),
         "unit": "tokens/s",
         "n_gpus": 1,
@@ -147,9 +155,10 @@ def main():
         "higher_is_better": True,
         "scaling": "weak",
         "vs_baseline": None,
-        "dtype": "f32",
+        "dtype": "bf16" if bf16 else "f32",
         "data": "synthetic (seeded uniform int32 token ids, GPT-2 init N(0,0.02))",
-        "config": {"workload": "GPT-2 124M training step, B=16 T=1024 fp32",
+        "config": {"workload": "GPT-2 124M training step, B=16 T=1024 "
+                               + ("bf16 mixed precision" if bf16 else "fp32"),
                    "global_batch": B, "seq_len": T, "layers": c["L"], "channels": c["C"],
                    "heads": c["NH"], "vocab": c["V"], "parallelism": "single GPU"},
         "roofline": roofline,
@@ -157,7 +166,7 @@ def main():
         "kernel_ms_per_step": {k: round(v["ms"] / args.steps, 3) for k, v in kc.items()},
         "loss_first_last": [round(losses[0], 5), round(losses[-1], 5)],
     }
-    if not args.no_cpu_baseline:
+    if not args.no_cpu_baseline and not bf16:
         out["cpu_baseline"] = cpu_baseline(c, params, tok, tgt)
     print(json.dumps(out), flush=True)
 

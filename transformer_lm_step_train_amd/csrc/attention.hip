@@ -59,13 +59,13 @@ struct TileRegs {
     static constexpr int C4 = HS / 4;
     static constexpr int PER = AT * C4 / 256;  // float4 per thread
     float4 v[PER];
-    __device__ __forceinline__ void load(const float* __restrict__ base, int64_t ld, int r0,
-                                         int T) {
+    template <class E>
+    __device__ __forceinline__ void load(const E* __restrict__ base, int64_t ld, int r0, int T) {
 #pragma unroll
         for (int i = 0; i < PER; i++) {
             const int idx = threadIdx.x + 256 * i;
             const int r = idx / C4, c = (idx - r * C4) * 4;
-            v[i] = r0 + r < T ? ld4(base + (int64_t)(r0 + r) * ld + c)
+            v[i] = r0 + r < T ? Act<E>::ld(base + (int64_t)(r0 + r) * ld + c)
                               : make_float4(0.f, 0.f, 0.f, 0.f);
         }
     }
@@ -93,24 +93,24 @@ struct TileRegs {
 
 // Write a lane's 32-row accumulator block(s) of one row: the lane holds
 // columns d*32 + 8*(e/4) + 4*g + e%4 of its row, i.e. float4 runs.
-template <int HS, int NDB>
-__device__ __forceinline__ void store_row(float* row, const floatx16 (&acc)[NDB], int g,
-                                          float mul) {
+template <int HS, int NDB, class E>
+__device__ __forceinline__ void store_row(E* row, const floatx16 (&acc)[NDB], int g, float mul) {
 #pragma unroll
     for (int d = 0; d < NDB; d++)
 #pragma unroll
         for (int c = 0; c < 4; c++) {
             const int dim0 = d * 32 + 8 * c + 4 * g;
             if (dim0 < HS)
-                st4(row + dim0, make_float4(acc[d][4 * c] * mul, acc[d][4 * c + 1] * mul,
-                                            acc[d][4 * c + 2] * mul, acc[d][4 * c + 3] * mul));
+                Act<E>::st(row + dim0,
+                           make_float4(acc[d][4 * c] * mul, acc[d][4 * c + 1] * mul,
+                                       acc[d][4 * c + 2] * mul, acc[d][4 * c + 3] * mul));
         }
 }
 
-template <int HS>
-__global__ __launch_bounds__(256, 2) void attn_fwd_kernel(float* __restrict__ out,
+template <int HS, class E>
+__global__ __launch_bounds__(256, 2) void attn_fwd_kernel(E* __restrict__ out,
                                                           float* __restrict__ lse,
-                                                          const float* __restrict__ qkv, int T,
+                                                          const E* __restrict__ qkv, int T,
                                                           int C, int NH, float qscale) {
     constexpr int LD = HS + 4, HALF = HS / 2, NDB = (HS + 31) / 32;
     constexpr int LDT = AT + 4;        // V^T row stride (keys)
@@ -135,7 +135,7 @@ __global__ __launch_bounds__(256, 2) void attn_fwd_kernel(float* __restrict__ ou
     const int lane = threadIdx.x & 63, wave = threadIdx.x >> 6;
     const int li = lane & 31, g = lane >> 5;
     const int64_t ld = 3 * (int64_t)C;
-    const float* qbase = qkv + (int64_t)b * T * ld + h * HS;
+    const E* qbase = qkv + (int64_t)b * T * ld + h * HS;
     const int q0 = qb * AQ;
     const int qw = q0 + wave * 32;
     const int q = qw + li;
@@ -146,7 +146,7 @@ __global__ __launch_bounds__(256, 2) void attn_fwd_kernel(float* __restrict__ ou
 #pragma unroll
     for (int s = 0; s < HALF; s += 4) {
         float4 x = make_float4(0.f, 0.f, 0.f, 0.f);
-        if (q < T) x = ld4(qbase + (int64_t)q * ld + g * HALF + s);
+        if (q < T) x = Act<E>::ld(qbase + (int64_t)q * ld + g * HALF + s);
         qr[s] = x.x * qscale;
         qr[s + 1] = x.y * qscale;
         qr[s + 2] = x.z * qscale;
@@ -255,10 +255,10 @@ __global__ __launch_bounds__(256, 2) void attn_fwd_kernel(float* __restrict__ ou
 }
 
 // dQ, and D = rowsum(dout * out) for the key/value kernel.
-template <int HS>
+template <int HS, class E>
 __global__ __launch_bounds__(256, 2) void attn_bwd_dq_kernel(
-    float* __restrict__ dqkv, float* __restrict__ Dout, const float* __restrict__ dout,
-    const float* __restrict__ out, const float* __restrict__ qkv, const float* __restrict__ lse,
+    E* __restrict__ dqkv, float* __restrict__ Dout, const E* __restrict__ dout,
+    const E* __restrict__ out, const E* __restrict__ qkv, const float* __restrict__ lse,
     int T, int C, int NH, float qscale, float scale) {
     constexpr int LD = HS + 4, HALF = HS / 2, NDB = (HS + 31) / 32;
     __shared__ __attribute__((aligned(16))) float ks[2][AT * LD];
@@ -272,9 +272,9 @@ __global__ __launch_bounds__(256, 2) void attn_bwd_dq_kernel(
     const int lane = threadIdx.x & 63, wave = threadIdx.x >> 6;
     const int li = lane & 31, g = lane >> 5;
     const int64_t ld = 3 * (int64_t)C;
-    const float* qbase = qkv + (int64_t)b * T * ld + h * HS;
-    const float* dobase = dout + (int64_t)b * T * C + h * HS;
-    const float* obase = out + (int64_t)b * T * C + h * HS;
+    const E* qbase = qkv + (int64_t)b * T * ld + h * HS;
+    const E* dobase = dout + (int64_t)b * T * C + h * HS;
+    const E* obase = out + (int64_t)b * T * C + h * HS;
     const int q0 = qb * AQ;
     const int qw = q0 + wave * 32;
     const int q = qw + li;
@@ -287,9 +287,9 @@ __global__ __launch_bounds__(256, 2) void attn_bwd_dq_kernel(
     for (int s = 0; s < HALF; s += 4) {
         float4 x = make_float4(0.f, 0.f, 0.f, 0.f), y = x, z = x;
         if (q < T) {
-            x = ld4(qbase + (int64_t)q * ld + g * HALF + s);
-            y = ld4(dobase + (int64_t)q * C + g * HALF + s);
-            z = ld4(obase + (int64_t)q * C + g * HALF + s);
+            x = Act<E>::ld(qbase + (int64_t)q * ld + g * HALF + s);
+            y = Act<E>::ld(dobase + (int64_t)q * C + g * HALF + s);
+            z = Act<E>::ld(obase + (int64_t)q * C + g * HALF + s);
         }
         qr[s] = x.x * qscale;
         qr[s + 1] = x.y * qscale;
@@ -385,9 +385,9 @@ __global__ __launch_bounds__(256, 2) void attn_bwd_dq_kernel(
     if (q < T) store_row<HS, NDB>(dqkv + ((int64_t)b * T + q) * ld + h * HS, dq, g, scale);
 }
 
-template <int HS>
+template <int HS, class E>
 __global__ __launch_bounds__(256, 2) void attn_bwd_dkdv_kernel(
-    float* __restrict__ dqkv, const float* __restrict__ dout, const float* __restrict__ qkv,
+    E* __restrict__ dqkv, const E* __restrict__ dout, const E* __restrict__ qkv,
     const float* __restrict__ lse, const float* __restrict__ D, int T, int C, int NH,
     float qscale, float scale) {
     constexpr int LD = HS + 4, HALF = HS / 2, NDB = (HS + 31) / 32;
@@ -403,8 +403,8 @@ __global__ __launch_bounds__(256, 2) void attn_bwd_dkdv_kernel(
     const int lane = threadIdx.x & 63, wave = threadIdx.x >> 6;
     const int li = lane & 31, g = lane >> 5;
     const int64_t ld = 3 * (int64_t)C;
-    const float* qbase = qkv + (int64_t)b * T * ld + h * HS;
-    const float* dobase = dout + (int64_t)b * T * C + h * HS;
+    const E* qbase = qkv + (int64_t)b * T * ld + h * HS;
+    const E* dobase = dout + (int64_t)b * T * C + h * HS;
     const int64_t srow = ((int64_t)b * NH + h) * T;
     const int kw = kb0 * AQ + wave * 32;  // first key of this wave
     const int key = kw + li;
@@ -414,8 +414,8 @@ __global__ __launch_bounds__(256, 2) void attn_bwd_dkdv_kernel(
     for (int s = 0; s < HALF; s += 4) {
         float4 x = make_float4(0.f, 0.f, 0.f, 0.f), y = x;
         if (key < T) {
-            x = ld4(qbase + C + (int64_t)key * ld + g * HALF + s);
-            y = ld4(qbase + 2 * C + (int64_t)key * ld + g * HALF + s);
+            x = Act<E>::ld(qbase + C + (int64_t)key * ld + g * HALF + s);
+            y = Act<E>::ld(qbase + 2 * C + (int64_t)key * ld + g * HALF + s);
         }
         kr[s] = x.x;
         kr[s + 1] = x.y;
@@ -523,58 +523,76 @@ __global__ __launch_bounds__(256, 2) void attn_bwd_dkdv_kernel(
         __syncthreads();
     }
     if (key < T) {
-        float* row = dqkv + ((int64_t)b * T + key) * ld + h * HS;
+        E* row = dqkv + ((int64_t)b * T + key) * ld + h * HS;
         store_row<HS, NDB>(row + C, dk, g, scale);
         store_row<HS, NDB>(row + 2 * C, dv, g, 1.f);
     }
 }
 
-template <int HS>
-hipError_t fwd_hs(hipStream_t s, float* out, float* lse, const float* qkv, int B, int T,
-                  int C, int NH) {
+template <int HS, class E>
+hipError_t fwd_hs(hipStream_t s, E* out, float* lse, const E* qkv, int B, int T, int C,
+                  int NH) {
     const int nqb = (T + AQ - 1) / AQ;
     const float qscale = LOG2E / sqrtf((float)HS);
-    hipLaunchKernelGGL((attn_fwd_kernel<HS>), dim3(B * NH * nqb), dim3(256), 0, s, out, lse,
+    hipLaunchKernelGGL((attn_fwd_kernel<HS, E>), dim3(B * NH * nqb), dim3(256), 0, s, out, lse,
                        qkv, T, C, NH, qscale);
     return hipGetLastError();
 }
 
-template <int HS>
-hipError_t bwd_hs(hipStream_t s, float* dqkv, float* D, const float* dout, const float* qkv,
-                  const float* out, const float* lse, int B, int T, int C, int NH) {
+template <int HS, class E>
+hipError_t bwd_hs(hipStream_t s, E* dqkv, float* D, const E* dout, const E* qkv, const E* out,
+                  const float* lse, int B, int T, int C, int NH) {
     const int nb = (T + AQ - 1) / AQ;
     const float scale = 1.0f / sqrtf((float)HS);
     const float qscale = LOG2E * scale;
-    hipLaunchKernelGGL((attn_bwd_dq_kernel<HS>), dim3(B * NH * nb), dim3(256), 0, s, dqkv, D,
+    hipLaunchKernelGGL((attn_bwd_dq_kernel<HS, E>), dim3(B * NH * nb), dim3(256), 0, s, dqkv, D,
                        dout, out, qkv, lse, T, C, NH, qscale, scale);
-    hipLaunchKernelGGL((attn_bwd_dkdv_kernel<HS>), dim3(B * NH * nb), dim3(256), 0, s, dqkv,
+    hipLaunchKernelGGL((attn_bwd_dkdv_kernel<HS, E>), dim3(B * NH * nb), dim3(256), 0, s, dqkv,
                        dout, qkv, lse, D, T, C, NH, qscale, scale);
     return hipGetLastError();
 }
 
-}  // namespace
-
-hipError_t attention_forward(hipStream_t s, float* out, float* lse, const float* qkv, int B,
-                             int T, int C, int NH) {
-    if (B <= 0 || T <= 0) return hipSuccess;
+template <class E>
+hipError_t forward_t(hipStream_t s, E* out, float* lse, const E* qkv, int B, int T, int C,
+                     int NH) {
     switch (C / NH) {
-        case 16: return fwd_hs<16>(s, out, lse, qkv, B, T, C, NH);
-        case 32: return fwd_hs<32>(s, out, lse, qkv, B, T, C, NH);
-        case 64: return fwd_hs<64>(s, out, lse, qkv, B, T, C, NH);
+        case 16: return fwd_hs<16, E>(s, out, lse, qkv, B, T, C, NH);
+        case 32: return fwd_hs<32, E>(s, out, lse, qkv, B, T, C, NH);
+        case 64: return fwd_hs<64, E>(s, out, lse, qkv, B, T, C, NH);
         default: return hipErrorInvalidValue;
     }
 }
 
-hipError_t attention_backward(hipStream_t s, float* dqkv, float* dpre, const float* dout,
-                              const float* qkv, const float* out, const float* lse, int B,
-                              int T, int C, int NH) {
-    if (B <= 0 || T <= 0) return hipSuccess;
+template <class E>
+hipError_t backward_t(hipStream_t s, E* dqkv, float* D, const E* dout, const E* qkv,
+                      const E* out, const float* lse, int B, int T, int C, int NH) {
     switch (C / NH) {
-        case 16: return bwd_hs<16>(s, dqkv, dpre, dout, qkv, out, lse, B, T, C, NH);
-        case 32: return bwd_hs<32>(s, dqkv, dpre, dout, qkv, out, lse, B, T, C, NH);
-        case 64: return bwd_hs<64>(s, dqkv, dpre, dout, qkv, out, lse, B, T, C, NH);
+        case 16: return bwd_hs<16, E>(s, dqkv, D, dout, qkv, out, lse, B, T, C, NH);
+        case 32: return bwd_hs<32, E>(s, dqkv, D, dout, qkv, out, lse, B, T, C, NH);
+        case 64: return bwd_hs<64, E>(s, dqkv, D, dout, qkv, out, lse, B, T, C, NH);
         default: return hipErrorInvalidValue;
     }
+}
+
+}  // namespace
+
+hipError_t attention_forward(hipStream_t s, void* out, float* lse, const void* qkv, int B, int T,
+                             int C, int NH, int bf16) {
+    if (B <= 0 || T <= 0) return hipSuccess;
+    if (bf16)
+        return forward_t<uint16_t>(s, (uint16_t*)out, lse, (const uint16_t*)qkv, B, T, C, NH);
+    return forward_t<float>(s, (float*)out, lse, (const float*)qkv, B, T, C, NH);
+}
+
+hipError_t attention_backward(hipStream_t s, void* dqkv, float* dpre, const void* dout,
+                              const void* qkv, const void* out, const float* lse, int B, int T,
+                              int C, int NH, int bf16) {
+    if (B <= 0 || T <= 0) return hipSuccess;
+    if (bf16)
+        return backward_t<uint16_t>(s, (uint16_t*)dqkv, dpre, (const uint16_t*)dout,
+                                    (const uint16_t*)qkv, (const uint16_t*)out, lse, B, T, C, NH);
+    return backward_t<float>(s, (float*)dqkv, dpre, (const float*)dout, (const float*)qkv,
+                             (const float*)out, lse, B, T, C, NH);
 }
 
 }  // namespace gk

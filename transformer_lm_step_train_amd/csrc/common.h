@@ -57,3 +57,43 @@ __device__ __forceinline__ int xcd_remap(int wg, int n) {
     int q = n >> 3;
     return wg < (q << 3) ? (wg & 7) * q + (wg >> 3) : wg;
 }
+
+// ---- bf16 storage ----------------------------------------------------------
+// bf16 is kept as raw uint16_t bits: the top half of an IEEE fp32.  Rounding
+// from fp32 is to nearest, ties to even; NaN stays NaN.
+__device__ __forceinline__ float bf2f(uint32_t h) { return __uint_as_float(h << 16); }
+
+__device__ __forceinline__ uint16_t f2bf(float f) {
+    uint32_t u = __float_as_uint(f);
+    if ((u & 0x7fffffffu) > 0x7f800000u) return (uint16_t)((u >> 16) | 0x40u);
+    u += 0x7fffu + ((u >> 16) & 1u);
+    return (uint16_t)(u >> 16);
+}
+
+// Loads and stores of four consecutive activations as fp32, whatever the
+// storage type (float or bf16 bits).
+template <class T>
+struct Act;
+
+template <>
+struct Act<float> {
+    static __device__ __forceinline__ float4 ld(const float* p) { return ld4(p); }
+    static __device__ __forceinline__ void st(float* p, float4 v) { st4(p, v); }
+    static __device__ __forceinline__ float ld1(const float* p) { return *p; }
+    static __device__ __forceinline__ void st1(float* p, float v) { *p = v; }
+};
+
+template <>
+struct Act<uint16_t> {
+    static __device__ __forceinline__ float4 ld(const uint16_t* p) {
+        const uint2 u = *reinterpret_cast<const uint2*>(p);
+        return make_float4(bf2f(u.x & 0xffffu), bf2f(u.x >> 16), bf2f(u.y & 0xffffu),
+                           bf2f(u.y >> 16));
+    }
+    static __device__ __forceinline__ void st(uint16_t* p, float4 v) {
+        *reinterpret_cast<uint2*>(p) = make_uint2(f2bf(v.x) | ((uint32_t)f2bf(v.y) << 16),
+                                                  f2bf(v.z) | ((uint32_t)f2bf(v.w) << 16));
+    }
+    static __device__ __forceinline__ float ld1(const uint16_t* p) { return bf2f(*p); }
+    static __device__ __forceinline__ void st1(uint16_t* p, float v) { *p = f2bf(v); }
+};

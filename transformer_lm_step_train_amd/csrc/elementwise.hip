@@ -19,7 +19,8 @@
 namespace gk {
 namespace {
 
-__global__ __launch_bounds__(256) void encoder_fwd_kernel(float* __restrict__ out,
+template <class E>
+__global__ __launch_bounds__(256) void encoder_fwd_kernel(E* __restrict__ out,
                                                           const int32_t* __restrict__ tok,
                                                           const float* __restrict__ wte,
                                                           const float* __restrict__ wpe,
@@ -41,7 +42,7 @@ __global__ __launch_bounds__(256) void encoder_fwd_kernel(float* __restrict__ ou
         } else if (c == 0) {
             atomicOr(flag, 1);
         }
-        st4(out + bt * C + c, r);
+        Act<E>::st(out + bt * C + c, r);
     }
 }
 
@@ -83,9 +84,9 @@ __global__ __launch_bounds__(1024) void encoder_sort_kernel(uint32_t* __restrict
 
 // One wave per sorted position; the first position of each run of equal
 // tokens sums the run's gradient rows in position order into wte's row.
-template <int NCH>
+template <int NCH, class E>
 __global__ __launch_bounds__(256) void encoder_bwd_wte_kernel(float* __restrict__ dwte,
-                                                              const float* __restrict__ dx,
+                                                              const E* __restrict__ dx,
                                                               const uint32_t* __restrict__ keys,
                                                               int n, int C, int V,
                                                               int pos_bits) {
@@ -101,12 +102,12 @@ __global__ __launch_bounds__(256) void encoder_bwd_wte_kernel(float* __restrict_
 #pragma unroll
     for (int c = 0; c < NCH; c++) acc[c] = make_float4(0.f, 0.f, 0.f, 0.f);
     for (int j = i; j < n && (keys[j] >> pos_bits) == tok; j++) {
-        const float* row = dx + (int64_t)(keys[j] & pmask) * C;
+        const E* row = dx + (int64_t)(keys[j] & pmask) * C;
 #pragma unroll
         for (int c = 0; c < NCH; c++) {
             const int c4 = lane + 64 * c;
             if (c4 < C4) {
-                const float4 d = ld4(row + 4 * c4);
+                const float4 d = Act<E>::ld(row + 4 * c4);
                 acc[c].x += d.x;
                 acc[c].y += d.y;
                 acc[c].z += d.z;
@@ -130,8 +131,9 @@ __global__ __launch_bounds__(256) void encoder_bwd_wte_kernel(float* __restrict_
 }
 
 // dwpe[t] += sum over b of dx[b,t], b in order.
+template <class E>
 __global__ __launch_bounds__(256) void encoder_bwd_wpe_kernel(float* __restrict__ dwpe,
-                                                              const float* __restrict__ dx,
+                                                              const E* __restrict__ dx,
                                                               int B, int T, int C) {
     const int C4 = C >> 2;
     const int64_t i = blockIdx.x * (int64_t)blockDim.x + threadIdx.x;
@@ -139,7 +141,7 @@ __global__ __launch_bounds__(256) void encoder_bwd_wpe_kernel(float* __restrict_
     const int t = (int)(i / C4), c = (int)(i - (int64_t)t * C4) * 4;
     float4 s = make_float4(0.f, 0.f, 0.f, 0.f);
     for (int b = 0; b < B; b++) {
-        const float4 d = ld4(dx + ((int64_t)b * T + t) * C + c);
+        const float4 d = Act<E>::ld(dx + ((int64_t)b * T + t) * C + c);
         s.x += d.x;
         s.y += d.y;
         s.z += d.z;
@@ -159,8 +161,9 @@ __global__ __launch_bounds__(256) void encoder_bwd_wpe_kernel(float* __restrict_
 // four), then a second kernel adds the chunk partials in chunk order.
 constexpr int BIAS_ROWS = 64;
 
+template <class E>
 __global__ __launch_bounds__(256) void bias_partial_kernel(float* __restrict__ part,
-                                                           const float* __restrict__ dy, int M,
+                                                           const E* __restrict__ dy, int M,
                                                            int N, int64_t ld) {
     __shared__ float4 sh[4][64];
     const int lane = threadIdx.x & 63, wave = threadIdx.x >> 6;
@@ -170,7 +173,7 @@ __global__ __launch_bounds__(256) void bias_partial_kernel(float* __restrict__ p
     float4 s = make_float4(0.f, 0.f, 0.f, 0.f);
     if (col < N) {
         for (int r = r0 + wave; r < r1; r += 4) {
-            const float4 d = ld4(dy + (int64_t)r * ld + col);
+            const float4 d = Act<E>::ld(dy + (int64_t)r * ld + col);
             s.x += d.x;
             s.y += d.y;
             s.z += d.z;
@@ -246,11 +249,14 @@ __device__ __forceinline__ float adamw_one(float& p, float g, float& m, float& v
     return p;
 }
 
+// shadow (optional): bf16 copy of the updated parameters for the matmuls of
+// the mixed-precision model.
 __global__ __launch_bounds__(256) void adamw_kernel(float* __restrict__ p,
                                                     const float* __restrict__ g,
                                                     float* __restrict__ m, float* __restrict__ v,
-                                                    int64_t n, float lr, float b1, float b2,
-                                                    float eps, float wd, float bc1, float bc2) {
+                                                    uint16_t* __restrict__ shadow, int64_t n,
+                                                    float lr, float b1, float b2, float eps,
+                                                    float wd, float bc1, float bc2) {
     const int64_t n4 = n >> 2;
     const int64_t stride = (int64_t)gridDim.x * blockDim.x;
     for (int64_t i = blockIdx.x * (int64_t)blockDim.x + threadIdx.x; i < n4; i += stride) {
@@ -262,9 +268,19 @@ __global__ __launch_bounds__(256) void adamw_kernel(float* __restrict__ p,
         st4(p + 4 * i, pp);
         st4(m + 4 * i, mm);
         st4(v + 4 * i, vv);
+        if (shadow) Act<uint16_t>::st(shadow + 4 * i, pp);
     }
-    for (int64_t i = 4 * n4 + blockIdx.x * (int64_t)blockDim.x + threadIdx.x; i < n; i += stride)
+    for (int64_t i = 4 * n4 + blockIdx.x * (int64_t)blockDim.x + threadIdx.x; i < n; i += stride) {
         adamw_one(p[i], g[i], m[i], v[i], lr, b1, b2, eps, wd, bc1, bc2);
+        if (shadow) shadow[i] = f2bf(p[i]);
+    }
+}
+
+__global__ __launch_bounds__(256) void to_bf16_kernel(uint16_t* __restrict__ out,
+                                                      const float* __restrict__ in, int64_t n) {
+    const int64_t stride = (int64_t)gridDim.x * blockDim.x;
+    for (int64_t i = blockIdx.x * (int64_t)blockDim.x + threadIdx.x; i < n; i += stride)
+        out[i] = f2bf(in[i]);
 }
 
 inline unsigned grid_for(int64_t work, int per_block, unsigned cap) {
@@ -275,12 +291,17 @@ inline unsigned grid_for(int64_t work, int per_block, unsigned cap) {
 
 }  // namespace
 
-hipError_t encoder_forward(hipStream_t s, float* out, const int32_t* tok, const float* wte,
-                           const float* wpe, int B, int T, int C, int V, int* flag) {
+hipError_t encoder_forward(hipStream_t s, void* out, const int32_t* tok, const float* wte,
+                           const float* wpe, int B, int T, int C, int V, int* flag, int bf16) {
     const int64_t n = (int64_t)B * T * (C / 4);
     if (n <= 0) return hipSuccess;
-    hipLaunchKernelGGL(encoder_fwd_kernel, dim3(grid_for(n, 256, 65535)), dim3(256), 0, s, out,
-                       tok, wte, wpe, B, T, C, V, flag);
+    const dim3 grid(grid_for(n, 256, 65535));
+    if (bf16)
+        hipLaunchKernelGGL(encoder_fwd_kernel<uint16_t>, grid, dim3(256), 0, s, (uint16_t*)out,
+                           tok, wte, wpe, B, T, C, V, flag);
+    else
+        hipLaunchKernelGGL(encoder_fwd_kernel<float>, grid, dim3(256), 0, s, (float*)out, tok, wte,
+                           wpe, B, T, C, V, flag);
     return hipGetLastError();
 }
 
@@ -297,37 +318,51 @@ hipError_t encoder_sort(hipStream_t s, uint32_t* keys, const int32_t* tok, int n
     return hipGetLastError();
 }
 
-hipError_t encoder_backward(hipStream_t s, float* dwte, float* dwpe, const float* dx,
-                            const uint32_t* keys, int B, int T, int C, int V, int pos_bits) {
-    const int n = B * T;
-    if (n <= 0) return hipSuccess;
-    const int nch = (C + 255) / 256;
+template <class E>
+hipError_t encoder_backward_t(hipStream_t s, float* dwte, float* dwpe, const E* dx,
+                              const uint32_t* keys, int B, int T_, int C, int V, int pos_bits) {
+    const int n = B * T_;
     dim3 grid((n + 3) / 4), block(256);
-    switch (nch) {
-        case 1: hipLaunchKernelGGL(encoder_bwd_wte_kernel<1>, grid, block, 0, s, dwte, dx, keys, n, C, V, pos_bits); break;
-        case 2: hipLaunchKernelGGL(encoder_bwd_wte_kernel<2>, grid, block, 0, s, dwte, dx, keys, n, C, V, pos_bits); break;
-        case 3: hipLaunchKernelGGL(encoder_bwd_wte_kernel<3>, grid, block, 0, s, dwte, dx, keys, n, C, V, pos_bits); break;
-        case 4: hipLaunchKernelGGL(encoder_bwd_wte_kernel<4>, grid, block, 0, s, dwte, dx, keys, n, C, V, pos_bits); break;
+    switch ((C + 255) / 256) {
+        case 1: hipLaunchKernelGGL((encoder_bwd_wte_kernel<1, E>), grid, block, 0, s, dwte, dx, keys, n, C, V, pos_bits); break;
+        case 2: hipLaunchKernelGGL((encoder_bwd_wte_kernel<2, E>), grid, block, 0, s, dwte, dx, keys, n, C, V, pos_bits); break;
+        case 3: hipLaunchKernelGGL((encoder_bwd_wte_kernel<3, E>), grid, block, 0, s, dwte, dx, keys, n, C, V, pos_bits); break;
+        case 4: hipLaunchKernelGGL((encoder_bwd_wte_kernel<4, E>), grid, block, 0, s, dwte, dx, keys, n, C, V, pos_bits); break;
         default: return hipErrorInvalidValue;
     }
     hipError_t e = hipGetLastError();
     if (e != hipSuccess) return e;
-    const int64_t nw = (int64_t)T * (C / 4);
-    hipLaunchKernelGGL(encoder_bwd_wpe_kernel, dim3(grid_for(nw, 256, 1u << 30)), dim3(256), 0,
-                       s, dwpe, dx, B, T, C);
+    const int64_t nw = (int64_t)T_ * (C / 4);
+    hipLaunchKernelGGL(encoder_bwd_wpe_kernel<E>, dim3(grid_for(nw, 256, 1u << 30)), dim3(256),
+                       0, s, dwpe, dx, B, T_, C);
     return hipGetLastError();
+}
+
+hipError_t encoder_backward(hipStream_t s, float* dwte, float* dwpe, const void* dx,
+                            const uint32_t* keys, int B, int T, int C, int V, int pos_bits,
+                            int bf16) {
+    if (B * T <= 0) return hipSuccess;
+    if (bf16)
+        return encoder_backward_t<uint16_t>(s, dwte, dwpe, (const uint16_t*)dx, keys, B, T, C, V,
+                                            pos_bits);
+    return encoder_backward_t<float>(s, dwte, dwpe, (const float*)dx, keys, B, T, C, V, pos_bits);
 }
 
 size_t bias_partials_floats(int M, int N) {
     return (size_t)((M + BIAS_ROWS - 1) / BIAS_ROWS) * N;
 }
 
-hipError_t bias_grad(hipStream_t s, float* db, float* part, const float* dy, int M, int N,
-                     int64_t ld) {
+hipError_t bias_grad(hipStream_t s, float* db, float* part, const void* dy, int M, int N,
+                     int64_t ld, int bf16) {
     if (M <= 0 || N <= 0) return hipSuccess;
     const int nchunks = (M + BIAS_ROWS - 1) / BIAS_ROWS;
     dim3 grid((N / 4 + 63) / 64, nchunks);
-    hipLaunchKernelGGL(bias_partial_kernel, grid, dim3(256), 0, s, part, dy, M, N, ld);
+    if (bf16)
+        hipLaunchKernelGGL(bias_partial_kernel<uint16_t>, grid, dim3(256), 0, s, part,
+                           (const uint16_t*)dy, M, N, ld);
+    else
+        hipLaunchKernelGGL(bias_partial_kernel<float>, grid, dim3(256), 0, s, part,
+                           (const float*)dy, M, N, ld);
     hipError_t e = hipGetLastError();
     if (e != hipSuccess) return e;
     return colsum_add(s, db, db, N, part, nchunks, N);
@@ -348,11 +383,18 @@ hipError_t fill_zero(hipStream_t s, float* p, int64_t n) {
     return hipGetLastError();
 }
 
-hipError_t adamw(hipStream_t s, float* p, const float* g, float* m, float* v, int64_t n,
-                 float lr, float b1, float b2, float eps, float wd, float bc1, float bc2) {
+hipError_t adamw(hipStream_t s, float* p, const float* g, float* m, float* v, uint16_t* shadow,
+                 int64_t n, float lr, float b1, float b2, float eps, float wd, float bc1,
+                 float bc2) {
     if (n <= 0) return hipSuccess;
     hipLaunchKernelGGL(adamw_kernel, dim3(grid_for(n / 4 + 1, 256, 8192)), dim3(256), 0, s, p,
-                       g, m, v, n, lr, b1, b2, eps, wd, bc1, bc2);
+                       g, m, v, shadow, n, lr, b1, b2, eps, wd, bc1, bc2);
+    return hipGetLastError();
+}
+
+hipError_t to_bf16(hipStream_t s, uint16_t* out, const float* in, int64_t n) {
+    if (n <= 0) return hipSuccess;
+    hipLaunchKernelGGL(to_bf16_kernel, dim3(grid_for(n, 256, 8192)), dim3(256), 0, s, out, in, n);
     return hipGetLastError();
 }
 

@@ -1,0 +1,416 @@
+// bf16 matrix multiply with fp32 accumulation on the CDNA4 matrix cores
+// (v_mfma_f32_32x32x16_bf16), for the mixed-precision model: activations and
+// weight copies in bf16, every sum in fp32 (ujoy.net article "徒手用 1000 行
+// C 语言实现", section "用C语言实现LLM": the matmul layer; the reduced-precision
+// extension is named by yinghuohong.cn, section "脚动完成每一个层前向/反向流传").
+//
+// Same operand conventions and tiling as the fp32 kernel: 128x128 output tile
+// per 256-thread workgroup, 64x64 per wave (2x2 blocks of the 32x32 MFMA), a
+// reduction step of 64 staged through two LDS buffers with a two-deep
+// register prefetch.  In LDS every operand is stored [row][k] (72 bf16 per
+// row), so each MFMA operand (8 consecutive k of one row) is one 16-byte
+// read.  Operands whose free index is contiguous in HBM are loaded as 8 rows
+// of k by 4 columns per thread and transposed in registers before the LDS
+// store.  Outputs are bf16 activations (with the fused bias, residual, GELU
+// or GELU-derivative epilogues) or fp32 weight gradients (+=).
+#include <algorithm>
+#include <type_traits>
+
+#include "common.h"
+#include "kernels.h"
+
+namespace gk {
+namespace {
+
+constexpr int BM = 128, BN = 128, BK = 64, NTHR = 256;
+constexpr int LDH = BK + 8;       // LDS row stride, bf16 elements (144 bytes)
+constexpr int EPI_PARTIAL = 100;  // internal: fp32 split-K partial sums
+typedef __bf16 bf16x8 __attribute__((ext_vector_type(8)));
+
+__device__ __forceinline__ floatx16 mfma(uint4 a, uint4 b, floatx16 c) {
+    return __builtin_amdgcn_mfma_f32_32x32x16_bf16(__builtin_bit_cast(bf16x8, a),
+                                                   __builtin_bit_cast(bf16x8, b), c, 0, 0, 0);
+}
+
+template <bool KC>
+struct TileH;
+
+// Reduction index contiguous: element (r, k) at g[r*ld + k].  Thread loads
+// 8 consecutive k of one row (16 bytes).
+template <>
+struct TileH<true> {
+    static constexpr int ELEMS = 128 * LDH;
+    uint4 v[4];
+    template <bool CHECK>
+    __device__ __forceinline__ void load(const uint16_t* __restrict__ g, int64_t ld, int r0,
+                                         int R, int k0, int K) {
+#pragma unroll
+        for (int i = 0; i < 4; i++) {
+            const int idx = threadIdx.x + NTHR * i;
+            const int r = r0 + (idx >> 3);
+            const int k = k0 + (idx & 7) * 8;
+            const uint16_t* p = g + (int64_t)r * ld + k;
+            if (!CHECK) {
+                v[i] = *reinterpret_cast<const uint4*>(p);
+            } else {
+                uint16_t e[8];
+#pragma unroll
+                for (int j = 0; j < 8; j++) e[j] = (r < R && k + j < K) ? p[j] : (uint16_t)0;
+                v[i] = make_uint4(e[0] | ((uint32_t)e[1] << 16), e[2] | ((uint32_t)e[3] << 16),
+                                  e[4] | ((uint32_t)e[5] << 16), e[6] | ((uint32_t)e[7] << 16));
+            }
+        }
+    }
+    __device__ __forceinline__ void store(uint16_t* s) const {
+#pragma unroll
+        for (int i = 0; i < 4; i++) {
+            const int idx = threadIdx.x + NTHR * i;
+            *reinterpret_cast<uint4*>(s + (idx >> 3) * LDH + (idx & 7) * 8) = v[i];
+        }
+    }
+};
+
+// Free index contiguous: element (r, k) at g[k*ld + r].  Thread loads 4
+// consecutive rows at each of 8 consecutive k (8 bytes each) and stores the 4
+// rows' 8-k runs after a register transpose.
+template <>
+struct TileH<false> {
+    static constexpr int ELEMS = 128 * LDH;
+    uint2 v[8];
+    template <bool CHECK>
+    __device__ __forceinline__ void load(const uint16_t* __restrict__ g, int64_t ld, int r0,
+                                         int R, int k0, int K) {
+        const int t = threadIdx.x;
+        const int r = r0 + (t & 31) * 4;
+        const int kb = k0 + (t >> 5) * 8;
+#pragma unroll
+        for (int i = 0; i < 8; i++) {
+            const int k = kb + i;
+            const uint16_t* p = g + (int64_t)k * ld + r;
+            if (!CHECK) {
+                v[i] = *reinterpret_cast<const uint2*>(p);
+            } else {
+                uint16_t e[4];
+#pragma unroll
+                for (int j = 0; j < 4; j++) e[j] = (k < K && r + j < R) ? p[j] : (uint16_t)0;
+                v[i] = make_uint2(e[0] | ((uint32_t)e[1] << 16), e[2] | ((uint32_t)e[3] << 16));
+            }
+        }
+    }
+    __device__ __forceinline__ void store(uint16_t* s) const {
+        const int t = threadIdx.x;
+        const int r = (t & 31) * 4;
+        const int kb = (t >> 5) * 8;
+#pragma unroll
+        for (int j = 0; j < 4; j++) {
+            uint32_t e[8];
+#pragma unroll
+            for (int i = 0; i < 8; i++) {
+                const uint32_t w = j < 2 ? v[i].x : v[i].y;
+                e[i] = (w >> (16 * (j & 1))) & 0xFFFFu;
+            }
+            *reinterpret_cast<uint4*>(s + (r + j) * LDH + kb) =
+                make_uint4(e[0] | (e[1] << 16), e[2] | (e[3] << 16), e[4] | (e[5] << 16),
+                           e[6] | (e[7] << 16));
+        }
+    }
+};
+
+__device__ __forceinline__ uint4 frag(const uint16_t* s, int r, int g, int q) {
+    return *reinterpret_cast<const uint4*>(s + r * LDH + 16 * q + 8 * g);
+}
+
+__device__ __forceinline__ float4 ld4h(const uint16_t* p) {
+    const uint2 u = *reinterpret_cast<const uint2*>(p);
+    return make_float4(bf2f(u.x & 0xFFFFu), bf2f(u.x >> 16), bf2f(u.y & 0xFFFFu), bf2f(u.y >> 16));
+}
+__device__ __forceinline__ void st4h(uint16_t* p, float4 v) {
+    *reinterpret_cast<uint2*>(p) = make_uint2(f2bf(v.x) | ((uint32_t)f2bf(v.y) << 16),
+                                              f2bf(v.z) | ((uint32_t)f2bf(v.w) << 16));
+}
+
+// Epilogue on 4 consecutive columns.  bf16 outputs: STORE, RESID, GELU,
+// GELU_BWD.  fp32 outputs: ACCUM (gradient +=), STORE when out_f32, PARTIAL.
+template <int EPI>
+__device__ __forceinline__ void epi4(const GemmArgsH& a, float* __restrict__ partial, int row,
+                                     int col, float4 v) {
+    if (EPI == EPI_PARTIAL) {
+        st4(partial + (int64_t)blockIdx.z * a.M * a.N + (int64_t)row * a.N + col, v);
+        return;
+    }
+    const int64_t idx = (int64_t)row * a.ldc + col;
+    if (EPI == EPI_ACCUM) {
+        float* c = reinterpret_cast<float*>(a.C) + idx;
+        const float4 o = ld4(c);
+        st4(c, make_float4(o.x + v.x, o.y + v.y, o.z + v.z, o.w + v.w));
+        return;
+    }
+    if (EPI == EPI_GELU_BWD) {
+        const float4 x = ld4h(a.aux + (int64_t)row * a.ldaux + col);
+        st4h(reinterpret_cast<uint16_t*>(a.C) + idx,
+             make_float4(v.x * gelu_grad_f(x.x), v.y * gelu_grad_f(x.y), v.z * gelu_grad_f(x.z),
+                         v.w * gelu_grad_f(x.w)));
+        return;
+    }
+    if (EPI == EPI_RESID || EPI == EPI_GELU || (EPI == EPI_STORE && a.bias)) {
+        const float4 bb = ld4(a.bias + col);
+        v = make_float4(v.x + bb.x, v.y + bb.y, v.z + bb.z, v.w + bb.w);
+    }
+    if (EPI == EPI_RESID) {
+        const float4 x = ld4h(a.aux + (int64_t)row * a.ldaux + col);
+        v = make_float4(v.x + x.x, v.y + x.y, v.z + x.z, v.w + x.w);
+    }
+    if (EPI == EPI_STORE && a.out_f32) {
+        st4(reinterpret_cast<float*>(a.C) + idx, v);
+        return;
+    }
+    st4h(reinterpret_cast<uint16_t*>(a.C) + idx, v);
+    if (EPI == EPI_GELU)
+        st4h(a.out2 + idx, make_float4(gelu_f(v.x), gelu_f(v.y), gelu_f(v.z), gelu_f(v.w)));
+}
+
+template <int EPI>
+__device__ __forceinline__ void epi1(const GemmArgsH& a, float* __restrict__ partial, int row,
+                                     int col, float v) {
+    if (EPI == EPI_PARTIAL) {
+        partial[(int64_t)blockIdx.z * a.M * a.N + (int64_t)row * a.N + col] = v;
+        return;
+    }
+    const int64_t idx = (int64_t)row * a.ldc + col;
+    if (EPI == EPI_ACCUM) {
+        reinterpret_cast<float*>(a.C)[idx] += v;
+        return;
+    }
+    if (EPI == EPI_GELU_BWD) {
+        reinterpret_cast<uint16_t*>(a.C)[idx] =
+            f2bf(v * gelu_grad_f(bf2f(a.aux[(int64_t)row * a.ldaux + col])));
+        return;
+    }
+    if (EPI == EPI_RESID || EPI == EPI_GELU || (EPI == EPI_STORE && a.bias)) v += a.bias[col];
+    if (EPI == EPI_RESID) v += bf2f(a.aux[(int64_t)row * a.ldaux + col]);
+    if (EPI == EPI_STORE && a.out_f32) {
+        reinterpret_cast<float*>(a.C)[idx] = v;
+        return;
+    }
+    reinterpret_cast<uint16_t*>(a.C)[idx] = f2bf(v);
+    if (EPI == EPI_GELU) a.out2[idx] = f2bf(gelu_f(v));
+}
+
+template <int OP, int EPI>
+__global__ __launch_bounds__(NTHR, 2) void gemm_bf16_kernel(const GemmArgsH a, int tiles_m,
+                                                            int tiles_n, int kchunk,
+                                                            float* __restrict__ partial) {
+    constexpr bool AKC = (OP != GEMM_TN);
+    constexpr bool BKC = (OP == GEMM_NT);
+    using TA = TileH<AKC>;
+    using TB = TileH<BKC>;
+    constexpr int MAIN_BYTES = 2 * (TA::ELEMS + TB::ELEMS) * 2;
+    constexpr int EPI_BYTES = 4 * 64 * 68 * 4;
+    constexpr int SMEM = MAIN_BYTES > EPI_BYTES ? MAIN_BYTES : EPI_BYTES;
+    __shared__ __attribute__((aligned(16))) unsigned char smraw[SMEM];
+    uint16_t* smh = reinterpret_cast<uint16_t*>(smraw);
+
+    const int tile = xcd_remap(blockIdx.x, tiles_m * tiles_n);
+    constexpr int GM = 8;
+    const int per_group = GM * tiles_n;
+    const int group = tile / per_group;
+    const int first_m = group * GM;
+    const int gm = min(tiles_m - first_m, GM);
+    const int in_g = tile - group * per_group;
+    const int m0 = (first_m + in_g % gm) * BM;
+    const int n0 = (in_g / gm) * BN;
+
+    const int k_begin = blockIdx.z * kchunk;
+    const int k_end = min(a.K, k_begin + kchunk);
+    const int nk = k_end > k_begin ? (k_end - k_begin + BK - 1) / BK : 0;
+    const bool interior = (m0 + BM <= a.M) && (n0 + BN <= a.N);
+
+    const int lane = threadIdx.x & 63, wave = threadIdx.x >> 6;
+    const int wm = (wave >> 1) * 64, wn = (wave & 1) * 64;
+    const int li = lane & 31, g = lane >> 5;
+
+    floatx16 acc[2][2];
+#pragma unroll
+    for (int i = 0; i < 2; i++)
+#pragma unroll
+        for (int j = 0; j < 2; j++)
+#pragma unroll
+            for (int e = 0; e < 16; e++) acc[i][j][e] = 0.f;
+
+    TA ta[2];
+    TB tb[2];
+    auto issue = [&](auto slotc, int kt) {
+        constexpr int S = decltype(slotc)::value;
+        const int kk = k_begin + kt * BK;
+        if (interior && kk + BK <= k_end) {
+            ta[S].template load<false>(a.A, a.lda, m0, a.M, kk, k_end);
+            tb[S].template load<false>(a.B, a.ldb, n0, a.N, kk, k_end);
+        } else {
+            ta[S].template load<true>(a.A, a.lda, m0, a.M, kk, k_end);
+            tb[S].template load<true>(a.B, a.ldb, n0, a.N, kk, k_end);
+        }
+    };
+    using I0 = std::integral_constant<int, 0>;
+    using I1 = std::integral_constant<int, 1>;
+    if (nk > 0) {
+        issue(I0{}, 0);
+        ta[0].store(smh);
+        tb[0].store(smh + 2 * TA::ELEMS);
+        if (nk > 1) issue(I1{}, 1);
+    }
+    __syncthreads();
+    auto step = [&](int kt, auto slotc) {
+        constexpr int S = decltype(slotc)::value;
+        constexpr int NS = S ^ 1;
+        const int cur = kt & 1;
+        if (kt + 2 < nk) issue(slotc, kt + 2);
+        const uint16_t* sa = smh + cur * TA::ELEMS;
+        const uint16_t* sb = smh + 2 * TA::ELEMS + cur * TB::ELEMS;
+#pragma unroll
+        for (int q = 0; q < BK / 16; q++) {
+            const uint4 a0 = frag(sa, wm + li, g, q);
+            const uint4 a1 = frag(sa, wm + 32 + li, g, q);
+            const uint4 b0 = frag(sb, wn + li, g, q);
+            const uint4 b1 = frag(sb, wn + 32 + li, g, q);
+            acc[0][0] = mfma(a0, b0, acc[0][0]);
+            acc[0][1] = mfma(a0, b1, acc[0][1]);
+            acc[1][0] = mfma(a1, b0, acc[1][0]);
+            acc[1][1] = mfma(a1, b1, acc[1][1]);
+        }
+        if (kt + 1 < nk) {
+            ta[NS].store(smh + (cur ^ 1) * TA::ELEMS);
+            tb[NS].store(smh + 2 * TA::ELEMS + (cur ^ 1) * TB::ELEMS);
+        }
+        __syncthreads();
+    };
+    for (int kt = 0; kt < nk; kt += 2) {
+        step(kt, I0{});
+        if (kt + 1 < nk) step(kt + 1, I1{});
+    }
+
+    // stage each wave's 64x64 fp32 block in LDS, then work along rows
+    float* ws = reinterpret_cast<float*>(smraw) + wave * 64 * 68;
+#pragma unroll
+    for (int bm = 0; bm < 2; bm++)
+#pragma unroll
+        for (int bn = 0; bn < 2; bn++)
+#pragma unroll
+            for (int e = 0; e < 16; e++)
+                ws[(32 * bm + 8 * (e >> 2) + 4 * g + (e & 3)) * 68 + 32 * bn + li] = acc[bm][bn][e];
+    __syncthreads();
+#pragma unroll 4
+    for (int j = 0; j < 16; j++) {
+        const int idx = lane + 64 * j;
+        const int r = idx >> 4, c4 = (idx & 15) * 4;
+        const float4 v = ld4(ws + r * 68 + c4);
+        const int row = m0 + wm + r, col = n0 + wn + c4;
+        if (row >= a.M) continue;
+        if (col + 3 < a.N) {
+            epi4<EPI>(a, partial, row, col, v);
+        } else {
+            if (col < a.N) epi1<EPI>(a, partial, row, col, v.x);
+            if (col + 1 < a.N) epi1<EPI>(a, partial, row, col + 1, v.y);
+            if (col + 2 < a.N) epi1<EPI>(a, partial, row, col + 2, v.z);
+        }
+    }
+}
+
+template <int EPI>
+__global__ __launch_bounds__(256) void splitk_reduce_bf16_kernel(const GemmArgsH a,
+                                                                 const float* __restrict__ partial,
+                                                                 int splits) {
+    const int M = a.M, N = a.N;
+    const int64_t n4 = (int64_t)M * (N / 4);
+    for (int64_t i = blockIdx.x * (int64_t)blockDim.x + threadIdx.x; i < n4;
+         i += (int64_t)gridDim.x * blockDim.x) {
+        const int64_t row = i / (N / 4);
+        const int col = (int)(i - row * (N / 4)) * 4;
+        float4 s = ld4(partial + row * N + col);
+        for (int z = 1; z < splits; z++) {
+            const float4 p = ld4(partial + (int64_t)z * M * N + row * N + col);
+            s.x += p.x;
+            s.y += p.y;
+            s.z += p.z;
+            s.w += p.w;
+        }
+        epi4<EPI>(a, nullptr, (int)row, col, s);
+    }
+}
+
+inline int cdiv(int64_t a, int64_t b) { return (int)((a + b - 1) / b); }
+
+// Weight gradients (K = B*T, few output tiles) are split over K.
+int choose_splits_h(int op, int epi, int M, int N, int K) {
+    if ((N % 4) != 0 || op != GEMM_TN || (epi != EPI_ACCUM && epi != EPI_STORE)) return 1;
+    const int tiles = cdiv(M, BM) * cdiv(N, BN);
+    const int target = 768;
+    if (tiles >= target / 2) return 1;
+    int splits = cdiv(target, tiles);
+    const int max_splits = K / (BK * 4);
+    if (splits > max_splits) splits = max_splits;
+    return splits < 1 ? 1 : splits;
+}
+
+int split_chunk_h(int K, int splits) { return cdiv(cdiv(K, splits), BK) * BK; }
+
+template <int OP, int EPI>
+hipError_t launch_h(hipStream_t s, const GemmArgsH& a, int splits, float* ws) {
+    const int tm = cdiv(a.M, BM), tn = cdiv(a.N, BN);
+    const int chunk = splits > 1 ? split_chunk_h(a.K, splits) : (a.K > 0 ? a.K : 1);
+    const int nz = splits > 1 ? cdiv(a.K, chunk) : 1;
+    hipLaunchKernelGGL((gemm_bf16_kernel<OP, EPI>), dim3(tm * tn, 1, nz), dim3(NTHR), 0, s, a, tm,
+                       tn, chunk, ws);
+    return hipGetLastError();
+}
+
+}  // namespace
+
+size_t gemm_bf16_workspace_bytes(int op, int epi, int M, int N, int K) {
+    const int splits = choose_splits_h(op, epi, M, N, K);
+    if (splits <= 1) return 0;
+    return (size_t)cdiv(K, split_chunk_h(K, splits)) * M * N * sizeof(float);
+}
+
+hipError_t gemm_bf16(hipStream_t s, const GemmArgsH& a, float* ws, size_t ws_bytes) {
+    if (a.M <= 0 || a.N <= 0) return hipSuccess;
+    int splits = choose_splits_h(a.op, a.epi, a.M, a.N, a.K);
+    if (splits > 1 && gemm_bf16_workspace_bytes(a.op, a.epi, a.M, a.N, a.K) > ws_bytes) splits = 1;
+    if (splits > 1) {
+        hipError_t e = launch_h<GEMM_TN, EPI_PARTIAL>(s, a, splits, ws);
+        if (e != hipSuccess) return e;
+        const int nz = cdiv(a.K, split_chunk_h(a.K, splits));
+        const int64_t n4 = (int64_t)a.M * (a.N / 4);
+        const int blocks = (int)std::min<int64_t>((n4 + 255) / 256, 4096);
+        if (a.epi == EPI_ACCUM)
+            hipLaunchKernelGGL(splitk_reduce_bf16_kernel<EPI_ACCUM>, dim3(blocks), dim3(256), 0, s,
+                               a, ws, nz);
+        else
+            hipLaunchKernelGGL(splitk_reduce_bf16_kernel<EPI_STORE>, dim3(blocks), dim3(256), 0, s,
+                               a, ws, nz);
+        return hipGetLastError();
+    }
+    switch (a.op) {
+        case GEMM_NT:
+            switch (a.epi) {
+                case EPI_STORE: return launch_h<GEMM_NT, EPI_STORE>(s, a, 1, ws);
+                case EPI_RESID: return launch_h<GEMM_NT, EPI_RESID>(s, a, 1, ws);
+                case EPI_GELU: return launch_h<GEMM_NT, EPI_GELU>(s, a, 1, ws);
+                default: return hipErrorInvalidValue;
+            }
+        case GEMM_NN:
+            switch (a.epi) {
+                case EPI_STORE: return launch_h<GEMM_NN, EPI_STORE>(s, a, 1, ws);
+                case EPI_GELU_BWD: return launch_h<GEMM_NN, EPI_GELU_BWD>(s, a, 1, ws);
+                default: return hipErrorInvalidValue;
+            }
+        case GEMM_TN:
+            switch (a.epi) {
+                case EPI_STORE: return launch_h<GEMM_TN, EPI_STORE>(s, a, 1, ws);
+                case EPI_ACCUM: return launch_h<GEMM_TN, EPI_ACCUM>(s, a, 1, ws);
+                default: return hipErrorInvalidValue;
+            }
+        default: return hipErrorInvalidValue;
+    }
+}
+
+}  // namespace gk

@@ -37,6 +37,28 @@ struct GemmArgs {
     float* out2;        // EPI_GELU
 };
 
+// bf16 variant (mixed precision): A and B are bf16, accumulation fp32.  C is
+// bf16 (activations; EPI_STORE with out_f32 != 0 writes fp32) or fp32
+// (EPI_ACCUM: weight gradients).  bias is fp32, aux and out2 are bf16.
+struct GemmArgsH {
+    int op, epi;
+    int M, N, K;
+    const uint16_t* A;
+    int64_t lda;
+    const uint16_t* B;
+    int64_t ldb;
+    void* C;
+    int64_t ldc;
+    int out_f32;
+    const float* bias;
+    const uint16_t* aux;
+    int64_t ldaux;
+    uint16_t* out2;
+};
+size_t gemm_bf16_workspace_bytes(int op, int epi, int M, int N, int K);
+hipError_t gemm_bf16(hipStream_t s, const GemmArgsH& a, float* workspace,
+                     size_t workspace_bytes);
+
 // Workspace bytes a call may need for split-K partial sums.
 size_t gemm_workspace_bytes(int op, int epi, int M, int N, int K);
 hipError_t gemm(hipStream_t s, const GemmArgs& a, float* workspace,
@@ -47,42 +69,44 @@ hipError_t gemm(hipStream_t s, const GemmArgs& a, float* workspace,
 // Forward writes out (B*T, C) and lse (B, NH, T) = log-sum-exp of each
 // scaled score row; backward reads dout and writes dqkv (B*T, 3C), using
 // dpre (B, NH, T) as scratch for rowsum(dout * out).
-hipError_t attention_forward(hipStream_t s, float* out, float* lse,
-                             const float* qkv, int B, int T, int C, int NH);
-hipError_t attention_backward(hipStream_t s, float* dqkv, float* dpre,
-                              const float* dout, const float* qkv,
-                              const float* out, const float* lse, int B, int T,
-                              int C, int NH);
+// Activations are fp32, or bf16 bits when bf16 != 0; lse and D are fp32.
+hipError_t attention_forward(hipStream_t s, void* out, float* lse, const void* qkv, int B,
+                             int T, int C, int NH, int bf16);
+hipError_t attention_backward(hipStream_t s, void* dqkv, float* dpre, const void* dout,
+                              const void* qkv, const void* out, const float* lse, int B,
+                              int T, int C, int NH, int bf16);
 
 // ---- layernorm ------------------------------------------------------------
-hipError_t layernorm_forward(hipStream_t s, float* out, float* mean,
-                             float* rstd, const float* inp, const float* w,
-                             const float* b, int N, int C);
+// Activations (out, inp, dres, dout) are fp32, or bf16 bits when bf16 != 0;
+// mean, rstd, weights and their gradients are always fp32.
+hipError_t layernorm_forward(hipStream_t s, void* out, float* mean, float* rstd,
+                             const void* inp, const float* w, const float* b, int N, int C,
+                             int bf16);
 // dres (+)= dx;  dw += sum dy*xhat, db += sum dy (two deterministic stages,
 // `partials` holds layernorm_partials_floats(N, C) floats).
 size_t layernorm_partials_floats(int N, int C);
-hipError_t layernorm_backward(hipStream_t s, float* dres, int accumulate,
-                              float* dw, float* db, float* partials,
-                              const float* dout, const float* inp,
-                              const float* w, const float* mean,
-                              const float* rstd, int N, int C);
+hipError_t layernorm_backward(hipStream_t s, void* dres, int accumulate, float* dw, float* db,
+                              float* partials, const void* dout, const void* inp,
+                              const float* w, const float* mean, const float* rstd, int N,
+                              int C, int bf16);
 
 // ---- fused softmax + cross-entropy -----------------------------------------
 // logits (N, ldv) with V valid columns.  losses[n] = lse - logit[target];
 // logits are overwritten by (softmax - onehot) * dscale, columns V..ldv-1 by
 // 0.  A target outside [0, V) sets *flag |= 2 and zeroes that row.
-hipError_t softmax_ce(hipStream_t s, float* logits, float* losses,
+// logits fp32, or bf16 bits when bf16 != 0 (the statistics are fp32).
+hipError_t softmax_ce(hipStream_t s, void* logits, float* losses,
                       const int32_t* targets, int N, int V, int ldv,
-                      float dscale, int* flag);
+                      float dscale, int* flag, int bf16);
 // out[0] = mean of x[0..n) (deterministic order)
 hipError_t mean_reduce(hipStream_t s, float* out, const float* x, int n);
 
 // ---- embedding -------------------------------------------------------------
 // out[b,t] = wte[tok] + wpe[t]; a token outside [0, V) sets *flag |= 1 and
 // gives a zero row.
-hipError_t encoder_forward(hipStream_t s, float* out, const int32_t* tok,
+hipError_t encoder_forward(hipStream_t s, void* out, const int32_t* tok,
                            const float* wte, const float* wpe, int B, int T,
-                           int C, int V, int* flag);
+                           int C, int V, int* flag, int bf16);
 // keys (n_pow2 uint32) sorted ascending: (token << pos_bits) | position.
 // encoder_sort_prepare(n_pow2) must run once (per process) before sorts of
 // up to n_pow2 keys: it raises the kernel's LDS limit.
@@ -91,21 +115,23 @@ hipError_t encoder_sort(hipStream_t s, uint32_t* keys, const int32_t* tok,
                         int n, int V, int pos_bits, int n_pow2);
 // dwte[tok] += dx rows (summed in position order), dwpe[t] += sum_b dx.
 hipError_t encoder_backward(hipStream_t s, float* dwte, float* dwpe,
-                            const float* dx, const uint32_t* sorted_keys,
-                            int B, int T, int C, int V, int pos_bits);
+                            const void* dx, const uint32_t* sorted_keys,
+                            int B, int T, int C, int V, int pos_bits, int bf16);
 
 // ---- reductions and elementwise -------------------------------------------
 // db[n] += sum_m dy[m*ld + n]; `partials` holds bias_partials_floats(M, N).
 size_t bias_partials_floats(int M, int N);
 hipError_t bias_grad(hipStream_t s, float* db, float* partials,
-                     const float* dy, int M, int N, int64_t ld);
+                     const void* dy, int M, int N, int64_t ld, int bf16);
 // out0[c] += sum_r part[r*ncols + c] for c < split, out1[c-split] likewise
 // for c >= split; rows summed in a fixed order.
 hipError_t colsum_add(hipStream_t s, float* out0, float* out1, int split, const float* part,
                       int nrows, int ncols);
 hipError_t fill_zero(hipStream_t s, float* p, int64_t n);
+// shadow: optional bf16 copy of the updated parameters (NULL = none).
 hipError_t adamw(hipStream_t s, float* p, const float* g, float* m, float* v,
-                 int64_t n, float lr, float b1, float b2, float eps, float wd,
-                 float bc1, float bc2);
+                 uint16_t* shadow, int64_t n, float lr, float b1, float b2, float eps,
+                 float wd, float bc1, float bc2);
+hipError_t to_bf16(hipStream_t s, uint16_t* out, const float* in, int64_t n);
 
 }  // namespace gk

@@ -23,11 +23,11 @@ namespace {
 
 constexpr float LN_EPS = 1e-5f;
 
-template <int NCH>  // float4 chunks per lane: C <= 256 * NCH
-__global__ __launch_bounds__(256) void ln_fwd_kernel(float* __restrict__ out,
+template <int NCH, class T>  // float4 chunks per lane: C <= 256 * NCH
+__global__ __launch_bounds__(256) void ln_fwd_kernel(T* __restrict__ out,
                                                      float* __restrict__ mean,
                                                      float* __restrict__ rstd,
-                                                     const float* __restrict__ inp,
+                                                     const T* __restrict__ inp,
                                                      const float* __restrict__ w,
                                                      const float* __restrict__ b, int N,
                                                      int C) {
@@ -35,13 +35,13 @@ __global__ __launch_bounds__(256) void ln_fwd_kernel(float* __restrict__ out,
     const int lane = threadIdx.x & 63;
     if (row >= N) return;
     const int C4 = C >> 2;
-    const float* x = inp + (int64_t)row * C;
+    const T* x = inp + (int64_t)row * C;
     float4 v[NCH];
     float s = 0.f;
 #pragma unroll
     for (int i = 0; i < NCH; i++) {
         const int c4 = lane + 64 * i;
-        v[i] = c4 < C4 ? ld4(x + 4 * c4) : make_float4(0.f, 0.f, 0.f, 0.f);
+        v[i] = c4 < C4 ? Act<T>::ld(x + 4 * c4) : make_float4(0.f, 0.f, 0.f, 0.f);
         s += (v[i].x + v[i].y) + (v[i].z + v[i].w);
     }
     const float m = wave_sum(s) / C;
@@ -56,13 +56,13 @@ __global__ __launch_bounds__(256) void ln_fwd_kernel(float* __restrict__ out,
     }
     const float var = wave_sum(ss) / C;
     const float r = 1.0f / sqrtf(var + LN_EPS);
-    float* y = out + (int64_t)row * C;
+    T* y = out + (int64_t)row * C;
 #pragma unroll
     for (int i = 0; i < NCH; i++) {
         const int c4 = lane + 64 * i;
         if (c4 < C4) {
             const float4 ww = ld4(w + 4 * c4), bb = ld4(b + 4 * c4);
-            st4(y + 4 * c4, make_float4((v[i].x - m) * r * ww.x + bb.x,
+            Act<T>::st(y + 4 * c4, make_float4((v[i].x - m) * r * ww.x + bb.x,
                                         (v[i].y - m) * r * ww.y + bb.y,
                                         (v[i].z - m) * r * ww.z + bb.z,
                                         (v[i].w - m) * r * ww.w + bb.w));
@@ -82,10 +82,10 @@ inline int ln_rows_per_block(int N) {
     return r < 4 ? 4 : r;
 }
 
-template <int NCH>
+template <int NCH, class T>
 __global__ __launch_bounds__(256) void ln_bwd_kernel(
-    float* __restrict__ dres, int accumulate, float* __restrict__ partials,
-    const float* __restrict__ dout, const float* __restrict__ inp, const float* __restrict__ w,
+    T* __restrict__ dres, int accumulate, float* __restrict__ partials,
+    const T* __restrict__ dout, const T* __restrict__ inp, const float* __restrict__ w,
     const float* __restrict__ mean, const float* __restrict__ rstd, int N, int C, int rpb) {
     extern __shared__ float red[];  // [4 waves][2][C]
     const int lane = threadIdx.x & 63, wave = threadIdx.x >> 6;
@@ -101,8 +101,8 @@ __global__ __launch_bounds__(256) void ln_bwd_kernel(
     const int r1 = min(N, r0 + rpb);
     for (int row = r0 + wave; row < r1; row += 4) {
         const float m = mean[row], rs = rstd[row];
-        const float* dy = dout + (int64_t)row * C;
-        const float* x = inp + (int64_t)row * C;
+        const T* dy = dout + (int64_t)row * C;
+        const T* x = inp + (int64_t)row * C;
         float4 g[NCH], xh[NCH];
         float sg = 0.f, sgx = 0.f;
 #pragma unroll
@@ -110,8 +110,8 @@ __global__ __launch_bounds__(256) void ln_bwd_kernel(
             const int c4 = lane + 64 * i;
             float4 d = make_float4(0.f, 0.f, 0.f, 0.f), xx = d;
             if (c4 < C4) {
-                d = ld4(dy + 4 * c4);
-                xx = ld4(x + 4 * c4);
+                d = Act<T>::ld(dy + 4 * c4);
+                xx = Act<T>::ld(x + 4 * c4);
             }
             xh[i] = make_float4((xx.x - m) * rs, (xx.y - m) * rs, (xx.z - m) * rs,
                                 (xx.w - m) * rs);
@@ -128,7 +128,7 @@ __global__ __launch_bounds__(256) void ln_bwd_kernel(
             pb[i].w += d.w;
         }
         const float mg = wave_sum(sg) / C, mgx = wave_sum(sgx) / C;
-        float* dx = dres + (int64_t)row * C;
+        T* dx = dres + (int64_t)row * C;
 #pragma unroll
         for (int i = 0; i < NCH; i++) {
             const int c4 = lane + 64 * i;
@@ -138,13 +138,13 @@ __global__ __launch_bounds__(256) void ln_bwd_kernel(
                                        rs * (g[i].z - mg - xh[i].z * mgx),
                                        rs * (g[i].w - mg - xh[i].w * mgx));
                 if (accumulate) {
-                    const float4 p = ld4(dx + 4 * c4);
+                    const float4 p = Act<T>::ld(dx + 4 * c4);
                     o.x += p.x;
                     o.y += p.y;
                     o.z += p.z;
                     o.w += p.w;
                 }
-                st4(dx + 4 * c4, o);
+                Act<T>::st(dx + 4 * c4, o);
             }
         }
     }
@@ -168,21 +168,45 @@ __global__ __launch_bounds__(256) void ln_bwd_kernel(
     }
 }
 
-}  // namespace
-
-hipError_t layernorm_forward(hipStream_t s, float* out, float* mean, float* rstd,
-                             const float* inp, const float* w, const float* b, int N, int C) {
-    if (N <= 0) return hipSuccess;
+template <class T>
+hipError_t ln_fwd_launch(hipStream_t s, T* out, float* mean, float* rstd, const T* inp,
+                         const float* w, const float* b, int N, int C) {
     dim3 grid((N + 3) / 4), block(256);
-    const int nch = (C + 255) / 256;
-    switch (nch) {
-        case 1: hipLaunchKernelGGL(ln_fwd_kernel<1>, grid, block, 0, s, out, mean, rstd, inp, w, b, N, C); break;
-        case 2: hipLaunchKernelGGL(ln_fwd_kernel<2>, grid, block, 0, s, out, mean, rstd, inp, w, b, N, C); break;
-        case 3: hipLaunchKernelGGL(ln_fwd_kernel<3>, grid, block, 0, s, out, mean, rstd, inp, w, b, N, C); break;
-        case 4: hipLaunchKernelGGL(ln_fwd_kernel<4>, grid, block, 0, s, out, mean, rstd, inp, w, b, N, C); break;
+    switch ((C + 255) / 256) {
+        case 1: hipLaunchKernelGGL((ln_fwd_kernel<1, T>), grid, block, 0, s, out, mean, rstd, inp, w, b, N, C); break;
+        case 2: hipLaunchKernelGGL((ln_fwd_kernel<2, T>), grid, block, 0, s, out, mean, rstd, inp, w, b, N, C); break;
+        case 3: hipLaunchKernelGGL((ln_fwd_kernel<3, T>), grid, block, 0, s, out, mean, rstd, inp, w, b, N, C); break;
+        case 4: hipLaunchKernelGGL((ln_fwd_kernel<4, T>), grid, block, 0, s, out, mean, rstd, inp, w, b, N, C); break;
         default: return hipErrorInvalidValue;
     }
     return hipGetLastError();
+}
+
+template <class T>
+hipError_t ln_bwd_launch(hipStream_t s, T* dres, int accumulate, float* partials, const T* dout,
+                         const T* inp, const float* w, const float* mean, const float* rstd,
+                         int N, int C, int rpb, int nb) {
+    const size_t shm = (size_t)8 * C * sizeof(float);
+    dim3 grid(nb), block(256);
+    switch ((C + 255) / 256) {
+        case 1: hipLaunchKernelGGL((ln_bwd_kernel<1, T>), grid, block, shm, s, dres, accumulate, partials, dout, inp, w, mean, rstd, N, C, rpb); break;
+        case 2: hipLaunchKernelGGL((ln_bwd_kernel<2, T>), grid, block, shm, s, dres, accumulate, partials, dout, inp, w, mean, rstd, N, C, rpb); break;
+        case 3: hipLaunchKernelGGL((ln_bwd_kernel<3, T>), grid, block, shm, s, dres, accumulate, partials, dout, inp, w, mean, rstd, N, C, rpb); break;
+        case 4: hipLaunchKernelGGL((ln_bwd_kernel<4, T>), grid, block, shm, s, dres, accumulate, partials, dout, inp, w, mean, rstd, N, C, rpb); break;
+        default: return hipErrorInvalidValue;
+    }
+    return hipGetLastError();
+}
+
+}  // namespace
+
+hipError_t layernorm_forward(hipStream_t s, void* out, float* mean, float* rstd, const void* inp,
+                             const float* w, const float* b, int N, int C, int bf16) {
+    if (N <= 0) return hipSuccess;
+    if (bf16)
+        return ln_fwd_launch<uint16_t>(s, (uint16_t*)out, mean, rstd, (const uint16_t*)inp, w, b,
+                                       N, C);
+    return ln_fwd_launch<float>(s, (float*)out, mean, rstd, (const float*)inp, w, b, N, C);
 }
 
 // Upper bound of the workgroup count over every row count up to N: at most
@@ -192,24 +216,19 @@ size_t layernorm_partials_floats(int N, int C) {
     return (size_t)nb * 2 * C;
 }
 
-hipError_t layernorm_backward(hipStream_t s, float* dres, int accumulate, float* dw, float* db,
-                              float* partials, const float* dout, const float* inp,
+hipError_t layernorm_backward(hipStream_t s, void* dres, int accumulate, float* dw, float* db,
+                              float* partials, const void* dout, const void* inp,
                               const float* w, const float* mean, const float* rstd, int N,
-                              int C) {
+                              int C, int bf16) {
     if (N <= 0) return hipSuccess;
     const int rpb = ln_rows_per_block(N);
     const int nb = (N + rpb - 1) / rpb;
-    const size_t shm = (size_t)8 * C * sizeof(float);
-    const int nch = (C + 255) / 256;
-    dim3 grid(nb), block(256);
-    switch (nch) {
-        case 1: hipLaunchKernelGGL(ln_bwd_kernel<1>, grid, block, shm, s, dres, accumulate, partials, dout, inp, w, mean, rstd, N, C, rpb); break;
-        case 2: hipLaunchKernelGGL(ln_bwd_kernel<2>, grid, block, shm, s, dres, accumulate, partials, dout, inp, w, mean, rstd, N, C, rpb); break;
-        case 3: hipLaunchKernelGGL(ln_bwd_kernel<3>, grid, block, shm, s, dres, accumulate, partials, dout, inp, w, mean, rstd, N, C, rpb); break;
-        case 4: hipLaunchKernelGGL(ln_bwd_kernel<4>, grid, block, shm, s, dres, accumulate, partials, dout, inp, w, mean, rstd, N, C, rpb); break;
-        default: return hipErrorInvalidValue;
-    }
-    hipError_t e = hipGetLastError();
+    hipError_t e =
+        bf16 ? ln_bwd_launch<uint16_t>(s, (uint16_t*)dres, accumulate, partials,
+                                       (const uint16_t*)dout, (const uint16_t*)inp, w, mean, rstd,
+                                       N, C, rpb, nb)
+             : ln_bwd_launch<float>(s, (float*)dres, accumulate, partials, (const float*)dout,
+                                    (const float*)inp, w, mean, rstd, N, C, rpb, nb);
     if (e != hipSuccess) return e;
     return colsum_add(s, dw, db, C, partials, nb, 2 * C);
 }

@@ -76,8 +76,6 @@ int check_config(const gpt2_config* c) {
     if (c->vocab_size > 65536) return fail(GPT2_EINVAL, "vocab_size > 65536 not supported");
     if (c->precision != GPT2_FP32 && c->precision != GPT2_BF16_MIXED)
         return fail(GPT2_EINVAL, "unknown precision %d", c->precision);
-    if (c->precision == GPT2_BF16_MIXED)
-        return fail(GPT2_EINVAL, "GPT2_BF16_MIXED is not built into this library");
     return GPT2_OK;
 }
 
@@ -86,8 +84,10 @@ inline size_t align256(size_t x) { return (x + 255) & ~size_t(255); }
 // Byte offsets of every sub-buffer inside the one device allocation.
 struct Layout {
     int L, C, NH, V, Vp, maxT, Bmax, Tmax, M, pos_bits, n_pow2;
+    int bf16;   // activations (and the matmul weight copy) in bf16
+    size_t es;  // bytes per activation element
     int64_t nparams, poff[16], psize[16];
-    size_t params, grads, m, v;
+    size_t params, grads, m, v, shadow;
     size_t encoded, ln1, ln1_mean, ln1_rstd, qkv, atty, lse, res2, ln2, ln2_mean, ln2_rstd, fch,
         fch_gelu, res3, lnf, lnf_mean, lnf_rstd, logits, losses;
     size_t dres, dtmp, dqkv, dfch, attn_d, ln_part, bias_part, gemm_ws, keys, tokens, targets,
@@ -95,6 +95,8 @@ struct Layout {
     size_t gemm_ws_bytes, total;
 
     void build(const gpt2_config* c) {
+        bf16 = c->precision == GPT2_BF16_MIXED;
+        es = bf16 ? 2 : 4;
         L = c->num_layers;
         C = c->channels;
         NH = c->num_heads;
@@ -124,36 +126,39 @@ struct Layout {
         grads = take(nparams * f);
         m = take(nparams * f);
         v = take(nparams * f);
-        encoded = take(MC * f);
-        ln1 = take(L * MC * f);
+        shadow = bf16 ? take(nparams * 2) : 0;
+        encoded = take(MC * es);
+        ln1 = take(L * MC * es);
         ln1_mean = take((size_t)L * M * f);
         ln1_rstd = take((size_t)L * M * f);
-        qkv = take(L * 3 * MC * f);
-        atty = take(L * MC * f);
+        qkv = take(L * 3 * MC * es);
+        atty = take(L * MC * es);
         lse = take((size_t)L * M * NH * f);
-        res2 = take(L * MC * f);
-        ln2 = take(L * MC * f);
+        res2 = take(L * MC * es);
+        ln2 = take(L * MC * es);
         ln2_mean = take((size_t)L * M * f);
         ln2_rstd = take((size_t)L * M * f);
-        fch = take(L * 4 * MC * f);
-        fch_gelu = take(L * 4 * MC * f);
-        res3 = take(L * MC * f);
-        lnf = take(MC * f);
+        fch = take(L * 4 * MC * es);
+        fch_gelu = take(L * 4 * MC * es);
+        res3 = take(L * MC * es);
+        lnf = take(MC * es);
         lnf_mean = take((size_t)M * f);
         lnf_rstd = take((size_t)M * f);
-        logits = take((size_t)M * Vp * f);
+        logits = take((size_t)M * Vp * es);
         losses = take((size_t)M * f);
-        dres = take(MC * f);
-        dtmp = take(MC * f);
-        dqkv = take(3 * MC * f);
-        dfch = take(4 * MC * f);
+        dres = take(MC * es);
+        dtmp = take(MC * es);
+        dqkv = take(3 * MC * es);
+        dfch = take(4 * MC * es);
         attn_d = take((size_t)M * NH * f);
         ln_part = take(gk::layernorm_partials_floats(M, C) * f);
         bias_part = take(gk::bias_partials_floats(M, 4 * C) * f);
         // the largest split-K workspace over every matmul of the step
         gemm_ws_bytes = 0;
         auto need = [&](int op, int epi, int m, int n, int k) {
-            gemm_ws_bytes = std::max(gemm_ws_bytes, gk::gemm_workspace_bytes(op, epi, m, n, k));
+            const size_t b = bf16 ? gk::gemm_bf16_workspace_bytes(op, epi, m, n, k)
+                                  : gk::gemm_workspace_bytes(op, epi, m, n, k);
+            gemm_ws_bytes = std::max(gemm_ws_bytes, b);
         };
         const int outs[4][2] = {{3 * C, C}, {C, C}, {4 * C, C}, {C, 4 * C}};
         for (auto& o : outs) need(gk::GEMM_TN, gk::EPI_ACCUM, o[0], o[1], M);
@@ -209,6 +214,12 @@ struct gpt2_model {
         return reinterpret_cast<X*>(base + off);
     }
     float* P(int i) const { return at<float>(lay.params) + lay.poff[i]; }
+    // weight operand of the matmuls: the fp32 master, or its bf16 copy
+    const void* W(int i) const {
+        return lay.bf16 ? (const void*)(at<uint16_t>(lay.shadow) + lay.poff[i]) : (const void*)P(i);
+    }
+    // activation buffer at byte offset `off`, element `idx`
+    char* A(size_t off, size_t idx = 0) const { return base + off + idx * lay.es; }
     float* G(int i) const { return at<float>(lay.grads) + lay.poff[i]; }
     int* flag() const { return at<int>(lay.scalars + 4); }
     float* dloss() const { return at<float>(lay.scalars); }
@@ -268,34 +279,91 @@ int hip_check(hipError_t e, const char* what) {
     return GPT2_OK;
 }
 
-gk::GemmArgs gemm_args(int op, int epi, int M, int N, int K, const float* A, int64_t lda,
-                       const float* B, int64_t ldb, float* C, int64_t ldc) {
-    gk::GemmArgs a{};
-    a.op = op;
-    a.epi = epi;
-    a.M = M;
-    a.N = N;
-    a.K = K;
-    a.A = A;
-    a.lda = lda;
-    a.B = B;
-    a.ldb = ldb;
-    a.C = C;
-    a.ldc = ldc;
-    return a;
+// One matmul of the step, independent of the precision: activations and
+// weights as untyped pointers (fp32, or bf16 in the mixed-precision model),
+// gradients (EPI_ACCUM outputs), biases and everything else fp32.
+struct Mm {
+    int op, epi, M, N, K;
+    const void* A;
+    int64_t lda;
+    const void* B;
+    int64_t ldb;
+    void* C;
+    int64_t ldc;
+    const float* bias = nullptr;
+    const void* aux = nullptr;
+    int64_t ldaux = 0;
+    void* out2 = nullptr;
+};
+
+Mm mm(int op, int epi, int M, int N, int K, const void* A, int64_t lda, const void* B,
+      int64_t ldb, void* C, int64_t ldc) {
+    Mm x;
+    x.op = op;
+    x.epi = epi;
+    x.M = M;
+    x.N = N;
+    x.K = K;
+    x.A = A;
+    x.lda = lda;
+    x.B = B;
+    x.ldb = ldb;
+    x.C = C;
+    x.ldc = ldc;
+    return x;
 }
 
-int run_gemm(gpt2_model* md, const gk::GemmArgs& a) {
-    const double flops = 2.0 * a.M * a.N * (double)a.K;
-    const double bytes = 4.0 * ((double)a.M * a.K + (double)a.K * a.N + (double)a.M * a.N);
-    LAUNCH(md, GPT2_KC_GEMM, flops, bytes,
-           gk::gemm(md->stream, a, md->at<float>(md->lay.gemm_ws), md->lay.gemm_ws_bytes));
+int run_gemm(gpt2_model* md, const Mm& x) {
+    const double flops = 2.0 * x.M * x.N * (double)x.K;
+    const double es = (double)md->lay.es;
+    const double bytes = es * ((double)x.M * x.K + (double)x.K * x.N) +
+                         (x.epi == gk::EPI_ACCUM ? 8.0 : es) * (double)x.M * x.N;
+    float* ws = md->at<float>(md->lay.gemm_ws);
+    const size_t wsb = md->lay.gemm_ws_bytes;
+    if (md->lay.bf16) {
+        gk::GemmArgsH a{};
+        a.op = x.op;
+        a.epi = x.epi;
+        a.M = x.M;
+        a.N = x.N;
+        a.K = x.K;
+        a.A = (const uint16_t*)x.A;
+        a.lda = x.lda;
+        a.B = (const uint16_t*)x.B;
+        a.ldb = x.ldb;
+        a.C = x.C;
+        a.ldc = x.ldc;
+        a.out_f32 = 0;
+        a.bias = x.bias;
+        a.aux = (const uint16_t*)x.aux;
+        a.ldaux = x.ldaux;
+        a.out2 = (uint16_t*)x.out2;
+        LAUNCH(md, GPT2_KC_GEMM, flops, bytes, gk::gemm_bf16(md->stream, a, ws, wsb));
+    } else {
+        gk::GemmArgs a{};
+        a.op = x.op;
+        a.epi = x.epi;
+        a.M = x.M;
+        a.N = x.N;
+        a.K = x.K;
+        a.A = (const float*)x.A;
+        a.lda = x.lda;
+        a.B = (const float*)x.B;
+        a.ldb = x.ldb;
+        a.C = (float*)x.C;
+        a.ldc = x.ldc;
+        a.bias = x.bias;
+        a.aux = (const float*)x.aux;
+        a.ldaux = x.ldaux;
+        a.out2 = (float*)x.out2;
+        LAUNCH(md, GPT2_KC_GEMM, flops, bytes, gk::gemm(md->stream, a, ws, wsb));
+    }
     return GPT2_OK;
 }
 
-#define TRY(x)                      \
-    do {                            \
-        int r_ = (x);               \
+#define TRY(x)                        \
+    do {                              \
+        int r_ = (x);                 \
         if (r_ != GPT2_OK) return r_; \
     } while (0)
 
@@ -304,76 +372,77 @@ int run_gemm(gpt2_model* md, const gk::GemmArgs& a) {
 int forward_impl(gpt2_model* md, const int32_t* tok, const int32_t* tgt, int B, int T) {
     const Layout& y = md->lay;
     const int L = y.L, C = y.C, NH = y.NH, V = y.V, M = B * T;
-    const size_t MC = (size_t)y.M * C;  // per-layer capacity stride
-    const double f4 = 4.0;
+    const int h = y.bf16;
+    const size_t MC = (size_t)y.M * C;  // per-layer capacity stride, elements
+    const double es = (double)y.es;
     hipStream_t s = md->stream;
-    float* enc = md->at<float>(y.encoded);
+    void* enc = md->A(y.encoded);
 
     LAUNCH(md, GPT2_KC_OTHER, 0, 4.0, gk::fill_zero(s, (float*)md->flag(), 1));
-    LAUNCH(md, GPT2_KC_OTHER, 0, f4 * (3.0 * M * C) + 4.0 * M,
-           gk::encoder_forward(s, enc, tok, md->P(P_WTE), md->P(P_WPE), B, T, C, V, md->flag()));
+    LAUNCH(md, GPT2_KC_OTHER, 0, 8.0 * M * C + es * M * C + 4.0 * M,
+           gk::encoder_forward(s, enc, tok, md->P(P_WTE), md->P(P_WPE), B, T, C, V, md->flag(), h));
     for (int l = 0; l < L; l++) {
-        const float* resid = l == 0 ? enc : md->at<float>(y.res3) + (l - 1) * MC;
-        float* ln1 = md->at<float>(y.ln1) + l * MC;
+        const void* resid = l == 0 ? enc : (const void*)md->A(y.res3, (l - 1) * MC);
+        void* ln1 = md->A(y.ln1, l * MC);
         float* ln1m = md->at<float>(y.ln1_mean) + (size_t)l * y.M;
         float* ln1r = md->at<float>(y.ln1_rstd) + (size_t)l * y.M;
-        float* qkv = md->at<float>(y.qkv) + l * 3 * MC;
-        float* atty = md->at<float>(y.atty) + l * MC;
+        void* qkv = md->A(y.qkv, l * 3 * MC);
+        void* atty = md->A(y.atty, l * MC);
         float* lse = md->at<float>(y.lse) + (size_t)l * y.M * NH;
-        float* res2 = md->at<float>(y.res2) + l * MC;
-        float* ln2 = md->at<float>(y.ln2) + l * MC;
+        void* res2 = md->A(y.res2, l * MC);
+        void* ln2 = md->A(y.ln2, l * MC);
         float* ln2m = md->at<float>(y.ln2_mean) + (size_t)l * y.M;
         float* ln2r = md->at<float>(y.ln2_rstd) + (size_t)l * y.M;
-        float* fch = md->at<float>(y.fch) + l * 4 * MC;
-        float* fchg = md->at<float>(y.fch_gelu) + l * 4 * MC;
-        float* res3 = md->at<float>(y.res3) + l * MC;
+        void* fch = md->A(y.fch, l * 4 * MC);
+        void* fchg = md->A(y.fch_gelu, l * 4 * MC);
+        void* res3 = md->A(y.res3, l * MC);
 
-        LAUNCH(md, GPT2_KC_LAYERNORM, 0, f4 * (2.0 * M * C + 2.0 * M),
+        LAUNCH(md, GPT2_KC_LAYERNORM, 0, es * 2.0 * M * C + 8.0 * M,
                gk::layernorm_forward(s, ln1, ln1m, ln1r, resid, md->P(P_LN1W) + l * C,
-                                     md->P(P_LN1B) + l * C, M, C));
-        gk::GemmArgs a = gemm_args(gk::GEMM_NT, gk::EPI_STORE, M, 3 * C, C, ln1, C,
-                                   md->P(P_QKVW) + (size_t)l * 3 * C * C, C, qkv, 3 * C);
+                                     md->P(P_LN1B) + l * C, M, C, h));
+        Mm a = mm(gk::GEMM_NT, gk::EPI_STORE, M, 3 * C, C, ln1, C,
+                  (const char*)md->W(P_QKVW) + (size_t)l * 3 * C * C * y.es, C, qkv, 3 * C);
         a.bias = md->P(P_QKVB) + l * 3 * C;
         TRY(run_gemm(md, a));
         {
             const double hs = C / NH;
             const double flops = 4.0 * B * NH * hs * (double)T * (T + 1) / 2.0;
-            LAUNCH(md, GPT2_KC_ATTENTION, flops, f4 * (4.0 * M * C + (double)M * NH),
-                   gk::attention_forward(s, atty, lse, qkv, B, T, C, NH));
+            LAUNCH(md, GPT2_KC_ATTENTION, flops, es * 4.0 * M * C + 4.0 * M * NH,
+                   gk::attention_forward(s, atty, lse, qkv, B, T, C, NH, h));
         }
-        a = gemm_args(gk::GEMM_NT, gk::EPI_RESID, M, C, C, atty, C,
-                      md->P(P_ATTPROJW) + (size_t)l * C * C, C, res2, C);
+        a = mm(gk::GEMM_NT, gk::EPI_RESID, M, C, C, atty, C,
+               (const char*)md->W(P_ATTPROJW) + (size_t)l * C * C * y.es, C, res2, C);
         a.bias = md->P(P_ATTPROJB) + l * C;
         a.aux = resid;
         a.ldaux = C;
         TRY(run_gemm(md, a));
-        LAUNCH(md, GPT2_KC_LAYERNORM, 0, f4 * (2.0 * M * C + 2.0 * M),
+        LAUNCH(md, GPT2_KC_LAYERNORM, 0, es * 2.0 * M * C + 8.0 * M,
                gk::layernorm_forward(s, ln2, ln2m, ln2r, res2, md->P(P_LN2W) + l * C,
-                                     md->P(P_LN2B) + l * C, M, C));
-        a = gemm_args(gk::GEMM_NT, gk::EPI_GELU, M, 4 * C, C, ln2, C,
-                      md->P(P_FCW) + (size_t)l * 4 * C * C, C, fch, 4 * C);
+                                     md->P(P_LN2B) + l * C, M, C, h));
+        a = mm(gk::GEMM_NT, gk::EPI_GELU, M, 4 * C, C, ln2, C,
+               (const char*)md->W(P_FCW) + (size_t)l * 4 * C * C * y.es, C, fch, 4 * C);
         a.bias = md->P(P_FCB) + l * 4 * C;
         a.out2 = fchg;
         TRY(run_gemm(md, a));
-        a = gemm_args(gk::GEMM_NT, gk::EPI_RESID, M, C, 4 * C, fchg, 4 * C,
-                      md->P(P_FCPROJW) + (size_t)l * C * 4 * C, 4 * C, res3, C);
+        a = mm(gk::GEMM_NT, gk::EPI_RESID, M, C, 4 * C, fchg, 4 * C,
+               (const char*)md->W(P_FCPROJW) + (size_t)l * C * 4 * C * y.es, 4 * C, res3, C);
         a.bias = md->P(P_FCPROJB) + l * C;
         a.aux = res2;
         a.ldaux = C;
         TRY(run_gemm(md, a));
     }
-    const float* last = md->at<float>(y.res3) + (L - 1) * MC;
-    float* lnf = md->at<float>(y.lnf);
-    LAUNCH(md, GPT2_KC_LAYERNORM, 0, f4 * (2.0 * M * C + 2.0 * M),
+    const void* last = md->A(y.res3, (L - 1) * MC);
+    void* lnf = md->A(y.lnf);
+    LAUNCH(md, GPT2_KC_LAYERNORM, 0, es * 2.0 * M * C + 8.0 * M,
            gk::layernorm_forward(s, lnf, md->at<float>(y.lnf_mean), md->at<float>(y.lnf_rstd),
-                                 last, md->P(P_LNFW), md->P(P_LNFB), M, C));
-    float* logits = md->at<float>(y.logits);
-    TRY(run_gemm(md, gemm_args(gk::GEMM_NT, gk::EPI_STORE, M, V, C, lnf, C, md->P(P_WTE), C,
-                               logits, y.Vp)));
+                                 last, md->P(P_LNFW), md->P(P_LNFB), M, C, h));
+    void* logits = md->A(y.logits);
+    TRY(run_gemm(md, mm(gk::GEMM_NT, gk::EPI_STORE, M, V, C, lnf, C, md->W(P_WTE), C, logits,
+                        y.Vp)));
     if (tgt) {
         float* losses = md->at<float>(y.losses);
-        LAUNCH(md, GPT2_KC_SOFTMAX_CE, 0, f4 * 2.0 * M * (double)V + 8.0 * M,
-               gk::softmax_ce(s, logits, losses, tgt, M, V, y.Vp, 1.0f / M, md->flag()));
+        LAUNCH(md, GPT2_KC_SOFTMAX_CE, 0, es * 2.0 * M * (double)V + 8.0 * M,
+               gk::softmax_ce(s, logits, losses, tgt, M, V, y.Vp, 1.0f / M, md->flag(), h));
         LAUNCH(md, GPT2_KC_OTHER, 0, 4.0 * M, gk::mean_reduce(s, md->dloss(), losses, M));
         const int np2 = 1 << ceil_log2(M);
         LAUNCH(md, GPT2_KC_OTHER, 0, 4.0 * M + 4.0 * np2,
@@ -411,91 +480,96 @@ int check_bt(gpt2_model* md, int B, int T) {
 int backward_impl(gpt2_model* md) {
     const Layout& y = md->lay;
     const int L = y.L, C = y.C, NH = y.NH, V = y.V, B = md->B, T = md->T, M = B * T;
+    const int h = y.bf16;
     const size_t MC = (size_t)y.M * C;
-    const double f4 = 4.0;
+    const size_t wes = y.es;  // bytes per weight element of the matmul copy
+    const double es = (double)y.es;
     hipStream_t s = md->stream;
-    float* dres = md->at<float>(y.dres);
-    float* dtmp = md->at<float>(y.dtmp);
-    float* dqkv = md->at<float>(y.dqkv);
-    float* dfch = md->at<float>(y.dfch);
+    void* dres = md->A(y.dres);
+    void* dtmp = md->A(y.dtmp);
+    void* dqkv = md->A(y.dqkv);
+    void* dfch = md->A(y.dfch);
     float* lnpart = md->at<float>(y.ln_part);
     float* bpart = md->at<float>(y.bias_part);
-    float* dlogits = md->at<float>(y.logits);
-    float* lnf = md->at<float>(y.lnf);
+    void* dlogits = md->A(y.logits);
+    void* lnf = md->A(y.lnf);
+    auto Wl = [&](int i, size_t elems) { return (const char*)md->W(i) + elems * wes; };
 
     // LM head (tied): dlnf = dlogits wte;  dwte += dlogits^T lnf
-    TRY(run_gemm(md, gemm_args(gk::GEMM_NN, gk::EPI_STORE, M, C, V, dlogits, y.Vp,
-                               md->P(P_WTE), C, dtmp, C)));
-    TRY(run_gemm(md, gemm_args(gk::GEMM_TN, gk::EPI_ACCUM, V, C, M, dlogits, y.Vp, lnf, C,
-                               md->G(P_WTE), C)));
-    const float* last = md->at<float>(y.res3) + (L - 1) * MC;
-    LAUNCH(md, GPT2_KC_LAYERNORM, 0, f4 * (3.0 * M * C + 2.0 * M),
+    TRY(run_gemm(md, mm(gk::GEMM_NN, gk::EPI_STORE, M, C, V, dlogits, y.Vp, md->W(P_WTE), C,
+                        dtmp, C)));
+    TRY(run_gemm(md, mm(gk::GEMM_TN, gk::EPI_ACCUM, V, C, M, dlogits, y.Vp, lnf, C,
+                        md->G(P_WTE), C)));
+    const void* last = md->A(y.res3, (L - 1) * MC);
+    LAUNCH(md, GPT2_KC_LAYERNORM, 0, es * 3.0 * M * C + 8.0 * M,
            gk::layernorm_backward(s, dres, 0, md->G(P_LNFW), md->G(P_LNFB), lnpart, dtmp, last,
                                   md->P(P_LNFW), md->at<float>(y.lnf_mean),
-                                  md->at<float>(y.lnf_rstd), M, C));
+                                  md->at<float>(y.lnf_rstd), M, C, h));
     for (int l = L - 1; l >= 0; l--) {
-        const float* resid = l == 0 ? md->at<float>(y.encoded) : md->at<float>(y.res3) + (l - 1) * MC;
-        const float* ln1 = md->at<float>(y.ln1) + l * MC;
+        const void* resid = l == 0 ? (const void*)md->A(y.encoded) : md->A(y.res3, (l - 1) * MC);
+        const void* ln1 = md->A(y.ln1, l * MC);
         const float* ln1m = md->at<float>(y.ln1_mean) + (size_t)l * y.M;
         const float* ln1r = md->at<float>(y.ln1_rstd) + (size_t)l * y.M;
-        const float* qkv = md->at<float>(y.qkv) + l * 3 * MC;
-        const float* atty = md->at<float>(y.atty) + l * MC;
+        const void* qkv = md->A(y.qkv, l * 3 * MC);
+        const void* atty = md->A(y.atty, l * MC);
         const float* lse = md->at<float>(y.lse) + (size_t)l * y.M * NH;
-        const float* res2 = md->at<float>(y.res2) + l * MC;
-        const float* ln2 = md->at<float>(y.ln2) + l * MC;
+        const void* res2 = md->A(y.res2, l * MC);
+        const void* ln2 = md->A(y.ln2, l * MC);
         const float* ln2m = md->at<float>(y.ln2_mean) + (size_t)l * y.M;
         const float* ln2r = md->at<float>(y.ln2_rstd) + (size_t)l * y.M;
-        const float* fch = md->at<float>(y.fch) + l * 4 * MC;
-        const float* fchg = md->at<float>(y.fch_gelu) + l * 4 * MC;
+        const void* fch = md->A(y.fch, l * 4 * MC);
+        const void* fchg = md->A(y.fch_gelu, l * 4 * MC);
 
         // MLP projection: dfch = (dres W) * gelu'(fch);  dW += dres^T gelu(fch)
-        gk::GemmArgs a = gemm_args(gk::GEMM_NN, gk::EPI_GELU_BWD, M, 4 * C, C, dres, C,
-                                   md->P(P_FCPROJW) + (size_t)l * C * 4 * C, 4 * C, dfch, 4 * C);
+        Mm a = mm(gk::GEMM_NN, gk::EPI_GELU_BWD, M, 4 * C, C, dres, C,
+                  Wl(P_FCPROJW, (size_t)l * C * 4 * C), 4 * C, dfch, 4 * C);
         a.aux = fch;
         a.ldaux = 4 * C;
         TRY(run_gemm(md, a));
-        TRY(run_gemm(md, gemm_args(gk::GEMM_TN, gk::EPI_ACCUM, C, 4 * C, M, dres, C, fchg,
-                                   4 * C, md->G(P_FCPROJW) + (size_t)l * C * 4 * C, 4 * C)));
-        LAUNCH(md, GPT2_KC_OTHER, 0, f4 * M * C,
-               gk::bias_grad(s, md->G(P_FCPROJB) + l * C, bpart, dres, M, C, C));
+        TRY(run_gemm(md, mm(gk::GEMM_TN, gk::EPI_ACCUM, C, 4 * C, M, dres, C, fchg, 4 * C,
+                            md->G(P_FCPROJW) + (size_t)l * C * 4 * C, 4 * C)));
+        LAUNCH(md, GPT2_KC_OTHER, 0, es * M * C,
+               gk::bias_grad(s, md->G(P_FCPROJB) + l * C, bpart, dres, M, C, C, h));
         // MLP fc: dln2 = dfch W;  dW += dfch^T ln2
-        TRY(run_gemm(md, gemm_args(gk::GEMM_NN, gk::EPI_STORE, M, C, 4 * C, dfch, 4 * C,
-                                   md->P(P_FCW) + (size_t)l * 4 * C * C, C, dtmp, C)));
-        TRY(run_gemm(md, gemm_args(gk::GEMM_TN, gk::EPI_ACCUM, 4 * C, C, M, dfch, 4 * C, ln2,
-                                   C, md->G(P_FCW) + (size_t)l * 4 * C * C, C)));
-        LAUNCH(md, GPT2_KC_OTHER, 0, f4 * 4.0 * M * C,
-               gk::bias_grad(s, md->G(P_FCB) + l * 4 * C, bpart, dfch, M, 4 * C, 4 * C));
-        LAUNCH(md, GPT2_KC_LAYERNORM, 0, f4 * (4.0 * M * C + 2.0 * M),
+        TRY(run_gemm(md, mm(gk::GEMM_NN, gk::EPI_STORE, M, C, 4 * C, dfch, 4 * C,
+                            Wl(P_FCW, (size_t)l * 4 * C * C), C, dtmp, C)));
+        TRY(run_gemm(md, mm(gk::GEMM_TN, gk::EPI_ACCUM, 4 * C, C, M, dfch, 4 * C, ln2, C,
+                            md->G(P_FCW) + (size_t)l * 4 * C * C, C)));
+        LAUNCH(md, GPT2_KC_OTHER, 0, es * 4.0 * M * C,
+               gk::bias_grad(s, md->G(P_FCB) + l * 4 * C, bpart, dfch, M, 4 * C, 4 * C, h));
+        LAUNCH(md, GPT2_KC_LAYERNORM, 0, es * 4.0 * M * C + 8.0 * M,
                gk::layernorm_backward(s, dres, 1, md->G(P_LN2W) + l * C, md->G(P_LN2B) + l * C,
-                                      lnpart, dtmp, res2, md->P(P_LN2W) + l * C, ln2m, ln2r, M, C));
+                                      lnpart, dtmp, res2, md->P(P_LN2W) + l * C, ln2m, ln2r, M, C,
+                                      h));
         // attention projection: datty = dres W;  dW += dres^T atty
-        TRY(run_gemm(md, gemm_args(gk::GEMM_NN, gk::EPI_STORE, M, C, C, dres, C,
-                                   md->P(P_ATTPROJW) + (size_t)l * C * C, C, dtmp, C)));
-        TRY(run_gemm(md, gemm_args(gk::GEMM_TN, gk::EPI_ACCUM, C, C, M, dres, C, atty, C,
-                                   md->G(P_ATTPROJW) + (size_t)l * C * C, C)));
-        LAUNCH(md, GPT2_KC_OTHER, 0, f4 * M * C,
-               gk::bias_grad(s, md->G(P_ATTPROJB) + l * C, bpart, dres, M, C, C));
+        TRY(run_gemm(md, mm(gk::GEMM_NN, gk::EPI_STORE, M, C, C, dres, C,
+                            Wl(P_ATTPROJW, (size_t)l * C * C), C, dtmp, C)));
+        TRY(run_gemm(md, mm(gk::GEMM_TN, gk::EPI_ACCUM, C, C, M, dres, C, atty, C,
+                            md->G(P_ATTPROJW) + (size_t)l * C * C, C)));
+        LAUNCH(md, GPT2_KC_OTHER, 0, es * M * C,
+               gk::bias_grad(s, md->G(P_ATTPROJB) + l * C, bpart, dres, M, C, C, h));
         {
             const double hs = C / NH;
             const double flops = 8.0 * B * NH * hs * (double)T * (T + 1) / 2.0;
-            LAUNCH(md, GPT2_KC_ATTENTION, flops, f4 * (7.0 * M * C + 2.0 * M * NH),
+            LAUNCH(md, GPT2_KC_ATTENTION, flops, es * 7.0 * M * C + 8.0 * M * NH,
                    gk::attention_backward(s, dqkv, md->at<float>(y.attn_d), dtmp, qkv, atty, lse,
-                                          B, T, C, NH));
+                                          B, T, C, NH, h));
         }
         // QKV: dln1 = dqkv W;  dW += dqkv^T ln1
-        TRY(run_gemm(md, gemm_args(gk::GEMM_NN, gk::EPI_STORE, M, C, 3 * C, dqkv, 3 * C,
-                                   md->P(P_QKVW) + (size_t)l * 3 * C * C, C, dtmp, C)));
-        TRY(run_gemm(md, gemm_args(gk::GEMM_TN, gk::EPI_ACCUM, 3 * C, C, M, dqkv, 3 * C, ln1, C,
-                                   md->G(P_QKVW) + (size_t)l * 3 * C * C, C)));
-        LAUNCH(md, GPT2_KC_OTHER, 0, f4 * 3.0 * M * C,
-               gk::bias_grad(s, md->G(P_QKVB) + l * 3 * C, bpart, dqkv, M, 3 * C, 3 * C));
-        LAUNCH(md, GPT2_KC_LAYERNORM, 0, f4 * (4.0 * M * C + 2.0 * M),
+        TRY(run_gemm(md, mm(gk::GEMM_NN, gk::EPI_STORE, M, C, 3 * C, dqkv, 3 * C,
+                            Wl(P_QKVW, (size_t)l * 3 * C * C), C, dtmp, C)));
+        TRY(run_gemm(md, mm(gk::GEMM_TN, gk::EPI_ACCUM, 3 * C, C, M, dqkv, 3 * C, ln1, C,
+                            md->G(P_QKVW) + (size_t)l * 3 * C * C, C)));
+        LAUNCH(md, GPT2_KC_OTHER, 0, es * 3.0 * M * C,
+               gk::bias_grad(s, md->G(P_QKVB) + l * 3 * C, bpart, dqkv, M, 3 * C, 3 * C, h));
+        LAUNCH(md, GPT2_KC_LAYERNORM, 0, es * 4.0 * M * C + 8.0 * M,
                gk::layernorm_backward(s, dres, 1, md->G(P_LN1W) + l * C, md->G(P_LN1B) + l * C,
-                                      lnpart, dtmp, resid, md->P(P_LN1W) + l * C, ln1m, ln1r, M, C));
+                                      lnpart, dtmp, resid, md->P(P_LN1W) + l * C, ln1m, ln1r, M, C,
+                                      h));
     }
-    LAUNCH(md, GPT2_KC_OTHER, 0, f4 * (2.0 * M * C + 2.0 * T * C) + 4.0 * M,
+    LAUNCH(md, GPT2_KC_OTHER, 0, es * M * C + 8.0 * M * C + 8.0 * T * C + 4.0 * M,
            gk::encoder_backward(s, md->G(P_WTE), md->G(P_WPE), dres, md->at<uint32_t>(y.keys), B,
-                                T, C, V, y.pos_bits));
+                                T, C, V, y.pos_bits, h));
     return GPT2_OK;
 }
 
@@ -628,7 +702,14 @@ int gpt2_copy_params(gpt2_model* md, float* dst, const float* src) {
     TRY(hip_check(hipStreamSynchronize(md->stream), "synchronize"));
     if (dst)
         return hip_check(hipMemcpy(dst, md->P(0), bytes, hipMemcpyDeviceToHost), "copy params");
-    return hip_check(hipMemcpy(md->P(0), src, bytes, hipMemcpyHostToDevice), "copy params");
+    TRY(hip_check(hipMemcpy(md->P(0), src, bytes, hipMemcpyHostToDevice), "copy params"));
+    if (md->lay.bf16) {
+        TRY(hip_check(gk::to_bf16(md->stream, md->at<uint16_t>(md->lay.shadow), md->P(0),
+                                  md->lay.nparams),
+                      "bf16 weight copy"));
+        TRY(hip_check(hipStreamSynchronize(md->stream), "synchronize"));
+    }
+    return GPT2_OK;
 }
 
 int gpt2_copy_grads(gpt2_model* md, float* dst) {
@@ -660,27 +741,28 @@ int gpt2_copy_activation(gpt2_model* md, const char* name, int layer, float* dst
         size_t off;
         size_t layer_stride;  // elements; 0 = not per layer
         int64_t width;        // per row of B*T
+        bool act;             // activation storage type (else fp32 statistics)
     };
     const Item items[] = {
-        {"encoded", y.encoded, 0, C},
-        {"ln1", y.ln1, MC, C},
-        {"ln1_mean", y.ln1_mean, (size_t)y.M, 1},
-        {"ln1_rstd", y.ln1_rstd, (size_t)y.M, 1},
-        {"qkv", y.qkv, 3 * MC, 3 * C},
-        {"atty", y.atty, MC, C},
-        {"att_lse", y.lse, (size_t)y.M * y.NH, y.NH},
-        {"residual2", y.res2, MC, C},
-        {"ln2", y.ln2, MC, C},
-        {"ln2_mean", y.ln2_mean, (size_t)y.M, 1},
-        {"ln2_rstd", y.ln2_rstd, (size_t)y.M, 1},
-        {"fch", y.fch, 4 * MC, 4 * C},
-        {"fch_gelu", y.fch_gelu, 4 * MC, 4 * C},
-        {"residual3", y.res3, MC, C},
-        {"lnf", y.lnf, 0, C},
-        {"lnf_mean", y.lnf_mean, 0, 1},
-        {"lnf_rstd", y.lnf_rstd, 0, 1},
-        {"logits", y.logits, 0, y.V},
-        {"losses", y.losses, 0, 1},
+        {"encoded", y.encoded, 0, C, true},
+        {"ln1", y.ln1, MC, C, true},
+        {"ln1_mean", y.ln1_mean, (size_t)y.M, 1, false},
+        {"ln1_rstd", y.ln1_rstd, (size_t)y.M, 1, false},
+        {"qkv", y.qkv, 3 * MC, 3 * C, true},
+        {"atty", y.atty, MC, C, true},
+        {"att_lse", y.lse, (size_t)y.M * y.NH, y.NH, false},
+        {"residual2", y.res2, MC, C, true},
+        {"ln2", y.ln2, MC, C, true},
+        {"ln2_mean", y.ln2_mean, (size_t)y.M, 1, false},
+        {"ln2_rstd", y.ln2_rstd, (size_t)y.M, 1, false},
+        {"fch", y.fch, 4 * MC, 4 * C, true},
+        {"fch_gelu", y.fch_gelu, 4 * MC, 4 * C, true},
+        {"residual3", y.res3, MC, C, true},
+        {"lnf", y.lnf, 0, C, true},
+        {"lnf_mean", y.lnf_mean, 0, 1, false},
+        {"lnf_rstd", y.lnf_rstd, 0, 1, false},
+        {"logits", y.logits, 0, y.V, true},
+        {"losses", y.losses, 0, 1, false},
     };
     for (const Item& it : items) {
         if (std::strcmp(it.n, name)) continue;
@@ -690,13 +772,31 @@ int gpt2_copy_activation(gpt2_model* md, const char* name, int layer, float* dst
         if (numel) *numel = n;
         if (!dst) return GPT2_OK;
         TRY(hip_check(hipStreamSynchronize(md->stream), "synchronize"));
-        const float* src = md->at<float>(it.off) + (it.layer_stride ? layer * it.layer_stride : 0);
-        if (std::strcmp(name, "logits") == 0)
-            return hip_check(hipMemcpy2D(dst, y.V * sizeof(float), src, y.Vp * sizeof(float),
-                                         y.V * sizeof(float), M, hipMemcpyDeviceToHost),
-                             "copy logits");
-        return hip_check(hipMemcpy(dst, src, n * sizeof(float), hipMemcpyDeviceToHost),
-                         "copy activation");
+        const size_t es = it.act ? y.es : sizeof(float);
+        const char* src = md->base + it.off + (it.layer_stride ? layer * it.layer_stride : 0) * es;
+        const bool logits = std::strcmp(name, "logits") == 0;
+        if (es == sizeof(float)) {
+            if (logits)
+                return hip_check(hipMemcpy2D(dst, y.V * sizeof(float), src, y.Vp * sizeof(float),
+                                             y.V * sizeof(float), M, hipMemcpyDeviceToHost),
+                                 "copy logits");
+            return hip_check(hipMemcpy(dst, src, n * sizeof(float), hipMemcpyDeviceToHost),
+                             "copy activation");
+        }
+        // bf16: copy the bits, widen on the host (bf16 is the top half of fp32)
+        std::vector<uint16_t> tmp((size_t)n);
+        if (logits)
+            TRY(hip_check(hipMemcpy2D(tmp.data(), y.V * 2, src, y.Vp * 2, y.V * 2, M,
+                                      hipMemcpyDeviceToHost),
+                          "copy logits"));
+        else
+            TRY(hip_check(hipMemcpy(tmp.data(), src, n * 2, hipMemcpyDeviceToHost),
+                          "copy activation"));
+        for (int64_t i = 0; i < n; i++) {
+            const uint32_t u = (uint32_t)tmp[(size_t)i] << 16;
+            std::memcpy(dst + i, &u, 4);
+        }
+        return GPT2_OK;
     }
     return fail(GPT2_EINVAL, "unknown activation name '%s'", name);
 }
@@ -768,9 +868,11 @@ int gpt2_update(gpt2_model* md, float lr, float beta1, float beta2, float eps,
     const float bc1 = (float)(1.0 - std::pow((double)beta1, (double)step));
     const float bc2 = (float)(1.0 - std::pow((double)beta2, (double)step));
     const int64_t n = md->lay.nparams;
-    LAUNCH(md, GPT2_KC_ADAMW, 0, 28.0 * n,
+    LAUNCH(md, GPT2_KC_ADAMW, 0, (md->lay.bf16 ? 30.0 : 28.0) * n,
            gk::adamw(md->stream, md->P(0), md->G(0), md->at<float>(md->lay.m),
-                     md->at<float>(md->lay.v), n, lr, beta1, beta2, eps, weight_decay, bc1, bc2));
+                     md->at<float>(md->lay.v),
+                     md->lay.bf16 ? md->at<uint16_t>(md->lay.shadow) : nullptr, n, lr, beta1,
+                     beta2, eps, weight_decay, bc1, bc2));
     return GPT2_OK;
 }
 

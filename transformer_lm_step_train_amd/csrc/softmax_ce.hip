@@ -41,15 +41,15 @@ __device__ __forceinline__ float block_sum(float v, float* sh) {
     return r;
 }
 
-template <int NT, int NJ>
-__global__ __launch_bounds__(NT) void softmax_ce_kernel(float* __restrict__ logits,
+template <int NT, int NJ, class T>
+__global__ __launch_bounds__(NT) void softmax_ce_kernel(T* __restrict__ logits,
                                                         float* __restrict__ losses,
                                                         const int32_t* __restrict__ targets,
                                                         int V, int ldv, float dscale,
                                                         int* __restrict__ flag) {
     __shared__ float sh[NT / 64];
     const int64_t row = blockIdx.x;
-    float* z = logits + row * ldv;
+    T* z = logits + row * ldv;
     const int V4 = ldv >> 2;
     const int tgt = targets[row];
     const bool bad = tgt < 0 || tgt >= V;
@@ -60,7 +60,7 @@ __global__ __launch_bounds__(NT) void softmax_ce_kernel(float* __restrict__ logi
         const int c4 = threadIdx.x + NT * j;
         float4 x = make_float4(-INFINITY, -INFINITY, -INFINITY, -INFINITY);
         if (c4 < V4) {
-            x = ld4(z + 4 * c4);
+            x = Act<T>::ld(z + 4 * c4);
             const int c = 4 * c4;
             if (c >= V) x.x = -INFINITY;
             if (c + 1 >= V) x.y = -INFINITY;
@@ -71,7 +71,7 @@ __global__ __launch_bounds__(NT) void softmax_ce_kernel(float* __restrict__ logi
         mx = fmaxf(mx, fmaxf(fmaxf(x.x, x.y), fmaxf(x.z, x.w)));
     }
     float zt = 0.f;
-    if (threadIdx.x == 0 && !bad) zt = z[tgt];
+    if (threadIdx.x == 0 && !bad) zt = Act<T>::ld1(z + tgt);
     mx = block_max<NT>(mx, sh);
     float s = 0.f;
 #pragma unroll
@@ -94,17 +94,32 @@ __global__ __launch_bounds__(NT) void softmax_ce_kernel(float* __restrict__ logi
             d.z = (expf(v[j].z - lse) - (c + 2 == tgt ? 1.f : 0.f)) * dscale;
             d.w = (expf(v[j].w - lse) - (c + 3 == tgt ? 1.f : 0.f)) * dscale;
             if (bad) d = make_float4(0.f, 0.f, 0.f, 0.f);
-            st4(z + c, d);  // exp(-inf) = 0 in the padding columns
+            Act<T>::st(z + c, d);  // exp(-inf) = 0 in the padding columns
         }
     }
 }
 
-template <int NT, int NJ>
-hipError_t launch_ce(hipStream_t s, float* logits, float* losses, const int32_t* targets,
-                     int N, int V, int ldv, float dscale, int* flag) {
-    hipLaunchKernelGGL((softmax_ce_kernel<NT, NJ>), dim3(N), dim3(NT), 0, s, logits, losses,
+template <int NT, int NJ, class T>
+hipError_t launch_ce(hipStream_t s, T* logits, float* losses, const int32_t* targets, int N,
+                     int V, int ldv, float dscale, int* flag) {
+    hipLaunchKernelGGL((softmax_ce_kernel<NT, NJ, T>), dim3(N), dim3(NT), 0, s, logits, losses,
                        targets, V, ldv, dscale, flag);
     return hipGetLastError();
+}
+
+template <class T>
+hipError_t softmax_ce_t(hipStream_t s, T* logits, float* losses, const int32_t* targets, int N,
+                        int V, int ldv, float dscale, int* flag) {
+    const int V4 = ldv / 4;
+    if (V4 <= 256) return launch_ce<256, 1>(s, logits, losses, targets, N, V, ldv, dscale, flag);
+    const int nj = (V4 + 1023) / 1024;
+    if (nj <= 1) return launch_ce<1024, 1>(s, logits, losses, targets, N, V, ldv, dscale, flag);
+    if (nj <= 2) return launch_ce<1024, 2>(s, logits, losses, targets, N, V, ldv, dscale, flag);
+    if (nj <= 4) return launch_ce<1024, 4>(s, logits, losses, targets, N, V, ldv, dscale, flag);
+    if (nj <= 8) return launch_ce<1024, 8>(s, logits, losses, targets, N, V, ldv, dscale, flag);
+    if (nj <= 13) return launch_ce<1024, 13>(s, logits, losses, targets, N, V, ldv, dscale, flag);
+    if (nj <= 16) return launch_ce<1024, 16>(s, logits, losses, targets, N, V, ldv, dscale, flag);
+    return hipErrorInvalidValue;
 }
 
 __global__ __launch_bounds__(1024) void mean_kernel(float* __restrict__ out,
@@ -124,19 +139,13 @@ __global__ __launch_bounds__(1024) void mean_kernel(float* __restrict__ out,
 
 }  // namespace
 
-hipError_t softmax_ce(hipStream_t s, float* logits, float* losses, const int32_t* targets,
-                      int N, int V, int ldv, float dscale, int* flag) {
+hipError_t softmax_ce(hipStream_t s, void* logits, float* losses, const int32_t* targets,
+                      int N, int V, int ldv, float dscale, int* flag, int bf16) {
     if (N <= 0) return hipSuccess;
-    const int V4 = ldv / 4;
-    if (V4 <= 256) return launch_ce<256, 1>(s, logits, losses, targets, N, V, ldv, dscale, flag);
-    const int nj = (V4 + 1023) / 1024;
-    if (nj <= 1) return launch_ce<1024, 1>(s, logits, losses, targets, N, V, ldv, dscale, flag);
-    if (nj <= 2) return launch_ce<1024, 2>(s, logits, losses, targets, N, V, ldv, dscale, flag);
-    if (nj <= 4) return launch_ce<1024, 4>(s, logits, losses, targets, N, V, ldv, dscale, flag);
-    if (nj <= 8) return launch_ce<1024, 8>(s, logits, losses, targets, N, V, ldv, dscale, flag);
-    if (nj <= 13) return launch_ce<1024, 13>(s, logits, losses, targets, N, V, ldv, dscale, flag);
-    if (nj <= 16) return launch_ce<1024, 16>(s, logits, losses, targets, N, V, ldv, dscale, flag);
-    return hipErrorInvalidValue;
+    if (bf16)
+        return softmax_ce_t<uint16_t>(s, (uint16_t*)logits, losses, targets, N, V, ldv, dscale,
+                                      flag);
+    return softmax_ce_t<float>(s, (float*)logits, losses, targets, N, V, ldv, dscale, flag);
 }
 
 hipError_t mean_reduce(hipStream_t s, float* out, const float* x, int n) {
