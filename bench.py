@@ -12,6 +12,7 @@ timed steps.  The CPU-oracle baseline is timed afterwards on a bounded sample
 (one sequence of the same batch shape) on the host cores.
 """
 import argparse
+import hashlib
 import json
 import os
 import sys
@@ -39,6 +40,20 @@ def parse():
     ap.add_argument("--no-kernel-timing", action="store_true",
                     help="do not record per-launch HIP events in the timed steps")
     return ap.parse_args()
+
+
+def measured_traffic(bf16):
+    """HBM bytes per matmul launch from the committed rocprofv3 FETCH_SIZE /
+    WRITE_SIZE summary, or None if the matmul source has changed since the
+    counters were taken (or for the bf16 model, which they do not cover)."""
+    path = os.path.join(ROOT, "profiles", "gemm_fp32_traffic.json")
+    if bf16 or not os.path.exists(path):
+        return None
+    rec = json.load(open(path))
+    src = os.path.join(ROOT, "transformer_lm_step_train_amd", "csrc", "gemm.hip")
+    if hashlib.sha256(open(src, "rb").read()).hexdigest() != rec["source_sha256_gemm_hip"]:
+        return None
+    return round(rec["hbm_bytes_per_launch"])
 
 
 def cpu_baseline(c, params, tok, tgt):
@@ -127,7 +142,9 @@ def main():
         achieved = (g["flops"] / n) / avg_s / 1e12 if avg_s > 0 else 0.0
         roofline = {"bound": "mfma", "achieved": round(achieved, 2),
                     "peak": peak, "unit": "TFLOP/s",
-                    "frac": round(achieved / peak, 4), "traffic": None,
+                    "frac": round(achieved / peak, 4), "traffic": measured_traffic(bf16),
+                    "traffic_unit": "HBM bytes per launch (rocprofv3 FETCH_SIZE+WRITE_SIZE)",
+                    "algorithmic_bytes_per_launch": round(g["bytes"] / n),
                     "kernel": "gemm (all %s MFMA matmul launches of the step)"
                               % ("bf16" if bf16 else "fp32"),
                     "launches_per_step": n // args.steps,
