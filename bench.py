@@ -33,7 +33,7 @@ def parse():
     ap = argparse.ArgumentParser()
     ap.add_argument("--gpus", type=int, default=1)
     ap.add_argument("--steps", type=int, default=20)
-    ap.add_argument("--warmup", type=int, default=3)
+    ap.add_argument("--warmup", type=int, default=5)
     ap.add_argument("--no-cpu-baseline", action="store_true")
     ap.add_argument("--precision", choices=["fp32", "bf16"], default="fp32",
                     help="fp32 (the headline workload) or the bf16 mixed-precision model")
@@ -101,11 +101,13 @@ def main():
 
     step = 0
     losses = []
+    marks = []
 
     def train_step():
         nonlocal step
         step += 1
         losses.append(m.forward_device(dtok, dtgt))
+        marks.append(time.perf_counter())
         m.zero_grad()
         m.backward()
         m.update(step=step, **adamw)
@@ -113,6 +115,7 @@ def main():
     for _ in range(args.warmup):
         train_step()
     m.synchronize()
+    marks.clear()
     if not args.no_kernel_timing:
         gpt2.gpt2_profile(m.h, True)
     torch.cuda.synchronize()
@@ -124,6 +127,10 @@ def main():
     dt = time.perf_counter() - t0
     ms = 1000.0 * dt / args.steps
     tokens_per_s = B * T * args.steps / dt
+    # The loss readback of step i+1 ends one full step after that of step i
+    # (zero-grad, backward and AdamW of step i, forward of step i+1).
+    per_step = np.diff(np.array(marks)) * 1000.0
+    ms_median = float(np.median(per_step)) if len(per_step) else ms
 
     kc = {}
     if not args.no_kernel_timing:
@@ -134,8 +141,15 @@ def main():
     m.close()
 
     roofline = None
+    step_roof = None
     peak = MFMA_BF16_PEAK_TFLOPS if bf16 else MFMA_FP32_PEAK_TFLOPS
     if kc:
+        # Composite bound of the whole step: every kernel class at the larger
+        # of its MFMA time and its HBM time for the algorithmic work.
+        t_roof = sum(max(r["flops"] / (peak * 1e12), r["bytes"] / (HBM_PEAK_GBS * 1e9))
+                     for r in kc.values()) / args.steps * 1000.0
+        step_roof = {"t_roof_ms": round(t_roof, 3), "frac": round(t_roof / ms, 4),
+                     "rule": "sum over kernel classes of max(FLOP/MFMA peak, bytes/HBM peak)"}
         g = kc["gemm"]
         n = max(g["launches"], 1)
         avg_s = g["ms"] / n / 1000.0
@@ -169,6 +183,7 @@ def main():
         "steps": args.steps,
         "warmup": args.warmup,
         "ms_per_step": round(ms, 3),
+        "ms_per_step_median": round(ms_median, 3),
         "higher_is_better": True,
         "scaling": "weak",
         "vs_baseline": None,
@@ -179,6 +194,7 @@ def main():
                    "global_batch": B, "seq_len": T, "layers": c["L"], "channels": c["C"],
                    "heads": c["NH"], "vocab": c["V"], "parallelism": "single GPU"},
         "roofline": roofline,
+        "step_roofline": step_roof,
         "cpu_baseline": None,
         "kernel_ms_per_step": {k: round(v["ms"] / args.steps, 3) for k, v in kc.items()},
         "loss_first_last": [round(losses[0], 5), round(losses[-1], 5)],
