@@ -12,7 +12,10 @@
 // each load has two steps of MFMA work to arrive.  Within a step the two
 // 32-lane halves of a wave own k = 0..15 and k = 16..31, so an operand
 // stored k-contiguous is read from LDS as float4 (four MFMA steps per read).
-// Tiles wholly inside the matrices load without bounds checks.
+// The main loop loads only whole reduction steps, with rows past the
+// matrix clamped to its last row, so every step issues the same loads and
+// the wait for the registers of the previous step is exact; a partial last
+// step is loaded with zero padding after the loop.
 //
 // Operands whose reduction index is contiguous in HBM are stored in LDS as
 // [row][k] (36-float rows); operands whose free index is contiguous are
@@ -25,6 +28,7 @@
 // over few output tiles are split over K into a workspace and summed in a
 // fixed order by a second kernel, so results are deterministic.
 #include <algorithm>
+#include <cmath>
 #include <type_traits>
 
 #include "common.h"
@@ -50,27 +54,26 @@ struct Tile<true, R, NT> {
     static constexpr int FLOATS = R * FM_LD;
     static constexpr int PER = R * 8 / NT;
     float4 v[PER];
-    template <bool CHECK>
+    // Rows past the matrix read its last row instead (their products land
+    // only in outputs that are never stored).  TAIL loads a last, partial
+    // step of the reduction and zeroes k >= K; the main loop loads only
+    // whole steps and so always issues the same loads.
+    template <bool TAIL>
     __device__ __forceinline__ void load(const float* __restrict__ g, int64_t ld, int r0, int Rn,
                                          int k0, int K) {
 #pragma unroll
         for (int i = 0; i < PER; i++) {
             const int idx = threadIdx.x + NT * i;
-            const int r = r0 + (idx >> 3);
+            const int r = min(r0 + (idx >> 3), Rn - 1);
             const int k = k0 + (idx & 7) * 4;
-            const float* p = g + (int64_t)r * ld + k;
-            if (!CHECK) {
-                v[i] = ld4(p);
+            if (!TAIL) {
+                v[i] = ld4(g + (int64_t)r * ld + k);
             } else {
-                float4 x = make_float4(0.f, 0.f, 0.f, 0.f);
-                if (r < Rn) {
-                    if (k + 3 < K) x = ld4(p);
-                    else {
-                        if (k < K) x.x = p[0];
-                        if (k + 1 < K) x.y = p[1];
-                        if (k + 2 < K) x.z = p[2];
-                    }
-                }
+                float4 x = ld4(g + (int64_t)r * ld + (k < K ? k : 0));
+                x.x = k < K ? x.x : 0.f;
+                x.y = k + 1 < K ? x.y : 0.f;
+                x.z = k + 2 < K ? x.z : 0.f;
+                x.w = k + 3 < K ? x.w : 0.f;
                 v[i] = x;
             }
         }
@@ -94,28 +97,23 @@ struct Tile<false, R, NT> {
     static constexpr int PER = BK * R / 4 / NT;
     static constexpr int R4 = R / 4;
     float4 v[PER];
-    template <bool CHECK>
+    // A float4 that starts inside the matrix but runs past its last row
+    // reads the row's padding (leading dimensions are multiples of 4); one
+    // that starts past it reads the last whole float4 instead.
+    template <bool TAIL>
     __device__ __forceinline__ void load(const float* __restrict__ g, int64_t ld, int r0, int Rn,
                                          int k0, int K) {
 #pragma unroll
         for (int i = 0; i < PER; i++) {
             const int idx = threadIdx.x + NT * i;
             const int k = k0 + idx / R4;
-            const int r = r0 + (idx % R4) * 4;
-            const float* p = g + (int64_t)k * ld + r;
-            if (!CHECK) {
-                v[i] = ld4(p);
+            int r = r0 + (idx % R4) * 4;
+            r = r < Rn ? r : ((Rn - 1) & ~3);
+            if (!TAIL) {
+                v[i] = ld4(g + (int64_t)k * ld + r);
             } else {
-                float4 x = make_float4(0.f, 0.f, 0.f, 0.f);
-                if (k < K) {
-                    if (r + 3 < Rn) x = ld4(p);
-                    else {
-                        if (r < Rn) x.x = p[0];
-                        if (r + 1 < Rn) x.y = p[1];
-                        if (r + 2 < Rn) x.z = p[2];
-                    }
-                }
-                v[i] = x;
+                const float4 x = ld4(g + (int64_t)(k < K ? k : 0) * ld + r);
+                v[i] = k < K ? x : make_float4(0.f, 0.f, 0.f, 0.f);
             }
         }
     }
@@ -207,8 +205,6 @@ __global__ __launch_bounds__(NTHR, 2) void gemm_kernel(
 
     const int k_begin = blockIdx.z * kchunk;
     const int k_end = min(a.K, k_begin + kchunk);
-    const int nk = k_end > k_begin ? (k_end - k_begin + BK - 1) / BK : 0;
-    const bool interior = (m0 + BM <= a.M) && (n0 + BN <= a.N);
 
     const int lane = threadIdx.x & 63, wave = threadIdx.x >> 6;
     const int wm = (wave >> 1) * 64, wn = (wave & 1) * 64;
@@ -224,35 +220,18 @@ __global__ __launch_bounds__(NTHR, 2) void gemm_kernel(
 
     TA ta[PF];
     TB tb[PF];
+    const int nfull = (k_end - k_begin) / BK;  // whole reduction steps
+    // Every step of the main loop issues the same loads (past the last
+    // whole step it reloads that step, never stored), so the wait for the
+    // previous step's registers is exact and two steps of loads stay in
+    // flight.
     auto issue = [&](auto slotc, int kt) {
         constexpr int S = decltype(slotc)::value;
-        const int kk = k_begin + kt * BK;
-        if (interior && kk + BK <= k_end) {
-            ta[S].template load<false>(a.A, a.lda, m0, a.M, kk, k_end);
-            tb[S].template load<false>(a.B, a.ldb, n0, a.N, kk, k_end);
-        } else {
-            ta[S].template load<true>(a.A, a.lda, m0, a.M, kk, k_end);
-            tb[S].template load<true>(a.B, a.ldb, n0, a.N, kk, k_end);
-        }
+        const int kk = k_begin + min(kt, nfull - 1) * BK;
+        ta[S].template load<false>(a.A, a.lda, m0, a.M, kk, k_end);
+        tb[S].template load<false>(a.B, a.ldb, n0, a.N, kk, k_end);
     };
-    using I0 = std::integral_constant<int, 0>;
-    using I1 = std::integral_constant<int, 1>;
-    if (nk > 0) {
-        issue(I0{}, 0);
-        ta[0].store(sm);
-        tb[0].store(sm + 2 * TA::FLOATS);
-        if (nk > 1) issue(I1{}, 1);
-    }
-    __syncthreads();
-    // Tile j's registers live in slot j & 1: while step j computes from LDS,
-    // tile j+2 is loading into the slot step j-1 just emptied into LDS.
-    auto step = [&](int kt, auto slotc) {
-        constexpr int S = decltype(slotc)::value;
-        constexpr int NS = S ^ 1;
-        const int cur = kt & 1;
-        if (kt + 2 < nk) issue(slotc, kt + 2);
-        const float* sa = sm + cur * TA::FLOATS;
-        const float* sb = sm + 2 * TA::FLOATS + cur * TB::FLOATS;
+    auto compute = [&](const float* sa, const float* sb) {
 #pragma unroll
         for (int q = 0; q < 4; q++) {
             const float4 a0 = TA::frag(sa, wm + li, g, q);
@@ -276,15 +255,45 @@ __global__ __launch_bounds__(NTHR, 2) void gemm_kernel(
             acc[1][0] = mfma(a1.w, b0.w, acc[1][0]);
             acc[1][1] = mfma(a1.w, b1.w, acc[1][1]);
         }
-        if (kt + 1 < nk) {
-            ta[NS].store(sm + (cur ^ 1) * TA::FLOATS);
-            tb[NS].store(sm + 2 * TA::FLOATS + (cur ^ 1) * TB::FLOATS);
-        }
+    };
+    using I0 = std::integral_constant<int, 0>;
+    using I1 = std::integral_constant<int, 1>;
+    if (nfull > 0) {
+        issue(I0{}, 0);
+        ta[0].store(sm);
+        tb[0].store(sm + 2 * TA::FLOATS);
+        issue(I1{}, 1);
+    }
+    __syncthreads();
+    // Tile j's registers live in slot j & 1: while step j computes from LDS,
+    // tile j+2 is loading into the slot step j-1 just emptied into LDS.
+    auto step = [&](int kt, auto slotc) {
+        constexpr int S = decltype(slotc)::value;
+        constexpr int NS = S ^ 1;
+        const int cur = kt & 1;
+        issue(slotc, kt + 2);
+        compute(sm + cur * TA::FLOATS, sm + 2 * TA::FLOATS + cur * TB::FLOATS);
+        // Unconditional, so that no path reaches the next step's loads with
+        // this slot still pending (after the last step the buffer is unused).
+        ta[NS].store(sm + (cur ^ 1) * TA::FLOATS);
+        tb[NS].store(sm + 2 * TA::FLOATS + (cur ^ 1) * TB::FLOATS);
         __syncthreads();
     };
-    for (int kt = 0; kt < nk; kt += 2) {
+    int kt = 0;
+    for (; kt + 1 < nfull; kt += 2) {
         step(kt, I0{});
-        if (kt + 1 < nk) step(kt + 1, I1{});
+        step(kt + 1, I1{});
+    }
+    if (kt < nfull) step(kt, I0{});
+    if (k_begin + nfull * BK < k_end) {  // partial last step, zero-padded
+        const int kk = k_begin + nfull * BK;
+        ta[0].template load<true>(a.A, a.lda, m0, a.M, kk, k_end);
+        tb[0].template load<true>(a.B, a.ldb, n0, a.N, kk, k_end);
+        ta[0].store(sm);
+        tb[0].store(sm + 2 * TA::FLOATS);
+        __syncthreads();
+        compute(sm, sm + 2 * TA::FLOATS);
+        __syncthreads();
     }
 
     // Stage this wave's 64x64 block in LDS (the main loop's buffers are free
@@ -356,22 +365,37 @@ int resident_slots() {
     return slots;
 }
 
+int split_chunk(int K, int splits) {
+    int c = cdiv(K, splits);
+    return cdiv(c, BK) * BK;
+}
+
 // Split the reduction over K when the output tiles alone leave the chip
-// idle: weight gradients of the C x C and 4C x C layers (K = B*T, few tiles),
-// and long-K forward / input-gradient products whose tile count falls
-// between one and two rounds of resident workgroups (two splits make whole
-// rounds).
+// idle: weight gradients of the C x C and 4C x C layers (K = B*T, few tiles,
+// split so that the workgroups fill about two whole rounds), and long-K
+// forward / input-gradient products whose tile count falls between one and
+// two rounds of resident workgroups (two splits make whole rounds).
 int choose_splits(int op, int epi, int M, int N, int K) {
     if ((N % 4) != 0) return 1;
     const int tiles = cdiv(M, BM) * cdiv(N, BN);
     if (op == GEMM_TN) {
         if (epi != EPI_ACCUM && epi != EPI_STORE) return 1;
-        const int target = 768;
-        if (tiles >= target / 2) return 1;
-        int splits = cdiv(target, tiles);
-        const int max_splits = K / (BK * 4);  // at least 4 reduction steps each
-        if (splits > max_splits) splits = max_splits;
-        return splits < 1 ? 1 : splits;
+        const int slots = resident_slots();
+        if (tiles >= 2 * slots) return 1;
+        // Smallest split count that fills about two rounds of resident
+        // workgroups with little idle tail; at least 4 reduction steps each.
+        const int max_splits = K / (BK * 4);
+        int best = 1;
+        double best_eff = 0.0;
+        for (int sp = 2; sp <= max_splits; sp++) {
+            const int nz = cdiv(K, split_chunk(K, sp));
+            const double x = (double)tiles * nz / slots;
+            if (x > 4.0) break;
+            const double eff = x / std::ceil(x);
+            if (x >= 1.8 && eff >= 0.9) return sp;
+            if (eff > best_eff + 0.02) { best_eff = eff; best = sp; }
+        }
+        return best;
     }
     if (epi != EPI_STORE && epi != EPI_RESID) return 1;
     const int slots = resident_slots();
@@ -381,10 +405,6 @@ int choose_splits(int op, int epi, int M, int N, int K) {
     return whole_rounds && K >= min_k ? 2 : 1;
 }
 
-int split_chunk(int K, int splits) {
-    int c = cdiv(K, splits);
-    return cdiv(c, BK) * BK;
-}
 
 template <int OP, int EPI>
 hipError_t launch(hipStream_t s, const GemmArgs& a, int splits, float* ws) {
@@ -434,6 +454,12 @@ hipError_t launch_split(hipStream_t s, const GemmArgs& a, int splits, float* ws)
 
 hipError_t gemm(hipStream_t s, const GemmArgs& a, float* ws, size_t ws_bytes) {
     if (a.M <= 0 || a.N <= 0) return hipSuccess;
+    // float4 access: leading dimensions are multiples of 4 and cover the
+    // contiguous extent of each operand.
+    if (((a.lda | a.ldb | a.ldc) & 3) != 0) return hipErrorInvalidValue;
+    if (a.lda < (a.op == GEMM_TN ? a.M : a.K) || a.ldb < (a.op == GEMM_NT ? a.K : a.N) ||
+        a.ldc < a.N)
+        return hipErrorInvalidValue;
     int splits = choose_splits(a.op, a.epi, a.M, a.N, a.K);
     if (splits > 1 && gemm_workspace_bytes(a.op, a.epi, a.M, a.N, a.K) > ws_bytes) splits = 1;
     if (splits > 1) {

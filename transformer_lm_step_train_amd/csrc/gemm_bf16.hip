@@ -7,13 +7,16 @@
 // Same operand conventions and tiling as the fp32 kernel: 128x128 output tile
 // per 256-thread workgroup, 64x64 per wave (2x2 blocks of the 32x32 MFMA), a
 // reduction step of 64 staged through two LDS buffers with a two-deep
-// register prefetch.  In LDS every operand is stored [row][k] (72 bf16 per
+// register prefetch (whole steps only in the main loop, rows past the
+// matrix clamped to its last row; a partial last step is zero-padded after
+// the loop).  In LDS every operand is stored [row][k] (72 bf16 per
 // row), so each MFMA operand (8 consecutive k of one row) is one 16-byte
 // read.  Operands whose free index is contiguous in HBM are loaded as 8 rows
 // of k by 4 columns per thread and transposed in registers before the LDS
 // store.  Outputs are bf16 activations (with the fused bias, residual, GELU
 // or GELU-derivative epilogues) or fp32 weight gradients (+=).
 #include <algorithm>
+#include <cmath>
 #include <type_traits>
 
 #include "common.h"
@@ -41,23 +44,31 @@ template <>
 struct TileH<true> {
     static constexpr int ELEMS = 128 * LDH;
     uint4 v[4];
-    template <bool CHECK>
+    // Rows past the matrix read its last row (their products reach only
+    // outputs that are never stored); TAIL zeroes k >= K of a partial last
+    // reduction step.
+    template <bool TAIL>
     __device__ __forceinline__ void load(const uint16_t* __restrict__ g, int64_t ld, int r0,
                                          int R, int k0, int K) {
 #pragma unroll
         for (int i = 0; i < 4; i++) {
             const int idx = threadIdx.x + NTHR * i;
-            const int r = r0 + (idx >> 3);
+            const int r = min(r0 + (idx >> 3), R - 1);
             const int k = k0 + (idx & 7) * 8;
-            const uint16_t* p = g + (int64_t)r * ld + k;
-            if (!CHECK) {
-                v[i] = *reinterpret_cast<const uint4*>(p);
+            if (!TAIL) {
+                v[i] = *reinterpret_cast<const uint4*>(g + (int64_t)r * ld + k);
             } else {
-                uint16_t e[8];
+                const uint4 x =
+                    *reinterpret_cast<const uint4*>(g + (int64_t)r * ld + (k < K ? k : 0));
+                const uint32_t w[4] = {x.x, x.y, x.z, x.w};
+                uint32_t o[4];
 #pragma unroll
-                for (int j = 0; j < 8; j++) e[j] = (r < R && k + j < K) ? p[j] : (uint16_t)0;
-                v[i] = make_uint4(e[0] | ((uint32_t)e[1] << 16), e[2] | ((uint32_t)e[3] << 16),
-                                  e[4] | ((uint32_t)e[5] << 16), e[6] | ((uint32_t)e[7] << 16));
+                for (int j = 0; j < 4; j++) {
+                    const uint32_t lo = k + 2 * j < K ? (w[j] & 0xFFFFu) : 0u;
+                    const uint32_t hi = k + 2 * j + 1 < K ? (w[j] & 0xFFFF0000u) : 0u;
+                    o[j] = lo | hi;
+                }
+                v[i] = make_uint4(o[0], o[1], o[2], o[3]);
             }
         }
     }
@@ -77,23 +88,24 @@ template <>
 struct TileH<false> {
     static constexpr int ELEMS = 128 * LDH;
     uint2 v[8];
-    template <bool CHECK>
+    // A run of 4 that starts inside the matrix but passes its last row reads
+    // the row's padding (leading dimensions are multiples of 4); one that
+    // starts past it reads the last whole run instead.
+    template <bool TAIL>
     __device__ __forceinline__ void load(const uint16_t* __restrict__ g, int64_t ld, int r0,
                                          int R, int k0, int K) {
         const int t = threadIdx.x;
-        const int r = r0 + (t & 31) * 4;
+        int r = r0 + (t & 31) * 4;
+        r = r < R ? r : ((R - 1) & ~3);
         const int kb = k0 + (t >> 5) * 8;
 #pragma unroll
         for (int i = 0; i < 8; i++) {
             const int k = kb + i;
-            const uint16_t* p = g + (int64_t)k * ld + r;
-            if (!CHECK) {
-                v[i] = *reinterpret_cast<const uint2*>(p);
+            if (!TAIL) {
+                v[i] = *reinterpret_cast<const uint2*>(g + (int64_t)k * ld + r);
             } else {
-                uint16_t e[4];
-#pragma unroll
-                for (int j = 0; j < 4; j++) e[j] = (k < K && r + j < R) ? p[j] : (uint16_t)0;
-                v[i] = make_uint2(e[0] | ((uint32_t)e[1] << 16), e[2] | ((uint32_t)e[3] << 16));
+                const uint2 x = *reinterpret_cast<const uint2*>(g + (int64_t)(k < K ? k : 0) * ld + r);
+                v[i] = k < K ? x : make_uint2(0u, 0u);
             }
         }
     }
@@ -222,8 +234,6 @@ __global__ __launch_bounds__(NTHR, 2) void gemm_bf16_kernel(const GemmArgsH a, i
 
     const int k_begin = blockIdx.z * kchunk;
     const int k_end = min(a.K, k_begin + kchunk);
-    const int nk = k_end > k_begin ? (k_end - k_begin + BK - 1) / BK : 0;
-    const bool interior = (m0 + BM <= a.M) && (n0 + BN <= a.N);
 
     const int lane = threadIdx.x & 63, wave = threadIdx.x >> 6;
     const int wm = (wave >> 1) * 64, wn = (wave & 1) * 64;
@@ -239,33 +249,17 @@ __global__ __launch_bounds__(NTHR, 2) void gemm_bf16_kernel(const GemmArgsH a, i
 
     TA ta[2];
     TB tb[2];
+    const int nfull = (k_end - k_begin) / BK;  // whole reduction steps
+    // Every main-loop step issues the same loads (past the last whole step
+    // it reloads that step), so the wait for the previous step's registers
+    // is exact and two steps of loads stay in flight.
     auto issue = [&](auto slotc, int kt) {
         constexpr int S = decltype(slotc)::value;
-        const int kk = k_begin + kt * BK;
-        if (interior && kk + BK <= k_end) {
-            ta[S].template load<false>(a.A, a.lda, m0, a.M, kk, k_end);
-            tb[S].template load<false>(a.B, a.ldb, n0, a.N, kk, k_end);
-        } else {
-            ta[S].template load<true>(a.A, a.lda, m0, a.M, kk, k_end);
-            tb[S].template load<true>(a.B, a.ldb, n0, a.N, kk, k_end);
-        }
+        const int kk = k_begin + min(kt, nfull - 1) * BK;
+        ta[S].template load<false>(a.A, a.lda, m0, a.M, kk, k_end);
+        tb[S].template load<false>(a.B, a.ldb, n0, a.N, kk, k_end);
     };
-    using I0 = std::integral_constant<int, 0>;
-    using I1 = std::integral_constant<int, 1>;
-    if (nk > 0) {
-        issue(I0{}, 0);
-        ta[0].store(smh);
-        tb[0].store(smh + 2 * TA::ELEMS);
-        if (nk > 1) issue(I1{}, 1);
-    }
-    __syncthreads();
-    auto step = [&](int kt, auto slotc) {
-        constexpr int S = decltype(slotc)::value;
-        constexpr int NS = S ^ 1;
-        const int cur = kt & 1;
-        if (kt + 2 < nk) issue(slotc, kt + 2);
-        const uint16_t* sa = smh + cur * TA::ELEMS;
-        const uint16_t* sb = smh + 2 * TA::ELEMS + cur * TB::ELEMS;
+    auto compute = [&](const uint16_t* sa, const uint16_t* sb) {
 #pragma unroll
         for (int q = 0; q < BK / 16; q++) {
             const uint4 a0 = frag(sa, wm + li, g, q);
@@ -277,15 +271,42 @@ __global__ __launch_bounds__(NTHR, 2) void gemm_bf16_kernel(const GemmArgsH a, i
             acc[1][0] = mfma(a1, b0, acc[1][0]);
             acc[1][1] = mfma(a1, b1, acc[1][1]);
         }
-        if (kt + 1 < nk) {
-            ta[NS].store(smh + (cur ^ 1) * TA::ELEMS);
-            tb[NS].store(smh + 2 * TA::ELEMS + (cur ^ 1) * TB::ELEMS);
-        }
+    };
+    using I0 = std::integral_constant<int, 0>;
+    using I1 = std::integral_constant<int, 1>;
+    if (nfull > 0) {
+        issue(I0{}, 0);
+        ta[0].store(smh);
+        tb[0].store(smh + 2 * TA::ELEMS);
+        issue(I1{}, 1);
+    }
+    __syncthreads();
+    auto step = [&](int kt, auto slotc) {
+        constexpr int S = decltype(slotc)::value;
+        constexpr int NS = S ^ 1;
+        const int cur = kt & 1;
+        issue(slotc, kt + 2);
+        compute(smh + cur * TA::ELEMS, smh + 2 * TA::ELEMS + cur * TB::ELEMS);
+        // unconditional: no path reaches the next loads with this slot pending
+        ta[NS].store(smh + (cur ^ 1) * TA::ELEMS);
+        tb[NS].store(smh + 2 * TA::ELEMS + (cur ^ 1) * TB::ELEMS);
         __syncthreads();
     };
-    for (int kt = 0; kt < nk; kt += 2) {
+    int kt = 0;
+    for (; kt + 1 < nfull; kt += 2) {
         step(kt, I0{});
-        if (kt + 1 < nk) step(kt + 1, I1{});
+        step(kt + 1, I1{});
+    }
+    if (kt < nfull) step(kt, I0{});
+    if (k_begin + nfull * BK < k_end) {  // partial last step, zero-padded
+        const int kk = k_begin + nfull * BK;
+        ta[0].template load<true>(a.A, a.lda, m0, a.M, kk, k_end);
+        tb[0].template load<true>(a.B, a.ldb, n0, a.N, kk, k_end);
+        ta[0].store(smh);
+        tb[0].store(smh + 2 * TA::ELEMS);
+        __syncthreads();
+        compute(smh, smh + 2 * TA::ELEMS);
+        __syncthreads();
     }
 
     // stage each wave's 64x64 fp32 block in LDS, then work along rows
@@ -339,19 +360,46 @@ __global__ __launch_bounds__(256) void splitk_reduce_bf16_kernel(const GemmArgsH
 
 inline int cdiv(int64_t a, int64_t b) { return (int)((a + b - 1) / b); }
 
-// Weight gradients (K = B*T, few output tiles) are split over K.
+int split_chunk_h(int K, int splits) { return cdiv(cdiv(K, splits), BK) * BK; }
+
+// Workgroups resident at once (two per compute unit).
+int resident_slots_h() {
+    static int slots = 0;
+    if (!slots) {
+        int dev = 0, cus = 0;
+        if (hipGetDevice(&dev) != hipSuccess ||
+            hipDeviceGetAttribute(&cus, hipDeviceAttributeMultiprocessorCount, dev) != hipSuccess ||
+            cus <= 0)
+            cus = 256;
+        slots = 2 * cus;
+    }
+    return slots;
+}
+
+// Weight gradients (K = B*T, few output tiles) are split over K: the
+// smallest split count that fills about two whole rounds of resident
+// workgroups, each split at least 4 reduction steps long.
 int choose_splits_h(int op, int epi, int M, int N, int K) {
     if ((N % 4) != 0 || op != GEMM_TN || (epi != EPI_ACCUM && epi != EPI_STORE)) return 1;
     const int tiles = cdiv(M, BM) * cdiv(N, BN);
-    const int target = 768;
-    if (tiles >= target / 2) return 1;
-    int splits = cdiv(target, tiles);
+    const int slots = resident_slots_h();
+    if (tiles >= 2 * slots) return 1;
     const int max_splits = K / (BK * 4);
-    if (splits > max_splits) splits = max_splits;
-    return splits < 1 ? 1 : splits;
+    int best = 1;
+    double best_eff = 0.0;
+    for (int sp = 2; sp <= max_splits; sp++) {
+        const int nz = cdiv(K, split_chunk_h(K, sp));
+        const double x = (double)tiles * nz / slots;
+        if (x > 4.0) break;
+        const double eff = x / std::ceil(x);
+        if (x >= 1.8 && eff >= 0.9) return sp;
+        if (eff > best_eff + 0.02) {
+            best_eff = eff;
+            best = sp;
+        }
+    }
+    return best;
 }
-
-int split_chunk_h(int K, int splits) { return cdiv(cdiv(K, splits), BK) * BK; }
 
 template <int OP, int EPI>
 hipError_t launch_h(hipStream_t s, const GemmArgsH& a, int splits, float* ws) {
@@ -373,6 +421,13 @@ size_t gemm_bf16_workspace_bytes(int op, int epi, int M, int N, int K) {
 
 hipError_t gemm_bf16(hipStream_t s, const GemmArgsH& a, float* ws, size_t ws_bytes) {
     if (a.M <= 0 || a.N <= 0) return hipSuccess;
+    // 16-byte runs along k for k-contiguous operands, 8-byte runs of 4 along
+    // the free index otherwise; leading dimensions cover each extent.
+    const int64_t lda_al = a.op == GEMM_TN ? 4 : 8, ldb_al = a.op == GEMM_NT ? 8 : 4;
+    if (a.lda % lda_al || a.ldb % ldb_al || (a.ldc & 3)) return hipErrorInvalidValue;
+    if (a.lda < (a.op == GEMM_TN ? a.M : a.K) || a.ldb < (a.op == GEMM_NT ? a.K : a.N) ||
+        a.ldc < a.N)
+        return hipErrorInvalidValue;
     int splits = choose_splits_h(a.op, a.epi, a.M, a.N, a.K);
     if (splits > 1 && gemm_bf16_workspace_bytes(a.op, a.epi, a.M, a.N, a.K) > ws_bytes) splits = 1;
     if (splits > 1) {
