@@ -15,7 +15,7 @@ BUILD = os.path.join(HERE, "_build")
 LIB = os.path.join(HERE, "libgpt2_hip.so")
 HIPCC = os.environ.get("HIPCC", "/opt/rocm/bin/hipcc")
 
-SOURCES = ["gemm.hip", "gemm_bf16.hip", "attention.hip", "layernorm.hip", "softmax_ce.hip",
+SOURCES = ["gemm.hip", "gemm_bf16.hip", "attention.hip", "attention_bf16.hip", "layernorm.hip", "softmax_ce.hip",
            "elementwise.hip", "runtime.cpp"]
 
 FLAGS = [

@@ -580,7 +580,7 @@ hipError_t attention_forward(hipStream_t s, void* out, float* lse, const void* q
                              int C, int NH, int bf16) {
     if (B <= 0 || T <= 0) return hipSuccess;
     if (bf16)
-        return forward_t<uint16_t>(s, (uint16_t*)out, lse, (const uint16_t*)qkv, B, T, C, NH);
+        return attention_forward_bf16(s, (uint16_t*)out, lse, (const uint16_t*)qkv, B, T, C, NH);
     return forward_t<float>(s, (float*)out, lse, (const float*)qkv, B, T, C, NH);
 }
 

@@ -1,0 +1,291 @@
+// Causal multi-head self-attention of the mixed-precision model on the bf16
+// matrix cores (v_mfma_f32_32x32x16_bf16): bf16 q, k, v, out and gradients,
+// fp32 accumulation and fp32 softmax statistics.
+//
+// The layer is GPT-2's masked self-attention (ujoy.net article "徒手用 1000 行
+// C 语言实现", section "用C语言实现LLM"; the reduced-precision extension is
+// named by yinghuohong.cn, section "脚动完成每一个层前向/反向流传").  The
+// algorithm is the one of the fp32 kernels: per sequence and head, an online
+// softmax over key tiles that keeps only the row log-sum-exp, and a backward
+// that recomputes the probabilities from it:
+//   s = q.k / sqrt(hs) (keys <= query),  out = softmax(s) v,
+//   D = rowsum(dout * out),  dS = P (dout v^T - D),
+//   dq = dS k / sqrt(hs),  dk = dS^T q / sqrt(hs),  dv = P^T dout.
+//
+// MFMA layout.  A 32x32x16 product takes, per lane l (column/row l % 32,
+// half g = l / 32), eight consecutive reduction elements 8g..8g+7 of its
+// row of A and of its column of B.  Scores are formed transposed, S^T = K
+// Q^T (lane owns a query), as in the fp32 kernels; each lane then holds 16
+// keys of a 32-key block: {0-3, 8-11, 16-19, 24-27} + 4g.  Those registers
+// become the B operand of the next product (P^T or dS^T) without any lane
+// exchange, because the reduction over keys may run in any order: within
+// each group of 16 keys the reduction position 8g + i is given to key
+// 8(i / 4) + 4g + i % 4, and the operand stored in LDS along keys (V^T, K^T,
+// Q^T, dout^T) is written in that same permuted order.  Operands stored
+// along head dimensions ([row][dim], 8 bf16 pad) are read as 16 bytes.
+//
+// P and dS are rounded to bf16 for their products; the row statistics, the
+// exponentials and every sum stay fp32.  As in the fp32 kernels each
+// workgroup is four waves owning 128 rows, tiles of 64 rows stream through
+// two LDS buffers with a register prefetch of the next tile (rows past T
+// read row T - 1: their scores are masked or their weights are zero), the
+// grid runs longest-first, and every output row has one owner, so results
+// are deterministic.
+#include "common.h"
+#include "kernels.h"
+
+namespace gk {
+namespace {
+
+typedef __bf16 bf16x8 __attribute__((ext_vector_type(8)));
+typedef __bf16 bf16x2v __attribute__((ext_vector_type(2)));
+typedef float f32x2v __attribute__((ext_vector_type(2)));
+
+constexpr int RQ = 128;  // rows owned per workgroup (four waves of 32)
+constexpr int RT = 64;   // rows per staged tile
+constexpr int LDP = RT + 8;  // stride of a tile stored along keys/queries
+constexpr float L2E = 1.4426950408889634f;
+constexpr float LN_2 = 0.6931471805599453f;
+
+__device__ __forceinline__ floatx16 mma(uint4 a, uint4 b, floatx16 c) {
+    return __builtin_amdgcn_mfma_f32_32x32x16_bf16(__builtin_bit_cast(bf16x8, a),
+                                                   __builtin_bit_cast(bf16x8, b), c, 0, 0, 0);
+}
+
+// two fp32 -> packed bf16 (round to nearest even, v_cvt_pk_bf16_f32)
+__device__ __forceinline__ uint32_t pk(float a, float b) {
+    const f32x2v f = {a, b};
+    return __builtin_bit_cast(uint32_t, __builtin_convertvector(f, bf16x2v));
+}
+
+__device__ __forceinline__ float lo_f(uint32_t w) { return __uint_as_float(w << 16); }
+__device__ __forceinline__ float hi_f(uint32_t w) { return __uint_as_float(w & 0xFFFF0000u); }
+
+__device__ __forceinline__ void zero(floatx16& x) {
+#pragma unroll
+    for (int e = 0; e < 16; e++) x[e] = 0.f;
+}
+
+// reduction position of key kk (0..63) in a tile stored along keys
+__device__ __forceinline__ int kpos(int kk) {
+    return (kk & ~15) | (((kk >> 2) & 1) << 3) | (((kk >> 3) & 1) << 2) | (kk & 3);
+}
+
+// Eight registers of a 32-row accumulator block, e = 8h..8h+7, as a bf16
+// B operand (reduction positions 8g..8g+7 of the 16-row group h).
+__device__ __forceinline__ uint4 pack8(const floatx16& x, int h) {
+    return make_uint4(pk(x[8 * h], x[8 * h + 1]), pk(x[8 * h + 2], x[8 * h + 3]),
+                      pk(x[8 * h + 4], x[8 * h + 5]), pk(x[8 * h + 6], x[8 * h + 7]));
+}
+
+// A 64-row tile of one head (HS bf16 per row) held in registers between its
+// global load (16 bytes per access, rows clamped to T - 1) and its LDS store.
+template <int HS>
+struct Tile16 {
+    static constexpr int CH = HS / 8;             // 16-byte chunks per row
+    static constexpr int N = RT * CH;             // chunks per tile
+    static constexpr int PER = (N + 255) / 256;   // per thread
+    uint4 v[PER];
+    __device__ __forceinline__ void load(const uint16_t* __restrict__ base, int64_t ld, int r0,
+                                         int T) {
+#pragma unroll
+        for (int i = 0; i < PER; i++) {
+            const int idx = threadIdx.x + 256 * i;
+            if (N % 256 == 0 || idx < N) {
+                const int r = min(r0 + idx / CH, T - 1), c = (idx % CH) * 8;
+                v[i] = *reinterpret_cast<const uint4*>(base + (int64_t)r * ld + c);
+            }
+        }
+    }
+    // [row][dim], row stride HS + 8
+    __device__ __forceinline__ void store_rows(uint16_t* sm) const {
+#pragma unroll
+        for (int i = 0; i < PER; i++) {
+            const int idx = threadIdx.x + 256 * i;
+            if (N % 256 == 0 || idx < N)
+                *reinterpret_cast<uint4*>(sm + (idx / CH) * (HS + 8) + (idx % CH) * 8) = v[i];
+        }
+    }
+    // [dim][reduction position of the row], row stride LDP
+    __device__ __forceinline__ void store_t(uint16_t* sm) const {
+#pragma unroll
+        for (int i = 0; i < PER; i++) {
+            const int idx = threadIdx.x + 256 * i;
+            if (N % 256 == 0 || idx < N) {
+                const int r = kpos(idx / CH), c = (idx % CH) * 8;
+                const uint32_t w[4] = {v[i].x, v[i].y, v[i].z, v[i].w};
+#pragma unroll
+                for (int j = 0; j < 4; j++) {
+                    sm[(c + 2 * j) * LDP + r] = (uint16_t)(w[j] & 0xFFFFu);
+                    sm[(c + 2 * j + 1) * LDP + r] = (uint16_t)(w[j] >> 16);
+                }
+            }
+        }
+    }
+};
+
+// 16-byte LDS operand read
+__device__ __forceinline__ uint4 rd(const uint16_t* p) {
+    return *reinterpret_cast<const uint4*>(p);
+}
+
+// Write one lane's accumulator blocks (rows = head dims d*32 + 8(e/4) +
+// 4g + e%4 of this lane's row) as bf16, scaled.
+template <int HS, int NDB>
+__device__ __forceinline__ void put_row(uint16_t* row, const floatx16 (&acc)[NDB], int g,
+                                        float mul) {
+#pragma unroll
+    for (int d = 0; d < NDB; d++)
+#pragma unroll
+        for (int c = 0; c < 4; c++) {
+            const int dim0 = d * 32 + 8 * c + 4 * g;
+            if (dim0 < HS)
+                *reinterpret_cast<uint2*>(row + dim0) =
+                    make_uint2(pk(acc[d][4 * c] * mul, acc[d][4 * c + 1] * mul),
+                               pk(acc[d][4 * c + 2] * mul, acc[d][4 * c + 3] * mul));
+        }
+}
+
+// Zero the rows HS..NDB*32-1 of a tile stored along keys (read by the MFMA
+// as padding head dimensions whose outputs are discarded).
+template <int HS, int NDB>
+__device__ __forceinline__ void zero_pad_rows(uint16_t* sm) {
+    if (NDB * 32 > HS)
+        for (int i = threadIdx.x; i < (NDB * 32 - HS) * LDP; i += blockDim.x) sm[HS * LDP + i] = 0;
+}
+
+template <int HS>
+__global__ __launch_bounds__(256, 2) void attn16_fwd_kernel(uint16_t* __restrict__ out,
+                                                            float* __restrict__ lse,
+                                                            const uint16_t* __restrict__ qkv,
+                                                            int T, int C, int NH, float qscale) {
+    constexpr int NKS = HS / 16, NDB = (HS + 31) / 32, LDK = HS + 8;
+    __shared__ __attribute__((aligned(16))) uint16_t ks[2][RT * LDK];
+    __shared__ __attribute__((aligned(16))) uint16_t vt[2][NDB * 32 * LDP];
+
+    const int nqb = (T + RQ - 1) / RQ;
+    const int nbh = gridDim.x / nqb;
+    const int bh = blockIdx.x % nbh;
+    const int qb = nqb - 1 - blockIdx.x / nbh;  // longest first
+    const int b = bh / NH, h = bh - b * NH;
+    const int lane = threadIdx.x & 63, wave = threadIdx.x >> 6;
+    const int li = lane & 31, g = lane >> 5;
+    const int64_t ld = 3 * (int64_t)C;
+    const uint16_t* base = qkv + (int64_t)b * T * ld + h * HS;
+    const int q0 = qb * RQ;
+    const int qw = q0 + wave * 32;
+    const int q = qw + li;
+    const int qmax = qw < T ? min(qw + 31, T - 1) : -1;
+    const int nkt = (min(q0 + RQ, T) - 1) / RT + 1;
+    zero_pad_rows<HS, NDB>(vt[0]);
+    zero_pad_rows<HS, NDB>(vt[1]);
+
+    uint4 qv[NKS];  // this lane's query, dims 16j + 8g .. +7
+#pragma unroll
+    for (int j = 0; j < NKS; j++)
+        qv[j] = rd(base + (int64_t)min(q, T - 1) * ld + 16 * j + 8 * g);
+    floatx16 o[NDB];
+#pragma unroll
+    for (int d = 0; d < NDB; d++) zero(o[d]);
+    float m = -INFINITY, l = 0.f;
+
+    Tile16<HS> kreg, vreg;
+    kreg.load(base + C, ld, 0, T);
+    vreg.load(base + 2 * C, ld, 0, T);
+    kreg.store_rows(ks[0]);
+    vreg.store_t(vt[0]);
+    __syncthreads();
+    for (int kt = 0; kt < nkt; kt++) {
+        const int cur = kt & 1;
+        const int nxt = min(kt + 1, nkt - 1) * RT;  // the last tile reloads itself
+        kreg.load(base + C, ld, nxt, T);
+        vreg.load(base + 2 * C, ld, nxt, T);
+        const int k0 = kt * RT;
+        if (k0 <= qmax) {
+            const uint16_t* kr = ks[cur] + li * LDK + 8 * g;
+            floatx16 sc[2];
+            zero(sc[0]);
+            zero(sc[1]);
+#pragma unroll
+            for (int j = 0; j < NKS; j++) {
+                sc[0] = mma(rd(kr + 16 * j), qv[j], sc[0]);
+                sc[1] = mma(rd(kr + 32 * LDK + 16 * j), qv[j], sc[1]);
+            }
+            if ((k0 + RT - 1 > qw) || (k0 + RT > T)) {  // tile touches the mask
+#pragma unroll
+                for (int kb = 0; kb < 2; kb++)
+#pragma unroll
+                    for (int e = 0; e < 16; e++) {
+                        const int key = k0 + kb * 32 + 8 * (e >> 2) + 4 * g + (e & 3);
+                        sc[kb][e] = (key > q) | (key >= T) ? -INFINITY : sc[kb][e];
+                    }
+            }
+            float mt = -INFINITY;
+#pragma unroll
+            for (int kb = 0; kb < 2; kb++)
+#pragma unroll
+                for (int e = 0; e < 16; e++) mt = fmaxf(mt, sc[kb][e]);
+            mt = fmaxf(mt, __shfl_xor(mt, 32, WAVE)) * qscale;
+            const float mn = fmaxf(m, mt);
+            const float corr = __builtin_amdgcn_exp2f(m - mn);
+            float ls = 0.f;
+#pragma unroll
+            for (int kb = 0; kb < 2; kb++)
+#pragma unroll
+                for (int e = 0; e < 16; e++) {
+                    const float p = __builtin_amdgcn_exp2f(fmaf(sc[kb][e], qscale, -mn));
+                    sc[kb][e] = p;
+                    ls += p;
+                }
+            ls += __shfl_xor(ls, 32, WAVE);
+            l = l * corr + ls;
+            m = mn;
+#pragma unroll
+            for (int d = 0; d < NDB; d++)
+#pragma unroll
+                for (int e = 0; e < 16; e++) o[d][e] *= corr;
+            const uint16_t* vr = vt[cur] + li * LDP + 8 * g;
+#pragma unroll
+            for (int kb = 0; kb < 2; kb++)
+#pragma unroll
+                for (int hh = 0; hh < 2; hh++) {
+                    const uint4 pb = pack8(sc[kb], hh);
+#pragma unroll
+                    for (int d = 0; d < NDB; d++)
+                        o[d] = mma(rd(vr + d * 32 * LDP + kb * 32 + 16 * hh), pb, o[d]);
+                }
+        }
+        kreg.store_rows(ks[cur ^ 1]);
+        vreg.store_t(vt[cur ^ 1]);
+        __syncthreads();
+    }
+    if (q < T) {
+        put_row<HS, NDB>(out + ((int64_t)b * T + q) * C + h * HS, o, g, 1.f / l);
+        if (g == 0) lse[((int64_t)b * NH + h) * T + q] = (m + log2f(l)) * LN_2;
+    }
+}
+
+template <int HS>
+hipError_t fwd16(hipStream_t s, uint16_t* out, float* lse, const uint16_t* qkv, int B, int T,
+                 int C, int NH) {
+    const int nqb = (T + RQ - 1) / RQ;
+    const float qscale = L2E / sqrtf((float)HS);
+    hipLaunchKernelGGL((attn16_fwd_kernel<HS>), dim3(B * NH * nqb), dim3(256), 0, s, out, lse,
+                       qkv, T, C, NH, qscale);
+    return hipGetLastError();
+}
+
+}  // namespace
+
+hipError_t attention_forward_bf16(hipStream_t s, uint16_t* out, float* lse, const uint16_t* qkv,
+                                  int B, int T, int C, int NH) {
+    if (B <= 0 || T <= 0) return hipSuccess;
+    switch (C / NH) {
+        case 16: return fwd16<16>(s, out, lse, qkv, B, T, C, NH);
+        case 32: return fwd16<32>(s, out, lse, qkv, B, T, C, NH);
+        case 64: return fwd16<64>(s, out, lse, qkv, B, T, C, NH);
+        default: return hipErrorInvalidValue;
+    }
+}
+
+}  // namespace gk

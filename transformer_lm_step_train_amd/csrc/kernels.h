@@ -75,6 +75,10 @@ hipError_t attention_forward(hipStream_t s, void* out, float* lse, const void* q
 hipError_t attention_backward(hipStream_t s, void* dqkv, float* dpre, const void* dout,
                               const void* qkv, const void* out, const float* lse, int B,
                               int T, int C, int NH, int bf16);
+// Mixed-precision attention on the bf16 matrix cores (all tensors bf16,
+// lse fp32).
+hipError_t attention_forward_bf16(hipStream_t s, uint16_t* out, float* lse, const uint16_t* qkv,
+                                  int B, int T, int C, int NH);
 
 // ---- layernorm ------------------------------------------------------------
 // Activations (out, inp, dres, dout) are fp32, or bf16 bits when bf16 != 0;
