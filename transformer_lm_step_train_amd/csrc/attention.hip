@@ -589,8 +589,9 @@ hipError_t attention_backward(hipStream_t s, void* dqkv, float* dpre, const void
                               int C, int NH, int bf16) {
     if (B <= 0 || T <= 0) return hipSuccess;
     if (bf16)
-        return backward_t<uint16_t>(s, (uint16_t*)dqkv, dpre, (const uint16_t*)dout,
-                                    (const uint16_t*)qkv, (const uint16_t*)out, lse, B, T, C, NH);
+        return attention_backward_bf16(s, (uint16_t*)dqkv, dpre, (const uint16_t*)dout,
+                                       (const uint16_t*)qkv, (const uint16_t*)out, lse, B, T, C,
+                                       NH);
     return backward_t<float>(s, (float*)dqkv, dpre, (const float*)dout, (const float*)qkv,
                              (const float*)out, lse, B, T, C, NH);
 }

@@ -265,6 +265,255 @@ __global__ __launch_bounds__(256, 2) void attn16_fwd_kernel(uint16_t* __restrict
     }
 }
 
+// dQ (lane owns a query) and D = rowsum(dout * out) for the key/value
+// kernel.  K is staged twice: as rows for S^T = K Q^T and along keys for
+// dQ^T = K^T dS^T; V as rows for dP^T = V dout^T.
+template <int HS>
+__global__ __launch_bounds__(256, 2) void attn16_dq_kernel(
+    uint16_t* __restrict__ dqkv, float* __restrict__ Dout, const uint16_t* __restrict__ dout,
+    const uint16_t* __restrict__ out, const uint16_t* __restrict__ qkv,
+    const float* __restrict__ lse, int T, int C, int NH, float qscale, float scale) {
+    constexpr int NKS = HS / 16, NDB = (HS + 31) / 32, LDK = HS + 8;
+    __shared__ __attribute__((aligned(16))) uint16_t ks[2][RT * LDK];
+    __shared__ __attribute__((aligned(16))) uint16_t vs[2][RT * LDK];
+    __shared__ __attribute__((aligned(16))) uint16_t kt_[2][NDB * 32 * LDP];
+
+    const int nqb = (T + RQ - 1) / RQ;
+    const int nbh = gridDim.x / nqb;
+    const int bh = blockIdx.x % nbh;
+    const int qb = nqb - 1 - blockIdx.x / nbh;  // longest first
+    const int b = bh / NH, h = bh - b * NH;
+    const int lane = threadIdx.x & 63, wave = threadIdx.x >> 6;
+    const int li = lane & 31, g = lane >> 5;
+    const int64_t ld = 3 * (int64_t)C;
+    const uint16_t* base = qkv + (int64_t)b * T * ld + h * HS;
+    const uint16_t* dobase = dout + (int64_t)b * T * C + h * HS;
+    const uint16_t* obase = out + (int64_t)b * T * C + h * HS;
+    const int q0 = qb * RQ;
+    const int qw = q0 + wave * 32;
+    const int q = qw + li;
+    const int qc = min(q, T - 1);
+    const int qmax = qw < T ? min(qw + 31, T - 1) : -1;
+    const int nkt = (min(q0 + RQ, T) - 1) / RT + 1;
+    zero_pad_rows<HS, NDB>(kt_[0]);
+    zero_pad_rows<HS, NDB>(kt_[1]);
+
+    uint4 qv[NKS], dv[NKS];
+    float dsum = 0.f;
+#pragma unroll
+    for (int j = 0; j < NKS; j++) {
+        qv[j] = rd(base + (int64_t)qc * ld + 16 * j + 8 * g);
+        dv[j] = rd(dobase + (int64_t)qc * C + 16 * j + 8 * g);
+        const uint4 ov = rd(obase + (int64_t)qc * C + 16 * j + 8 * g);
+        const uint32_t dw[4] = {dv[j].x, dv[j].y, dv[j].z, dv[j].w};
+        const uint32_t ow[4] = {ov.x, ov.y, ov.z, ov.w};
+#pragma unroll
+        for (int i = 0; i < 4; i++)
+            dsum += lo_f(dw[i]) * lo_f(ow[i]) + hi_f(dw[i]) * hi_f(ow[i]);
+    }
+    const float Dq = dsum + __shfl_xor(dsum, 32, WAVE);
+    const int64_t srow = ((int64_t)b * NH + h) * T;
+    if (q < T && g == 0) Dout[srow + q] = Dq;
+    const float lq = lse[srow + qc] * L2E;
+    floatx16 dq[NDB];
+#pragma unroll
+    for (int d = 0; d < NDB; d++) zero(dq[d]);
+
+    Tile16<HS> kreg, vreg;
+    kreg.load(base + C, ld, 0, T);
+    vreg.load(base + 2 * C, ld, 0, T);
+    kreg.store_rows(ks[0]);
+    kreg.store_t(kt_[0]);
+    vreg.store_rows(vs[0]);
+    __syncthreads();
+    for (int kt = 0; kt < nkt; kt++) {
+        const int cur = kt & 1;
+        const int nxt = min(kt + 1, nkt - 1) * RT;
+        kreg.load(base + C, ld, nxt, T);
+        vreg.load(base + 2 * C, ld, nxt, T);
+        const int k0 = kt * RT;
+        if (k0 <= qmax) {
+            const uint16_t* kr = ks[cur] + li * LDK + 8 * g;
+            const uint16_t* vr = vs[cur] + li * LDK + 8 * g;
+            floatx16 sc[2], dp[2];
+#pragma unroll
+            for (int kb = 0; kb < 2; kb++) {
+                zero(sc[kb]);
+                zero(dp[kb]);
+            }
+#pragma unroll
+            for (int j = 0; j < NKS; j++)
+#pragma unroll
+                for (int kb = 0; kb < 2; kb++) {
+                    sc[kb] = mma(rd(kr + kb * 32 * LDK + 16 * j), qv[j], sc[kb]);
+                    dp[kb] = mma(rd(vr + kb * 32 * LDK + 16 * j), dv[j], dp[kb]);
+                }
+#pragma unroll
+            for (int kb = 0; kb < 2; kb++)
+#pragma unroll
+                for (int e = 0; e < 16; e++) {
+                    const int key = k0 + kb * 32 + 8 * (e >> 2) + 4 * g + (e & 3);
+                    const bool live = (key <= q) & (key < T);
+                    const float p = __builtin_amdgcn_exp2f(fmaf(sc[kb][e], qscale, -lq));
+                    sc[kb][e] = live ? p * (dp[kb][e] - Dq) : 0.f;
+                }
+            const uint16_t* ktr = kt_[cur] + li * LDP + 8 * g;
+#pragma unroll
+            for (int kb = 0; kb < 2; kb++)
+#pragma unroll
+                for (int hh = 0; hh < 2; hh++) {
+                    const uint4 sb = pack8(sc[kb], hh);
+#pragma unroll
+                    for (int d = 0; d < NDB; d++)
+                        dq[d] = mma(rd(ktr + d * 32 * LDP + kb * 32 + 16 * hh), sb, dq[d]);
+                }
+        }
+        kreg.store_rows(ks[cur ^ 1]);
+        kreg.store_t(kt_[cur ^ 1]);
+        vreg.store_rows(vs[cur ^ 1]);
+        __syncthreads();
+    }
+    if (q < T) put_row<HS, NDB>(dqkv + ((int64_t)b * T + q) * ld + h * HS, dq, g, scale);
+}
+
+// dK and dV (lane owns a key).  Q and dout are staged as rows (for S = Q K^T
+// and dP = dout V^T, queries down the accumulator) and along queries (for
+// dK^T = Q^T dS and dV^T = dout^T P).
+template <int HS>
+__global__ __launch_bounds__(256, 2) void attn16_dkdv_kernel(
+    uint16_t* __restrict__ dqkv, const uint16_t* __restrict__ dout,
+    const uint16_t* __restrict__ qkv, const float* __restrict__ lse, const float* __restrict__ D,
+    int T, int C, int NH, float qscale, float scale) {
+    constexpr int NKS = HS / 16, NDB = (HS + 31) / 32, LDK = HS + 8;
+    __shared__ __attribute__((aligned(16))) uint16_t qs[2][RT * LDK];
+    __shared__ __attribute__((aligned(16))) uint16_t ds[2][RT * LDK];
+    __shared__ __attribute__((aligned(16))) uint16_t qt_[2][NDB * 32 * LDP];
+    __shared__ __attribute__((aligned(16))) uint16_t dt_[2][NDB * 32 * LDP];
+    __shared__ float lsm[2][RT], dsm[2][RT];
+
+    const int nkb = (T + RQ - 1) / RQ;
+    const int nbh = gridDim.x / nkb;
+    const int bh = blockIdx.x % nbh;
+    const int kb0 = blockIdx.x / nbh;  // lowest keys = most query tiles: first
+    const int b = bh / NH, h = bh - b * NH;
+    const int lane = threadIdx.x & 63, wave = threadIdx.x >> 6;
+    const int li = lane & 31, g = lane >> 5;
+    const int64_t ld = 3 * (int64_t)C;
+    const uint16_t* base = qkv + (int64_t)b * T * ld + h * HS;
+    const uint16_t* dobase = dout + (int64_t)b * T * C + h * HS;
+    const int64_t srow = ((int64_t)b * NH + h) * T;
+    const int kw = kb0 * RQ + wave * 32;  // first key of this wave
+    const int key = kw + li;
+    const int kc = min(key, T - 1);
+    zero_pad_rows<HS, NDB>(qt_[0]);
+    zero_pad_rows<HS, NDB>(qt_[1]);
+    zero_pad_rows<HS, NDB>(dt_[0]);
+    zero_pad_rows<HS, NDB>(dt_[1]);
+
+    uint4 kv[NKS], vv[NKS];
+#pragma unroll
+    for (int j = 0; j < NKS; j++) {
+        kv[j] = rd(base + C + (int64_t)kc * ld + 16 * j + 8 * g);
+        vv[j] = rd(base + 2 * C + (int64_t)kc * ld + 16 * j + 8 * g);
+    }
+    floatx16 dk[NDB], dvv[NDB];
+#pragma unroll
+    for (int d = 0; d < NDB; d++) {
+        zero(dk[d]);
+        zero(dvv[d]);
+    }
+    const int qt0 = (kb0 * RQ) / RT;
+    const int nqt = (T + RT - 1) / RT;
+    Tile16<HS> qreg, dreg;
+    float sreg = 0.f;  // one lse (threads 0..63) or D (64..127) value per thread
+    auto load_stats = [&](int qt) {  // every thread loads (a fixed count per step)
+        const int t = min(qt * RT + (threadIdx.x & 63), T - 1);
+        const float x = (threadIdx.x < 64 ? lse : D)[srow + t];
+        sreg = threadIdx.x < 64 ? x * L2E : x;
+    };
+    auto store_stats = [&](int buf) {
+        if (threadIdx.x < 64) lsm[buf][threadIdx.x] = sreg;
+        else if (threadIdx.x < 128) dsm[buf][threadIdx.x - 64] = sreg;
+    };
+    qreg.load(base, ld, qt0 * RT, T);
+    dreg.load(dobase, C, qt0 * RT, T);
+    load_stats(qt0);
+    qreg.store_rows(qs[0]);
+    qreg.store_t(qt_[0]);
+    dreg.store_rows(ds[0]);
+    dreg.store_t(dt_[0]);
+    store_stats(0);
+    __syncthreads();
+    for (int qt = qt0; qt < nqt; qt++) {
+        const int cur = (qt - qt0) & 1;
+        const int nxt = min(qt + 1, nqt - 1);
+        qreg.load(base, ld, nxt * RT, T);
+        dreg.load(dobase, C, nxt * RT, T);
+        load_stats(nxt);
+#pragma unroll
+        for (int qh = 0; qh < 2; qh++) {
+            const int qlo = qt * RT + qh * 32;
+            if (kw >= T || qlo + 31 < kw || qlo >= T) continue;  // empty under the mask
+            const uint16_t* qr = qs[cur] + (qh * 32 + li) * LDK + 8 * g;
+            const uint16_t* dr = ds[cur] + (qh * 32 + li) * LDK + 8 * g;
+            floatx16 sc, dp;
+            zero(sc);
+            zero(dp);
+#pragma unroll
+            for (int j = 0; j < NKS; j++) {
+                sc = mma(rd(qr + 16 * j), kv[j], sc);
+                dp = mma(rd(dr + 16 * j), vv[j], dp);
+            }
+#pragma unroll
+            for (int e = 0; e < 16; e++) {
+                const int ql = qh * 32 + 8 * (e >> 2) + 4 * g + (e & 3);
+                const int qa = qt * RT + ql;
+                const bool live = (qa < T) & (key <= qa);
+                const float p =
+                    live ? __builtin_amdgcn_exp2f(fmaf(sc[e], qscale, -lsm[cur][ql])) : 0.f;
+                sc[e] = p;
+                dp[e] = p * (dp[e] - dsm[cur][ql]);
+            }
+            const uint16_t* qtr = qt_[cur] + li * LDP + 8 * g + qh * 32;
+            const uint16_t* dtr = dt_[cur] + li * LDP + 8 * g + qh * 32;
+#pragma unroll
+            for (int hh = 0; hh < 2; hh++) {
+                const uint4 pb = pack8(sc, hh), sb = pack8(dp, hh);
+#pragma unroll
+                for (int d = 0; d < NDB; d++) {
+                    dvv[d] = mma(rd(dtr + d * 32 * LDP + 16 * hh), pb, dvv[d]);
+                    dk[d] = mma(rd(qtr + d * 32 * LDP + 16 * hh), sb, dk[d]);
+                }
+            }
+        }
+        qreg.store_rows(qs[cur ^ 1]);
+        qreg.store_t(qt_[cur ^ 1]);
+        dreg.store_rows(ds[cur ^ 1]);
+        dreg.store_t(dt_[cur ^ 1]);
+        store_stats(cur ^ 1);
+        __syncthreads();
+    }
+    if (key < T) {
+        uint16_t* row = dqkv + ((int64_t)b * T + key) * ld + h * HS;
+        put_row<HS, NDB>(row + C, dk, g, scale);
+        put_row<HS, NDB>(row + 2 * C, dvv, g, 1.f);
+    }
+}
+
+template <int HS>
+hipError_t bwd16(hipStream_t s, uint16_t* dqkv, float* D, const uint16_t* dout,
+                 const uint16_t* qkv, const uint16_t* out, const float* lse, int B, int T, int C,
+                 int NH) {
+    const int nb = (T + RQ - 1) / RQ;
+    const float scale = 1.0f / sqrtf((float)HS);
+    const float qscale = L2E * scale;
+    hipLaunchKernelGGL((attn16_dq_kernel<HS>), dim3(B * NH * nb), dim3(256), 0, s, dqkv, D, dout,
+                       out, qkv, lse, T, C, NH, qscale, scale);
+    hipLaunchKernelGGL((attn16_dkdv_kernel<HS>), dim3(B * NH * nb), dim3(256), 0, s, dqkv, dout,
+                       qkv, lse, D, T, C, NH, qscale, scale);
+    return hipGetLastError();
+}
+
 template <int HS>
 hipError_t fwd16(hipStream_t s, uint16_t* out, float* lse, const uint16_t* qkv, int B, int T,
                  int C, int NH) {
@@ -284,6 +533,19 @@ hipError_t attention_forward_bf16(hipStream_t s, uint16_t* out, float* lse, cons
         case 16: return fwd16<16>(s, out, lse, qkv, B, T, C, NH);
         case 32: return fwd16<32>(s, out, lse, qkv, B, T, C, NH);
         case 64: return fwd16<64>(s, out, lse, qkv, B, T, C, NH);
+        default: return hipErrorInvalidValue;
+    }
+}
+
+hipError_t attention_backward_bf16(hipStream_t s, uint16_t* dqkv, float* D,
+                                   const uint16_t* dout, const uint16_t* qkv,
+                                   const uint16_t* out, const float* lse, int B, int T, int C,
+                                   int NH) {
+    if (B <= 0 || T <= 0) return hipSuccess;
+    switch (C / NH) {
+        case 16: return bwd16<16>(s, dqkv, D, dout, qkv, out, lse, B, T, C, NH);
+        case 32: return bwd16<32>(s, dqkv, D, dout, qkv, out, lse, B, T, C, NH);
+        case 64: return bwd16<64>(s, dqkv, D, dout, qkv, out, lse, B, T, C, NH);
         default: return hipErrorInvalidValue;
     }
 }

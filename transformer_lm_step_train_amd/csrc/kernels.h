@@ -79,6 +79,10 @@ hipError_t attention_backward(hipStream_t s, void* dqkv, float* dpre, const void
 // lse fp32).
 hipError_t attention_forward_bf16(hipStream_t s, uint16_t* out, float* lse, const uint16_t* qkv,
                                   int B, int T, int C, int NH);
+hipError_t attention_backward_bf16(hipStream_t s, uint16_t* dqkv, float* D,
+                                   const uint16_t* dout, const uint16_t* qkv,
+                                   const uint16_t* out, const float* lse, int B, int T, int C,
+                                   int NH);
 
 // ---- layernorm ------------------------------------------------------------
 // Activations (out, inp, dres, dout) are fp32, or bf16 bits when bf16 != 0;
