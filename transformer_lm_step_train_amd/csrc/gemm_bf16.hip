@@ -4,17 +4,22 @@
 // C 语言实现", section "用C语言实现LLM": the matmul layer; the reduced-precision
 // extension is named by yinghuohong.cn, section "脚动完成每一个层前向/反向流传").
 //
-// Same operand conventions and tiling as the fp32 kernel: 128x128 output tile
-// per 256-thread workgroup, 64x64 per wave (2x2 blocks of the 32x32 MFMA), a
+// Two kernels share the operand conventions of the fp32 one (NT forward, NN
+// input gradient, TN weight gradient) and its fused epilogues; outputs are
+// bf16 activations or fp32 weight gradients (+=).
+//
+// The forward and most input-gradient products use a 128x128 output tile per
+// 256-thread workgroup, 64x64 per wave (2x2 blocks of the 32x32 MFMA), a
 // reduction step of 64 staged through two LDS buffers with a two-deep
 // register prefetch (whole steps only in the main loop, rows past the
 // matrix clamped to its last row; a partial last step is zero-padded after
-// the loop).  In LDS every operand is stored [row][k] (72 bf16 per
-// row), so each MFMA operand (8 consecutive k of one row) is one 16-byte
-// read.  Operands whose free index is contiguous in HBM are loaded as 8 rows
-// of k by 4 columns per thread and transposed in registers before the LDS
-// store.  Outputs are bf16 activations (with the fused bias, residual, GELU
-// or GELU-derivative epilogues) or fp32 weight gradients (+=).
+// the loop).  In LDS every operand is stored [row][k] (72 bf16 per row), so
+// each MFMA operand (8 consecutive k of one row) is one 16-byte read.
+// Operands whose free index is contiguous in HBM are loaded as 8 rows of k by
+// 4 columns per thread and transposed in registers before the LDS store.
+//
+// Weight gradients and the LM-head input gradient split K and take the
+// 256x256 kernel further below.
 #include <algorithm>
 #include <cmath>
 #include <type_traits>
@@ -336,6 +341,265 @@ __global__ __launch_bounds__(NTHR, 2) void gemm_bf16_kernel(const GemmArgsH a, i
     }
 }
 
+// ---- large tiles for the weight-gradient and long-K products -------------
+//
+// The products above use 128x128 tiles (2 x 2 MFMA blocks per wave).  The
+// weight gradients (K = B*T, few output tiles) and the LM-head input
+// gradient (K = V) split K; there a 256x256 tile per workgroup (4 x 4 blocks
+// per wave, one workgroup per CU) halves the operand traffic per MFMA from
+// LDS and L2 and measured 10-45% faster.  Its LDS rows hold 64 bf16 with the
+// eight 16-byte chunks permuted by chunk ^ ((row >> 1) & 7), so operand
+// reads and the stores of both loaders avoid bank conflicts without padding;
+// operands whose free index is contiguous are loaded as 8 rows x 8 k blocks
+// and transposed in registers.
+// element offset of 16-byte chunk c (0..7) of row r
+__device__ __forceinline__ int sw(int r, int c) { return r * BK + 8 * (c ^ ((r >> 1) & 7)); }
+
+template <bool KC, int R>
+struct TileS;
+
+// Reduction index contiguous: element (r, k) at g[r*ld + k].  A thread moves
+// 16-byte chunks (8 consecutive k of one row).
+template <int R>
+struct TileS<true, R> {
+    static constexpr int PER = R * 8 / NTHR;
+    uint4 v[PER];
+    template <bool TAIL>
+    __device__ __forceinline__ void load(const uint16_t* __restrict__ g, int64_t ld, int r0,
+                                         int Rn, int k0, int K) {
+#pragma unroll
+        for (int i = 0; i < PER; i++) {
+            const int idx = threadIdx.x + NTHR * i;
+            const int r = min(r0 + (idx >> 3), Rn - 1);
+            const int k = k0 + (idx & 7) * 8;
+            if (!TAIL) {
+                v[i] = *reinterpret_cast<const uint4*>(g + (int64_t)r * ld + k);
+            } else {
+                const uint4 x =
+                    *reinterpret_cast<const uint4*>(g + (int64_t)r * ld + (k < K ? k : 0));
+                const uint32_t w[4] = {x.x, x.y, x.z, x.w};
+                uint32_t o[4];
+#pragma unroll
+                for (int j = 0; j < 4; j++) {
+                    const uint32_t lo = k + 2 * j < K ? (w[j] & 0xFFFFu) : 0u;
+                    const uint32_t hi = k + 2 * j + 1 < K ? (w[j] & 0xFFFF0000u) : 0u;
+                    o[j] = lo | hi;
+                }
+                v[i] = make_uint4(o[0], o[1], o[2], o[3]);
+            }
+        }
+    }
+    __device__ __forceinline__ void store(uint16_t* s) const {
+#pragma unroll
+        for (int i = 0; i < PER; i++) {
+            const int idx = threadIdx.x + NTHR * i;
+            *reinterpret_cast<uint4*>(s + sw(idx >> 3, idx & 7)) = v[i];
+        }
+    }
+};
+
+// Free index contiguous: element (r, k) at g[k*ld + r].  A task is 8 rows x
+// 8 k: eight 16-byte loads (8 rows at one k), transposed in registers into
+// eight 16-byte row chunks.  With fewer tasks than threads the spare
+// threads repeat a task's loads (the same count of loads everywhere) and
+// skip its store.
+template <int R>
+struct TileS<false, R> {
+    static constexpr int TASKS = R;  // (R / 8 row groups) x (8 k chunks)
+    static constexpr int PER = (TASKS + NTHR - 1) / NTHR;
+    uint4 v[PER][8];
+    template <bool TAIL>
+    __device__ __forceinline__ void load(const uint16_t* __restrict__ g, int64_t ld, int r0,
+                                         int Rn, int k0, int K) {
+#pragma unroll
+        for (int t = 0; t < PER; t++) {
+            const int idx = (threadIdx.x + NTHR * t) % TASKS;
+            const int c = idx & 7;
+            int r = r0 + (idx >> 3) * 8;
+            r = r < Rn ? r : ((Rn - 1) & ~7);
+#pragma unroll
+            for (int i = 0; i < 8; i++) {
+                const int k = k0 + 8 * c + i;
+                if (!TAIL) {
+                    v[t][i] = *reinterpret_cast<const uint4*>(g + (int64_t)k * ld + r);
+                } else {
+                    const uint4 x =
+                        *reinterpret_cast<const uint4*>(g + (int64_t)(k < K ? k : 0) * ld + r);
+                    v[t][i] = k < K ? x : make_uint4(0u, 0u, 0u, 0u);
+                }
+            }
+        }
+    }
+    __device__ __forceinline__ void store(uint16_t* s) const {
+#pragma unroll
+        for (int t = 0; t < PER; t++) {
+            const int idx = threadIdx.x + NTHR * t;
+            if (TASKS % NTHR != 0 && idx >= TASKS) continue;
+            const int c = idx & 7, rb = (idx >> 3) * 8;
+            // row rb + j holds element j of each of the 8 loaded k-rows
+#pragma unroll
+            for (int j = 0; j < 8; j++) {
+                uint32_t e[8];
+#pragma unroll
+                for (int i = 0; i < 8; i++) {
+                    const uint32_t w = (&v[t][i].x)[j >> 1];
+                    e[i] = (j & 1) ? (w >> 16) : (w & 0xFFFFu);
+                }
+                *reinterpret_cast<uint4*>(s + sw(rb + j, c)) =
+                    make_uint4(e[0] | (e[1] << 16), e[2] | (e[3] << 16), e[4] | (e[5] << 16),
+                               e[6] | (e[7] << 16));
+            }
+        }
+    }
+};
+
+__device__ __forceinline__ uint4 frag_s(const uint16_t* s, int r, int g, int q) {
+    return *reinterpret_cast<const uint4*>(s + sw(r, 2 * q + g));
+}
+
+template <int MI, int NI>
+struct Shape {
+    static constexpr int BM = 64 * MI, BN = 64 * NI;
+    static constexpr int WM = 32 * MI, WN = 32 * NI;
+    static constexpr int STAGE = (BM + BN) * BK;   // bf16 elements per LDS stage
+    static constexpr int EPI_LD = WN + 4;          // fp32 staging row stride
+    static constexpr int EPI_F = 4 * 32 * EPI_LD;  // staging floats (4 waves x 32 rows)
+    static constexpr int LDS_BYTES = 2 * STAGE * 2 > EPI_F * 4 ? 2 * STAGE * 2 : EPI_F * 4;
+    static constexpr int OCC = LDS_BYTES <= 80 * 1024 ? 2 : 1;  // workgroups per CU
+};
+
+template <int OP, int EPI, int MI, int NI>
+__global__ __launch_bounds__(NTHR, (Shape<MI, NI>::OCC)) void gemm_bf16_big_kernel(
+    const GemmArgsH a, int tiles_m, int tiles_n, int kchunk, float* __restrict__ partial) {
+    using SH = Shape<MI, NI>;
+    constexpr bool AKC = (OP != GEMM_TN);
+    constexpr bool BKC = (OP == GEMM_NT);
+    using TA = TileS<AKC, SH::BM>;
+    using TB = TileS<BKC, SH::BN>;
+    __shared__ __attribute__((aligned(16))) unsigned char smraw[SH::LDS_BYTES];
+    uint16_t* smh = reinterpret_cast<uint16_t*>(smraw);
+
+    const int tile = xcd_remap(blockIdx.x, tiles_m * tiles_n);
+    constexpr int GM = 8;
+    const int per_group = GM * tiles_n;
+    const int group = tile / per_group;
+    const int first_m = group * GM;
+    const int gm = min(tiles_m - first_m, GM);
+    const int in_g = tile - group * per_group;
+    const int m0 = (first_m + in_g % gm) * SH::BM;
+    const int n0 = (in_g / gm) * SH::BN;
+
+    const int k_begin = blockIdx.z * kchunk;
+    const int k_end = min(a.K, k_begin + kchunk);
+    const int nfull = (k_end - k_begin) / BK;
+
+    const int lane = threadIdx.x & 63, wave = threadIdx.x >> 6;
+    const int wm = (wave >> 1) * SH::WM, wn = (wave & 1) * SH::WN;
+    const int li = lane & 31, g = lane >> 5;
+
+    floatx16 acc[MI][NI];
+#pragma unroll
+    for (int i = 0; i < MI; i++)
+#pragma unroll
+        for (int j = 0; j < NI; j++)
+#pragma unroll
+            for (int e = 0; e < 16; e++) acc[i][j][e] = 0.f;
+
+    TA ta[2];
+    TB tb[2];
+    auto issue = [&](auto slotc, int kt) {
+        constexpr int S = decltype(slotc)::value;
+        const int kk = k_begin + min(kt, nfull - 1) * BK;
+        ta[S].template load<false>(a.A, a.lda, m0, a.M, kk, k_end);
+        tb[S].template load<false>(a.B, a.ldb, n0, a.N, kk, k_end);
+    };
+    auto compute = [&](const uint16_t* sa, const uint16_t* sb) {
+#pragma unroll
+        for (int q = 0; q < BK / 16; q++) {
+            uint4 af[MI], bf[NI];
+#pragma unroll
+            for (int i = 0; i < MI; i++) af[i] = frag_s(sa, wm + 32 * i + li, g, q);
+#pragma unroll
+            for (int j = 0; j < NI; j++) bf[j] = frag_s(sb, wn + 32 * j + li, g, q);
+#pragma unroll
+            for (int i = 0; i < MI; i++)
+#pragma unroll
+                for (int j = 0; j < NI; j++) acc[i][j] = mfma(af[i], bf[j], acc[i][j]);
+        }
+    };
+    using I0 = std::integral_constant<int, 0>;
+    using I1 = std::integral_constant<int, 1>;
+    auto sA = [&](int b) { return smh + b * SH::STAGE; };
+    auto sB = [&](int b) { return smh + b * SH::STAGE + SH::BM * BK; };
+    if (nfull > 0) {
+        issue(I0{}, 0);
+        ta[0].store(sA(0));
+        tb[0].store(sB(0));
+        issue(I1{}, 1);
+    }
+    __syncthreads();
+    auto step = [&](int kt, auto slotc) {
+        constexpr int S = decltype(slotc)::value;
+        constexpr int NS = S ^ 1;
+        const int cur = kt & 1;
+        issue(slotc, kt + 2);
+        __builtin_amdgcn_sched_barrier(0);  // loads stay ahead of the MFMAs
+        compute(sA(cur), sB(cur));
+        // unconditional: no path reaches the next loads with this slot pending
+        ta[NS].store(sA(cur ^ 1));
+        tb[NS].store(sB(cur ^ 1));
+        __syncthreads();
+    };
+    int kt = 0;
+    for (; kt + 1 < nfull; kt += 2) {
+        step(kt, I0{});
+        step(kt + 1, I1{});
+    }
+    if (kt < nfull) step(kt, I0{});
+    if (k_begin + nfull * BK < k_end) {  // partial last step, zero-padded
+        const int kk = k_begin + nfull * BK;
+        ta[0].template load<true>(a.A, a.lda, m0, a.M, kk, k_end);
+        tb[0].template load<true>(a.B, a.ldb, n0, a.N, kk, k_end);
+        ta[0].store(sA(0));
+        tb[0].store(sB(0));
+        __syncthreads();
+        compute(sA(0), sB(0));
+        __syncthreads();
+    }
+
+    // Epilogue: each wave stages one 32-row strip (32 x WN fp32) at a time in
+    // its own LDS region and applies the epilogue along rows (the main
+    // loop's buffers are free after the last barrier; a wave reads back only
+    // what it wrote).
+    float* ws = reinterpret_cast<float*>(smraw) + wave * 32 * SH::EPI_LD;
+#pragma unroll
+    for (int i = 0; i < MI; i++) {
+#pragma unroll
+        for (int j = 0; j < NI; j++)
+#pragma unroll
+            for (int e = 0; e < 16; e++)
+                ws[(8 * (e >> 2) + 4 * g + (e & 3)) * SH::EPI_LD + 32 * j + li] = acc[i][j][e];
+        __builtin_amdgcn_s_waitcnt(0xc07f);  // lgkmcnt(0): the strip is in LDS
+        __builtin_amdgcn_wave_barrier();
+        constexpr int C4 = SH::WN / 4;
+#pragma unroll 4
+        for (int idx = lane; idx < 32 * C4; idx += 64) {
+            const int r = idx / C4, c4 = (idx % C4) * 4;
+            const float4 v = ld4(ws + r * SH::EPI_LD + c4);
+            const int row = m0 + wm + 32 * i + r, col = n0 + wn + c4;
+            if (row >= a.M) continue;
+            if (col + 3 < a.N) {
+                epi4<EPI>(a, partial, row, col, v);
+            } else {
+                if (col < a.N) epi1<EPI>(a, partial, row, col, v.x);
+                if (col + 1 < a.N) epi1<EPI>(a, partial, row, col + 1, v.y);
+                if (col + 2 < a.N) epi1<EPI>(a, partial, row, col + 2, v.z);
+            }
+        }
+        __builtin_amdgcn_wave_barrier();
+    }
+}
+
 template <int EPI>
 __global__ __launch_bounds__(256) void splitk_reduce_bf16_kernel(const GemmArgsH a,
                                                                  const float* __restrict__ partial,
@@ -362,61 +626,134 @@ inline int cdiv(int64_t a, int64_t b) { return (int)((a + b - 1) / b); }
 
 int split_chunk_h(int K, int splits) { return cdiv(cdiv(K, splits), BK) * BK; }
 
-// Workgroups resident at once (two per compute unit).
-int resident_slots_h() {
-    static int slots = 0;
-    if (!slots) {
-        int dev = 0, cus = 0;
-        if (hipGetDevice(&dev) != hipSuccess ||
-            hipDeviceGetAttribute(&cus, hipDeviceAttributeMultiprocessorCount, dev) != hipSuccess ||
-            cus <= 0)
+int cu_count_h() {
+    static int cus = 0;
+    if (!cus) {
+        int dev = 0, n = 0;
+        if (hipGetDevice(&dev) == hipSuccess &&
+            hipDeviceGetAttribute(&n, hipDeviceAttributeMultiprocessorCount, dev) == hipSuccess &&
+            n > 0)
+            cus = n;
+        else
             cus = 256;
-        slots = 2 * cus;
     }
-    return slots;
+    return cus;
 }
 
-// Weight gradients (K = B*T, few output tiles) are split over K: the
-// smallest split count that fills about two whole rounds of resident
-// workgroups, each split at least 4 reduction steps long.
-int choose_splits_h(int op, int epi, int M, int N, int K) {
-    if ((N % 4) != 0 || op != GEMM_TN || (epi != EPI_ACCUM && epi != EPI_STORE)) return 1;
-    const int tiles = cdiv(M, BM) * cdiv(N, BN);
-    const int slots = resident_slots_h();
-    if (tiles >= 2 * slots) return 1;
-    const int max_splits = K / (BK * 4);
-    int best = 1;
-    double best_eff = 0.0;
-    for (int sp = 2; sp <= max_splits; sp++) {
-        const int nz = cdiv(K, split_chunk_h(K, sp));
-        const double x = (double)tiles * nz / slots;
-        if (x > 4.0) break;
-        const double eff = x / std::ceil(x);
-        if (x >= 1.8 && eff >= 0.9) return sp;
-        if (eff > best_eff + 0.02) {
-            best_eff = eff;
-            best = sp;
+// Which kernel, and how many K splits.  Weight gradients (TN) and input
+// gradients with a very long K (the LM head, K = V) take the 256x256 kernel
+// with the split count that minimises (rounds of one-per-CU workgroups) x
+// (reduction steps per workgroup), each split at least 4 steps; everything
+// else takes the 128x128 kernel unsplit.
+struct PlanH {
+    bool big;
+    int splits;
+};
+
+PlanH plan_h(const GemmArgsH& a) {
+    const bool big = (a.op == GEMM_TN || (a.op == GEMM_NN && a.K >= 16384)) && a.lda % 8 == 0 &&
+                     a.ldb % 8 == 0;
+    if (!big) return {false, 1};
+    const bool can_split = (a.N % 4) == 0 && (a.epi == EPI_ACCUM || a.epi == EPI_STORE);
+    const int tiles = cdiv(a.M, 256) * cdiv(a.N, 256);
+    const int cus = cu_count_h();
+    const int max_splits = can_split ? std::min(32, std::max(1, a.K / (4 * BK))) : 1;
+    PlanH best{true, 1};
+    double best_t = 1e300;
+    for (int sp = 1; sp <= max_splits; sp++) {
+        const int chunk = sp > 1 ? split_chunk_h(a.K, sp) : a.K;
+        const int nz = sp > 1 ? cdiv(a.K, chunk) : 1;
+        if (nz != sp) continue;
+        const double t = std::ceil((double)tiles * nz / cus) * std::ceil((double)chunk / BK);
+        if (t < best_t) {
+            best_t = t;
+            best.splits = sp;
         }
     }
     return best;
 }
 
 template <int OP, int EPI>
-hipError_t launch_h(hipStream_t s, const GemmArgsH& a, int splits, float* ws) {
+hipError_t launch_h(hipStream_t s, const GemmArgsH& a, float* ws) {
     const int tm = cdiv(a.M, BM), tn = cdiv(a.N, BN);
+    hipLaunchKernelGGL((gemm_bf16_kernel<OP, EPI>), dim3(tm * tn, 1, 1), dim3(NTHR), 0, s, a, tm,
+                       tn, a.K > 0 ? a.K : 1, ws);
+    return hipGetLastError();
+}
+
+template <int OP, int EPI>
+hipError_t launch_big(hipStream_t s, const GemmArgsH& a, int splits, float* ws) {
+    const int tm = cdiv(a.M, 256), tn = cdiv(a.N, 256);
     const int chunk = splits > 1 ? split_chunk_h(a.K, splits) : (a.K > 0 ? a.K : 1);
     const int nz = splits > 1 ? cdiv(a.K, chunk) : 1;
-    hipLaunchKernelGGL((gemm_bf16_kernel<OP, EPI>), dim3(tm * tn, 1, nz), dim3(NTHR), 0, s, a, tm,
-                       tn, chunk, ws);
+    hipLaunchKernelGGL((gemm_bf16_big_kernel<OP, EPI, 4, 4>), dim3(tm * tn, 1, nz), dim3(NTHR), 0,
+                       s, a, tm, tn, chunk, ws);
     return hipGetLastError();
+}
+
+hipError_t run_big(hipStream_t s, const GemmArgsH& a, int splits, float* ws) {
+    if (splits > 1) {
+        switch (a.op) {
+            case GEMM_NN: return launch_big<GEMM_NN, EPI_PARTIAL>(s, a, splits, ws);
+            case GEMM_TN: return launch_big<GEMM_TN, EPI_PARTIAL>(s, a, splits, ws);
+            default: return hipErrorInvalidValue;
+        }
+    }
+    switch (a.op) {
+        case GEMM_NN:
+            switch (a.epi) {
+                case EPI_STORE: return launch_big<GEMM_NN, EPI_STORE>(s, a, 1, ws);
+                case EPI_GELU_BWD: return launch_big<GEMM_NN, EPI_GELU_BWD>(s, a, 1, ws);
+                default: return hipErrorInvalidValue;
+            }
+        case GEMM_TN:
+            switch (a.epi) {
+                case EPI_STORE: return launch_big<GEMM_TN, EPI_STORE>(s, a, 1, ws);
+                case EPI_ACCUM: return launch_big<GEMM_TN, EPI_ACCUM>(s, a, 1, ws);
+                default: return hipErrorInvalidValue;
+            }
+        default: return hipErrorInvalidValue;
+    }
+}
+
+hipError_t run_small(hipStream_t s, const GemmArgsH& a, float* ws) {
+    switch (a.op) {
+        case GEMM_NT:
+            switch (a.epi) {
+                case EPI_STORE: return launch_h<GEMM_NT, EPI_STORE>(s, a, ws);
+                case EPI_RESID: return launch_h<GEMM_NT, EPI_RESID>(s, a, ws);
+                case EPI_GELU: return launch_h<GEMM_NT, EPI_GELU>(s, a, ws);
+                default: return hipErrorInvalidValue;
+            }
+        case GEMM_NN:
+            switch (a.epi) {
+                case EPI_STORE: return launch_h<GEMM_NN, EPI_STORE>(s, a, ws);
+                case EPI_GELU_BWD: return launch_h<GEMM_NN, EPI_GELU_BWD>(s, a, ws);
+                default: return hipErrorInvalidValue;
+            }
+        case GEMM_TN:
+            switch (a.epi) {
+                case EPI_STORE: return launch_h<GEMM_TN, EPI_STORE>(s, a, ws);
+                case EPI_ACCUM: return launch_h<GEMM_TN, EPI_ACCUM>(s, a, ws);
+                default: return hipErrorInvalidValue;
+            }
+        default: return hipErrorInvalidValue;
+    }
 }
 
 }  // namespace
 
 size_t gemm_bf16_workspace_bytes(int op, int epi, int M, int N, int K) {
-    const int splits = choose_splits_h(op, epi, M, N, K);
-    if (splits <= 1) return 0;
-    return (size_t)cdiv(K, split_chunk_h(K, splits)) * M * N * sizeof(float);
+    GemmArgsH a{};
+    a.op = op;
+    a.epi = epi;
+    a.M = M;
+    a.N = N;
+    a.K = K;
+    a.lda = a.ldb = 8;  // the workspace bound assumes the large-tile path is eligible
+    const PlanH p = plan_h(a);
+    if (!p.big || p.splits <= 1) return 0;
+    return (size_t)cdiv(K, split_chunk_h(K, p.splits)) * M * N * sizeof(float);
 }
 
 hipError_t gemm_bf16(hipStream_t s, const GemmArgsH& a, float* ws, size_t ws_bytes) {
@@ -428,44 +765,23 @@ hipError_t gemm_bf16(hipStream_t s, const GemmArgsH& a, float* ws, size_t ws_byt
     if (a.lda < (a.op == GEMM_TN ? a.M : a.K) || a.ldb < (a.op == GEMM_NT ? a.K : a.N) ||
         a.ldc < a.N)
         return hipErrorInvalidValue;
-    int splits = choose_splits_h(a.op, a.epi, a.M, a.N, a.K);
-    if (splits > 1 && gemm_bf16_workspace_bytes(a.op, a.epi, a.M, a.N, a.K) > ws_bytes) splits = 1;
-    if (splits > 1) {
-        hipError_t e = launch_h<GEMM_TN, EPI_PARTIAL>(s, a, splits, ws);
-        if (e != hipSuccess) return e;
-        const int nz = cdiv(a.K, split_chunk_h(a.K, splits));
-        const int64_t n4 = (int64_t)a.M * (a.N / 4);
-        const int blocks = (int)std::min<int64_t>((n4 + 255) / 256, 4096);
-        if (a.epi == EPI_ACCUM)
-            hipLaunchKernelGGL(splitk_reduce_bf16_kernel<EPI_ACCUM>, dim3(blocks), dim3(256), 0, s,
-                               a, ws, nz);
-        else
-            hipLaunchKernelGGL(splitk_reduce_bf16_kernel<EPI_STORE>, dim3(blocks), dim3(256), 0, s,
-                               a, ws, nz);
-        return hipGetLastError();
-    }
-    switch (a.op) {
-        case GEMM_NT:
-            switch (a.epi) {
-                case EPI_STORE: return launch_h<GEMM_NT, EPI_STORE>(s, a, 1, ws);
-                case EPI_RESID: return launch_h<GEMM_NT, EPI_RESID>(s, a, 1, ws);
-                case EPI_GELU: return launch_h<GEMM_NT, EPI_GELU>(s, a, 1, ws);
-                default: return hipErrorInvalidValue;
-            }
-        case GEMM_NN:
-            switch (a.epi) {
-                case EPI_STORE: return launch_h<GEMM_NN, EPI_STORE>(s, a, 1, ws);
-                case EPI_GELU_BWD: return launch_h<GEMM_NN, EPI_GELU_BWD>(s, a, 1, ws);
-                default: return hipErrorInvalidValue;
-            }
-        case GEMM_TN:
-            switch (a.epi) {
-                case EPI_STORE: return launch_h<GEMM_TN, EPI_STORE>(s, a, 1, ws);
-                case EPI_ACCUM: return launch_h<GEMM_TN, EPI_ACCUM>(s, a, 1, ws);
-                default: return hipErrorInvalidValue;
-            }
-        default: return hipErrorInvalidValue;
-    }
+    PlanH p = plan_h(a);
+    if (!p.big) return run_small(s, a, ws);
+    if (p.splits > 1 &&
+        (size_t)cdiv(a.K, split_chunk_h(a.K, p.splits)) * a.M * a.N * sizeof(float) > ws_bytes)
+        p.splits = 1;
+    hipError_t e = run_big(s, a, p.splits, ws);
+    if (e != hipSuccess || p.splits <= 1) return e;
+    const int nz = cdiv(a.K, split_chunk_h(a.K, p.splits));
+    const int64_t n4 = (int64_t)a.M * (a.N / 4);
+    const int blocks = (int)std::min<int64_t>((n4 + 255) / 256, 4096);
+    if (a.epi == EPI_ACCUM)
+        hipLaunchKernelGGL(splitk_reduce_bf16_kernel<EPI_ACCUM>, dim3(blocks), dim3(256), 0, s, a,
+                           ws, nz);
+    else
+        hipLaunchKernelGGL(splitk_reduce_bf16_kernel<EPI_STORE>, dim3(blocks), dim3(256), 0, s, a,
+                           ws, nz);
+    return hipGetLastError();
 }
 
 }  // namespace gk
