@@ -146,6 +146,32 @@ GPT2_API int gpt2_forward_device(gpt2_model* model, const int32_t* tokens,
                         const int32_t* targets, int B, int T,
                         float* mean_loss);
 
+/* One token drawn from the model's next-token distribution at position
+ * (b, t) of the last forward, which must have been run without targets (a
+ * forward with targets replaces the logits by their gradient): the softmax of
+ * that logits row, sampled by the inverse CDF -- the smallest token v with
+ * coin < sum_{u <= v} p_u (V - 1 if rounding leaves none).  coin is a
+ * uniform draw in [0, 1) supplied by the caller, so callers own the random
+ * stream.  The pages' training loop samples text from the model from a
+ * leading token 50256 (ujoy.net article "徒手用 1000 行 C 语言实现", section
+ * "训练过程": the "generated:" line); sampling from the softmax is the
+ * plainest reading.  *token is written on the host; the call synchronizes.
+ * Returns GPT2_OK, GPT2_EINVAL (NULL, position outside the last forward's
+ * B x T, coin outside [0, 1)) or GPT2_ESTATE (no forward, or the last one
+ * had targets). */
+GPT2_API int gpt2_sample(gpt2_model* model, int b, int t, float coin, int32_t* token);
+
+/* Autoregressive generation for one sequence: tokens[0 .. prompt_len) is the
+ * prompt (host, ids in [0, V)); for t = prompt_len .. n-1 it runs a forward
+ * of tokens[0 .. t) (B = 1, T = t, no targets) and writes
+ * gpt2_sample(0, t-1, coins[t - prompt_len]) to tokens[t].  coins holds
+ * n - prompt_len uniforms in [0, 1).  Every step recomputes the whole prefix
+ * (no key/value cache).  Requires 1 <= prompt_len
+ * <= n <= seq_len of the config.  Errors as gpt2_forward / gpt2_sample; on
+ * error tokens[prompt_len .. n) may be partly written. */
+GPT2_API int gpt2_generate(gpt2_model* model, int32_t* tokens, int prompt_len, int n,
+                           const float* coins);
+
 /* Clears the parameter gradients (backward accumulates into them). */
 GPT2_API int gpt2_zero_grad(gpt2_model* model);
 

@@ -65,6 +65,10 @@ def _lib(precision: str):
     lib.oracle_backward.restype = _int
     lib.oracle_backward.argtypes = [_vp]
     lib.oracle_update.argtypes = [_vp] + [ctypes.c_double] * 5 + [_int]
+    lib.oracle_sample.restype = _int
+    lib.oracle_sample.argtypes = [_vp, _int, ctypes.c_double]
+    lib.oracle_generate.restype = _int
+    lib.oracle_generate.argtypes = [_vp, _vp, _int, _int, _vp]
     # layer primitives: pointers are passed as void*, sizes as int / int64
     sig = {
         "oracle_encoder_forward": [_vp, _vp, _vp, _vp, _int, _int, _int],
@@ -203,3 +207,20 @@ class OracleModel:
     def update(self, lr=1e-4, beta1=0.9, beta2=0.999, eps=1e-8,
                weight_decay=0.0, step=1):
         self.lib.oracle_update(self.h, lr, beta1, beta2, eps, weight_decay, step)
+
+    def generate(self, prompt, n, coins):
+        """B = 1 model: tokens 0..n-1, the prompt then n - len(prompt) draws
+        (the model's T positions are run each step; n <= T)."""
+        tok = np.zeros(self.T, dtype=np.int32)
+        tok[:len(prompt)] = prompt
+        c = np.ascontiguousarray(coins, dtype=np.float64)
+        if self.lib.oracle_generate(self.h, ptr(tok), len(prompt), n, ptr(c)) != 0:
+            raise ValueError("oracle_generate: bad arguments")
+        return tok[:n].copy()
+
+
+def sample(probs, coin, precision="f32"):
+    """Inverse-CDF draw from one probability row (oracle_sample)."""
+    lb = _lib(precision)
+    p = np.ascontiguousarray(probs, dtype=lb.dtype)
+    return int(lb.oracle_sample(ptr(p), p.size, float(coin)))

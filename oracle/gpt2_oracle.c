@@ -648,6 +648,41 @@ EXPORT double oracle_forward(OracleModel* M, const int* tokens,
     return M->mean_loss;
 }
 
+/* One draw from a probability row by the inverse CDF: the smallest v with
+ * coin * sum_u probs[u] < sum_{u <= v} probs[u] (sums in double, in index
+ * order), or V - 1 if rounding leaves none.  The pages show the trainer
+ * sampling text from the model after training (ujoy.net, section
+ * "训练过程": the "generated:" line); drawing from the softmax
+ * probabilities with a uniform coin is the plainest reading. */
+EXPORT int oracle_sample(const real* probs, int V, double coin) {
+    double total = 0;
+    for (int v = 0; v < V; v++) total += (double)probs[v];
+    const double target = coin * total;
+    double cum = 0;
+    for (int v = 0; v < V; v++) {
+        cum += (double)probs[v];
+        if (target < cum) return v;
+    }
+    return V - 1;
+}
+
+/* Generation for a B = 1 model: tokens[0 .. prompt_len) is the prompt; for
+ * t = prompt_len .. n-1, run the forward over all T positions (tokens at
+ * positions >= t do not reach position t-1 under the causal mask) and set
+ * tokens[t] = oracle_sample(probs at position t-1, coins[t - prompt_len]).
+ * tokens has M->T entries.  Returns 0, or -1 on a bad argument. */
+EXPORT int oracle_generate(OracleModel* M, int* tokens, int prompt_len, int n,
+                           const double* coins) {
+    const int V = M->cfg.vocab_size;
+    if (M->B != 1 || prompt_len < 1 || n < prompt_len || n > M->T) return -1;
+    for (int t = prompt_len; t < n; t++) {
+        oracle_forward(M, tokens, NULL);
+        const real* probs = M->a[A_PROBS] + (int64_t)(t - 1) * V;
+        tokens[t] = oracle_sample(probs, V, coins[t - prompt_len]);
+    }
+    return 0;
+}
+
 EXPORT void oracle_zero_grad(OracleModel* M) {
     memset(M->grads, 0, (size_t)M->num_params * sizeof(real));
 }

@@ -1,0 +1,162 @@
+"""GPU parity of sampling and generation (gpt2_sample / gpt2_generate)
+against the oracle's inverse-CDF draw (oracle_sample / oracle_generate) on
+the same weights and the same coins.
+
+A draw is an integer decided by floating point: both sides compare the
+coin against a CDF summed in double, but from logits that differ by fp32
+rounding, so a coin that falls within that rounding of a CDF step can pick
+the neighbouring token.  The tests require identical tokens, except that
+the first disagreement is accepted when the oracle's coin lies within 1e-5
+(relative) of a step of its own CDF at that position; comparison stops
+there because the sequences diverge.
+"""
+import json
+import os
+
+import numpy as np
+import pytest
+
+torch = pytest.importorskip("torch")
+
+import oracle
+from oracle import OracleModel
+from transformer_lm_step_train_amd import synth
+
+pytestmark = [
+    pytest.mark.gpu,
+    pytest.mark.skipif(not torch.cuda.is_available(), reason="needs a GPU"),
+]
+
+GOLDEN = os.path.join(os.path.dirname(__file__), "golden")
+
+
+def gpt2():
+    from transformer_lm_step_train_amd import gpt2 as g
+    return g
+
+
+def models(name, n, precision=None):
+    g = gpt2()
+    c = synth.CONFIGS[name]
+    params = synth.init_params(c["L"], c["C"], c["V"], c["maxT"])
+    m = g.Model(c["L"], c["C"], c["NH"], c["V"], c["maxT"], 1, n,
+                precision=g.GPT2_FP32 if precision is None else precision)
+    m.set_params(params)
+    o = OracleModel(c["L"], c["C"], c["NH"], c["V"], c["maxT"], 1, n)
+    o.params[:] = params
+    return m, o, c
+
+
+def compare(tok_gpu, tok_ref, o, coins, prompt_len, V):
+    """Index of the first accepted boundary divergence, or len(tok) if equal."""
+    probs = o.act("probs").reshape(-1, V)
+    for t in range(prompt_len, len(tok_ref)):
+        if tok_gpu[t] == tok_ref[t]:
+            continue
+        cdf = np.cumsum(probs[t - 1].astype(np.float64))
+        gap = np.min(np.abs(cdf - float(coins[t - prompt_len]) * cdf[-1])) / cdf[-1]
+        print(f"[gen] divergence at t={t}: gpu {tok_gpu[t]} oracle {tok_ref[t]} "
+              f"coin-to-step gap {gap:.2e}", flush=True)
+        assert gap < 1e-5, (t, tok_gpu[t], tok_ref[t], gap)
+        return t
+    return len(tok_ref)
+
+
+@pytest.mark.parametrize("name", ["tiny", "ragged"])
+def test_generate_matches_oracle(name):
+    c = synth.CONFIGS[name]
+    n = c["maxT"]
+    print(f"[gen] config={name} n={n}", flush=True)
+    m, o, _ = models(name, n)
+    coins = synth.coins(n - 1)
+    prompt = [c["V"] - 1]
+    tg = m.generate(prompt, n, coins)
+    to = o.generate(prompt, n, coins)
+    assert np.all((tg >= 0) & (tg < c["V"]))
+    upto = compare(tg, to, o, coins, 1, c["V"])
+    print(f"[gen] {name}: identical through position {upto} of {n}", flush=True)
+    m.close()
+    o.close()
+
+
+def test_generate_page_shape_124m():
+    """The pages' generation: 64 tokens from a leading 50256, on the 124M
+    model (random weights here; the page's own ids need trained ones)."""
+    g = json.load(open(os.path.join(GOLDEN, "gpt2_124m_printout.json")))
+    n, first = g["generated_length"], g["generated_first_token"]
+    m, o, c = models("gpt2_124m_b4t64", n)
+    coins = synth.coins(n - 1)
+    tg = m.generate([first], n, coins)
+    to = o.generate([first], n, coins)
+    upto = compare(tg, to, o, coins, 1, c["V"])
+    print(f"[gen] 124M: identical through position {upto} of {n}; gpu {tg[:12].tolist()}",
+          flush=True)
+    assert tg[0] == 50256
+    m.close()
+    o.close()
+
+
+def test_sample_rows_of_a_batch_forward():
+    """gpt2_sample at every position of a B x T forward without targets
+    equals the oracle's draw from its probabilities at that position."""
+    gg = gpt2()
+    c = synth.CONFIGS["ragged"]
+    params = synth.init_params(c["L"], c["C"], c["V"], c["maxT"])
+    m = gg.Model(c["L"], c["C"], c["NH"], c["V"], c["maxT"], c["B"], c["T"])
+    m.set_params(params)
+    o = OracleModel(c["L"], c["C"], c["NH"], c["V"], c["maxT"], c["B"], c["T"])
+    o.params[:] = params
+    tok, _ = synth.token_stream(c["B"], c["T"], c["V"])
+    m.forward(tok)
+    o.forward(tok)
+    probs = o.act("probs").reshape(c["B"], c["T"], c["V"])
+    coins = synth.coins(c["B"] * c["T"], seed=99).reshape(c["B"], c["T"])
+    bad = 0
+    for b in range(c["B"]):
+        for t in range(c["T"]):
+            got = m.sample(b, t, float(coins[b, t]))
+            want = oracle.sample(probs[b, t], coins[b, t])
+            if got != want:
+                cdf = np.cumsum(probs[b, t].astype(np.float64))
+                gap = np.min(np.abs(cdf - float(coins[b, t]) * cdf[-1])) / cdf[-1]
+                assert gap < 1e-5, (b, t, got, want, gap)
+                bad += 1
+    assert bad <= 2
+    m.close()
+    o.close()
+
+
+def test_sample_errors():
+    gg = gpt2()
+    c = synth.CONFIGS["tiny"]
+    m = gg.Model(c["L"], c["C"], c["NH"], c["V"], c["maxT"], c["B"], c["T"])
+    m.set_params(synth.init_params(c["L"], c["C"], c["V"], c["maxT"]))
+    with pytest.raises(gg.GPT2Error):  # no forward yet
+        m.sample(0, 0, 0.5)
+    tok, tgt = synth.token_stream(c["B"], c["T"], c["V"])
+    m.forward(tok, tgt)
+    with pytest.raises(gg.GPT2Error):  # logits replaced by their gradient
+        m.sample(0, 0, 0.5)
+    m.forward(tok)
+    for b, t, coin in ((c["B"], 0, 0.5), (0, c["T"], 0.5), (0, 0, 1.0), (0, 0, -0.1)):
+        with pytest.raises(gg.GPT2Error):
+            m.sample(b, t, coin)
+    assert 0 <= m.sample(0, 0, 0.5) < c["V"]
+    with pytest.raises(gg.GPT2Error):  # n beyond seq_len
+        m.generate([1], c["T"] + 1, synth.coins(c["T"]))
+    m.close()
+
+
+def test_generate_bf16_valid_and_deterministic():
+    g = gpt2()
+    c = synth.CONFIGS["tiny"]
+    n = c["maxT"]
+    coins = synth.coins(n - 1)
+    outs = []
+    for _ in range(2):
+        m, o, _ = models("tiny", n, precision=g.GPT2_BF16_MIXED)
+        outs.append(m.generate([c["V"] - 1], n, coins))
+        m.close()
+        o.close()
+    assert np.array_equal(outs[0], outs[1])
+    assert np.all((outs[0] >= 0) & (outs[0] < c["V"]))

@@ -401,3 +401,94 @@ def test_synth_generator_reference_values():
     assert t.min() >= 0 and t.max() < 50257
     tok, tgt = synth.token_stream(2, 5, 100)
     assert np.array_equal(tok.reshape(-1)[1:], tgt.reshape(-1)[:-1])
+
+
+# ---------------------------------------------------------------- sampling --
+
+def _near_boundary(probs, coin, tol=1e-6):
+    cdf = np.cumsum(np.asarray(probs, dtype=np.float64))
+    return np.min(np.abs(cdf - coin * cdf[-1])) < tol * cdf[-1]
+
+
+def test_sample_uniform_row_is_floor_coin_times_V():
+    """Equal probabilities: the inverse-CDF draw is floor(coin * V)."""
+    for V in (7, 512, 50257):
+        probs = np.full(V, 1.0 / V, dtype=np.float32)
+        for coin in synth.coins(200, seed=11):
+            if _near_boundary(probs, coin):
+                continue
+            assert oracle.sample(probs, coin) == math.floor(float(coin) * V)
+
+
+def test_sample_one_hot_and_edges():
+    probs = np.zeros(100, dtype=np.float32)
+    probs[37] = 1.0
+    for coin in (0.0, 0.25, 0.999999):
+        assert oracle.sample(probs, coin) == 37
+    # coin 0 takes the first token with nonzero probability
+    probs = np.zeros(10, dtype=np.float32)
+    probs[[3, 8]] = 0.5
+    assert oracle.sample(probs, 0.0) == 3
+    assert oracle.sample(probs, 0.4999) == 3
+    assert oracle.sample(probs, 0.5) == 8
+
+
+def test_sample_matches_numpy_searchsorted():
+    """Library routine: the first index whose cumulative sum exceeds
+    coin * total (numpy cumsum + searchsorted, float64)."""
+    r = np.random.default_rng(5)
+    for V in (3, 97, 1001):
+        for _ in range(20):
+            probs = r.dirichlet(np.full(V, 0.3)).astype(np.float32)
+            coin = float(r.random())
+            if _near_boundary(probs, coin):
+                continue
+            cdf = np.cumsum(probs.astype(np.float64))
+            want = int(np.searchsorted(cdf, coin * cdf[-1], side="right"))
+            assert oracle.sample(probs, coin) == min(want, V - 1)
+
+
+def test_sample_frequencies_follow_probabilities():
+    probs = np.array([0.05, 0.1, 0.4, 0.15, 0.3], dtype=np.float32)
+    n = 200000
+    counts = np.bincount([oracle.sample(probs, c) for c in synth.coins(n, seed=3)],
+                         minlength=5)
+    sigma = np.sqrt(n * probs * (1 - probs))
+    assert np.all(np.abs(counts - n * probs) < 5 * sigma), counts
+
+
+def test_generate_with_zero_embeddings_is_floor_coin_times_V():
+    """wte = 0 makes every logit exactly 0, so every draw is floor(coin * V);
+    the prompt and the other weights do not matter."""
+    c = synth.CONFIGS["tiny"]
+    m = OracleModel(c["L"], c["C"], c["NH"], c["V"], c["maxT"], 1, c["maxT"])
+    m.params[:] = synth.init_params(c["L"], c["C"], c["V"], c["maxT"])
+    m.param("wte")[:] = 0
+    n = c["maxT"]
+    coins = synth.coins(n - 1)
+    tok = m.generate([c["V"] - 1], n, coins)
+    want = np.floor(coins.astype(np.float64) * c["V"]).astype(np.int64)
+    assert tok[0] == c["V"] - 1
+    assert np.array_equal(tok[1:], want)
+    m.close()
+
+
+def test_generate_is_causal_and_deterministic():
+    """Each draw depends only on the prefix: generating n tokens, then n + 8
+    with the same coins, agrees on the first n."""
+    c = synth.CONFIGS["tiny"]
+    params = synth.init_params(c["L"], c["C"], c["V"], c["maxT"])
+    m = OracleModel(c["L"], c["C"], c["NH"], c["V"], c["maxT"], 1, c["maxT"])
+    m.params[:] = params
+    coins = synth.coins(c["maxT"])
+    a = m.generate([5], 40, coins[:39])
+    b = m.generate([5], 48, coins[:47])
+    assert np.array_equal(a, b[:40])
+    assert np.all((b >= 0) & (b < c["V"]))
+    m.close()
+
+
+def test_page_generation_shape():
+    g = json.load(open(os.path.join(GOLDEN, "gpt2_124m_printout.json")))
+    assert g["generated_length"] == 64 and g["generated_first_token"] == 50256
+    assert g["generated_first_token"] == g["config"]["vocab_size"] - 1

@@ -107,6 +107,10 @@ hipError_t softmax_ce(hipStream_t s, void* logits, float* losses,
                       const int32_t* targets, int N, int V, int ldv,
                       float dscale, int* flag, int bf16);
 // out[0] = mean of x[0..n) (deterministic order)
+// One inverse-CDF draw (coin in [0, 1)) from softmax of one logits row of V
+// values; writes the token to out (device).
+hipError_t sample_row(hipStream_t s, const void* logits, int V, float coin, int32_t* out,
+                      int bf16);
 hipError_t mean_reduce(hipStream_t s, float* out, const float* x, int n);
 
 // ---- embedding -------------------------------------------------------------

@@ -207,6 +207,7 @@ struct gpt2_model {
     bool stage_pending = false;
     int B = 0, T = 0;
     bool have_fwd = false, have_targets = false;
+    bool logits_valid = false;  // last forward had no targets: logits intact
     Prof prof;
 
     template <class X>
@@ -222,6 +223,7 @@ struct gpt2_model {
     char* A(size_t off, size_t idx = 0) const { return base + off + idx * lay.es; }
     float* G(int i) const { return at<float>(lay.grads) + lay.poff[i]; }
     int* flag() const { return at<int>(lay.scalars + 4); }
+    int32_t* drawn() const { return at<int32_t>(lay.scalars + 8); }
     float* dloss() const { return at<float>(lay.scalars); }
 };
 
@@ -452,6 +454,7 @@ int forward_impl(gpt2_model* md, const int32_t* tok, const int32_t* tgt, int B, 
     md->T = T;
     md->have_fwd = true;
     md->have_targets = tgt != nullptr;
+    md->logits_valid = tgt == nullptr;
     return GPT2_OK;
 }
 
@@ -840,6 +843,39 @@ int gpt2_forward_device(gpt2_model* md, const int32_t* tokens, const int32_t* ta
     TRY(check_bt(md, B, T));
     TRY(forward_impl(md, tokens, targets, B, T));
     if (mean_loss) return read_loss(md, mean_loss);
+    return GPT2_OK;
+}
+
+int gpt2_sample(gpt2_model* md, int b, int t, float coin, int32_t* token) {
+    if (!valid_model(md) || !token) return fail(GPT2_EINVAL, "NULL argument");
+    if (!md->have_fwd || !md->logits_valid)
+        return fail(GPT2_ESTATE, "sampling needs a preceding forward without targets");
+    if (b < 0 || b >= md->B || t < 0 || t >= md->T)
+        return fail(GPT2_EINVAL, "position (%d, %d) outside the last forward's %d x %d", b, t,
+                    md->B, md->T);
+    if (!(coin >= 0.f && coin < 1.f)) return fail(GPT2_EINVAL, "coin must be in [0, 1)");
+    const Layout& y = md->lay;
+    const char* row = md->A(y.logits, ((size_t)b * md->T + t) * y.Vp);
+    LAUNCH(md, GPT2_KC_SOFTMAX_CE, 0, y.es * (double)y.V * 2.0 + 4.0,
+           gk::sample_row(md->stream, row, y.V, coin, md->drawn(), y.bf16));
+    TRY(hip_check(hipMemcpyAsync(md->h_scal + 2, md->drawn(), 4, hipMemcpyDeviceToHost,
+                                 md->stream),
+                  "token readback"));
+    TRY(hip_check(hipStreamSynchronize(md->stream), "stream synchronize"));
+    std::memcpy(token, md->h_scal + 2, 4);
+    return GPT2_OK;
+}
+
+int gpt2_generate(gpt2_model* md, int32_t* tokens, int prompt_len, int n, const float* coins) {
+    if (!valid_model(md) || !tokens || (!coins && n > prompt_len))
+        return fail(GPT2_EINVAL, "NULL argument");
+    if (prompt_len < 1 || n < prompt_len || n > md->lay.Tmax)
+        return fail(GPT2_EINVAL, "prompt_len=%d n=%d outside 1 <= prompt_len <= n <= %d",
+                    prompt_len, n, md->lay.Tmax);
+    for (int t = prompt_len; t < n; t++) {
+        TRY(gpt2_forward(md, tokens, nullptr, 1, t, nullptr));
+        TRY(gpt2_sample(md, 0, t - 1, coins[t - prompt_len], tokens + t));
+    }
     return GPT2_OK;
 }
 

@@ -137,7 +137,66 @@ __global__ __launch_bounds__(1024) void mean_kernel(float* __restrict__ out,
     }
 }
 
+// One draw from softmax(z) over a row of V logits by the inverse CDF: the
+// smallest v with coin * sum_u p_u < sum_{u <= v} p_u, or V - 1 if rounding
+// leaves none.  Each of the 1024 threads owns a contiguous run of the row;
+// the exponentials are fp32 and every sum is fp64 (run sums, then an ordered
+// exclusive scan over the runs), so the draw is deterministic and the CDF is
+// far more precise than the spacing between its steps.
+template <class T>
+__global__ __launch_bounds__(1024) void sample_kernel(const T* __restrict__ z, int V, float coin,
+                                                      int32_t* __restrict__ out) {
+    __shared__ float shm[16];
+    __shared__ double run[1024];
+    __shared__ double total;
+    __shared__ int best;
+    const int tid = threadIdx.x;
+    const int per = (V + 1023) / 1024;
+    const int b0 = min(V, tid * per), b1 = min(V, b0 + per);
+    float mx = -INFINITY;
+    for (int v = b0; v < b1; v++) mx = fmaxf(mx, Act<T>::ld1(z + v));
+    mx = block_max<1024>(mx, shm);
+    double s = 0.0;
+    for (int v = b0; v < b1; v++) s += (double)expf(Act<T>::ld1(z + v) - mx);
+    run[tid] = s;
+    __syncthreads();
+    if (tid == 0) {  // exclusive scan over the runs, in thread order
+        double acc = 0.0;
+        for (int i = 0; i < 1024; i++) {
+            const double t = run[i];
+            run[i] = acc;
+            acc += t;
+        }
+        total = acc;
+        best = V - 1;
+    }
+    __syncthreads();
+    const double target = (double)coin * total;
+    double c = run[tid];
+    for (int v = b0; v < b1; v++) {
+        c += (double)expf(Act<T>::ld1(z + v) - mx);
+        if (target < c) {
+            atomicMin(&best, v);
+            break;
+        }
+    }
+    __syncthreads();
+    if (tid == 0) *out = best;
+}
+
 }  // namespace
+
+hipError_t sample_row(hipStream_t s, const void* logits, int V, float coin, int32_t* out,
+                      int bf16) {
+    if (V <= 0) return hipErrorInvalidValue;
+    if (bf16)
+        hipLaunchKernelGGL(sample_kernel<uint16_t>, dim3(1), dim3(1024), 0, s,
+                           (const uint16_t*)logits, V, coin, out);
+    else
+        hipLaunchKernelGGL(sample_kernel<float>, dim3(1), dim3(1024), 0, s, (const float*)logits,
+                           V, coin, out);
+    return hipGetLastError();
+}
 
 hipError_t softmax_ce(hipStream_t s, void* logits, float* losses, const int32_t* targets,
                       int N, int V, int ldv, float dscale, int* flag, int bf16) {

@@ -78,6 +78,8 @@ def _load():
         "gpt2_forward": (_c.c_int, [_vp, _vp, _vp, _c.c_int, _c.c_int, P(_c.c_float)]),
         "gpt2_forward_device": (_c.c_int, [_vp, _vp, _vp, _c.c_int, _c.c_int,
                                            P(_c.c_float)]),
+        "gpt2_sample": (_c.c_int, [_vp, _c.c_int, _c.c_int, _c.c_float, P(_c.c_int32)]),
+        "gpt2_generate": (_c.c_int, [_vp, _vp, _c.c_int, _c.c_int, _vp]),
         "gpt2_zero_grad": (_c.c_int, [_vp]),
         "gpt2_backward": (_c.c_int, [_vp]),
         "gpt2_update": (_c.c_int, [_vp] + [_c.c_float] * 5 + [_c.c_int]),
@@ -202,6 +204,20 @@ def gpt2_forward_device(h, tokens_ptr, targets_ptr, B, T, want_loss=True):
     return loss.value
 
 
+def gpt2_sample(h, b, t, coin):
+    tok = _c.c_int32(-1)
+    _check(lib.gpt2_sample(h, b, t, coin, _c.byref(tok)))
+    return tok.value
+
+
+def gpt2_generate(h, tokens, prompt_len, n, coins):
+    """tokens: int32 array of length >= n (filled in place from prompt_len);
+    coins: float32 array of n - prompt_len uniforms in [0, 1)."""
+    assert coins is None or (coins.dtype == np.float32 and coins.flags["C_CONTIGUOUS"])
+    _check(lib.gpt2_generate(h, _i32p(tokens), prompt_len, n,
+                             None if coins is None else coins.ctypes.data_as(_vp)))
+
+
 def gpt2_zero_grad(h):
     _check(lib.gpt2_zero_grad(h))
 
@@ -319,6 +335,17 @@ class Model:
         return gpt2_forward_device(self.h, tokens.data_ptr(),
                                    None if targets is None else targets.data_ptr(), B, T,
                                    want_loss)
+
+    def sample(self, b, t, coin):
+        return gpt2_sample(self.h, b, t, coin)
+
+    def generate(self, prompt, n, coins):
+        """Tokens 0..n-1: the prompt, then n - len(prompt) draws."""
+        tok = np.zeros(n, dtype=np.int32)
+        tok[:len(prompt)] = prompt
+        c = np.ascontiguousarray(coins, dtype=np.float32)
+        gpt2_generate(self.h, tok, len(prompt), n, c)
+        return tok
 
     def zero_grad(self):
         gpt2_zero_grad(self.h)

@@ -24,6 +24,7 @@ _M2 = np.uint64(0x94D049BB133111EB)
 
 PARAM_SEED = 1337
 TOKEN_SEED = 42
+COIN_SEED = 7
 
 PARAM_NAMES = ["wte", "wpe", "ln1w", "ln1b", "qkvw", "qkvb", "attprojw",
                "attprojb", "ln2w", "ln2b", "fcw", "fcb", "fcprojw", "fcprojb",
@@ -125,6 +126,13 @@ def zipf_tokens(B, T, V, a=1.1, seed=TOKEN_SEED):
 
 # The five workloads.  `steps` is how many consecutive training steps the
 # workload runs on its one fixed batch.
+def coins(count: int, seed: int = COIN_SEED) -> np.ndarray:
+    """Uniform float32 draws in [0, 1) for sampling (float32 so that both
+    sides see the same values)."""
+    u = uniform01(seed, 0, count).astype(np.float32)
+    return np.minimum(u, np.float32(1.0) - np.finfo(np.float32).epsneg)
+
+
 CONFIGS = {
     "tiny": dict(L=2, C=64, NH=4, V=512, maxT=64, B=2, T=64, steps=1),
     "small": dict(L=4, C=256, NH=4, V=8192, maxT=256, B=4, T=256, steps=10),
