@@ -186,6 +186,32 @@ GPT2_API int gpt2_backward(gpt2_model* model);
 GPT2_API int gpt2_update(gpt2_model* model, float lr, float beta1, float beta2,
                 float eps, float weight_decay, int step);
 
+/* ---- token files ---------------------------------------------------------
+ * A token file is a raw stream of little-endian int32 GPT-2 token ids with no
+ * header (ujoy.net article "徒手用 1000 行 C 语言实现", section "训练过程":
+ * the .bin files the data preparation writes).  A loader cuts batches of B
+ * sequences of T tokens from it: from a window of B*T + 1 consecutive ids,
+ * tokens = ids [0, B*T) and targets = ids [1, B*T] (row-major (B, T) host
+ * arrays; each sequence's targets are its tokens shifted by one).  Successive
+ * batches advance by B*T ids; when fewer than B*T + 1 ids remain the
+ * position returns to the start of the file.  The loader reads one window
+ * per batch; it does not check ids against a vocabulary (gpt2_forward does).
+ * Host only: no GPU call. */
+typedef struct gpt2_loader gpt2_loader;
+
+/* Opens path for batches of B x T.  Errors: GPT2_EINVAL (NULL, B or T <= 0,
+ * unreadable file, size not a multiple of 4, fewer than B*T + 1 ids),
+ * GPT2_ENOMEM.  The loader owns the open file until gpt2_loader_close. */
+GPT2_API int gpt2_loader_open(const char* path, int B, int T, gpt2_loader** out);
+/* Ids in the file, and floor(ids / (B*T)) batches per pass (-1 if NULL). */
+GPT2_API int64_t gpt2_loader_num_tokens(const gpt2_loader* loader);
+GPT2_API int64_t gpt2_loader_num_batches(const gpt2_loader* loader);
+/* Writes the next batch into caller-owned host arrays of B*T int32 each. */
+GPT2_API int gpt2_loader_next(gpt2_loader* loader, int32_t* tokens, int32_t* targets);
+/* Back to the first batch. */
+GPT2_API int gpt2_loader_reset(gpt2_loader* loader);
+GPT2_API void gpt2_loader_close(gpt2_loader* loader);
+
 /* Waits for the model's stream; reports a pending device-side id error. */
 GPT2_API int gpt2_synchronize(gpt2_model* model);
 

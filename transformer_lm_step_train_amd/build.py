@@ -16,7 +16,7 @@ LIB = os.path.join(HERE, "libgpt2_hip.so")
 HIPCC = os.environ.get("HIPCC", "/opt/rocm/bin/hipcc")
 
 SOURCES = ["gemm.hip", "gemm_bf16.hip", "attention.hip", "attention_bf16.hip", "layernorm.hip", "softmax_ce.hip",
-           "elementwise.hip", "runtime.cpp"]
+           "elementwise.hip", "runtime.cpp", "loader.cpp"]
 
 FLAGS = [
     "-O3", "-std=c++17", "-fPIC", "--offload-arch=gfx950",

@@ -37,6 +37,17 @@ int fail(int code, const char* fmt, ...) {
     return code;
 }
 
+}  // namespace
+
+// Sets the thread's last-error message (for the host-only parts of the
+// library in other files).
+int gpt2_set_error(int code, const char* msg) {
+    g_err = msg;
+    return code;
+}
+
+namespace {
+
 const char* kParamNames[16] = {"wte",      "wpe",      "ln1w", "ln1b", "qkvw",    "qkvb",
                                "attprojw", "attprojb", "ln2w", "ln2b", "fcw",     "fcb",
                                "fcprojw",  "fcprojb",  "lnfw", "lnfb"};

@@ -80,6 +80,12 @@ def _load():
                                            P(_c.c_float)]),
         "gpt2_sample": (_c.c_int, [_vp, _c.c_int, _c.c_int, _c.c_float, P(_c.c_int32)]),
         "gpt2_generate": (_c.c_int, [_vp, _vp, _c.c_int, _c.c_int, _vp]),
+        "gpt2_loader_open": (_c.c_int, [_c.c_char_p, _c.c_int, _c.c_int, P(_vp)]),
+        "gpt2_loader_num_tokens": (_i64, [_vp]),
+        "gpt2_loader_num_batches": (_i64, [_vp]),
+        "gpt2_loader_next": (_c.c_int, [_vp, _vp, _vp]),
+        "gpt2_loader_reset": (_c.c_int, [_vp]),
+        "gpt2_loader_close": (None, [_vp]),
         "gpt2_zero_grad": (_c.c_int, [_vp]),
         "gpt2_backward": (_c.c_int, [_vp]),
         "gpt2_update": (_c.c_int, [_vp] + [_c.c_float] * 5 + [_c.c_int]),
@@ -216,6 +222,35 @@ def gpt2_generate(h, tokens, prompt_len, n, coins):
     assert coins is None or (coins.dtype == np.float32 and coins.flags["C_CONTIGUOUS"])
     _check(lib.gpt2_generate(h, _i32p(tokens), prompt_len, n,
                              None if coins is None else coins.ctypes.data_as(_vp)))
+
+
+class Loader:
+    """Batches of a raw int32 token file (gpt2_loader_*): next() returns
+    (tokens, targets) as (B, T) int32 arrays."""
+
+    def __init__(self, path, B, T):
+        h = _vp()
+        _check(lib.gpt2_loader_open(os.fsencode(path), B, T, _c.byref(h)))
+        self.h, self.B, self.T = h, B, T
+        self.num_tokens = int(lib.gpt2_loader_num_tokens(h))
+        self.num_batches = int(lib.gpt2_loader_num_batches(h))
+
+    def next(self):
+        tok = np.empty((self.B, self.T), dtype=np.int32)
+        tgt = np.empty((self.B, self.T), dtype=np.int32)
+        _check(lib.gpt2_loader_next(self.h, tok.ctypes.data_as(_vp), tgt.ctypes.data_as(_vp)))
+        return tok, tgt
+
+    def reset(self):
+        _check(lib.gpt2_loader_reset(self.h))
+
+    def close(self):
+        if getattr(self, "h", None):
+            lib.gpt2_loader_close(self.h)
+            self.h = None
+
+    def __del__(self):
+        self.close()
 
 
 def gpt2_zero_grad(h):
