@@ -58,11 +58,22 @@ typedef struct gpt2_model gpt2_model; /* opaque */
 
 /* Model shape plus the largest batch the arenas are sized for.  Limits:
  * channels % num_heads == 0 with head size 16, 32 or 64; channels <= 1024;
- * seq_len <= max_seq_len; batch_size*seq_len <= 32768; vocab_size <= 65536. */
+ * seq_len <= max_seq_len; batch_size*seq_len <= 32768; vocab_size <= 65536.
+ *
+ * rope = 1 replaces the learned position table by a rotary position
+ * embedding, the architectural extension the pages name (yinghuohong.cn,
+ * section "脚动完成每一个层前向/反向流传": more layers such as RoPE for newer
+ * architectures).  Reading (RoFormer, Su et al. 2021): the encoder output is
+ * wte[token] alone, and in every layer the q and k slices of each head are
+ * rotated after the QKV matmul: the channel pair (2i, 2i+1) of the row at
+ * position t turns by t * 10000^(-2i/hs).  The wpe tensor then has 0
+ * elements (the other 15 tensors keep their order). */
 typedef struct {
     int32_t max_seq_len, vocab_size, num_layers, num_heads, channels;
     int32_t batch_size, seq_len; /* arena sizing, fixed at create */
     int32_t precision;           /* GPT2_FP32 or GPT2_BF16_MIXED */
+    int32_t rope;                /* 0: learned position table wpe (GPT-2);
+                                    1: rotary position embedding instead */
 } gpt2_config;
 
 /* Optional device allocator.  alloc returns device memory of at least

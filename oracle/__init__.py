@@ -29,7 +29,8 @@ _vp = ctypes.c_void_p
 
 class OracleConfig(ctypes.Structure):
     _fields_ = [("max_seq_len", _int), ("vocab_size", _int),
-                ("num_layers", _int), ("num_heads", _int), ("channels", _int)]
+                ("num_layers", _int), ("num_heads", _int), ("channels", _int),
+                ("rope", _int)]
 
 
 _loaded = {}
@@ -87,6 +88,8 @@ def _lib(precision: str):
         "oracle_crossentropy_forward": [_vp, _vp, _vp, _int, _int],
         "oracle_crossentropy_softmax_backward": [_vp] * 4 + [_int, _int],
         "oracle_adamw": [_vp] * 4 + [_i64] + [real] * 5 + [_int],
+        "oracle_rope_forward": [_vp] + [_int] * 4,
+        "oracle_rope_backward": [_vp] + [_int] * 4,
     }
     for name, args in sig.items():
         getattr(lib, name).argtypes = args
@@ -107,13 +110,13 @@ def ptr(a: np.ndarray):
     return a.ctypes.data_as(_vp)
 
 
-def make_config(L, C, NH, V, maxT) -> OracleConfig:
+def make_config(L, C, NH, V, maxT, rope=0) -> OracleConfig:
     return OracleConfig(max_seq_len=maxT, vocab_size=V, num_layers=L,
-                        num_heads=NH, channels=C)
+                        num_heads=NH, channels=C, rope=int(rope))
 
 
-def param_sizes(L, C, NH, V, maxT):
-    cfg = make_config(L, C, NH, V, maxT)
+def param_sizes(L, C, NH, V, maxT, rope=0):
+    cfg = make_config(L, C, NH, V, maxT, rope)
     sizes = np.zeros(16, dtype=np.int64)
     total = _lib("f32").oracle_param_sizes(ctypes.byref(cfg), ptr(sizes))
     return dict(zip(PARAM_NAMES, sizes.tolist())), int(total)
@@ -129,19 +132,20 @@ def act_sizes(L, C, NH, V, maxT, B, T):
 class OracleModel:
     """One GPT-2 with its four parameter arenas and two activation arenas."""
 
-    def __init__(self, L, C, NH, V, maxT, B, T, precision="f32"):
+    def __init__(self, L, C, NH, V, maxT, B, T, precision="f32", rope=0):
         self.lib = _lib(precision)
         self.dtype = self.lib.dtype
         self.L, self.C, self.NH, self.V, self.maxT = L, C, NH, V, maxT
         self.B, self.T = B, T
-        self._cfg = make_config(L, C, NH, V, maxT)
+        self._cfg = make_config(L, C, NH, V, maxT, rope)
+        self.rope = int(rope)
         h = self.lib.oracle_create(ctypes.byref(self._cfg), B, T)
         if not h:
             raise MemoryError("oracle_create failed (bad config or no memory)")
         self.h = h
         self.num_params = int(self.lib.oracle_num_params(h))
         self.num_acts = int(self.lib.oracle_num_acts(h))
-        self.param_sizes, _ = param_sizes(L, C, NH, V, maxT)
+        self.param_sizes, _ = param_sizes(L, C, NH, V, maxT, rope)
         self.act_sizes, _ = act_sizes(L, C, NH, V, maxT, B, T)
 
         def view(fn, n):

@@ -60,15 +60,16 @@ EXPORT int oracle_real_size(void) { return (int)sizeof(real); }
 /* ------------------------------------------------------------------------ */
 
 /* Token + position embedding: out[b,t,:] = wte[tok[b,t],:] + wpe[t,:].
- * Every sequence in the batch starts at position 0. */
+ * Every sequence in the batch starts at position 0.  wpe may be NULL (the
+ * rotary model has no position table): then out = wte[tok]. */
 EXPORT void oracle_encoder_forward(real* out, const int* tok, const real* wte,
                                    const real* wpe, int B, int T, int C) {
     for (int b = 0; b < B; b++) {
         for (int t = 0; t < T; t++) {
             real* o = out + ((size_t)b * T + t) * C;
             const real* we = wte + (size_t)tok[b * T + t] * C;
-            const real* pe = wpe + (size_t)t * C;
-            for (int c = 0; c < C; c++) o[c] = we[c] + pe[c];
+            for (int c = 0; c < C; c++)
+                o[c] = wpe ? we[c] + wpe[(size_t)t * C + c] : we[c];
         }
     }
 }
@@ -81,10 +82,9 @@ EXPORT void oracle_encoder_backward(real* dwte, real* dwpe, const real* dout,
         for (int t = 0; t < T; t++) {
             const real* d = dout + ((size_t)b * T + t) * C;
             real* dwe = dwte + (size_t)tok[b * T + t] * C;
-            real* dpe = dwpe + (size_t)t * C;
             for (int c = 0; c < C; c++) {
                 dwe[c] += d[c];
-                dpe[c] += d[c];
+                if (dwpe) dwpe[(size_t)t * C + c] += d[c];
             }
         }
     }
@@ -405,12 +405,48 @@ EXPORT void oracle_adamw(real* p, const real* g, real* m, real* v, int64_t n,
     }
 }
 
+/* Rotary position embedding (RoFormer, Su et al. 2021), the architectural
+ * extension named by yinghuohong.cn (section "脚动完成每一个层前向/反向流传").
+ * In place on the q and k slices of each qkv row (B*T rows of 3C): in every
+ * head of size hs, the channel pair (2i, 2i+1) of the row at position t is
+ * rotated by the angle t * 10000^(-2i/hs):
+ *   x' = x cos a - y sin a,   y' = x sin a + y cos a.
+ * Angles and their cosines are taken in double. */
+static void rope_rotate(real* qkv, int B, int T, int C, int NH, double sign) {
+    const int hs = C / NH;
+    for (int b = 0; b < B; b++)
+        for (int t = 0; t < T; t++) {
+            real* row = qkv + ((size_t)b * T + t) * 3 * C;
+            for (int part = 0; part < 2; part++)      /* q, then k */
+                for (int h = 0; h < NH; h++)
+                    for (int i = 0; i < hs / 2; i++) {
+                        real* x = row + part * C + h * hs + 2 * i;
+                        const double a = t * pow(10000.0, -2.0 * i / hs);
+                        const double cs = cos(a), sn = sign * sin(a);
+                        const double x0 = x[0], x1 = x[1];
+                        x[0] = (real)(x0 * cs - x1 * sn);
+                        x[1] = (real)(x0 * sn + x1 * cs);
+                    }
+        }
+}
+
+EXPORT void oracle_rope_forward(real* qkv, int B, int T, int C, int NH) {
+    rope_rotate(qkv, B, T, C, NH, 1.0);
+}
+
+/* The rotation is orthogonal, so its backward is the inverse rotation of the
+ * q and k gradients (the v gradient passes through). */
+EXPORT void oracle_rope_backward(real* dqkv, int B, int T, int C, int NH) {
+    rope_rotate(dqkv, B, T, C, NH, -1.0);
+}
+
 /* ------------------------------------------------------------------------ */
 /* Model: arenas and the chained step                                        */
 /* ------------------------------------------------------------------------ */
 
 typedef struct {
     int max_seq_len, vocab_size, num_layers, num_heads, channels;
+    int rope; /* 1: rotary position embedding instead of the wpe table */
 } OracleConfig;
 
 enum { NPARAM = 16, NACT = 23 };
@@ -422,7 +458,7 @@ EXPORT int64_t oracle_param_sizes(const OracleConfig* cfg, int64_t* sizes) {
     int64_t maxT = cfg->max_seq_len;
     int64_t s[NPARAM] = {
         V * C,         /* wte      */
-        maxT * C,      /* wpe      */
+        cfg->rope ? 0 : maxT * C, /* wpe (none in the rotary model) */
         L * C,         /* ln1w     */
         L * C,         /* ln1b     */
         L * 3 * C * C, /* qkvw     */
@@ -593,7 +629,8 @@ EXPORT double oracle_forward(OracleModel* M, const int* tokens,
     M->have_targets = targets != NULL;
     if (targets) memcpy(M->targets, targets, sizeof(int) * BT);
 
-    oracle_encoder_forward(a[A_ENCODED], tokens, p[P_WTE], p[P_WPE], B, T, C);
+    oracle_encoder_forward(a[A_ENCODED], tokens, p[P_WTE], M->cfg.rope ? NULL : p[P_WPE],
+                           B, T, C);
     for (int l = 0; l < L; l++) {
         const real* resid = l == 0 ? a[A_ENCODED] : a[A_RESIDUAL3] + (l - 1) * BTC;
         real* ln1 = a[A_LN1] + l * BTC;
@@ -617,6 +654,7 @@ EXPORT double oracle_forward(OracleModel* M, const int* tokens,
                                  p[P_LN1W] + l * C, p[P_LN1B] + l * C, BT, C);
         oracle_matmul_forward(qkv, ln1, p[P_QKVW] + (int64_t)l * 3 * C * C,
                               p[P_QKVB] + l * 3 * C, BT, C, 3 * C);
+        if (M->cfg.rope) oracle_rope_forward(qkv, B, T, C, NH);
         oracle_attention_forward(atty, preatt, att, qkv, B, T, C, NH);
         oracle_matmul_forward(attproj, atty, p[P_ATTPROJW] + (int64_t)l * C * C,
                               p[P_ATTPROJB] + l * C, BT, C, C);
@@ -761,6 +799,7 @@ EXPORT int oracle_backward(OracleModel* M) {
                                p[P_ATTPROJW] + (int64_t)l * C * C, BT, C, C);
         oracle_attention_backward(dqkv, dpreatt, datt, datty, qkv, att, B, T, C,
                                   NH);
+        if (M->cfg.rope) oracle_rope_backward(dqkv, B, T, C, NH);
         oracle_matmul_backward(dln1, g[P_QKVW] + (int64_t)l * 3 * C * C,
                                g[P_QKVB] + l * 3 * C, dqkv, ln1,
                                p[P_QKVW] + (int64_t)l * 3 * C * C, BT, C, 3 * C);
@@ -768,7 +807,8 @@ EXPORT int oracle_backward(OracleModel* M) {
                                   dln1, resid, p[P_LN1W] + l * C, ln1_mean,
                                   ln1_rstd, BT, C);
     }
-    oracle_encoder_backward(g[P_WTE], g[P_WPE], da[A_ENCODED], M->tokens, B, T, C);
+    oracle_encoder_backward(g[P_WTE], M->cfg.rope ? NULL : g[P_WPE], da[A_ENCODED], M->tokens,
+                            B, T, C);
     return 0;
 }
 

@@ -34,6 +34,8 @@ def gpt2():
 def rel(a, r):
     a = np.asarray(a, dtype=np.float64)
     r = np.asarray(r, dtype=np.float64)
+    if r.size == 0:  # the rotary model's empty wpe
+        return 0.0
     return float(np.max(np.abs(a - r)) / max(np.max(np.abs(r)), 1e-30))
 
 
@@ -41,16 +43,17 @@ def pair(name):
     g = gpt2()
     c = synth.CONFIGS[name]
     print(f"[bf16] config={name}", flush=True)
-    params = synth.init_params(c["L"], c["C"], c["V"], c["maxT"])
+    rope = c.get("rope", False)
+    params = synth.init_params(c["L"], c["C"], c["V"], c["maxT"], rope=rope)
     m = g.Model(c["L"], c["C"], c["NH"], c["V"], c["maxT"], c["B"], c["T"],
-                precision=g.GPT2_BF16_MIXED)
+                precision=g.GPT2_BF16_MIXED, rope=rope)
     m.set_params(params)
-    o = OracleModel(c["L"], c["C"], c["NH"], c["V"], c["maxT"], c["B"], c["T"])
+    o = OracleModel(c["L"], c["C"], c["NH"], c["V"], c["maxT"], c["B"], c["T"], rope=rope)
     o.params[:] = params
     return m, o, c
 
 
-@pytest.mark.parametrize("name", ["tiny", "ragged", "gpt2_124m_b4t64"])
+@pytest.mark.parametrize("name", ["tiny", "ragged", "gpt2_124m_b4t64", "ragged_rope"])
 def test_bf16_step(name):
     m, o, c = pair(name)
     tok, tgt = synth.token_stream(c["B"], c["T"], c["V"])

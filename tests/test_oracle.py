@@ -31,10 +31,11 @@ def rel(a, r):
 
 def make_model(name, precision="f32", params=None):
     c = synth.CONFIGS[name]
+    rope = c.get("rope", False)
     m = OracleModel(c["L"], c["C"], c["NH"], c["V"], c["maxT"], c["B"], c["T"],
-                    precision=precision)
+                    precision=precision, rope=rope)
     if params is None:
-        params = synth.init_params(c["L"], c["C"], c["V"], c["maxT"])
+        params = synth.init_params(c["L"], c["C"], c["V"], c["maxT"], rope=rope)
     m.params[:] = params
     return m, c
 
@@ -315,9 +316,10 @@ def test_whole_step_vs_torch_autograd(name):
     m.close()
 
 
-def test_finite_differences_f64():
+@pytest.mark.parametrize("name", ["tiny", "tiny_rope"])
+def test_finite_differences_f64(name):
     """Central differences (L(th+h) - L(th-h)) / 2h on the float64 build."""
-    m, c = make_model("tiny", "f64")
+    m, c = make_model(name, "f64")
     tok, tgt = synth.token_stream(c["B"], c["T"], c["V"])
     m.forward(tok, tgt)
     m.zero_grad()
@@ -332,8 +334,10 @@ def test_finite_differences_f64():
         if n in ("lnfw", "lnfb"):
             idx += list(range(lo, hi))
         else:
-            if n == "wpe":  # only rows t < T are used
-                hi = lo + c["T"] * c["C"]
+            if n == "wpe":  # only rows t < T are used (none in the rotary model)
+                hi = lo + min(c["T"] * c["C"], hi - lo)
+                if hi <= lo:
+                    continue
             if n == "wte":  # bias the sample toward rows that occur as tokens
                 rows = np.unique(tok.reshape(-1))[:8]
                 idx += [lo + int(rr) * c["C"] + int(cc) for rr in rows
@@ -492,3 +496,73 @@ def test_page_generation_shape():
     g = json.load(open(os.path.join(GOLDEN, "gpt2_124m_printout.json")))
     assert g["generated_length"] == 64 and g["generated_first_token"] == 50256
     assert g["generated_first_token"] == g["config"]["vocab_size"] - 1
+
+
+# ------------------------------------------------------------------ rotary --
+
+def _rope(qkv, B, T, C, NH, inverse=False, precision="f64"):
+    lb = lib(precision)
+    x = np.ascontiguousarray(qkv, dtype=lb.dtype).copy()
+    fn = lb.oracle_rope_backward if inverse else lb.oracle_rope_forward
+    fn(ptr(x), B, T, C, NH)
+    return x
+
+
+def test_rope_scores_depend_only_on_relative_position():
+    """The defining property of the rotary embedding: with the same q and k
+    vector at every position, q'_t . k'_s depends only on t - s, per head."""
+    B, T, C, NH = 1, 40, 64, 4
+    hs = C // NH
+    r = np.random.default_rng(8)
+    row = r.standard_normal(3 * C)
+    qkv = np.tile(row, (B * T, 1))
+    out = _rope(qkv, B, T, C, NH).reshape(T, 3 * C)
+    for h in range(NH):
+        q = out[:, h * hs:(h + 1) * hs]
+        k = out[:, C + h * hs:C + (h + 1) * hs]
+        S = q @ k.T
+        for d in range(-T + 1, T):
+            diag = np.diagonal(S, offset=d)
+            assert np.max(np.abs(diag - diag[0])) < 1e-9 * max(1.0, np.abs(diag).max()), (h, d)
+    # position 0 is the identity, v is untouched, pair norms are kept
+    assert np.allclose(out[0], row, atol=1e-15)
+    assert np.array_equal(out[:, 2 * C:], qkv[:, 2 * C:])
+    pairs_in = qkv[:, :2 * C].reshape(T, -1, 2)
+    pairs_out = out[:, :2 * C].reshape(T, -1, 2)
+    assert np.allclose(np.hypot(*pairs_in.transpose(2, 0, 1)),
+                       np.hypot(*pairs_out.transpose(2, 0, 1)), rtol=1e-13)
+
+
+def test_rope_two_dim_head_turns_by_t_radians():
+    """hs = 2: one pair per head with frequency 10000^0 = 1, so position t
+    turns it by t radians (a closed form)."""
+    B, T, C, NH = 2, 9, 4, 2
+    r = np.random.default_rng(9)
+    qkv = r.standard_normal((B * T, 3 * C))
+    out = _rope(qkv, B, T, C, NH)
+    for row in range(B * T):
+        t = row % T
+        for j in range(0, 2 * C, 2):
+            x, y = qkv[row, j], qkv[row, j + 1]
+            assert abs(out[row, j] - (x * math.cos(t) - y * math.sin(t))) < 1e-12
+            assert abs(out[row, j + 1] - (x * math.sin(t) + y * math.cos(t))) < 1e-12
+
+
+def test_rope_backward_is_the_adjoint():
+    """<R u, w> = <u, R^T w>: the backward (inverse rotation) is the adjoint
+    of the forward, so it is the gradient map; and R^T R = I."""
+    B, T, C, NH = 2, 13, 96, 3
+    r = np.random.default_rng(10)
+    u = r.standard_normal((B * T, 3 * C))
+    w = r.standard_normal((B * T, 3 * C))
+    lhs = np.sum(_rope(u, B, T, C, NH) * w)
+    rhs = np.sum(u * _rope(w, B, T, C, NH, inverse=True))
+    assert abs(lhs - rhs) < 1e-10 * abs(lhs)
+    assert np.allclose(_rope(_rope(u, B, T, C, NH), B, T, C, NH, inverse=True), u, atol=1e-13)
+
+
+def test_rope_param_count():
+    """The rotary model drops only the wpe table."""
+    _, full = oracle.param_sizes(12, 768, 12, 50257, 1024)
+    sizes, rope = oracle.param_sizes(12, 768, 12, 50257, 1024, rope=1)
+    assert sizes["wpe"] == 0 and full - rope == 1024 * 768

@@ -37,7 +37,7 @@ __global__ __launch_bounds__(256) void encoder_fwd_kernel(E* __restrict__ out,
         float4 r = make_float4(0.f, 0.f, 0.f, 0.f);
         if (id >= 0 && id < V) {
             const float4 a = ld4(wte + (int64_t)id * C + c);
-            const float4 p = ld4(wpe + (int64_t)t * C + c);
+            const float4 p = wpe ? ld4(wpe + (int64_t)t * C + c) : make_float4(0.f, 0.f, 0.f, 0.f);
             r = make_float4(a.x + p.x, a.y + p.y, a.z + p.z, a.w + p.w);
         } else if (c == 0) {
             atomicOr(flag, 1);
@@ -289,6 +289,35 @@ inline unsigned grid_for(int64_t work, int per_block, unsigned cap) {
     return (unsigned)(g > cap ? cap : g);
 }
 
+// Rotary position embedding of the q and k slices of each qkv row, in place
+// (RoFormer: Su et al. 2021).  Within every head, the pair of channels
+// (2i, 2i+1) of a row at position t is rotated by the angle t * theta_i,
+// theta_i = 10000^(-2i/hs); dir = -1 applies the inverse rotation, which is
+// the backward of the forward rotation (an orthogonal map).  cs holds
+// (cos, sin) of t * theta_i for t < T, i < hs/2, computed on the host in
+// double.  One thread per pair.
+template <class E>
+__global__ __launch_bounds__(256) void rope_kernel(E* __restrict__ qkv, const float2* __restrict__ cs,
+                                                   int M, int T, int C, int hs, int64_t ld,
+                                                   float dir) {
+    const int half = hs >> 1;
+    const int64_t n = (int64_t)M * C;  // pairs per row: C/2 of q and C/2 of k
+    for (int64_t i = blockIdx.x * (int64_t)blockDim.x + threadIdx.x; i < n;
+         i += (int64_t)gridDim.x * blockDim.x) {
+        const int64_t row = i / C;
+        const int k = (int)(i - row * C);           // pair index within q|k
+        const int col = 2 * k;                       // 0 .. 2C-1 over [q | k]
+        const int t = (int)(row % T);
+        const int pi = (col % hs) >> 1;              // pair index within the head
+        const float2 r = cs[(int64_t)t * half + pi];
+        E* p = qkv + row * ld + col;
+        const float x = Act<E>::ld1(p), y = Act<E>::ld1(p + 1);
+        const float sn = dir * r.y;
+        Act<E>::st1(p, x * r.x - y * sn);
+        Act<E>::st1(p + 1, x * sn + y * r.x);
+    }
+}
+
 }  // namespace
 
 hipError_t encoder_forward(hipStream_t s, void* out, const int32_t* tok, const float* wte,
@@ -331,7 +360,7 @@ hipError_t encoder_backward_t(hipStream_t s, float* dwte, float* dwpe, const E* 
         default: return hipErrorInvalidValue;
     }
     hipError_t e = hipGetLastError();
-    if (e != hipSuccess) return e;
+    if (e != hipSuccess || !dwpe) return e;  // no position table (rotary model)
     const int64_t nw = (int64_t)T_ * (C / 4);
     hipLaunchKernelGGL(encoder_bwd_wpe_kernel<E>, dim3(grid_for(nw, 256, 1u << 30)), dim3(256),
                        0, s, dwpe, dx, B, T_, C);
@@ -346,6 +375,21 @@ hipError_t encoder_backward(hipStream_t s, float* dwte, float* dwpe, const void*
         return encoder_backward_t<uint16_t>(s, dwte, dwpe, (const uint16_t*)dx, keys, B, T, C, V,
                                             pos_bits);
     return encoder_backward_t<float>(s, dwte, dwpe, (const float*)dx, keys, B, T, C, V, pos_bits);
+}
+
+hipError_t rope_apply(hipStream_t s, void* qkv, const float* cs, int B, int T, int C, int NH,
+                      int dir, int bf16) {
+    const int64_t n = (int64_t)B * T * C;
+    if (n <= 0) return hipSuccess;
+    const dim3 grid(grid_for(n, 256, 65535));
+    const int hs = C / NH;
+    if (bf16)
+        hipLaunchKernelGGL(rope_kernel<uint16_t>, grid, dim3(256), 0, s, (uint16_t*)qkv,
+                           (const float2*)cs, B * T, T, C, hs, (int64_t)3 * C, (float)dir);
+    else
+        hipLaunchKernelGGL(rope_kernel<float>, grid, dim3(256), 0, s, (float*)qkv,
+                           (const float2*)cs, B * T, T, C, hs, (int64_t)3 * C, (float)dir);
+    return hipGetLastError();
 }
 
 size_t bias_partials_floats(int M, int N) {

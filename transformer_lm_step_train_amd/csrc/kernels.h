@@ -84,6 +84,13 @@ hipError_t attention_backward_bf16(hipStream_t s, uint16_t* dqkv, float* D,
                                    const uint16_t* out, const float* lse, int B, int T, int C,
                                    int NH);
 
+// ---- rotary position embedding ---------------------------------------------
+// Rotates the q and k slices of qkv (B*T rows of 3C, fp32 or bf16 bits) in
+// place, dir = +1 (forward) or -1 (inverse, the backward).  cs: (T_table,
+// hs/2) float pairs (cos, sin) of t * 10000^(-2i/hs), T <= T_table.
+hipError_t rope_apply(hipStream_t s, void* qkv, const float* cs, int B, int T, int C, int NH,
+                      int dir, int bf16);
+
 // ---- layernorm ------------------------------------------------------------
 // Activations (out, inp, dres, dout) are fp32, or bf16 bits when bf16 != 0;
 // mean, rstd, weights and their gradients are always fp32.

@@ -56,7 +56,8 @@ enum { P_WTE, P_WPE, P_LN1W, P_LN1B, P_QKVW, P_QKVB, P_ATTPROJW, P_ATTPROJB,
 
 void param_sizes(const gpt2_config* c, int64_t* s) {
     const int64_t L = c->num_layers, C = c->channels, V = c->vocab_size, T = c->max_seq_len;
-    const int64_t v[16] = {V * C, T * C, L * C, L * C, L * 3 * C * C, L * 3 * C, L * C * C,
+    const int64_t P = c->rope ? 0 : T * C;  // the rotary model has no position table
+    const int64_t v[16] = {V * C, P, L * C, L * C, L * 3 * C * C, L * 3 * C, L * C * C,
                            L * C, L * C, L * C, L * 4 * C * C, L * 4 * C, L * C * 4 * C,
                            L * C, C, C};
     for (int i = 0; i < 16; i++) s[i] = v[i];
@@ -87,6 +88,7 @@ int check_config(const gpt2_config* c) {
     if (c->vocab_size > 65536) return fail(GPT2_EINVAL, "vocab_size > 65536 not supported");
     if (c->precision != GPT2_FP32 && c->precision != GPT2_BF16_MIXED)
         return fail(GPT2_EINVAL, "unknown precision %d", c->precision);
+    if (c->rope != 0 && c->rope != 1) return fail(GPT2_EINVAL, "rope must be 0 or 1");
     return GPT2_OK;
 }
 
@@ -96,17 +98,19 @@ inline size_t align256(size_t x) { return (x + 255) & ~size_t(255); }
 struct Layout {
     int L, C, NH, V, Vp, maxT, Bmax, Tmax, M, pos_bits, n_pow2;
     int bf16;   // activations (and the matmul weight copy) in bf16
+    int rope;   // rotary position embedding instead of the wpe table
     size_t es;  // bytes per activation element
     int64_t nparams, poff[16], psize[16];
     size_t params, grads, m, v, shadow;
     size_t encoded, ln1, ln1_mean, ln1_rstd, qkv, atty, lse, res2, ln2, ln2_mean, ln2_rstd, fch,
         fch_gelu, res3, lnf, lnf_mean, lnf_rstd, logits, losses;
     size_t dres, dtmp, dqkv, dfch, attn_d, ln_part, bias_part, gemm_ws, keys, tokens, targets,
-        scalars;
+        scalars, rope_cs;
     size_t gemm_ws_bytes, total;
 
     void build(const gpt2_config* c) {
         bf16 = c->precision == GPT2_BF16_MIXED;
+        rope = c->rope;
         es = bf16 ? 2 : 4;
         L = c->num_layers;
         C = c->channels;
@@ -185,6 +189,7 @@ struct Layout {
         tokens = take((size_t)M * sizeof(int32_t));
         targets = take((size_t)M * sizeof(int32_t));
         scalars = take(256);
+        rope_cs = rope ? take((size_t)Tmax * (C / NH / 2) * 2 * f) : 0;
         total = off;
     }
 };
@@ -393,7 +398,8 @@ int forward_impl(gpt2_model* md, const int32_t* tok, const int32_t* tgt, int B, 
 
     LAUNCH(md, GPT2_KC_OTHER, 0, 4.0, gk::fill_zero(s, (float*)md->flag(), 1));
     LAUNCH(md, GPT2_KC_OTHER, 0, 8.0 * M * C + es * M * C + 4.0 * M,
-           gk::encoder_forward(s, enc, tok, md->P(P_WTE), md->P(P_WPE), B, T, C, V, md->flag(), h));
+           gk::encoder_forward(s, enc, tok, md->P(P_WTE), y.rope ? nullptr : md->P(P_WPE), B, T, C,
+                               V, md->flag(), h));
     for (int l = 0; l < L; l++) {
         const void* resid = l == 0 ? enc : (const void*)md->A(y.res3, (l - 1) * MC);
         void* ln1 = md->A(y.ln1, l * MC);
@@ -417,6 +423,9 @@ int forward_impl(gpt2_model* md, const int32_t* tok, const int32_t* tgt, int B, 
                   (const char*)md->W(P_QKVW) + (size_t)l * 3 * C * C * y.es, C, qkv, 3 * C);
         a.bias = md->P(P_QKVB) + l * 3 * C;
         TRY(run_gemm(md, a));
+        if (y.rope)
+            LAUNCH(md, GPT2_KC_OTHER, 0, es * 4.0 * M * C,
+                   gk::rope_apply(s, qkv, md->at<float>(y.rope_cs), B, T, C, NH, 1, h));
         {
             const double hs = C / NH;
             const double flops = 4.0 * B * NH * hs * (double)T * (T + 1) / 2.0;
@@ -569,6 +578,9 @@ int backward_impl(gpt2_model* md) {
                    gk::attention_backward(s, dqkv, md->at<float>(y.attn_d), dtmp, qkv, atty, lse,
                                           B, T, C, NH, h));
         }
+        if (y.rope)  // back through the rotation: dq, dk of the unrotated q, k
+            LAUNCH(md, GPT2_KC_OTHER, 0, es * 4.0 * M * C,
+                   gk::rope_apply(s, dqkv, md->at<float>(y.rope_cs), B, T, C, NH, -1, h));
         // QKV: dln1 = dqkv W;  dW += dqkv^T ln1
         TRY(run_gemm(md, mm(gk::GEMM_NN, gk::EPI_STORE, M, C, 3 * C, dqkv, 3 * C,
                             Wl(P_QKVW, (size_t)l * 3 * C * C), C, dtmp, C)));
@@ -582,7 +594,8 @@ int backward_impl(gpt2_model* md) {
                                       h));
     }
     LAUNCH(md, GPT2_KC_OTHER, 0, es * M * C + 8.0 * M * C + 8.0 * T * C + 4.0 * M,
-           gk::encoder_backward(s, md->G(P_WTE), md->G(P_WPE), dres, md->at<uint32_t>(y.keys), B,
+           gk::encoder_backward(s, md->G(P_WTE), y.rope ? nullptr : md->G(P_WPE), dres,
+                                md->at<uint32_t>(y.keys), B,
                                 T, C, V, y.pos_bits, h));
     return GPT2_OK;
 }
@@ -682,6 +695,20 @@ int gpt2_create(const gpt2_config* cfg, const gpt2_allocator* alloc, void* hip_s
     if (rc == GPT2_OK) {
         const hipError_t e = gk::encoder_sort_prepare(md->lay.n_pow2);
         rc = hip_check(e, "encoder sort setup");
+    }
+    if (rc == GPT2_OK && md->lay.rope) {
+        // (cos, sin) of t * 10000^(-2i/hs), computed in double
+        const int half = md->lay.C / md->lay.NH / 2;
+        std::vector<float> cs((size_t)md->lay.Tmax * half * 2);
+        for (int t = 0; t < md->lay.Tmax; t++)
+            for (int i = 0; i < half; i++) {
+                const double a = t * std::pow(10000.0, -2.0 * i / (2.0 * half));
+                cs[((size_t)t * half + i) * 2] = (float)std::cos(a);
+                cs[((size_t)t * half + i) * 2 + 1] = (float)std::sin(a);
+            }
+        rc = hip_check(hipMemcpy(md->at<char>(md->lay.rope_cs), cs.data(), cs.size() * sizeof(float),
+                                 hipMemcpyHostToDevice),
+                       "rotary table upload");
     }
     if (rc == GPT2_OK) {
         // parameters, gradients and both moments start at zero

@@ -71,10 +71,11 @@ def randint(seed: int, start: int, count: int, n: int) -> np.ndarray:
     return ((z * np.uint64(n)) >> np.uint64(32)).astype(np.int32)
 
 
-def param_sizes(L, C, V, maxT):
-    """Element count of each of the 16 parameter tensors, arena order."""
+def param_sizes(L, C, V, maxT, rope=False):
+    """Element count of each of the 16 parameter tensors, arena order (the
+    rotary model has no position table: wpe has 0 elements)."""
     return {
-        "wte": V * C, "wpe": maxT * C, "ln1w": L * C, "ln1b": L * C,
+        "wte": V * C, "wpe": 0 if rope else maxT * C, "ln1w": L * C, "ln1b": L * C,
         "qkvw": L * 3 * C * C, "qkvb": L * 3 * C, "attprojw": L * C * C,
         "attprojb": L * C, "ln2w": L * C, "ln2b": L * C, "fcw": L * 4 * C * C,
         "fcb": L * 4 * C, "fcprojw": L * C * 4 * C, "fcprojb": L * C,
@@ -83,10 +84,10 @@ def param_sizes(L, C, V, maxT):
 
 
 def init_params(L, C, V, maxT, seed=PARAM_SEED, dtype=np.float32,
-                chunk=1 << 23) -> np.ndarray:
+                chunk=1 << 23, rope=False) -> np.ndarray:
     """The flat parameter arena, GPT-2 initialisation.  Element j of a
     normally-initialised tensor is normal number (arena offset of j)."""
-    sizes = param_sizes(L, C, V, maxT)
+    sizes = param_sizes(L, C, V, maxT, rope)
     total = sum(sizes.values())
     out = np.empty(total, dtype=dtype)
     resid_std = 0.02 / math.sqrt(2 * L)
@@ -142,6 +143,9 @@ CONFIGS = {
                                T=1024, steps=1),
     # ragged: odd vocab, odd T, non-power-of-two width; exercises every tail
     "ragged": dict(L=2, C=96, NH=3, V=1001, maxT=80, B=3, T=77, steps=1),
+    # rotary position embedding instead of the wpe table
+    "tiny_rope": dict(L=2, C=64, NH=4, V=512, maxT=64, B=2, T=64, steps=1, rope=True),
+    "ragged_rope": dict(L=2, C=96, NH=3, V=1001, maxT=80, B=3, T=77, steps=1, rope=True),
 }
 
 ADAMW = dict(lr=1e-4, beta1=0.9, beta2=0.999, eps=1e-8, weight_decay=0.0)
