@@ -35,19 +35,20 @@ def parse():
     ap.add_argument("--steps", type=int, default=20)
     ap.add_argument("--warmup", type=int, default=5)
     ap.add_argument("--no-cpu-baseline", action="store_true")
-    ap.add_argument("--precision", choices=["fp32", "bf16"], default="fp32",
-                    help="fp32 (the headline workload) or the bf16 mixed-precision model")
+    ap.add_argument("--precision", choices=["fp32", "bf16", "fp16"], default="fp32",
+                    help="fp32 (the headline workload), or the bf16 / fp16 mixed-precision "
+                         "model")
     ap.add_argument("--no-kernel-timing", action="store_true",
                     help="do not record per-launch HIP events in the timed steps")
     return ap.parse_args()
 
 
-def measured_traffic(bf16):
+def measured_traffic(half):
     """HBM bytes per matmul launch from the committed rocprofv3 FETCH_SIZE /
     WRITE_SIZE summary, or None if the matmul source has changed since the
-    counters were taken (or for the bf16 model, which they do not cover)."""
+    counters were taken (or for the 16-bit models, which they do not cover)."""
     path = os.path.join(ROOT, "profiles", "gemm_fp32_traffic.json")
-    if bf16 or not os.path.exists(path):
+    if half or not os.path.exists(path):
         return None
     rec = json.load(open(path))
     src = os.path.join(ROOT, "transformer_lm_step_train_amd", "csrc", "gemm.hip")
@@ -91,9 +92,10 @@ def main():
     B, T = c["B"], c["T"]
     params = synth.init_params(c["L"], c["C"], c["V"], c["maxT"])
     tok, tgt = synth.token_stream(B, T, c["V"])
-    bf16 = args.precision == "bf16"
-    m = gpt2.Model(c["L"], c["C"], c["NH"], c["V"], c["maxT"], B, T,
-                   precision=gpt2.GPT2_BF16_MIXED if bf16 else gpt2.GPT2_FP32)
+    half = args.precision in ("bf16", "fp16")
+    prec = {"fp32": gpt2.GPT2_FP32, "bf16": gpt2.GPT2_BF16_MIXED,
+            "fp16": gpt2.GPT2_F16_MIXED}[args.precision]
+    m = gpt2.Model(c["L"], c["C"], c["NH"], c["V"], c["maxT"], B, T, precision=prec)
     m.set_params(params)
     dtok = torch.tensor(tok, dtype=torch.int32, device="cuda")
     dtgt = torch.tensor(tgt, dtype=torch.int32, device="cuda")
@@ -142,7 +144,7 @@ def main():
 
     roofline = None
     step_roof = None
-    peak = MFMA_BF16_PEAK_TFLOPS if bf16 else MFMA_FP32_PEAK_TFLOPS
+    peak = MFMA_BF16_PEAK_TFLOPS if half else MFMA_FP32_PEAK_TFLOPS
     if kc:
         # Composite bound of the whole step: every kernel class at the larger
         # of its MFMA time and its HBM time for the algorithmic work.
@@ -156,11 +158,11 @@ def main():
         achieved = (g["flops"] / n) / avg_s / 1e12 if avg_s > 0 else 0.0
         roofline = {"bound": "mfma", "achieved": round(achieved, 2),
                     "peak": peak, "unit": "TFLOP/s",
-                    "frac": round(achieved / peak, 4), "traffic": measured_traffic(bf16),
+                    "frac": round(achieved / peak, 4), "traffic": measured_traffic(half),
                     "traffic_unit": "HBM bytes per launch (rocprofv3 FETCH_SIZE+WRITE_SIZE)",
                     "algorithmic_bytes_per_launch": round(g["bytes"] / n),
                     "kernel": "gemm (all %s MFMA matmul launches of the step)"
-                              % ("bf16" if bf16 else "fp32"),
+                              % {"fp32": "fp32", "bf16": "bf16", "fp16": "fp16"}[args.precision],
                     "launches_per_step": n // args.steps,
                     "avg_launch_ms": round(g["ms"] / n, 4)}
         print("per-class kernel time per step:", file=sys.stderr)
@@ -176,7 +178,7 @@ def main():
 
     out = {
         "metric": "training tokens/sec (fwd+bwd+AdamW), GPT-2 124M B16 T1024 at 1 GPU"
-                  + ("" if not bf16 else " (bf16 mixed precision)"),
+                  + ("" if not half else f" ({args.precision} mixed precision)"),
         "value": round(tokens_per_s, 1),
         "unit": "tokens/s",
         "n_gpus": 1,
@@ -187,10 +189,10 @@ def main():
         "higher_is_better": True,
         "scaling": "weak",
         "vs_baseline": None,
-        "dtype": "bf16" if bf16 else "f32",
+        "dtype": {"fp32": "f32", "bf16": "bf16", "fp16": "f16"}[args.precision],
         "data": "synthetic (seeded uniform int32 token ids, GPT-2 init N(0,0.02))",
         "config": {"workload": "GPT-2 124M training step, B=16 T=1024 "
-                               + ("bf16 mixed precision" if bf16 else "fp32"),
+                               + (f"{args.precision} mixed precision" if half else "fp32"),
                    "global_batch": B, "seq_len": T, "layers": c["L"], "channels": c["C"],
                    "heads": c["NH"], "vocab": c["V"], "parallelism": "single GPU"},
         "roofline": roofline,
@@ -199,7 +201,7 @@ def main():
         "kernel_ms_per_step": {k: round(v["ms"] / args.steps, 3) for k, v in kc.items()},
         "loss_first_last": [round(losses[0], 5), round(losses[-1], 5)],
     }
-    if not args.no_cpu_baseline and not bf16:
+    if not args.no_cpu_baseline and not half:
         out["cpu_baseline"] = cpu_baseline(c, params, tok, tgt)
     print(json.dumps(out), flush=True)
 

@@ -53,6 +53,8 @@ extern "C" {
 #define GPT2_BF16_MIXED 1 /* bf16 activations and matmul inputs (fp32
                              accumulate); fp32 master weights, gradients,
                              Adam state, loss and softmax statistics      */
+#define GPT2_F16_MIXED 2  /* as GPT2_BF16_MIXED with IEEE fp16 instead of
+                             bf16, and dynamic loss scaling (below)       */
 
 typedef struct gpt2_model gpt2_model; /* opaque */
 
@@ -71,7 +73,7 @@ typedef struct gpt2_model gpt2_model; /* opaque */
 typedef struct {
     int32_t max_seq_len, vocab_size, num_layers, num_heads, channels;
     int32_t batch_size, seq_len; /* arena sizing, fixed at create */
-    int32_t precision;           /* GPT2_FP32 or GPT2_BF16_MIXED */
+    int32_t precision;           /* GPT2_FP32, GPT2_BF16_MIXED, GPT2_F16_MIXED */
     int32_t rope;                /* 0: learned position table wpe (GPT-2);
                                     1: rotary position embedding instead */
 } gpt2_config;
@@ -196,6 +198,28 @@ GPT2_API int gpt2_backward(gpt2_model* model);
  *   p -= lr (m/(1-b1^step) / (sqrt(v/(1-b2^step)) + eps) + weight_decay p). */
 GPT2_API int gpt2_update(gpt2_model* model, float lr, float beta1, float beta2,
                 float eps, float weight_decay, int step);
+
+/* ---- loss scaling (GPT2_F16_MIXED only) ----------------------------------
+ * The pages name lower precision such as fp16 as an extension (yinghuohong.cn,
+ * section "脚动完成每一个层前向/反向流传").  fp16's range is narrow, so the
+ * fp16 model trains with dynamic loss scaling (Micikevicius et al. 2018, the
+ * reading taken here): the loss gradient is multiplied by a scale S, so every
+ * activation gradient and the accumulated parameter gradients hold S times
+ * their value; gpt2_update first checks the gradients, skips the whole update
+ * if any is inf or NaN and then halves S (not below 1), and otherwise divides
+ * them by S, updates, and doubles S after growth_interval clean updates in a
+ * row.  S starts at 2^16 with growth_interval 2000.  gpt2_copy_grads returns
+ * gradients divided by the current S; the "logits" activation after a
+ * forward with targets holds S times the logits gradient.  The update-step
+ * number passed to gpt2_update is the caller's: a skipped update still
+ * consumed its number unless the caller re-uses it. */
+
+/* Sets S (finite, >= 1) and growth_interval (>= 1) and clears the count of
+ * clean updates.  GPT2_EINVAL for other models or bad values. */
+GPT2_API int gpt2_set_loss_scale(gpt2_model* model, float scale, int growth_interval);
+/* Reads S and whether the last gpt2_update was skipped (waits for the
+ * stream).  Either pointer may be NULL.  GPT2_EINVAL for other models. */
+GPT2_API int gpt2_get_loss_scale(gpt2_model* model, float* scale, int* last_update_skipped);
 
 /* ---- token files ---------------------------------------------------------
  * A token file is a raw stream of little-endian int32 GPT-2 token ids with no

@@ -66,6 +66,8 @@ def _lib(precision: str):
     lib.oracle_backward.restype = _int
     lib.oracle_backward.argtypes = [_vp]
     lib.oracle_update.argtypes = [_vp] + [ctypes.c_double] * 5 + [_int]
+    lib.oracle_loss_scale_step.restype = _int
+    lib.oracle_loss_scale_step.argtypes = [_vp, _vp, _int, _int, ctypes.c_double]
     lib.oracle_sample.restype = _int
     lib.oracle_sample.argtypes = [_vp, _int, ctypes.c_double]
     lib.oracle_generate.restype = _int
@@ -228,3 +230,16 @@ def sample(probs, coin, precision="f32"):
     lb = _lib(precision)
     p = np.ascontiguousarray(probs, dtype=lb.dtype)
     return int(lb.oracle_sample(ptr(p), p.size, float(coin)))
+
+
+def loss_scale_schedule(scale, found_inf_seq, interval, min_scale=1.0):
+    """Runs oracle_loss_scale_step over a sequence of overflow flags; returns
+    [(applied, scale after the step)] per step."""
+    lb = _lib("f32")
+    sc = np.array([scale], dtype=np.float64)
+    good = np.zeros(1, dtype=np.int32)
+    out = []
+    for f in found_inf_seq:
+        a = lb.oracle_loss_scale_step(ptr(sc), ptr(good), int(bool(f)), interval, min_scale)
+        out.append((bool(a), float(sc[0])))
+    return out

@@ -686,6 +686,28 @@ EXPORT double oracle_forward(OracleModel* M, const int* tokens,
     return M->mean_loss;
 }
 
+/* Dynamic loss scaling for the fp16 model, one update: the reading taken
+ * for the pages' "fp16" extension (yinghuohong.cn, section
+ * "脚动完成每一个层前向/反向流传") is the schedule of Micikevicius et al.
+ * (2018).  A step whose scaled gradients hold an inf or NaN is not applied
+ * and halves the scale (not below min_scale) and restarts the count of
+ * clean steps; a clean step is applied, and the interval-th clean step in a
+ * row doubles the scale.  Returns 1 if the update is applied. */
+EXPORT int oracle_loss_scale_step(double* scale, int* good, int found_inf, int interval,
+                                  double min_scale) {
+    if (found_inf) {
+        *scale = *scale / 2 < min_scale ? min_scale : *scale / 2;
+        *good = 0;
+        return 0;
+    }
+    *good += 1;
+    if (*good >= interval) {
+        *scale *= 2;
+        *good = 0;
+    }
+    return 1;
+}
+
 /* One draw from a probability row by the inverse CDF: the smallest v with
  * coin * sum_u probs[u] < sum_{u <= v} probs[u] (sums in double, in index
  * order), or V - 1 if rounding leaves none.  The pages show the trainer

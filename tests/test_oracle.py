@@ -566,3 +566,27 @@ def test_rope_param_count():
     _, full = oracle.param_sizes(12, 768, 12, 50257, 1024)
     sizes, rope = oracle.param_sizes(12, 768, 12, 50257, 1024, rope=1)
     assert sizes["wpe"] == 0 and full - rope == 1024 * 768
+
+
+# ------------------------------------------------------------ loss scaling --
+
+def test_loss_scale_schedule_worked_example():
+    """Hand-worked: start 2^16, interval 3.  Steps: clean, clean, clean
+    (third clean step doubles), overflow (halves, skipped), clean, overflow,
+    overflow, clean x3 (doubles)."""
+    seq = [0, 0, 0, 1, 0, 1, 1, 0, 0, 0]
+    got = oracle.loss_scale_schedule(65536.0, seq, 3)
+    want = [(True, 65536.0), (True, 65536.0), (True, 131072.0), (False, 65536.0),
+            (True, 65536.0), (False, 32768.0), (False, 16384.0), (True, 16384.0),
+            (True, 16384.0), (True, 32768.0)]
+    assert got == want
+
+
+def test_loss_scale_floor_and_long_run():
+    """The scale never drops below the floor; k overflows from S give
+    max(S / 2^k, floor); n * interval clean steps multiply by 2^n."""
+    got = oracle.loss_scale_schedule(8.0, [1] * 6, 5, min_scale=1.0)
+    assert [s for _, s in got] == [4.0, 2.0, 1.0, 1.0, 1.0, 1.0]
+    assert not any(a for a, _ in got)
+    got = oracle.loss_scale_schedule(2.0 ** 10, [0] * 40, 8)
+    assert got[-1] == (True, 2.0 ** 15) and all(a for a, _ in got)

@@ -577,21 +577,22 @@ hipError_t backward_t(hipStream_t s, E* dqkv, float* D, const E* dout, const E* 
 }  // namespace
 
 hipError_t attention_forward(hipStream_t s, void* out, float* lse, const void* qkv, int B, int T,
-                             int C, int NH, int bf16) {
+                             int C, int NH, int dt) {
     if (B <= 0 || T <= 0) return hipSuccess;
-    if (bf16)
-        return attention_forward_bf16(s, (uint16_t*)out, lse, (const uint16_t*)qkv, B, T, C, NH);
+    if (dt != DT_F32)
+        return attention_forward_half(s, (uint16_t*)out, lse, (const uint16_t*)qkv, B, T, C, NH,
+                                      dt);
     return forward_t<float>(s, (float*)out, lse, (const float*)qkv, B, T, C, NH);
 }
 
 hipError_t attention_backward(hipStream_t s, void* dqkv, float* dpre, const void* dout,
                               const void* qkv, const void* out, const float* lse, int B, int T,
-                              int C, int NH, int bf16) {
+                              int C, int NH, int dt) {
     if (B <= 0 || T <= 0) return hipSuccess;
-    if (bf16)
-        return attention_backward_bf16(s, (uint16_t*)dqkv, dpre, (const uint16_t*)dout,
+    if (dt != DT_F32)
+        return attention_backward_half(s, (uint16_t*)dqkv, dpre, (const uint16_t*)dout,
                                        (const uint16_t*)qkv, (const uint16_t*)out, lse, B, T, C,
-                                       NH);
+                                       NH, dt);
     return backward_t<float>(s, (float*)dqkv, dpre, (const float*)dout, (const float*)qkv,
                              (const float*)out, lse, B, T, C, NH);
 }

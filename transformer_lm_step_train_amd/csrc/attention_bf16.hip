@@ -37,9 +37,6 @@
 namespace gk {
 namespace {
 
-typedef __bf16 bf16x8 __attribute__((ext_vector_type(8)));
-typedef __bf16 bf16x2v __attribute__((ext_vector_type(2)));
-typedef float f32x2v __attribute__((ext_vector_type(2)));
 
 constexpr int RQ = 128;  // rows owned per workgroup (four waves of 32)
 constexpr int RT = 64;   // rows per staged tile
@@ -47,19 +44,6 @@ constexpr int LDP = RT + 8;  // stride of a tile stored along keys/queries
 constexpr float L2E = 1.4426950408889634f;
 constexpr float LN_2 = 0.6931471805599453f;
 
-__device__ __forceinline__ floatx16 mma(uint4 a, uint4 b, floatx16 c) {
-    return __builtin_amdgcn_mfma_f32_32x32x16_bf16(__builtin_bit_cast(bf16x8, a),
-                                                   __builtin_bit_cast(bf16x8, b), c, 0, 0, 0);
-}
-
-// two fp32 -> packed bf16 (round to nearest even, v_cvt_pk_bf16_f32)
-__device__ __forceinline__ uint32_t pk(float a, float b) {
-    const f32x2v f = {a, b};
-    return __builtin_bit_cast(uint32_t, __builtin_convertvector(f, bf16x2v));
-}
-
-__device__ __forceinline__ float lo_f(uint32_t w) { return __uint_as_float(w << 16); }
-__device__ __forceinline__ float hi_f(uint32_t w) { return __uint_as_float(w & 0xFFFF0000u); }
 
 __device__ __forceinline__ void zero(floatx16& x) {
 #pragma unroll
@@ -73,9 +57,10 @@ __device__ __forceinline__ int kpos(int kk) {
 
 // Eight registers of a 32-row accumulator block, e = 8h..8h+7, as a bf16
 // B operand (reduction positions 8g..8g+7 of the 16-row group h).
+template <class H>
 __device__ __forceinline__ uint4 pack8(const floatx16& x, int h) {
-    return make_uint4(pk(x[8 * h], x[8 * h + 1]), pk(x[8 * h + 2], x[8 * h + 3]),
-                      pk(x[8 * h + 4], x[8 * h + 5]), pk(x[8 * h + 6], x[8 * h + 7]));
+    return make_uint4(H::pk(x[8 * h], x[8 * h + 1]), H::pk(x[8 * h + 2], x[8 * h + 3]),
+                      H::pk(x[8 * h + 4], x[8 * h + 5]), H::pk(x[8 * h + 6], x[8 * h + 7]));
 }
 
 // A 64-row tile of one head (HS bf16 per row) held in registers between its
@@ -131,7 +116,7 @@ __device__ __forceinline__ uint4 rd(const uint16_t* p) {
 
 // Write one lane's accumulator blocks (rows = head dims d*32 + 8(e/4) +
 // 4g + e%4 of this lane's row) as bf16, scaled.
-template <int HS, int NDB>
+template <int HS, int NDB, class H>
 __device__ __forceinline__ void put_row(uint16_t* row, const floatx16 (&acc)[NDB], int g,
                                         float mul) {
 #pragma unroll
@@ -141,8 +126,8 @@ __device__ __forceinline__ void put_row(uint16_t* row, const floatx16 (&acc)[NDB
             const int dim0 = d * 32 + 8 * c + 4 * g;
             if (dim0 < HS)
                 *reinterpret_cast<uint2*>(row + dim0) =
-                    make_uint2(pk(acc[d][4 * c] * mul, acc[d][4 * c + 1] * mul),
-                               pk(acc[d][4 * c + 2] * mul, acc[d][4 * c + 3] * mul));
+                    make_uint2(H::pk(acc[d][4 * c] * mul, acc[d][4 * c + 1] * mul),
+                               H::pk(acc[d][4 * c + 2] * mul, acc[d][4 * c + 3] * mul));
         }
 }
 
@@ -154,7 +139,7 @@ __device__ __forceinline__ void zero_pad_rows(uint16_t* sm) {
         for (int i = threadIdx.x; i < (NDB * 32 - HS) * LDP; i += blockDim.x) sm[HS * LDP + i] = 0;
 }
 
-template <int HS>
+template <int HS, class H>
 __global__ __launch_bounds__(256, 2) void attn16_fwd_kernel(uint16_t* __restrict__ out,
                                                             float* __restrict__ lse,
                                                             const uint16_t* __restrict__ qkv,
@@ -208,8 +193,8 @@ __global__ __launch_bounds__(256, 2) void attn16_fwd_kernel(uint16_t* __restrict
             zero(sc[1]);
 #pragma unroll
             for (int j = 0; j < NKS; j++) {
-                sc[0] = mma(rd(kr + 16 * j), qv[j], sc[0]);
-                sc[1] = mma(rd(kr + 32 * LDK + 16 * j), qv[j], sc[1]);
+                sc[0] = H::mma(rd(kr + 16 * j), qv[j], sc[0]);
+                sc[1] = H::mma(rd(kr + 32 * LDK + 16 * j), qv[j], sc[1]);
             }
             if ((k0 + RT - 1 > qw) || (k0 + RT > T)) {  // tile touches the mask
 #pragma unroll
@@ -249,10 +234,10 @@ __global__ __launch_bounds__(256, 2) void attn16_fwd_kernel(uint16_t* __restrict
             for (int kb = 0; kb < 2; kb++)
 #pragma unroll
                 for (int hh = 0; hh < 2; hh++) {
-                    const uint4 pb = pack8(sc[kb], hh);
+                    const uint4 pb = pack8<H>(sc[kb], hh);
 #pragma unroll
                     for (int d = 0; d < NDB; d++)
-                        o[d] = mma(rd(vr + d * 32 * LDP + kb * 32 + 16 * hh), pb, o[d]);
+                        o[d] = H::mma(rd(vr + d * 32 * LDP + kb * 32 + 16 * hh), pb, o[d]);
                 }
         }
         kreg.store_rows(ks[cur ^ 1]);
@@ -260,7 +245,7 @@ __global__ __launch_bounds__(256, 2) void attn16_fwd_kernel(uint16_t* __restrict
         __syncthreads();
     }
     if (q < T) {
-        put_row<HS, NDB>(out + ((int64_t)b * T + q) * C + h * HS, o, g, 1.f / l);
+        put_row<HS, NDB, H>(out + ((int64_t)b * T + q) * C + h * HS, o, g, 1.f / l);
         if (g == 0) lse[((int64_t)b * NH + h) * T + q] = (m + log2f(l)) * LN_2;
     }
 }
@@ -268,7 +253,7 @@ __global__ __launch_bounds__(256, 2) void attn16_fwd_kernel(uint16_t* __restrict
 // dQ (lane owns a query) and D = rowsum(dout * out) for the key/value
 // kernel.  K is staged twice: as rows for S^T = K Q^T and along keys for
 // dQ^T = K^T dS^T; V as rows for dP^T = V dout^T.
-template <int HS>
+template <int HS, class H>
 __global__ __launch_bounds__(256, 2) void attn16_dq_kernel(
     uint16_t* __restrict__ dqkv, float* __restrict__ Dout, const uint16_t* __restrict__ dout,
     const uint16_t* __restrict__ out, const uint16_t* __restrict__ qkv,
@@ -309,7 +294,7 @@ __global__ __launch_bounds__(256, 2) void attn16_dq_kernel(
         const uint32_t ow[4] = {ov.x, ov.y, ov.z, ov.w};
 #pragma unroll
         for (int i = 0; i < 4; i++)
-            dsum += lo_f(dw[i]) * lo_f(ow[i]) + hi_f(dw[i]) * hi_f(ow[i]);
+            dsum += H::lo(dw[i]) * H::lo(ow[i]) + H::hi(dw[i]) * H::hi(ow[i]);
     }
     const float Dq = dsum + __shfl_xor(dsum, 32, WAVE);
     const int64_t srow = ((int64_t)b * NH + h) * T;
@@ -345,8 +330,8 @@ __global__ __launch_bounds__(256, 2) void attn16_dq_kernel(
             for (int j = 0; j < NKS; j++)
 #pragma unroll
                 for (int kb = 0; kb < 2; kb++) {
-                    sc[kb] = mma(rd(kr + kb * 32 * LDK + 16 * j), qv[j], sc[kb]);
-                    dp[kb] = mma(rd(vr + kb * 32 * LDK + 16 * j), dv[j], dp[kb]);
+                    sc[kb] = H::mma(rd(kr + kb * 32 * LDK + 16 * j), qv[j], sc[kb]);
+                    dp[kb] = H::mma(rd(vr + kb * 32 * LDK + 16 * j), dv[j], dp[kb]);
                 }
 #pragma unroll
             for (int kb = 0; kb < 2; kb++)
@@ -362,10 +347,10 @@ __global__ __launch_bounds__(256, 2) void attn16_dq_kernel(
             for (int kb = 0; kb < 2; kb++)
 #pragma unroll
                 for (int hh = 0; hh < 2; hh++) {
-                    const uint4 sb = pack8(sc[kb], hh);
+                    const uint4 sb = pack8<H>(sc[kb], hh);
 #pragma unroll
                     for (int d = 0; d < NDB; d++)
-                        dq[d] = mma(rd(ktr + d * 32 * LDP + kb * 32 + 16 * hh), sb, dq[d]);
+                        dq[d] = H::mma(rd(ktr + d * 32 * LDP + kb * 32 + 16 * hh), sb, dq[d]);
                 }
         }
         kreg.store_rows(ks[cur ^ 1]);
@@ -373,13 +358,13 @@ __global__ __launch_bounds__(256, 2) void attn16_dq_kernel(
         vreg.store_rows(vs[cur ^ 1]);
         __syncthreads();
     }
-    if (q < T) put_row<HS, NDB>(dqkv + ((int64_t)b * T + q) * ld + h * HS, dq, g, scale);
+    if (q < T) put_row<HS, NDB, H>(dqkv + ((int64_t)b * T + q) * ld + h * HS, dq, g, scale);
 }
 
 // dK and dV (lane owns a key).  Q and dout are staged as rows (for S = Q K^T
 // and dP = dout V^T, queries down the accumulator) and along queries (for
 // dK^T = Q^T dS and dV^T = dout^T P).
-template <int HS>
+template <int HS, class H>
 __global__ __launch_bounds__(256, 2) void attn16_dkdv_kernel(
     uint16_t* __restrict__ dqkv, const uint16_t* __restrict__ dout,
     const uint16_t* __restrict__ qkv, const float* __restrict__ lse, const float* __restrict__ D,
@@ -461,8 +446,8 @@ __global__ __launch_bounds__(256, 2) void attn16_dkdv_kernel(
             zero(dp);
 #pragma unroll
             for (int j = 0; j < NKS; j++) {
-                sc = mma(rd(qr + 16 * j), kv[j], sc);
-                dp = mma(rd(dr + 16 * j), vv[j], dp);
+                sc = H::mma(rd(qr + 16 * j), kv[j], sc);
+                dp = H::mma(rd(dr + 16 * j), vv[j], dp);
             }
 #pragma unroll
             for (int e = 0; e < 16; e++) {
@@ -478,11 +463,11 @@ __global__ __launch_bounds__(256, 2) void attn16_dkdv_kernel(
             const uint16_t* dtr = dt_[cur] + li * LDP + 8 * g + qh * 32;
 #pragma unroll
             for (int hh = 0; hh < 2; hh++) {
-                const uint4 pb = pack8(sc, hh), sb = pack8(dp, hh);
+                const uint4 pb = pack8<H>(sc, hh), sb = pack8<H>(dp, hh);
 #pragma unroll
                 for (int d = 0; d < NDB; d++) {
-                    dvv[d] = mma(rd(dtr + d * 32 * LDP + 16 * hh), pb, dvv[d]);
-                    dk[d] = mma(rd(qtr + d * 32 * LDP + 16 * hh), sb, dk[d]);
+                    dvv[d] = H::mma(rd(dtr + d * 32 * LDP + 16 * hh), pb, dvv[d]);
+                    dk[d] = H::mma(rd(qtr + d * 32 * LDP + 16 * hh), sb, dk[d]);
                 }
             }
         }
@@ -495,59 +480,75 @@ __global__ __launch_bounds__(256, 2) void attn16_dkdv_kernel(
     }
     if (key < T) {
         uint16_t* row = dqkv + ((int64_t)b * T + key) * ld + h * HS;
-        put_row<HS, NDB>(row + C, dk, g, scale);
-        put_row<HS, NDB>(row + 2 * C, dvv, g, 1.f);
+        put_row<HS, NDB, H>(row + C, dk, g, scale);
+        put_row<HS, NDB, H>(row + 2 * C, dvv, g, 1.f);
     }
 }
 
-template <int HS>
+template <int HS, class H>
 hipError_t bwd16(hipStream_t s, uint16_t* dqkv, float* D, const uint16_t* dout,
                  const uint16_t* qkv, const uint16_t* out, const float* lse, int B, int T, int C,
                  int NH) {
     const int nb = (T + RQ - 1) / RQ;
     const float scale = 1.0f / sqrtf((float)HS);
     const float qscale = L2E * scale;
-    hipLaunchKernelGGL((attn16_dq_kernel<HS>), dim3(B * NH * nb), dim3(256), 0, s, dqkv, D, dout,
+    hipLaunchKernelGGL((attn16_dq_kernel<HS, H>), dim3(B * NH * nb), dim3(256), 0, s, dqkv, D, dout,
                        out, qkv, lse, T, C, NH, qscale, scale);
-    hipLaunchKernelGGL((attn16_dkdv_kernel<HS>), dim3(B * NH * nb), dim3(256), 0, s, dqkv, dout,
+    hipLaunchKernelGGL((attn16_dkdv_kernel<HS, H>), dim3(B * NH * nb), dim3(256), 0, s, dqkv, dout,
                        qkv, lse, D, T, C, NH, qscale, scale);
     return hipGetLastError();
 }
 
-template <int HS>
+template <int HS, class H>
 hipError_t fwd16(hipStream_t s, uint16_t* out, float* lse, const uint16_t* qkv, int B, int T,
                  int C, int NH) {
     const int nqb = (T + RQ - 1) / RQ;
     const float qscale = L2E / sqrtf((float)HS);
-    hipLaunchKernelGGL((attn16_fwd_kernel<HS>), dim3(B * NH * nqb), dim3(256), 0, s, out, lse,
+    hipLaunchKernelGGL((attn16_fwd_kernel<HS, H>), dim3(B * NH * nqb), dim3(256), 0, s, out, lse,
                        qkv, T, C, NH, qscale);
     return hipGetLastError();
 }
 
-}  // namespace
 
-hipError_t attention_forward_bf16(hipStream_t s, uint16_t* out, float* lse, const uint16_t* qkv,
-                                  int B, int T, int C, int NH) {
-    if (B <= 0 || T <= 0) return hipSuccess;
+template <class H>
+hipError_t fwd_h(hipStream_t s, uint16_t* out, float* lse, const uint16_t* qkv, int B, int T,
+                 int C, int NH) {
     switch (C / NH) {
-        case 16: return fwd16<16>(s, out, lse, qkv, B, T, C, NH);
-        case 32: return fwd16<32>(s, out, lse, qkv, B, T, C, NH);
-        case 64: return fwd16<64>(s, out, lse, qkv, B, T, C, NH);
+        case 16: return fwd16<16, H>(s, out, lse, qkv, B, T, C, NH);
+        case 32: return fwd16<32, H>(s, out, lse, qkv, B, T, C, NH);
+        case 64: return fwd16<64, H>(s, out, lse, qkv, B, T, C, NH);
         default: return hipErrorInvalidValue;
     }
 }
 
-hipError_t attention_backward_bf16(hipStream_t s, uint16_t* dqkv, float* D,
-                                   const uint16_t* dout, const uint16_t* qkv,
-                                   const uint16_t* out, const float* lse, int B, int T, int C,
-                                   int NH) {
-    if (B <= 0 || T <= 0) return hipSuccess;
+template <class H>
+hipError_t bwd_h(hipStream_t s, uint16_t* dqkv, float* D, const uint16_t* dout,
+                 const uint16_t* qkv, const uint16_t* out, const float* lse, int B, int T, int C,
+                 int NH) {
     switch (C / NH) {
-        case 16: return bwd16<16>(s, dqkv, D, dout, qkv, out, lse, B, T, C, NH);
-        case 32: return bwd16<32>(s, dqkv, D, dout, qkv, out, lse, B, T, C, NH);
-        case 64: return bwd16<64>(s, dqkv, D, dout, qkv, out, lse, B, T, C, NH);
+        case 16: return bwd16<16, H>(s, dqkv, D, dout, qkv, out, lse, B, T, C, NH);
+        case 32: return bwd16<32, H>(s, dqkv, D, dout, qkv, out, lse, B, T, C, NH);
+        case 64: return bwd16<64, H>(s, dqkv, D, dout, qkv, out, lse, B, T, C, NH);
         default: return hipErrorInvalidValue;
     }
+}
+
+}  // namespace
+
+hipError_t attention_forward_half(hipStream_t s, uint16_t* out, float* lse, const uint16_t* qkv,
+                                  int B, int T, int C, int NH, int dt) {
+    if (B <= 0 || T <= 0) return hipSuccess;
+    return dt == DT_F16 ? fwd_h<HF16>(s, out, lse, qkv, B, T, C, NH)
+                        : fwd_h<HBF16>(s, out, lse, qkv, B, T, C, NH);
+}
+
+hipError_t attention_backward_half(hipStream_t s, uint16_t* dqkv, float* D,
+                                   const uint16_t* dout, const uint16_t* qkv,
+                                   const uint16_t* out, const float* lse, int B, int T, int C,
+                                   int NH, int dt) {
+    if (B <= 0 || T <= 0) return hipSuccess;
+    return dt == DT_F16 ? bwd_h<HF16>(s, dqkv, D, dout, qkv, out, lse, B, T, C, NH)
+                        : bwd_h<HBF16>(s, dqkv, D, dout, qkv, out, lse, B, T, C, NH);
 }
 
 }  // namespace gk

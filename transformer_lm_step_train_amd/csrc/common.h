@@ -58,6 +58,9 @@ __device__ __forceinline__ int xcd_remap(int wg, int n) {
     return wg < (q << 3) ? (wg & 7) * q + (wg >> 3) : wg;
 }
 
+// ---- 16-bit storage -------------------------------------------------------
+#include "dtype.h"
+
 // ---- bf16 storage ----------------------------------------------------------
 // bf16 is kept as raw uint16_t bits: the top half of an IEEE fp32.  Rounding
 // from fp32 is to nearest, ties to even; NaN stays NaN.
@@ -97,3 +100,74 @@ struct Act<uint16_t> {
     static __device__ __forceinline__ float ld1(const uint16_t* p) { return bf2f(*p); }
     static __device__ __forceinline__ void st1(uint16_t* p, float v) { *p = f2bf(v); }
 };
+
+// IEEE fp16 storage; conversion from fp32 rounds to nearest, ties to even.
+template <>
+struct Act<_Float16> {
+    static __device__ __forceinline__ float4 ld(const _Float16* p) {
+        typedef _Float16 h4 __attribute__((ext_vector_type(4)));
+        const h4 u = *reinterpret_cast<const h4*>(p);
+        return make_float4((float)u[0], (float)u[1], (float)u[2], (float)u[3]);
+    }
+    static __device__ __forceinline__ void st(_Float16* p, float4 v) {
+        typedef _Float16 h4 __attribute__((ext_vector_type(4)));
+        h4 u = {(_Float16)v.x, (_Float16)v.y, (_Float16)v.z, (_Float16)v.w};
+        *reinterpret_cast<h4*>(p) = u;
+    }
+    static __device__ __forceinline__ float ld1(const _Float16* p) { return (float)*p; }
+    static __device__ __forceinline__ void st1(_Float16* p, float v) { *p = (_Float16)v; }
+};
+
+// The 16-bit formats as matrix-core operands: bits <-> fp32, a packed pair,
+// and the 32x32x16 MFMA with fp32 accumulation.
+typedef __bf16 bf16x8_t __attribute__((ext_vector_type(8)));
+typedef _Float16 f16x8_t __attribute__((ext_vector_type(8)));
+typedef __bf16 bf16x2_t __attribute__((ext_vector_type(2)));
+typedef _Float16 f16x2_t __attribute__((ext_vector_type(2)));
+typedef float f32x2_t __attribute__((ext_vector_type(2)));
+
+struct HBF16 {
+    static constexpr int dt = DT_BF16;
+    static __device__ __forceinline__ float f(uint32_t h) { return bf2f(h & 0xFFFFu); }
+    static __device__ __forceinline__ uint16_t h(float x) { return f2bf(x); }
+    static __device__ __forceinline__ float lo(uint32_t w) { return __uint_as_float(w << 16); }
+    static __device__ __forceinline__ float hi(uint32_t w) { return __uint_as_float(w & 0xFFFF0000u); }
+    static __device__ __forceinline__ uint32_t pk(float a, float b) {
+        const f32x2_t v = {a, b};
+        return __builtin_bit_cast(uint32_t, __builtin_convertvector(v, bf16x2_t));
+    }
+    static __device__ __forceinline__ floatx16 mma(uint4 a, uint4 b, floatx16 c) {
+        return __builtin_amdgcn_mfma_f32_32x32x16_bf16(__builtin_bit_cast(bf16x8_t, a),
+                                                       __builtin_bit_cast(bf16x8_t, b), c, 0, 0, 0);
+    }
+};
+
+struct HF16 {
+    static constexpr int dt = DT_F16;
+    static __device__ __forceinline__ float f(uint32_t h) {
+        return (float)__builtin_bit_cast(_Float16, (uint16_t)(h & 0xFFFFu));
+    }
+    static __device__ __forceinline__ uint16_t h(float x) {
+        return __builtin_bit_cast(uint16_t, (_Float16)x);
+    }
+    static __device__ __forceinline__ float lo(uint32_t w) { return f(w); }
+    static __device__ __forceinline__ float hi(uint32_t w) { return f(w >> 16); }
+    static __device__ __forceinline__ uint32_t pk(float a, float b) {
+        const f32x2_t v = {a, b};
+        return __builtin_bit_cast(uint32_t, __builtin_convertvector(v, f16x2_t));
+    }
+    static __device__ __forceinline__ floatx16 mma(uint4 a, uint4 b, floatx16 c) {
+        return __builtin_amdgcn_mfma_f32_32x32x16_f16(__builtin_bit_cast(f16x8_t, a),
+                                                      __builtin_bit_cast(f16x8_t, b), c, 0, 0, 0);
+    }
+};
+
+// Runs f with a value of the storage type of dt (float, bf16 bits or fp16).
+template <class F>
+inline hipError_t by_dt(int dt, F&& f) {
+    switch (dt) {
+        case DT_BF16: return f(uint16_t{});
+        case DT_F16: return f(_Float16{});
+        default: return f(float{});
+    }
+}

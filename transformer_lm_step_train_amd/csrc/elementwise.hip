@@ -251,16 +251,27 @@ __device__ __forceinline__ float adamw_one(float& p, float g, float& m, float& v
 
 // shadow (optional): bf16 copy of the updated parameters for the matmuls of
 // the mixed-precision model.
+// The AdamW sweep.  S is the storage type of the optional 16-bit weight copy
+// written in the same pass (uint16_t bf16 bits or _Float16; float = none).
+// With loss scaling (fp16 model) the gradients hold scale * dL/dp: they are
+// divided by *gscale, and the whole sweep is skipped when *skip is set (a
+// non-finite gradient was found).
+template <class S>
 __global__ __launch_bounds__(256) void adamw_kernel(float* __restrict__ p,
                                                     const float* __restrict__ g,
                                                     float* __restrict__ m, float* __restrict__ v,
-                                                    uint16_t* __restrict__ shadow, int64_t n,
+                                                    S* __restrict__ shadow, int64_t n,
                                                     float lr, float b1, float b2, float eps,
-                                                    float wd, float bc1, float bc2) {
+                                                    float wd, float bc1, float bc2,
+                                                    const float* __restrict__ gscale,
+                                                    const int* __restrict__ skip) {
+    if (skip && *skip) return;
+    const float ig = gscale ? 1.0f / *gscale : 1.0f;
     const int64_t n4 = n >> 2;
     const int64_t stride = (int64_t)gridDim.x * blockDim.x;
     for (int64_t i = blockIdx.x * (int64_t)blockDim.x + threadIdx.x; i < n4; i += stride) {
         float4 pp = ld4(p + 4 * i), gg = ld4(g + 4 * i), mm = ld4(m + 4 * i), vv = ld4(v + 4 * i);
+        gg = make_float4(gg.x * ig, gg.y * ig, gg.z * ig, gg.w * ig);
         adamw_one(pp.x, gg.x, mm.x, vv.x, lr, b1, b2, eps, wd, bc1, bc2);
         adamw_one(pp.y, gg.y, mm.y, vv.y, lr, b1, b2, eps, wd, bc1, bc2);
         adamw_one(pp.z, gg.z, mm.z, vv.z, lr, b1, b2, eps, wd, bc1, bc2);
@@ -268,19 +279,52 @@ __global__ __launch_bounds__(256) void adamw_kernel(float* __restrict__ p,
         st4(p + 4 * i, pp);
         st4(m + 4 * i, mm);
         st4(v + 4 * i, vv);
-        if (shadow) Act<uint16_t>::st(shadow + 4 * i, pp);
+        if (shadow) Act<S>::st(shadow + 4 * i, pp);
     }
     for (int64_t i = 4 * n4 + blockIdx.x * (int64_t)blockDim.x + threadIdx.x; i < n; i += stride) {
-        adamw_one(p[i], g[i], m[i], v[i], lr, b1, b2, eps, wd, bc1, bc2);
-        if (shadow) shadow[i] = f2bf(p[i]);
+        adamw_one(p[i], g[i] * ig, m[i], v[i], lr, b1, b2, eps, wd, bc1, bc2);
+        if (shadow) Act<S>::st1(shadow + i, p[i]);
     }
 }
 
-__global__ __launch_bounds__(256) void to_bf16_kernel(uint16_t* __restrict__ out,
+template <class S>
+__global__ __launch_bounds__(256) void to_half_kernel(S* __restrict__ out,
                                                       const float* __restrict__ in, int64_t n) {
     const int64_t stride = (int64_t)gridDim.x * blockDim.x;
     for (int64_t i = blockIdx.x * (int64_t)blockDim.x + threadIdx.x; i < n; i += stride)
-        out[i] = f2bf(in[i]);
+        Act<S>::st1(out + i, in[i]);
+}
+
+// *flag = 1 if any of g[0..n) is not finite (inf or NaN).
+__global__ __launch_bounds__(256) void check_finite_kernel(const float* __restrict__ g, int64_t n,
+                                                           int* __restrict__ flag) {
+    const int64_t stride = (int64_t)gridDim.x * blockDim.x;
+    bool bad = false;
+    for (int64_t i = blockIdx.x * (int64_t)blockDim.x + threadIdx.x; i < n; i += stride)
+        bad |= !__builtin_isfinite(g[i]);
+    if (__any(bad) && (threadIdx.x & 63) == 0) atomicOr(flag, 1);
+}
+
+// Dynamic loss scaling, one step: st = {scale (float bits), good steps,
+// found_inf, skipped}.  A step with a non-finite gradient is skipped and
+// halves the scale; `interval` clean steps in a row double it.  found_inf is
+// cleared for the next step.
+__global__ void loss_scale_kernel(float* __restrict__ scale, int* __restrict__ good,
+                                  int* __restrict__ found, int* __restrict__ skipped,
+                                  int interval, float min_scale) {
+    if (threadIdx.x != 0 || blockIdx.x != 0) return;
+    if (*found) {
+        *scale = fmaxf(*scale * 0.5f, min_scale);
+        *good = 0;
+        *skipped = 1;
+    } else {
+        *skipped = 0;
+        if (++*good >= interval) {
+            *scale = *scale * 2.0f;
+            *good = 0;
+        }
+    }
+    *found = 0;
 }
 
 inline unsigned grid_for(int64_t work, int per_block, unsigned cap) {
@@ -321,17 +365,16 @@ __global__ __launch_bounds__(256) void rope_kernel(E* __restrict__ qkv, const fl
 }  // namespace
 
 hipError_t encoder_forward(hipStream_t s, void* out, const int32_t* tok, const float* wte,
-                           const float* wpe, int B, int T, int C, int V, int* flag, int bf16) {
+                           const float* wpe, int B, int T, int C, int V, int* flag, int dt) {
     const int64_t n = (int64_t)B * T * (C / 4);
     if (n <= 0) return hipSuccess;
     const dim3 grid(grid_for(n, 256, 65535));
-    if (bf16)
-        hipLaunchKernelGGL(encoder_fwd_kernel<uint16_t>, grid, dim3(256), 0, s, (uint16_t*)out,
-                           tok, wte, wpe, B, T, C, V, flag);
-    else
-        hipLaunchKernelGGL(encoder_fwd_kernel<float>, grid, dim3(256), 0, s, (float*)out, tok, wte,
-                           wpe, B, T, C, V, flag);
-    return hipGetLastError();
+    return by_dt(dt, [&](auto e) {
+        using E = decltype(e);
+        hipLaunchKernelGGL(encoder_fwd_kernel<E>, grid, dim3(256), 0, s, (E*)out, tok, wte, wpe,
+                           B, T, C, V, flag);
+        return hipGetLastError();
+    });
 }
 
 hipError_t encoder_sort_prepare(int n_pow2) {
@@ -369,27 +412,26 @@ hipError_t encoder_backward_t(hipStream_t s, float* dwte, float* dwpe, const E* 
 
 hipError_t encoder_backward(hipStream_t s, float* dwte, float* dwpe, const void* dx,
                             const uint32_t* keys, int B, int T, int C, int V, int pos_bits,
-                            int bf16) {
+                            int dt) {
     if (B * T <= 0) return hipSuccess;
-    if (bf16)
-        return encoder_backward_t<uint16_t>(s, dwte, dwpe, (const uint16_t*)dx, keys, B, T, C, V,
-                                            pos_bits);
-    return encoder_backward_t<float>(s, dwte, dwpe, (const float*)dx, keys, B, T, C, V, pos_bits);
+    return by_dt(dt, [&](auto e) {
+        using E = decltype(e);
+        return encoder_backward_t<E>(s, dwte, dwpe, (const E*)dx, keys, B, T, C, V, pos_bits);
+    });
 }
 
 hipError_t rope_apply(hipStream_t s, void* qkv, const float* cs, int B, int T, int C, int NH,
-                      int dir, int bf16) {
+                      int dir, int dt) {
     const int64_t n = (int64_t)B * T * C;
     if (n <= 0) return hipSuccess;
     const dim3 grid(grid_for(n, 256, 65535));
     const int hs = C / NH;
-    if (bf16)
-        hipLaunchKernelGGL(rope_kernel<uint16_t>, grid, dim3(256), 0, s, (uint16_t*)qkv,
-                           (const float2*)cs, B * T, T, C, hs, (int64_t)3 * C, (float)dir);
-    else
-        hipLaunchKernelGGL(rope_kernel<float>, grid, dim3(256), 0, s, (float*)qkv,
-                           (const float2*)cs, B * T, T, C, hs, (int64_t)3 * C, (float)dir);
-    return hipGetLastError();
+    return by_dt(dt, [&](auto e) {
+        using E = decltype(e);
+        hipLaunchKernelGGL(rope_kernel<E>, grid, dim3(256), 0, s, (E*)qkv, (const float2*)cs,
+                           B * T, T, C, hs, (int64_t)3 * C, (float)dir);
+        return hipGetLastError();
+    });
 }
 
 size_t bias_partials_floats(int M, int N) {
@@ -397,17 +439,16 @@ size_t bias_partials_floats(int M, int N) {
 }
 
 hipError_t bias_grad(hipStream_t s, float* db, float* part, const void* dy, int M, int N,
-                     int64_t ld, int bf16) {
+                     int64_t ld, int dt) {
     if (M <= 0 || N <= 0) return hipSuccess;
     const int nchunks = (M + BIAS_ROWS - 1) / BIAS_ROWS;
     dim3 grid((N / 4 + 63) / 64, nchunks);
-    if (bf16)
-        hipLaunchKernelGGL(bias_partial_kernel<uint16_t>, grid, dim3(256), 0, s, part,
-                           (const uint16_t*)dy, M, N, ld);
-    else
-        hipLaunchKernelGGL(bias_partial_kernel<float>, grid, dim3(256), 0, s, part,
-                           (const float*)dy, M, N, ld);
-    hipError_t e = hipGetLastError();
+    hipError_t e = by_dt(dt, [&](auto x) {
+        using E = decltype(x);
+        hipLaunchKernelGGL(bias_partial_kernel<E>, grid, dim3(256), 0, s, part, (const E*)dy, M,
+                           N, ld);
+        return hipGetLastError();
+    });
     if (e != hipSuccess) return e;
     return colsum_add(s, db, db, N, part, nchunks, N);
 }
@@ -427,18 +468,41 @@ hipError_t fill_zero(hipStream_t s, float* p, int64_t n) {
     return hipGetLastError();
 }
 
-hipError_t adamw(hipStream_t s, float* p, const float* g, float* m, float* v, uint16_t* shadow,
-                 int64_t n, float lr, float b1, float b2, float eps, float wd, float bc1,
-                 float bc2) {
+hipError_t adamw(hipStream_t s, float* p, const float* g, float* m, float* v, void* shadow,
+                 int shadow_dt, int64_t n, float lr, float b1, float b2, float eps, float wd,
+                 float bc1, float bc2, const float* gscale, const int* skip) {
     if (n <= 0) return hipSuccess;
-    hipLaunchKernelGGL(adamw_kernel, dim3(grid_for(n / 4 + 1, 256, 8192)), dim3(256), 0, s, p,
-                       g, m, v, shadow, n, lr, b1, b2, eps, wd, bc1, bc2);
+    const dim3 grid(grid_for(n / 4 + 1, 256, 8192));
+    if (!shadow) shadow_dt = DT_F32;
+    return by_dt(shadow_dt, [&](auto e) {
+        using S = decltype(e);
+        hipLaunchKernelGGL(adamw_kernel<S>, grid, dim3(256), 0, s, p, g, m, v, (S*)shadow, n, lr,
+                           b1, b2, eps, wd, bc1, bc2, gscale, skip);
+        return hipGetLastError();
+    });
+}
+
+hipError_t to_half(hipStream_t s, void* out, const float* in, int64_t n, int dt) {
+    if (n <= 0) return hipSuccess;
+    return by_dt(dt, [&](auto e) {
+        using S = decltype(e);
+        hipLaunchKernelGGL(to_half_kernel<S>, dim3(grid_for(n, 256, 8192)), dim3(256), 0, s,
+                           (S*)out, in, n);
+        return hipGetLastError();
+    });
+}
+
+hipError_t check_finite(hipStream_t s, const float* g, int64_t n, int* flag) {
+    if (n <= 0) return hipSuccess;
+    hipLaunchKernelGGL(check_finite_kernel, dim3(grid_for(n, 256, 8192)), dim3(256), 0, s, g, n,
+                       flag);
     return hipGetLastError();
 }
 
-hipError_t to_bf16(hipStream_t s, uint16_t* out, const float* in, int64_t n) {
-    if (n <= 0) return hipSuccess;
-    hipLaunchKernelGGL(to_bf16_kernel, dim3(grid_for(n, 256, 8192)), dim3(256), 0, s, out, in, n);
+hipError_t loss_scale_update(hipStream_t s, float* scale, int* good, int* found, int* skipped,
+                             int interval, float min_scale) {
+    hipLaunchKernelGGL(loss_scale_kernel, dim3(1), dim3(64), 0, s, scale, good, found, skipped,
+                       interval, min_scale);
     return hipGetLastError();
 }
 

@@ -33,12 +33,6 @@ namespace {
 constexpr int BM = 128, BN = 128, BK = 64, NTHR = 256;
 constexpr int LDH = BK + 8;       // LDS row stride, bf16 elements (144 bytes)
 constexpr int EPI_PARTIAL = 100;  // internal: fp32 split-K partial sums
-typedef __bf16 bf16x8 __attribute__((ext_vector_type(8)));
-
-__device__ __forceinline__ floatx16 mfma(uint4 a, uint4 b, floatx16 c) {
-    return __builtin_amdgcn_mfma_f32_32x32x16_bf16(__builtin_bit_cast(bf16x8, a),
-                                                   __builtin_bit_cast(bf16x8, b), c, 0, 0, 0);
-}
 
 template <bool KC>
 struct TileH;
@@ -137,18 +131,19 @@ __device__ __forceinline__ uint4 frag(const uint16_t* s, int r, int g, int q) {
     return *reinterpret_cast<const uint4*>(s + r * LDH + 16 * q + 8 * g);
 }
 
+template <class H>
 __device__ __forceinline__ float4 ld4h(const uint16_t* p) {
     const uint2 u = *reinterpret_cast<const uint2*>(p);
-    return make_float4(bf2f(u.x & 0xFFFFu), bf2f(u.x >> 16), bf2f(u.y & 0xFFFFu), bf2f(u.y >> 16));
+    return make_float4(H::lo(u.x), H::hi(u.x), H::lo(u.y), H::hi(u.y));
 }
+template <class H>
 __device__ __forceinline__ void st4h(uint16_t* p, float4 v) {
-    *reinterpret_cast<uint2*>(p) = make_uint2(f2bf(v.x) | ((uint32_t)f2bf(v.y) << 16),
-                                              f2bf(v.z) | ((uint32_t)f2bf(v.w) << 16));
+    *reinterpret_cast<uint2*>(p) = make_uint2(H::pk(v.x, v.y), H::pk(v.z, v.w));
 }
 
 // Epilogue on 4 consecutive columns.  bf16 outputs: STORE, RESID, GELU,
 // GELU_BWD.  fp32 outputs: ACCUM (gradient +=), STORE when out_f32, PARTIAL.
-template <int EPI>
+template <int EPI, class H>
 __device__ __forceinline__ void epi4(const GemmArgsH& a, float* __restrict__ partial, int row,
                                      int col, float4 v) {
     if (EPI == EPI_PARTIAL) {
@@ -163,8 +158,8 @@ __device__ __forceinline__ void epi4(const GemmArgsH& a, float* __restrict__ par
         return;
     }
     if (EPI == EPI_GELU_BWD) {
-        const float4 x = ld4h(a.aux + (int64_t)row * a.ldaux + col);
-        st4h(reinterpret_cast<uint16_t*>(a.C) + idx,
+        const float4 x = ld4h<H>(a.aux + (int64_t)row * a.ldaux + col);
+        st4h<H>(reinterpret_cast<uint16_t*>(a.C) + idx,
              make_float4(v.x * gelu_grad_f(x.x), v.y * gelu_grad_f(x.y), v.z * gelu_grad_f(x.z),
                          v.w * gelu_grad_f(x.w)));
         return;
@@ -174,19 +169,19 @@ __device__ __forceinline__ void epi4(const GemmArgsH& a, float* __restrict__ par
         v = make_float4(v.x + bb.x, v.y + bb.y, v.z + bb.z, v.w + bb.w);
     }
     if (EPI == EPI_RESID) {
-        const float4 x = ld4h(a.aux + (int64_t)row * a.ldaux + col);
+        const float4 x = ld4h<H>(a.aux + (int64_t)row * a.ldaux + col);
         v = make_float4(v.x + x.x, v.y + x.y, v.z + x.z, v.w + x.w);
     }
     if (EPI == EPI_STORE && a.out_f32) {
         st4(reinterpret_cast<float*>(a.C) + idx, v);
         return;
     }
-    st4h(reinterpret_cast<uint16_t*>(a.C) + idx, v);
+    st4h<H>(reinterpret_cast<uint16_t*>(a.C) + idx, v);
     if (EPI == EPI_GELU)
-        st4h(a.out2 + idx, make_float4(gelu_f(v.x), gelu_f(v.y), gelu_f(v.z), gelu_f(v.w)));
+        st4h<H>(a.out2 + idx, make_float4(gelu_f(v.x), gelu_f(v.y), gelu_f(v.z), gelu_f(v.w)));
 }
 
-template <int EPI>
+template <int EPI, class H>
 __device__ __forceinline__ void epi1(const GemmArgsH& a, float* __restrict__ partial, int row,
                                      int col, float v) {
     if (EPI == EPI_PARTIAL) {
@@ -200,20 +195,20 @@ __device__ __forceinline__ void epi1(const GemmArgsH& a, float* __restrict__ par
     }
     if (EPI == EPI_GELU_BWD) {
         reinterpret_cast<uint16_t*>(a.C)[idx] =
-            f2bf(v * gelu_grad_f(bf2f(a.aux[(int64_t)row * a.ldaux + col])));
+            H::h(v * gelu_grad_f(H::f(a.aux[(int64_t)row * a.ldaux + col])));
         return;
     }
     if (EPI == EPI_RESID || EPI == EPI_GELU || (EPI == EPI_STORE && a.bias)) v += a.bias[col];
-    if (EPI == EPI_RESID) v += bf2f(a.aux[(int64_t)row * a.ldaux + col]);
+    if (EPI == EPI_RESID) v += H::f(a.aux[(int64_t)row * a.ldaux + col]);
     if (EPI == EPI_STORE && a.out_f32) {
         reinterpret_cast<float*>(a.C)[idx] = v;
         return;
     }
-    reinterpret_cast<uint16_t*>(a.C)[idx] = f2bf(v);
-    if (EPI == EPI_GELU) a.out2[idx] = f2bf(gelu_f(v));
+    reinterpret_cast<uint16_t*>(a.C)[idx] = H::h(v);
+    if (EPI == EPI_GELU) a.out2[idx] = H::h(gelu_f(v));
 }
 
-template <int OP, int EPI>
+template <int OP, int EPI, class H>
 __global__ __launch_bounds__(NTHR, 2) void gemm_bf16_kernel(const GemmArgsH a, int tiles_m,
                                                             int tiles_n, int kchunk,
                                                             float* __restrict__ partial) {
@@ -271,10 +266,10 @@ __global__ __launch_bounds__(NTHR, 2) void gemm_bf16_kernel(const GemmArgsH a, i
             const uint4 a1 = frag(sa, wm + 32 + li, g, q);
             const uint4 b0 = frag(sb, wn + li, g, q);
             const uint4 b1 = frag(sb, wn + 32 + li, g, q);
-            acc[0][0] = mfma(a0, b0, acc[0][0]);
-            acc[0][1] = mfma(a0, b1, acc[0][1]);
-            acc[1][0] = mfma(a1, b0, acc[1][0]);
-            acc[1][1] = mfma(a1, b1, acc[1][1]);
+            acc[0][0] = H::mma(a0, b0, acc[0][0]);
+            acc[0][1] = H::mma(a0, b1, acc[0][1]);
+            acc[1][0] = H::mma(a1, b0, acc[1][0]);
+            acc[1][1] = H::mma(a1, b1, acc[1][1]);
         }
     };
     using I0 = std::integral_constant<int, 0>;
@@ -332,11 +327,11 @@ __global__ __launch_bounds__(NTHR, 2) void gemm_bf16_kernel(const GemmArgsH a, i
         const int row = m0 + wm + r, col = n0 + wn + c4;
         if (row >= a.M) continue;
         if (col + 3 < a.N) {
-            epi4<EPI>(a, partial, row, col, v);
+            epi4<EPI, H>(a, partial, row, col, v);
         } else {
-            if (col < a.N) epi1<EPI>(a, partial, row, col, v.x);
-            if (col + 1 < a.N) epi1<EPI>(a, partial, row, col + 1, v.y);
-            if (col + 2 < a.N) epi1<EPI>(a, partial, row, col + 2, v.z);
+            if (col < a.N) epi1<EPI, H>(a, partial, row, col, v.x);
+            if (col + 1 < a.N) epi1<EPI, H>(a, partial, row, col + 1, v.y);
+            if (col + 2 < a.N) epi1<EPI, H>(a, partial, row, col + 2, v.z);
         }
     }
 }
@@ -468,7 +463,7 @@ struct Shape {
     static constexpr int OCC = LDS_BYTES <= 80 * 1024 ? 2 : 1;  // workgroups per CU
 };
 
-template <int OP, int EPI, int MI, int NI>
+template <int OP, int EPI, int MI, int NI, class H>
 __global__ __launch_bounds__(NTHR, (Shape<MI, NI>::OCC)) void gemm_bf16_big_kernel(
     const GemmArgsH a, int tiles_m, int tiles_n, int kchunk, float* __restrict__ partial) {
     using SH = Shape<MI, NI>;
@@ -524,7 +519,7 @@ __global__ __launch_bounds__(NTHR, (Shape<MI, NI>::OCC)) void gemm_bf16_big_kern
 #pragma unroll
             for (int i = 0; i < MI; i++)
 #pragma unroll
-                for (int j = 0; j < NI; j++) acc[i][j] = mfma(af[i], bf[j], acc[i][j]);
+                for (int j = 0; j < NI; j++) acc[i][j] = H::mma(af[i], bf[j], acc[i][j]);
         }
     };
     using I0 = std::integral_constant<int, 0>;
@@ -589,18 +584,18 @@ __global__ __launch_bounds__(NTHR, (Shape<MI, NI>::OCC)) void gemm_bf16_big_kern
             const int row = m0 + wm + 32 * i + r, col = n0 + wn + c4;
             if (row >= a.M) continue;
             if (col + 3 < a.N) {
-                epi4<EPI>(a, partial, row, col, v);
+                epi4<EPI, H>(a, partial, row, col, v);
             } else {
-                if (col < a.N) epi1<EPI>(a, partial, row, col, v.x);
-                if (col + 1 < a.N) epi1<EPI>(a, partial, row, col + 1, v.y);
-                if (col + 2 < a.N) epi1<EPI>(a, partial, row, col + 2, v.z);
+                if (col < a.N) epi1<EPI, H>(a, partial, row, col, v.x);
+                if (col + 1 < a.N) epi1<EPI, H>(a, partial, row, col + 1, v.y);
+                if (col + 2 < a.N) epi1<EPI, H>(a, partial, row, col + 2, v.z);
             }
         }
         __builtin_amdgcn_wave_barrier();
     }
 }
 
-template <int EPI>
+template <int EPI, class H>
 __global__ __launch_bounds__(256) void splitk_reduce_bf16_kernel(const GemmArgsH a,
                                                                  const float* __restrict__ partial,
                                                                  int splits) {
@@ -618,7 +613,7 @@ __global__ __launch_bounds__(256) void splitk_reduce_bf16_kernel(const GemmArgsH
             s.z += p.z;
             s.w += p.w;
         }
-        epi4<EPI>(a, nullptr, (int)row, col, s);
+        epi4<EPI, H>(a, nullptr, (int)row, col, s);
     }
 }
 
@@ -673,72 +668,91 @@ PlanH plan_h(const GemmArgsH& a) {
     return best;
 }
 
-template <int OP, int EPI>
+template <int OP, int EPI, class H>
 hipError_t launch_h(hipStream_t s, const GemmArgsH& a, float* ws) {
     const int tm = cdiv(a.M, BM), tn = cdiv(a.N, BN);
-    hipLaunchKernelGGL((gemm_bf16_kernel<OP, EPI>), dim3(tm * tn, 1, 1), dim3(NTHR), 0, s, a, tm,
+    hipLaunchKernelGGL((gemm_bf16_kernel<OP, EPI, H>), dim3(tm * tn, 1, 1), dim3(NTHR), 0, s, a, tm,
                        tn, a.K > 0 ? a.K : 1, ws);
     return hipGetLastError();
 }
 
-template <int OP, int EPI>
+template <int OP, int EPI, class H>
 hipError_t launch_big(hipStream_t s, const GemmArgsH& a, int splits, float* ws) {
     const int tm = cdiv(a.M, 256), tn = cdiv(a.N, 256);
     const int chunk = splits > 1 ? split_chunk_h(a.K, splits) : (a.K > 0 ? a.K : 1);
     const int nz = splits > 1 ? cdiv(a.K, chunk) : 1;
-    hipLaunchKernelGGL((gemm_bf16_big_kernel<OP, EPI, 4, 4>), dim3(tm * tn, 1, nz), dim3(NTHR), 0,
+    hipLaunchKernelGGL((gemm_bf16_big_kernel<OP, EPI, 4, 4, H>), dim3(tm * tn, 1, nz), dim3(NTHR), 0,
                        s, a, tm, tn, chunk, ws);
     return hipGetLastError();
 }
 
+template <class H>
 hipError_t run_big(hipStream_t s, const GemmArgsH& a, int splits, float* ws) {
     if (splits > 1) {
         switch (a.op) {
-            case GEMM_NN: return launch_big<GEMM_NN, EPI_PARTIAL>(s, a, splits, ws);
-            case GEMM_TN: return launch_big<GEMM_TN, EPI_PARTIAL>(s, a, splits, ws);
+            case GEMM_NN: return launch_big<GEMM_NN, EPI_PARTIAL, H>(s, a, splits, ws);
+            case GEMM_TN: return launch_big<GEMM_TN, EPI_PARTIAL, H>(s, a, splits, ws);
             default: return hipErrorInvalidValue;
         }
     }
     switch (a.op) {
         case GEMM_NN:
             switch (a.epi) {
-                case EPI_STORE: return launch_big<GEMM_NN, EPI_STORE>(s, a, 1, ws);
-                case EPI_GELU_BWD: return launch_big<GEMM_NN, EPI_GELU_BWD>(s, a, 1, ws);
+                case EPI_STORE: return launch_big<GEMM_NN, EPI_STORE, H>(s, a, 1, ws);
+                case EPI_GELU_BWD: return launch_big<GEMM_NN, EPI_GELU_BWD, H>(s, a, 1, ws);
                 default: return hipErrorInvalidValue;
             }
         case GEMM_TN:
             switch (a.epi) {
-                case EPI_STORE: return launch_big<GEMM_TN, EPI_STORE>(s, a, 1, ws);
-                case EPI_ACCUM: return launch_big<GEMM_TN, EPI_ACCUM>(s, a, 1, ws);
+                case EPI_STORE: return launch_big<GEMM_TN, EPI_STORE, H>(s, a, 1, ws);
+                case EPI_ACCUM: return launch_big<GEMM_TN, EPI_ACCUM, H>(s, a, 1, ws);
                 default: return hipErrorInvalidValue;
             }
         default: return hipErrorInvalidValue;
     }
 }
 
+template <class H>
 hipError_t run_small(hipStream_t s, const GemmArgsH& a, float* ws) {
     switch (a.op) {
         case GEMM_NT:
             switch (a.epi) {
-                case EPI_STORE: return launch_h<GEMM_NT, EPI_STORE>(s, a, ws);
-                case EPI_RESID: return launch_h<GEMM_NT, EPI_RESID>(s, a, ws);
-                case EPI_GELU: return launch_h<GEMM_NT, EPI_GELU>(s, a, ws);
+                case EPI_STORE: return launch_h<GEMM_NT, EPI_STORE, H>(s, a, ws);
+                case EPI_RESID: return launch_h<GEMM_NT, EPI_RESID, H>(s, a, ws);
+                case EPI_GELU: return launch_h<GEMM_NT, EPI_GELU, H>(s, a, ws);
                 default: return hipErrorInvalidValue;
             }
         case GEMM_NN:
             switch (a.epi) {
-                case EPI_STORE: return launch_h<GEMM_NN, EPI_STORE>(s, a, ws);
-                case EPI_GELU_BWD: return launch_h<GEMM_NN, EPI_GELU_BWD>(s, a, ws);
+                case EPI_STORE: return launch_h<GEMM_NN, EPI_STORE, H>(s, a, ws);
+                case EPI_GELU_BWD: return launch_h<GEMM_NN, EPI_GELU_BWD, H>(s, a, ws);
                 default: return hipErrorInvalidValue;
             }
         case GEMM_TN:
             switch (a.epi) {
-                case EPI_STORE: return launch_h<GEMM_TN, EPI_STORE>(s, a, ws);
-                case EPI_ACCUM: return launch_h<GEMM_TN, EPI_ACCUM>(s, a, ws);
+                case EPI_STORE: return launch_h<GEMM_TN, EPI_STORE, H>(s, a, ws);
+                case EPI_ACCUM: return launch_h<GEMM_TN, EPI_ACCUM, H>(s, a, ws);
                 default: return hipErrorInvalidValue;
             }
         default: return hipErrorInvalidValue;
     }
+}
+
+template <class H>
+hipError_t run(hipStream_t s, const GemmArgsH& a, const PlanH& p, float* ws) {
+    if (!p.big) return run_small<H>(s, a, ws);
+    hipError_t e = run_big<H>(s, a, p.splits, ws);
+    if (e != hipSuccess || p.splits <= 1) return e;
+    const int nz = cdiv(a.K, split_chunk_h(a.K, p.splits));
+    const int64_t n4 = (int64_t)a.M * (a.N / 4);
+    const int blocks = (int)std::min<int64_t>((n4 + 255) / 256, 4096);
+    if (a.epi == EPI_ACCUM)
+        hipLaunchKernelGGL((splitk_reduce_bf16_kernel<EPI_ACCUM, H>), dim3(blocks), dim3(256), 0,
+                           s, a, ws, nz);
+    else
+        hipLaunchKernelGGL((splitk_reduce_bf16_kernel<EPI_STORE, H>), dim3(blocks), dim3(256), 0,
+                           s, a, ws, nz);
+    return hipGetLastError();
 }
 
 }  // namespace
@@ -766,22 +780,10 @@ hipError_t gemm_bf16(hipStream_t s, const GemmArgsH& a, float* ws, size_t ws_byt
         a.ldc < a.N)
         return hipErrorInvalidValue;
     PlanH p = plan_h(a);
-    if (!p.big) return run_small(s, a, ws);
     if (p.splits > 1 &&
         (size_t)cdiv(a.K, split_chunk_h(a.K, p.splits)) * a.M * a.N * sizeof(float) > ws_bytes)
         p.splits = 1;
-    hipError_t e = run_big(s, a, p.splits, ws);
-    if (e != hipSuccess || p.splits <= 1) return e;
-    const int nz = cdiv(a.K, split_chunk_h(a.K, p.splits));
-    const int64_t n4 = (int64_t)a.M * (a.N / 4);
-    const int blocks = (int)std::min<int64_t>((n4 + 255) / 256, 4096);
-    if (a.epi == EPI_ACCUM)
-        hipLaunchKernelGGL(splitk_reduce_bf16_kernel<EPI_ACCUM>, dim3(blocks), dim3(256), 0, s, a,
-                           ws, nz);
-    else
-        hipLaunchKernelGGL(splitk_reduce_bf16_kernel<EPI_STORE>, dim3(blocks), dim3(256), 0, s, a,
-                           ws, nz);
-    return hipGetLastError();
+    return a.f16 ? run<HF16>(s, a, p, ws) : run<HBF16>(s, a, p, ws);
 }
 
 }  // namespace gk

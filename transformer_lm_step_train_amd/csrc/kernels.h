@@ -37,11 +37,13 @@ struct GemmArgs {
     float* out2;        // EPI_GELU
 };
 
-// bf16 variant (mixed precision): A and B are bf16, accumulation fp32.  C is
-// bf16 (activations; EPI_STORE with out_f32 != 0 writes fp32) or fp32
-// (EPI_ACCUM: weight gradients).  bias is fp32, aux and out2 are bf16.
+// 16-bit variant (mixed precision): A and B are bf16 (f16 = 0) or fp16
+// (f16 = 1) bits, accumulation fp32.  C is 16-bit (activations; EPI_STORE
+// with out_f32 != 0 writes fp32) or fp32 (EPI_ACCUM: weight gradients).
+// bias is fp32, aux and out2 are 16-bit like A.
 struct GemmArgsH {
     int op, epi;
+    int f16;
     int M, N, K;
     const uint16_t* A;
     int64_t lda;
@@ -69,55 +71,57 @@ hipError_t gemm(hipStream_t s, const GemmArgs& a, float* workspace,
 // Forward writes out (B*T, C) and lse (B, NH, T) = log-sum-exp of each
 // scaled score row; backward reads dout and writes dqkv (B*T, 3C), using
 // dpre (B, NH, T) as scratch for rowsum(dout * out).
-// Activations are fp32, or bf16 bits when bf16 != 0; lse and D are fp32.
+// Activations are stored per dt (DT_F32, DT_BF16, DT_F16); lse and D fp32.
 hipError_t attention_forward(hipStream_t s, void* out, float* lse, const void* qkv, int B,
-                             int T, int C, int NH, int bf16);
+                             int T, int C, int NH, int dt);
 hipError_t attention_backward(hipStream_t s, void* dqkv, float* dpre, const void* dout,
                               const void* qkv, const void* out, const float* lse, int B,
-                              int T, int C, int NH, int bf16);
-// Mixed-precision attention on the bf16 matrix cores (all tensors bf16,
-// lse fp32).
-hipError_t attention_forward_bf16(hipStream_t s, uint16_t* out, float* lse, const uint16_t* qkv,
-                                  int B, int T, int C, int NH);
-hipError_t attention_backward_bf16(hipStream_t s, uint16_t* dqkv, float* D,
+                              int T, int C, int NH, int dt);
+// Mixed-precision attention on the 16-bit matrix cores (all tensors bf16 or
+// fp16 bits per dt, lse and D fp32).
+hipError_t attention_forward_half(hipStream_t s, uint16_t* out, float* lse, const uint16_t* qkv,
+                                  int B, int T, int C, int NH, int dt);
+hipError_t attention_backward_half(hipStream_t s, uint16_t* dqkv, float* D,
                                    const uint16_t* dout, const uint16_t* qkv,
                                    const uint16_t* out, const float* lse, int B, int T, int C,
-                                   int NH);
+                                   int NH, int dt);
 
 // ---- rotary position embedding ---------------------------------------------
-// Rotates the q and k slices of qkv (B*T rows of 3C, fp32 or bf16 bits) in
+// Rotates the q and k slices of qkv (B*T rows of 3C, stored per dt) in
 // place, dir = +1 (forward) or -1 (inverse, the backward).  cs: (T_table,
 // hs/2) float pairs (cos, sin) of t * 10000^(-2i/hs), T <= T_table.
 hipError_t rope_apply(hipStream_t s, void* qkv, const float* cs, int B, int T, int C, int NH,
-                      int dir, int bf16);
+                      int dir, int dt);
 
 // ---- layernorm ------------------------------------------------------------
-// Activations (out, inp, dres, dout) are fp32, or bf16 bits when bf16 != 0;
-// mean, rstd, weights and their gradients are always fp32.
+// Activations (out, inp, dres, dout) are stored per dt (DT_F32, DT_BF16,
+// DT_F16); mean, rstd, weights and their gradients are always fp32.
 hipError_t layernorm_forward(hipStream_t s, void* out, float* mean, float* rstd,
                              const void* inp, const float* w, const float* b, int N, int C,
-                             int bf16);
+                             int dt);
 // dres (+)= dx;  dw += sum dy*xhat, db += sum dy (two deterministic stages,
 // `partials` holds layernorm_partials_floats(N, C) floats).
 size_t layernorm_partials_floats(int N, int C);
 hipError_t layernorm_backward(hipStream_t s, void* dres, int accumulate, float* dw, float* db,
                               float* partials, const void* dout, const void* inp,
                               const float* w, const float* mean, const float* rstd, int N,
-                              int C, int bf16);
+                              int C, int dt);
 
 // ---- fused softmax + cross-entropy -----------------------------------------
 // logits (N, ldv) with V valid columns.  losses[n] = lse - logit[target];
 // logits are overwritten by (softmax - onehot) * dscale, columns V..ldv-1 by
 // 0.  A target outside [0, V) sets *flag |= 2 and zeroes that row.
-// logits fp32, or bf16 bits when bf16 != 0 (the statistics are fp32).
+// logits fp32, bf16 bits or fp16 per dt (the statistics are fp32).
+// gscale (device, NULL = none): the loss scale of the fp16 model, which
+// multiplies dscale.
 hipError_t softmax_ce(hipStream_t s, void* logits, float* losses,
                       const int32_t* targets, int N, int V, int ldv,
-                      float dscale, int* flag, int bf16);
+                      float dscale, const float* gscale, int* flag, int dt);
 // out[0] = mean of x[0..n) (deterministic order)
 // One inverse-CDF draw (coin in [0, 1)) from softmax of one logits row of V
 // values; writes the token to out (device).
 hipError_t sample_row(hipStream_t s, const void* logits, int V, float coin, int32_t* out,
-                      int bf16);
+                      int dt);
 hipError_t mean_reduce(hipStream_t s, float* out, const float* x, int n);
 
 // ---- embedding -------------------------------------------------------------
@@ -125,7 +129,7 @@ hipError_t mean_reduce(hipStream_t s, float* out, const float* x, int n);
 // gives a zero row.
 hipError_t encoder_forward(hipStream_t s, void* out, const int32_t* tok,
                            const float* wte, const float* wpe, int B, int T,
-                           int C, int V, int* flag, int bf16);
+                           int C, int V, int* flag, int dt);
 // keys (n_pow2 uint32) sorted ascending: (token << pos_bits) | position.
 // encoder_sort_prepare(n_pow2) must run once (per process) before sorts of
 // up to n_pow2 keys: it raises the kernel's LDS limit.
@@ -135,22 +139,33 @@ hipError_t encoder_sort(hipStream_t s, uint32_t* keys, const int32_t* tok,
 // dwte[tok] += dx rows (summed in position order), dwpe[t] += sum_b dx.
 hipError_t encoder_backward(hipStream_t s, float* dwte, float* dwpe,
                             const void* dx, const uint32_t* sorted_keys,
-                            int B, int T, int C, int V, int pos_bits, int bf16);
+                            int B, int T, int C, int V, int pos_bits, int dt);
 
 // ---- reductions and elementwise -------------------------------------------
 // db[n] += sum_m dy[m*ld + n]; `partials` holds bias_partials_floats(M, N).
 size_t bias_partials_floats(int M, int N);
 hipError_t bias_grad(hipStream_t s, float* db, float* partials,
-                     const void* dy, int M, int N, int64_t ld, int bf16);
+                     const void* dy, int M, int N, int64_t ld, int dt);
 // out0[c] += sum_r part[r*ncols + c] for c < split, out1[c-split] likewise
 // for c >= split; rows summed in a fixed order.
 hipError_t colsum_add(hipStream_t s, float* out0, float* out1, int split, const float* part,
                       int nrows, int ncols);
 hipError_t fill_zero(hipStream_t s, float* p, int64_t n);
-// shadow: optional bf16 copy of the updated parameters (NULL = none).
-hipError_t adamw(hipStream_t s, float* p, const float* g, float* m, float* v,
-                 uint16_t* shadow, int64_t n, float lr, float b1, float b2, float eps,
-                 float wd, float bc1, float bc2);
-hipError_t to_bf16(hipStream_t s, uint16_t* out, const float* in, int64_t n);
+// shadow: optional 16-bit copy of the updated parameters (NULL = none) of
+// storage type shadow_dt (DT_BF16 or DT_F16).  Loss scaling (fp16 model):
+// gscale (device, NULL = none) divides the gradients; *skip != 0 (device,
+// NULL = none) skips the whole sweep.
+hipError_t adamw(hipStream_t s, float* p, const float* g, float* m, float* v, void* shadow,
+                 int shadow_dt, int64_t n, float lr, float b1, float b2, float eps, float wd,
+                 float bc1, float bc2, const float* gscale, const int* skip);
+// out[i] = in[i] rounded to the 16-bit type dt (DT_BF16 or DT_F16).
+hipError_t to_half(hipStream_t s, void* out, const float* in, int64_t n, int dt);
+// *flag = 1 if any g[i] is inf or NaN (flag is only ever set).
+hipError_t check_finite(hipStream_t s, const float* g, int64_t n, int* flag);
+// One step of dynamic loss scaling (device state, one thread): a non-finite
+// step halves *scale (not below min_scale) and sets *skipped; `interval`
+// clean steps in a row double it; *found is cleared.
+hipError_t loss_scale_update(hipStream_t s, float* scale, int* good, int* found, int* skipped,
+                             int interval, float min_scale);
 
 }  // namespace gk

@@ -201,12 +201,12 @@ hipError_t ln_bwd_launch(hipStream_t s, T* dres, int accumulate, float* partials
 }  // namespace
 
 hipError_t layernorm_forward(hipStream_t s, void* out, float* mean, float* rstd, const void* inp,
-                             const float* w, const float* b, int N, int C, int bf16) {
+                             const float* w, const float* b, int N, int C, int dt) {
     if (N <= 0) return hipSuccess;
-    if (bf16)
-        return ln_fwd_launch<uint16_t>(s, (uint16_t*)out, mean, rstd, (const uint16_t*)inp, w, b,
-                                       N, C);
-    return ln_fwd_launch<float>(s, (float*)out, mean, rstd, (const float*)inp, w, b, N, C);
+    return by_dt(dt, [&](auto e) {
+        using E = decltype(e);
+        return ln_fwd_launch<E>(s, (E*)out, mean, rstd, (const E*)inp, w, b, N, C);
+    });
 }
 
 // Upper bound of the workgroup count over every row count up to N: at most
@@ -219,16 +219,15 @@ size_t layernorm_partials_floats(int N, int C) {
 hipError_t layernorm_backward(hipStream_t s, void* dres, int accumulate, float* dw, float* db,
                               float* partials, const void* dout, const void* inp,
                               const float* w, const float* mean, const float* rstd, int N,
-                              int C, int bf16) {
+                              int C, int dt) {
     if (N <= 0) return hipSuccess;
     const int rpb = ln_rows_per_block(N);
     const int nb = (N + rpb - 1) / rpb;
-    hipError_t e =
-        bf16 ? ln_bwd_launch<uint16_t>(s, (uint16_t*)dres, accumulate, partials,
-                                       (const uint16_t*)dout, (const uint16_t*)inp, w, mean, rstd,
-                                       N, C, rpb, nb)
-             : ln_bwd_launch<float>(s, (float*)dres, accumulate, partials, (const float*)dout,
-                                    (const float*)inp, w, mean, rstd, N, C, rpb, nb);
+    hipError_t e = by_dt(dt, [&](auto x) {
+        using E = decltype(x);
+        return ln_bwd_launch<E>(s, (E*)dres, accumulate, partials, (const E*)dout,
+                                (const E*)inp, w, mean, rstd, N, C, rpb, nb);
+    });
     if (e != hipSuccess) return e;
     return colsum_add(s, dw, db, C, partials, nb, 2 * C);
 }

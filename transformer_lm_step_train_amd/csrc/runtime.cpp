@@ -21,6 +21,7 @@
 #include <vector>
 
 #include "../../include/gpt2.h"
+#include "dtype.h"
 #include "kernels.h"
 
 namespace {
@@ -86,7 +87,8 @@ int check_config(const gpt2_config* c) {
     if ((int64_t)c->batch_size * c->seq_len > 32768)
         return fail(GPT2_EINVAL, "batch_size*seq_len > 32768 not supported");
     if (c->vocab_size > 65536) return fail(GPT2_EINVAL, "vocab_size > 65536 not supported");
-    if (c->precision != GPT2_FP32 && c->precision != GPT2_BF16_MIXED)
+    if (c->precision != GPT2_FP32 && c->precision != GPT2_BF16_MIXED &&
+        c->precision != GPT2_F16_MIXED)
         return fail(GPT2_EINVAL, "unknown precision %d", c->precision);
     if (c->rope != 0 && c->rope != 1) return fail(GPT2_EINVAL, "rope must be 0 or 1");
     return GPT2_OK;
@@ -94,10 +96,30 @@ int check_config(const gpt2_config* c) {
 
 inline size_t align256(size_t x) { return (x + 255) & ~size_t(255); }
 
+// bf16 is the top half of an fp32.
+float bf16_bits_to_float(uint16_t h) {
+    const uint32_t u = (uint32_t)h << 16;
+    float f;
+    std::memcpy(&f, &u, 4);
+    return f;
+}
+
+// IEEE binary16: sign, 5-bit exponent (bias 15), 10-bit fraction; exponent 0
+// holds zero and the subnormals (fraction * 2^-24), 31 holds inf and NaN.
+float half_bits_to_float(uint16_t h) {
+    const int sign = h >> 15, e = (h >> 10) & 31, f = h & 1023;
+    float v;
+    if (e == 0) v = std::ldexp((float)f, -24);
+    else if (e == 31) v = f ? NAN : INFINITY;
+    else v = std::ldexp((float)(1024 + f), e - 25);
+    return sign ? -v : v;
+}
+
 // Byte offsets of every sub-buffer inside the one device allocation.
 struct Layout {
     int L, C, NH, V, Vp, maxT, Bmax, Tmax, M, pos_bits, n_pow2;
-    int bf16;   // activations (and the matmul weight copy) in bf16
+    int dt;     // activation storage: DT_F32, DT_BF16 or DT_F16
+    int half;   // 16-bit activations and a 16-bit copy of the matmul weights
     int rope;   // rotary position embedding instead of the wpe table
     size_t es;  // bytes per activation element
     int64_t nparams, poff[16], psize[16];
@@ -109,9 +131,12 @@ struct Layout {
     size_t gemm_ws_bytes, total;
 
     void build(const gpt2_config* c) {
-        bf16 = c->precision == GPT2_BF16_MIXED;
+        dt = c->precision == GPT2_BF16_MIXED ? DT_BF16
+             : c->precision == GPT2_F16_MIXED  ? DT_F16
+                                               : DT_F32;
+        half = dt != DT_F32;
         rope = c->rope;
-        es = bf16 ? 2 : 4;
+        es = half ? 2 : 4;
         L = c->num_layers;
         C = c->channels;
         NH = c->num_heads;
@@ -141,7 +166,7 @@ struct Layout {
         grads = take(nparams * f);
         m = take(nparams * f);
         v = take(nparams * f);
-        shadow = bf16 ? take(nparams * 2) : 0;
+        shadow = half ? take(nparams * 2) : 0;
         encoded = take(MC * es);
         ln1 = take(L * MC * es);
         ln1_mean = take((size_t)L * M * f);
@@ -171,7 +196,7 @@ struct Layout {
         // the largest split-K workspace over every matmul of the step
         gemm_ws_bytes = 0;
         auto need = [&](int op, int epi, int m, int n, int k) {
-            const size_t b = bf16 ? gk::gemm_bf16_workspace_bytes(op, epi, m, n, k)
+            const size_t b = half ? gk::gemm_bf16_workspace_bytes(op, epi, m, n, k)
                                   : gk::gemm_workspace_bytes(op, epi, m, n, k);
             gemm_ws_bytes = std::max(gemm_ws_bytes, b);
         };
@@ -231,15 +256,22 @@ struct gpt2_model {
         return reinterpret_cast<X*>(base + off);
     }
     float* P(int i) const { return at<float>(lay.params) + lay.poff[i]; }
-    // weight operand of the matmuls: the fp32 master, or its bf16 copy
+    // weight operand of the matmuls: the fp32 master, or its 16-bit copy
     const void* W(int i) const {
-        return lay.bf16 ? (const void*)(at<uint16_t>(lay.shadow) + lay.poff[i]) : (const void*)P(i);
+        return lay.half ? (const void*)(at<uint16_t>(lay.shadow) + lay.poff[i]) : (const void*)P(i);
     }
     // activation buffer at byte offset `off`, element `idx`
     char* A(size_t off, size_t idx = 0) const { return base + off + idx * lay.es; }
     float* G(int i) const { return at<float>(lay.grads) + lay.poff[i]; }
     int* flag() const { return at<int>(lay.scalars + 4); }
     int32_t* drawn() const { return at<int32_t>(lay.scalars + 8); }
+    // dynamic loss scaling of the fp16 model: scale, clean steps in a row,
+    // non-finite gradient found this step, last update skipped
+    float* lscale() const { return at<float>(lay.scalars + 12); }
+    int* lgood() const { return at<int>(lay.scalars + 16); }
+    int* lfound() const { return at<int>(lay.scalars + 20); }
+    int* lskipped() const { return at<int>(lay.scalars + 24); }
+    int growth_interval = 2000;
     float* dloss() const { return at<float>(lay.scalars); }
 };
 
@@ -338,8 +370,9 @@ int run_gemm(gpt2_model* md, const Mm& x) {
                          (x.epi == gk::EPI_ACCUM ? 8.0 : es) * (double)x.M * x.N;
     float* ws = md->at<float>(md->lay.gemm_ws);
     const size_t wsb = md->lay.gemm_ws_bytes;
-    if (md->lay.bf16) {
+    if (md->lay.half) {
         gk::GemmArgsH a{};
+        a.f16 = md->lay.dt == DT_F16;
         a.op = x.op;
         a.epi = x.epi;
         a.M = x.M;
@@ -390,7 +423,7 @@ int run_gemm(gpt2_model* md, const Mm& x) {
 int forward_impl(gpt2_model* md, const int32_t* tok, const int32_t* tgt, int B, int T) {
     const Layout& y = md->lay;
     const int L = y.L, C = y.C, NH = y.NH, V = y.V, M = B * T;
-    const int h = y.bf16;
+    const int h = y.dt;
     const size_t MC = (size_t)y.M * C;  // per-layer capacity stride, elements
     const double es = (double)y.es;
     hipStream_t s = md->stream;
@@ -464,7 +497,8 @@ int forward_impl(gpt2_model* md, const int32_t* tok, const int32_t* tgt, int B, 
     if (tgt) {
         float* losses = md->at<float>(y.losses);
         LAUNCH(md, GPT2_KC_SOFTMAX_CE, 0, es * 2.0 * M * (double)V + 8.0 * M,
-               gk::softmax_ce(s, logits, losses, tgt, M, V, y.Vp, 1.0f / M, md->flag(), h));
+               gk::softmax_ce(s, logits, losses, tgt, M, V, y.Vp, 1.0f / M,
+                              y.dt == DT_F16 ? md->lscale() : nullptr, md->flag(), h));
         LAUNCH(md, GPT2_KC_OTHER, 0, 4.0 * M, gk::mean_reduce(s, md->dloss(), losses, M));
         const int np2 = 1 << ceil_log2(M);
         LAUNCH(md, GPT2_KC_OTHER, 0, 4.0 * M + 4.0 * np2,
@@ -503,7 +537,7 @@ int check_bt(gpt2_model* md, int B, int T) {
 int backward_impl(gpt2_model* md) {
     const Layout& y = md->lay;
     const int L = y.L, C = y.C, NH = y.NH, V = y.V, B = md->B, T = md->T, M = B * T;
-    const int h = y.bf16;
+    const int h = y.dt;
     const size_t MC = (size_t)y.M * C;
     const size_t wes = y.es;  // bytes per weight element of the matmul copy
     const double es = (double)y.es;
@@ -717,6 +751,13 @@ int gpt2_create(const gpt2_config* cfg, const gpt2_allocator* alloc, void* hip_s
         rc = hip_check(e, "zero arenas");
         if (rc == GPT2_OK) rc = hip_check(hipStreamSynchronize(md->stream), "synchronize");
     }
+    if (rc == GPT2_OK && md->lay.dt == DT_F16) {
+        const float s0 = 65536.0f;  // 2^16; halves on overflow, doubles after 2000 clean steps
+        const int32_t st[4] = {0, 0, 0, 0};
+        rc = hip_check(hipMemcpy(md->lscale(), &s0, 4, hipMemcpyHostToDevice), "scale init");
+        if (rc == GPT2_OK)
+            rc = hip_check(hipMemcpy(md->lgood(), st, 12, hipMemcpyHostToDevice), "scale init");
+    }
     if (rc != GPT2_OK) {
         std::string msg = g_err;
         gpt2_destroy(md);
@@ -744,10 +785,10 @@ int gpt2_copy_params(gpt2_model* md, float* dst, const float* src) {
     if (dst)
         return hip_check(hipMemcpy(dst, md->P(0), bytes, hipMemcpyDeviceToHost), "copy params");
     TRY(hip_check(hipMemcpy(md->P(0), src, bytes, hipMemcpyHostToDevice), "copy params"));
-    if (md->lay.bf16) {
-        TRY(hip_check(gk::to_bf16(md->stream, md->at<uint16_t>(md->lay.shadow), md->P(0),
-                                  md->lay.nparams),
-                      "bf16 weight copy"));
+    if (md->lay.half) {
+        TRY(hip_check(gk::to_half(md->stream, md->at<uint16_t>(md->lay.shadow), md->P(0),
+                                  md->lay.nparams, md->lay.dt),
+                      "16-bit weight copy"));
         TRY(hip_check(hipStreamSynchronize(md->stream), "synchronize"));
     }
     return GPT2_OK;
@@ -756,6 +797,16 @@ int gpt2_copy_params(gpt2_model* md, float* dst, const float* src) {
 int gpt2_copy_grads(gpt2_model* md, float* dst) {
     if (!valid_model(md) || !dst) return fail(GPT2_EINVAL, "NULL argument");
     TRY(hip_check(hipStreamSynchronize(md->stream), "synchronize"));
+    if (md->lay.dt == DT_F16) {  // the arena holds scale * gradient
+        float sc;
+        TRY(hip_check(hipMemcpy(&sc, md->lscale(), 4, hipMemcpyDeviceToHost), "scale readback"));
+        TRY(hip_check(hipMemcpy(dst, md->G(0), md->lay.nparams * sizeof(float),
+                                hipMemcpyDeviceToHost),
+                      "copy grads"));
+        const float inv = 1.0f / sc;
+        for (int64_t i = 0; i < md->lay.nparams; i++) dst[i] *= inv;
+        return GPT2_OK;
+    }
     return hip_check(hipMemcpy(dst, md->G(0), md->lay.nparams * sizeof(float),
                                hipMemcpyDeviceToHost),
                      "copy grads");
@@ -824,7 +875,7 @@ int gpt2_copy_activation(gpt2_model* md, const char* name, int layer, float* dst
             return hip_check(hipMemcpy(dst, src, n * sizeof(float), hipMemcpyDeviceToHost),
                              "copy activation");
         }
-        // bf16: copy the bits, widen on the host (bf16 is the top half of fp32)
+        // 16-bit: copy the bits, widen on the host
         std::vector<uint16_t> tmp((size_t)n);
         if (logits)
             TRY(hip_check(hipMemcpy2D(tmp.data(), y.V * 2, src, y.Vp * 2, y.V * 2, M,
@@ -833,10 +884,9 @@ int gpt2_copy_activation(gpt2_model* md, const char* name, int layer, float* dst
         else
             TRY(hip_check(hipMemcpy(tmp.data(), src, n * 2, hipMemcpyDeviceToHost),
                           "copy activation"));
-        for (int64_t i = 0; i < n; i++) {
-            const uint32_t u = (uint32_t)tmp[(size_t)i] << 16;
-            std::memcpy(dst + i, &u, 4);
-        }
+        for (int64_t i = 0; i < n; i++)
+            dst[i] = y.dt == DT_F16 ? half_bits_to_float(tmp[(size_t)i])
+                                    : bf16_bits_to_float(tmp[(size_t)i]);
         return GPT2_OK;
     }
     return fail(GPT2_EINVAL, "unknown activation name '%s'", name);
@@ -895,7 +945,7 @@ int gpt2_sample(gpt2_model* md, int b, int t, float coin, int32_t* token) {
     const Layout& y = md->lay;
     const char* row = md->A(y.logits, ((size_t)b * md->T + t) * y.Vp);
     LAUNCH(md, GPT2_KC_SOFTMAX_CE, 0, y.es * (double)y.V * 2.0 + 4.0,
-           gk::sample_row(md->stream, row, y.V, coin, md->drawn(), y.bf16));
+           gk::sample_row(md->stream, row, y.V, coin, md->drawn(), y.dt));
     TRY(hip_check(hipMemcpyAsync(md->h_scal + 2, md->drawn(), 4, hipMemcpyDeviceToHost,
                                  md->stream),
                   "token readback"));
@@ -942,11 +992,46 @@ int gpt2_update(gpt2_model* md, float lr, float beta1, float beta2, float eps,
     const float bc1 = (float)(1.0 - std::pow((double)beta1, (double)step));
     const float bc2 = (float)(1.0 - std::pow((double)beta2, (double)step));
     const int64_t n = md->lay.nparams;
-    LAUNCH(md, GPT2_KC_ADAMW, 0, (md->lay.bf16 ? 30.0 : 28.0) * n,
+    const bool scaled = md->lay.dt == DT_F16;
+    if (scaled)  // a non-finite (overflowed) gradient skips the whole update
+        LAUNCH(md, GPT2_KC_ADAMW, 0, 4.0 * n,
+               gk::check_finite(md->stream, md->G(0), n, md->lfound()));
+    LAUNCH(md, GPT2_KC_ADAMW, 0, (md->lay.half ? 30.0 : 28.0) * n,
            gk::adamw(md->stream, md->P(0), md->G(0), md->at<float>(md->lay.m),
                      md->at<float>(md->lay.v),
-                     md->lay.bf16 ? md->at<uint16_t>(md->lay.shadow) : nullptr, n, lr, beta1,
-                     beta2, eps, weight_decay, bc1, bc2));
+                     md->lay.half ? md->at<uint16_t>(md->lay.shadow) : nullptr, md->lay.dt, n,
+                     lr, beta1, beta2, eps, weight_decay, bc1, bc2,
+                     scaled ? md->lscale() : nullptr, scaled ? md->lfound() : nullptr));
+    if (scaled)
+        LAUNCH(md, GPT2_KC_OTHER, 0, 16.0,
+               gk::loss_scale_update(md->stream, md->lscale(), md->lgood(), md->lfound(),
+                                     md->lskipped(), md->growth_interval, 1.0f));
+    return GPT2_OK;
+}
+
+int gpt2_set_loss_scale(gpt2_model* md, float scale, int growth_interval) {
+    if (!valid_model(md)) return fail(GPT2_EINVAL, "model is NULL");
+    if (md->lay.dt != DT_F16) return fail(GPT2_EINVAL, "loss scaling applies to the fp16 model");
+    if (!(scale >= 1.0f && scale < INFINITY) || growth_interval < 1)
+        return fail(GPT2_EINVAL, "scale must be finite and >= 1, growth_interval >= 1");
+    const int32_t st[4] = {0, 0, 0, 0};
+    TRY(hip_check(hipStreamSynchronize(md->stream), "synchronize"));
+    TRY(hip_check(hipMemcpy(md->lscale(), &scale, 4, hipMemcpyHostToDevice), "scale upload"));
+    TRY(hip_check(hipMemcpy(md->lgood(), st, 12, hipMemcpyHostToDevice), "scale state"));
+    md->growth_interval = growth_interval;
+    return GPT2_OK;
+}
+
+int gpt2_get_loss_scale(gpt2_model* md, float* scale, int* last_update_skipped) {
+    if (!valid_model(md)) return fail(GPT2_EINVAL, "model is NULL");
+    if (md->lay.dt != DT_F16) return fail(GPT2_EINVAL, "loss scaling applies to the fp16 model");
+    TRY(hip_check(hipStreamSynchronize(md->stream), "synchronize"));
+    float sc;
+    int sk;
+    TRY(hip_check(hipMemcpy(&sc, md->lscale(), 4, hipMemcpyDeviceToHost), "scale readback"));
+    TRY(hip_check(hipMemcpy(&sk, md->lskipped(), 4, hipMemcpyDeviceToHost), "scale readback"));
+    if (scale) *scale = sc;
+    if (last_update_skipped) *last_update_skipped = sk;
     return GPT2_OK;
 }
 

@@ -46,9 +46,11 @@ __global__ __launch_bounds__(NT) void softmax_ce_kernel(T* __restrict__ logits,
                                                         float* __restrict__ losses,
                                                         const int32_t* __restrict__ targets,
                                                         int V, int ldv, float dscale,
+                                                        const float* __restrict__ gscale,
                                                         int* __restrict__ flag) {
     __shared__ float sh[NT / 64];
     const int64_t row = blockIdx.x;
+    if (gscale) dscale *= *gscale;  // loss scaling of the fp16 model
     T* z = logits + row * ldv;
     const int V4 = ldv >> 2;
     const int tgt = targets[row];
@@ -101,24 +103,24 @@ __global__ __launch_bounds__(NT) void softmax_ce_kernel(T* __restrict__ logits,
 
 template <int NT, int NJ, class T>
 hipError_t launch_ce(hipStream_t s, T* logits, float* losses, const int32_t* targets, int N,
-                     int V, int ldv, float dscale, int* flag) {
+                     int V, int ldv, float dscale, const float* gscale, int* flag) {
     hipLaunchKernelGGL((softmax_ce_kernel<NT, NJ, T>), dim3(N), dim3(NT), 0, s, logits, losses,
-                       targets, V, ldv, dscale, flag);
+                       targets, V, ldv, dscale, gscale, flag);
     return hipGetLastError();
 }
 
 template <class T>
 hipError_t softmax_ce_t(hipStream_t s, T* logits, float* losses, const int32_t* targets, int N,
-                        int V, int ldv, float dscale, int* flag) {
+                        int V, int ldv, float dscale, const float* gs, int* flag) {
     const int V4 = ldv / 4;
-    if (V4 <= 256) return launch_ce<256, 1>(s, logits, losses, targets, N, V, ldv, dscale, flag);
+    if (V4 <= 256) return launch_ce<256, 1>(s, logits, losses, targets, N, V, ldv, dscale, gs, flag);
     const int nj = (V4 + 1023) / 1024;
-    if (nj <= 1) return launch_ce<1024, 1>(s, logits, losses, targets, N, V, ldv, dscale, flag);
-    if (nj <= 2) return launch_ce<1024, 2>(s, logits, losses, targets, N, V, ldv, dscale, flag);
-    if (nj <= 4) return launch_ce<1024, 4>(s, logits, losses, targets, N, V, ldv, dscale, flag);
-    if (nj <= 8) return launch_ce<1024, 8>(s, logits, losses, targets, N, V, ldv, dscale, flag);
-    if (nj <= 13) return launch_ce<1024, 13>(s, logits, losses, targets, N, V, ldv, dscale, flag);
-    if (nj <= 16) return launch_ce<1024, 16>(s, logits, losses, targets, N, V, ldv, dscale, flag);
+    if (nj <= 1) return launch_ce<1024, 1>(s, logits, losses, targets, N, V, ldv, dscale, gs, flag);
+    if (nj <= 2) return launch_ce<1024, 2>(s, logits, losses, targets, N, V, ldv, dscale, gs, flag);
+    if (nj <= 4) return launch_ce<1024, 4>(s, logits, losses, targets, N, V, ldv, dscale, gs, flag);
+    if (nj <= 8) return launch_ce<1024, 8>(s, logits, losses, targets, N, V, ldv, dscale, gs, flag);
+    if (nj <= 13) return launch_ce<1024, 13>(s, logits, losses, targets, N, V, ldv, dscale, gs, flag);
+    if (nj <= 16) return launch_ce<1024, 16>(s, logits, losses, targets, N, V, ldv, dscale, gs, flag);
     return hipErrorInvalidValue;
 }
 
@@ -187,24 +189,24 @@ __global__ __launch_bounds__(1024) void sample_kernel(const T* __restrict__ z, i
 }  // namespace
 
 hipError_t sample_row(hipStream_t s, const void* logits, int V, float coin, int32_t* out,
-                      int bf16) {
+                      int dt) {
     if (V <= 0) return hipErrorInvalidValue;
-    if (bf16)
-        hipLaunchKernelGGL(sample_kernel<uint16_t>, dim3(1), dim3(1024), 0, s,
-                           (const uint16_t*)logits, V, coin, out);
-    else
-        hipLaunchKernelGGL(sample_kernel<float>, dim3(1), dim3(1024), 0, s, (const float*)logits,
-                           V, coin, out);
-    return hipGetLastError();
+    return by_dt(dt, [&](auto e) {
+        using E = decltype(e);
+        hipLaunchKernelGGL(sample_kernel<E>, dim3(1), dim3(1024), 0, s, (const E*)logits, V, coin,
+                           out);
+        return hipGetLastError();
+    });
 }
 
 hipError_t softmax_ce(hipStream_t s, void* logits, float* losses, const int32_t* targets,
-                      int N, int V, int ldv, float dscale, int* flag, int bf16) {
+                      int N, int V, int ldv, float dscale, const float* gscale, int* flag,
+                      int dt) {
     if (N <= 0) return hipSuccess;
-    if (bf16)
-        return softmax_ce_t<uint16_t>(s, (uint16_t*)logits, losses, targets, N, V, ldv, dscale,
-                                      flag);
-    return softmax_ce_t<float>(s, (float*)logits, losses, targets, N, V, ldv, dscale, flag);
+    return by_dt(dt, [&](auto e) {
+        using E = decltype(e);
+        return softmax_ce_t<E>(s, (E*)logits, losses, targets, N, V, ldv, dscale, gscale, flag);
+    });
 }
 
 hipError_t mean_reduce(hipStream_t s, float* out, const float* x, int n) {

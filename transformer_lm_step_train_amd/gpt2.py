@@ -20,7 +20,7 @@ HERE = os.path.dirname(os.path.abspath(__file__))
 LIB_PATH = os.path.join(HERE, "libgpt2_hip.so")
 
 GPT2_OK, GPT2_EINVAL, GPT2_ERANGE, GPT2_ESTATE, GPT2_ENOMEM, GPT2_EDEVICE = 0, -1, -2, -3, -4, -5
-GPT2_FP32, GPT2_BF16_MIXED = 0, 1
+GPT2_FP32, GPT2_BF16_MIXED, GPT2_F16_MIXED = 0, 1, 2
 KC_GEMM, KC_ATTENTION, KC_LAYERNORM, KC_SOFTMAX_CE, KC_ADAMW, KC_OTHER = range(6)
 KC_NAMES = ["gemm", "attention", "layernorm", "softmax_ce", "adamw", "other"]
 
@@ -86,6 +86,8 @@ def _load():
         "gpt2_loader_next": (_c.c_int, [_vp, _vp, _vp]),
         "gpt2_loader_reset": (_c.c_int, [_vp]),
         "gpt2_loader_close": (None, [_vp]),
+        "gpt2_set_loss_scale": (_c.c_int, [_vp, _c.c_float, _c.c_int]),
+        "gpt2_get_loss_scale": (_c.c_int, [_vp, P(_c.c_float), P(_c.c_int)]),
         "gpt2_zero_grad": (_c.c_int, [_vp]),
         "gpt2_backward": (_c.c_int, [_vp]),
         "gpt2_update": (_c.c_int, [_vp] + [_c.c_float] * 5 + [_c.c_int]),
@@ -383,6 +385,15 @@ class Model:
         c = np.ascontiguousarray(coins, dtype=np.float32)
         gpt2_generate(self.h, tok, len(prompt), n, c)
         return tok
+
+    def set_loss_scale(self, scale, growth_interval=2000):
+        _check(lib.gpt2_set_loss_scale(self.h, scale, growth_interval))
+
+    def loss_scale(self):
+        """(scale, last update skipped) of the fp16 model."""
+        sc, sk = _c.c_float(0.0), _c.c_int(0)
+        _check(lib.gpt2_get_loss_scale(self.h, _c.byref(sc), _c.byref(sk)))
+        return sc.value, bool(sk.value)
 
     def zero_grad(self):
         gpt2_zero_grad(self.h)
