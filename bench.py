@@ -43,6 +43,14 @@ def parse():
     return ap.parse_args()
 
 
+def source_hash():
+    """SHA-256 of the fp32 matmul kernel's sources (kernel and its helpers)."""
+    h = hashlib.sha256()
+    for f in ("gemm.hip", "common.h"):
+        h.update(open(os.path.join(ROOT, "transformer_lm_step_train_amd", "csrc", f), "rb").read())
+    return h.hexdigest()
+
+
 def measured_traffic(half):
     """HBM bytes per matmul launch from the committed rocprofv3 FETCH_SIZE /
     WRITE_SIZE summary, or None if the matmul source has changed since the
@@ -51,8 +59,7 @@ def measured_traffic(half):
     if half or not os.path.exists(path):
         return None
     rec = json.load(open(path))
-    src = os.path.join(ROOT, "transformer_lm_step_train_amd", "csrc", "gemm.hip")
-    if hashlib.sha256(open(src, "rb").read()).hexdigest() != rec["source_sha256_gemm_hip"]:
+    if source_hash() != rec.get("source_sha256"):
         return None
     return round(rec["hbm_bytes_per_launch"])
 
