@@ -78,10 +78,62 @@ def cpu_baseline(c, params, tok, tgt):
     o.update(step=1, lr=1e-4)
     dt = time.perf_counter() - t0
     o.close()
-    return {"value": round(c["T"] / dt, 2), "unit": "tokens/s", "cores": cores,
-            "kind": "oracle",
-            "sample": f"1 training step (fwd+bwd+AdamW) on 1 sequence of T={c['T']} "
-                      f"(1/{c['B']} of the batch), {dt:.2f} s"}
+    out = {"value": round(c["T"] / dt, 2), "unit": "tokens/s", "cores": cores,
+           "kind": "oracle",
+           "sample": f"1 training step (fwd+bwd+AdamW) on 1 sequence of T={c['T']} "
+                     f"(1/{c['B']} of the batch), {dt:.2f} s"}
+    # The pages' own run: 124M at B=4, T=64 with 8 threads, printed at
+    # 1.29-1.45 s per step on an M3 Max (ujoy.net, section "训练过程").
+    import oracle as _o
+    from transformer_lm_step_train_amd import synth
+    p4 = synth.CONFIGS["gpt2_124m_b4t64"]
+    lb = _o.lib("f32")
+    lb.oracle_set_threads(8)
+    o = OracleModel(p4["L"], p4["C"], p4["NH"], p4["V"], p4["maxT"], p4["B"], p4["T"])
+    o.params[:] = params
+    t4, g4 = synth.token_stream(p4["B"], p4["T"], p4["V"])
+    times = []
+    for s in range(1, 4):  # 1 warm-up + 2 timed
+        t0 = time.perf_counter()
+        o.forward(t4, g4)
+        o.zero_grad()
+        o.backward()
+        o.update(step=s, lr=1e-4)
+        times.append(time.perf_counter() - t0)
+    o.close()
+    lb.oracle_set_threads(cores)
+    out["pages_shape"] = {"workload": "GPT-2 124M, B=4 T=64 (the pages' run)", "threads": 8,
+                          "s_per_step": round(sum(times[1:]) / 2, 3),
+                          "page_m3max_s_per_step": [1.289, 1.452]}
+    return out
+
+
+def pages_shape_gpu(params):
+    """The GPU step at the pages' run shape (124M, B=4, T=64, fp32)."""
+    from transformer_lm_step_train_amd import gpt2, synth
+    import torch
+    p4 = synth.CONFIGS["gpt2_124m_b4t64"]
+    m = gpt2.Model(p4["L"], p4["C"], p4["NH"], p4["V"], p4["maxT"], p4["B"], p4["T"])
+    m.set_params(params)
+    tok, tgt = synth.token_stream(p4["B"], p4["T"], p4["V"])
+    dtok = torch.tensor(tok, dtype=torch.int32, device="cuda")
+    dtgt = torch.tensor(tgt, dtype=torch.int32, device="cuda")
+    def one(s):
+        m.forward_device(dtok, dtgt)
+        m.zero_grad()
+        m.backward()
+        m.update(step=s, lr=1e-4)
+    for s in range(1, 6):
+        one(s)
+    m.synchronize()
+    t0 = time.perf_counter()
+    for s in range(6, 26):
+        one(s)
+    m.synchronize()
+    ms = (time.perf_counter() - t0) / 20 * 1000.0
+    m.close()
+    return {"workload": "GPT-2 124M, B=4 T=64 (the pages' run), fp32", "ms_per_step": round(ms, 3),
+            "tokens_per_s": round(256 / ms * 1000.0, 1)}
 
 
 def main():
@@ -210,6 +262,7 @@ def main():
     }
     if not args.no_cpu_baseline and not half:
         out["cpu_baseline"] = cpu_baseline(c, params, tok, tgt)
+        out["pages_shape_gpu"] = pages_shape_gpu(params)
     print(json.dumps(out), flush=True)
 
 

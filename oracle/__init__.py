@@ -66,6 +66,8 @@ def _lib(precision: str):
     lib.oracle_backward.restype = _int
     lib.oracle_backward.argtypes = [_vp]
     lib.oracle_update.argtypes = [_vp] + [ctypes.c_double] * 5 + [_int]
+    lib.oracle_set_threads.restype = None
+    lib.oracle_set_threads.argtypes = [_int]
     lib.oracle_loss_scale_step.restype = _int
     lib.oracle_loss_scale_step.argtypes = [_vp, _vp, _int, _int, ctypes.c_double]
     lib.oracle_sample.restype = _int

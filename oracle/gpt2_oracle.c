@@ -55,6 +55,15 @@ typedef float real;
 
 EXPORT int oracle_real_size(void) { return (int)sizeof(real); }
 
+/* OpenMP threads for the following calls (timing runs only; results do
+ * not depend on the count). */
+#ifdef _OPENMP
+#include <omp.h>
+EXPORT void oracle_set_threads(int n) { omp_set_num_threads(n > 0 ? n : 1); }
+#else
+EXPORT void oracle_set_threads(int n) { (void)n; }
+#endif
+
 /* ------------------------------------------------------------------------ */
 /* Layer definitions                                                         */
 /* ------------------------------------------------------------------------ */

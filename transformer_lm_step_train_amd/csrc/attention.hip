@@ -417,10 +417,10 @@ __global__ __launch_bounds__(256, 2) void attn_bwd_dkdv_kernel(
             x = Act<E>::ld(qbase + C + (int64_t)key * ld + g * HALF + s);
             y = Act<E>::ld(qbase + 2 * C + (int64_t)key * ld + g * HALF + s);
         }
-        kr[s] = x.x;
-        kr[s + 1] = x.y;
-        kr[s + 2] = x.z;
-        kr[s + 3] = x.w;
+        kr[s] = x.x * qscale;  // the score scale folded into the key once
+        kr[s + 1] = x.y * qscale;
+        kr[s + 2] = x.z * qscale;
+        kr[s + 3] = x.w * qscale;
         vr[s] = y.x;
         vr[s + 1] = y.y;
         vr[s + 2] = y.z;
@@ -474,10 +474,10 @@ __global__ __launch_bounds__(256, 2) void attn_bwd_dkdv_kernel(
             for (int s = 0; s < HALF; s += 4) {
                 const float4 qf = ld4(qrow + s);
                 const float4 df = ld4(drow + s);
-                sc = mfma(qf.x * qscale, kr[s], sc);
-                sc = mfma(qf.y * qscale, kr[s + 1], sc);
-                sc = mfma(qf.z * qscale, kr[s + 2], sc);
-                sc = mfma(qf.w * qscale, kr[s + 3], sc);
+                sc = mfma(qf.x, kr[s], sc);
+                sc = mfma(qf.y, kr[s + 1], sc);
+                sc = mfma(qf.z, kr[s + 2], sc);
+                sc = mfma(qf.w, kr[s + 3], sc);
                 dp = mfma(df.x, vr[s], dp);
                 dp = mfma(df.y, vr[s + 1], dp);
                 dp = mfma(df.z, vr[s + 2], dp);
