@@ -128,6 +128,65 @@ struct Act<_Float16> {
     static __device__ __forceinline__ void st1(_Float16* p, float v) { *p = (_Float16)v; }
 };
 
+// The same four-element accesses through a buffer resource: the row base
+// and byte size sit in scalar registers and each lane supplies one 32-bit
+// byte offset (plus a uniform one), so a thread's many loads of one row
+// share a single address register.  Callers keep every access inside the
+// size they give the resource.
+typedef unsigned int u32x4_t __attribute__((ext_vector_type(4)));
+typedef unsigned int u32x2_t __attribute__((ext_vector_type(2)));
+
+__device__ __forceinline__ __amdgpu_buffer_rsrc_t buf_rsrc(const void* p, uint32_t bytes) {
+    return __builtin_amdgcn_make_buffer_rsrc(const_cast<void*>(p), 0, (int)bytes, 0x00020000);
+}
+
+template <class T>
+struct BufAct;
+
+template <>
+struct BufAct<float> {
+    static constexpr int BYTES = 16;  // four elements
+    static __device__ __forceinline__ float4 ld(__amdgpu_buffer_rsrc_t r, int vo, int so) {
+        const u32x4_t u = __builtin_amdgcn_raw_buffer_load_b128(r, vo, so, 0);
+        return make_float4(__uint_as_float(u[0]), __uint_as_float(u[1]), __uint_as_float(u[2]),
+                           __uint_as_float(u[3]));
+    }
+    static __device__ __forceinline__ void st(__amdgpu_buffer_rsrc_t r, int vo, int so, float4 v) {
+        const u32x4_t u = {__float_as_uint(v.x), __float_as_uint(v.y), __float_as_uint(v.z),
+                           __float_as_uint(v.w)};
+        __builtin_amdgcn_raw_buffer_store_b128(u, r, vo, so, 0);
+    }
+};
+
+template <>
+struct BufAct<uint16_t> {
+    static constexpr int BYTES = 8;
+    static __device__ __forceinline__ float4 ld(__amdgpu_buffer_rsrc_t r, int vo, int so) {
+        const u32x2_t u = __builtin_amdgcn_raw_buffer_load_b64(r, vo, so, 0);
+        return make_float4(__uint_as_float(u[0] << 16), __uint_as_float(u[0] & 0xffff0000u),
+                           __uint_as_float(u[1] << 16), __uint_as_float(u[1] & 0xffff0000u));
+    }
+    static __device__ __forceinline__ void st(__amdgpu_buffer_rsrc_t r, int vo, int so, float4 v) {
+        const u32x2_t u = {f2bf(v.x) | ((uint32_t)f2bf(v.y) << 16),
+                           f2bf(v.z) | ((uint32_t)f2bf(v.w) << 16)};
+        __builtin_amdgcn_raw_buffer_store_b64(u, r, vo, so, 0);
+    }
+};
+
+template <>
+struct BufAct<_Float16> {
+    static constexpr int BYTES = 8;
+    typedef _Float16 h4 __attribute__((ext_vector_type(4)));
+    static __device__ __forceinline__ float4 ld(__amdgpu_buffer_rsrc_t r, int vo, int so) {
+        const h4 u = __builtin_bit_cast(h4, __builtin_amdgcn_raw_buffer_load_b64(r, vo, so, 0));
+        return make_float4((float)u[0], (float)u[1], (float)u[2], (float)u[3]);
+    }
+    static __device__ __forceinline__ void st(__amdgpu_buffer_rsrc_t r, int vo, int so, float4 v) {
+        const h4 u = {(_Float16)v.x, (_Float16)v.y, (_Float16)v.z, (_Float16)v.w};
+        __builtin_amdgcn_raw_buffer_store_b64(__builtin_bit_cast(u32x2_t, u), r, vo, so, 0);
+    }
+};
+
 // The 16-bit formats as matrix-core operands: bits <-> fp32, a packed pair,
 // and the 32x32x16 MFMA with fp32 accumulation.
 typedef __bf16 bf16x8_t __attribute__((ext_vector_type(8)));

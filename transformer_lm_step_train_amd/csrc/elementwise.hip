@@ -239,13 +239,14 @@ __global__ __launch_bounds__(256) void fill_zero_kernel(float* __restrict__ p, i
 }
 
 __device__ __forceinline__ float adamw_one(float& p, float g, float& m, float& v, float lr,
-                                           float b1, float b2, float eps, float wd, float bc1,
-                                           float bc2) {
-    m = b1 * m + (1.f - b1) * g;
-    v = b2 * v + (1.f - b2) * g * g;
-    const float mhat = m / bc1;
-    const float vhat = v / bc2;
-    p -= lr * (mhat / (sqrtf(vhat) + eps) + wd * p);
+                                           float b1, float b2, float eps, float wd, float ibc1,
+                                           float ibc2) {
+    m = fmaf(b1, m, (1.f - b1) * g);
+    v = fmaf(b2, v, (1.f - b2) * g * g);
+    const float mhat = m * ibc1;
+    const float vhat = v * ibc2;
+    // Hardware square root and reciprocal (about 1 ulp each).
+    p -= lr * fmaf(mhat, __builtin_amdgcn_rcpf(__builtin_amdgcn_sqrtf(vhat) + eps), wd * p);
     return p;
 }
 
@@ -267,23 +268,35 @@ __global__ __launch_bounds__(256) void adamw_kernel(float* __restrict__ p,
                                                     const int* __restrict__ skip) {
     if (skip && *skip) return;
     const float ig = gscale ? 1.0f / *gscale : 1.0f;
+    const float ibc1 = 1.0f / bc1, ibc2 = 1.0f / bc2;
     const int64_t n4 = n >> 2;
     const int64_t stride = (int64_t)gridDim.x * blockDim.x;
-    for (int64_t i = blockIdx.x * (int64_t)blockDim.x + threadIdx.x; i < n4; i += stride) {
-        float4 pp = ld4(p + 4 * i), gg = ld4(g + 4 * i), mm = ld4(m + 4 * i), vv = ld4(v + 4 * i);
+    auto one4 = [&](int64_t i, float4 pp, float4 gg, float4 mm, float4 vv) {
         gg = make_float4(gg.x * ig, gg.y * ig, gg.z * ig, gg.w * ig);
-        adamw_one(pp.x, gg.x, mm.x, vv.x, lr, b1, b2, eps, wd, bc1, bc2);
-        adamw_one(pp.y, gg.y, mm.y, vv.y, lr, b1, b2, eps, wd, bc1, bc2);
-        adamw_one(pp.z, gg.z, mm.z, vv.z, lr, b1, b2, eps, wd, bc1, bc2);
-        adamw_one(pp.w, gg.w, mm.w, vv.w, lr, b1, b2, eps, wd, bc1, bc2);
+        adamw_one(pp.x, gg.x, mm.x, vv.x, lr, b1, b2, eps, wd, ibc1, ibc2);
+        adamw_one(pp.y, gg.y, mm.y, vv.y, lr, b1, b2, eps, wd, ibc1, ibc2);
+        adamw_one(pp.z, gg.z, mm.z, vv.z, lr, b1, b2, eps, wd, ibc1, ibc2);
+        adamw_one(pp.w, gg.w, mm.w, vv.w, lr, b1, b2, eps, wd, ibc1, ibc2);
         st4(p + 4 * i, pp);
         st4(m + 4 * i, mm);
         st4(v + 4 * i, vv);
         if (shadow) Act<S>::st(shadow + 4 * i, pp);
+    };
+    // Two groups of four per trip, so that eight loads are in flight.
+    int64_t i = blockIdx.x * (int64_t)blockDim.x + threadIdx.x;
+    for (; i + stride < n4; i += 2 * stride) {
+        const int64_t k = i + stride;
+        const float4 p0 = ld4(p + 4 * i), g0 = ld4(g + 4 * i), m0 = ld4(m + 4 * i),
+                     v0 = ld4(v + 4 * i);
+        const float4 p1 = ld4(p + 4 * k), g1 = ld4(g + 4 * k), m1 = ld4(m + 4 * k),
+                     v1 = ld4(v + 4 * k);
+        one4(i, p0, g0, m0, v0);
+        one4(k, p1, g1, m1, v1);
     }
-    for (int64_t i = 4 * n4 + blockIdx.x * (int64_t)blockDim.x + threadIdx.x; i < n; i += stride) {
-        adamw_one(p[i], g[i] * ig, m[i], v[i], lr, b1, b2, eps, wd, bc1, bc2);
-        if (shadow) Act<S>::st1(shadow + i, p[i]);
+    if (i < n4) one4(i, ld4(p + 4 * i), ld4(g + 4 * i), ld4(m + 4 * i), ld4(v + 4 * i));
+    for (int64_t t = 4 * n4 + blockIdx.x * (int64_t)blockDim.x + threadIdx.x; t < n; t += stride) {
+        adamw_one(p[t], g[t] * ig, m[t], v[t], lr, b1, b2, eps, wd, ibc1, ibc2);
+        if (shadow) Act<S>::st1(shadow + t, p[t]);
     }
 }
 

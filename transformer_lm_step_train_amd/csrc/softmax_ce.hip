@@ -28,76 +28,97 @@ __device__ __forceinline__ float block_max(float v, float* sh) {
     return r;
 }
 
-template <int NT>
-__device__ __forceinline__ float block_sum(float v, float* sh) {
-    v = wave_sum(v);
-    const int lane = threadIdx.x & 63, wave = threadIdx.x >> 6;
-    __syncthreads();
-    if (lane == 0) sh[wave] = v;
-    __syncthreads();
-    float r = sh[0];
-#pragma unroll
-    for (int i = 1; i < NT / 64; i++) r += sh[i];
-    return r;
-}
-
 template <int NT, int NJ, class T>
-__global__ __launch_bounds__(NT) void softmax_ce_kernel(T* __restrict__ logits,
+__global__ __launch_bounds__(NT) __attribute__((amdgpu_waves_per_eu(4))) void softmax_ce_kernel(T* __restrict__ logits,
                                                         float* __restrict__ losses,
                                                         const int32_t* __restrict__ targets,
                                                         int V, int ldv, float dscale,
                                                         const float* __restrict__ gscale,
                                                         int* __restrict__ flag) {
-    __shared__ float sh[NT / 64];
+    constexpr float LOG2E = 1.4426950408889634f;
+    constexpr int NW = NT / 64;
+    __shared__ float shm[NW], shs[NW];
     const int64_t row = blockIdx.x;
     if (gscale) dscale *= *gscale;  // loss scaling of the fp16 model
     T* z = logits + row * ldv;
     const int V4 = ldv >> 2;
+    const auto zr = buf_rsrc(z, (uint32_t)ldv * sizeof(T));
+    constexpr int JB = NT * BufAct<T>::BYTES;  // byte stride between a thread's groups
+    const int vo = threadIdx.x * BufAct<T>::BYTES;
     const int tgt = targets[row];
     const bool bad = tgt < 0 || tgt >= V;
     float4 v[NJ];
-    float mx = -INFINITY;
 #pragma unroll
     for (int j = 0; j < NJ; j++) {
-        const int c4 = threadIdx.x + NT * j;
-        float4 x = make_float4(-INFINITY, -INFINITY, -INFINITY, -INFINITY);
-        if (c4 < V4) {
-            x = Act<T>::ld(z + 4 * c4);
-            const int c = 4 * c4;
-            if (c >= V) x.x = -INFINITY;
-            if (c + 1 >= V) x.y = -INFINITY;
-            if (c + 2 >= V) x.z = -INFINITY;
-            if (c + 3 >= V) x.w = -INFINITY;
-        }
-        v[j] = x;
-        mx = fmaxf(mx, fmaxf(fmaxf(x.x, x.y), fmaxf(x.z, x.w)));
+        // Groups wholly inside the row (a uniform test) load unconditionally.
+        if (NT * (j + 1) <= V4 || threadIdx.x + NT * j < V4)
+            v[j] = BufAct<T>::ld(zr, vo, JB * j);
+        else
+            v[j] = make_float4(-INFINITY, -INFINITY, -INFINITY, -INFINITY);
     }
     float zt = 0.f;
     if (threadIdx.x == 0 && !bad) zt = Act<T>::ld1(z + tgt);
-    mx = block_max<NT>(mx, sh);
+    float m = -INFINITY;
+#pragma unroll
+    for (int j = 0; j < NJ; j++) {
+        if (4 * NT * (j + 1) > V) {  // a group reaching the padding columns
+            const int c = 4 * (threadIdx.x + NT * j);
+            if (c >= V) v[j].x = -INFINITY;
+            if (c + 1 >= V) v[j].y = -INFINITY;
+            if (c + 2 >= V) v[j].z = -INFINITY;
+            if (c + 3 >= V) v[j].w = -INFINITY;
+        }
+        m = fmaxf(m, fmaxf(fmaxf(v[j].x, v[j].y), fmaxf(v[j].z, v[j].w)));
+    }
+    // A thread whose columns are all padding has m = -inf: shift by 0 so that
+    // its exponentials are exp(-inf) = 0 rather than NaN.
+    const float ms = m == -INFINITY ? 0.f : m * LOG2E;
     float s = 0.f;
 #pragma unroll
-    for (int j = 0; j < NJ; j++)
-        s += (expf(v[j].x - mx) + expf(v[j].y - mx)) + (expf(v[j].z - mx) + expf(v[j].w - mx));
-    s = block_sum<NT>(s, sh);
-    const float lse = mx + logf(s);
+    for (int j = 0; j < NJ; j++) {
+        v[j].x = __builtin_amdgcn_exp2f(fmaf(v[j].x, LOG2E, -ms));
+        v[j].y = __builtin_amdgcn_exp2f(fmaf(v[j].y, LOG2E, -ms));
+        v[j].z = __builtin_amdgcn_exp2f(fmaf(v[j].z, LOG2E, -ms));
+        v[j].w = __builtin_amdgcn_exp2f(fmaf(v[j].w, LOG2E, -ms));
+        s += (v[j].x + v[j].y) + (v[j].z + v[j].w);
+        __builtin_amdgcn_sched_barrier(0);  // in place, one group at a time
+    }
+    // Merge (m, s) over the wave, then over the waves.
+    const float mw = wave_max(m);
+    float sw = wave_sum(m == -INFINITY ? 0.f : s * __builtin_amdgcn_exp2f((m - mw) * LOG2E));
+    const int lane = threadIdx.x & 63, wave = threadIdx.x >> 6;
+    if (lane == 0) {
+        shm[wave] = mw;
+        shs[wave] = sw;
+    }
+    __syncthreads();
+    float M = shm[0];
+#pragma unroll
+    for (int i = 1; i < NW; i++) M = fmaxf(M, shm[i]);
+    float S = 0.f;
+#pragma unroll
+    for (int i = 0; i < NW; i++)
+        S += shm[i] == -INFINITY ? 0.f : shs[i] * __builtin_amdgcn_exp2f((shm[i] - M) * LOG2E);
+    const float lse = M + logf(S);
     if (threadIdx.x == 0) {
         losses[row] = bad ? 0.f : lse - zt;
         if (bad) atomicOr(flag, 2);
     }
+    // exp(z - lse) = e * exp(m_t - lse); the padding columns give 0.
+    const float f = bad || m == -INFINITY ? 0.f : __builtin_amdgcn_exp2f((m - lse) * LOG2E) * dscale;
+    // The target column: group jt of thread `owner`, component tc.
+    const int jt = bad ? -1 : (tgt >> 2) / NT, owner = (tgt >> 2) % NT, tc = tgt & 3;
+    const float hit = bad ? 0.f : dscale;
 #pragma unroll
     for (int j = 0; j < NJ; j++) {
-        const int c4 = threadIdx.x + NT * j;
-        if (c4 < V4) {
-            const int c = 4 * c4;
-            float4 d;
-            d.x = (expf(v[j].x - lse) - (c == tgt ? 1.f : 0.f)) * dscale;
-            d.y = (expf(v[j].y - lse) - (c + 1 == tgt ? 1.f : 0.f)) * dscale;
-            d.z = (expf(v[j].z - lse) - (c + 2 == tgt ? 1.f : 0.f)) * dscale;
-            d.w = (expf(v[j].w - lse) - (c + 3 == tgt ? 1.f : 0.f)) * dscale;
-            if (bad) d = make_float4(0.f, 0.f, 0.f, 0.f);
-            Act<T>::st(z + c, d);  // exp(-inf) = 0 in the padding columns
+        float4 d = make_float4(v[j].x * f, v[j].y * f, v[j].z * f, v[j].w * f);
+        if (j == jt && threadIdx.x == owner) {
+            if (tc == 0) d.x -= hit;
+            if (tc == 1) d.y -= hit;
+            if (tc == 2) d.z -= hit;
+            if (tc == 3) d.w -= hit;
         }
+        if (NT * (j + 1) <= V4 || threadIdx.x + NT * j < V4) BufAct<T>::st(zr, vo, JB * j, d);
     }
 }
 
@@ -109,18 +130,21 @@ hipError_t launch_ce(hipStream_t s, T* logits, float* losses, const int32_t* tar
     return hipGetLastError();
 }
 
+// 512-thread workgroups, so that two rows share a compute unit and one
+// row's loads overlap the other's reduction and stores.
 template <class T>
 hipError_t softmax_ce_t(hipStream_t s, T* logits, float* losses, const int32_t* targets, int N,
                         int V, int ldv, float dscale, const float* gs, int* flag) {
     const int V4 = ldv / 4;
     if (V4 <= 256) return launch_ce<256, 1>(s, logits, losses, targets, N, V, ldv, dscale, gs, flag);
-    const int nj = (V4 + 1023) / 1024;
-    if (nj <= 1) return launch_ce<1024, 1>(s, logits, losses, targets, N, V, ldv, dscale, gs, flag);
-    if (nj <= 2) return launch_ce<1024, 2>(s, logits, losses, targets, N, V, ldv, dscale, gs, flag);
-    if (nj <= 4) return launch_ce<1024, 4>(s, logits, losses, targets, N, V, ldv, dscale, gs, flag);
-    if (nj <= 8) return launch_ce<1024, 8>(s, logits, losses, targets, N, V, ldv, dscale, gs, flag);
-    if (nj <= 13) return launch_ce<1024, 13>(s, logits, losses, targets, N, V, ldv, dscale, gs, flag);
-    if (nj <= 16) return launch_ce<1024, 16>(s, logits, losses, targets, N, V, ldv, dscale, gs, flag);
+    const int nj = (V4 + 511) / 512;
+    if (nj <= 1) return launch_ce<512, 1>(s, logits, losses, targets, N, V, ldv, dscale, gs, flag);
+    if (nj <= 2) return launch_ce<512, 2>(s, logits, losses, targets, N, V, ldv, dscale, gs, flag);
+    if (nj <= 4) return launch_ce<512, 4>(s, logits, losses, targets, N, V, ldv, dscale, gs, flag);
+    if (nj <= 8) return launch_ce<512, 8>(s, logits, losses, targets, N, V, ldv, dscale, gs, flag);
+    if (nj <= 16) return launch_ce<512, 16>(s, logits, losses, targets, N, V, ldv, dscale, gs, flag);
+    if (nj <= 25) return launch_ce<512, 25>(s, logits, losses, targets, N, V, ldv, dscale, gs, flag);
+    if (nj <= 32) return launch_ce<512, 32>(s, logits, losses, targets, N, V, ldv, dscale, gs, flag);
     return hipErrorInvalidValue;
 }
 
@@ -203,6 +227,7 @@ hipError_t softmax_ce(hipStream_t s, void* logits, float* losses, const int32_t*
                       int N, int V, int ldv, float dscale, const float* gscale, int* flag,
                       int dt) {
     if (N <= 0) return hipSuccess;
+    if (V <= 0 || ldv < V || (ldv & 3) != 0) return hipErrorInvalidValue;
     return by_dt(dt, [&](auto e) {
         using E = decltype(e);
         return softmax_ce_t<E>(s, (E*)logits, losses, targets, N, V, ldv, dscale, gscale, flag);
