@@ -36,14 +36,18 @@ __global__ __launch_bounds__(256) void ln_fwd_kernel(T* __restrict__ out,
     if (row >= N) return;
     const int C4 = C >> 2;
     const T* x = inp + (int64_t)row * C;
-    float4 v[NCH];
+    float4 v[NCH], wv[NCH], bv[NCH];
     float s = 0.f;
 #pragma unroll
     for (int i = 0; i < NCH; i++) {
         const int c4 = lane + 64 * i;
         v[i] = c4 < C4 ? Act<T>::ld(x + 4 * c4) : make_float4(0.f, 0.f, 0.f, 0.f);
-        s += (v[i].x + v[i].y) + (v[i].z + v[i].w);
+        // the affine parameters load alongside the row, not after its reductions
+        wv[i] = c4 < C4 ? ld4(w + 4 * c4) : make_float4(0.f, 0.f, 0.f, 0.f);
+        bv[i] = c4 < C4 ? ld4(b + 4 * c4) : make_float4(0.f, 0.f, 0.f, 0.f);
     }
+#pragma unroll
+    for (int i = 0; i < NCH; i++) s += (v[i].x + v[i].y) + (v[i].z + v[i].w);
     const float m = wave_sum(s) / C;
     float ss = 0.f;
 #pragma unroll
@@ -61,7 +65,7 @@ __global__ __launch_bounds__(256) void ln_fwd_kernel(T* __restrict__ out,
     for (int i = 0; i < NCH; i++) {
         const int c4 = lane + 64 * i;
         if (c4 < C4) {
-            const float4 ww = ld4(w + 4 * c4), bb = ld4(b + 4 * c4);
+            const float4 ww = wv[i], bb = bv[i];
             Act<T>::st(y + 4 * c4, make_float4((v[i].x - m) * r * ww.x + bb.x,
                                         (v[i].y - m) * r * ww.y + bb.y,
                                         (v[i].z - m) * r * ww.z + bb.z,
@@ -77,7 +81,7 @@ __global__ __launch_bounds__(256) void ln_fwd_kernel(T* __restrict__ out,
 // Rows per backward workgroup: enough workgroups to fill the chip, few
 // enough partial rows to keep the second stage small.
 inline int ln_rows_per_block(int N) {
-    int r = (N + 511) / 512;
+    int r = (N + 1023) / 1024;
     r = (r + 3) & ~3;
     return r < 4 ? 4 : r;
 }
@@ -103,16 +107,23 @@ __global__ __launch_bounds__(256) void ln_bwd_kernel(
         const float m = mean[row], rs = rstd[row];
         const T* dy = dout + (int64_t)row * C;
         const T* x = inp + (int64_t)row * C;
-        float4 g[NCH], xh[NCH];
+        T* dx = dres + (int64_t)row * C;
+        float4 g[NCH], xh[NCH], dd[NCH], xv[NCH], old[NCH];
         float sg = 0.f, sgx = 0.f;
+        // every load of the row is issued before the first use
 #pragma unroll
         for (int i = 0; i < NCH; i++) {
             const int c4 = lane + 64 * i;
-            float4 d = make_float4(0.f, 0.f, 0.f, 0.f), xx = d;
+            dd[i] = xv[i] = old[i] = make_float4(0.f, 0.f, 0.f, 0.f);
             if (c4 < C4) {
-                d = Act<T>::ld(dy + 4 * c4);
-                xx = Act<T>::ld(x + 4 * c4);
+                dd[i] = Act<T>::ld(dy + 4 * c4);
+                xv[i] = Act<T>::ld(x + 4 * c4);
+                if (accumulate) old[i] = Act<T>::ld(dx + 4 * c4);
             }
+        }
+#pragma unroll
+        for (int i = 0; i < NCH; i++) {
+            const float4 d = dd[i], xx = xv[i];
             xh[i] = make_float4((xx.x - m) * rs, (xx.y - m) * rs, (xx.z - m) * rs,
                                 (xx.w - m) * rs);
             g[i] = make_float4(d.x * wv[i].x, d.y * wv[i].y, d.z * wv[i].z, d.w * wv[i].w);
@@ -128,7 +139,6 @@ __global__ __launch_bounds__(256) void ln_bwd_kernel(
             pb[i].w += d.w;
         }
         const float mg = wave_sum(sg) / C, mgx = wave_sum(sgx) / C;
-        T* dx = dres + (int64_t)row * C;
 #pragma unroll
         for (int i = 0; i < NCH; i++) {
             const int c4 = lane + 64 * i;
@@ -137,13 +147,10 @@ __global__ __launch_bounds__(256) void ln_bwd_kernel(
                                        rs * (g[i].y - mg - xh[i].y * mgx),
                                        rs * (g[i].z - mg - xh[i].z * mgx),
                                        rs * (g[i].w - mg - xh[i].w * mgx));
-                if (accumulate) {
-                    const float4 p = Act<T>::ld(dx + 4 * c4);
-                    o.x += p.x;
-                    o.y += p.y;
-                    o.z += p.z;
-                    o.w += p.w;
-                }
+                o.x += old[i].x;  // zero unless accumulating
+                o.y += old[i].y;
+                o.z += old[i].z;
+                o.w += old[i].w;
                 Act<T>::st(dx + 4 * c4, o);
             }
         }
@@ -210,9 +217,9 @@ hipError_t layernorm_forward(hipStream_t s, void* out, float* mean, float* rstd,
 }
 
 // Upper bound of the workgroup count over every row count up to N: at most
-// 512 (rows per workgroup grow past 2048 rows) and at most ceil(N/4).
+// 1024 (rows per workgroup grow past 4096 rows) and at most ceil(N/4).
 size_t layernorm_partials_floats(int N, int C) {
-    const int nb = std::min(512, (N + 3) / 4);
+    const int nb = std::min(1024, (N + 3) / 4);
     return (size_t)nb * 2 * C;
 }
 
