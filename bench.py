@@ -177,8 +177,10 @@ def main():
         train_step()
     m.synchronize()
     marks.clear()
+    # Inside the timed region only the matmul family (the roofline's kernel)
+    # is timed; every class still counts its launches and algorithmic work.
     if not args.no_kernel_timing:
-        gpt2.gpt2_profile(m.h, True)
+        gpt2.gpt2_profile(m.h, 1 << gpt2.KC_NAMES.index("gemm"))
     torch.cuda.synchronize()
     t0 = time.perf_counter()
     for _ in range(args.steps):
@@ -193,10 +195,22 @@ def main():
     per_step = np.diff(np.array(marks)) * 1000.0
     ms_median = float(np.median(per_step)) if len(per_step) else ms
 
-    kc = {}
+    timed_losses = list(losses)
+    kc, kci, inst_ms = {}, {}, None
     if not args.no_kernel_timing:
         for i, name in enumerate(gpt2.KC_NAMES):
             kc[name] = gpt2.gpt2_profile_read(m.h, i)
+        gpt2.gpt2_profile(m.h, False)
+        # A second pass of K steps with every launch timed, for the per-class
+        # breakdown (each timed dispatch costs a few microseconds of issue).
+        gpt2.gpt2_profile(m.h, True)
+        ti = time.perf_counter()
+        for _ in range(args.steps):
+            train_step()
+        m.synchronize()
+        inst_ms = 1000.0 * (time.perf_counter() - ti) / args.steps
+        for i, name in enumerate(gpt2.KC_NAMES):
+            kci[name] = gpt2.gpt2_profile_read(m.h, i)
         gpt2.gpt2_profile(m.h, False)
     assert all(np.isfinite(losses)), losses
     m.close()
@@ -224,16 +238,17 @@ def main():
                               % {"fp32": "fp32", "bf16": "bf16", "fp16": "fp16"}[args.precision],
                     "launches_per_step": n // args.steps,
                     "avg_launch_ms": round(g["ms"] / n, 4)}
-        print("per-class kernel time per step:", file=sys.stderr)
+        print(f"per-class kernel time per step (instrumented pass, {inst_ms:.3f} ms per step):",
+              file=sys.stderr)
         total = 0.0
-        for name, r in kc.items():
+        for name, r in kci.items():
             per = r["ms"] / args.steps
             total += per
             gbs = r["bytes"] / (r["ms"] / 1e3) / 1e9 if r["ms"] > 0 else 0.0
             tf = r["flops"] / (r["ms"] / 1e3) / 1e12 if r["ms"] > 0 else 0.0
             print(f"  {name:11s} {per:9.3f} ms  launches/step {r['launches'] // args.steps:4d}"
                   f"  {tf:7.2f} TFLOP/s  {gbs:8.1f} GB/s", file=sys.stderr)
-        print(f"  {'sum':11s} {total:9.3f} ms of {ms:.3f} ms per step", file=sys.stderr)
+        print(f"  {'sum':11s} {total:9.3f} ms of {inst_ms:.3f} ms per step", file=sys.stderr)
 
     out = {
         "metric": "training tokens/sec (fwd+bwd+AdamW), GPT-2 124M B16 T1024 at 1 GPU"
@@ -257,8 +272,12 @@ def main():
         "roofline": roofline,
         "step_roofline": step_roof,
         "cpu_baseline": None,
-        "kernel_ms_per_step": {k: round(v["ms"] / args.steps, 3) for k, v in kc.items()},
-        "loss_first_last": [round(losses[0], 5), round(losses[-1], 5)],
+        "kernel_ms_per_step": {k: round(v["ms"] / args.steps, 3) for k, v in kci.items()},
+        "kernel_timing": None if not kc else (
+            "the timed region times the matmul family only (roofline); kernel_ms_per_step "
+            f"comes from a second pass of {args.steps} steps with every launch timed, "
+            f"{inst_ms:.3f} ms per step there"),
+        "loss_first_last": [round(timed_losses[0], 5), round(timed_losses[-1], 5)],
     }
     if not args.no_cpu_baseline and not half:
         out["cpu_baseline"] = cpu_baseline(c, params, tok, tgt)

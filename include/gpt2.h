@@ -263,13 +263,22 @@ GPT2_API const char* gpt2_last_error(void);
 #define GPT2_KC_OTHER 5     /* encoder, bias sums, zero-grad, loss mean   */
 #define GPT2_KC_COUNT 6
 
-/* enable != 0 records an event pair around every launch from now on and
- * clears the counters; enable == 0 stops recording. */
-GPT2_API int gpt2_profile(gpt2_model* model, int enable);
+#define GPT2_PROFILE_ALL ((1 << GPT2_KC_COUNT) - 1)
+
+/* class_mask != 0 clears the counters and from now on counts the launches
+ * and algorithmic work of every class; the classes whose bit is set in
+ * class_mask (bit k = class k; GPT2_PROFILE_ALL for all) are also timed.  A
+ * timed call's first kernel dispatch carries a start event and its last one
+ * a stop event (hipExtLaunchKernel), so timing adds no packets between
+ * kernels, but each timed dispatch still costs about 3 us of issue time.
+ * class_mask == 0 stops profiling.  Returns GPT2_EINVAL for bits past the
+ * last class. */
+GPT2_API int gpt2_profile(gpt2_model* model, int class_mask);
 
 /* Totals since profiling was enabled for one kernel class: summed kernel
- * time (ms, waits for the stream), number of launches, and the algorithmic
- * work of those launches: floating-point operations and HBM bytes. */
+ * time (ms, waits for the stream; 0 for an untimed class), number of
+ * launches, and the algorithmic work of those launches: floating-point
+ * operations and HBM bytes. */
 GPT2_API int gpt2_profile_read(gpt2_model* model, int kernel_class, double* total_ms,
                       int64_t* launches, double* flops, double* bytes);
 

@@ -534,7 +534,7 @@ hipError_t fwd_hs(hipStream_t s, E* out, float* lse, const E* qkv, int B, int T,
                   int NH) {
     const int nqb = (T + AQ - 1) / AQ;
     const float qscale = LOG2E / sqrtf((float)HS);
-    hipLaunchKernelGGL((attn_fwd_kernel<HS, E>), dim3(B * NH * nqb), dim3(256), 0, s, out, lse,
+    launch((attn_fwd_kernel<HS, E>), dim3(B * NH * nqb), dim3(256), 0, s, out, lse,
                        qkv, T, C, NH, qscale);
     return hipGetLastError();
 }
@@ -545,9 +545,9 @@ hipError_t bwd_hs(hipStream_t s, E* dqkv, float* D, const E* dout, const E* qkv,
     const int nb = (T + AQ - 1) / AQ;
     const float scale = 1.0f / sqrtf((float)HS);
     const float qscale = LOG2E * scale;
-    hipLaunchKernelGGL((attn_bwd_dq_kernel<HS, E>), dim3(B * NH * nb), dim3(256), 0, s, dqkv, D,
+    launch((attn_bwd_dq_kernel<HS, E>), dim3(B * NH * nb), dim3(256), 0, s, dqkv, D,
                        dout, out, qkv, lse, T, C, NH, qscale, scale);
-    hipLaunchKernelGGL((attn_bwd_dkdv_kernel<HS, E>), dim3(B * NH * nb), dim3(256), 0, s, dqkv,
+    launch((attn_bwd_dkdv_kernel<HS, E>), dim3(B * NH * nb), dim3(256), 0, s, dqkv,
                        dout, qkv, lse, D, T, C, NH, qscale, scale);
     return hipGetLastError();
 }

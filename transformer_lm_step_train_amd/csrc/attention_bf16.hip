@@ -492,9 +492,9 @@ hipError_t bwd16(hipStream_t s, uint16_t* dqkv, float* D, const uint16_t* dout,
     const int nb = (T + RQ - 1) / RQ;
     const float scale = 1.0f / sqrtf((float)HS);
     const float qscale = L2E * scale;
-    hipLaunchKernelGGL((attn16_dq_kernel<HS, H>), dim3(B * NH * nb), dim3(256), 0, s, dqkv, D, dout,
+    launch((attn16_dq_kernel<HS, H>), dim3(B * NH * nb), dim3(256), 0, s, dqkv, D, dout,
                        out, qkv, lse, T, C, NH, qscale, scale);
-    hipLaunchKernelGGL((attn16_dkdv_kernel<HS, H>), dim3(B * NH * nb), dim3(256), 0, s, dqkv, dout,
+    launch((attn16_dkdv_kernel<HS, H>), dim3(B * NH * nb), dim3(256), 0, s, dqkv, dout,
                        qkv, lse, D, T, C, NH, qscale, scale);
     return hipGetLastError();
 }
@@ -504,7 +504,7 @@ hipError_t fwd16(hipStream_t s, uint16_t* out, float* lse, const uint16_t* qkv, 
                  int C, int NH) {
     const int nqb = (T + RQ - 1) / RQ;
     const float qscale = L2E / sqrtf((float)HS);
-    hipLaunchKernelGGL((attn16_fwd_kernel<HS, H>), dim3(B * NH * nqb), dim3(256), 0, s, out, lse,
+    launch((attn16_fwd_kernel<HS, H>), dim3(B * NH * nqb), dim3(256), 0, s, out, lse,
                        qkv, T, C, NH, qscale);
     return hipGetLastError();
 }

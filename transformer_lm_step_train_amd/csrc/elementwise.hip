@@ -384,7 +384,7 @@ hipError_t encoder_forward(hipStream_t s, void* out, const int32_t* tok, const f
     const dim3 grid(grid_for(n, 256, 65535));
     return by_dt(dt, [&](auto e) {
         using E = decltype(e);
-        hipLaunchKernelGGL(encoder_fwd_kernel<E>, grid, dim3(256), 0, s, (E*)out, tok, wte, wpe,
+        launch(encoder_fwd_kernel<E>, grid, dim3(256), 0, s, (E*)out, tok, wte, wpe,
                            B, T, C, V, flag);
         return hipGetLastError();
     });
@@ -398,7 +398,7 @@ hipError_t encoder_sort_prepare(int n_pow2) {
 hipError_t encoder_sort(hipStream_t s, uint32_t* keys, const int32_t* tok, int n, int V,
                         int pos_bits, int n_pow2) {
     if (n <= 0) return hipSuccess;
-    hipLaunchKernelGGL(encoder_sort_kernel, dim3(1), dim3(1024), (size_t)n_pow2 * 4, s, keys,
+    launch(encoder_sort_kernel, dim3(1), dim3(1024), (size_t)n_pow2 * 4, s, keys,
                        tok, n, V, pos_bits, n_pow2);
     return hipGetLastError();
 }
@@ -409,16 +409,16 @@ hipError_t encoder_backward_t(hipStream_t s, float* dwte, float* dwpe, const E* 
     const int n = B * T_;
     dim3 grid((n + 3) / 4), block(256);
     switch ((C + 255) / 256) {
-        case 1: hipLaunchKernelGGL((encoder_bwd_wte_kernel<1, E>), grid, block, 0, s, dwte, dx, keys, n, C, V, pos_bits); break;
-        case 2: hipLaunchKernelGGL((encoder_bwd_wte_kernel<2, E>), grid, block, 0, s, dwte, dx, keys, n, C, V, pos_bits); break;
-        case 3: hipLaunchKernelGGL((encoder_bwd_wte_kernel<3, E>), grid, block, 0, s, dwte, dx, keys, n, C, V, pos_bits); break;
-        case 4: hipLaunchKernelGGL((encoder_bwd_wte_kernel<4, E>), grid, block, 0, s, dwte, dx, keys, n, C, V, pos_bits); break;
+        case 1: launch((encoder_bwd_wte_kernel<1, E>), grid, block, 0, s, dwte, dx, keys, n, C, V, pos_bits); break;
+        case 2: launch((encoder_bwd_wte_kernel<2, E>), grid, block, 0, s, dwte, dx, keys, n, C, V, pos_bits); break;
+        case 3: launch((encoder_bwd_wte_kernel<3, E>), grid, block, 0, s, dwte, dx, keys, n, C, V, pos_bits); break;
+        case 4: launch((encoder_bwd_wte_kernel<4, E>), grid, block, 0, s, dwte, dx, keys, n, C, V, pos_bits); break;
         default: return hipErrorInvalidValue;
     }
     hipError_t e = hipGetLastError();
     if (e != hipSuccess || !dwpe) return e;  // no position table (rotary model)
     const int64_t nw = (int64_t)T_ * (C / 4);
-    hipLaunchKernelGGL(encoder_bwd_wpe_kernel<E>, dim3(grid_for(nw, 256, 1u << 30)), dim3(256),
+    launch(encoder_bwd_wpe_kernel<E>, dim3(grid_for(nw, 256, 1u << 30)), dim3(256),
                        0, s, dwpe, dx, B, T_, C);
     return hipGetLastError();
 }
@@ -441,7 +441,7 @@ hipError_t rope_apply(hipStream_t s, void* qkv, const float* cs, int B, int T, i
     const int hs = C / NH;
     return by_dt(dt, [&](auto e) {
         using E = decltype(e);
-        hipLaunchKernelGGL(rope_kernel<E>, grid, dim3(256), 0, s, (E*)qkv, (const float2*)cs,
+        launch(rope_kernel<E>, grid, dim3(256), 0, s, (E*)qkv, (const float2*)cs,
                            B * T, T, C, hs, (int64_t)3 * C, (float)dir);
         return hipGetLastError();
     });
@@ -458,7 +458,7 @@ hipError_t bias_grad(hipStream_t s, float* db, float* part, const void* dy, int 
     dim3 grid((N / 4 + 63) / 64, nchunks);
     hipError_t e = by_dt(dt, [&](auto x) {
         using E = decltype(x);
-        hipLaunchKernelGGL(bias_partial_kernel<E>, grid, dim3(256), 0, s, part, (const E*)dy, M,
+        launch(bias_partial_kernel<E>, grid, dim3(256), 0, s, part, (const E*)dy, M,
                            N, ld);
         return hipGetLastError();
     });
@@ -469,14 +469,14 @@ hipError_t bias_grad(hipStream_t s, float* db, float* part, const void* dy, int 
 hipError_t colsum_add(hipStream_t s, float* out0, float* out1, int split, const float* part,
                       int nrows, int ncols) {
     if (nrows <= 0 || ncols <= 0) return hipSuccess;
-    hipLaunchKernelGGL(colsum_finish_kernel, dim3((ncols + 63) / 64), dim3(1024), 0, s, out0,
+    launch(colsum_finish_kernel, dim3((ncols + 63) / 64), dim3(1024), 0, s, out0,
                        out1, split, part, nrows, ncols);
     return hipGetLastError();
 }
 
 hipError_t fill_zero(hipStream_t s, float* p, int64_t n) {
     if (n <= 0) return hipSuccess;
-    hipLaunchKernelGGL(fill_zero_kernel, dim3(grid_for(n / 4 + 1, 256, 8192)), dim3(256), 0, s,
+    launch(fill_zero_kernel, dim3(grid_for(n / 4 + 1, 256, 8192)), dim3(256), 0, s,
                        p, n);
     return hipGetLastError();
 }
@@ -489,7 +489,7 @@ hipError_t adamw(hipStream_t s, float* p, const float* g, float* m, float* v, vo
     if (!shadow) shadow_dt = DT_F32;
     return by_dt(shadow_dt, [&](auto e) {
         using S = decltype(e);
-        hipLaunchKernelGGL(adamw_kernel<S>, grid, dim3(256), 0, s, p, g, m, v, (S*)shadow, n, lr,
+        launch(adamw_kernel<S>, grid, dim3(256), 0, s, p, g, m, v, (S*)shadow, n, lr,
                            b1, b2, eps, wd, bc1, bc2, gscale, skip);
         return hipGetLastError();
     });
@@ -499,7 +499,7 @@ hipError_t to_half(hipStream_t s, void* out, const float* in, int64_t n, int dt)
     if (n <= 0) return hipSuccess;
     return by_dt(dt, [&](auto e) {
         using S = decltype(e);
-        hipLaunchKernelGGL(to_half_kernel<S>, dim3(grid_for(n, 256, 8192)), dim3(256), 0, s,
+        launch(to_half_kernel<S>, dim3(grid_for(n, 256, 8192)), dim3(256), 0, s,
                            (S*)out, in, n);
         return hipGetLastError();
     });
@@ -507,14 +507,14 @@ hipError_t to_half(hipStream_t s, void* out, const float* in, int64_t n, int dt)
 
 hipError_t check_finite(hipStream_t s, const float* g, int64_t n, int* flag) {
     if (n <= 0) return hipSuccess;
-    hipLaunchKernelGGL(check_finite_kernel, dim3(grid_for(n, 256, 8192)), dim3(256), 0, s, g, n,
+    launch(check_finite_kernel, dim3(grid_for(n, 256, 8192)), dim3(256), 0, s, g, n,
                        flag);
     return hipGetLastError();
 }
 
 hipError_t loss_scale_update(hipStream_t s, float* scale, int* good, int* found, int* skipped,
                              int interval, float min_scale) {
-    hipLaunchKernelGGL(loss_scale_kernel, dim3(1), dim3(64), 0, s, scale, good, found, skipped,
+    launch(loss_scale_kernel, dim3(1), dim3(64), 0, s, scale, good, found, skipped,
                        interval, min_scale);
     return hipGetLastError();
 }

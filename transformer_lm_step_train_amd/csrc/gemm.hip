@@ -412,7 +412,7 @@ hipError_t launch(hipStream_t s, const GemmArgs& a, int splits, float* ws) {
     const int chunk = splits > 1 ? split_chunk(a.K, splits) : (a.K > 0 ? a.K : 1);
     const int nz = splits > 1 ? cdiv(a.K, chunk) : 1;
     dim3 grid(tm * tn, 1, nz);
-    hipLaunchKernelGGL((gemm_kernel<OP, EPI>), grid, dim3(NTHR), 0, s, a, tm, tn, chunk,
+    launch((gemm_kernel<OP, EPI>), grid, dim3(NTHR), 0, s, a, tm, tn, chunk,
                        ws);
     return hipGetLastError();
 }
@@ -436,15 +436,15 @@ hipError_t launch_split(hipStream_t s, const GemmArgs& a, int splits, float* ws)
     const int blocks = (int)std::min<int64_t>((n4 + 255) / 256, 4096);
     switch (a.epi) {
         case EPI_STORE:
-            hipLaunchKernelGGL(splitk_reduce_kernel<EPI_STORE>, dim3(blocks), dim3(256), 0, s, a,
+            launch(splitk_reduce_kernel<EPI_STORE>, dim3(blocks), dim3(256), 0, s, a,
                                ws, nz);
             break;
         case EPI_RESID:
-            hipLaunchKernelGGL(splitk_reduce_kernel<EPI_RESID>, dim3(blocks), dim3(256), 0, s, a,
+            launch(splitk_reduce_kernel<EPI_RESID>, dim3(blocks), dim3(256), 0, s, a,
                                ws, nz);
             break;
         case EPI_ACCUM:
-            hipLaunchKernelGGL(splitk_reduce_kernel<EPI_ACCUM>, dim3(blocks), dim3(256), 0, s, a,
+            launch(splitk_reduce_kernel<EPI_ACCUM>, dim3(blocks), dim3(256), 0, s, a,
                                ws, nz);
             break;
         default: return hipErrorInvalidValue;

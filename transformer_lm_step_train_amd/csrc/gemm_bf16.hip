@@ -671,7 +671,7 @@ PlanH plan_h(const GemmArgsH& a) {
 template <int OP, int EPI, class H>
 hipError_t launch_h(hipStream_t s, const GemmArgsH& a, float* ws) {
     const int tm = cdiv(a.M, BM), tn = cdiv(a.N, BN);
-    hipLaunchKernelGGL((gemm_bf16_kernel<OP, EPI, H>), dim3(tm * tn, 1, 1), dim3(NTHR), 0, s, a, tm,
+    launch((gemm_bf16_kernel<OP, EPI, H>), dim3(tm * tn, 1, 1), dim3(NTHR), 0, s, a, tm,
                        tn, a.K > 0 ? a.K : 1, ws);
     return hipGetLastError();
 }
@@ -681,7 +681,7 @@ hipError_t launch_big(hipStream_t s, const GemmArgsH& a, int splits, float* ws) 
     const int tm = cdiv(a.M, 256), tn = cdiv(a.N, 256);
     const int chunk = splits > 1 ? split_chunk_h(a.K, splits) : (a.K > 0 ? a.K : 1);
     const int nz = splits > 1 ? cdiv(a.K, chunk) : 1;
-    hipLaunchKernelGGL((gemm_bf16_big_kernel<OP, EPI, 4, 4, H>), dim3(tm * tn, 1, nz), dim3(NTHR), 0,
+    launch((gemm_bf16_big_kernel<OP, EPI, 4, 4, H>), dim3(tm * tn, 1, nz), dim3(NTHR), 0,
                        s, a, tm, tn, chunk, ws);
     return hipGetLastError();
 }
@@ -747,10 +747,10 @@ hipError_t run(hipStream_t s, const GemmArgsH& a, const PlanH& p, float* ws) {
     const int64_t n4 = (int64_t)a.M * (a.N / 4);
     const int blocks = (int)std::min<int64_t>((n4 + 255) / 256, 4096);
     if (a.epi == EPI_ACCUM)
-        hipLaunchKernelGGL((splitk_reduce_bf16_kernel<EPI_ACCUM, H>), dim3(blocks), dim3(256), 0,
+        launch((splitk_reduce_bf16_kernel<EPI_ACCUM, H>), dim3(blocks), dim3(256), 0,
                            s, a, ws, nz);
     else
-        hipLaunchKernelGGL((splitk_reduce_bf16_kernel<EPI_STORE, H>), dim3(blocks), dim3(256), 0,
+        launch((splitk_reduce_bf16_kernel<EPI_STORE, H>), dim3(blocks), dim3(256), 0,
                            s, a, ws, nz);
     return hipGetLastError();
 }

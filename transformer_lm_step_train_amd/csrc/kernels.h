@@ -1,11 +1,33 @@
 // Internal launchers of the gfx950 kernels.  Every launcher queues work on
 // the given stream and returns the launch error (hipSuccess on success).
 #pragma once
+#include <hip/hip_ext.h>
 #include <hip/hip_runtime.h>
 #include <stddef.h>
 #include <stdint.h>
 
 namespace gk {
+
+// ---- launch-time events ---------------------------------------------------
+// While the runtime times a group of launches it sets `start` and `stop`;
+// every launch of the group then carries them in its own dispatch (the first
+// launch the start event, each launch the stop event, so the last one
+// stands), so timing adds no event packets between kernels.  One per host
+// thread.
+struct LaunchEvents {
+    hipEvent_t start = nullptr, stop = nullptr;
+    int launched = 0;
+};
+LaunchEvents& launch_events();  // runtime.cpp
+
+// Every kernel of the library is launched through here.
+template <class F, class... Args>
+inline void launch(F kernel, dim3 grid, dim3 block, uint32_t shm, hipStream_t s, Args... args) {
+    LaunchEvents& e = launch_events();
+    hipExtLaunchKernelGGL(kernel, grid, block, shm, s, e.start, e.stop, 0, args...);
+    e.start = nullptr;
+    e.launched++;
+}
 
 // ---- matmul ---------------------------------------------------------------
 // C[m,n] = sum_k A(m,k) B(k,n), all fp32, row-major with leading dims:

@@ -180,10 +180,10 @@ hipError_t ln_fwd_launch(hipStream_t s, T* out, float* mean, float* rstd, const 
                          const float* w, const float* b, int N, int C) {
     dim3 grid((N + 3) / 4), block(256);
     switch ((C + 255) / 256) {
-        case 1: hipLaunchKernelGGL((ln_fwd_kernel<1, T>), grid, block, 0, s, out, mean, rstd, inp, w, b, N, C); break;
-        case 2: hipLaunchKernelGGL((ln_fwd_kernel<2, T>), grid, block, 0, s, out, mean, rstd, inp, w, b, N, C); break;
-        case 3: hipLaunchKernelGGL((ln_fwd_kernel<3, T>), grid, block, 0, s, out, mean, rstd, inp, w, b, N, C); break;
-        case 4: hipLaunchKernelGGL((ln_fwd_kernel<4, T>), grid, block, 0, s, out, mean, rstd, inp, w, b, N, C); break;
+        case 1: launch((ln_fwd_kernel<1, T>), grid, block, 0, s, out, mean, rstd, inp, w, b, N, C); break;
+        case 2: launch((ln_fwd_kernel<2, T>), grid, block, 0, s, out, mean, rstd, inp, w, b, N, C); break;
+        case 3: launch((ln_fwd_kernel<3, T>), grid, block, 0, s, out, mean, rstd, inp, w, b, N, C); break;
+        case 4: launch((ln_fwd_kernel<4, T>), grid, block, 0, s, out, mean, rstd, inp, w, b, N, C); break;
         default: return hipErrorInvalidValue;
     }
     return hipGetLastError();
@@ -196,10 +196,10 @@ hipError_t ln_bwd_launch(hipStream_t s, T* dres, int accumulate, float* partials
     const size_t shm = (size_t)8 * C * sizeof(float);
     dim3 grid(nb), block(256);
     switch ((C + 255) / 256) {
-        case 1: hipLaunchKernelGGL((ln_bwd_kernel<1, T>), grid, block, shm, s, dres, accumulate, partials, dout, inp, w, mean, rstd, N, C, rpb); break;
-        case 2: hipLaunchKernelGGL((ln_bwd_kernel<2, T>), grid, block, shm, s, dres, accumulate, partials, dout, inp, w, mean, rstd, N, C, rpb); break;
-        case 3: hipLaunchKernelGGL((ln_bwd_kernel<3, T>), grid, block, shm, s, dres, accumulate, partials, dout, inp, w, mean, rstd, N, C, rpb); break;
-        case 4: hipLaunchKernelGGL((ln_bwd_kernel<4, T>), grid, block, shm, s, dres, accumulate, partials, dout, inp, w, mean, rstd, N, C, rpb); break;
+        case 1: launch((ln_bwd_kernel<1, T>), grid, block, shm, s, dres, accumulate, partials, dout, inp, w, mean, rstd, N, C, rpb); break;
+        case 2: launch((ln_bwd_kernel<2, T>), grid, block, shm, s, dres, accumulate, partials, dout, inp, w, mean, rstd, N, C, rpb); break;
+        case 3: launch((ln_bwd_kernel<3, T>), grid, block, shm, s, dres, accumulate, partials, dout, inp, w, mean, rstd, N, C, rpb); break;
+        case 4: launch((ln_bwd_kernel<4, T>), grid, block, shm, s, dres, accumulate, partials, dout, inp, w, mean, rstd, N, C, rpb); break;
         default: return hipErrorInvalidValue;
     }
     return hipGetLastError();

@@ -24,6 +24,13 @@
 #include "dtype.h"
 #include "kernels.h"
 
+namespace gk {
+LaunchEvents& launch_events() {
+    static thread_local LaunchEvents e;
+    return e;
+}
+}  // namespace gk
+
 namespace {
 
 thread_local std::string g_err;
@@ -223,6 +230,7 @@ constexpr int kEventPool = 4096;
 
 struct Prof {
     bool on = false;
+    int mask = 0;  // classes whose launches carry timing events
     std::vector<hipEvent_t> ev;
     struct Rec {
         int kc;
@@ -295,21 +303,36 @@ void prof_flush(gpt2_model* md) {
     p.recs.clear();
 }
 
+// Times the launches of one library call: the first kernel's dispatch
+// carries the start event and the last one's the stop event (a call that
+// launches nothing records nothing).
 struct Scope {
     gpt2_model* md;
     int kc;
     double flops, bytes;
-    bool on;
+    bool on, timed;
     Scope(gpt2_model* m, int k, double f, double b) : md(m), kc(k), flops(f), bytes(b) {
         on = md->prof.on;
-        if (!on) return;
+        timed = on && ((md->prof.mask >> kc) & 1);
+        gk::LaunchEvents& le = gk::launch_events();
+        le = gk::LaunchEvents{};
+        if (!timed) return;
         if (2 * (md->prof.recs.size() + 1) > md->prof.ev.size()) prof_flush(md);
-        hipEventRecord(md->prof.ev[2 * md->prof.recs.size()], md->stream);
+        le.start = md->prof.ev[2 * md->prof.recs.size()];
+        le.stop = md->prof.ev[2 * md->prof.recs.size() + 1];
     }
     ~Scope() {
         if (!on) return;
-        hipEventRecord(md->prof.ev[2 * md->prof.recs.size() + 1], md->stream);
-        md->prof.recs.push_back({kc, flops, bytes});
+        Prof& p = md->prof;
+        gk::LaunchEvents& le = gk::launch_events();
+        if (timed) {
+            if (le.launched > 0) p.recs.push_back({kc, flops, bytes});
+        } else if (le.launched > 0) {  // counted, not timed
+            p.n[kc] += 1;
+            p.fl[kc] += flops;
+            p.by[kc] += bytes;
+        }
+        le = gk::LaunchEvents{};
     }
 };
 
@@ -1045,10 +1068,12 @@ int gpt2_synchronize(gpt2_model* md) {
     return GPT2_OK;
 }
 
-int gpt2_profile(gpt2_model* md, int enable) {
+int gpt2_profile(gpt2_model* md, int class_mask) {
     if (!valid_model(md)) return fail(GPT2_EINVAL, "model is NULL");
+    if (class_mask & ~GPT2_PROFILE_ALL) return fail(GPT2_EINVAL, "class mask 0x%x", class_mask);
     Prof& p = md->prof;
-    if (enable) {
+    if (class_mask) {
+        p.mask = class_mask;
         if (p.ev.empty()) {
             p.ev.resize(kEventPool);
             for (auto& e : p.ev) TRY(hip_check(hipEventCreate(&e), "hipEventCreate"));

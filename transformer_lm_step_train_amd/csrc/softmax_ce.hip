@@ -125,7 +125,7 @@ __global__ __launch_bounds__(NT) __attribute__((amdgpu_waves_per_eu(4))) void so
 template <int NT, int NJ, class T>
 hipError_t launch_ce(hipStream_t s, T* logits, float* losses, const int32_t* targets, int N,
                      int V, int ldv, float dscale, const float* gscale, int* flag) {
-    hipLaunchKernelGGL((softmax_ce_kernel<NT, NJ, T>), dim3(N), dim3(NT), 0, s, logits, losses,
+    launch((softmax_ce_kernel<NT, NJ, T>), dim3(N), dim3(NT), 0, s, logits, losses,
                        targets, V, ldv, dscale, gscale, flag);
     return hipGetLastError();
 }
@@ -217,7 +217,7 @@ hipError_t sample_row(hipStream_t s, const void* logits, int V, float coin, int3
     if (V <= 0) return hipErrorInvalidValue;
     return by_dt(dt, [&](auto e) {
         using E = decltype(e);
-        hipLaunchKernelGGL(sample_kernel<E>, dim3(1), dim3(1024), 0, s, (const E*)logits, V, coin,
+        launch(sample_kernel<E>, dim3(1), dim3(1024), 0, s, (const E*)logits, V, coin,
                            out);
         return hipGetLastError();
     });
@@ -235,7 +235,7 @@ hipError_t softmax_ce(hipStream_t s, void* logits, float* losses, const int32_t*
 }
 
 hipError_t mean_reduce(hipStream_t s, float* out, const float* x, int n) {
-    hipLaunchKernelGGL(mean_kernel, dim3(1), dim3(1024), 0, s, out, x, n);
+    launch(mean_kernel, dim3(1), dim3(1024), 0, s, out, x, n);
     return hipGetLastError();
 }
 

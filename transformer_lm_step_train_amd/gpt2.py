@@ -272,8 +272,13 @@ def gpt2_synchronize(h):
     _check(lib.gpt2_synchronize(h))
 
 
+GPT2_PROFILE_ALL = (1 << len(KC_NAMES)) - 1
+
+
 def gpt2_profile(h, enable):
-    _check(lib.gpt2_profile(h, 1 if enable else 0))
+    """enable: False/0 stops; True times every class; an int is a class mask."""
+    mask = GPT2_PROFILE_ALL if enable is True else int(enable)
+    _check(lib.gpt2_profile(h, mask))
 
 
 def gpt2_profile_read(h, kernel_class):
