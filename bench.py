@@ -139,7 +139,7 @@ def pages_shape_gpu(params):
 def main():
     args = parse()
     if args.gpus != 1:
-        print(f"bench.py: --gpus {args.gpus} is not supported: this build runs on one GPU "
+        print(f"bench.py: --gpus {args.gpus} is not supported: this library runs on one GPU "
               f"only (no collectives); run with --gpus 1", file=sys.stderr)
         sys.exit(2)
     import torch

@@ -333,3 +333,36 @@ def test_full_size_sampled_rows():
     loss2 = m.forward_device(dtok, dtgt)
     assert loss2 < loss, (loss, loss2)
     m.close()
+
+
+def test_profile_class_mask():
+    """Timed classes report kernel time; the others only count launches and
+    algorithmic work, identical to the timed run's counts."""
+    g = gpt2()
+    c = synth.CONFIGS["tiny"]
+    m = g.Model(c["L"], c["C"], c["NH"], c["V"], c["maxT"], c["B"], c["T"])
+    m.set_params(synth.init_params(c["L"], c["C"], c["V"], c["maxT"]))
+    tok, tgt = synth.token_stream(c["B"], c["T"], c["V"])
+
+    def run(mask, step):
+        g.gpt2_profile(m.h, mask)
+        m.step(tok, tgt, step)
+        m.synchronize()
+        out = {n: g.gpt2_profile_read(m.h, i) for i, n in enumerate(g.KC_NAMES)}
+        g.gpt2_profile(m.h, False)
+        return out
+
+    gemm_only = run(1 << g.KC_NAMES.index("gemm"), 1)
+    every = run(True, 2)
+    assert gemm_only["gemm"]["ms"] > 0 and gemm_only["gemm"]["launches"] > 0
+    for n in g.KC_NAMES:
+        assert every[n]["launches"] == gemm_only[n]["launches"] > 0, n
+        assert every[n]["flops"] == gemm_only[n]["flops"], n
+        assert every[n]["bytes"] == gemm_only[n]["bytes"], n
+        assert every[n]["ms"] > 0, n
+        if n != "gemm":
+            assert gemm_only[n]["ms"] == 0.0, n
+    with pytest.raises(g.GPT2Error) as e:
+        g.gpt2_profile(m.h, 1 << len(g.KC_NAMES))
+    assert e.value.code == g.GPT2_EINVAL
+    m.close()
