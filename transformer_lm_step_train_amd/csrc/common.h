@@ -33,6 +33,17 @@ __device__ __forceinline__ void st4(float* p, float4 v) {
     *reinterpret_cast<float4*>(p) = v;
 }
 
+// Streaming (non-temporal) forms for single-use sweeps over large arrays.
+typedef float f32x4_t __attribute__((ext_vector_type(4)));
+__device__ __forceinline__ float4 ld4_nt(const float* p) {
+    const f32x4_t v = __builtin_nontemporal_load(reinterpret_cast<const f32x4_t*>(p));
+    return make_float4(v[0], v[1], v[2], v[3]);
+}
+__device__ __forceinline__ void st4_nt(float* p, float4 v) {
+    const f32x4_t w = {v.x, v.y, v.z, v.w};
+    __builtin_nontemporal_store(w, reinterpret_cast<f32x4_t*>(p));
+}
+
 // tanh-form GELU and its derivative.  sqrt(2/pi) is the constant of the
 // definition.  tanh(u) is evaluated from the identity
 // tanh(u) = 1 - 2 / (1 + e^(2u)) with the hardware base-2 exponential and

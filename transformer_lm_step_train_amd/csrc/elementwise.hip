@@ -269,32 +269,25 @@ __global__ __launch_bounds__(256) void adamw_kernel(float* __restrict__ p,
     if (skip && *skip) return;
     const float ig = gscale ? 1.0f / *gscale : 1.0f;
     const float ibc1 = 1.0f / bc1, ibc2 = 1.0f / bc2;
+    // One group of four per thread over the whole grid (no grid-stride
+    // loop: a grid of every group keeps the most loads in flight), with
+    // streaming loads and stores; the n % 4 tail goes to the next threads.
     const int64_t n4 = n >> 2;
-    const int64_t stride = (int64_t)gridDim.x * blockDim.x;
-    auto one4 = [&](int64_t i, float4 pp, float4 gg, float4 mm, float4 vv) {
+    const int64_t i = blockIdx.x * (int64_t)blockDim.x + threadIdx.x;
+    if (i < n4) {
+        float4 pp = ld4_nt(p + 4 * i), gg = ld4_nt(g + 4 * i), mm = ld4_nt(m + 4 * i),
+               vv = ld4_nt(v + 4 * i);
         gg = make_float4(gg.x * ig, gg.y * ig, gg.z * ig, gg.w * ig);
         adamw_one(pp.x, gg.x, mm.x, vv.x, lr, b1, b2, eps, wd, ibc1, ibc2);
         adamw_one(pp.y, gg.y, mm.y, vv.y, lr, b1, b2, eps, wd, ibc1, ibc2);
         adamw_one(pp.z, gg.z, mm.z, vv.z, lr, b1, b2, eps, wd, ibc1, ibc2);
         adamw_one(pp.w, gg.w, mm.w, vv.w, lr, b1, b2, eps, wd, ibc1, ibc2);
-        st4(p + 4 * i, pp);
-        st4(m + 4 * i, mm);
-        st4(v + 4 * i, vv);
+        st4_nt(p + 4 * i, pp);
+        st4_nt(m + 4 * i, mm);
+        st4_nt(v + 4 * i, vv);
         if (shadow) Act<S>::st(shadow + 4 * i, pp);
-    };
-    // Two groups of four per trip, so that eight loads are in flight.
-    int64_t i = blockIdx.x * (int64_t)blockDim.x + threadIdx.x;
-    for (; i + stride < n4; i += 2 * stride) {
-        const int64_t k = i + stride;
-        const float4 p0 = ld4(p + 4 * i), g0 = ld4(g + 4 * i), m0 = ld4(m + 4 * i),
-                     v0 = ld4(v + 4 * i);
-        const float4 p1 = ld4(p + 4 * k), g1 = ld4(g + 4 * k), m1 = ld4(m + 4 * k),
-                     v1 = ld4(v + 4 * k);
-        one4(i, p0, g0, m0, v0);
-        one4(k, p1, g1, m1, v1);
-    }
-    if (i < n4) one4(i, ld4(p + 4 * i), ld4(g + 4 * i), ld4(m + 4 * i), ld4(v + 4 * i));
-    for (int64_t t = 4 * n4 + blockIdx.x * (int64_t)blockDim.x + threadIdx.x; t < n; t += stride) {
+    } else if (i - n4 < (n & 3)) {
+        const int64_t t = 4 * n4 + (i - n4);
         adamw_one(p[t], g[t] * ig, m[t], v[t], lr, b1, b2, eps, wd, ibc1, ibc2);
         if (shadow) Act<S>::st1(shadow + t, p[t]);
     }
@@ -308,13 +301,21 @@ __global__ __launch_bounds__(256) void to_half_kernel(S* __restrict__ out,
         Act<S>::st1(out + i, in[i]);
 }
 
-// *flag = 1 if any of g[0..n) is not finite (inf or NaN).
+// *flag = 1 if any of g[0..n) is not finite (inf or NaN).  One group of
+// four per thread over the whole grid; the n % 4 tail goes to the next
+// threads.
 __global__ __launch_bounds__(256) void check_finite_kernel(const float* __restrict__ g, int64_t n,
                                                            int* __restrict__ flag) {
-    const int64_t stride = (int64_t)gridDim.x * blockDim.x;
+    const int64_t n4 = n >> 2;
+    const int64_t i = blockIdx.x * (int64_t)blockDim.x + threadIdx.x;
     bool bad = false;
-    for (int64_t i = blockIdx.x * (int64_t)blockDim.x + threadIdx.x; i < n; i += stride)
-        bad |= !__builtin_isfinite(g[i]);
+    if (i < n4) {
+        const float4 x = ld4_nt(g + 4 * i);
+        bad = !(__builtin_isfinite(x.x) && __builtin_isfinite(x.y) && __builtin_isfinite(x.z) &&
+                __builtin_isfinite(x.w));
+    } else if (i - n4 < (n & 3)) {
+        bad = !__builtin_isfinite(g[4 * n4 + (i - n4)]);
+    }
     if (__any(bad) && (threadIdx.x & 63) == 0) atomicOr(flag, 1);
 }
 
@@ -485,7 +486,8 @@ hipError_t adamw(hipStream_t s, float* p, const float* g, float* m, float* v, vo
                  int shadow_dt, int64_t n, float lr, float b1, float b2, float eps, float wd,
                  float bc1, float bc2, const float* gscale, const int* skip) {
     if (n <= 0) return hipSuccess;
-    const dim3 grid(grid_for(n / 4 + 1, 256, 8192));
+    // one thread per group of four, plus up to three for the tail
+    const dim3 grid(grid_for((n >> 2) + (n & 3), 256, 1u << 30));
     if (!shadow) shadow_dt = DT_F32;
     return by_dt(shadow_dt, [&](auto e) {
         using S = decltype(e);
@@ -507,8 +509,8 @@ hipError_t to_half(hipStream_t s, void* out, const float* in, int64_t n, int dt)
 
 hipError_t check_finite(hipStream_t s, const float* g, int64_t n, int* flag) {
     if (n <= 0) return hipSuccess;
-    launch(check_finite_kernel, dim3(grid_for(n, 256, 8192)), dim3(256), 0, s, g, n,
-                       flag);
+    launch(check_finite_kernel, dim3(grid_for((n >> 2) + (n & 3), 256, 1u << 30)), dim3(256), 0,
+           s, g, n, flag);
     return hipGetLastError();
 }
 
