@@ -381,7 +381,10 @@ int choose_splits(int op, int epi, int M, int N, int K) {
     if (op == GEMM_TN) {
         if (epi != EPI_ACCUM && epi != EPI_STORE) return 1;
         const int slots = resident_slots();
-        if (tiles >= 2 * slots) return 1;
+        // Many tiles and a long reduction (the LM-head weight gradient,
+        // K = B*T): four splits of at least 4096 each measured 11% faster
+        // than none (shorter reductions per tile, a fuller last round).
+        if (tiles >= 2 * slots) return K >= 4 * 4096 ? 4 : 1;
         // Smallest split count that fills about two rounds of resident
         // workgroups with little idle tail; at least 4 reduction steps each.
         const int max_splits = K / (BK * 4);
