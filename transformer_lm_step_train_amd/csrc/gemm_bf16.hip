@@ -599,22 +599,34 @@ template <int EPI, class H>
 __global__ __launch_bounds__(256) void splitk_reduce_bf16_kernel(const GemmArgsH a,
                                                                  const float* __restrict__ partial,
                                                                  int splits) {
-    const int M = a.M, N = a.N;
-    const int64_t n4 = (int64_t)M * (N / 4);
-    for (int64_t i = blockIdx.x * (int64_t)blockDim.x + threadIdx.x; i < n4;
-         i += (int64_t)gridDim.x * blockDim.x) {
-        const int64_t row = i / (N / 4);
-        const int col = (int)(i - row * (N / 4)) * 4;
-        float4 s = ld4(partial + row * N + col);
-        for (int z = 1; z < splits; z++) {
-            const float4 p = ld4(partial + (int64_t)z * M * N + row * N + col);
-            s.x += p.x;
-            s.y += p.y;
-            s.z += p.z;
-            s.w += p.w;
-        }
-        epi4<EPI, H>(a, nullptr, (int)row, col, s);
+    // One group of four outputs per thread over a grid that covers them all
+    // (the host keeps M * N / 4 below 2^31); the partial sums of a group are
+    // loaded four splits at a time, and added in split order.
+    const int N4 = a.N / 4;
+    const int64_t MN = (int64_t)a.M * a.N;
+    const int i = blockIdx.x * blockDim.x + threadIdx.x;
+    if (i >= a.M * N4) return;
+    const int row = i / N4;
+    const int col = (i - row * N4) * 4;
+    const float* p0 = partial + (int64_t)row * a.N + col;
+    float4 s = ld4(p0);
+    int z = 1;
+    for (; z + 3 < splits; z += 4) {
+        const float4 q1 = ld4(p0 + z * MN), q2 = ld4(p0 + (z + 1) * MN),
+                     q3 = ld4(p0 + (z + 2) * MN), q4 = ld4(p0 + (z + 3) * MN);
+        s.x = (((s.x + q1.x) + q2.x) + q3.x) + q4.x;
+        s.y = (((s.y + q1.y) + q2.y) + q3.y) + q4.y;
+        s.z = (((s.z + q1.z) + q2.z) + q3.z) + q4.z;
+        s.w = (((s.w + q1.w) + q2.w) + q3.w) + q4.w;
     }
+    for (; z < splits; z++) {
+        const float4 q = ld4(p0 + z * MN);
+        s.x += q.x;
+        s.y += q.y;
+        s.z += q.z;
+        s.w += q.w;
+    }
+    epi4<EPI, H>(a, nullptr, (int)row, col, s);
 }
 
 inline int cdiv(int64_t a, int64_t b) { return (int)((a + b - 1) / b); }
@@ -638,8 +650,8 @@ int cu_count_h() {
 // Which kernel, and how many K splits.  Weight gradients (TN) and input
 // gradients with a very long K (the LM head, K = V) take the 256x256 kernel
 // with the split count that minimises (rounds of one-per-CU workgroups) x
-// (reduction steps per workgroup), each split at least 4 steps; everything
-// else takes the 128x128 kernel unsplit.
+// (reduction steps per workgroup) plus the cost of the partial sums, each
+// split at least 4 steps; everything else takes the 128x128 kernel unsplit.
 struct PlanH {
     bool big;
     int splits;
@@ -659,7 +671,11 @@ PlanH plan_h(const GemmArgsH& a) {
         const int chunk = sp > 1 ? split_chunk_h(a.K, sp) : a.K;
         const int nz = sp > 1 ? cdiv(a.K, chunk) : 1;
         if (nz != sp) continue;
-        const double t = std::ceil((double)tiles * nz / cus) * std::ceil((double)chunk / BK);
+        // Each split also writes an M x N fp32 partial that the sum kernel
+        // reads back: at about 4 TB/s against about 3.4 us per 256x256x64
+        // step, M*N/1.7e6 steps per split.
+        const double t = std::ceil((double)tiles * nz / cus) * std::ceil((double)chunk / BK) +
+                         (sp > 1 ? sp * (double)a.M * a.N / 1.7e6 : 0.0);
         if (t < best_t) {
             best_t = t;
             best.splits = sp;
@@ -745,7 +761,8 @@ hipError_t run(hipStream_t s, const GemmArgsH& a, const PlanH& p, float* ws) {
     if (e != hipSuccess || p.splits <= 1) return e;
     const int nz = cdiv(a.K, split_chunk_h(a.K, p.splits));
     const int64_t n4 = (int64_t)a.M * (a.N / 4);
-    const int blocks = (int)std::min<int64_t>((n4 + 255) / 256, 4096);
+    if (n4 >= (int64_t)1 << 31) return hipErrorInvalidValue;
+    const int blocks = (int)((n4 + 255) / 256);
     if (a.epi == EPI_ACCUM)
         launch((splitk_reduce_bf16_kernel<EPI_ACCUM, H>), dim3(blocks), dim3(256), 0,
                            s, a, ws, nz);
