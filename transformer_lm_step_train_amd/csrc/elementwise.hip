@@ -229,6 +229,49 @@ __global__ __launch_bounds__(1024) void colsum_finish_kernel(float* __restrict__
     }
 }
 
+// The same sums when ncols % 4 == 0, with four columns per load: one
+// workgroup per 32 columns, 8 column lanes x 128 row lanes (lane l takes rows
+// l, l+128, ...), then a fixed pairwise tree over the row lanes, so the
+// result is the same on every run.
+__global__ __launch_bounds__(1024) void colsum4_finish_kernel(float* __restrict__ out0,
+                                                              float* __restrict__ out1,
+                                                              int split,
+                                                              const float* __restrict__ part,
+                                                              int nrows, int ncols) {
+    __shared__ float4 sh[128][8];
+    const int cl = threadIdx.x & 7, rl = threadIdx.x >> 3;
+    const int c = blockIdx.x * 32 + cl * 4;
+    float4 s = make_float4(0.f, 0.f, 0.f, 0.f);
+    if (c < ncols)
+        for (int r = rl; r < nrows; r += 128) {
+            const float4 v = ld4(part + (int64_t)r * ncols + c);
+            s.x += v.x;
+            s.y += v.y;
+            s.z += v.z;
+            s.w += v.w;
+        }
+    sh[rl][cl] = s;
+    __syncthreads();
+    for (int h = 64; h > 0; h >>= 1) {
+        if (rl < h) {
+            const float4 a = sh[rl][cl], b = sh[rl + h][cl];
+            sh[rl][cl] = make_float4(a.x + b.x, a.y + b.y, a.z + b.z, a.w + b.w);
+        }
+        __syncthreads();
+    }
+    if (rl == 0 && c < ncols) {
+        const float4 t = sh[0][cl];
+        const float v[4] = {t.x, t.y, t.z, t.w};
+#pragma unroll
+        for (int k = 0; k < 4; k++) {
+            if (c + k < split)
+                out0[c + k] += v[k];
+            else
+                out1[c + k - split] += v[k];
+        }
+    }
+}
+
 __global__ __launch_bounds__(256) void fill_zero_kernel(float* __restrict__ p, int64_t n) {
     const int64_t n4 = n >> 2;
     const int64_t stride = (int64_t)gridDim.x * blockDim.x;
@@ -470,8 +513,12 @@ hipError_t bias_grad(hipStream_t s, float* db, float* part, const void* dy, int 
 hipError_t colsum_add(hipStream_t s, float* out0, float* out1, int split, const float* part,
                       int nrows, int ncols) {
     if (nrows <= 0 || ncols <= 0) return hipSuccess;
-    launch(colsum_finish_kernel, dim3((ncols + 63) / 64), dim3(1024), 0, s, out0,
-                       out1, split, part, nrows, ncols);
+    if ((ncols & 3) == 0)
+        launch(colsum4_finish_kernel, dim3((ncols + 31) / 32), dim3(1024), 0, s, out0, out1,
+               split, part, nrows, ncols);
+    else
+        launch(colsum_finish_kernel, dim3((ncols + 63) / 64), dim3(1024), 0, s, out0, out1,
+               split, part, nrows, ncols);
     return hipGetLastError();
 }
 
