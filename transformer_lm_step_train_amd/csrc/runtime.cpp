@@ -16,6 +16,7 @@
 #include <cmath>
 #include <cstdarg>
 #include <cstdio>
+#include <cerrno>
 #include <cstring>
 #include <string>
 #include <vector>
@@ -841,6 +842,97 @@ int gpt2_copy_opt_state(gpt2_model* md, float* hm, float* hv) {
     const size_t bytes = md->lay.nparams * sizeof(float);
     if (hm) TRY(hip_check(hipMemcpy(hm, md->at<float>(md->lay.m), bytes, hipMemcpyDeviceToHost), "copy m"));
     if (hv) TRY(hip_check(hipMemcpy(hv, md->at<float>(md->lay.v), bytes, hipMemcpyDeviceToHost), "copy v"));
+    return GPT2_OK;
+}
+
+// ---- checkpoint -----------------------------------------------------------
+//
+// File: a 32-byte header {"GPT2CKPT", version 1 (u32), precision (u32),
+// nparams (i64), step (i64)}, then params, m and v as nparams little-endian
+// fp32 each, in the arena order.  Streamed through one host buffer of at most
+// 16M floats.
+
+namespace {
+
+constexpr char kCkptMagic[8] = {'G', 'P', 'T', '2', 'C', 'K', 'P', 'T'};
+struct CkptHeader {
+    char magic[8];
+    uint32_t version, precision;
+    int64_t nparams, step;
+};
+static_assert(sizeof(CkptHeader) == 32, "checkpoint header is 32 bytes");
+
+int ckpt_stream(gpt2_model* md, FILE* f, bool save) {
+    const int64_t n = md->lay.nparams;
+    const size_t chunk = (size_t)std::min<int64_t>(n, (int64_t)1 << 24);
+    std::vector<float> buf;
+    try {
+        buf.resize(chunk);
+    } catch (...) {
+        return fail(GPT2_ENOMEM, "checkpoint buffer");
+    }
+    float* arenas[3] = {md->P(0), md->at<float>(md->lay.m), md->at<float>(md->lay.v)};
+    for (float* a : arenas)
+        for (int64_t off = 0; off < n; off += (int64_t)chunk) {
+            const size_t cnt = (size_t)std::min<int64_t>((int64_t)chunk, n - off);
+            if (save) {
+                TRY(hip_check(hipMemcpy(buf.data(), a + off, cnt * 4, hipMemcpyDeviceToHost),
+                              "checkpoint read"));
+                if (fwrite(buf.data(), 4, cnt, f) != cnt)
+                    return fail(GPT2_EINVAL, "checkpoint write failed: %s", strerror(errno));
+            } else {
+                if (fread(buf.data(), 4, cnt, f) != cnt)
+                    return fail(GPT2_EINVAL, "checkpoint is truncated");
+                TRY(hip_check(hipMemcpy(a + off, buf.data(), cnt * 4, hipMemcpyHostToDevice),
+                              "checkpoint write"));
+            }
+        }
+    return GPT2_OK;
+}
+
+}  // namespace
+
+int gpt2_save_checkpoint(gpt2_model* md, const char* path, int64_t step) {
+    if (!valid_model(md) || !path) return fail(GPT2_EINVAL, "NULL argument");
+    if (step < 0) return fail(GPT2_EINVAL, "step %lld < 0", (long long)step);
+    TRY(hip_check(hipStreamSynchronize(md->stream), "synchronize"));
+    FILE* f = fopen(path, "wb");
+    if (!f) return fail(GPT2_EINVAL, "cannot open %s: %s", path, strerror(errno));
+    CkptHeader h{};
+    memcpy(h.magic, kCkptMagic, 8);
+    h.version = 1;
+    h.precision = (uint32_t)md->cfg.precision;
+    h.nparams = md->lay.nparams;
+    h.step = step;
+    int rc = fwrite(&h, sizeof h, 1, f) == 1 ? ckpt_stream(md, f, true)
+                                             : fail(GPT2_EINVAL, "checkpoint write failed");
+    if (fclose(f) != 0 && rc == GPT2_OK) rc = fail(GPT2_EINVAL, "checkpoint close failed");
+    return rc;
+}
+
+int gpt2_load_checkpoint(gpt2_model* md, const char* path, int64_t* step) {
+    if (!valid_model(md) || !path) return fail(GPT2_EINVAL, "NULL argument");
+    FILE* f = fopen(path, "rb");
+    if (!f) return fail(GPT2_EINVAL, "cannot open %s: %s", path, strerror(errno));
+    CkptHeader h{};
+    int rc = GPT2_OK;
+    if (fread(&h, sizeof h, 1, f) != 1 || memcmp(h.magic, kCkptMagic, 8) != 0 || h.version != 1)
+        rc = fail(GPT2_EINVAL, "%s is not a version-1 checkpoint", path);
+    else if (h.nparams != md->lay.nparams)
+        rc = fail(GPT2_EINVAL, "checkpoint holds %lld parameters, the model %lld",
+                  (long long)h.nparams, (long long)md->lay.nparams);
+    if (rc == GPT2_OK) rc = hip_check(hipStreamSynchronize(md->stream), "synchronize");
+    if (rc == GPT2_OK) rc = ckpt_stream(md, f, false);
+    if (rc == GPT2_OK && fgetc(f) != EOF) rc = fail(GPT2_EINVAL, "checkpoint has trailing bytes");
+    fclose(f);
+    if (rc != GPT2_OK) return rc;
+    if (md->lay.half) {  // the 16-bit weight copies follow the loaded weights
+        TRY(hip_check(gk::to_half(md->stream, md->at<uint16_t>(md->lay.shadow), md->P(0),
+                                  md->lay.nparams, md->lay.dt),
+                      "16-bit weight copy"));
+        TRY(hip_check(hipStreamSynchronize(md->stream), "synchronize"));
+    }
+    if (step) *step = h.step;
     return GPT2_OK;
 }
 

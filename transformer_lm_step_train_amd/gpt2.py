@@ -74,6 +74,8 @@ def _load():
         "gpt2_copy_params": (_c.c_int, [_vp, _vp, _vp]),
         "gpt2_copy_grads": (_c.c_int, [_vp, _vp]),
         "gpt2_copy_opt_state": (_c.c_int, [_vp, _vp, _vp]),
+        "gpt2_save_checkpoint": (_c.c_int, [_vp, _c.c_char_p, _i64]),
+        "gpt2_load_checkpoint": (_c.c_int, [_vp, _c.c_char_p, P(_i64)]),
         "gpt2_copy_activation": (_c.c_int, [_vp, _c.c_char_p, _c.c_int, _vp, P(_i64)]),
         "gpt2_forward": (_c.c_int, [_vp, _vp, _vp, _c.c_int, _c.c_int, P(_c.c_float)]),
         "gpt2_forward_device": (_c.c_int, [_vp, _vp, _vp, _c.c_int, _c.c_int,
@@ -138,6 +140,16 @@ def gpt2_config_param_tensor(cfg, i):
     _check(lib.gpt2_config_param_tensor(_c.byref(cfg), i, _c.byref(name), _c.byref(off),
                                         _c.byref(n)))
     return name.value.decode(), off.value, n.value
+
+
+def gpt2_save_checkpoint(h, path, step):
+    _check(lib.gpt2_save_checkpoint(h, os.fsencode(path), step))
+
+
+def gpt2_load_checkpoint(h, path) -> int:
+    step = _i64()
+    _check(lib.gpt2_load_checkpoint(h, os.fsencode(path), _c.byref(step)))
+    return step.value
 
 
 def gpt2_config_device_bytes(cfg) -> int:
@@ -360,6 +372,14 @@ class Model:
         v = np.empty(self.num_params, dtype=np.float32)
         gpt2_copy_opt_state(self.h, m, v)
         return m, v
+
+    def save_checkpoint(self, path, step):
+        """Parameters, AdamW moments and the step counter to one file."""
+        gpt2_save_checkpoint(self.h, path, step)
+
+    def load_checkpoint(self, path):
+        """Restores a save_checkpoint file; returns its step counter."""
+        return gpt2_load_checkpoint(self.h, path)
 
     def activation(self, name, layer=0):
         n = gpt2_copy_activation(self.h, name, layer)
