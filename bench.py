@@ -39,8 +39,11 @@ def parse():
                     help="fp32 (the headline workload), or the bf16 / fp16 mixed-precision "
                          "model")
     ap.add_argument("--no-kernel-timing", action="store_true",
-                    help="do not record per-launch HIP events in the timed steps")
-    return ap.parse_args()
+                    help="no kernel events: no roofline object and no instrumented second pass")
+    a = ap.parse_args()
+    if a.steps < 1 or a.warmup < 0:
+        ap.error("--steps must be at least 1 and --warmup at least 0")
+    return a
 
 
 def source_hash():
