@@ -7,26 +7,29 @@
 //
 // Tiling: a 256-thread workgroup owns a 128x128 output tile; its four waves
 // each own 64x64 (2x2 blocks of the 32x32 MFMA).  The reduction runs in
-// steps of 32 staged through two LDS buffers (one barrier per step) while
-// the global loads of the step after next are in flight in registers, so
-// each load has two steps of MFMA work to arrive.  Within a step the two
-// 32-lane halves of a wave own k = 0..15 and k = 16..31, so an operand
-// stored k-contiguous is read from LDS as float4 (four MFMA steps per read).
-// The main loop loads only whole reduction steps, with rows past the
-// matrix clamped to its last row, so every step issues the same loads and
-// the wait for the registers of the previous step is exact; a partial last
-// step is loaded with zero padding after the loop.
+// steps of BK (16, or 32 for the LM head's long-K input gradient) staged
+// through two LDS buffers (one barrier per step) while the global loads of
+// the step after next are in flight in registers.  Within a step the two
+// 32-lane halves of a wave own k = 0..BK/2-1 and k = BK/2..BK-1, so an
+// operand stored k-contiguous is read from LDS as float4 (four MFMA steps
+// per read).  The main loop loads only whole reduction steps, with rows past
+// the matrix clamped to its last row, so every step issues the same loads
+// and the wait for the registers of the previous step is exact; a partial
+// last step is loaded with zero padding after the loop.
 //
 // Operands whose reduction index is contiguous in HBM are stored in LDS as
-// [row][k] (36-float rows); operands whose free index is contiguous are
-// stored as [k][row] (132-float rows).  Both are written with float4.
+// [row][k] (BK+4 floats per row); operands whose free index is contiguous
+// are stored as [k][row] (132-float rows).  Both are written with float4.
+// At BK = 16 the workgroup needs 40 KB of LDS and at most 168 VGPRs, so
+// three share a compute unit.
 //
-// The epilogue stages each wave's 64x64 block through LDS and then works
-// along rows with float4 loads and stores, fusing what the layer does next:
-// bias, residual add, GELU (writing both pre- and post-activation), the
-// GELU derivative of the backward, or += into a gradient.  Large reductions
-// over few output tiles are split over K into a workspace and summed in a
-// fixed order by a second kernel, so results are deterministic.
+// The epilogue stages each wave's 64x64 block through LDS in two 32-row
+// halves and then works along rows with float4 loads and stores, fusing
+// what the layer does next: bias, residual add, GELU (writing both pre- and
+// post-activation), the GELU derivative of the backward, or += into a
+// gradient.  Large reductions over few output tiles are split over K into a
+// workspace and summed in a fixed order by a second kernel, so results are
+// deterministic.
 #include <algorithm>
 #include <cmath>
 #include <type_traits>
@@ -37,22 +40,24 @@
 namespace gk {
 namespace {
 
-constexpr int BM = 128, BN = 128, BK = 32, NTHR = 256;
+constexpr int BM = 128, BN = 128, NTHR = 256;
+constexpr int BK_SPLIT = 32;     // split-K chunks are multiples of every step depth
 constexpr int PF = 2;            // register prefetch depth (tiles in flight)
-constexpr int FM_LD = BK + 4;    // [row][k] tile row stride
 constexpr int EPI_PARTIAL = 100; // internal: write split-K partial sums
 
 __device__ __forceinline__ floatx16 mfma(float a, float b, floatx16 c) {
     return __builtin_amdgcn_mfma_f32_32x32x2f32(a, b, c, 0, 0, 0);
 }
 
-template <bool KC, int R, int NT>
+template <bool KC, int R, int NT, int BK>
 struct Tile;
 
-template <int R, int NT>
-struct Tile<true, R, NT> {
+template <int R, int NT, int BK>
+struct Tile<true, R, NT, BK> {
+    static constexpr int FM_LD = BK + 4;  // [row][k] row stride
+    static constexpr int KV = BK / 4;     // float4 per row per step
     static constexpr int FLOATS = R * FM_LD;
-    static constexpr int PER = R * 8 / NT;
+    static constexpr int PER = R * KV / NT;
     float4 v[PER];
     // Rows past the matrix read its last row instead (their products land
     // only in outputs that are never stored).  TAIL loads a last, partial
@@ -64,8 +69,8 @@ struct Tile<true, R, NT> {
 #pragma unroll
         for (int i = 0; i < PER; i++) {
             const int idx = threadIdx.x + NT * i;
-            const int r = min(r0 + (idx >> 3), Rn - 1);
-            const int k = k0 + (idx & 7) * 4;
+            const int r = min(r0 + idx / KV, Rn - 1);
+            const int k = k0 + (idx % KV) * 4;
             if (!TAIL) {
                 v[i] = ld4(g + (int64_t)r * ld + k);
             } else {
@@ -82,16 +87,16 @@ struct Tile<true, R, NT> {
 #pragma unroll
         for (int i = 0; i < PER; i++) {
             const int idx = threadIdx.x + NT * i;
-            st4(s + (idx >> 3) * FM_LD + (idx & 7) * 4, v[i]);
+            st4(s + (idx / KV) * FM_LD + (idx % KV) * 4, v[i]);
         }
     }
     __device__ static __forceinline__ float4 frag(const float* s, int r, int g, int q) {
-        return ld4(s + r * FM_LD + 16 * g + 4 * q);
+        return ld4(s + r * FM_LD + (BK / 2) * g + 4 * q);
     }
 };
 
-template <int R, int NT>
-struct Tile<false, R, NT> {
+template <int R, int NT, int BK>
+struct Tile<false, R, NT, BK> {
     static constexpr int LDK = R + 4;
     static constexpr int FLOATS = BK * LDK;
     static constexpr int PER = BK * R / 4 / NT;
@@ -125,7 +130,7 @@ struct Tile<false, R, NT> {
         }
     }
     __device__ static __forceinline__ float4 frag(const float* s, int r, int g, int q) {
-        const float* p = s + (16 * g + 4 * q) * LDK + r;
+        const float* p = s + ((BK / 2) * g + 4 * q) * LDK + r;
         return make_float4(p[0], p[LDK], p[2 * LDK], p[3 * LDK]);
     }
 };
@@ -180,16 +185,16 @@ __device__ __forceinline__ void epi_scalar(const GemmArgs& a, float* __restrict_
     if (EPI == EPI_GELU) a.out2[idx] = gelu_f(v);
 }
 
-template <int OP, int EPI>
-__global__ __launch_bounds__(NTHR, 2) void gemm_kernel(
+template <int OP, int EPI, int BK>
+__global__ __launch_bounds__(NTHR, BK == 16 ? 3 : 2) void gemm_kernel(
     const GemmArgs a, int tiles_m, int tiles_n, int kchunk, float* __restrict__ partial) {
     constexpr int NT = NTHR;
     constexpr bool AKC = (OP != GEMM_TN);
     constexpr bool BKC = (OP == GEMM_NT);
-    using TA = Tile<AKC, BM, NT>;
-    using TB = Tile<BKC, BN, NT>;
+    using TA = Tile<AKC, BM, NT, BK>;
+    using TB = Tile<BKC, BN, NT, BK>;
     constexpr int MAIN = 2 * (TA::FLOATS + TB::FLOATS);
-    constexpr int EPIF = (NT / 64) * 64 * 68;  // epilogue staging, one 64x68 block per wave
+    constexpr int EPIF = (NT / 64) * 32 * 68;  // epilogue staging, one 32x68 half-block per wave
     constexpr int SMEM = MAIN > EPIF ? MAIN : EPIF;
     __shared__ __attribute__((aligned(16))) float sm[SMEM];
 
@@ -233,7 +238,7 @@ __global__ __launch_bounds__(NTHR, 2) void gemm_kernel(
     };
     auto compute = [&](const float* sa, const float* sb) {
 #pragma unroll
-        for (int q = 0; q < 4; q++) {
+        for (int q = 0; q < BK / 8; q++) {
             const float4 a0 = TA::frag(sa, wm + li, g, q);
             const float4 a1 = TA::frag(sa, wm + 32 + li, g, q);
             const float4 b0 = TB::frag(sb, wn + li, g, q);
@@ -296,30 +301,33 @@ __global__ __launch_bounds__(NTHR, 2) void gemm_kernel(
         __syncthreads();
     }
 
-    // Stage this wave's 64x64 block in LDS (the main loop's buffers are free
-    // after the last barrier), then apply the epilogue along rows with float4.
-    float* ws = sm + wave * 64 * 68;
+    // Stage this wave's 64x64 block in LDS one 32-row half at a time (the
+    // main loop's buffers are free after its last barrier), then apply the
+    // epilogue along rows with float4.
+    float* ws = sm + wave * 32 * 68;
 #pragma unroll
-    for (int bm = 0; bm < 2; bm++)
+    for (int bm = 0; bm < 2; bm++) {
+        if (bm == 1) __syncthreads();  // every wave has read its first half
 #pragma unroll
         for (int bn = 0; bn < 2; bn++)
 #pragma unroll
             for (int e = 0; e < 16; e++)
-                ws[(32 * bm + 8 * (e >> 2) + 4 * g + (e & 3)) * 68 + 32 * bn + li] = acc[bm][bn][e];
-    __syncthreads();
+                ws[(8 * (e >> 2) + 4 * g + (e & 3)) * 68 + 32 * bn + li] = acc[bm][bn][e];
+        __syncthreads();
 #pragma unroll 4
-    for (int j = 0; j < 16; j++) {
-        const int idx = lane + 64 * j;
-        const int r = idx >> 4, c4 = (idx & 15) * 4;
-        const float4 v = ld4(ws + r * 68 + c4);
-        const int row = m0 + wm + r, col = n0 + wn + c4;
-        if (row >= a.M) continue;
-        if (col + 3 < a.N) {
-            epi_store<EPI>(a, partial, row, col, v);
-        } else {
-            if (col < a.N) epi_scalar<EPI>(a, partial, row, col, v.x);
-            if (col + 1 < a.N) epi_scalar<EPI>(a, partial, row, col + 1, v.y);
-            if (col + 2 < a.N) epi_scalar<EPI>(a, partial, row, col + 2, v.z);
+        for (int j = 0; j < 8; j++) {
+            const int idx = lane + 64 * j;
+            const int r = idx >> 4, c4 = (idx & 15) * 4;
+            const float4 v = ld4(ws + r * 68 + c4);
+            const int row = m0 + wm + 32 * bm + r, col = n0 + wn + c4;
+            if (row >= a.M) continue;
+            if (col + 3 < a.N) {
+                epi_store<EPI>(a, partial, row, col, v);
+            } else {
+                if (col < a.N) epi_scalar<EPI>(a, partial, row, col, v.x);
+                if (col + 1 < a.N) epi_scalar<EPI>(a, partial, row, col + 1, v.y);
+                if (col + 2 < a.N) epi_scalar<EPI>(a, partial, row, col + 2, v.z);
+            }
         }
     }
 }
@@ -363,7 +371,9 @@ __global__ __launch_bounds__(256) void splitk_reduce_kernel(const GemmArgs a,
 
 inline int cdiv(int64_t a, int64_t b) { return (int)((a + b - 1) / b); }
 
-// Workgroups resident at once (two per compute unit).
+// The unit of the split plan: two workgroups per compute unit.  The 16-step
+// kernel can hold three, but plans sized for three split the weight
+// gradients further and measured slower.
 int resident_slots() {
     static int slots = 0;
     if (!slots) {
@@ -379,7 +389,7 @@ int resident_slots() {
 
 int split_chunk(int K, int splits) {
     int c = cdiv(K, splits);
-    return cdiv(c, BK) * BK;
+    return cdiv(c, BK_SPLIT) * BK_SPLIT;
 }
 
 // Split the reduction over K when the output tiles alone leave the chip
@@ -399,7 +409,7 @@ int choose_splits(int op, int epi, int M, int N, int K) {
         if (tiles >= 2 * slots) return K >= 4 * 4096 ? 4 : 1;
         // Smallest split count that fills about two rounds of resident
         // workgroups with little idle tail; at least 4 reduction steps each.
-        const int max_splits = K / (BK * 4);
+        const int max_splits = K / (BK_SPLIT * 4);
         int best = 1;
         double best_eff = 0.0;
         for (int sp = 2; sp <= max_splits; sp++) {
@@ -422,14 +432,23 @@ int choose_splits(int op, int epi, int M, int N, int K) {
 }
 
 
+// Reduction steps of 16 let three workgroups share a compute unit (40 KB of
+// LDS each) and measured 2-5% faster on every product of the step but one:
+// the input gradient of the LM head (K = V), whose A operand streams from
+// HBM, keeps steps of 32 so that each row is fetched in 128-byte pieces.
 template <int OP, int EPI>
 hipError_t launch(hipStream_t s, const GemmArgs& a, int splits, float* ws) {
     const int tm = cdiv(a.M, BM), tn = cdiv(a.N, BN);
     const int chunk = splits > 1 ? split_chunk(a.K, splits) : (a.K > 0 ? a.K : 1);
     const int nz = splits > 1 ? cdiv(a.K, chunk) : 1;
     dim3 grid(tm * tn, 1, nz);
-    launch((gemm_kernel<OP, EPI>), grid, dim3(NTHR), 0, s, a, tm, tn, chunk,
-                       ws);
+    if constexpr (OP == GEMM_NN) {
+        if (a.K >= 8192) {
+            launch((gemm_kernel<OP, EPI, 32>), grid, dim3(NTHR), 0, s, a, tm, tn, chunk, ws);
+            return hipGetLastError();
+        }
+    }
+    launch((gemm_kernel<OP, EPI, 16>), grid, dim3(NTHR), 0, s, a, tm, tn, chunk, ws);
     return hipGetLastError();
 }
 
