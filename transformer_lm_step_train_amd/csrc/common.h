@@ -151,6 +151,11 @@ __device__ __forceinline__ __amdgpu_buffer_rsrc_t buf_rsrc(const void* p, uint32
     return __builtin_amdgcn_make_buffer_rsrc(const_cast<void*>(p), 0, (int)bytes, 0x00020000);
 }
 
+// Cache policy of the streaming buffer accesses below: non-temporal (the
+// data is touched once).  On the vocabulary softmax (3.3 GB read, 3.3 GB
+// written) it measured 1182 against 1293 us with the default policy.
+constexpr int BUF_NT = 2;
+
 template <class T>
 struct BufAct;
 
@@ -158,14 +163,14 @@ template <>
 struct BufAct<float> {
     static constexpr int BYTES = 16;  // four elements
     static __device__ __forceinline__ float4 ld(__amdgpu_buffer_rsrc_t r, int vo, int so) {
-        const u32x4_t u = __builtin_amdgcn_raw_buffer_load_b128(r, vo, so, 0);
+        const u32x4_t u = __builtin_amdgcn_raw_buffer_load_b128(r, vo, so, BUF_NT);
         return make_float4(__uint_as_float(u[0]), __uint_as_float(u[1]), __uint_as_float(u[2]),
                            __uint_as_float(u[3]));
     }
     static __device__ __forceinline__ void st(__amdgpu_buffer_rsrc_t r, int vo, int so, float4 v) {
         const u32x4_t u = {__float_as_uint(v.x), __float_as_uint(v.y), __float_as_uint(v.z),
                            __float_as_uint(v.w)};
-        __builtin_amdgcn_raw_buffer_store_b128(u, r, vo, so, 0);
+        __builtin_amdgcn_raw_buffer_store_b128(u, r, vo, so, BUF_NT);
     }
 };
 
@@ -173,14 +178,14 @@ template <>
 struct BufAct<uint16_t> {
     static constexpr int BYTES = 8;
     static __device__ __forceinline__ float4 ld(__amdgpu_buffer_rsrc_t r, int vo, int so) {
-        const u32x2_t u = __builtin_amdgcn_raw_buffer_load_b64(r, vo, so, 0);
+        const u32x2_t u = __builtin_amdgcn_raw_buffer_load_b64(r, vo, so, BUF_NT);
         return make_float4(__uint_as_float(u[0] << 16), __uint_as_float(u[0] & 0xffff0000u),
                            __uint_as_float(u[1] << 16), __uint_as_float(u[1] & 0xffff0000u));
     }
     static __device__ __forceinline__ void st(__amdgpu_buffer_rsrc_t r, int vo, int so, float4 v) {
         const u32x2_t u = {f2bf(v.x) | ((uint32_t)f2bf(v.y) << 16),
                            f2bf(v.z) | ((uint32_t)f2bf(v.w) << 16)};
-        __builtin_amdgcn_raw_buffer_store_b64(u, r, vo, so, 0);
+        __builtin_amdgcn_raw_buffer_store_b64(u, r, vo, so, BUF_NT);
     }
 };
 
@@ -189,12 +194,12 @@ struct BufAct<_Float16> {
     static constexpr int BYTES = 8;
     typedef _Float16 h4 __attribute__((ext_vector_type(4)));
     static __device__ __forceinline__ float4 ld(__amdgpu_buffer_rsrc_t r, int vo, int so) {
-        const h4 u = __builtin_bit_cast(h4, __builtin_amdgcn_raw_buffer_load_b64(r, vo, so, 0));
+        const h4 u = __builtin_bit_cast(h4, __builtin_amdgcn_raw_buffer_load_b64(r, vo, so, BUF_NT));
         return make_float4((float)u[0], (float)u[1], (float)u[2], (float)u[3]);
     }
     static __device__ __forceinline__ void st(__amdgpu_buffer_rsrc_t r, int vo, int so, float4 v) {
         const h4 u = {(_Float16)v.x, (_Float16)v.y, (_Float16)v.z, (_Float16)v.w};
-        __builtin_amdgcn_raw_buffer_store_b64(__builtin_bit_cast(u32x2_t, u), r, vo, so, 0);
+        __builtin_amdgcn_raw_buffer_store_b64(__builtin_bit_cast(u32x2_t, u), r, vo, so, BUF_NT);
     }
 };
 
