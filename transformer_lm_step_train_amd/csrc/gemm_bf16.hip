@@ -15,8 +15,11 @@
 // matrix clamped to its last row; a partial last step is zero-padded after
 // the loop).  In LDS every operand is stored [row][k] (72 bf16 per row), so
 // each MFMA operand (8 consecutive k of one row) is one 16-byte read.
-// Operands whose free index is contiguous in HBM are loaded as 8 rows of k by
-// 4 columns per thread and transposed in registers before the LDS store.
+// The B operand of the input gradients (NN: the weight, contiguous along n)
+// stays [k][n] in LDS and is read with gfx950's transposing LDS loads (see
+// TileT below); other operands whose free index is contiguous in HBM are
+// loaded as 8 rows of k by 4 columns per thread and transposed in registers
+// before the LDS store.
 //
 // Weight gradients and the LM-head input gradient split K and take the
 // 256x256 kernel further below.
@@ -131,6 +134,63 @@ __device__ __forceinline__ uint4 frag(const uint16_t* s, int r, int g, int q) {
     return *reinterpret_cast<const uint4*>(s + r * LDH + 16 * q + 8 * g);
 }
 
+// Free index contiguous, kept in LDS as it lies in HBM: [k][n], 16-byte runs
+// of 8 consecutive n (leading dimension a multiple of 8, base 16-byte
+// aligned).  The MFMA operand (8 consecutive k of one column) is gathered by
+// two transposing LDS reads (ds_read_b64_tr_b16).  In each 16-lane group of
+// such a read, lane r addresses 4 consecutive columns of one k-row, and lane
+// j receives element j of each 16-element row of the group's 16x4 block.
+// Lane r at (k0 + r/4, n0 + 4*(r%4)) therefore hands lane j the four values
+// (k0..k0+3, n0 + j).
+struct TileT {
+    static constexpr int LDN = BN + 16;  // LDS row stride along n, bf16 elements
+    static constexpr int ELEMS = BK * LDN;
+    uint4 v[4];
+    // Runs past the last column read the last whole run instead (their
+    // products reach only outputs that are never stored); TAIL zeroes
+    // k >= K of a partial last reduction step.
+    template <bool TAIL>
+    __device__ __forceinline__ void load(const uint16_t* __restrict__ g, int64_t ld, int n0,
+                                         int N, int k0, int K) {
+#pragma unroll
+        for (int i = 0; i < 4; i++) {
+            const int idx = threadIdx.x + NTHR * i;
+            const int k = k0 + (idx >> 4);
+            int n = n0 + (idx & 15) * 8;
+            n = n < N ? n : ((N - 1) & ~7);
+            if (!TAIL) {
+                v[i] = *reinterpret_cast<const uint4*>(g + (int64_t)k * ld + n);
+            } else {
+                const uint4 x = *reinterpret_cast<const uint4*>(g + (int64_t)(k < K ? k : 0) * ld + n);
+                v[i] = k < K ? x : make_uint4(0u, 0u, 0u, 0u);
+            }
+        }
+    }
+    __device__ __forceinline__ void store(uint16_t* s) const {
+#pragma unroll
+        for (int i = 0; i < 4; i++) {
+            const int idx = threadIdx.x + NTHR * i;
+            *reinterpret_cast<uint4*>(s + (idx >> 4) * LDN + (idx & 15) * 8) = v[i];
+        }
+    }
+};
+
+typedef short tr4_t __attribute__((ext_vector_type(4)));
+typedef __attribute__((address_space(3))) tr4_t* lds_tr4_ptr;
+
+// Operand of columns nb..nb+31 (lane li = column nb + li), k = 16q + 8g .. +7,
+// from a TileT tile.
+__device__ __forceinline__ uint4 frag_tr(const uint16_t* s, int nb, int q, int lane) {
+    const int grp = lane >> 4, r = lane & 15;
+    const int n = nb + 16 * (grp & 1) + 4 * (r & 3);
+    const int k = 16 * q + 8 * (grp >> 1) + (r >> 2);
+    const uint16_t* p = s + k * TileT::LDN + n;
+    const tr4_t lo = __builtin_amdgcn_ds_read_tr16_b64_v4i16((lds_tr4_ptr)p);
+    const tr4_t hi = __builtin_amdgcn_ds_read_tr16_b64_v4i16((lds_tr4_ptr)(p + 4 * TileT::LDN));
+    const uint2 a = __builtin_bit_cast(uint2, lo), b = __builtin_bit_cast(uint2, hi);
+    return make_uint4(a.x, a.y, b.x, b.y);
+}
+
 template <class H>
 __device__ __forceinline__ float4 ld4h(const uint16_t* p) {
     const uint2 u = *reinterpret_cast<const uint2*>(p);
@@ -208,14 +268,14 @@ __device__ __forceinline__ void epi1(const GemmArgsH& a, float* __restrict__ par
     if (EPI == EPI_GELU) a.out2[idx] = H::h(gelu_f(v));
 }
 
-template <int OP, int EPI, class H>
+template <int OP, int EPI, class H, bool TRB>
 __global__ __launch_bounds__(NTHR, 2) void gemm_bf16_kernel(const GemmArgsH a, int tiles_m,
                                                             int tiles_n, int kchunk,
                                                             float* __restrict__ partial) {
     constexpr bool AKC = (OP != GEMM_TN);
     constexpr bool BKC = (OP == GEMM_NT);
     using TA = TileH<AKC>;
-    using TB = TileH<BKC>;
+    using TB = std::conditional_t<TRB, TileT, TileH<BKC>>;
     constexpr int MAIN_BYTES = 2 * (TA::ELEMS + TB::ELEMS) * 2;
     constexpr int EPI_BYTES = 4 * 64 * 68 * 4;
     constexpr int SMEM = MAIN_BYTES > EPI_BYTES ? MAIN_BYTES : EPI_BYTES;
@@ -264,8 +324,14 @@ __global__ __launch_bounds__(NTHR, 2) void gemm_bf16_kernel(const GemmArgsH a, i
         for (int q = 0; q < BK / 16; q++) {
             const uint4 a0 = frag(sa, wm + li, g, q);
             const uint4 a1 = frag(sa, wm + 32 + li, g, q);
-            const uint4 b0 = frag(sb, wn + li, g, q);
-            const uint4 b1 = frag(sb, wn + 32 + li, g, q);
+            uint4 b0, b1;
+            if constexpr (TRB) {
+                b0 = frag_tr(sb, wn, q, lane);
+                b1 = frag_tr(sb, wn + 32, q, lane);
+            } else {
+                b0 = frag(sb, wn + li, g, q);
+                b1 = frag(sb, wn + 32 + li, g, q);
+            }
             acc[0][0] = H::mma(a0, b0, acc[0][0]);
             acc[0][1] = H::mma(a0, b1, acc[0][1]);
             acc[1][0] = H::mma(a1, b0, acc[1][0]);
@@ -687,7 +753,14 @@ PlanH plan_h(const GemmArgsH& a) {
 template <int OP, int EPI, class H>
 hipError_t launch_h(hipStream_t s, const GemmArgsH& a, float* ws) {
     const int tm = cdiv(a.M, BM), tn = cdiv(a.N, BN);
-    launch((gemm_bf16_kernel<OP, EPI, H>), dim3(tm * tn, 1, 1), dim3(NTHR), 0, s, a, tm,
+    if constexpr (OP == GEMM_NN) {
+        if (a.ldb % 8 == 0 && ((uintptr_t)a.B & 15) == 0) {
+            launch((gemm_bf16_kernel<OP, EPI, H, true>), dim3(tm * tn, 1, 1), dim3(NTHR), 0, s,
+                   a, tm, tn, a.K > 0 ? a.K : 1, ws);
+            return hipGetLastError();
+        }
+    }
+    launch((gemm_bf16_kernel<OP, EPI, H, false>), dim3(tm * tn, 1, 1), dim3(NTHR), 0, s, a, tm,
                        tn, a.K > 0 ? a.K : 1, ws);
     return hipGetLastError();
 }
