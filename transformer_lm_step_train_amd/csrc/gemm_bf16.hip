@@ -408,11 +408,14 @@ __global__ __launch_bounds__(NTHR, 2) void gemm_bf16_kernel(const GemmArgsH a, i
 // weight gradients (K = B*T, few output tiles) and the LM-head input
 // gradient (K = V) split K; there a 256x256 tile per workgroup (4 x 4 blocks
 // per wave, one workgroup per CU) halves the operand traffic per MFMA from
-// LDS and L2 and measured 10-45% faster.  Its LDS rows hold 64 bf16 with the
-// eight 16-byte chunks permuted by chunk ^ ((row >> 1) & 7), so operand
-// reads and the stores of both loaders avoid bank conflicts without padding;
-// operands whose free index is contiguous are loaded as 8 rows x 8 k blocks
-// and transposed in registers.
+// LDS and L2 and measured 10-45% faster.  Operands contiguous in k sit in LDS
+// as rows of 64 bf16 with the eight 16-byte chunks permuted by
+// chunk ^ ((row >> 1) & 7), so their reads and stores avoid bank conflicts
+// without padding.  Operands contiguous in the free index (both operands of
+// the weight gradients, the weight of the LM-head input gradient) stay
+// [k][row] and are read with the transposing LDS loads; against an 8 x 8
+// register transpose that took these products from 8.2 to 7.4 ms per step
+// with bit-identical results.
 // element offset of 16-byte chunk c (0..7) of row r
 __device__ __forceinline__ int sw(int r, int c) { return r * BK + 8 * (c ^ ((r >> 1) & 7)); }
 
@@ -423,6 +426,7 @@ struct TileS;
 // 16-byte chunks (8 consecutive k of one row).
 template <int R>
 struct TileS<true, R> {
+    static constexpr int ELEMS = R * BK;
     static constexpr int PER = R * 8 / NTHR;
     uint4 v[PER];
     template <bool TAIL>
@@ -459,64 +463,56 @@ struct TileS<true, R> {
     }
 };
 
-// Free index contiguous: element (r, k) at g[k*ld + r].  A task is 8 rows x
-// 8 k: eight 16-byte loads (8 rows at one k), transposed in registers into
-// eight 16-byte row chunks.  With fewer tasks than threads the spare
-// threads repeat a task's loads (the same count of loads everywhere) and
-// skip its store.
+__device__ __forceinline__ uint4 frag_s(const uint16_t* s, int r, int g, int q) {
+    return *reinterpret_cast<const uint4*>(s + sw(r, 2 * q + g));
+}
+
+// Free index contiguous, kept [k][r] in LDS (rows of R + 16 values) and read
+// with the transposing LDS loads, as TileT above: a thread moves 16-byte runs
+// of 8 consecutive r at one k.
 template <int R>
-struct TileS<false, R> {
-    static constexpr int TASKS = R;  // (R / 8 row groups) x (8 k chunks)
-    static constexpr int PER = (TASKS + NTHR - 1) / NTHR;
-    uint4 v[PER][8];
+struct TileSTr {
+    static constexpr int LDR = R + 16;
+    static constexpr int ELEMS = BK * LDR;
+    static constexpr int RUNS = R / 8;              // runs per k-row
+    static constexpr int PER = BK * RUNS / NTHR;
+    uint4 v[PER];
     template <bool TAIL>
     __device__ __forceinline__ void load(const uint16_t* __restrict__ g, int64_t ld, int r0,
                                          int Rn, int k0, int K) {
 #pragma unroll
-        for (int t = 0; t < PER; t++) {
-            const int idx = (threadIdx.x + NTHR * t) % TASKS;
-            const int c = idx & 7;
-            int r = r0 + (idx >> 3) * 8;
+        for (int i = 0; i < PER; i++) {
+            const int idx = threadIdx.x + NTHR * i;
+            const int k = k0 + idx / RUNS;
+            int r = r0 + (idx % RUNS) * 8;
             r = r < Rn ? r : ((Rn - 1) & ~7);
-#pragma unroll
-            for (int i = 0; i < 8; i++) {
-                const int k = k0 + 8 * c + i;
-                if (!TAIL) {
-                    v[t][i] = *reinterpret_cast<const uint4*>(g + (int64_t)k * ld + r);
-                } else {
-                    const uint4 x =
-                        *reinterpret_cast<const uint4*>(g + (int64_t)(k < K ? k : 0) * ld + r);
-                    v[t][i] = k < K ? x : make_uint4(0u, 0u, 0u, 0u);
-                }
+            if (!TAIL) {
+                v[i] = *reinterpret_cast<const uint4*>(g + (int64_t)k * ld + r);
+            } else {
+                const uint4 x = *reinterpret_cast<const uint4*>(g + (int64_t)(k < K ? k : 0) * ld + r);
+                v[i] = k < K ? x : make_uint4(0u, 0u, 0u, 0u);
             }
         }
     }
     __device__ __forceinline__ void store(uint16_t* s) const {
 #pragma unroll
-        for (int t = 0; t < PER; t++) {
-            const int idx = threadIdx.x + NTHR * t;
-            if (TASKS % NTHR != 0 && idx >= TASKS) continue;
-            const int c = idx & 7, rb = (idx >> 3) * 8;
-            // row rb + j holds element j of each of the 8 loaded k-rows
-#pragma unroll
-            for (int j = 0; j < 8; j++) {
-                uint32_t e[8];
-#pragma unroll
-                for (int i = 0; i < 8; i++) {
-                    const uint32_t w = (&v[t][i].x)[j >> 1];
-                    e[i] = (j & 1) ? (w >> 16) : (w & 0xFFFFu);
-                }
-                *reinterpret_cast<uint4*>(s + sw(rb + j, c)) =
-                    make_uint4(e[0] | (e[1] << 16), e[2] | (e[3] << 16), e[4] | (e[5] << 16),
-                               e[6] | (e[7] << 16));
-            }
+        for (int i = 0; i < PER; i++) {
+            const int idx = threadIdx.x + NTHR * i;
+            *reinterpret_cast<uint4*>(s + (idx / RUNS) * LDR + (idx % RUNS) * 8) = v[i];
         }
     }
+    // operand of rows rb..rb+31 (lane li = row rb + li), k = 16q + 8g .. +7
+    __device__ static __forceinline__ uint4 frag(const uint16_t* s, int rb, int q, int lane) {
+        const int grp = lane >> 4, rr = lane & 15;
+        const int r = rb + 16 * (grp & 1) + 4 * (rr & 3);
+        const int k = 16 * q + 8 * (grp >> 1) + (rr >> 2);
+        const uint16_t* p = s + k * LDR + r;
+        const tr4_t lo = __builtin_amdgcn_ds_read_tr16_b64_v4i16((lds_tr4_ptr)p);
+        const tr4_t hi = __builtin_amdgcn_ds_read_tr16_b64_v4i16((lds_tr4_ptr)(p + 4 * LDR));
+        const uint2 a = __builtin_bit_cast(uint2, lo), b = __builtin_bit_cast(uint2, hi);
+        return make_uint4(a.x, a.y, b.x, b.y);
+    }
 };
-
-__device__ __forceinline__ uint4 frag_s(const uint16_t* s, int r, int g, int q) {
-    return *reinterpret_cast<const uint4*>(s + sw(r, 2 * q + g));
-}
 
 template <int MI, int NI>
 struct Shape {
@@ -535,9 +531,11 @@ __global__ __launch_bounds__(NTHR, (Shape<MI, NI>::OCC)) void gemm_bf16_big_kern
     using SH = Shape<MI, NI>;
     constexpr bool AKC = (OP != GEMM_TN);
     constexpr bool BKC = (OP == GEMM_NT);
-    using TA = TileS<AKC, SH::BM>;
-    using TB = TileS<BKC, SH::BN>;
-    __shared__ __attribute__((aligned(16))) unsigned char smraw[SH::LDS_BYTES];
+    using TA = std::conditional_t<AKC, TileS<true, SH::BM>, TileSTr<SH::BM>>;
+    using TB = std::conditional_t<BKC, TileS<true, SH::BN>, TileSTr<SH::BN>>;
+    constexpr int STAGE = TA::ELEMS + TB::ELEMS;  // bf16 elements per LDS stage
+    constexpr int LDS_BYTES = 2 * STAGE * 2 > SH::EPI_F * 4 ? 2 * STAGE * 2 : SH::EPI_F * 4;
+    __shared__ __attribute__((aligned(16))) unsigned char smraw[LDS_BYTES];
     uint16_t* smh = reinterpret_cast<uint16_t*>(smraw);
 
     const int tile = xcd_remap(blockIdx.x, tiles_m * tiles_n);
@@ -579,9 +577,15 @@ __global__ __launch_bounds__(NTHR, (Shape<MI, NI>::OCC)) void gemm_bf16_big_kern
         for (int q = 0; q < BK / 16; q++) {
             uint4 af[MI], bf[NI];
 #pragma unroll
-            for (int i = 0; i < MI; i++) af[i] = frag_s(sa, wm + 32 * i + li, g, q);
+            for (int i = 0; i < MI; i++) {
+                if constexpr (AKC) af[i] = frag_s(sa, wm + 32 * i + li, g, q);
+                else af[i] = TA::frag(sa, wm + 32 * i, q, lane);
+            }
 #pragma unroll
-            for (int j = 0; j < NI; j++) bf[j] = frag_s(sb, wn + 32 * j + li, g, q);
+            for (int j = 0; j < NI; j++) {
+                if constexpr (BKC) bf[j] = frag_s(sb, wn + 32 * j + li, g, q);
+                else bf[j] = TB::frag(sb, wn + 32 * j, q, lane);
+            }
 #pragma unroll
             for (int i = 0; i < MI; i++)
 #pragma unroll
@@ -590,8 +594,8 @@ __global__ __launch_bounds__(NTHR, (Shape<MI, NI>::OCC)) void gemm_bf16_big_kern
     };
     using I0 = std::integral_constant<int, 0>;
     using I1 = std::integral_constant<int, 1>;
-    auto sA = [&](int b) { return smh + b * SH::STAGE; };
-    auto sB = [&](int b) { return smh + b * SH::STAGE + SH::BM * BK; };
+    auto sA = [&](int b) { return smh + b * STAGE; };
+    auto sB = [&](int b) { return smh + b * STAGE + TA::ELEMS; };
     if (nfull > 0) {
         issue(I0{}, 0);
         ta[0].store(sA(0));
