@@ -20,9 +20,14 @@
 // become the B operand of the next product (P^T or dS^T) without any lane
 // exchange, because the reduction over keys may run in any order: within
 // each group of 16 keys the reduction position 8g + i is given to key
-// 8(i / 4) + 4g + i % 4, and the operand stored in LDS along keys (V^T, K^T,
-// Q^T, dout^T) is written in that same permuted order.  Operands stored
-// along head dimensions ([row][dim], 8 bf16 pad) are read as 16 bytes.
+// 8(i / 4) + 4g + i % 4.  Every tile is stored in LDS once, as rows
+// [row][dim] (NDB*32 + 8 bf16 per row).  The operands along head dimensions
+// are read from it as 16 bytes; the operands along rows (V^T, K^T, Q^T,
+// dout^T) are gathered in the permuted order above by gfx950's transposing
+// LDS reads (frag_rt).  Against transposed copies written with 16-bit LDS
+// stores this took the attention from 3.61 to 2.82 ms per step, with
+// bit-identical results, and halved the backward kernels' LDS, so their
+// workgroups now fit three per compute unit.
 //
 // P and dS are rounded to bf16 for their products; the row statistics, the
 // exponentials and every sum stay fp32.  As in the fp32 kernels each
@@ -40,7 +45,6 @@ namespace {
 
 constexpr int RQ = 128;  // rows owned per workgroup (four waves of 32)
 constexpr int RT = 64;   // rows per staged tile
-constexpr int LDP = RT + 8;  // stride of a tile stored along keys/queries
 constexpr float L2E = 1.4426950408889634f;
 constexpr float LN_2 = 0.6931471805599453f;
 
@@ -50,10 +54,6 @@ __device__ __forceinline__ void zero(floatx16& x) {
     for (int e = 0; e < 16; e++) x[e] = 0.f;
 }
 
-// reduction position of key kk (0..63) in a tile stored along keys
-__device__ __forceinline__ int kpos(int kk) {
-    return (kk & ~15) | (((kk >> 2) & 1) << 3) | (((kk >> 3) & 1) << 2) | (kk & 3);
-}
 
 // Eight registers of a 32-row accumulator block, e = 8h..8h+7, as a bf16
 // B operand (reduction positions 8g..8g+7 of the 16-row group h).
@@ -82,29 +82,14 @@ struct Tile16 {
             }
         }
     }
-    // [row][dim], row stride HS + 8
+    // [row][dim], row stride LD
+    template <int LD>
     __device__ __forceinline__ void store_rows(uint16_t* sm) const {
 #pragma unroll
         for (int i = 0; i < PER; i++) {
             const int idx = threadIdx.x + 256 * i;
             if (N % 256 == 0 || idx < N)
-                *reinterpret_cast<uint4*>(sm + (idx / CH) * (HS + 8) + (idx % CH) * 8) = v[i];
-        }
-    }
-    // [dim][reduction position of the row], row stride LDP
-    __device__ __forceinline__ void store_t(uint16_t* sm) const {
-#pragma unroll
-        for (int i = 0; i < PER; i++) {
-            const int idx = threadIdx.x + 256 * i;
-            if (N % 256 == 0 || idx < N) {
-                const int r = kpos(idx / CH), c = (idx % CH) * 8;
-                const uint32_t w[4] = {v[i].x, v[i].y, v[i].z, v[i].w};
-#pragma unroll
-                for (int j = 0; j < 4; j++) {
-                    sm[(c + 2 * j) * LDP + r] = (uint16_t)(w[j] & 0xFFFFu);
-                    sm[(c + 2 * j + 1) * LDP + r] = (uint16_t)(w[j] >> 16);
-                }
-            }
+                *reinterpret_cast<uint4*>(sm + (idx / CH) * LD + (idx % CH) * 8) = v[i];
         }
     }
 };
@@ -112,6 +97,39 @@ struct Tile16 {
 // 16-byte LDS operand read
 __device__ __forceinline__ uint4 rd(const uint16_t* p) {
     return *reinterpret_cast<const uint4*>(p);
+}
+
+typedef short tr4_t __attribute__((ext_vector_type(4)));
+typedef __attribute__((address_space(3))) tr4_t* lds_tr4_ptr;
+
+// MFMA operand of head dims db..db+31 (lane li = dim db + li) over reduction
+// positions 8g..8g+7 of the 16-row group starting at row kb16, from a tile
+// stored as rows [row][dim] (stride ld), with two transposing LDS reads
+// (ds_read_b64_tr_b16).  In each 16-lane group of such a read, lane r
+// addresses 4 consecutive dims of one row and lane j receives element j of
+// each 16-element row of the group's 16x4 block, so lane r at
+// (row0 + r/4, dim0 + 4*(r%4)) hands lane j rows row0..row0+3 of dim0 + j.
+// Reduction positions 8g..8g+3 and 8g+4..8g+7 are rows kb16 + 4g + 0..3 and
+// kb16 + 8 + 4g + 0..3: the order in which the score registers feed the
+// other operand.
+__device__ __forceinline__ uint4 frag_rt(const uint16_t* s, int ld, int db, int kb16, int lane) {
+    const int grp = lane >> 4, r = lane & 15;
+    const int dim = db + 16 * (grp & 1) + 4 * (r & 3);
+    const int row = kb16 + 4 * (grp >> 1) + (r >> 2);
+    const uint16_t* p = s + row * ld + dim;
+    const tr4_t lo = __builtin_amdgcn_ds_read_tr16_b64_v4i16((lds_tr4_ptr)p);
+    const tr4_t hi = __builtin_amdgcn_ds_read_tr16_b64_v4i16((lds_tr4_ptr)(p + 8 * ld));
+    const uint2 a = __builtin_bit_cast(uint2, lo), b = __builtin_bit_cast(uint2, hi);
+    return make_uint4(a.x, a.y, b.x, b.y);
+}
+
+// Zero dims HS..NDB*32-1 of every row of a [row][dim] tile (read by the
+// MFMA as padding head dimensions whose outputs are discarded).
+template <int HS, int NDB, int LD>
+__device__ __forceinline__ void zero_pad_cols(uint16_t* sm) {
+    if (NDB * 32 > HS)
+        for (int i = threadIdx.x; i < RT * (NDB * 32 - HS); i += blockDim.x)
+            sm[(i / (NDB * 32 - HS)) * LD + HS + i % (NDB * 32 - HS)] = 0;
 }
 
 // Write one lane's accumulator blocks (rows = head dims d*32 + 8(e/4) +
@@ -131,22 +149,14 @@ __device__ __forceinline__ void put_row(uint16_t* row, const floatx16 (&acc)[NDB
         }
 }
 
-// Zero the rows HS..NDB*32-1 of a tile stored along keys (read by the MFMA
-// as padding head dimensions whose outputs are discarded).
-template <int HS, int NDB>
-__device__ __forceinline__ void zero_pad_rows(uint16_t* sm) {
-    if (NDB * 32 > HS)
-        for (int i = threadIdx.x; i < (NDB * 32 - HS) * LDP; i += blockDim.x) sm[HS * LDP + i] = 0;
-}
-
 template <int HS, class H>
 __global__ __launch_bounds__(256, 2) void attn16_fwd_kernel(uint16_t* __restrict__ out,
                                                             float* __restrict__ lse,
                                                             const uint16_t* __restrict__ qkv,
                                                             int T, int C, int NH, float qscale) {
-    constexpr int NKS = HS / 16, NDB = (HS + 31) / 32, LDK = HS + 8;
+    constexpr int NKS = HS / 16, NDB = (HS + 31) / 32, LDK = NDB * 32 + 8;
     __shared__ __attribute__((aligned(16))) uint16_t ks[2][RT * LDK];
-    __shared__ __attribute__((aligned(16))) uint16_t vt[2][NDB * 32 * LDP];
+    __shared__ __attribute__((aligned(16))) uint16_t vs[2][RT * LDK];
 
     const int nqb = (T + RQ - 1) / RQ;
     const int nbh = gridDim.x / nqb;
@@ -162,8 +172,8 @@ __global__ __launch_bounds__(256, 2) void attn16_fwd_kernel(uint16_t* __restrict
     const int q = qw + li;
     const int qmax = qw < T ? min(qw + 31, T - 1) : -1;
     const int nkt = (min(q0 + RQ, T) - 1) / RT + 1;
-    zero_pad_rows<HS, NDB>(vt[0]);
-    zero_pad_rows<HS, NDB>(vt[1]);
+    zero_pad_cols<HS, NDB, LDK>(vs[0]);
+    zero_pad_cols<HS, NDB, LDK>(vs[1]);
 
     uint4 qv[NKS];  // this lane's query, dims 16j + 8g .. +7
 #pragma unroll
@@ -177,8 +187,8 @@ __global__ __launch_bounds__(256, 2) void attn16_fwd_kernel(uint16_t* __restrict
     Tile16<HS> kreg, vreg;
     kreg.load(base + C, ld, 0, T);
     vreg.load(base + 2 * C, ld, 0, T);
-    kreg.store_rows(ks[0]);
-    vreg.store_t(vt[0]);
+    kreg.template store_rows<LDK>(ks[0]);
+    vreg.template store_rows<LDK>(vs[0]);
     __syncthreads();
     for (int kt = 0; kt < nkt; kt++) {
         const int cur = kt & 1;
@@ -229,7 +239,6 @@ __global__ __launch_bounds__(256, 2) void attn16_fwd_kernel(uint16_t* __restrict
             for (int d = 0; d < NDB; d++)
 #pragma unroll
                 for (int e = 0; e < 16; e++) o[d][e] *= corr;
-            const uint16_t* vr = vt[cur] + li * LDP + 8 * g;
 #pragma unroll
             for (int kb = 0; kb < 2; kb++)
 #pragma unroll
@@ -237,11 +246,12 @@ __global__ __launch_bounds__(256, 2) void attn16_fwd_kernel(uint16_t* __restrict
                     const uint4 pb = pack8<H>(sc[kb], hh);
 #pragma unroll
                     for (int d = 0; d < NDB; d++)
-                        o[d] = H::mma(rd(vr + d * 32 * LDP + kb * 32 + 16 * hh), pb, o[d]);
+                        o[d] = H::mma(frag_rt(vs[cur], LDK, d * 32, kb * 32 + 16 * hh, lane), pb,
+                                      o[d]);
                 }
         }
-        kreg.store_rows(ks[cur ^ 1]);
-        vreg.store_t(vt[cur ^ 1]);
+        kreg.template store_rows<LDK>(ks[cur ^ 1]);
+        vreg.template store_rows<LDK>(vs[cur ^ 1]);
         __syncthreads();
     }
     if (q < T) {
@@ -251,17 +261,16 @@ __global__ __launch_bounds__(256, 2) void attn16_fwd_kernel(uint16_t* __restrict
 }
 
 // dQ (lane owns a query) and D = rowsum(dout * out) for the key/value
-// kernel.  K is staged twice: as rows for S^T = K Q^T and along keys for
-// dQ^T = K^T dS^T; V as rows for dP^T = V dout^T.
+// kernel.  K is staged as rows, read as 16 bytes for S^T = K Q^T and with
+// the transposing reads for dQ^T = K^T dS^T; V as rows for dP^T = V dout^T.
 template <int HS, class H>
-__global__ __launch_bounds__(256, 2) void attn16_dq_kernel(
+__global__ __launch_bounds__(256, 3) void attn16_dq_kernel(
     uint16_t* __restrict__ dqkv, float* __restrict__ Dout, const uint16_t* __restrict__ dout,
     const uint16_t* __restrict__ out, const uint16_t* __restrict__ qkv,
     const float* __restrict__ lse, int T, int C, int NH, float qscale, float scale) {
-    constexpr int NKS = HS / 16, NDB = (HS + 31) / 32, LDK = HS + 8;
+    constexpr int NKS = HS / 16, NDB = (HS + 31) / 32, LDK = NDB * 32 + 8;
     __shared__ __attribute__((aligned(16))) uint16_t ks[2][RT * LDK];
     __shared__ __attribute__((aligned(16))) uint16_t vs[2][RT * LDK];
-    __shared__ __attribute__((aligned(16))) uint16_t kt_[2][NDB * 32 * LDP];
 
     const int nqb = (T + RQ - 1) / RQ;
     const int nbh = gridDim.x / nqb;
@@ -280,8 +289,8 @@ __global__ __launch_bounds__(256, 2) void attn16_dq_kernel(
     const int qc = min(q, T - 1);
     const int qmax = qw < T ? min(qw + 31, T - 1) : -1;
     const int nkt = (min(q0 + RQ, T) - 1) / RT + 1;
-    zero_pad_rows<HS, NDB>(kt_[0]);
-    zero_pad_rows<HS, NDB>(kt_[1]);
+    zero_pad_cols<HS, NDB, LDK>(ks[0]);
+    zero_pad_cols<HS, NDB, LDK>(ks[1]);
 
     uint4 qv[NKS], dv[NKS];
     float dsum = 0.f;
@@ -307,9 +316,8 @@ __global__ __launch_bounds__(256, 2) void attn16_dq_kernel(
     Tile16<HS> kreg, vreg;
     kreg.load(base + C, ld, 0, T);
     vreg.load(base + 2 * C, ld, 0, T);
-    kreg.store_rows(ks[0]);
-    kreg.store_t(kt_[0]);
-    vreg.store_rows(vs[0]);
+    kreg.template store_rows<LDK>(ks[0]);
+    vreg.template store_rows<LDK>(vs[0]);
     __syncthreads();
     for (int kt = 0; kt < nkt; kt++) {
         const int cur = kt & 1;
@@ -342,7 +350,6 @@ __global__ __launch_bounds__(256, 2) void attn16_dq_kernel(
                     const float p = __builtin_amdgcn_exp2f(fmaf(sc[kb][e], qscale, -lq));
                     sc[kb][e] = live ? p * (dp[kb][e] - Dq) : 0.f;
                 }
-            const uint16_t* ktr = kt_[cur] + li * LDP + 8 * g;
 #pragma unroll
             for (int kb = 0; kb < 2; kb++)
 #pragma unroll
@@ -350,30 +357,30 @@ __global__ __launch_bounds__(256, 2) void attn16_dq_kernel(
                     const uint4 sb = pack8<H>(sc[kb], hh);
 #pragma unroll
                     for (int d = 0; d < NDB; d++)
-                        dq[d] = H::mma(rd(ktr + d * 32 * LDP + kb * 32 + 16 * hh), sb, dq[d]);
+                        dq[d] = H::mma(frag_rt(ks[cur], LDK, d * 32, kb * 32 + 16 * hh, lane), sb,
+                                       dq[d]);
                 }
         }
-        kreg.store_rows(ks[cur ^ 1]);
-        kreg.store_t(kt_[cur ^ 1]);
-        vreg.store_rows(vs[cur ^ 1]);
+        kreg.template store_rows<LDK>(ks[cur ^ 1]);
+        vreg.template store_rows<LDK>(vs[cur ^ 1]);
         __syncthreads();
     }
     if (q < T) put_row<HS, NDB, H>(dqkv + ((int64_t)b * T + q) * ld + h * HS, dq, g, scale);
 }
 
-// dK and dV (lane owns a key).  Q and dout are staged as rows (for S = Q K^T
-// and dP = dout V^T, queries down the accumulator) and along queries (for
-// dK^T = Q^T dS and dV^T = dout^T P).
+// dK and dV (lane owns a key).  Q and dout are staged as rows, read as 16
+// bytes for S = Q K^T and dP = dout V^T (queries down the accumulator) and
+// with the transposing reads for dK^T = Q^T dS and dV^T = dout^T P.  At 175
+// VGPRs it spills a few registers at three workgroups per compute unit and
+// still measured 5% faster than at two.
 template <int HS, class H>
-__global__ __launch_bounds__(256, 2) void attn16_dkdv_kernel(
+__global__ __launch_bounds__(256, 3) void attn16_dkdv_kernel(
     uint16_t* __restrict__ dqkv, const uint16_t* __restrict__ dout,
     const uint16_t* __restrict__ qkv, const float* __restrict__ lse, const float* __restrict__ D,
     int T, int C, int NH, float qscale, float scale) {
-    constexpr int NKS = HS / 16, NDB = (HS + 31) / 32, LDK = HS + 8;
+    constexpr int NKS = HS / 16, NDB = (HS + 31) / 32, LDK = NDB * 32 + 8;
     __shared__ __attribute__((aligned(16))) uint16_t qs[2][RT * LDK];
     __shared__ __attribute__((aligned(16))) uint16_t ds[2][RT * LDK];
-    __shared__ __attribute__((aligned(16))) uint16_t qt_[2][NDB * 32 * LDP];
-    __shared__ __attribute__((aligned(16))) uint16_t dt_[2][NDB * 32 * LDP];
     __shared__ float lsm[2][RT], dsm[2][RT];
 
     const int nkb = (T + RQ - 1) / RQ;
@@ -390,10 +397,10 @@ __global__ __launch_bounds__(256, 2) void attn16_dkdv_kernel(
     const int kw = kb0 * RQ + wave * 32;  // first key of this wave
     const int key = kw + li;
     const int kc = min(key, T - 1);
-    zero_pad_rows<HS, NDB>(qt_[0]);
-    zero_pad_rows<HS, NDB>(qt_[1]);
-    zero_pad_rows<HS, NDB>(dt_[0]);
-    zero_pad_rows<HS, NDB>(dt_[1]);
+    zero_pad_cols<HS, NDB, LDK>(qs[0]);
+    zero_pad_cols<HS, NDB, LDK>(qs[1]);
+    zero_pad_cols<HS, NDB, LDK>(ds[0]);
+    zero_pad_cols<HS, NDB, LDK>(ds[1]);
 
     uint4 kv[NKS], vv[NKS];
 #pragma unroll
@@ -423,10 +430,8 @@ __global__ __launch_bounds__(256, 2) void attn16_dkdv_kernel(
     qreg.load(base, ld, qt0 * RT, T);
     dreg.load(dobase, C, qt0 * RT, T);
     load_stats(qt0);
-    qreg.store_rows(qs[0]);
-    qreg.store_t(qt_[0]);
-    dreg.store_rows(ds[0]);
-    dreg.store_t(dt_[0]);
+    qreg.template store_rows<LDK>(qs[0]);
+    dreg.template store_rows<LDK>(ds[0]);
     store_stats(0);
     __syncthreads();
     for (int qt = qt0; qt < nqt; qt++) {
@@ -459,22 +464,20 @@ __global__ __launch_bounds__(256, 2) void attn16_dkdv_kernel(
                 sc[e] = p;
                 dp[e] = p * (dp[e] - dsm[cur][ql]);
             }
-            const uint16_t* qtr = qt_[cur] + li * LDP + 8 * g + qh * 32;
-            const uint16_t* dtr = dt_[cur] + li * LDP + 8 * g + qh * 32;
 #pragma unroll
             for (int hh = 0; hh < 2; hh++) {
                 const uint4 pb = pack8<H>(sc, hh), sb = pack8<H>(dp, hh);
 #pragma unroll
                 for (int d = 0; d < NDB; d++) {
-                    dvv[d] = H::mma(rd(dtr + d * 32 * LDP + 16 * hh), pb, dvv[d]);
-                    dk[d] = H::mma(rd(qtr + d * 32 * LDP + 16 * hh), sb, dk[d]);
+                    dvv[d] = H::mma(frag_rt(ds[cur], LDK, d * 32, qh * 32 + 16 * hh, lane), pb,
+                                    dvv[d]);
+                    dk[d] = H::mma(frag_rt(qs[cur], LDK, d * 32, qh * 32 + 16 * hh, lane), sb,
+                                   dk[d]);
                 }
             }
         }
-        qreg.store_rows(qs[cur ^ 1]);
-        qreg.store_t(qt_[cur ^ 1]);
-        dreg.store_rows(ds[cur ^ 1]);
-        dreg.store_t(dt_[cur ^ 1]);
+        qreg.template store_rows<LDK>(qs[cur ^ 1]);
+        dreg.template store_rows<LDK>(ds[cur ^ 1]);
         store_stats(cur ^ 1);
         __syncthreads();
     }
