@@ -46,40 +46,93 @@ __global__ __launch_bounds__(256) void encoder_fwd_kernel(E* __restrict__ out,
     }
 }
 
-// Bitonic sort of (token << pos_bits | position) keys in LDS, one workgroup.
-// Ids outside [0, V) get the token field V so the backward skips them.
+// Sort of the (token << pos_bits | position) keys, one workgroup of 1024
+// threads.  Ids outside [0, V) get the token field V so the backward skips
+// them; slots past n get all bits set and sort last.  The keys are built in
+// position order and are unique, so a stable sort on the token field alone
+// gives them in (token, position) order: a least-significant-digit radix
+// sort, 4 bits per pass.  Thread t holds keys [t*EPT, (t+1)*EPT) in
+// registers; each pass counts its digits into a [16][1024] table in LDS,
+// scans the table in digit-major order (so equal digits keep thread order)
+// and scatters the keys through LDS.
+template <int EPT>
 __global__ __launch_bounds__(1024) void encoder_sort_kernel(uint32_t* __restrict__ keys,
                                                             const int32_t* __restrict__ tok,
                                                             int n, int V, int pos_bits,
-                                                            int n_pow2) {
-    extern __shared__ uint32_t sk[];
-    for (int i = threadIdx.x; i < n_pow2; i += blockDim.x) {
-        uint32_t k = 0xFFFFFFFFu;
+                                                            int n_pow2, int passes) {
+    constexpr int NT = 1024, NK = EPT * NT;
+    extern __shared__ uint32_t sm[];
+    uint32_t* sk = sm;                                      // NK keys
+    uint16_t* cnt = reinterpret_cast<uint16_t*>(sm + NK);   // [16][NT] counts
+    uint32_t* wsum = sm + NK + 16 * NT / 2;                 // 16 wave totals
+    const int t = threadIdx.x, lane = t & 63, wave = t >> 6;
+    uint32_t k[EPT];
+#pragma unroll
+    for (int e = 0; e < EPT; e++) {
+        const int i = t * EPT + e;
+        uint32_t key = 0xFFFFFFFFu;
         if (i < n) {
             const int id = tok[i];
             const uint32_t tf = (id >= 0 && id < V) ? (uint32_t)id : (uint32_t)V;
-            k = (tf << pos_bits) | (uint32_t)i;
+            key = (tf << pos_bits) | (uint32_t)i;
         }
-        sk[i] = k;
+        k[e] = key;
     }
-    __syncthreads();
-    for (int k = 2; k <= n_pow2; k <<= 1) {
-        for (int j = k >> 1; j > 0; j >>= 1) {
-            for (int i = threadIdx.x; i < n_pow2; i += blockDim.x) {
-                const int p = i ^ j;
-                if (p > i) {
-                    const uint32_t a = sk[i], b = sk[p];
-                    const bool up = (i & k) == 0;
-                    if ((a > b) == up) {
-                        sk[i] = b;
-                        sk[p] = a;
-                    }
-                }
-            }
-            __syncthreads();
+    for (int pass = 0; pass < passes; pass++) {
+        const int sh = pos_bits + 4 * pass;
+        // digit counts of this thread's keys
+        uint32_t total = 0;
+#pragma unroll
+        for (int d = 0; d < 16; d++) {
+            uint32_t c = 0;
+#pragma unroll
+            for (int e = 0; e < EPT; e++) c += ((k[e] >> sh) & 15u) == (uint32_t)d;
+            cnt[d * NT + t] = (uint16_t)c;
         }
+        __syncthreads();
+        // exclusive scan of the 16*NT counts in index order: thread t owns
+        // entries [16t, 16t + 16)
+        uint32_t v[16];
+#pragma unroll
+        for (int j = 0; j < 16; j++) {
+            v[j] = cnt[16 * t + j];
+            total += v[j];
+        }
+        uint32_t incl = total;  // inclusive scan of the per-thread totals over the wave
+#pragma unroll
+        for (int off = 1; off < 64; off <<= 1) {
+            const uint32_t up = __shfl_up(incl, off, 64);
+            if (lane >= off) incl += up;
+        }
+        if (lane == 63) wsum[wave] = incl;
+        __syncthreads();
+        uint32_t base = incl - total;
+        for (int w = 0; w < wave; w++) base += wsum[w];
+#pragma unroll
+        for (int j = 0; j < 16; j++) {
+            cnt[16 * t + j] = (uint16_t)base;
+            base += v[j];
+        }
+        __syncthreads();
+        // stable scatter: each thread's keys of digit d go, in order, to the
+        // slots its scanned count for d starts at
+#pragma unroll
+        for (int e = 0; e < EPT; e++) {
+            const uint32_t d = (k[e] >> sh) & 15u;
+            const uint32_t dst = cnt[d * NT + t];
+            cnt[d * NT + t] = (uint16_t)(dst + 1);
+            sk[dst] = k[e];
+        }
+        __syncthreads();
+#pragma unroll
+        for (int e = 0; e < EPT; e++) k[e] = sk[t * EPT + e];
+        __syncthreads();
     }
-    for (int i = threadIdx.x; i < n_pow2; i += blockDim.x) keys[i] = sk[i];
+#pragma unroll
+    for (int e = 0; e < EPT; e++) {
+        const int i = t * EPT + e;
+        if (i < n_pow2) keys[i] = k[e];
+    }
 }
 
 // One wave per sorted position; the first position of each run of equal
@@ -434,16 +487,52 @@ hipError_t encoder_forward(hipStream_t s, void* out, const int32_t* tok, const f
     });
 }
 
+// keys per thread of the sort for n_pow2 slots (1024 threads)
+inline int sort_ept(int n_pow2) { return n_pow2 <= 1024 ? 1 : n_pow2 / 1024; }
+inline size_t sort_lds(int ept) { return (size_t)ept * 1024 * 4 + 16 * 1024 * 2 + 64; }
+
+template <int EPT>
+hipError_t sort_attr() {
+    return hipFuncSetAttribute((const void*)encoder_sort_kernel<EPT>,
+                               hipFuncAttributeMaxDynamicSharedMemorySize, (int)sort_lds(EPT));
+}
+
 hipError_t encoder_sort_prepare(int n_pow2) {
-    return hipFuncSetAttribute((const void*)encoder_sort_kernel,
-                               hipFuncAttributeMaxDynamicSharedMemorySize, n_pow2 * 4);
+    switch (sort_ept(n_pow2)) {
+        case 1: return sort_attr<1>();
+        case 2: return sort_attr<2>();
+        case 4: return sort_attr<4>();
+        case 8: return sort_attr<8>();
+        case 16: return sort_attr<16>();
+        case 32: return sort_attr<32>();
+        default: return hipErrorInvalidValue;
+    }
 }
 
 hipError_t encoder_sort(hipStream_t s, uint32_t* keys, const int32_t* tok, int n, int V,
                         int pos_bits, int n_pow2) {
     if (n <= 0) return hipSuccess;
-    launch(encoder_sort_kernel, dim3(1), dim3(1024), (size_t)n_pow2 * 4, s, keys,
-                       tok, n, V, pos_bits, n_pow2);
+    // 4-bit passes over the token field, whose largest value is V
+    int bits = 1;
+    while (bits < 32 && ((uint64_t)V >> bits) != 0) bits++;
+    const int passes = (bits + 3) / 4;
+    const int ept = sort_ept(n_pow2);
+    const size_t lds = sort_lds(ept);
+    switch (ept) {
+#define SORT_CASE(E)                                                                          \
+    case E:                                                                                   \
+        launch(encoder_sort_kernel<E>, dim3(1), dim3(1024), lds, s, keys, tok, n, V, pos_bits, \
+               n_pow2, passes);                                                               \
+        break;
+        SORT_CASE(1)
+        SORT_CASE(2)
+        SORT_CASE(4)
+        SORT_CASE(8)
+        SORT_CASE(16)
+        SORT_CASE(32)
+#undef SORT_CASE
+        default: return hipErrorInvalidValue;
+    }
     return hipGetLastError();
 }
 
