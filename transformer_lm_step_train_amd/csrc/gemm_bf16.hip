@@ -531,6 +531,9 @@ __global__ __launch_bounds__(NTHR, (Shape<MI, NI>::OCC)) void gemm_bf16_big_kern
     using SH = Shape<MI, NI>;
     constexpr bool AKC = (OP != GEMM_TN);
     constexpr bool BKC = (OP == GEMM_NT);
+    // Fragment pipelining: bit-identical, 3-5% faster on the weight
+    // gradients, 1-2% slower on the long-K input gradient.
+    constexpr bool PIPE = (OP == GEMM_TN);
     using TA = std::conditional_t<AKC, TileS<true, SH::BM>, TileSTr<SH::BM>>;
     using TB = std::conditional_t<BKC, TileS<true, SH::BN>, TileSTr<SH::BN>>;
     constexpr int STAGE = TA::ELEMS + TB::ELEMS;  // bf16 elements per LDS stage
@@ -572,24 +575,48 @@ __global__ __launch_bounds__(NTHR, (Shape<MI, NI>::OCC)) void gemm_bf16_big_kern
         ta[S].template load<false>(a.A, a.lda, m0, a.M, kk, k_end);
         tb[S].template load<false>(a.B, a.ldb, n0, a.N, kk, k_end);
     };
-    auto compute = [&](const uint16_t* sa, const uint16_t* sb) {
+    auto rd = [&](uint4 (&af)[MI], uint4 (&bf)[NI], const uint16_t* sa, const uint16_t* sb,
+                  int q) {
 #pragma unroll
-        for (int q = 0; q < BK / 16; q++) {
-            uint4 af[MI], bf[NI];
+        for (int i = 0; i < MI; i++) {
+            if constexpr (AKC) af[i] = frag_s(sa, wm + 32 * i + li, g, q);
+            else af[i] = TA::frag(sa, wm + 32 * i, q, lane);
+        }
 #pragma unroll
-            for (int i = 0; i < MI; i++) {
-                if constexpr (AKC) af[i] = frag_s(sa, wm + 32 * i + li, g, q);
-                else af[i] = TA::frag(sa, wm + 32 * i, q, lane);
+        for (int j = 0; j < NI; j++) {
+            if constexpr (BKC) bf[j] = frag_s(sb, wn + 32 * j + li, g, q);
+            else bf[j] = TB::frag(sb, wn + 32 * j, q, lane);
+        }
+    };
+    auto mm = [&](const uint4 (&af)[MI], const uint4 (&bf)[NI]) {
+#pragma unroll
+        for (int i = 0; i < MI; i++)
+#pragma unroll
+            for (int j = 0; j < NI; j++) acc[i][j] = H::mma(af[i], bf[j], acc[i][j]);
+    };
+    // One reduction step from LDS.  PIPE: the fragments of sub-step q + 1 are
+    // read before the MFMAs of sub-step q, so their LDS latency overlaps the
+    // matrix work; the next stage's LDS stores (st) go in the middle of the
+    // step.  Otherwise each sub-step reads its fragments and then multiplies,
+    // and st runs after the step.
+    auto compute = [&](const uint16_t* sa, const uint16_t* sb, auto st) {
+        if constexpr (PIPE) {
+            uint4 af[2][MI], bf[2][NI];
+            rd(af[0], bf[0], sa, sb, 0);
+#pragma unroll
+            for (int q = 0; q < BK / 16; q++) {
+                if (q + 1 < BK / 16) rd(af[(q + 1) & 1], bf[(q + 1) & 1], sa, sb, q + 1);
+                mm(af[q & 1], bf[q & 1]);
+                if (q == 1) st();
             }
+        } else {
 #pragma unroll
-            for (int j = 0; j < NI; j++) {
-                if constexpr (BKC) bf[j] = frag_s(sb, wn + 32 * j + li, g, q);
-                else bf[j] = TB::frag(sb, wn + 32 * j, q, lane);
+            for (int q = 0; q < BK / 16; q++) {
+                uint4 af[MI], bf[NI];
+                rd(af, bf, sa, sb, q);
+                mm(af, bf);
             }
-#pragma unroll
-            for (int i = 0; i < MI; i++)
-#pragma unroll
-                for (int j = 0; j < NI; j++) acc[i][j] = H::mma(af[i], bf[j], acc[i][j]);
+            st();
         }
     };
     using I0 = std::integral_constant<int, 0>;
@@ -609,10 +636,13 @@ __global__ __launch_bounds__(NTHR, (Shape<MI, NI>::OCC)) void gemm_bf16_big_kern
         const int cur = kt & 1;
         issue(slotc, kt + 2);
         __builtin_amdgcn_sched_barrier(0);  // loads stay ahead of the MFMAs
-        compute(sA(cur), sB(cur));
-        // unconditional: no path reaches the next loads with this slot pending
-        ta[NS].store(sA(cur ^ 1));
-        tb[NS].store(sB(cur ^ 1));
+        // The stores fill the other buffer, which every wave finished reading
+        // before the previous barrier; unconditional, so no path reaches the
+        // next loads with this slot pending.
+        compute(sA(cur), sB(cur), [&]() {
+            ta[NS].store(sA(cur ^ 1));
+            tb[NS].store(sB(cur ^ 1));
+        });
         __syncthreads();
     };
     int kt = 0;
@@ -628,7 +658,7 @@ __global__ __launch_bounds__(NTHR, (Shape<MI, NI>::OCC)) void gemm_bf16_big_kern
         ta[0].store(sA(0));
         tb[0].store(sB(0));
         __syncthreads();
-        compute(sA(0), sB(0));
+        compute(sA(0), sB(0), []() {});
         __syncthreads();
     }
 
