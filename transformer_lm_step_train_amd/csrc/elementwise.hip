@@ -247,12 +247,13 @@ __global__ __launch_bounds__(256) void bias_partial_kernel(float* __restrict__ p
     }
 }
 
-// out[c] += sum over rows r of part[r*ncols + c], for c < split into out0 and
-// c >= split into out1[c - split].  One workgroup per 64 columns; its 16
+// out[c] += sum over rows r of part[r*ncols + c], into out_k[c - k*split]
+// with k = c / split (0, 1 or 2).  One workgroup per 64 columns; its 16
 // waves sum interleaved rows (wave w takes rows w, w+16, ...) and are then
 // added in wave order, so the result is the same on every run.
 __global__ __launch_bounds__(1024) void colsum_finish_kernel(float* __restrict__ out0,
                                                              float* __restrict__ out1,
+                                                             float* __restrict__ out2,
                                                              int split,
                                                              const float* __restrict__ part,
                                                              int nrows, int ncols) {
@@ -275,10 +276,9 @@ __global__ __launch_bounds__(1024) void colsum_finish_kernel(float* __restrict__
     if (wave == 0 && c < ncols) {
         float t = sh[0][lane];
         for (int w = 1; w < 16; w++) t += sh[w][lane];
-        if (c < split)
-            out0[c] += t;
-        else
-            out1[c - split] += t;
+        const int k = c / split;
+        float* o = k == 0 ? out0 : k == 1 ? out1 : out2;
+        o[c - k * split] += t;
     }
 }
 
@@ -288,6 +288,7 @@ __global__ __launch_bounds__(1024) void colsum_finish_kernel(float* __restrict__
 // result is the same on every run.
 __global__ __launch_bounds__(1024) void colsum4_finish_kernel(float* __restrict__ out0,
                                                               float* __restrict__ out1,
+                                                              float* __restrict__ out2,
                                                               int split,
                                                               const float* __restrict__ part,
                                                               int nrows, int ncols) {
@@ -316,11 +317,10 @@ __global__ __launch_bounds__(1024) void colsum4_finish_kernel(float* __restrict_
         const float4 t = sh[0][cl];
         const float v[4] = {t.x, t.y, t.z, t.w};
 #pragma unroll
-        for (int k = 0; k < 4; k++) {
-            if (c + k < split)
-                out0[c + k] += v[k];
-            else
-                out1[c + k - split] += v[k];
+        for (int j = 0; j < 4; j++) {
+            const int k = (c + j) / split;
+            float* o = k == 0 ? out0 : k == 1 ? out1 : out2;
+            o[c + j - k * split] += v[j];
         }
     }
 }
@@ -596,18 +596,21 @@ hipError_t bias_grad(hipStream_t s, float* db, float* part, const void* dy, int 
         return hipGetLastError();
     });
     if (e != hipSuccess) return e;
-    return colsum_add(s, db, db, N, part, nchunks, N);
+    return colsum_add(s, db, nullptr, nullptr, N, part, nchunks, N);
 }
 
-hipError_t colsum_add(hipStream_t s, float* out0, float* out1, int split, const float* part,
-                      int nrows, int ncols) {
+hipError_t colsum_add(hipStream_t s, float* out0, float* out1, float* out2, int split,
+                      const float* part, int nrows, int ncols) {
     if (nrows <= 0 || ncols <= 0) return hipSuccess;
+    if (split <= 0 || ncols > 3 * split || (ncols > split && !out1) ||
+        (ncols > 2 * split && !out2))
+        return hipErrorInvalidValue;
     if ((ncols & 3) == 0)
         launch(colsum4_finish_kernel, dim3((ncols + 31) / 32), dim3(1024), 0, s, out0, out1,
-               split, part, nrows, ncols);
+               out2, split, part, nrows, ncols);
     else
         launch(colsum_finish_kernel, dim3((ncols + 63) / 64), dim3(1024), 0, s, out0, out1,
-               split, part, nrows, ncols);
+               out2, split, part, nrows, ncols);
     return hipGetLastError();
 }
 

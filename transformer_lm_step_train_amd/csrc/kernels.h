@@ -121,11 +121,13 @@ hipError_t rope_apply(hipStream_t s, void* qkv, const float* cs, int B, int T, i
 hipError_t layernorm_forward(hipStream_t s, void* out, float* mean, float* rstd,
                              const void* inp, const float* w, const float* b, int N, int C,
                              int dt);
-// dres (+)= dx;  dw += sum dy*xhat, db += sum dy (two deterministic stages,
-// `partials` holds layernorm_partials_floats(N, C) floats).
+// dres (+)= dx;  dw += sum dy*xhat, db += sum dy, and when dbias is not
+// NULL dbias += the column sums of dres as stored after this call (two
+// deterministic stages; `partials` holds layernorm_partials_floats(N, C)
+// floats).
 size_t layernorm_partials_floats(int N, int C);
 hipError_t layernorm_backward(hipStream_t s, void* dres, int accumulate, float* dw, float* db,
-                              float* partials, const void* dout, const void* inp,
+                              float* dbias, float* partials, const void* dout, const void* inp,
                               const float* w, const float* mean, const float* rstd, int N,
                               int C, int dt);
 
@@ -168,10 +170,11 @@ hipError_t encoder_backward(hipStream_t s, float* dwte, float* dwpe,
 size_t bias_partials_floats(int M, int N);
 hipError_t bias_grad(hipStream_t s, float* db, float* partials,
                      const void* dy, int M, int N, int64_t ld, int dt);
-// out0[c] += sum_r part[r*ncols + c] for c < split, out1[c-split] likewise
-// for c >= split; rows summed in a fixed order.
-hipError_t colsum_add(hipStream_t s, float* out0, float* out1, int split, const float* part,
-                      int nrows, int ncols);
+// Column c of part (nrows x ncols) is summed over rows in a fixed order and
+// added to out_k[c - k*split], k = c / split (k <= 2; out2 may be NULL when
+// ncols <= 2*split, out1 when ncols <= split).
+hipError_t colsum_add(hipStream_t s, float* out0, float* out1, float* out2, int split,
+                      const float* part, int nrows, int ncols);
 hipError_t fill_zero(hipStream_t s, float* p, int64_t n);
 // shadow: optional 16-bit copy of the updated parameters (NULL = none) of
 // storage type shadow_dt (DT_BF16 or DT_F16).  Loss scaling (fp16 model):

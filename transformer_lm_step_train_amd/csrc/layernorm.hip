@@ -9,6 +9,11 @@
 //             dx = rstd (g - mean(g) - xhat mean(g xhat)),
 //             dw += sum_rows dy xhat,  db += sum_rows dy.
 //
+// The backward can also sum its own output over rows: the residual-stream
+// gradient it leaves behind is the output gradient of the projection whose
+// result was added into that stream, so that column sum is the projection's
+// bias gradient, taken here without reading the stream again.
+//
 // One wave per row; the row stays in registers between the two reductions,
 // so x is read once.  The backward's column sums are deterministic: each
 // workgroup reduces its rows to one partial row, a second kernel adds the
@@ -22,6 +27,23 @@ namespace gk {
 namespace {
 
 constexpr float LN_EPS = 1e-5f;
+
+// The value a store of v leaves in memory, back in fp32.
+template <class T>
+__device__ __forceinline__ float4 as_stored(float4 v);
+template <>
+__device__ __forceinline__ float4 as_stored<float>(float4 v) {
+    return v;
+}
+template <>
+__device__ __forceinline__ float4 as_stored<uint16_t>(float4 v) {
+    return make_float4(bf2f(f2bf(v.x)), bf2f(f2bf(v.y)), bf2f(f2bf(v.z)), bf2f(f2bf(v.w)));
+}
+template <>
+__device__ __forceinline__ float4 as_stored<_Float16>(float4 v) {
+    return make_float4((float)(_Float16)v.x, (float)(_Float16)v.y, (float)(_Float16)v.z,
+                       (float)(_Float16)v.w);
+}
 
 template <int NCH, class T>  // float4 chunks per lane: C <= 256 * NCH
 __global__ __launch_bounds__(256) void ln_fwd_kernel(T* __restrict__ out,
@@ -86,14 +108,21 @@ inline int ln_rows_per_block(int N) {
     return r < 4 ? 4 : r;
 }
 
+// nsum = 2: partial rows of (dw, db); nsum = 3: (dw, db, column sums of the
+// stored dres rows).  The third sum runs in the wave's own LDS row rather
+// than in registers, which keeps four waves per SIMD.
 template <int NCH, class T>
 __global__ __launch_bounds__(256) void ln_bwd_kernel(
     T* __restrict__ dres, int accumulate, float* __restrict__ partials,
     const T* __restrict__ dout, const T* __restrict__ inp, const float* __restrict__ w,
-    const float* __restrict__ mean, const float* __restrict__ rstd, int N, int C, int rpb) {
-    extern __shared__ float red[];  // [4 waves][2][C]
+    const float* __restrict__ mean, const float* __restrict__ rstd, int N, int C, int rpb,
+    int nsum) {
+    extern __shared__ float red[];  // [4 waves][nsum][C]
     const int lane = threadIdx.x & 63, wave = threadIdx.x >> 6;
     const int C4 = C >> 2;
+    float* osum = red + (wave * nsum + 2) * C;  // this wave's output sums (nsum == 3)
+    if (nsum == 3)
+        for (int c4 = lane; c4 < C4; c4 += 64) st4(osum + 4 * c4, make_float4(0.f, 0.f, 0.f, 0.f));
     float4 pw[NCH], pb[NCH], wv[NCH];
 #pragma unroll
     for (int i = 0; i < NCH; i++) {
@@ -152,6 +181,15 @@ __global__ __launch_bounds__(256) void ln_bwd_kernel(
                 o.z += old[i].z;
                 o.w += old[i].w;
                 Act<T>::st(dx + 4 * c4, o);
+                if (nsum == 3) {
+                    const float4 v = as_stored<T>(o);
+                    float4 t = ld4(osum + 4 * c4);
+                    t.x += v.x;
+                    t.y += v.y;
+                    t.z += v.z;
+                    t.w += v.w;
+                    st4(osum + 4 * c4, t);
+                }
             }
         }
     }
@@ -160,18 +198,18 @@ __global__ __launch_bounds__(256) void ln_bwd_kernel(
     for (int i = 0; i < NCH; i++) {
         const int c4 = lane + 64 * i;
         if (c4 < C4) {
-            st4(red + (wave * 2) * C + 4 * c4, pw[i]);
-            st4(red + (wave * 2 + 1) * C + 4 * c4, pb[i]);
+            st4(red + (wave * nsum) * C + 4 * c4, pw[i]);
+            st4(red + (wave * nsum + 1) * C + 4 * c4, pb[i]);
         }
     }
     __syncthreads();
-    for (int c = threadIdx.x; c < 2 * C; c += blockDim.x) {
+    for (int c = threadIdx.x; c < nsum * C; c += blockDim.x) {
         const int k = c / C, cc = c - k * C;
-        float s = red[(0 * 2 + k) * C + cc];
-        s += red[(1 * 2 + k) * C + cc];
-        s += red[(2 * 2 + k) * C + cc];
-        s += red[(3 * 2 + k) * C + cc];
-        partials[(int64_t)blockIdx.x * 2 * C + c] = s;
+        float s = red[(0 * nsum + k) * C + cc];
+        s += red[(1 * nsum + k) * C + cc];
+        s += red[(2 * nsum + k) * C + cc];
+        s += red[(3 * nsum + k) * C + cc];
+        partials[(int64_t)blockIdx.x * nsum * C + c] = s;
     }
 }
 
@@ -192,14 +230,14 @@ hipError_t ln_fwd_launch(hipStream_t s, T* out, float* mean, float* rstd, const 
 template <class T>
 hipError_t ln_bwd_launch(hipStream_t s, T* dres, int accumulate, float* partials, const T* dout,
                          const T* inp, const float* w, const float* mean, const float* rstd,
-                         int N, int C, int rpb, int nb) {
-    const size_t shm = (size_t)8 * C * sizeof(float);
+                         int N, int C, int rpb, int nb, int nsum) {
+    const size_t shm = (size_t)4 * nsum * C * sizeof(float);
     dim3 grid(nb), block(256);
     switch ((C + 255) / 256) {
-        case 1: launch((ln_bwd_kernel<1, T>), grid, block, shm, s, dres, accumulate, partials, dout, inp, w, mean, rstd, N, C, rpb); break;
-        case 2: launch((ln_bwd_kernel<2, T>), grid, block, shm, s, dres, accumulate, partials, dout, inp, w, mean, rstd, N, C, rpb); break;
-        case 3: launch((ln_bwd_kernel<3, T>), grid, block, shm, s, dres, accumulate, partials, dout, inp, w, mean, rstd, N, C, rpb); break;
-        case 4: launch((ln_bwd_kernel<4, T>), grid, block, shm, s, dres, accumulate, partials, dout, inp, w, mean, rstd, N, C, rpb); break;
+        case 1: launch((ln_bwd_kernel<1, T>), grid, block, shm, s, dres, accumulate, partials, dout, inp, w, mean, rstd, N, C, rpb, nsum); break;
+        case 2: launch((ln_bwd_kernel<2, T>), grid, block, shm, s, dres, accumulate, partials, dout, inp, w, mean, rstd, N, C, rpb, nsum); break;
+        case 3: launch((ln_bwd_kernel<3, T>), grid, block, shm, s, dres, accumulate, partials, dout, inp, w, mean, rstd, N, C, rpb, nsum); break;
+        case 4: launch((ln_bwd_kernel<4, T>), grid, block, shm, s, dres, accumulate, partials, dout, inp, w, mean, rstd, N, C, rpb, nsum); break;
         default: return hipErrorInvalidValue;
     }
     return hipGetLastError();
@@ -220,23 +258,24 @@ hipError_t layernorm_forward(hipStream_t s, void* out, float* mean, float* rstd,
 // 1024 (rows per workgroup grow past 4096 rows) and at most ceil(N/4).
 size_t layernorm_partials_floats(int N, int C) {
     const int nb = std::min(1024, (N + 3) / 4);
-    return (size_t)nb * 2 * C;
+    return (size_t)nb * 3 * C;
 }
 
 hipError_t layernorm_backward(hipStream_t s, void* dres, int accumulate, float* dw, float* db,
-                              float* partials, const void* dout, const void* inp,
+                              float* dbias, float* partials, const void* dout, const void* inp,
                               const float* w, const float* mean, const float* rstd, int N,
                               int C, int dt) {
     if (N <= 0) return hipSuccess;
     const int rpb = ln_rows_per_block(N);
     const int nb = (N + rpb - 1) / rpb;
+    const int nsum = dbias ? 3 : 2;
     hipError_t e = by_dt(dt, [&](auto x) {
         using E = decltype(x);
         return ln_bwd_launch<E>(s, (E*)dres, accumulate, partials, (const E*)dout,
-                                (const E*)inp, w, mean, rstd, N, C, rpb, nb);
+                                (const E*)inp, w, mean, rstd, N, C, rpb, nb, nsum);
     });
     if (e != hipSuccess) return e;
-    return colsum_add(s, dw, db, C, partials, nb, 2 * C);
+    return colsum_add(s, dw, db, dbias, C, partials, nb, nsum * C);
 }
 
 }  // namespace gk

@@ -581,9 +581,14 @@ int backward_impl(gpt2_model* md) {
                         dtmp, C)));
     TRY(run_gemm(md, mm(gk::GEMM_TN, gk::EPI_ACCUM, V, C, M, dlogits, y.Vp, lnf, C,
                         md->G(P_WTE), C)));
+    // Each layernorm backward also sums the residual-stream gradient it
+    // leaves, over rows: that is the output gradient of the projection whose
+    // result was added into the stream there, so the sum is that projection's
+    // bias gradient.  After the final layernorm: the last MLP projection's.
     const void* last = md->A(y.res3, (L - 1) * MC);
     LAUNCH(md, GPT2_KC_LAYERNORM, 0, es * 3.0 * M * C + 8.0 * M,
-           gk::layernorm_backward(s, dres, 0, md->G(P_LNFW), md->G(P_LNFB), lnpart, dtmp, last,
+           gk::layernorm_backward(s, dres, 0, md->G(P_LNFW), md->G(P_LNFB),
+                                  md->G(P_FCPROJB) + (size_t)(L - 1) * C, lnpart, dtmp, last,
                                   md->P(P_LNFW), md->at<float>(y.lnf_mean),
                                   md->at<float>(y.lnf_rstd), M, C, h));
     for (int l = L - 1; l >= 0; l--) {
@@ -609,8 +614,7 @@ int backward_impl(gpt2_model* md) {
         TRY(run_gemm(md, a));
         TRY(run_gemm(md, mm(gk::GEMM_TN, gk::EPI_ACCUM, C, 4 * C, M, dres, C, fchg, 4 * C,
                             md->G(P_FCPROJW) + (size_t)l * C * 4 * C, 4 * C)));
-        LAUNCH(md, GPT2_KC_OTHER, 0, es * M * C,
-               gk::bias_grad(s, md->G(P_FCPROJB) + l * C, bpart, dres, M, C, C, h));
+        // (its bias gradient came from the layernorm backward that left dres)
         // MLP fc: dln2 = dfch W;  dW += dfch^T ln2
         TRY(run_gemm(md, mm(gk::GEMM_NN, gk::EPI_STORE, M, C, 4 * C, dfch, 4 * C,
                             Wl(P_FCW, (size_t)l * 4 * C * C), C, dtmp, C)));
@@ -618,17 +622,16 @@ int backward_impl(gpt2_model* md) {
                             md->G(P_FCW) + (size_t)l * 4 * C * C, C)));
         LAUNCH(md, GPT2_KC_OTHER, 0, es * 4.0 * M * C,
                gk::bias_grad(s, md->G(P_FCB) + l * 4 * C, bpart, dfch, M, 4 * C, 4 * C, h));
+        // ln2; its output column sums are the attention projection's bias gradient
         LAUNCH(md, GPT2_KC_LAYERNORM, 0, es * 4.0 * M * C + 8.0 * M,
                gk::layernorm_backward(s, dres, 1, md->G(P_LN2W) + l * C, md->G(P_LN2B) + l * C,
-                                      lnpart, dtmp, res2, md->P(P_LN2W) + l * C, ln2m, ln2r, M, C,
-                                      h));
+                                      md->G(P_ATTPROJB) + (size_t)l * C, lnpart, dtmp, res2,
+                                      md->P(P_LN2W) + l * C, ln2m, ln2r, M, C, h));
         // attention projection: datty = dres W;  dW += dres^T atty
         TRY(run_gemm(md, mm(gk::GEMM_NN, gk::EPI_STORE, M, C, C, dres, C,
                             Wl(P_ATTPROJW, (size_t)l * C * C), C, dtmp, C)));
         TRY(run_gemm(md, mm(gk::GEMM_TN, gk::EPI_ACCUM, C, C, M, dres, C, atty, C,
                             md->G(P_ATTPROJW) + (size_t)l * C * C, C)));
-        LAUNCH(md, GPT2_KC_OTHER, 0, es * M * C,
-               gk::bias_grad(s, md->G(P_ATTPROJB) + l * C, bpart, dres, M, C, C, h));
         {
             const double hs = C / NH;
             const double flops = 8.0 * B * NH * hs * (double)T * (T + 1) / 2.0;
@@ -646,10 +649,13 @@ int backward_impl(gpt2_model* md) {
                             md->G(P_QKVW) + (size_t)l * 3 * C * C, C)));
         LAUNCH(md, GPT2_KC_OTHER, 0, es * 3.0 * M * C,
                gk::bias_grad(s, md->G(P_QKVB) + l * 3 * C, bpart, dqkv, M, 3 * C, 3 * C, h));
+        // ln1; its output is the gradient at the previous layer's output, whose
+        // column sums are that layer's MLP-projection bias gradient
         LAUNCH(md, GPT2_KC_LAYERNORM, 0, es * 4.0 * M * C + 8.0 * M,
                gk::layernorm_backward(s, dres, 1, md->G(P_LN1W) + l * C, md->G(P_LN1B) + l * C,
-                                      lnpart, dtmp, resid, md->P(P_LN1W) + l * C, ln1m, ln1r, M, C,
-                                      h));
+                                      l > 0 ? md->G(P_FCPROJB) + (size_t)(l - 1) * C : nullptr,
+                                      lnpart, dtmp, resid, md->P(P_LN1W) + l * C, ln1m, ln1r, M,
+                                      C, h));
     }
     LAUNCH(md, GPT2_KC_OTHER, 0, es * M * C + 8.0 * M * C + 8.0 * T * C + 4.0 * M,
            gk::encoder_backward(s, md->G(P_WTE), y.rope ? nullptr : md->G(P_WPE), dres,
