@@ -135,24 +135,26 @@ struct Tile<false, R, NT, BK> {
     }
 };
 
+// Returns the values stored into C (used for the EPI_GELU_BWD column sums).
 template <int EPI>
-__device__ __forceinline__ void epi_store(const GemmArgs& a, float* __restrict__ partial,
-                                          int row, int col, float4 v) {
+__device__ __forceinline__ float4 epi_store(const GemmArgs& a, float* __restrict__ partial,
+                                            int row, int col, float4 v) {
     if (EPI == EPI_PARTIAL) {
         st4(partial + (int64_t)blockIdx.z * a.M * a.N + (int64_t)row * a.N + col, v);
-        return;
+        return v;
     }
     float* c = a.C + (int64_t)row * a.ldc + col;
     if (EPI == EPI_ACCUM) {
         const float4 o = ld4(c);
         st4(c, make_float4(o.x + v.x, o.y + v.y, o.z + v.z, o.w + v.w));
-        return;
+        return v;
     }
     if (EPI == EPI_GELU_BWD) {
         const float4 x = ld4(a.aux + (int64_t)row * a.ldaux + col);
-        st4(c, make_float4(v.x * gelu_grad_f(x.x), v.y * gelu_grad_f(x.y), v.z * gelu_grad_f(x.z),
-                           v.w * gelu_grad_f(x.w)));
-        return;
+        const float4 o = make_float4(v.x * gelu_grad_f(x.x), v.y * gelu_grad_f(x.y),
+                                     v.z * gelu_grad_f(x.z), v.w * gelu_grad_f(x.w));
+        st4(c, o);
+        return o;
     }
     float4 bb = make_float4(0.f, 0.f, 0.f, 0.f);
     if (EPI != EPI_STORE || a.bias) bb = ld4(a.bias + col);
@@ -165,24 +167,30 @@ __device__ __forceinline__ void epi_store(const GemmArgs& a, float* __restrict__
     if (EPI == EPI_GELU)
         st4(a.out2 + (int64_t)row * a.ldc + col,
             make_float4(gelu_f(v.x), gelu_f(v.y), gelu_f(v.z), gelu_f(v.w)));
+    return v;
 }
 
 template <int EPI>
-__device__ __forceinline__ void epi_scalar(const GemmArgs& a, float* __restrict__ partial,
-                                           int row, int col, float v) {
+__device__ __forceinline__ float epi_scalar(const GemmArgs& a, float* __restrict__ partial,
+                                            int row, int col, float v) {
     if (EPI == EPI_PARTIAL) {
         partial[(int64_t)blockIdx.z * a.M * a.N + (int64_t)row * a.N + col] = v;
-        return;
+        return v;
     }
     const int64_t idx = (int64_t)row * a.ldc + col;
-    if (EPI == EPI_ACCUM) { a.C[idx] += v; return; }
-    if (EPI == EPI_GELU_BWD) { a.C[idx] = v * gelu_grad_f(a.aux[(int64_t)row * a.ldaux + col]); return; }
+    if (EPI == EPI_ACCUM) { a.C[idx] += v; return v; }
+    if (EPI == EPI_GELU_BWD) {
+        const float o = v * gelu_grad_f(a.aux[(int64_t)row * a.ldaux + col]);
+        a.C[idx] = o;
+        return o;
+    }
     float bb = 0.f;
     if (EPI != EPI_STORE || a.bias) bb = a.bias[col];
     v += bb;
     if (EPI == EPI_RESID) v += a.aux[(int64_t)row * a.ldaux + col];
     a.C[idx] = v;
     if (EPI == EPI_GELU) a.out2[idx] = gelu_f(v);
+    return v;
 }
 
 template <int OP, int EPI, int BK>
@@ -305,6 +313,10 @@ __global__ __launch_bounds__(NTHR, BK == 16 ? 3 : 2) void gemm_kernel(
     // main loop's buffers are free after its last barrier), then apply the
     // epilogue along rows with float4.
     float* ws = sm + wave * 32 * 68;
+    // EPI_GELU_BWD column sums: a lane keeps columns 4*(lane & 15) .. +3 of
+    // the wave's block through both halves
+    const bool csum = EPI == EPI_GELU_BWD && a.colsum != nullptr;
+    float4 cs = make_float4(0.f, 0.f, 0.f, 0.f);
 #pragma unroll
     for (int bm = 0; bm < 2; bm++) {
         if (bm == 1) __syncthreads();  // every wave has read its first half
@@ -321,12 +333,40 @@ __global__ __launch_bounds__(NTHR, BK == 16 ? 3 : 2) void gemm_kernel(
             const float4 v = ld4(ws + r * 68 + c4);
             const int row = m0 + wm + 32 * bm + r, col = n0 + wn + c4;
             if (row >= a.M) continue;
+            float4 o = make_float4(0.f, 0.f, 0.f, 0.f);
             if (col + 3 < a.N) {
-                epi_store<EPI>(a, partial, row, col, v);
+                o = epi_store<EPI>(a, partial, row, col, v);
             } else {
-                if (col < a.N) epi_scalar<EPI>(a, partial, row, col, v.x);
-                if (col + 1 < a.N) epi_scalar<EPI>(a, partial, row, col + 1, v.y);
-                if (col + 2 < a.N) epi_scalar<EPI>(a, partial, row, col + 2, v.z);
+                if (col < a.N) o.x = epi_scalar<EPI>(a, partial, row, col, v.x);
+                if (col + 1 < a.N) o.y = epi_scalar<EPI>(a, partial, row, col + 1, v.y);
+                if (col + 2 < a.N) o.z = epi_scalar<EPI>(a, partial, row, col + 2, v.z);
+            }
+            if (csum) {
+                cs.x += o.x;
+                cs.y += o.y;
+                cs.z += o.z;
+                cs.w += o.w;
+            }
+        }
+    }
+    if (csum) {
+        // the four lanes that share columns, added in a fixed order
+#pragma unroll
+        for (int off = 16; off < 64; off <<= 1) {
+            cs.x += __shfl_xor(cs.x, off, WAVE);
+            cs.y += __shfl_xor(cs.y, off, WAVE);
+            cs.z += __shfl_xor(cs.z, off, WAVE);
+            cs.w += __shfl_xor(cs.w, off, WAVE);
+        }
+        const int col = n0 + wn + (lane & 15) * 4;
+        if (lane < 16 && m0 + wm < a.M) {
+            float* p = a.colsum + (int64_t)((m0 + wm) >> 6) * a.N + col;
+            if (col + 3 < a.N) {
+                st4(p, cs);
+            } else {
+                if (col < a.N) p[0] = cs.x;
+                if (col + 1 < a.N) p[1] = cs.y;
+                if (col + 2 < a.N) p[2] = cs.z;
             }
         }
     }
@@ -498,6 +538,10 @@ hipError_t gemm(hipStream_t s, const GemmArgs& a, float* ws, size_t ws_bytes) {
         return hipErrorInvalidValue;
     int splits = choose_splits(a.op, a.epi, a.M, a.N, a.K);
     if (splits > 1 && gemm_workspace_bytes(a.op, a.epi, a.M, a.N, a.K) > ws_bytes) splits = 1;
+    if (a.colsum) {
+        if (a.epi != EPI_GELU_BWD) return hipErrorInvalidValue;
+        splits = 1;  // the column sums are taken in the matmul's own epilogue
+    }
     if (splits > 1) {
         switch (a.op) {
             case GEMM_NT: return launch_split<GEMM_NT>(s, a, splits, ws);

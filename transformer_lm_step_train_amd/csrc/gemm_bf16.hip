@@ -203,26 +203,27 @@ __device__ __forceinline__ void st4h(uint16_t* p, float4 v) {
 
 // Epilogue on 4 consecutive columns.  bf16 outputs: STORE, RESID, GELU,
 // GELU_BWD.  fp32 outputs: ACCUM (gradient +=), STORE when out_f32, PARTIAL.
+// GELU_BWD returns the values as stored (for its column sums).
 template <int EPI, class H>
-__device__ __forceinline__ void epi4(const GemmArgsH& a, float* __restrict__ partial, int row,
-                                     int col, float4 v) {
+__device__ __forceinline__ float4 epi4(const GemmArgsH& a, float* __restrict__ partial, int row,
+                                       int col, float4 v) {
     if (EPI == EPI_PARTIAL) {
         st4(partial + (int64_t)blockIdx.z * a.M * a.N + (int64_t)row * a.N + col, v);
-        return;
+        return v;
     }
     const int64_t idx = (int64_t)row * a.ldc + col;
     if (EPI == EPI_ACCUM) {
         float* c = reinterpret_cast<float*>(a.C) + idx;
         const float4 o = ld4(c);
         st4(c, make_float4(o.x + v.x, o.y + v.y, o.z + v.z, o.w + v.w));
-        return;
+        return v;
     }
     if (EPI == EPI_GELU_BWD) {
         const float4 x = ld4h<H>(a.aux + (int64_t)row * a.ldaux + col);
-        st4h<H>(reinterpret_cast<uint16_t*>(a.C) + idx,
-             make_float4(v.x * gelu_grad_f(x.x), v.y * gelu_grad_f(x.y), v.z * gelu_grad_f(x.z),
-                         v.w * gelu_grad_f(x.w)));
-        return;
+        const uint2 u = make_uint2(H::pk(v.x * gelu_grad_f(x.x), v.y * gelu_grad_f(x.y)),
+                                   H::pk(v.z * gelu_grad_f(x.z), v.w * gelu_grad_f(x.w)));
+        *reinterpret_cast<uint2*>(reinterpret_cast<uint16_t*>(a.C) + idx) = u;
+        return make_float4(H::lo(u.x), H::hi(u.x), H::lo(u.y), H::hi(u.y));
     }
     if (EPI == EPI_RESID || EPI == EPI_GELU || (EPI == EPI_STORE && a.bias)) {
         const float4 bb = ld4(a.bias + col);
@@ -234,38 +235,40 @@ __device__ __forceinline__ void epi4(const GemmArgsH& a, float* __restrict__ par
     }
     if (EPI == EPI_STORE && a.out_f32) {
         st4(reinterpret_cast<float*>(a.C) + idx, v);
-        return;
+        return v;
     }
     st4h<H>(reinterpret_cast<uint16_t*>(a.C) + idx, v);
     if (EPI == EPI_GELU)
         st4h<H>(a.out2 + idx, make_float4(gelu_f(v.x), gelu_f(v.y), gelu_f(v.z), gelu_f(v.w)));
+    return v;
 }
 
 template <int EPI, class H>
-__device__ __forceinline__ void epi1(const GemmArgsH& a, float* __restrict__ partial, int row,
-                                     int col, float v) {
+__device__ __forceinline__ float epi1(const GemmArgsH& a, float* __restrict__ partial, int row,
+                                      int col, float v) {
     if (EPI == EPI_PARTIAL) {
         partial[(int64_t)blockIdx.z * a.M * a.N + (int64_t)row * a.N + col] = v;
-        return;
+        return v;
     }
     const int64_t idx = (int64_t)row * a.ldc + col;
     if (EPI == EPI_ACCUM) {
         reinterpret_cast<float*>(a.C)[idx] += v;
-        return;
+        return v;
     }
     if (EPI == EPI_GELU_BWD) {
-        reinterpret_cast<uint16_t*>(a.C)[idx] =
-            H::h(v * gelu_grad_f(H::f(a.aux[(int64_t)row * a.ldaux + col])));
-        return;
+        const uint16_t o = H::h(v * gelu_grad_f(H::f(a.aux[(int64_t)row * a.ldaux + col])));
+        reinterpret_cast<uint16_t*>(a.C)[idx] = o;
+        return H::f(o);
     }
     if (EPI == EPI_RESID || EPI == EPI_GELU || (EPI == EPI_STORE && a.bias)) v += a.bias[col];
     if (EPI == EPI_RESID) v += H::f(a.aux[(int64_t)row * a.ldaux + col]);
     if (EPI == EPI_STORE && a.out_f32) {
         reinterpret_cast<float*>(a.C)[idx] = v;
-        return;
+        return v;
     }
     reinterpret_cast<uint16_t*>(a.C)[idx] = H::h(v);
     if (EPI == EPI_GELU) a.out2[idx] = H::h(gelu_f(v));
+    return v;
 }
 
 template <int OP, int EPI, class H, bool TRB>
@@ -375,7 +378,10 @@ __global__ __launch_bounds__(NTHR, 2) void gemm_bf16_kernel(const GemmArgsH a, i
         __syncthreads();
     }
 
-    // stage each wave's 64x64 fp32 block in LDS, then work along rows
+    // stage each wave's 64x64 fp32 block in LDS, then work along rows;
+    // EPI_GELU_BWD column sums: a lane keeps columns 4*(lane & 15) .. +3
+    const bool csum = EPI == EPI_GELU_BWD && a.colsum != nullptr;
+    float4 cs = make_float4(0.f, 0.f, 0.f, 0.f);
     float* ws = reinterpret_cast<float*>(smraw) + wave * 64 * 68;
 #pragma unroll
     for (int bm = 0; bm < 2; bm++)
@@ -392,12 +398,41 @@ __global__ __launch_bounds__(NTHR, 2) void gemm_bf16_kernel(const GemmArgsH a, i
         const float4 v = ld4(ws + r * 68 + c4);
         const int row = m0 + wm + r, col = n0 + wn + c4;
         if (row >= a.M) continue;
+        float4 o = make_float4(0.f, 0.f, 0.f, 0.f);
         if (col + 3 < a.N) {
-            epi4<EPI, H>(a, partial, row, col, v);
+            o = epi4<EPI, H>(a, partial, row, col, v);
         } else {
-            if (col < a.N) epi1<EPI, H>(a, partial, row, col, v.x);
-            if (col + 1 < a.N) epi1<EPI, H>(a, partial, row, col + 1, v.y);
-            if (col + 2 < a.N) epi1<EPI, H>(a, partial, row, col + 2, v.z);
+            if (col < a.N) o.x = epi1<EPI, H>(a, partial, row, col, v.x);
+            if (col + 1 < a.N) o.y = epi1<EPI, H>(a, partial, row, col + 1, v.y);
+            if (col + 2 < a.N) o.z = epi1<EPI, H>(a, partial, row, col + 2, v.z);
+        }
+        if (csum) {
+            cs.x += o.x;
+            cs.y += o.y;
+            cs.z += o.z;
+            cs.w += o.w;
+        }
+    }
+    if (csum) {
+        // the four lanes that share columns, added in a fixed order; one
+        // partial row per 64 output rows
+#pragma unroll
+        for (int off = 16; off < 64; off <<= 1) {
+            cs.x += __shfl_xor(cs.x, off, WAVE);
+            cs.y += __shfl_xor(cs.y, off, WAVE);
+            cs.z += __shfl_xor(cs.z, off, WAVE);
+            cs.w += __shfl_xor(cs.w, off, WAVE);
+        }
+        const int col = n0 + wn + (lane & 15) * 4;
+        if (lane < 16 && m0 + wm < a.M) {
+            float* p = a.colsum + (int64_t)((m0 + wm) >> 6) * a.N + col;
+            if (col + 3 < a.N) {
+                st4(p, cs);
+            } else {
+                if (col < a.N) p[0] = cs.x;
+                if (col + 1 < a.N) p[1] = cs.y;
+                if (col + 2 < a.N) p[2] = cs.z;
+            }
         }
     }
 }
@@ -907,6 +942,10 @@ hipError_t gemm_bf16(hipStream_t s, const GemmArgsH& a, float* ws, size_t ws_byt
     if (p.splits > 1 &&
         (size_t)cdiv(a.K, split_chunk_h(a.K, p.splits)) * a.M * a.N * sizeof(float) > ws_bytes)
         p.splits = 1;
+    if (a.colsum) {
+        if (a.epi != EPI_GELU_BWD) return hipErrorInvalidValue;
+        p = {false, 1};  // the column sums are taken in the 128x128 kernel's epilogue
+    }
     return a.f16 ? run<HF16>(s, a, p, ws) : run<HBF16>(s, a, p, ws);
 }
 

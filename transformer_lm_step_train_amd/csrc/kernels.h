@@ -57,6 +57,10 @@ struct GemmArgs {
     const float* aux;   // EPI_RESID, EPI_GELU_BWD
     int64_t ldaux;
     float* out2;        // EPI_GELU
+    // EPI_GELU_BWD, optional: colsum[(m / 64) * N + n] = the sum of the stored
+    // C[m', n] over the 64 rows m' of that block (cdiv(M, 64) x N floats; the
+    // product then runs without a K split).
+    float* colsum;
 };
 
 // 16-bit variant (mixed precision): A and B are bf16 (f16 = 0) or fp16
@@ -78,6 +82,7 @@ struct GemmArgsH {
     const uint16_t* aux;
     int64_t ldaux;
     uint16_t* out2;
+    float* colsum;  // as in GemmArgs, of C as stored (rounded to 16 bits)
 };
 size_t gemm_bf16_workspace_bytes(int op, int epi, int M, int N, int K);
 hipError_t gemm_bf16(hipStream_t s, const GemmArgsH& a, float* workspace,

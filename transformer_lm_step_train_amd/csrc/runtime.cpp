@@ -368,6 +368,7 @@ struct Mm {
     const void* aux = nullptr;
     int64_t ldaux = 0;
     void* out2 = nullptr;
+    float* colsum = nullptr;  // EPI_GELU_BWD: per-64-row column sums of C
 };
 
 Mm mm(int op, int epi, int M, int N, int K, const void* A, int64_t lda, const void* B,
@@ -413,6 +414,7 @@ int run_gemm(gpt2_model* md, const Mm& x) {
         a.aux = (const uint16_t*)x.aux;
         a.ldaux = x.ldaux;
         a.out2 = (uint16_t*)x.out2;
+        a.colsum = x.colsum;
         LAUNCH(md, GPT2_KC_GEMM, flops, bytes, gk::gemm_bf16(md->stream, a, ws, wsb));
     } else {
         gk::GemmArgs a{};
@@ -431,6 +433,7 @@ int run_gemm(gpt2_model* md, const Mm& x) {
         a.aux = (const float*)x.aux;
         a.ldaux = x.ldaux;
         a.out2 = (float*)x.out2;
+        a.colsum = x.colsum;
         LAUNCH(md, GPT2_KC_GEMM, flops, bytes, gk::gemm(md->stream, a, ws, wsb));
     }
     return GPT2_OK;
@@ -606,11 +609,14 @@ int backward_impl(gpt2_model* md) {
         const void* fch = md->A(y.fch, l * 4 * MC);
         const void* fchg = md->A(y.fch_gelu, l * 4 * MC);
 
-        // MLP projection: dfch = (dres W) * gelu'(fch);  dW += dres^T gelu(fch)
+        // MLP projection: dfch = (dres W) * gelu'(fch);  dW += dres^T gelu(fch).
+        // The epilogue also sums dfch (the fc output gradient) over each
+        // 64-row block: partial rows of the fc bias gradient.
         Mm a = mm(gk::GEMM_NN, gk::EPI_GELU_BWD, M, 4 * C, C, dres, C,
                   Wl(P_FCPROJW, (size_t)l * C * 4 * C), 4 * C, dfch, 4 * C);
         a.aux = fch;
         a.ldaux = 4 * C;
+        a.colsum = bpart;
         TRY(run_gemm(md, a));
         TRY(run_gemm(md, mm(gk::GEMM_TN, gk::EPI_ACCUM, C, 4 * C, M, dres, C, fchg, 4 * C,
                             md->G(P_FCPROJW) + (size_t)l * C * 4 * C, 4 * C)));
@@ -620,8 +626,9 @@ int backward_impl(gpt2_model* md) {
                             Wl(P_FCW, (size_t)l * 4 * C * C), C, dtmp, C)));
         TRY(run_gemm(md, mm(gk::GEMM_TN, gk::EPI_ACCUM, 4 * C, C, M, dfch, 4 * C, ln2, C,
                             md->G(P_FCW) + (size_t)l * 4 * C * C, C)));
-        LAUNCH(md, GPT2_KC_OTHER, 0, es * 4.0 * M * C,
-               gk::bias_grad(s, md->G(P_FCB) + l * 4 * C, bpart, dfch, M, 4 * C, 4 * C, h));
+        LAUNCH(md, GPT2_KC_OTHER, 0, 4.0 * ((M + 63) / 64) * 4 * C,
+               gk::colsum_add(s, md->G(P_FCB) + l * 4 * C, nullptr, nullptr, 4 * C, bpart,
+                              (M + 63) / 64, 4 * C));
         // ln2; its output column sums are the attention projection's bias gradient
         LAUNCH(md, GPT2_KC_LAYERNORM, 0, es * 4.0 * M * C + 8.0 * M,
                gk::layernorm_backward(s, dres, 1, md->G(P_LN2W) + l * C, md->G(P_LN2B) + l * C,
