@@ -4,9 +4,9 @@
 // C 语言实现", section "用C语言实现LLM": the matmul layer; the reduced-precision
 // extension is named by yinghuohong.cn, section "脚动完成每一个层前向/反向流传").
 //
-// Two kernels share the operand conventions of the fp32 one (NT forward, NN
-// input gradient, TN weight gradient) and its fused epilogues; outputs are
-// bf16 activations or fp32 weight gradients (+=).
+// Three kernels share the operand conventions of the fp32 one (NT forward,
+// NN input gradient, TN weight gradient) and its fused epilogues; outputs
+// are bf16 activations or fp32 weight gradients (+=).
 //
 // The forward and input-gradient products use a 128x128 output tile per
 // 256-thread workgroup, 64x64 per wave (2x2 blocks of the 32x32 MFMA), and
