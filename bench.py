@@ -6,10 +6,13 @@ Usage: python bench.py [--gpus 1] [--steps K] [--warmup W]
 Prints one JSON line.  The timed region covers exactly K training steps,
 each = forward with the loss read back to the host + zero-grad + backward +
 AdamW update, with token ids already resident in device memory; it is
-bracketed by device synchronizations.  Per-kernel-class times come from HIP
-events the library records around its own launches on its stream during the
-timed steps.  The CPU-oracle baseline is timed afterwards on a bounded sample
-(one sequence of the same batch shape) on the host cores.
+bracketed by device synchronizations.  The matmul family's launch times come
+from HIP events carried in the library's own dispatches on its stream during
+the timed steps; the per-class breakdown from a second, fully instrumented
+pass.  By default the line also carries `mixed_bf16`: the same measurement
+of the bf16 mixed-precision model on the same batch.  The CPU-oracle
+baseline is timed afterwards on a bounded sample (one sequence of the batch)
+on the host cores.
 """
 import argparse
 import hashlib
@@ -38,6 +41,8 @@ def parse():
     ap.add_argument("--precision", choices=["fp32", "bf16", "fp16"], default="fp32",
                     help="fp32 (the headline workload), or the bf16 / fp16 mixed-precision "
                          "model")
+    ap.add_argument("--no-mixed", action="store_true",
+                    help="fp32 run only: no mixed_bf16 leg")
     ap.add_argument("--no-kernel-timing", action="store_true",
                     help="no kernel events: no roofline object and no instrumented second pass")
     a = ap.parse_args()
@@ -67,47 +72,66 @@ def measured_traffic(half):
     return round(rec["hbm_bytes_per_launch"])
 
 
-def cpu_baseline(c, params, tok, tgt):
-    """The oracle (plain C, OpenMP) on one sequence of the batch: one full
-    training step at B=1, T=1024, i.e. 1/16 of the GPU step's tokens."""
-    from oracle import OracleModel
-    cores = int(os.environ.get("OMP_NUM_THREADS") or len(os.sched_getaffinity(0)))
-    o = OracleModel(c["L"], c["C"], c["NH"], c["V"], c["maxT"], 1, c["T"])
-    o.params[:] = params
-    t0 = time.perf_counter()
-    o.forward(tok[:1], tgt[:1])
-    o.zero_grad()
-    o.backward()
-    o.update(step=1, lr=1e-4)
-    dt = time.perf_counter() - t0
-    o.close()
-    out = {"value": round(c["T"] / dt, 2), "unit": "tokens/s", "cores": cores,
-           "kind": "oracle",
-           "sample": f"1 training step (fwd+bwd+AdamW) on 1 sequence of T={c['T']} "
-                     f"(1/{c['B']} of the batch), {dt:.2f} s"}
-    # The pages' own run: 124M at B=4, T=64 with 8 threads, printed at
-    # 1.29-1.45 s per step on an M3 Max (ujoy.net, section "训练过程").
-    import oracle as _o
-    from transformer_lm_step_train_amd import synth
-    p4 = synth.CONFIGS["gpt2_124m_b4t64"]
-    lb = _o.lib("f32")
-    lb.oracle_set_threads(8)
-    o = OracleModel(p4["L"], p4["C"], p4["NH"], p4["V"], p4["maxT"], p4["B"], p4["T"])
-    o.params[:] = params
-    t4, g4 = synth.token_stream(p4["B"], p4["T"], p4["V"])
+def host_ram_gib():
+    try:
+        return round(os.sysconf("SC_PAGE_SIZE") * os.sysconf("SC_PHYS_PAGES") / 2**30, 1)
+    except (ValueError, OSError):
+        return None
+
+
+def oracle_steps(o, tok, tgt, n):
+    """n full training steps of the oracle; seconds per step."""
     times = []
-    for s in range(1, 4):  # 1 warm-up + 2 timed
+    for s in range(1, n + 1):
         t0 = time.perf_counter()
-        o.forward(t4, g4)
+        o.forward(tok, tgt)
         o.zero_grad()
         o.backward()
         o.update(step=s, lr=1e-4)
         times.append(time.perf_counter() - t0)
+    return times
+
+
+def cpu_baseline(c, params, tok, tgt):
+    """The oracle (plain C, OpenMP over rows) timed as it is, on a bounded
+    sample of the workload: one sequence of the batch (B=1, T=1024), 1
+    warm-up step (first touch of its arenas) and 2 timed steps on every host
+    core.  Its per-token work equals the full batch's (sequences are
+    independent and every matmul is linear in the rows), so tokens/s carries
+    over to B=16, which needs about 76 GB of host memory and 3 minutes per
+    step.  A second leg runs the pages' own shape (124M, B=4, T=64) at 8
+    threads, the setting of the pages' run, printed at 1.29-1.45 s per step
+    on an M3 Max (ujoy.net, section "训练过程")."""
+    import oracle as _o
+    from oracle import OracleModel
+    from transformer_lm_step_train_amd import synth
+    cores = int(os.environ.get("OMP_NUM_THREADS") or len(os.sched_getaffinity(0)))
+    lb = _o.lib("f32")
+    lb.oracle_set_threads(cores)
+    o = OracleModel(c["L"], c["C"], c["NH"], c["V"], c["maxT"], 1, c["T"])
+    o.params[:] = params
+    times = oracle_steps(o, tok[:1], tgt[:1], 3)
+    o.close()
+    dt = sum(times[1:]) / 2
+    out = {"value": round(c["T"] / dt, 2), "unit": "tokens/s", "cores": cores,
+           "kind": "oracle",
+           "sample": f"B=1 T={c['T']} (one sequence of the B={c['B']} batch): 1 warm-up + 2 "
+                     f"timed training steps (fwd+bwd+AdamW), {times[1]:.2f} / {times[2]:.2f} s "
+                     f"(warm-up {times[0]:.2f} s); host RAM {host_ram_gib()} GiB",
+           "threads_8": None}
+    p4 = synth.CONFIGS["gpt2_124m_b4t64"]
+    lb.oracle_set_threads(8)
+    o = OracleModel(p4["L"], p4["C"], p4["NH"], p4["V"], p4["maxT"], p4["B"], p4["T"])
+    o.params[:] = params
+    t4, g4 = synth.token_stream(p4["B"], p4["T"], p4["V"])
+    times = oracle_steps(o, t4, g4, 3)
     o.close()
     lb.oracle_set_threads(cores)
-    out["pages_shape"] = {"workload": "GPT-2 124M, B=4 T=64 (the pages' run)", "threads": 8,
-                          "s_per_step": round(sum(times[1:]) / 2, 3),
-                          "page_m3max_s_per_step": [1.289, 1.452]}
+    s8 = sum(times[1:]) / 2
+    out["threads_8"] = {"workload": "GPT-2 124M, B=4 T=64 (the pages' run)", "threads": 8,
+                        "steps": "1 warm-up + 2 timed", "s_per_step": round(s8, 3),
+                        "tokens_per_s": round(256 / s8, 1),
+                        "page_m3max_s_per_step": [1.289, 1.452]}
     return out
 
 
@@ -139,24 +163,16 @@ def pages_shape_gpu(params):
             "tokens_per_s": round(256 / ms * 1000.0, 1)}
 
 
-def main():
-    args = parse()
-    if args.gpus != 1:
-        print(f"bench.py: --gpus {args.gpus} is not supported: this library runs on one GPU "
-              f"only (no collectives); run with --gpus 1", file=sys.stderr)
-        sys.exit(2)
+def run_leg(precision, args, params, tok, tgt):
+    """Warm-up, K timed training steps, then K instrumented steps of one
+    model on the batch; its throughput, step roofline and per-class times."""
     import torch
     from transformer_lm_step_train_amd import gpt2, synth
-
-    assert torch.cuda.is_available(), "bench.py needs a GPU"
-    torch.cuda.set_device(0)
     c = synth.CONFIGS[WORKLOAD]
     B, T = c["B"], c["T"]
-    params = synth.init_params(c["L"], c["C"], c["V"], c["maxT"])
-    tok, tgt = synth.token_stream(B, T, c["V"])
-    half = args.precision in ("bf16", "fp16")
+    half = precision in ("bf16", "fp16")
     prec = {"fp32": gpt2.GPT2_FP32, "bf16": gpt2.GPT2_BF16_MIXED,
-            "fp16": gpt2.GPT2_F16_MIXED}[args.precision]
+            "fp16": gpt2.GPT2_F16_MIXED}[precision]
     m = gpt2.Model(c["L"], c["C"], c["NH"], c["V"], c["maxT"], B, T, precision=prec)
     m.set_params(params)
     dtok = torch.tensor(tok, dtype=torch.int32, device="cuda")
@@ -237,12 +253,11 @@ def main():
                     "frac": round(achieved / peak, 4), "traffic": measured_traffic(half),
                     "traffic_unit": "HBM bytes per launch (rocprofv3 FETCH_SIZE+WRITE_SIZE)",
                     "algorithmic_bytes_per_launch": round(g["bytes"] / n),
-                    "kernel": "gemm (all %s MFMA matmul launches of the step)"
-                              % {"fp32": "fp32", "bf16": "bf16", "fp16": "fp16"}[args.precision],
+                    "kernel": "gemm (all %s MFMA matmul launches of the step)" % precision,
                     "launches_per_step": n // args.steps,
                     "avg_launch_ms": round(g["ms"] / n, 4)}
-        print(f"per-class kernel time per step (instrumented pass, {inst_ms:.3f} ms per step):",
-              file=sys.stderr)
+        print(f"[{precision}] per-class kernel time per step (instrumented pass, "
+              f"{inst_ms:.3f} ms per step):", file=sys.stderr)
         total = 0.0
         for name, r in kci.items():
             per = r["ms"] / args.steps
@@ -252,29 +267,15 @@ def main():
             print(f"  {name:11s} {per:9.3f} ms  launches/step {r['launches'] // args.steps:4d}"
                   f"  {tf:7.2f} TFLOP/s  {gbs:8.1f} GB/s", file=sys.stderr)
         print(f"  {'sum':11s} {total:9.3f} ms of {inst_ms:.3f} ms per step", file=sys.stderr)
-
-    out = {
-        "metric": "training tokens/sec (fwd+bwd+AdamW), GPT-2 124M B16 T1024 at 1 GPU"
-                  + ("" if not half else f" ({args.precision} mixed precision)"),
+    return {
         "value": round(tokens_per_s, 1),
-        "unit": "tokens/s",
-        "n_gpus": 1,
-        "steps": args.steps,
-        "warmup": args.warmup,
         "ms_per_step": round(ms, 3),
         "ms_per_step_median": round(ms_median, 3),
-        "higher_is_better": True,
-        "scaling": "weak",
-        "vs_baseline": None,
-        "dtype": {"fp32": "f32", "bf16": "bf16", "fp16": "f16"}[args.precision],
-        "data": "synthetic (seeded uniform int32 token ids, GPT-2 init N(0,0.02))",
-        "config": {"workload": "GPT-2 124M training step, B=16 T=1024 "
-                               + (f"{args.precision} mixed precision" if half else "fp32"),
-                   "global_batch": B, "seq_len": T, "layers": c["L"], "channels": c["C"],
-                   "heads": c["NH"], "vocab": c["V"], "parallelism": "single GPU"},
+        "dtype": {"fp32": "f32", "bf16": "bf16", "fp16": "f16"}[precision],
+        "workload": "GPT-2 124M training step, B=16 T=1024 "
+                    + (f"{precision} mixed precision" if half else "fp32"),
         "roofline": roofline,
         "step_roofline": step_roof,
-        "cpu_baseline": None,
         "kernel_ms_per_step": {k: round(v["ms"] / args.steps, 3) for k, v in kci.items()},
         "kernel_timing": None if not kc else (
             "the timed region times the matmul family only (roofline); kernel_ms_per_step "
@@ -282,6 +283,55 @@ def main():
             f"{inst_ms:.3f} ms per step there"),
         "loss_first_last": [round(timed_losses[0], 5), round(timed_losses[-1], 5)],
     }
+
+
+def main():
+    args = parse()
+    if args.gpus != 1:
+        print(f"bench.py: --gpus {args.gpus} is not supported: this library runs on one GPU "
+              f"only (no collectives); run with --gpus 1", file=sys.stderr)
+        sys.exit(2)
+    import torch
+    from transformer_lm_step_train_amd import synth
+
+    assert torch.cuda.is_available(), "bench.py needs a GPU"
+    torch.cuda.set_device(0)
+    c = synth.CONFIGS[WORKLOAD]
+    B, T = c["B"], c["T"]
+    params = synth.init_params(c["L"], c["C"], c["V"], c["maxT"])
+    tok, tgt = synth.token_stream(B, T, c["V"])
+    half = args.precision in ("bf16", "fp16")
+    head = run_leg(args.precision, args, params, tok, tgt)
+
+    out = {
+        "metric": "training tokens/sec (fwd+bwd+AdamW), GPT-2 124M B16 T1024 at 1 GPU"
+                  + ("" if not half else f" ({args.precision} mixed precision)"),
+        "value": head["value"],
+        "unit": "tokens/s",
+        "n_gpus": 1,
+        "steps": args.steps,
+        "warmup": args.warmup,
+        "ms_per_step": head["ms_per_step"],
+        "ms_per_step_median": head["ms_per_step_median"],
+        "higher_is_better": True,
+        "scaling": "weak",
+        "vs_baseline": None,
+        "dtype": head["dtype"],
+        "data": "synthetic (seeded uniform int32 token ids, GPT-2 init N(0,0.02))",
+        "config": {"workload": head["workload"],
+                   "global_batch": B, "seq_len": T, "layers": c["L"], "channels": c["C"],
+                   "heads": c["NH"], "vocab": c["V"], "parallelism": "single GPU"},
+        "roofline": head["roofline"],
+        "step_roofline": head["step_roofline"],
+        "cpu_baseline": None,
+        "kernel_ms_per_step": head["kernel_ms_per_step"],
+        "kernel_timing": head["kernel_timing"],
+        "loss_first_last": head["loss_first_last"],
+    }
+    if not half and not args.no_mixed:
+        # the mixed-precision configuration of the same workload (bf16
+        # activations and matmul operands, fp32 master weights and Adam state)
+        out["mixed_bf16"] = run_leg("bf16", args, params, tok, tgt)
     if not args.no_cpu_baseline and not half:
         out["cpu_baseline"] = cpu_baseline(c, params, tok, tgt)
         out["pages_shape_gpu"] = pages_shape_gpu(params)

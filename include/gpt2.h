@@ -47,6 +47,7 @@ extern "C" {
                              with targets)                                  */
 #define GPT2_ENOMEM (-4)  /* the allocator returned NULL                    */
 #define GPT2_EDEVICE (-5) /* a HIP runtime error (message has its string)   */
+#define GPT2_ECORRUPT (-6) /* a debug guard word was overwritten            */
 
 /* ---- precision --------------------------------------------------------- */
 #define GPT2_FP32 0       /* everything fp32, fp32 matrix cores            */
@@ -60,7 +61,8 @@ typedef struct gpt2_model gpt2_model; /* opaque */
 
 /* Model shape plus the largest batch the arenas are sized for.  Limits:
  * channels % num_heads == 0 with head size 16, 32 or 64; channels <= 1024;
- * seq_len <= max_seq_len; batch_size*seq_len <= 32768; vocab_size <= 65536.
+ * num_layers <= 1024; seq_len <= max_seq_len <= 65536; batch_size*seq_len <=
+ * 32768; vocab_size <= 65536.
  *
  * rope = 1 replaces the learned position table by a rotary position
  * embedding, the architectural extension the pages name (yinghuohong.cn,
@@ -177,9 +179,22 @@ GPT2_API int gpt2_forward_device(gpt2_model* model, const int32_t* tokens,
                         const int32_t* targets, int B, int T,
                         float* mean_loss);
 
+/* Forward-only evaluation: the mean cross-entropy of B <= batch_size
+ * sequences of T <= seq_len host ids against host targets (both (B,T)
+ * int32, range-checked on the host: GPT2_ERANGE) into *mean_loss (waits for
+ * the stream).  Unlike a training forward it writes no gradient over the
+ * logits (the loss kernel only reads them) and keeps no backward state:
+ * gpt2_backward afterwards returns GPT2_ESTATE, and the logits stay valid
+ * for gpt2_sample.  The pages' loop prints such a "val loss" between
+ * training steps (ujoy.net article "徒手用 1000 行 C 语言实现", section
+ * "训练过程").  All arguments are required (GPT2_EINVAL if NULL). */
+GPT2_API int gpt2_evaluate(gpt2_model* model, const int32_t* tokens, const int32_t* targets,
+                           int B, int T, float* mean_loss);
+
 /* One token drawn from the model's next-token distribution at position
- * (b, t) of the last forward, which must have been run without targets (a
- * forward with targets replaces the logits by their gradient): the softmax of
+ * (b, t) of the last forward, which must have been run without targets or
+ * by gpt2_evaluate (a training forward replaces the logits by their
+ * gradient): the softmax of
  * that logits row, sampled by the inverse CDF -- the smallest token v with
  * coin < sum_{u <= v} p_u (V - 1 if rounding leaves none).  coin is a
  * uniform draw in [0, 1) supplied by the caller, so callers own the random
@@ -253,7 +268,8 @@ GPT2_API int gpt2_get_loss_scale(gpt2_model* model, float* scale, int* last_upda
 typedef struct gpt2_loader gpt2_loader;
 
 /* Opens path for batches of B x T.  Errors: GPT2_EINVAL (NULL, B or T <= 0,
- * unreadable file, size not a multiple of 4, fewer than B*T + 1 ids),
+ * B*T > 2^30, unreadable or not a regular file, size not a multiple of 4,
+ * fewer than B*T + 1 ids),
  * GPT2_ENOMEM.  The loader owns the open file until gpt2_loader_close. */
 GPT2_API int gpt2_loader_open(const char* path, int B, int T, gpt2_loader** out);
 /* Ids in the file, and floor(ids / (B*T)) batches per pass (-1 if NULL). */
@@ -264,6 +280,17 @@ GPT2_API int gpt2_loader_next(gpt2_loader* loader, int32_t* tokens, int32_t* tar
 /* Back to the first batch. */
 GPT2_API int gpt2_loader_reset(gpt2_loader* loader);
 GPT2_API void gpt2_loader_close(gpt2_loader* loader);
+
+/* Debug guard words.  With the environment variable GPT2_GUARD_WORDS set
+ * (and not "0") when gpt2_create runs, every sub-buffer of the arena is
+ * followed by 256 bytes of the word 0xC0DEFACE (the arena grows by 256 bytes
+ * per sub-buffer).  The pages stress that in one flat allocation every
+ * tensor offset has to line up by hand (yinghuohong.cn, section
+ * "脚动完成每一个层前向/反向流传"); the guards catch a kernel that writes
+ * past its buffer.  gpt2_check_guards waits for the stream and reads every
+ * guard: GPT2_OK, GPT2_ECORRUPT naming the first buffer whose guard changed,
+ * or GPT2_EINVAL if the model has no guards. */
+GPT2_API int gpt2_check_guards(gpt2_model* model);
 
 /* Waits for the model's stream; reports a pending device-side id error. */
 GPT2_API int gpt2_synchronize(gpt2_model* model);

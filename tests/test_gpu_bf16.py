@@ -9,8 +9,6 @@ activations max-abs-normalised within 5e-2, gradients within 5e-2 (several
 roundings compound through twelve layers; about 1.5e-2 is observed); these
 are sanity bounds, the loss is the pinned quantity.
 """
-import time
-
 import numpy as np
 import pytest
 
@@ -53,7 +51,8 @@ def pair(name):
     return m, o, c
 
 
-@pytest.mark.parametrize("name", ["tiny", "ragged", "gpt2_124m_b4t64", "ragged_rope"])
+@pytest.mark.parametrize("name", ["tiny", "ragged", "ragged80", "gpt2_124m_b4t64",
+                                  "ragged_rope"])
 def test_bf16_step(name):
     m, o, c = pair(name)
     tok, tgt = synth.token_stream(c["B"], c["T"], c["V"])
@@ -123,36 +122,3 @@ def test_bf16_deterministic():
     assert outs[0][0] == outs[1][0]
     assert np.array_equal(outs[0][1], outs[1][1])
     assert np.array_equal(outs[0][2], outs[1][2])
-
-
-def test_bf16_full_size_loss():
-    """GPT-2 124M, B=16, T=1024, mixed precision: the mean loss of one
-    sampled sequence against the fp32 oracle on that sequence alone, and the
-    batch loss against the oracle's sequence losses' scale."""
-    g = gpt2()
-    c = synth.CONFIGS["gpt2_124m_b16t1024"]
-    B, T, V = c["B"], c["T"], c["V"]
-    params = synth.init_params(c["L"], c["C"], V, c["maxT"])
-    tok, tgt = synth.token_stream(B, T, V)
-    m = g.Model(c["L"], c["C"], c["NH"], V, c["maxT"], B, T, precision=g.GPT2_BF16_MIXED)
-    m.set_params(params)
-    dtok = torch.tensor(tok, dtype=torch.int32, device="cuda")
-    dtgt = torch.tensor(tgt, dtype=torch.int32, device="cuda")
-    loss = m.forward_device(dtok, dtgt)
-    losses = m.activation("losses").reshape(B, T)
-    b = 11
-    t0 = time.time()
-    o = OracleModel(c["L"], c["C"], c["NH"], V, c["maxT"], 1, T)
-    o.params[:] = params
-    lo = o.forward(tok[b:b + 1], tgt[b:b + 1])
-    print(f"[bf16] oracle forward of one sequence: {time.time() - t0:.1f} s; "
-          f"gpu {losses[b].mean():.6f} oracle {lo:.6f}", flush=True)
-    assert abs(losses[b].mean() - lo) / lo < 2e-2
-    assert abs(loss - losses.mean()) / loss < 1e-5
-    o.close()
-    m.zero_grad()
-    m.backward()
-    m.update(lr=1e-4, step=1)
-    loss2 = m.forward_device(dtok, dtgt)
-    assert loss2 < loss, (loss, loss2)
-    m.close()

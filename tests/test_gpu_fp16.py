@@ -49,7 +49,8 @@ def pair(name):
     return m, o, c, params
 
 
-@pytest.mark.parametrize("name", ["tiny", "ragged", "gpt2_124m_b4t64", "ragged_rope"])
+@pytest.mark.parametrize("name", ["tiny", "ragged", "ragged80", "gpt2_124m_b4t64",
+                                  "ragged_rope"])
 def test_fp16_step(name):
     m, o, c, _ = pair(name)
     tok, tgt = synth.token_stream(c["B"], c["T"], c["V"])

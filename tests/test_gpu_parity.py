@@ -4,13 +4,9 @@ same seeded inputs.
 Tolerances (max |a - r| / max |r| per tensor unless noted):
   loss rel 1e-5; logits, their gradient and every parameter gradient 1e-3;
   parameters after the AdamW step 1e-4; forward activations 1e-4.
-The AdamW step is sign-like on step 1 (dp = -lr g/(|g| + eps)); an element
-whose gradient is at rounding-noise level gets an undetermined update from
-two correct fp32 implementations.  Such elements (|g_gpu - g_ref| >
-1e-3 |g_ref|, or |g_ref| so close to eps that a 1e-3 gradient error moves the
-update past the parameter tolerance) are counted and excluded from the
-parameter check (at most 0.5% of the arena), and the update itself is
-checked exactly by applying the oracle's AdamW to the GPU's own gradients.
+Step-1 AdamW updates that a tolerated gradient error leaves undetermined are
+excluded and counted by tests/parity.py; the update itself is checked exactly
+by applying the oracle's AdamW to the GPU's own gradients.
 """
 import math
 import time
@@ -24,6 +20,8 @@ import oracle
 from oracle import OracleModel, ptr
 from transformer_lm_step_train_amd import synth
 
+from parity import check_params_after_step1, rel, split
+
 pytestmark = [
     pytest.mark.gpu,
     pytest.mark.skipif(not torch.cuda.is_available(), reason="needs a GPU"),
@@ -33,22 +31,6 @@ pytestmark = [
 def gpt2():
     from transformer_lm_step_train_amd import gpt2 as g
     return g
-
-
-def rel(a, r):
-    a = np.asarray(a, dtype=np.float64)
-    r = np.asarray(r, dtype=np.float64)
-    if r.size == 0:  # the rotary model's empty wpe
-        return 0.0
-    return float(np.max(np.abs(a - r)) / max(np.max(np.abs(r)), 1e-30))
-
-
-def split(flat, sizes):
-    out, off = {}, 0
-    for n in oracle.PARAM_NAMES:
-        out[n] = flat[off:off + sizes[n]]
-        off += sizes[n]
-    return out
 
 
 class Pair:
@@ -149,37 +131,15 @@ def check_step(P, tok, tgt, lr=1e-4, wd=0.0):
         assert rel(a, b) < 1e-6, n
     mg, vg = P.gpu.opt_state()
     assert rel(mg, m0) < 1e-6 and rel(vg, v0) < 1e-6
-    # the whole step against the oracle's own step.  Step-1 Adam moves an
-    # element by ~lr whatever the size of its gradient, so an element whose
-    # own gradient is not determined to 1e-3 (rounding noise: e.g. the key
-    # bias, whose exact gradient is 0 because softmax ignores a constant
-    # shift of a row) has no determined update; such elements are counted
-    # and excluded, and must stay a small fraction of the arena.
-    excluded = 0
-    PG, PO = split(pg, P.sizes), split(P.orc.params.copy(), P.sizes)
-    for n in oracle.PARAM_NAMES:
-        if PO[n].size == 0:  # the rotary model's empty wpe
-            continue
-        scale = max(np.max(np.abs(PO[n])), 1e-30)
-        bad = np.abs(PG[n].astype(np.float64) - PO[n]) > 1e-4 * scale
-        r = np.abs(R[n].astype(np.float64))
-        # d(update)/d(g) of step-1 Adam is lr*eps/(|g|+eps)^2: a gradient error
-        # at the 1e-3 tolerance moves the update by more than the parameter
-        # tolerance when the gradient sits within a few eps of zero
-        sensitive = lr * 1e-8 * 1e-3 * r / (r + 1e-8) ** 2 > 1e-4 * scale
-        ill = (np.abs(G[n].astype(np.float64) - R[n]) > 1e-3 * r) | sensitive
-        excluded += int(np.sum(bad & ill))
-        idx = np.flatnonzero(bad & ~ill)[:5]
-        assert idx.size == 0, (n, [(int(i), float(G[n][i]), float(R[n][i]),
-                                    float(PG[n][i]), float(PO[n][i])) for i in idx])
-    print(f"[parity] params: {excluded} elements with undetermined gradients excluded",
-          flush=True)
-    assert excluded <= 0.005 * pg.size
+    # the whole step against the oracle's own step, with the elements whose
+    # step-1 update is undetermined counted and excluded (tests/parity.py)
+    check_params_after_step1(split(pg, P.sizes), split(P.orc.params.copy(), P.sizes), G, R,
+                             lr=lr, rope=bool(c.get("rope", False)))
     return loss_g
 
 
-@pytest.mark.parametrize("name", ["tiny", "ragged", "gpt2_124m_b4t64", "tiny_rope",
-                                  "ragged_rope"])
+@pytest.mark.parametrize("name", ["tiny", "ragged", "small", "ragged80", "gpt2_124m_b4t64",
+                                  "tiny_rope", "ragged_rope"])
 def test_one_training_step(name):
     P = Pair(name)
     tok, tgt = synth.token_stream(P.B, P.T, P.c["V"])
@@ -200,6 +160,46 @@ def test_smaller_batch_than_allocated(name):
     tok, tgt = synth.token_stream(P.B, P.T, P.c["V"])
     check_step(P, tok, tgt)
     P.close()
+
+
+@pytest.mark.parametrize("B", [256, 512])
+def test_large_batch_sort_variants(B):
+    """B*T = 16384 and 32768 positions on the tiny model: the embedding
+    backward's key sort runs with 16 and 32 keys per thread (the latter fills
+    the 160 KiB of LDS), and the weight gradients take their largest K
+    splits.  Every token id repeats about B/8 times."""
+    P = Pair("tiny", B=B, T=64)
+    tok, tgt = synth.token_stream(P.B, P.T, P.c["V"])
+    check_step(P, tok, tgt)
+    P.close()
+
+
+def test_sort_variant_below_allocation():
+    """A model allocated for B*T = 32768 run at B*T = 6400 and 150: each run
+    picks a smaller sort variant than the allocation's (8 keys and 1 key per
+    thread), whose LDS limit must have been raised at create."""
+    c = synth.CONFIGS["tiny"]
+    params = synth.init_params(c["L"], c["C"], c["V"], c["maxT"])
+    g = gpt2()
+    m = g.Model(c["L"], c["C"], c["NH"], c["V"], c["maxT"], 512, 64)
+    for B, T in ((100, 64), (3, 50)):
+        print(f"[parity] tiny allocated 512x64, run B={B} T={T}", flush=True)
+        m.set_params(params)
+        o = OracleModel(c["L"], c["C"], c["NH"], c["V"], c["maxT"], B, T)
+        o.params[:] = params
+        tok, tgt = synth.token_stream(B, T, c["V"])
+        lg = m.forward(tok, tgt)
+        lo = o.forward(tok, tgt)
+        assert abs(lg - lo) / lo < 1e-5, (lg, lo)
+        m.zero_grad()
+        m.backward()
+        o.zero_grad()
+        o.backward()
+        G, R = split(m.grads(), o.param_sizes), split(o.grads.copy(), o.param_sizes)
+        for n in oracle.PARAM_NAMES:
+            assert rel(G[n], R[n]) < 1e-3, (B, T, n, rel(G[n], R[n]))
+        o.close()
+    m.close()
 
 
 @pytest.mark.parametrize("kind", ["all_same", "zipf"])
@@ -230,6 +230,75 @@ def test_small_ten_steps_overfit():
     for a, b in zip(lg, lo):
         assert abs(a - b) / b < 1e-4, (lg, lo)
     P.close()
+
+
+@pytest.mark.parametrize("prec", ["fp32", "bf16", "fp16"])
+def test_evaluate_loss_only(prec):
+    """gpt2_evaluate: the same loss as a training forward (same kernels up to
+    the loss), the logits left as an inference forward leaves them, no
+    backward state, and sampling from its logits."""
+    g = gpt2()
+    c = synth.CONFIGS["ragged"]
+    p = {"fp32": g.GPT2_FP32, "bf16": g.GPT2_BF16_MIXED, "fp16": g.GPT2_F16_MIXED}[prec]
+    params = synth.init_params(c["L"], c["C"], c["V"], c["maxT"])
+    m = g.Model(c["L"], c["C"], c["NH"], c["V"], c["maxT"], c["B"], c["T"], precision=p)
+    m.set_params(params)
+    tok, tgt = synth.token_stream(c["B"], c["T"], c["V"])
+    le = m.evaluate(tok, tgt)
+    z_eval = m.activation("logits")
+    d_eval = m.sample(1, 40, 0.625)
+    with pytest.raises(g.GPT2Error) as e:
+        m.backward()
+    assert e.value.code == g.GPT2_ESTATE
+    m.forward(tok)
+    assert np.array_equal(m.activation("logits"), z_eval)
+    assert m.sample(1, 40, 0.625) == d_eval
+    lt = m.forward(tok, tgt)
+    assert le == lt, (le, lt)
+    if prec == "fp32":
+        o = OracleModel(c["L"], c["C"], c["NH"], c["V"], c["maxT"], c["B"], c["T"])
+        o.params[:] = params
+        lo = o.forward(tok, tgt)
+        assert abs(le - lo) / lo < 1e-5
+        o.close()
+    m.zero_grad()
+    m.backward()  # the training forward's state is intact
+    m.close()
+
+
+@pytest.mark.parametrize("name,prec,B", [("tiny", "fp32", 2), ("ragged", "bf16", 3),
+                                         ("ragged80", "fp16", 3), ("ragged_rope", "fp32", 3),
+                                         ("small", "fp32", 4), ("tiny", "bf16", 512)])
+def test_guard_words_intact(name, prec, B, monkeypatch):
+    """With GPT2_GUARD_WORDS every arena sub-buffer is followed by a guard
+    region: two training steps, an evaluation, a smaller batch and a sample
+    leave every guard intact, and the results equal an unguarded model's bit
+    for bit."""
+    g = gpt2()
+    c = synth.CONFIGS[name]
+    p = {"fp32": g.GPT2_FP32, "bf16": g.GPT2_BF16_MIXED, "fp16": g.GPT2_F16_MIXED}[prec]
+    rope = c.get("rope", False)
+    params = synth.init_params(c["L"], c["C"], c["V"], c["maxT"], rope=rope)
+    tok, tgt = synth.token_stream(B, c["T"], c["V"])
+    out = []
+    for guards in ("1", "0"):
+        monkeypatch.setenv("GPT2_GUARD_WORDS", guards)
+        m = g.Model(c["L"], c["C"], c["NH"], c["V"], c["maxT"], B, c["T"], precision=p,
+                    rope=rope)
+        m.set_params(params)
+        losses = [m.step(tok, tgt, s, **synth.ADAMW) for s in (1, 2)]
+        losses.append(m.evaluate(tok[:1, :c["T"] // 2], tgt[:1, :c["T"] // 2]))
+        losses.append(m.sample(0, 3, 0.5))
+        if guards == "1":
+            m.check_guards()
+        else:
+            with pytest.raises(g.GPT2Error) as e:
+                m.check_guards()
+            assert e.value.code == g.GPT2_EINVAL
+        out.append((losses, m.params()))
+        m.close()
+    assert out[0][0] == out[1][0]
+    assert np.array_equal(out[0][1], out[1][1])
 
 
 def test_deterministic():
@@ -287,51 +356,6 @@ def test_error_paths():
     with pytest.raises(g.GPT2Error) as e:
         m.update(step=0)
     assert e.value.code == g.GPT2_EINVAL
-    m.close()
-
-
-def test_full_size_sampled_rows():
-    """GPT-2 124M at B=16, T=1024 in the benchmark's launch configuration
-    (device-resident ids): per-position losses and logit gradients of one
-    sampled sequence against the oracle run on that sequence alone (rows of
-    the batch are independent in the forward), bitwise repeatability, and
-    descent of the loss after one step."""
-    g = gpt2()
-    c = synth.CONFIGS["gpt2_124m_b16t1024"]
-    B, T, V = c["B"], c["T"], c["V"]
-    params = synth.init_params(c["L"], c["C"], V, c["maxT"])
-    tok, tgt = synth.token_stream(B, T, V)
-    m = g.Model(c["L"], c["C"], c["NH"], V, c["maxT"], B, T)
-    m.set_params(params)
-    dtok = torch.tensor(tok, dtype=torch.int32, device="cuda")
-    dtgt = torch.tensor(tgt, dtype=torch.int32, device="cuda")
-    loss = m.forward_device(dtok, dtgt)
-    assert m.forward_device(dtok, dtgt) == loss
-    losses = m.activation("losses").reshape(B, T)
-    b = 5
-    rows = [3, 517, 1023]
-    dl = m.activation("logits").reshape(B, T, V)[b, rows].copy()
-    t0 = time.time()
-    o = OracleModel(c["L"], c["C"], c["NH"], V, c["maxT"], 1, T)
-    o.params[:] = params
-    lo = o.forward(tok[b:b + 1], tgt[b:b + 1])
-    print(f"[parity] oracle forward of one sequence: {time.time() - t0:.1f} s", flush=True)
-    assert abs(losses[b].mean() - lo) / lo < 1e-5
-    assert rel(losses[b], o.act("losses")) < 1e-5
-    probs = o.act("probs").reshape(T, V)[rows].astype(np.float64)
-    want = probs.copy()
-    want[np.arange(len(rows)), tgt[b, rows]] -= 1.0
-    want /= B * T
-    assert rel(dl, want) < 1e-3
-    o.close()
-    assert abs(loss - losses.mean()) / loss < 1e-5
-    m.zero_grad()
-    m.backward()
-    gr = m.grads()
-    assert np.all(np.isfinite(gr))
-    m.update(lr=1e-4, step=1)
-    loss2 = m.forward_device(dtok, dtgt)
-    assert loss2 < loss, (loss, loss2)
     m.close()
 
 

@@ -64,7 +64,11 @@ __global__ __launch_bounds__(1024) void encoder_sort_kernel(uint32_t* __restrict
     extern __shared__ uint32_t sm[];
     uint32_t* sk = sm;                                      // NK keys
     uint16_t* cnt = reinterpret_cast<uint16_t*>(sm + NK);   // [16][NT] counts
-    uint32_t* wsum = sm + NK + 16 * NT / 2;                 // 16 wave totals
+    // The 16 wave totals of the scan borrow the first slots of the key area:
+    // between a pass's last read of sk (the barrier that ends the previous
+    // pass) and its scatter (after the scan's last barrier) nothing else
+    // touches it.  This keeps the 32-key variant at exactly 160 KiB.
+    uint32_t* wsum = sm;
     const int t = threadIdx.x, lane = t & 63, wave = t >> 6;
     uint32_t k[EPT];
 #pragma unroll
@@ -212,7 +216,7 @@ __global__ __launch_bounds__(256) void encoder_bwd_wpe_kernel(float* __restrict_
 // Column sums of dy (M rows, N % 4 == 0 columns, leading dim ld): each
 // workgroup sums a chunk of rows for 256 columns (four waves, rows strided by
 // four), then a second kernel adds the chunk partials in chunk order.
-constexpr int BIAS_ROWS = 64;
+constexpr int BIAS_ROWS = kBiasRows;
 
 template <class E>
 __global__ __launch_bounds__(256) void bias_partial_kernel(float* __restrict__ part,
@@ -489,7 +493,10 @@ hipError_t encoder_forward(hipStream_t s, void* out, const int32_t* tok, const f
 
 // keys per thread of the sort for n_pow2 slots (1024 threads)
 inline int sort_ept(int n_pow2) { return n_pow2 <= 1024 ? 1 : n_pow2 / 1024; }
-inline size_t sort_lds(int ept) { return (size_t)ept * 1024 * 4 + 16 * 1024 * 2 + 64; }
+// keys, then the [16][1024] 16-bit count table: 163,840 bytes (gfx950's LDS
+// per workgroup) at 32 keys per thread
+inline size_t sort_lds(int ept) { return (size_t)ept * 1024 * 4 + 16 * 1024 * 2; }
+static_assert(32 * 1024 * 4 + 16 * 1024 * 2 <= 163840, "sort fits the LDS");
 
 template <int EPT>
 hipError_t sort_attr() {
@@ -497,16 +504,18 @@ hipError_t sort_attr() {
                                hipFuncAttributeMaxDynamicSharedMemorySize, (int)sort_lds(EPT));
 }
 
+// A forward may run fewer positions than the arenas hold, which picks a
+// smaller variant, so every variant up to the largest gets its LDS limit.
 hipError_t encoder_sort_prepare(int n_pow2) {
-    switch (sort_ept(n_pow2)) {
-        case 1: return sort_attr<1>();
-        case 2: return sort_attr<2>();
-        case 4: return sort_attr<4>();
-        case 8: return sort_attr<8>();
-        case 16: return sort_attr<16>();
-        case 32: return sort_attr<32>();
-        default: return hipErrorInvalidValue;
-    }
+    const int top = sort_ept(n_pow2);
+    if (top > 32) return hipErrorInvalidValue;
+    hipError_t e = sort_attr<1>();
+    if (e == hipSuccess && top >= 2) e = sort_attr<2>();
+    if (e == hipSuccess && top >= 4) e = sort_attr<4>();
+    if (e == hipSuccess && top >= 8) e = sort_attr<8>();
+    if (e == hipSuccess && top >= 16) e = sort_attr<16>();
+    if (e == hipSuccess && top >= 32) e = sort_attr<32>();
+    return e;
 }
 
 hipError_t encoder_sort(hipStream_t s, uint32_t* keys, const int32_t* tok, int n, int V,
@@ -578,10 +587,6 @@ hipError_t rope_apply(hipStream_t s, void* qkv, const float* cs, int B, int T, i
                            B * T, T, C, hs, (int64_t)3 * C, (float)dir);
         return hipGetLastError();
     });
-}
-
-size_t bias_partials_floats(int M, int N) {
-    return (size_t)((M + BIAS_ROWS - 1) / BIAS_ROWS) * N;
 }
 
 hipError_t bias_grad(hipStream_t s, float* db, float* part, const void* dy, int M, int N,

@@ -40,8 +40,7 @@
 namespace gk {
 namespace {
 
-constexpr int BM = 128, BN = 128, NTHR = 256;
-constexpr int BK_SPLIT = 32;     // split-K chunks are multiples of every step depth
+constexpr int BM = kGemmTile, BN = kGemmTile, NTHR = 256;
 constexpr int PF = 2;            // register prefetch depth (tiles in flight)
 constexpr int EPI_PARTIAL = 100; // internal: write split-K partial sums
 
@@ -409,68 +408,24 @@ __global__ __launch_bounds__(256) void splitk_reduce_kernel(const GemmArgs a,
     epi_store<EPI>(a, nullptr, (int)row, col, s);
 }
 
-inline int cdiv(int64_t a, int64_t b) { return (int)((a + b - 1) / b); }
+}  // namespace
 
-// The unit of the split plan: two workgroups per compute unit.  The 16-step
-// kernel can hold three, but plans sized for three split the weight
-// gradients further and measured slower.
-int resident_slots() {
-    static int slots = 0;
-    if (!slots) {
-        int dev = 0, cus = 0;
-        if (hipGetDevice(&dev) != hipSuccess ||
-            hipDeviceGetAttribute(&cus, hipDeviceAttributeMultiprocessorCount, dev) != hipSuccess ||
-            cus <= 0)
+// Compute units of the current device (read once; 256 if unknown).
+int device_cu_count() {
+    static int cus = 0;
+    if (!cus) {
+        int dev = 0, n = 0;
+        if (hipGetDevice(&dev) == hipSuccess &&
+            hipDeviceGetAttribute(&n, hipDeviceAttributeMultiprocessorCount, dev) == hipSuccess &&
+            n > 0)
+            cus = n;
+        else
             cus = 256;
-        slots = 2 * cus;
     }
-    return slots;
+    return cus;
 }
 
-int split_chunk(int K, int splits) {
-    int c = cdiv(K, splits);
-    return cdiv(c, BK_SPLIT) * BK_SPLIT;
-}
-
-// Split the reduction over K when the output tiles alone leave the chip
-// idle: weight gradients of the C x C and 4C x C layers (K = B*T, few tiles,
-// split so that the workgroups fill about two whole rounds), and long-K
-// forward / input-gradient products whose tile count falls between one and
-// two rounds of resident workgroups (two splits make whole rounds).
-int choose_splits(int op, int epi, int M, int N, int K) {
-    if ((N % 4) != 0) return 1;
-    const int tiles = cdiv(M, BM) * cdiv(N, BN);
-    if (op == GEMM_TN) {
-        if (epi != EPI_ACCUM && epi != EPI_STORE) return 1;
-        const int slots = resident_slots();
-        // Many tiles and a long reduction (the LM-head weight gradient,
-        // K = B*T): four splits of at least 4096 each measured 11% faster
-        // than none (shorter reductions per tile, a fuller last round).
-        if (tiles >= 2 * slots) return K >= 4 * 4096 ? 4 : 1;
-        // Smallest split count that fills about two rounds of resident
-        // workgroups with little idle tail; at least 4 reduction steps each.
-        const int max_splits = K / (BK_SPLIT * 4);
-        int best = 1;
-        double best_eff = 0.0;
-        for (int sp = 2; sp <= max_splits; sp++) {
-            const int nz = cdiv(K, split_chunk(K, sp));
-            const double x = (double)tiles * nz / slots;
-            if (x > 4.0) break;
-            const double eff = x / std::ceil(x);
-            if (x >= 1.8 && eff >= 0.9) return sp;
-            if (eff > best_eff + 0.02) { best_eff = eff; best = sp; }
-        }
-        return best;
-    }
-    // Forward products: never (the fc-proj forward, K = 3072, measured 3%
-    // faster unsplit).  Input gradients with a very long K whose tiles fill
-    // between one and two rounds (the LM-head dX, K = V): two splits.
-    if (op == GEMM_NT || (epi != EPI_STORE && epi != EPI_RESID)) return 1;
-    const int slots = resident_slots();
-    const bool whole_rounds = tiles > slots && tiles < 2 * slots && (2 * tiles) % slots == 0;
-    return whole_rounds && K >= 8192 ? 2 : 1;
-}
-
+namespace {
 
 // Reduction steps of 16 let three workgroups share a compute unit (40 KB of
 // LDS each) and measured 2-5% faster on every product of the step but one:
@@ -479,7 +434,7 @@ int choose_splits(int op, int epi, int M, int N, int K) {
 template <int OP, int EPI>
 hipError_t launch(hipStream_t s, const GemmArgs& a, int splits, float* ws) {
     const int tm = cdiv(a.M, BM), tn = cdiv(a.N, BN);
-    const int chunk = splits > 1 ? split_chunk(a.K, splits) : (a.K > 0 ? a.K : 1);
+    const int chunk = splits > 1 ? gemm_split_chunk(a.K, splits) : (a.K > 0 ? a.K : 1);
     const int nz = splits > 1 ? cdiv(a.K, chunk) : 1;
     dim3 grid(tm * tn, 1, nz);
     if constexpr (OP == GEMM_NN) {
@@ -494,19 +449,11 @@ hipError_t launch(hipStream_t s, const GemmArgs& a, int splits, float* ws) {
 
 }  // namespace
 
-size_t gemm_workspace_bytes(int op, int epi, int M, int N, int K) {
-    const int splits = choose_splits(op, epi, M, N, K);
-    if (splits <= 1) return 0;
-    const int chunk = split_chunk(K, splits);
-    const int nz = cdiv(K, chunk);
-    return (size_t)nz * M * N * sizeof(float);
-}
-
 template <int OP>
 hipError_t launch_split(hipStream_t s, const GemmArgs& a, int splits, float* ws) {
     hipError_t e = launch<OP, EPI_PARTIAL>(s, a, splits, ws);
     if (e != hipSuccess) return e;
-    const int nz = cdiv(a.K, split_chunk(a.K, splits));
+    const int nz = cdiv(a.K, gemm_split_chunk(a.K, splits));
     const int64_t n4 = (int64_t)a.M * (a.N / 4);
     if (n4 >= (int64_t)1 << 31) return hipErrorInvalidValue;
     const int blocks = (int)((n4 + 255) / 256);
@@ -536,8 +483,10 @@ hipError_t gemm(hipStream_t s, const GemmArgs& a, float* ws, size_t ws_bytes) {
     if (a.lda < (a.op == GEMM_TN ? a.M : a.K) || a.ldb < (a.op == GEMM_NT ? a.K : a.N) ||
         a.ldc < a.N)
         return hipErrorInvalidValue;
-    int splits = choose_splits(a.op, a.epi, a.M, a.N, a.K);
-    if (splits > 1 && gemm_workspace_bytes(a.op, a.epi, a.M, a.N, a.K) > ws_bytes) splits = 1;
+    const int cus = device_cu_count();
+    int splits = gemm_choose_splits(a.op, a.epi, a.M, a.N, a.K, cus);
+    if (splits > 1 && gemm_workspace_bytes(a.op, a.epi, a.M, a.N, a.K, cus) > ws_bytes)
+        splits = 1;
     if (a.colsum) {
         if (a.epi != EPI_GELU_BWD) return hipErrorInvalidValue;
         splits = 1;  // the column sums are taken in the matmul's own epilogue

@@ -37,6 +37,7 @@ namespace gk {
 namespace {
 
 constexpr int BM = 128, BN = 128, BK = 64, NTHR = 256;
+static_assert(BK == kGemm16Step, "the split plan counts 64-deep steps");
 constexpr int LDH = BK + 8;       // LDS row stride, bf16 elements (144 bytes)
 constexpr int EPI_PARTIAL = 100;  // internal: fp32 split-K partial sums
 
@@ -974,61 +975,6 @@ __global__ __launch_bounds__(256) void splitk_reduce_bf16_kernel(const GemmArgsH
     epi4<EPI, H>(a, nullptr, (int)row, col, s);
 }
 
-inline int cdiv(int64_t a, int64_t b) { return (int)((a + b - 1) / b); }
-
-int split_chunk_h(int K, int splits) { return cdiv(cdiv(K, splits), BK) * BK; }
-
-int cu_count_h() {
-    static int cus = 0;
-    if (!cus) {
-        int dev = 0, n = 0;
-        if (hipGetDevice(&dev) == hipSuccess &&
-            hipDeviceGetAttribute(&n, hipDeviceAttributeMultiprocessorCount, dev) == hipSuccess &&
-            n > 0)
-            cus = n;
-        else
-            cus = 256;
-    }
-    return cus;
-}
-
-// Which kernel, and how many K splits.  Weight gradients (TN) and input
-// gradients with a very long K (the LM head, K = V) take the 256x256 kernel
-// with the split count that minimises (rounds of one-per-CU workgroups) x
-// (reduction steps per workgroup) plus the cost of the partial sums, each
-// split at least 4 steps; everything else takes the 128x128 kernel unsplit.
-struct PlanH {
-    bool big;
-    int splits;
-};
-
-PlanH plan_h(const GemmArgsH& a) {
-    const bool big = (a.op == GEMM_TN || (a.op == GEMM_NN && a.K >= 16384)) && a.lda % 8 == 0 &&
-                     a.ldb % 8 == 0;
-    if (!big) return {false, 1};
-    const bool can_split = (a.N % 4) == 0 && (a.epi == EPI_ACCUM || a.epi == EPI_STORE);
-    const int tiles = cdiv(a.M, 256) * cdiv(a.N, 256);
-    const int cus = cu_count_h();
-    const int max_splits = can_split ? std::min(32, std::max(1, a.K / (4 * BK))) : 1;
-    PlanH best{true, 1};
-    double best_t = 1e300;
-    for (int sp = 1; sp <= max_splits; sp++) {
-        const int chunk = sp > 1 ? split_chunk_h(a.K, sp) : a.K;
-        const int nz = sp > 1 ? cdiv(a.K, chunk) : 1;
-        if (nz != sp) continue;
-        // Each split also writes an M x N fp32 partial that the sum kernel
-        // reads back: at about 4 TB/s against about 3.4 us per 256x256x64
-        // step, M*N/1.7e6 steps per split.
-        const double t = std::ceil((double)tiles * nz / cus) * std::ceil((double)chunk / BK) +
-                         (sp > 1 ? sp * (double)a.M * a.N / 1.7e6 : 0.0);
-        if (t < best_t) {
-            best_t = t;
-            best.splits = sp;
-        }
-    }
-    return best;
-}
-
 template <int OP, int EPI, class H>
 hipError_t launch_h(hipStream_t s, const GemmArgsH& a, float* ws) {
     const int tm = cdiv(a.M, BM), tn = cdiv(a.N, BN);
@@ -1054,7 +1000,7 @@ hipError_t launch_h(hipStream_t s, const GemmArgsH& a, float* ws) {
 template <int OP, int EPI, class H>
 hipError_t launch_big(hipStream_t s, const GemmArgsH& a, int splits, float* ws) {
     const int tm = cdiv(a.M, 256), tn = cdiv(a.N, 256);
-    const int chunk = splits > 1 ? split_chunk_h(a.K, splits) : (a.K > 0 ? a.K : 1);
+    const int chunk = splits > 1 ? gemm16_split_chunk(a.K, splits) : (a.K > 0 ? a.K : 1);
     const int nz = splits > 1 ? cdiv(a.K, chunk) : 1;
     launch((gemm_bf16_big_kernel<OP, EPI, 4, 4, H>), dim3(tm * tn, 1, nz), dim3(NTHR), 0,
                        s, a, tm, tn, chunk, ws);
@@ -1118,7 +1064,7 @@ hipError_t run(hipStream_t s, const GemmArgsH& a, const PlanH& p, float* ws) {
     if (!p.big) return run_small<H>(s, a, ws);
     hipError_t e = run_big<H>(s, a, p.splits, ws);
     if (e != hipSuccess || p.splits <= 1) return e;
-    const int nz = cdiv(a.K, split_chunk_h(a.K, p.splits));
+    const int nz = cdiv(a.K, gemm16_split_chunk(a.K, p.splits));
     const int64_t n4 = (int64_t)a.M * (a.N / 4);
     if (n4 >= (int64_t)1 << 31) return hipErrorInvalidValue;
     const int blocks = (int)((n4 + 255) / 256);
@@ -1133,19 +1079,6 @@ hipError_t run(hipStream_t s, const GemmArgsH& a, const PlanH& p, float* ws) {
 
 }  // namespace
 
-size_t gemm_bf16_workspace_bytes(int op, int epi, int M, int N, int K) {
-    GemmArgsH a{};
-    a.op = op;
-    a.epi = epi;
-    a.M = M;
-    a.N = N;
-    a.K = K;
-    a.lda = a.ldb = 8;  // the workspace bound assumes the large-tile path is eligible
-    const PlanH p = plan_h(a);
-    if (!p.big || p.splits <= 1) return 0;
-    return (size_t)cdiv(K, split_chunk_h(K, p.splits)) * M * N * sizeof(float);
-}
-
 hipError_t gemm_bf16(hipStream_t s, const GemmArgsH& a, float* ws, size_t ws_bytes) {
     if (a.M <= 0 || a.N <= 0) return hipSuccess;
     // 16-byte runs along k for k-contiguous operands, 8-byte runs of 4 along
@@ -1155,9 +1088,9 @@ hipError_t gemm_bf16(hipStream_t s, const GemmArgsH& a, float* ws, size_t ws_byt
     if (a.lda < (a.op == GEMM_TN ? a.M : a.K) || a.ldb < (a.op == GEMM_NT ? a.K : a.N) ||
         a.ldc < a.N)
         return hipErrorInvalidValue;
-    PlanH p = plan_h(a);
+    PlanH p = gemm16_plan(a.op, a.epi, a.M, a.N, a.K, a.lda, a.ldb, device_cu_count());
     if (p.splits > 1 &&
-        (size_t)cdiv(a.K, split_chunk_h(a.K, p.splits)) * a.M * a.N * sizeof(float) > ws_bytes)
+        (size_t)cdiv(a.K, gemm16_split_chunk(a.K, p.splits)) * a.M * a.N * sizeof(float) > ws_bytes)
         p.splits = 1;
     if (a.colsum) {
         if (a.epi != EPI_GELU_BWD) return hipErrorInvalidValue;

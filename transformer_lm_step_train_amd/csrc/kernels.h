@@ -6,6 +6,8 @@
 #include <stddef.h>
 #include <stdint.h>
 
+#include "plan.h"
+
 namespace gk {
 
 // ---- launch-time events ---------------------------------------------------
@@ -30,20 +32,7 @@ inline void launch(F kernel, dim3 grid, dim3 block, uint32_t shm, hipStream_t s,
 }
 
 // ---- matmul ---------------------------------------------------------------
-// C[m,n] = sum_k A(m,k) B(k,n), all fp32, row-major with leading dims:
-//   NT: A(m,k) = A[m*lda + k], B(k,n) = B[n*ldb + k]   (Y = X W^T, forward)
-//   NN: A(m,k) = A[m*lda + k], B(k,n) = B[k*ldb + n]   (dX = dY W)
-//   TN: A(m,k) = A[k*lda + m], B(k,n) = B[k*ldb + n]   (dW = dY^T X)
-enum GemmOp { GEMM_NT = 0, GEMM_NN = 1, GEMM_TN = 2 };
-
-enum GemmEpi {
-    EPI_STORE = 0,     // C = acc (+ bias[n])
-    EPI_RESID = 1,     // C = acc + bias[n] + aux[m,n]           (residual add)
-    EPI_GELU = 2,      // C = acc + bias[n];  out2 = gelu(C)
-    EPI_GELU_BWD = 3,  // C = acc * gelu'(aux[m,n])
-    EPI_ACCUM = 4,     // C += acc
-};
-
+// Operand layouts (GemmOp) and fused epilogues (GemmEpi) are in plan.h.
 struct GemmArgs {
     int op, epi;
     int M, N, K;
@@ -84,12 +73,11 @@ struct GemmArgsH {
     uint16_t* out2;
     float* colsum;  // as in GemmArgs, of C as stored (rounded to 16 bits)
 };
-size_t gemm_bf16_workspace_bytes(int op, int epi, int M, int N, int K);
 hipError_t gemm_bf16(hipStream_t s, const GemmArgsH& a, float* workspace,
                      size_t workspace_bytes);
 
-// Workspace bytes a call may need for split-K partial sums.
-size_t gemm_workspace_bytes(int op, int epi, int M, int N, int K);
+// The number of compute units the plans are made for (the current device's).
+int device_cu_count();
 hipError_t gemm(hipStream_t s, const GemmArgs& a, float* workspace,
                 size_t workspace_bytes);
 
@@ -130,7 +118,6 @@ hipError_t layernorm_forward(hipStream_t s, void* out, float* mean, float* rstd,
 // NULL dbias += the column sums of dres as stored after this call (two
 // deterministic stages; `partials` holds layernorm_partials_floats(N, C)
 // floats).
-size_t layernorm_partials_floats(int N, int C);
 hipError_t layernorm_backward(hipStream_t s, void* dres, int accumulate, float* dw, float* db,
                               float* dbias, float* partials, const void* dout, const void* inp,
                               const float* w, const float* mean, const float* rstd, int N,
@@ -139,7 +126,7 @@ hipError_t layernorm_backward(hipStream_t s, void* dres, int accumulate, float* 
 // ---- fused softmax + cross-entropy -----------------------------------------
 // logits (N, ldv) with V valid columns.  losses[n] = lse - logit[target];
 // logits are overwritten by (softmax - onehot) * dscale, columns V..ldv-1 by
-// 0.  A target outside [0, V) sets *flag |= 2 and zeroes that row.
+// 0; dscale == 0 leaves the logits untouched (loss only).  A target outside [0, V) sets *flag |= 2 and zeroes that row.
 // logits fp32, bf16 bits or fp16 per dt (the statistics are fp32).
 // gscale (device, NULL = none): the loss scale of the fp16 model, which
 // multiplies dscale.
@@ -172,7 +159,6 @@ hipError_t encoder_backward(hipStream_t s, float* dwte, float* dwpe,
 
 // ---- reductions and elementwise -------------------------------------------
 // db[n] += sum_m dy[m*ld + n]; `partials` holds bias_partials_floats(M, N).
-size_t bias_partials_floats(int M, int N);
 hipError_t bias_grad(hipStream_t s, float* db, float* partials,
                      const void* dy, int M, int N, int64_t ld, int dt);
 // Column c of part (nrows x ncols) is summed over rows in a fixed order and

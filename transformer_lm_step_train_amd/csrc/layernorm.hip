@@ -254,13 +254,6 @@ hipError_t layernorm_forward(hipStream_t s, void* out, float* mean, float* rstd,
     });
 }
 
-// Upper bound of the workgroup count over every row count up to N: at most
-// 1024 (rows per workgroup grow past 4096 rows) and at most ceil(N/4).
-size_t layernorm_partials_floats(int N, int C) {
-    const int nb = std::min(1024, (N + 3) / 4);
-    return (size_t)nb * 3 * C;
-}
-
 hipError_t layernorm_backward(hipStream_t s, void* dres, int accumulate, float* dw, float* db,
                               float* dbias, float* partials, const void* dout, const void* inp,
                               const float* w, const float* mean, const float* rstd, int N,

@@ -27,7 +27,7 @@
 
 #include "gpt2.h"
 
-int gpt2_set_error(int code, const char* msg);  // runtime.cpp
+int gpt2_set_error(int code, const char* msg);  // host.cpp
 
 struct gpt2_loader {
     int fd = -1;
@@ -64,6 +64,10 @@ int gpt2_loader_open(const char* path, int B, int T, gpt2_loader** out) {
     if (fstat(fd, &st) != 0) {
         ::close(fd);
         return lfail(GPT2_EINVAL, "cannot stat %s: %s", path, strerror(errno));
+    }
+    if (!S_ISREG(st.st_mode)) {
+        ::close(fd);
+        return lfail(GPT2_EINVAL, "%s is not a regular file", path);
     }
     if (st.st_size % 4 != 0) {
         ::close(fd);

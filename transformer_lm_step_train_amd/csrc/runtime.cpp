@@ -1,6 +1,6 @@
-// Host runtime behind the C ABI (include/gpt2.h): config checks, the arena
-// layout, one device allocation, and the launch sequence of one training
-// step on one HIP stream.
+// Host runtime behind the C ABI (include/gpt2.h): one device allocation laid
+// out by host.cpp, and the launch sequence of one training step on one HIP
+// stream.
 //
 // The arenas follow the llm.c design of allocating everything once as flat
 // 1-D memory and pointing every tensor into it (yinghuohong.cn article
@@ -17,12 +17,14 @@
 #include <cstdarg>
 #include <cstdio>
 #include <cerrno>
+#include <cstdlib>
 #include <cstring>
 #include <string>
 #include <vector>
 
 #include "../../include/gpt2.h"
 #include "dtype.h"
+#include "host.h"
 #include "kernels.h"
 
 namespace gk {
@@ -32,200 +34,13 @@ LaunchEvents& launch_events() {
 }
 }  // namespace gk
 
-namespace {
-
-thread_local std::string g_err;
-
-int fail(int code, const char* fmt, ...) {
-    char buf[512];
-    va_list ap;
-    va_start(ap, fmt);
-    vsnprintf(buf, sizeof buf, fmt, ap);
-    va_end(ap);
-    g_err = buf;
-    return code;
-}
-
-}  // namespace
-
-// Sets the thread's last-error message (for the host-only parts of the
-// library in other files).
-int gpt2_set_error(int code, const char* msg) {
-    g_err = msg;
-    return code;
-}
+// Compute units the split plans are made for: the current device's.
+int gh::host_cu_count() { return gk::device_cu_count(); }
 
 namespace {
 
-const char* kParamNames[16] = {"wte",      "wpe",      "ln1w", "ln1b", "qkvw",    "qkvb",
-                               "attprojw", "attprojb", "ln2w", "ln2b", "fcw",     "fcb",
-                               "fcprojw",  "fcprojb",  "lnfw", "lnfb"};
-enum { P_WTE, P_WPE, P_LN1W, P_LN1B, P_QKVW, P_QKVB, P_ATTPROJW, P_ATTPROJB,
-       P_LN2W, P_LN2B, P_FCW, P_FCB, P_FCPROJW, P_FCPROJB, P_LNFW, P_LNFB };
-
-void param_sizes(const gpt2_config* c, int64_t* s) {
-    const int64_t L = c->num_layers, C = c->channels, V = c->vocab_size, T = c->max_seq_len;
-    const int64_t P = c->rope ? 0 : T * C;  // the rotary model has no position table
-    const int64_t v[16] = {V * C, P, L * C, L * C, L * 3 * C * C, L * 3 * C, L * C * C,
-                           L * C, L * C, L * C, L * 4 * C * C, L * 4 * C, L * C * 4 * C,
-                           L * C, C, C};
-    for (int i = 0; i < 16; i++) s[i] = v[i];
-}
-
-int ceil_log2(int64_t n) {
-    int b = 0;
-    while ((int64_t(1) << b) < n) b++;
-    return b;
-}
-
-int check_config(const gpt2_config* c) {
-    if (!c) return fail(GPT2_EINVAL, "config is NULL");
-    if (c->num_layers <= 0 || c->channels <= 0 || c->num_heads <= 0 || c->vocab_size <= 0 ||
-        c->max_seq_len <= 0 || c->batch_size <= 0 || c->seq_len <= 0)
-        return fail(GPT2_EINVAL, "every config field must be positive");
-    if (c->channels % c->num_heads)
-        return fail(GPT2_EINVAL, "channels (%d) must be a multiple of num_heads (%d)",
-                    c->channels, c->num_heads);
-    const int hs = c->channels / c->num_heads;
-    if (hs != 16 && hs != 32 && hs != 64)
-        return fail(GPT2_EINVAL, "head size %d not supported (16, 32 or 64)", hs);
-    if (c->channels > 1024) return fail(GPT2_EINVAL, "channels > 1024 not supported");
-    if (c->seq_len > c->max_seq_len)
-        return fail(GPT2_EINVAL, "seq_len %d > max_seq_len %d", c->seq_len, c->max_seq_len);
-    if ((int64_t)c->batch_size * c->seq_len > 32768)
-        return fail(GPT2_EINVAL, "batch_size*seq_len > 32768 not supported");
-    if (c->vocab_size > 65536) return fail(GPT2_EINVAL, "vocab_size > 65536 not supported");
-    if (c->precision != GPT2_FP32 && c->precision != GPT2_BF16_MIXED &&
-        c->precision != GPT2_F16_MIXED)
-        return fail(GPT2_EINVAL, "unknown precision %d", c->precision);
-    if (c->rope != 0 && c->rope != 1) return fail(GPT2_EINVAL, "rope must be 0 or 1");
-    return GPT2_OK;
-}
-
-inline size_t align256(size_t x) { return (x + 255) & ~size_t(255); }
-
-// bf16 is the top half of an fp32.
-float bf16_bits_to_float(uint16_t h) {
-    const uint32_t u = (uint32_t)h << 16;
-    float f;
-    std::memcpy(&f, &u, 4);
-    return f;
-}
-
-// IEEE binary16: sign, 5-bit exponent (bias 15), 10-bit fraction; exponent 0
-// holds zero and the subnormals (fraction * 2^-24), 31 holds inf and NaN.
-float half_bits_to_float(uint16_t h) {
-    const int sign = h >> 15, e = (h >> 10) & 31, f = h & 1023;
-    float v;
-    if (e == 0) v = std::ldexp((float)f, -24);
-    else if (e == 31) v = f ? NAN : INFINITY;
-    else v = std::ldexp((float)(1024 + f), e - 25);
-    return sign ? -v : v;
-}
-
-// Byte offsets of every sub-buffer inside the one device allocation.
-struct Layout {
-    int L, C, NH, V, Vp, maxT, Bmax, Tmax, M, pos_bits, n_pow2;
-    int dt;     // activation storage: DT_F32, DT_BF16 or DT_F16
-    int half;   // 16-bit activations and a 16-bit copy of the matmul weights
-    int rope;   // rotary position embedding instead of the wpe table
-    size_t es;  // bytes per activation element
-    int64_t nparams, poff[16], psize[16];
-    size_t params, grads, m, v, shadow;
-    size_t encoded, ln1, ln1_mean, ln1_rstd, qkv, atty, lse, res2, ln2, ln2_mean, ln2_rstd, fch,
-        fch_gelu, res3, lnf, lnf_mean, lnf_rstd, logits, losses;
-    size_t dres, dtmp, dqkv, dfch, attn_d, ln_part, bias_part, gemm_ws, keys, tokens, targets,
-        scalars, rope_cs;
-    size_t gemm_ws_bytes, total;
-
-    void build(const gpt2_config* c) {
-        dt = c->precision == GPT2_BF16_MIXED ? DT_BF16
-             : c->precision == GPT2_F16_MIXED  ? DT_F16
-                                               : DT_F32;
-        half = dt != DT_F32;
-        rope = c->rope;
-        es = half ? 2 : 4;
-        L = c->num_layers;
-        C = c->channels;
-        NH = c->num_heads;
-        V = c->vocab_size;
-        Vp = (V + 63) / 64 * 64;
-        maxT = c->max_seq_len;
-        Bmax = c->batch_size;
-        Tmax = c->seq_len;
-        M = Bmax * Tmax;
-        pos_bits = std::max(1, ceil_log2(M));
-        n_pow2 = 1 << ceil_log2(M);
-        param_sizes(c, psize);
-        nparams = 0;
-        for (int i = 0; i < 16; i++) {
-            poff[i] = nparams;
-            nparams += psize[i];
-        }
-        size_t off = 0;
-        auto take = [&](size_t bytes) {
-            size_t o = off;
-            off = align256(off + bytes);
-            return o;
-        };
-        const size_t f = sizeof(float);
-        const size_t MC = (size_t)M * C;
-        params = take(nparams * f);
-        grads = take(nparams * f);
-        m = take(nparams * f);
-        v = take(nparams * f);
-        shadow = half ? take(nparams * 2) : 0;
-        encoded = take(MC * es);
-        ln1 = take(L * MC * es);
-        ln1_mean = take((size_t)L * M * f);
-        ln1_rstd = take((size_t)L * M * f);
-        qkv = take(L * 3 * MC * es);
-        atty = take(L * MC * es);
-        lse = take((size_t)L * M * NH * f);
-        res2 = take(L * MC * es);
-        ln2 = take(L * MC * es);
-        ln2_mean = take((size_t)L * M * f);
-        ln2_rstd = take((size_t)L * M * f);
-        fch = take(L * 4 * MC * es);
-        fch_gelu = take(L * 4 * MC * es);
-        res3 = take(L * MC * es);
-        lnf = take(MC * es);
-        lnf_mean = take((size_t)M * f);
-        lnf_rstd = take((size_t)M * f);
-        logits = take((size_t)M * Vp * es);
-        losses = take((size_t)M * f);
-        dres = take(MC * es);
-        dtmp = take(MC * es);
-        dqkv = take(3 * MC * es);
-        dfch = take(4 * MC * es);
-        attn_d = take((size_t)M * NH * f);
-        ln_part = take(gk::layernorm_partials_floats(M, C) * f);
-        bias_part = take(gk::bias_partials_floats(M, 4 * C) * f);
-        // the largest split-K workspace over every matmul of the step
-        gemm_ws_bytes = 0;
-        auto need = [&](int op, int epi, int m, int n, int k) {
-            const size_t b = half ? gk::gemm_bf16_workspace_bytes(op, epi, m, n, k)
-                                  : gk::gemm_workspace_bytes(op, epi, m, n, k);
-            gemm_ws_bytes = std::max(gemm_ws_bytes, b);
-        };
-        const int outs[4][2] = {{3 * C, C}, {C, C}, {4 * C, C}, {C, 4 * C}};
-        for (auto& o : outs) need(gk::GEMM_TN, gk::EPI_ACCUM, o[0], o[1], M);
-        need(gk::GEMM_TN, gk::EPI_ACCUM, V, C, M);
-        for (int k : {C, 3 * C, 4 * C}) {
-            need(gk::GEMM_NT, gk::EPI_RESID, M, C, k);
-            need(gk::GEMM_NN, gk::EPI_STORE, M, C, k);
-        }
-        need(gk::GEMM_NT, gk::EPI_STORE, M, 3 * C, C);
-        need(gk::GEMM_NN, gk::EPI_STORE, M, C, V);
-        gemm_ws = take(gemm_ws_bytes);
-        keys = take((size_t)n_pow2 * sizeof(uint32_t));
-        tokens = take((size_t)M * sizeof(int32_t));
-        targets = take((size_t)M * sizeof(int32_t));
-        scalars = take(256);
-        rope_cs = rope ? take((size_t)Tmax * (C / NH / 2) * 2 * f) : 0;
-        total = off;
-    }
-};
+// config checks, the arena layout, parameter indices P_*, error messages
+using namespace gh;
 
 constexpr int kEventPool = 4096;
 
@@ -256,7 +71,7 @@ struct gpt2_model {
     hipEvent_t stage_done = nullptr;
     bool stage_pending = false;
     int B = 0, T = 0;
-    bool have_fwd = false, have_targets = false;
+    bool have_fwd = false, have_targets = false, have_loss = false;
     bool logits_valid = false;  // last forward had no targets: logits intact
     Prof prof;
 
@@ -447,7 +262,14 @@ int run_gemm(gpt2_model* md, const Mm& x) {
 
 // ---- forward ---------------------------------------------------------------
 
-int forward_impl(gpt2_model* md, const int32_t* tok, const int32_t* tgt, int B, int T) {
+// What a forward computes after the logits: nothing (inference: the logits
+// stay for sampling), the loss with the logits' gradient written over them
+// and the embedding keys sorted for the backward (training), or the loss
+// alone (evaluation: the logits stay, no backward state).
+enum FwdMode { FWD_INFER = 0, FWD_TRAIN = 1, FWD_EVAL = 2 };
+
+int forward_impl(gpt2_model* md, const int32_t* tok, const int32_t* tgt, int B, int T,
+                 int mode) {
     const Layout& y = md->lay;
     const int L = y.L, C = y.C, NH = y.NH, V = y.V, M = B * T;
     const int h = y.dt;
@@ -521,12 +343,15 @@ int forward_impl(gpt2_model* md, const int32_t* tok, const int32_t* tgt, int B, 
     void* logits = md->A(y.logits);
     TRY(run_gemm(md, mm(gk::GEMM_NT, gk::EPI_STORE, M, V, C, lnf, C, md->W(P_WTE), C, logits,
                         y.Vp)));
+    const bool train = mode == FWD_TRAIN;
     if (tgt) {
         float* losses = md->at<float>(y.losses);
-        LAUNCH(md, GPT2_KC_SOFTMAX_CE, 0, es * 2.0 * M * (double)V + 8.0 * M,
-               gk::softmax_ce(s, logits, losses, tgt, M, V, y.Vp, 1.0f / M,
-                              y.dt == DT_F16 ? md->lscale() : nullptr, md->flag(), h));
+        LAUNCH(md, GPT2_KC_SOFTMAX_CE, 0, es * (train ? 2.0 : 1.0) * M * (double)V + 8.0 * M,
+               gk::softmax_ce(s, logits, losses, tgt, M, V, y.Vp, train ? 1.0f / M : 0.0f,
+                              train && y.dt == DT_F16 ? md->lscale() : nullptr, md->flag(), h));
         LAUNCH(md, GPT2_KC_OTHER, 0, 4.0 * M, gk::mean_reduce(s, md->dloss(), losses, M));
+    }
+    if (train) {
         const int np2 = 1 << ceil_log2(M);
         LAUNCH(md, GPT2_KC_OTHER, 0, 4.0 * M + 4.0 * np2,
                gk::encoder_sort(s, md->at<uint32_t>(y.keys), tok, M, V, y.pos_bits, np2));
@@ -534,8 +359,9 @@ int forward_impl(gpt2_model* md, const int32_t* tok, const int32_t* tgt, int B, 
     md->B = B;
     md->T = T;
     md->have_fwd = true;
-    md->have_targets = tgt != nullptr;
-    md->logits_valid = tgt == nullptr;
+    md->have_loss = tgt != nullptr;
+    md->have_targets = train;
+    md->logits_valid = !train;
     return GPT2_OK;
 }
 
@@ -546,7 +372,7 @@ int read_loss(gpt2_model* md, float* mean_loss) {
     TRY(hip_check(hipStreamSynchronize(md->stream), "stream synchronize"));
     int flag;
     std::memcpy(&flag, md->h_scal + 1, 4);
-    if (mean_loss) *mean_loss = md->have_targets ? md->h_scal[0] : NAN;
+    if (mean_loss) *mean_loss = md->have_loss ? md->h_scal[0] : NAN;
     if (flag & 1) return fail(GPT2_ERANGE, "a token id is outside [0, vocab_size)");
     if (flag & 2) return fail(GPT2_ERANGE, "a target id is outside [0, vocab_size)");
     return GPT2_OK;
@@ -673,6 +499,24 @@ int backward_impl(gpt2_model* md) {
 
 bool valid_model(gpt2_model* md) { return md != nullptr && md->base != nullptr; }
 
+// ---- debug guard words ---------------------------------------------------------
+
+// GPT2_GUARD_WORDS set (and not "0") at create puts a guard region after
+// every sub-buffer of the arena.
+bool guards_requested() {
+    const char* e = std::getenv("GPT2_GUARD_WORDS");
+    return e && *e && std::strcmp(e, "0") != 0;
+}
+
+int write_guards(gpt2_model* md) {
+    std::vector<uint32_t> pat(gh::kGuardBytes / 4, gh::kGuardWord);
+    for (const auto& r : md->lay.regions)
+        TRY(hip_check(hipMemcpy(md->base + r.guard, pat.data(), gh::kGuardBytes,
+                                hipMemcpyHostToDevice),
+                      "guard write"));
+    return GPT2_OK;
+}
+
 }  // namespace
 
 // ============================================================================
@@ -680,38 +524,6 @@ bool valid_model(gpt2_model* md) { return md != nullptr && md->base != nullptr; 
 // ============================================================================
 
 extern "C" {
-
-const char* gpt2_last_error(void) { return g_err.c_str(); }
-
-int gpt2_validate_config(const gpt2_config* cfg) { return check_config(cfg); }
-
-int64_t gpt2_config_num_parameters(const gpt2_config* cfg) {
-    if (check_config(cfg) != GPT2_OK) return -1;
-    int64_t s[16], n = 0;
-    param_sizes(cfg, s);
-    for (int i = 0; i < 16; i++) n += s[i];
-    return n;
-}
-
-int gpt2_config_param_tensor(const gpt2_config* cfg, int i, const char** name, int64_t* offset,
-                             int64_t* numel) {
-    TRY(check_config(cfg));
-    if (i < 0 || i >= 16) return fail(GPT2_EINVAL, "parameter index %d outside 0..15", i);
-    int64_t s[16], off = 0;
-    param_sizes(cfg, s);
-    for (int k = 0; k < i; k++) off += s[k];
-    if (name) *name = kParamNames[i];
-    if (offset) *offset = off;
-    if (numel) *numel = s[i];
-    return GPT2_OK;
-}
-
-int64_t gpt2_config_device_bytes(const gpt2_config* cfg) {
-    if (check_config(cfg) != GPT2_OK) return -1;
-    Layout y;
-    y.build(cfg);
-    return (int64_t)y.total;
-}
 
 void gpt2_destroy(gpt2_model* md) {
     if (!md) return;
@@ -738,7 +550,7 @@ int gpt2_create(const gpt2_config* cfg, const gpt2_allocator* alloc, void* hip_s
         return fail(GPT2_EINVAL, "allocator needs both alloc and free");
     gpt2_model* md = new gpt2_model();
     md->cfg = *cfg;
-    md->lay.build(cfg);
+    md->lay.build(cfg, gk::device_cu_count(), guards_requested());
     md->stream = (hipStream_t)hip_stream;
     int rc = GPT2_OK;
     if (alloc) {
@@ -795,10 +607,11 @@ int gpt2_create(const gpt2_config* cfg, const gpt2_allocator* alloc, void* hip_s
         if (rc == GPT2_OK)
             rc = hip_check(hipMemcpy(md->lgood(), st, 12, hipMemcpyHostToDevice), "scale init");
     }
+    if (rc == GPT2_OK && md->lay.guards) rc = write_guards(md);
     if (rc != GPT2_OK) {
-        std::string msg = g_err;
+        const std::string msg = gpt2_last_error();
         gpt2_destroy(md);
-        g_err = msg;
+        gpt2_set_error(rc, msg.c_str());
         return rc;
     }
     *out = md;
@@ -867,14 +680,6 @@ int gpt2_copy_opt_state(gpt2_model* md, float* hm, float* hv) {
 
 namespace {
 
-constexpr char kCkptMagic[8] = {'G', 'P', 'T', '2', 'C', 'K', 'P', 'T'};
-struct CkptHeader {
-    char magic[8];
-    uint32_t version, precision;
-    int64_t nparams, step;
-};
-static_assert(sizeof(CkptHeader) == 32, "checkpoint header is 32 bytes");
-
 int ckpt_stream(gpt2_model* md, FILE* f, bool save) {
     const int64_t n = md->lay.nparams;
     const size_t chunk = (size_t)std::min<int64_t>(n, (int64_t)1 << 24);
@@ -911,12 +716,8 @@ int gpt2_save_checkpoint(gpt2_model* md, const char* path, int64_t step) {
     TRY(hip_check(hipStreamSynchronize(md->stream), "synchronize"));
     FILE* f = fopen(path, "wb");
     if (!f) return fail(GPT2_EINVAL, "cannot open %s: %s", path, strerror(errno));
-    CkptHeader h{};
-    memcpy(h.magic, kCkptMagic, 8);
-    h.version = 1;
-    h.precision = (uint32_t)md->cfg.precision;
-    h.nparams = md->lay.nparams;
-    h.step = step;
+    gh::CkptHeader h;
+    gh::ckpt_header_make(&h, md->cfg.precision, md->lay.nparams, step);
     int rc = fwrite(&h, sizeof h, 1, f) == 1 ? ckpt_stream(md, f, true)
                                              : fail(GPT2_EINVAL, "checkpoint write failed");
     if (fclose(f) != 0 && rc == GPT2_OK) rc = fail(GPT2_EINVAL, "checkpoint close failed");
@@ -927,13 +728,9 @@ int gpt2_load_checkpoint(gpt2_model* md, const char* path, int64_t* step) {
     if (!valid_model(md) || !path) return fail(GPT2_EINVAL, "NULL argument");
     FILE* f = fopen(path, "rb");
     if (!f) return fail(GPT2_EINVAL, "cannot open %s: %s", path, strerror(errno));
-    CkptHeader h{};
-    int rc = GPT2_OK;
-    if (fread(&h, sizeof h, 1, f) != 1 || memcmp(h.magic, kCkptMagic, 8) != 0 || h.version != 1)
-        rc = fail(GPT2_EINVAL, "%s is not a version-1 checkpoint", path);
-    else if (h.nparams != md->lay.nparams)
-        rc = fail(GPT2_EINVAL, "checkpoint holds %lld parameters, the model %lld",
-                  (long long)h.nparams, (long long)md->lay.nparams);
+    gh::CkptHeader h{};
+    const size_t got = fread(&h, 1, sizeof h, f);
+    int rc = gh::ckpt_header_check(&h, got, md->lay.nparams, path);
     if (rc == GPT2_OK) rc = hip_check(hipStreamSynchronize(md->stream), "synchronize");
     if (rc == GPT2_OK) rc = ckpt_stream(md, f, false);
     if (rc == GPT2_OK && fgetc(f) != EOF) rc = fail(GPT2_EINVAL, "checkpoint has trailing bytes");
@@ -1020,9 +817,13 @@ int gpt2_copy_activation(gpt2_model* md, const char* name, int layer, float* dst
     return fail(GPT2_EINVAL, "unknown activation name '%s'", name);
 }
 
-int gpt2_forward(gpt2_model* md, const int32_t* tokens, const int32_t* targets, int B, int T,
-                 float* mean_loss) {
-    if (!valid_model(md) || !tokens) return fail(GPT2_EINVAL, "NULL argument");
+namespace {
+
+// Checks host ids and queues their upload through the pinned staging buffer
+// (waiting until the previous upload has left it); *dtok / *dtgt get the
+// device copies (*dtgt = NULL without targets).
+int stage_ids(gpt2_model* md, const int32_t* tokens, const int32_t* targets, int B, int T,
+              int32_t** dtok, int32_t** dtgt) {
     TRY(check_bt(md, B, T));
     const int M = B * T, V = md->lay.V;
     for (int i = 0; i < M; i++)
@@ -1033,31 +834,50 @@ int gpt2_forward(gpt2_model* md, const int32_t* tokens, const int32_t* targets, 
             if (targets[i] < 0 || targets[i] >= V)
                 return fail(GPT2_ERANGE, "target %d at position %d outside [0, %d)", targets[i],
                             i, V);
-    // stage through pinned memory; wait until the previous upload has left it
     if (md->stage_pending) TRY(hip_check(hipEventSynchronize(md->stage_done), "stage wait"));
     std::memcpy(md->h_stage, tokens, M * sizeof(int32_t));
     if (targets) std::memcpy(md->h_stage + md->lay.M, targets, M * sizeof(int32_t));
-    int32_t* dtok = md->at<int32_t>(md->lay.tokens);
-    int32_t* dtgt = md->at<int32_t>(md->lay.targets);
-    TRY(hip_check(hipMemcpyAsync(dtok, md->h_stage, M * sizeof(int32_t), hipMemcpyHostToDevice,
+    *dtok = md->at<int32_t>(md->lay.tokens);
+    *dtgt = targets ? md->at<int32_t>(md->lay.targets) : nullptr;
+    TRY(hip_check(hipMemcpyAsync(*dtok, md->h_stage, M * sizeof(int32_t), hipMemcpyHostToDevice,
                                  md->stream),
                   "token upload"));
     if (targets)
-        TRY(hip_check(hipMemcpyAsync(dtgt, md->h_stage + md->lay.M, M * sizeof(int32_t),
+        TRY(hip_check(hipMemcpyAsync(*dtgt, md->h_stage + md->lay.M, M * sizeof(int32_t),
                                      hipMemcpyHostToDevice, md->stream),
                       "target upload"));
     TRY(hip_check(hipEventRecord(md->stage_done, md->stream), "event record"));
     md->stage_pending = true;
-    TRY(forward_impl(md, dtok, targets ? dtgt : nullptr, B, T));
+    return GPT2_OK;
+}
+
+}  // namespace
+
+int gpt2_forward(gpt2_model* md, const int32_t* tokens, const int32_t* targets, int B, int T,
+                 float* mean_loss) {
+    if (!valid_model(md) || !tokens) return fail(GPT2_EINVAL, "NULL argument");
+    int32_t *dtok, *dtgt;
+    TRY(stage_ids(md, tokens, targets, B, T, &dtok, &dtgt));
+    TRY(forward_impl(md, dtok, dtgt, B, T, targets ? FWD_TRAIN : FWD_INFER));
     if (mean_loss) return read_loss(md, mean_loss);
     return GPT2_OK;
+}
+
+int gpt2_evaluate(gpt2_model* md, const int32_t* tokens, const int32_t* targets, int B, int T,
+                  float* mean_loss) {
+    if (!valid_model(md) || !tokens || !targets || !mean_loss)
+        return fail(GPT2_EINVAL, "NULL argument");
+    int32_t *dtok, *dtgt;
+    TRY(stage_ids(md, tokens, targets, B, T, &dtok, &dtgt));
+    TRY(forward_impl(md, dtok, dtgt, B, T, FWD_EVAL));
+    return read_loss(md, mean_loss);
 }
 
 int gpt2_forward_device(gpt2_model* md, const int32_t* tokens, const int32_t* targets, int B,
                         int T, float* mean_loss) {
     if (!valid_model(md) || !tokens) return fail(GPT2_EINVAL, "NULL argument");
     TRY(check_bt(md, B, T));
-    TRY(forward_impl(md, tokens, targets, B, T));
+    TRY(forward_impl(md, tokens, targets, B, T, targets ? FWD_TRAIN : FWD_INFER));
     if (mean_loss) return read_loss(md, mean_loss);
     return GPT2_OK;
 }
@@ -1160,6 +980,25 @@ int gpt2_get_loss_scale(gpt2_model* md, float* scale, int* last_update_skipped) 
     TRY(hip_check(hipMemcpy(&sk, md->lskipped(), 4, hipMemcpyDeviceToHost), "scale readback"));
     if (scale) *scale = sc;
     if (last_update_skipped) *last_update_skipped = sk;
+    return GPT2_OK;
+}
+
+int gpt2_check_guards(gpt2_model* md) {
+    if (!valid_model(md)) return fail(GPT2_EINVAL, "model is NULL");
+    if (!md->lay.guards)
+        return fail(GPT2_EINVAL, "the model was created without GPT2_GUARD_WORDS");
+    TRY(hip_check(hipStreamSynchronize(md->stream), "synchronize"));
+    std::vector<uint32_t> got(gh::kGuardBytes / 4);
+    for (const auto& r : md->lay.regions) {
+        TRY(hip_check(hipMemcpy(got.data(), md->base + r.guard, gh::kGuardBytes,
+                                hipMemcpyDeviceToHost),
+                      "guard read"));
+        for (size_t i = 0; i < got.size(); i++)
+            if (got[i] != gh::kGuardWord)
+                return fail(GPT2_ECORRUPT,
+                            "guard after '%s' (%zu bytes) overwritten at byte %zu: 0x%08x",
+                            r.name, r.bytes, 4 * i, got[i]);
+    }
     return GPT2_OK;
 }
 

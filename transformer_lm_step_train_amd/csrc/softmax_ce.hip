@@ -8,7 +8,8 @@
 //   d(mean loss)/dz_v = (exp(z_v - lse) - [v == y]) / N.
 // This equals the materialized softmax followed by -log p_y.  One workgroup
 // holds a whole row in registers (one HBM read), and writes the gradient over
-// the logits (one HBM write).
+// the logits (one HBM write).  The evaluation variant (no gradient) only
+// reads the row and leaves the logits as they are.
 #include "common.h"
 #include "kernels.h"
 
@@ -28,7 +29,7 @@ __device__ __forceinline__ float block_max(float v, float* sh) {
     return r;
 }
 
-template <int NT, int NJ, class T>
+template <int NT, int NJ, bool GRAD, class T>
 __global__ __launch_bounds__(NT) __attribute__((amdgpu_waves_per_eu(4))) void softmax_ce_kernel(T* __restrict__ logits,
                                                         float* __restrict__ losses,
                                                         const int32_t* __restrict__ targets,
@@ -104,6 +105,7 @@ __global__ __launch_bounds__(NT) __attribute__((amdgpu_waves_per_eu(4))) void so
         losses[row] = bad ? 0.f : lse - zt;
         if (bad) atomicOr(flag, 2);
     }
+    if constexpr (!GRAD) return;
     // exp(z - lse) = e * exp(m_t - lse); the padding columns give 0.
     const float f = bad || m == -INFINITY ? 0.f : __builtin_amdgcn_exp2f((m - lse) * LOG2E) * dscale;
     // The target column: group jt of thread `owner`, component tc.
@@ -125,8 +127,12 @@ __global__ __launch_bounds__(NT) __attribute__((amdgpu_waves_per_eu(4))) void so
 template <int NT, int NJ, class T>
 hipError_t launch_ce(hipStream_t s, T* logits, float* losses, const int32_t* targets, int N,
                      int V, int ldv, float dscale, const float* gscale, int* flag) {
-    launch((softmax_ce_kernel<NT, NJ, T>), dim3(N), dim3(NT), 0, s, logits, losses,
-                       targets, V, ldv, dscale, gscale, flag);
+    if (dscale != 0.f)
+        launch((softmax_ce_kernel<NT, NJ, true, T>), dim3(N), dim3(NT), 0, s, logits, losses,
+               targets, V, ldv, dscale, gscale, flag);
+    else
+        launch((softmax_ce_kernel<NT, NJ, false, T>), dim3(N), dim3(NT), 0, s, logits, losses,
+               targets, V, ldv, dscale, gscale, flag);
     return hipGetLastError();
 }
 

@@ -20,6 +20,7 @@ HERE = os.path.dirname(os.path.abspath(__file__))
 LIB_PATH = os.path.join(HERE, "libgpt2_hip.so")
 
 GPT2_OK, GPT2_EINVAL, GPT2_ERANGE, GPT2_ESTATE, GPT2_ENOMEM, GPT2_EDEVICE = 0, -1, -2, -3, -4, -5
+GPT2_ECORRUPT = -6
 GPT2_FP32, GPT2_BF16_MIXED, GPT2_F16_MIXED = 0, 1, 2
 KC_GEMM, KC_ATTENTION, KC_LAYERNORM, KC_SOFTMAX_CE, KC_ADAMW, KC_OTHER = range(6)
 KC_NAMES = ["gemm", "attention", "layernorm", "softmax_ce", "adamw", "other"]
@@ -80,6 +81,7 @@ def _load():
         "gpt2_forward": (_c.c_int, [_vp, _vp, _vp, _c.c_int, _c.c_int, P(_c.c_float)]),
         "gpt2_forward_device": (_c.c_int, [_vp, _vp, _vp, _c.c_int, _c.c_int,
                                            P(_c.c_float)]),
+        "gpt2_evaluate": (_c.c_int, [_vp, _vp, _vp, _c.c_int, _c.c_int, P(_c.c_float)]),
         "gpt2_sample": (_c.c_int, [_vp, _c.c_int, _c.c_int, _c.c_float, P(_c.c_int32)]),
         "gpt2_generate": (_c.c_int, [_vp, _vp, _c.c_int, _c.c_int, _vp]),
         "gpt2_loader_open": (_c.c_int, [_c.c_char_p, _c.c_int, _c.c_int, P(_vp)]),
@@ -94,6 +96,7 @@ def _load():
         "gpt2_backward": (_c.c_int, [_vp]),
         "gpt2_update": (_c.c_int, [_vp] + [_c.c_float] * 5 + [_c.c_int]),
         "gpt2_synchronize": (_c.c_int, [_vp]),
+        "gpt2_check_guards": (_c.c_int, [_vp]),
         "gpt2_last_error": (_c.c_char_p, []),
         "gpt2_profile": (_c.c_int, [_vp, _c.c_int]),
         "gpt2_profile_read": (_c.c_int, [_vp, _c.c_int, P(_c.c_double), P(_i64),
@@ -222,6 +225,12 @@ def gpt2_forward_device(h, tokens_ptr, targets_ptr, B, T, want_loss=True):
     loss = _c.c_float(float("nan"))
     _check(lib.gpt2_forward_device(h, tokens_ptr, targets_ptr, B, T,
                                    _c.byref(loss) if want_loss else None))
+    return loss.value
+
+
+def gpt2_evaluate(h, tokens, targets, B, T):
+    loss = _c.c_float(float("nan"))
+    _check(lib.gpt2_evaluate(h, _i32p(tokens), _i32p(targets), B, T, _c.byref(loss)))
     return loss.value
 
 
@@ -393,6 +402,12 @@ class Model:
         tgt = None if targets is None else np.ascontiguousarray(targets, dtype=np.int32)
         return gpt2_forward(self.h, tok, tgt, B, T)
 
+    def evaluate(self, tokens, targets):
+        """Mean loss without gradient or backward state (the logits stay)."""
+        tok = np.ascontiguousarray(tokens, dtype=np.int32)
+        B, T = tok.shape
+        return gpt2_evaluate(self.h, tok, np.ascontiguousarray(targets, dtype=np.int32), B, T)
+
     def forward_device(self, tokens, targets=None, want_loss=True):
         """tokens / targets: int32 device tensors of shape (B, T)."""
         B, T = tokens.shape
@@ -431,6 +446,10 @@ class Model:
 
     def synchronize(self):
         gpt2_synchronize(self.h)
+
+    def check_guards(self):
+        """Raises GPT2Error (GPT2_ECORRUPT) if a debug guard word changed."""
+        _check(lib.gpt2_check_guards(self.h))
 
     def step(self, tokens, targets, step, **adamw):
         loss = self.forward(tokens, targets)

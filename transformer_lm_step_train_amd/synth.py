@@ -143,6 +143,9 @@ CONFIGS = {
                                T=1024, steps=1),
     # ragged: odd vocab, odd T, non-power-of-two width; exercises every tail
     "ragged": dict(L=2, C=96, NH=3, V=1001, maxT=80, B=3, T=77, steps=1),
+    # width 80 (head size 16): every matmul reduction length (80, 240, 320)
+    # leaves a partial 32-deep step
+    "ragged80": dict(L=2, C=80, NH=5, V=1001, maxT=80, B=3, T=77, steps=1),
     # rotary position embedding instead of the wpe table
     "tiny_rope": dict(L=2, C=64, NH=4, V=512, maxT=64, B=2, T=64, steps=1, rope=True),
     "ragged_rope": dict(L=2, C=96, NH=3, V=1001, maxT=80, B=3, T=77, steps=1, rope=True),

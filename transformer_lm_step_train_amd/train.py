@@ -6,7 +6,8 @@ ms)" and "generated: ..." lines).  The pages do not print their intervals;
 they are arguments here.
 
 Every number comes from the library: the batches from gpt2_loader_*, the
-losses from gpt2_forward, the sample from gpt2_generate.  This module only
+training losses from gpt2_forward, the validation losses from gpt2_evaluate
+(no gradient, no backward state), the sample from gpt2_generate.  This module only
 sequences the calls and formats the log.
 """
 import time
@@ -22,7 +23,7 @@ def val_loss(model, loader, batches):
     total = 0.0
     for _ in range(batches):
         tok, tgt = loader.next()
-        total += model.forward(tok, tgt)
+        total += model.evaluate(tok, tgt)
     return total / batches
 
 
