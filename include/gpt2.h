@@ -281,6 +281,37 @@ GPT2_API int gpt2_loader_next(gpt2_loader* loader, int32_t* tokens, int32_t* tar
 GPT2_API int gpt2_loader_reset(gpt2_loader* loader);
 GPT2_API void gpt2_loader_close(gpt2_loader* loader);
 
+/* ---- loss without allocation ------------------------------------------------
+ * For callers that cannot allocate device memory (code under HIP graph
+ * capture, tight serving loops, harnesses that forbid hipMalloc): the loss
+ * step that ends gpt2_forward / gpt2_evaluate, on caller-owned device
+ * buffers, with no allocation of any kind.  The per-row losses go to a fixed
+ * device array of the library (32768 floats, 128 KiB per device, held until
+ * the process ends), so N <= 32768.  Every call on a device shares that
+ * array: calls that overlap on one device (different streams or threads)
+ * race and must be serialized by the caller.
+ *
+ * logits   device, N rows of ldv elements (fp32, or bf16 / fp16 bits for
+ *          GPT2_BF16_MIXED / GPT2_F16_MIXED), V valid columns;
+ *          V <= ldv <= 65536, ldv % 4 == 0, the buffer 16-byte aligned.
+ * targets  device int32 (N), each in [0, V).
+ * grad_scale 0: the logits are only read.  Otherwise they are overwritten by
+ *          (softmax(row) - onehot(target)) * grad_scale and columns
+ *          V..ldv-1 by 0 (gpt2_forward uses 1/N, the mean's gradient).
+ * mean_loss device float: the mean over the rows of lse(row) - row[target].
+ * flag     device int32: set to 0, then to 2 if some target is outside
+ *          [0, V) (that row then counts 0 loss and gets a 0 gradient).
+ * hip_stream the stream everything is queued on (NULL = null stream); the
+ *          call does not wait for it.
+ * Rows are the same kernels' rows as the model's, so the loss and gradient
+ * equal the model's for the same logits, ldv and targets bit for bit.
+ * Errors (nothing is launched): GPT2_EINVAL for NULL pointers, N outside
+ * 1..32768, bad V / ldv, an unknown precision; GPT2_EDEVICE for a HIP error.
+ */
+GPT2_API int gpt2_cross_entropy_static(const void* logits, int64_t ldv, const int32_t* targets,
+                                       int N, int V, int precision, float grad_scale,
+                                       float* mean_loss, int32_t* flag, void* hip_stream);
+
 /* Debug guard words.  With the environment variable GPT2_GUARD_WORDS set
  * (and not "0") when gpt2_create runs, every sub-buffer of the arena is
  * followed by 256 bytes of the word 0xC0DEFACE (the arena grows by 256 bytes

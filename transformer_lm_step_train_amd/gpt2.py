@@ -92,6 +92,8 @@ def _load():
         "gpt2_loader_close": (None, [_vp]),
         "gpt2_set_loss_scale": (_c.c_int, [_vp, _c.c_float, _c.c_int]),
         "gpt2_get_loss_scale": (_c.c_int, [_vp, P(_c.c_float), P(_c.c_int)]),
+        "gpt2_cross_entropy_static": (_c.c_int, [_vp, _i64, _vp, _c.c_int, _c.c_int, _c.c_int,
+                                                 _c.c_float, _vp, _vp, _vp]),
         "gpt2_zero_grad": (_c.c_int, [_vp]),
         "gpt2_backward": (_c.c_int, [_vp]),
         "gpt2_update": (_c.c_int, [_vp] + [_c.c_float] * 5 + [_c.c_int]),
@@ -232,6 +234,13 @@ def gpt2_evaluate(h, tokens, targets, B, T):
     loss = _c.c_float(float("nan"))
     _check(lib.gpt2_evaluate(h, _i32p(tokens), _i32p(targets), B, T, _c.byref(loss)))
     return loss.value
+
+
+def gpt2_cross_entropy_static(logits_ptr, ldv, targets_ptr, N, V, precision, grad_scale,
+                              mean_loss_ptr, flag_ptr, stream=None):
+    """Device pointers in, device outputs written; nothing allocated."""
+    _check(lib.gpt2_cross_entropy_static(logits_ptr, ldv, targets_ptr, N, V, precision,
+                                         grad_scale, mean_loss_ptr, flag_ptr, stream))
 
 
 def gpt2_sample(h, b, t, coin):
