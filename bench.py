@@ -41,6 +41,9 @@ def parse():
     ap.add_argument("--precision", choices=["fp32", "bf16", "fp16"], default="fp32",
                     help="fp32 (the headline workload), or the bf16 / fp16 mixed-precision "
                          "model")
+    ap.add_argument("--tokens", choices=["uniform", "zipf"], default="uniform",
+                    help="token ids: uniform (the workload), or Zipf(1.1) like real text "
+                         "(many repeats of a few ids; for timing the embedding backward)")
     ap.add_argument("--no-mixed", action="store_true",
                     help="fp32 run only: no mixed_bf16 leg")
     ap.add_argument("--no-kernel-timing", action="store_true",
@@ -299,7 +302,10 @@ def main():
     c = synth.CONFIGS[WORKLOAD]
     B, T = c["B"], c["T"]
     params = synth.init_params(c["L"], c["C"], c["V"], c["maxT"])
-    tok, tgt = synth.token_stream(B, T, c["V"])
+    if args.tokens == "zipf":
+        tok, tgt = synth.zipf_tokens(B, T, c["V"])
+    else:
+        tok, tgt = synth.token_stream(B, T, c["V"])
     half = args.precision in ("bf16", "fp16")
     head = run_leg(args.precision, args, params, tok, tgt)
 
@@ -317,7 +323,7 @@ def main():
         "scaling": "weak",
         "vs_baseline": None,
         "dtype": head["dtype"],
-        "data": "synthetic (seeded uniform int32 token ids, GPT-2 init N(0,0.02))",
+        "data": f"synthetic (seeded {args.tokens} int32 token ids, GPT-2 init N(0,0.02))",
         "config": {"workload": head["workload"],
                    "global_batch": B, "seq_len": T, "layers": c["L"], "channels": c["C"],
                    "heads": c["NH"], "vocab": c["V"], "parallelism": "single GPU"},

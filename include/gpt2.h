@@ -130,18 +130,22 @@ GPT2_API int gpt2_copy_grads(gpt2_model* model, float* host_dst);
 GPT2_API int gpt2_copy_opt_state(gpt2_model* model, float* host_m, float* host_v);
 
 /* ---- checkpoint ----------------------------------------------------------
- * Save and resume training state: the fp32 parameters and both AdamW moments
- * (the whole training state of the fp32 and bf16 models) and the caller's
- * step counter, as one raw file: a 32-byte header {"GPT2CKPT", u32 version
- * 1, u32 precision, i64 nparams, i64 step} followed by params, m and v as
- * nparams little-endian fp32 each, in arena order.  Both calls wait for the
- * stream and stream the arenas through a host buffer of at most 64 MB.
- * Loading requires the same parameter count (any precision: master weights
- * are fp32 in every model), refreshes the 16-bit weight copies, and returns
- * the saved step in *step (may be NULL).  For the fp16 model the loss scale
- * is not part of the file: restore it with gpt2_set_loss_scale.  Errors:
+ * Save and resume training state: the fp32 parameters, both AdamW moments,
+ * the fp16 model's dynamic loss-scale state and the caller's step counter,
+ * as one raw file: a 32-byte header {"GPT2CKPT", u32 version 2, u32
+ * precision, i64 nparams, i64 step}, a 16-byte block {f32 loss scale, i32
+ * clean updates in a row, i32 growth interval, u32 0} (1, 0, 0 for the fp32
+ * and bf16 models), then params, m and v as nparams little-endian fp32 each,
+ * in arena order.  Both calls wait for the stream and stream the arenas
+ * through a host buffer of at most 64 MB.  Loading requires the same
+ * parameter count (any precision: master weights are fp32 in every model),
+ * refreshes the 16-bit weight copies, restores the loss-scale state when
+ * both the file and the model are fp16 (otherwise the model keeps its own),
+ * and returns the saved step in *step (may be NULL).  Version-1 files (the
+ * 32-byte header directly followed by the arenas) load too.  Errors:
  * GPT2_EINVAL for a NULL model or path, step < 0, an unreadable or foreign
- * file, a parameter-count mismatch (these leave the model untouched), or a
+ * file, an unknown precision or an invalid loss-scale block, a
+ * parameter-count mismatch (these leave the model untouched), or a
  * truncated or oversized file (found while streaming: the model is then
  * partly overwritten); GPT2_ENOMEM, GPT2_EDEVICE. */
 GPT2_API int gpt2_save_checkpoint(gpt2_model* model, const char* path, int64_t step);

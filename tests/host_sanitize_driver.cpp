@@ -193,9 +193,21 @@ static void test_checkpoint_headers() {
     gh::CkptHeader b = h;
     b.magic[3] = 'X';
     CHECK(gh::ckpt_header_check(&b, sizeof b, 124439808, "x") == GPT2_EINVAL);
+    CHECK(h.version == 2);
     b = h;
-    b.version = 2;
+    b.version = 1;
+    CHECK(gh::ckpt_header_check(&b, sizeof b, 124439808, "x") == GPT2_OK);
+    b.version = 3;
     CHECK(gh::ckpt_header_check(&b, sizeof b, 124439808, "x") == GPT2_EINVAL);
+    // the loss-scale block
+    const gh::CkptScale ok16 = {1024.0f, 1, 2, 0u}, ok32 = {1.0f, 0, 0, 0u};
+    CHECK(gh::ckpt_scale_check(&ok16, sizeof ok16, GPT2_F16_MIXED, "x") == GPT2_OK);
+    CHECK(gh::ckpt_scale_check(&ok32, sizeof ok32, GPT2_FP32, "x") == GPT2_OK);
+    CHECK(gh::ckpt_scale_check(&ok32, sizeof ok32, GPT2_F16_MIXED, "x") == GPT2_EINVAL);
+    CHECK(gh::ckpt_scale_check(&ok16, 15, GPT2_F16_MIXED, "x") == GPT2_EINVAL);
+    const gh::CkptScale bad_s[] = {{0.5f, 0, 2, 0u}, {INFINITY, 0, 2, 0u}, {NAN, 0, 2, 0u},
+                                   {4.0f, -1, 2, 0u}, {4.0f, 2, 2, 0u}, {4.0f, 0, 2, 9u}};
+    for (const auto& x : bad_s) CHECK(gh::ckpt_scale_check(&x, sizeof x, GPT2_F16_MIXED, "x") == GPT2_EINVAL);
     b = h;
     b.precision = 9;
     CHECK(gh::ckpt_header_check(&b, sizeof b, 124439808, "x") == GPT2_EINVAL);

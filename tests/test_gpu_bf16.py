@@ -3,11 +3,10 @@ attention operands, fp32 accumulation, fp32 master weights, gradients, Adam
 state, loss and softmax statistics) against the fp32 CPU oracle.
 
 The stated tolerance for this configuration is on the loss: rel <= 2e-2.
-Activations and gradients are checked against bounds derived from bf16's
-8-bit significand (unit roundoff 2^-9 ~ 2e-3 per stored value): forward
-activations max-abs-normalised within 5e-2, gradients within 5e-2 (several
-roundings compound through twelve layers; about 1.5e-2 is observed); these
-are sanity bounds, the loss is the pinned quantity.
+Activations and gradients are checked against a bound derived from bf16's
+8-bit significand: 15 unit roundoffs (u = 2^-9 ~ 2e-3 per stored value),
+3e-2 max-abs-normalised, since each value passes about a dozen roundings on
+its way through the layers; up to 1.34e-2 (about 7u) is observed.
 """
 import numpy as np
 import pytest
@@ -17,6 +16,8 @@ torch = pytest.importorskip("torch")
 import oracle
 from oracle import OracleModel
 from transformer_lm_step_train_amd import synth
+
+BOUND = 15 * 2.0 ** -9  # 2.9e-2
 
 pytestmark = [
     pytest.mark.gpu,
@@ -65,7 +66,7 @@ def test_bf16_step(name):
         worst[n] = max(rel(m.activation(n, l), ref[l]) for l in range(L))
     worst["logits"] = rel(m.activation("logits"), o.act("logits"))
     print("[bf16] forward rel:", {k: f"{v:.2e}" for k, v in worst.items()}, flush=True)
-    assert all(v < 5e-2 for v in worst.values()), worst
+    assert all(v < BOUND for v in worst.values()), worst
     lg = m.forward(tok, tgt)
     print(f"[bf16] loss {lg:.6f} oracle {lo:.6f} rel {abs(lg - lo) / lo:.2e}", flush=True)
     assert abs(lg - lo) / lo < 2e-2
@@ -80,7 +81,7 @@ def test_bf16_step(name):
         errs[n] = rel(gg[off:off + sz], go[off:off + sz])
         off += sz
     print("[bf16] grad rel:", {k: f"{v:.2e}" for k, v in errs.items()}, flush=True)
-    assert all(v < 5e-2 for v in errs.values()), errs
+    assert all(v < BOUND for v in errs.values()), errs
     assert np.all(np.isfinite(gg))
     m.update(step=1, **synth.ADAMW)
     assert np.all(np.isfinite(m.params()))

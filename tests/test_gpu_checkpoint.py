@@ -1,8 +1,10 @@
 """Checkpoint and resume through the C ABI (gpt2_save_checkpoint /
-gpt2_load_checkpoint): two steps, save, load into a fresh model, one more
-step must equal three straight steps bit for bit (parameters and both AdamW
-moments), in the fp32 and the bf16 model; and the file errors."""
+gpt2_load_checkpoint): steps, save, load into a fresh model, more steps must
+equal straight steps bit for bit (parameters, both AdamW moments and, in the
+fp16 model, the loss-scale schedule); version-1 files; and the file
+errors."""
 import os
+import struct
 
 import numpy as np
 import pytest
@@ -52,7 +54,7 @@ def test_resume_is_bitwise(tmp_path, prec):
     path = os.path.join(tmp_path, "state.ckpt")
     b.save_checkpoint(path, 2)
     b.close()
-    assert os.path.getsize(path) == 32 + 12 * len(params)
+    assert os.path.getsize(path) == 48 + 12 * len(params)
 
     r, _ = model("small", precision)
     r.set_params(np.zeros_like(params))  # overwritten by the load
@@ -63,6 +65,67 @@ def test_resume_is_bitwise(tmp_path, prec):
     r.close()
     for w, x, what in zip(want, got, ("params", "m", "v")):
         assert np.array_equal(w, x), what
+
+
+def test_fp16_resume_keeps_loss_scale_schedule(tmp_path):
+    """Growth interval 2: the scale doubles after the second clean update.
+    Saving after one update and resuming must carry the count of clean
+    updates, or the resumed run doubles one step late."""
+    g = gpt2()
+    print("[ckpt] resume fp16", flush=True)
+    c = synth.CONFIGS["ragged"]
+    params = synth.init_params(c["L"], c["C"], c["V"], c["maxT"])
+    tok, tgt = synth.token_stream(c["B"], c["T"], c["V"])
+
+    a, _ = model("ragged", g.GPT2_F16_MIXED)
+    a.set_params(params)
+    a.set_loss_scale(1024.0, 2)
+    scales = []
+    for s in (1, 2, 3):
+        a.step(tok, tgt, s)
+        scales.append(a.loss_scale()[0])
+    assert scales == [1024.0, 2048.0, 2048.0], scales
+    want = (a.params(), *a.opt_state())
+    a.close()
+
+    b, _ = model("ragged", g.GPT2_F16_MIXED)
+    b.set_params(params)
+    b.set_loss_scale(1024.0, 2)
+    b.step(tok, tgt, 1)
+    path = os.path.join(tmp_path, "fp16.ckpt")
+    b.save_checkpoint(path, 1)
+    b.close()
+
+    r, _ = model("ragged", g.GPT2_F16_MIXED)  # starts at 2^16, interval 2000
+    assert r.load_checkpoint(path) == 1
+    assert r.loss_scale()[0] == 1024.0
+    r.step(tok, tgt, 2)
+    assert r.loss_scale()[0] == 2048.0
+    r.step(tok, tgt, 3)
+    got = (r.params(), *r.opt_state())
+    r.close()
+    for w, x, what in zip(want, got, ("params", "m", "v")):
+        assert np.array_equal(w, x), what
+
+
+def test_version1_file_loads(tmp_path):
+    """A version-1 file (32-byte header, then the arenas) loads as before."""
+    g = gpt2()
+    m, c = model("tiny", g.GPT2_FP32)
+    params = synth.init_params(c["L"], c["C"], c["V"], c["maxT"])
+    m.set_params(params)
+    path = os.path.join(tmp_path, "v2.ckpt")
+    m.save_checkpoint(path, 5)
+    raw = open(path, "rb").read()
+    assert struct.unpack_from("<I", raw, 8)[0] == 2
+    v1 = bytearray(raw[:32] + raw[48:])
+    struct.pack_into("<I", v1, 8, 1)
+    p1 = os.path.join(tmp_path, "v1.ckpt")
+    open(p1, "wb").write(bytes(v1))
+    m.set_params(np.zeros_like(params))
+    assert m.load_checkpoint(p1) == 5
+    assert np.array_equal(m.params(), params)
+    m.close()
 
 
 def test_checkpoint_errors(tmp_path):
@@ -89,6 +152,11 @@ def test_checkpoint_errors(tmp_path):
     assert code(lambda: m.load_checkpoint(bad)) == g.GPT2_EINVAL
     open(bad, "wb").write(raw + b"\0")  # trailing bytes
     assert code(lambda: m.load_checkpoint(bad)) == g.GPT2_EINVAL
+    for off, fmt, val in ((12, "<I", 7), (44, "<I", 1)):  # unknown precision; nonzero pad
+        b = bytearray(raw)
+        struct.pack_into(fmt, b, off, val)
+        open(bad, "wb").write(bytes(b))
+        assert code(lambda: m.load_checkpoint(bad)) == g.GPT2_EINVAL
     other, _ = model("ragged", g.GPT2_FP32)  # another parameter count
     assert code(lambda: other.load_checkpoint(path)) == g.GPT2_EINVAL
     other.close()

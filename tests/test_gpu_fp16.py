@@ -3,9 +3,10 @@ matmul / attention operands, fp32 accumulation, fp32 master weights,
 gradients, Adam state and statistics, dynamic loss scaling) against the fp32
 CPU oracle, and of its loss-scale schedule against oracle_loss_scale_step.
 
-Tolerances follow fp16's 11-bit significand (unit roundoff 2^-11 ~ 4.9e-4
+Tolerances follow fp16's 11-bit significand (unit roundoff u = 2^-11 ~ 4.9e-4
 per stored value, 4x finer than bf16): loss rel 5e-3, forward activations
-and gradients max-abs-normalised within 2e-2 (a few 1e-3 are observed).
+and gradients max-abs-normalised within 15u = 7.3e-3, the same multiple of
+u as the bf16 bound (up to 1.8e-3, about 4u, is observed).
 """
 import numpy as np
 import pytest
@@ -15,6 +16,8 @@ torch = pytest.importorskip("torch")
 import oracle
 from oracle import OracleModel
 from transformer_lm_step_train_amd import synth
+
+BOUND = 15 * 2.0 ** -11  # 7.3e-3
 
 pytestmark = [
     pytest.mark.gpu,
@@ -63,7 +66,7 @@ def test_fp16_step(name):
         worst[n] = max(rel(m.activation(n, l), ref[l]) for l in range(L))
     worst["logits"] = rel(m.activation("logits"), o.act("logits"))
     print("[fp16] forward rel:", {k: f"{v:.2e}" for k, v in worst.items()}, flush=True)
-    assert all(v < 2e-2 for v in worst.values()), worst
+    assert all(v < BOUND for v in worst.values()), worst
     lg = m.forward(tok, tgt)
     print(f"[fp16] loss {lg:.6f} oracle {lo:.6f} rel {abs(lg - lo) / lo:.2e}", flush=True)
     assert abs(lg - lo) / lo < 5e-3
@@ -78,7 +81,7 @@ def test_fp16_step(name):
         errs[n] = rel(gg[off:off + sz], go[off:off + sz])
         off += sz
     print("[fp16] grad rel:", {k: f"{v:.2e}" for k, v in errs.items()}, flush=True)
-    assert all(v < 2e-2 for v in errs.values()), errs
+    assert all(v < BOUND for v in errs.values()), errs
     m.update(step=1, **synth.ADAMW)
     assert m.loss_scale() == (65536.0, False)
     assert np.all(np.isfinite(m.params()))

@@ -45,7 +45,7 @@ pytestmark = [
 CFG = synth.CONFIGS["gpt2_124m_b16t1024"]
 B, T, V = CFG["B"], CFG["T"], CFG["V"]
 LR = synth.ADAMW["lr"]
-BF16_GRAD_BOUND = 5e-2
+BF16_GRAD_BOUND = 15 * 2.0 ** -9  # 15 bf16 unit roundoffs, as in tests/test_gpu_bf16.py
 BF16_LOSS_BOUND = 2e-2
 
 
@@ -152,7 +152,9 @@ def test_fp32_batch_step(inputs, gpu32, orc):
     params, _, _ = inputs
     R = reference_gradient(orc, inputs)
     lref = float(np.mean([orc["loss"][b] for b in range(B)]))
-    assert abs(gpu32["loss"] - lref) / lref < 1e-5, (gpu32["loss"], lref)
+    r = abs(gpu32["loss"] - lref) / lref
+    print(f"[full] fp32 loss {gpu32['loss']:.6f} oracle {lref:.6f} rel {r:.2e}", flush=True)
+    assert r < 1e-5, (gpu32["loss"], lref)
     assert gpu32["loss_repeat"] == gpu32["loss"]
     assert gpu32["loss_after"] < gpu32["loss"]
     sizes = orc["model"].param_sizes

@@ -162,14 +162,19 @@ def test_smaller_batch_than_allocated(name):
     P.close()
 
 
-@pytest.mark.parametrize("B", [256, 512])
-def test_large_batch_sort_variants(B):
+@pytest.mark.parametrize("B,kind", [(256, "uniform"), (512, "uniform"), (256, "zipf")])
+def test_large_batch_sort_variants(B, kind):
     """B*T = 16384 and 32768 positions on the tiny model: the embedding
     backward's key sort runs with 16 and 32 keys per thread (the latter fills
     the 160 KiB of LDS), and the weight gradients take their largest K
-    splits.  Every token id repeats about B/8 times."""
+    splits.  Uniform ids repeat about B/8 times each; with Zipf(1.1) ids the
+    most frequent one fills a run of thousands of positions across hundreds
+    of the backward's 16-key chunks."""
     P = Pair("tiny", B=B, T=64)
-    tok, tgt = synth.token_stream(P.B, P.T, P.c["V"])
+    if kind == "zipf":
+        tok, tgt = synth.zipf_tokens(P.B, P.T, P.c["V"])
+    else:
+        tok, tgt = synth.token_stream(P.B, P.T, P.c["V"])
     check_step(P, tok, tgt)
     P.close()
 

@@ -44,31 +44,31 @@ __device__ __forceinline__ void st4_nt(float* p, float4 v) {
     __builtin_nontemporal_store(w, reinterpret_cast<f32x4_t*>(p));
 }
 
-// tanh-form GELU and its derivative.  sqrt(2/pi) is the constant of the
-// definition.  tanh(u) is evaluated from the identity
-// tanh(u) = 1 - 2 / (1 + e^(2u)) with the hardware base-2 exponential and
-// reciprocal: a few instructions instead of a library call in the matmul
-// epilogues.  Its absolute error is a few fp32 ulps of 1, which GELU turns
-// into a relative error of the same size (1 + tanh is O(1) wherever the
-// output is not negligible); it saturates cleanly to +-1 (no inf/inf).
-#define GELU_K0 0.7978845608028654f
-#define GELU_K1 0.044715f
-#define TWO_LOG2E 2.8853900817779268f  // 2 / ln 2
+// tanh-form GELU and its derivative:
+//   GELU(x) = 0.5 x (1 + tanh(u)),  u = sqrt(2/pi) (x + 0.044715 x^3).
+// Since (1 + tanh(u)) / 2 = 1 / (1 + e^(-2u)) = s, GELU(x) = x s, and
+//   GELU'(x) = s + x s (1 - s) du2,  du2 = d(2u)/dx = 2 sqrt(2/pi) (1 + 3 * 0.044715 x^2).
+// e^(-2u) = 2^z with z = x (A + B x^2), A = -2 sqrt(2/pi) log2(e), B = 0.044715 A.
+// One hardware base-2 exponential and one reciprocal per element (a few
+// fp32 ulps), half the other arithmetic of the tanh form: these run in the
+// matmul epilogues.  Both ends saturate cleanly: x -> -inf gives 2^z = inf,
+// s = 0; x -> +inf gives s = 1.
+#define GELU_A (-2.302208198144325f)
+#define GELU_B (-0.1029432395800235f)
+#define GELU_D0 1.5957691216057308f   // 2 sqrt(2/pi)
+#define GELU_D1 0.21406444881780076f  // 2 sqrt(2/pi) * 3 * 0.044715
 
-__device__ __forceinline__ float tanh_fast(float u) {
-    return 1.0f - 2.0f * __builtin_amdgcn_rcpf(1.0f + __builtin_amdgcn_exp2f(TWO_LOG2E * u));
+__device__ __forceinline__ float gelu_sigmoid(float x, float x2) {
+    const float z = x * fmaf(GELU_B, x2, GELU_A);
+    return __builtin_amdgcn_rcpf(1.0f + __builtin_amdgcn_exp2f(z));
 }
 
-__device__ __forceinline__ float gelu_f(float x) {
-    float u = GELU_K0 * (x + GELU_K1 * x * x * x);
-    return 0.5f * x * (1.0f + tanh_fast(u));
-}
+__device__ __forceinline__ float gelu_f(float x) { return x * gelu_sigmoid(x, x * x); }
 
 __device__ __forceinline__ float gelu_grad_f(float x) {
-    float u = GELU_K0 * (x + GELU_K1 * x * x * x);
-    float th = tanh_fast(u);
-    float du = GELU_K0 * (1.0f + 3.0f * GELU_K1 * x * x);
-    return 0.5f * (1.0f + th) + 0.5f * x * (1.0f - th * th) * du;
+    const float x2 = x * x;
+    const float s = gelu_sigmoid(x, x2);
+    return fmaf(x * fmaf(GELU_D1, x2, GELU_D0), fmaf(-s, s, s), s);
 }
 
 // Maps a linear workgroup id to a logical tile id so that the 8 XCDs (which

@@ -139,51 +139,182 @@ __global__ __launch_bounds__(1024) void encoder_sort_kernel(uint32_t* __restrict
     }
 }
 
-// One wave per sorted position; the first position of each run of equal
-// tokens sums the run's gradient rows in position order into wte's row.
+// Embedding backward into wte, in two fixed-order stages over the sorted
+// (token, position) keys cut into chunks of EB_CHUNK consecutive keys, so
+// that a token repeated r times (frequent tokens of real text) costs about
+// r / EB_CHUNK serial row additions instead of r.
+//   Stage 1, one wave per chunk: the chunk's keys form pieces of runs of
+//   equal tokens; each piece's gradient rows are summed in key (= position)
+//   order.  A piece that is a whole run is added into its wte row at once
+//   (no other chunk holds that token).  A piece that continues from the
+//   previous chunk goes to the chunk's slot 0; one that continues into the
+//   next chunk and not from the previous one to slot 1.
+//   Stage 2, one wave per chunk where a run spanning later chunks starts:
+//   the run's slot 1, then slot 0 of each later chunk it reaches, summed in
+//   chunk order and added into the run's wte row.
+// Ids outside [0, V) were sorted with the token field V and are skipped.
+constexpr int EB_CHUNK = 16;
+
 template <int NCH, class E>
-__global__ __launch_bounds__(256) void encoder_bwd_wte_kernel(float* __restrict__ dwte,
-                                                              const E* __restrict__ dx,
-                                                              const uint32_t* __restrict__ keys,
-                                                              int n, int C, int V,
-                                                              int pos_bits) {
-    const int i = blockIdx.x * 4 + (threadIdx.x >> 6);
+__global__ __launch_bounds__(256) void encoder_bwd_chunk_kernel(float* __restrict__ dwte,
+                                                                float* __restrict__ ws,
+                                                                const E* __restrict__ dx,
+                                                                const uint32_t* __restrict__ keys,
+                                                                int n, int C, int V,
+                                                                int pos_bits) {
+    const int c = blockIdx.x * 4 + (threadIdx.x >> 6);
     const int lane = threadIdx.x & 63;
-    if (i >= n) return;
-    const uint32_t tok = keys[i] >> pos_bits;
-    if (tok >= (uint32_t)V) return;
-    if (i > 0 && (keys[i - 1] >> pos_bits) == tok) return;
+    const int i0 = c * EB_CHUNK;
+    if (i0 >= n) return;
+    const int cnt = min(n - i0, EB_CHUNK);
     const uint32_t pmask = (1u << pos_bits) - 1u;
     const int C4 = C >> 2;
-    float4 acc[NCH];
+    const uint32_t kl = lane < cnt ? keys[i0 + lane] : 0xFFFFFFFFu;
+    const uint32_t tprev = i0 > 0 ? keys[i0 - 1] >> pos_bits : 0xFFFFFFFFu;
+    const uint32_t tnext = i0 + cnt < n ? keys[i0 + cnt] >> pos_bits : 0xFFFFFFFFu;
+    float4 acc[NCH], pre[NCH];
 #pragma unroll
-    for (int c = 0; c < NCH; c++) acc[c] = make_float4(0.f, 0.f, 0.f, 0.f);
-    for (int j = i; j < n && (keys[j] >> pos_bits) == tok; j++) {
-        const E* row = dx + (int64_t)(keys[j] & pmask) * C;
+    for (int ch = 0; ch < NCH; ch++) acc[ch] = make_float4(0.f, 0.f, 0.f, 0.f);
+    uint32_t cur = (uint32_t)__shfl((int)kl, 0, 64) >> pos_bits;
+    int start = 0;  // first key of the current piece, relative to i0
+    // The wte row of the current piece's token is read when the piece starts,
+    // so the read overlaps the piece's own row sums (used if the piece turns
+    // out to be a whole run).
+    auto prefetch = [&]() {
 #pragma unroll
-        for (int c = 0; c < NCH; c++) {
-            const int c4 = lane + 64 * c;
-            if (c4 < C4) {
-                const float4 d = Act<E>::ld(row + 4 * c4);
-                acc[c].x += d.x;
-                acc[c].y += d.y;
-                acc[c].z += d.z;
-                acc[c].w += d.w;
+        for (int ch = 0; ch < NCH; ch++) {
+            const int c4 = lane + 64 * ch;
+            pre[ch] = cur < (uint32_t)V && c4 < C4 ? ld4(dwte + (int64_t)cur * C + 4 * c4)
+                                                   : make_float4(0.f, 0.f, 0.f, 0.f);
+        }
+    };
+    prefetch();
+    // piece [start, end) of token cur, summed in acc
+    auto flush = [&](int end) {
+        if (cur >= (uint32_t)V) return;
+        const bool left = start == 0 && tprev == cur;
+        const bool right = end == cnt && tnext == cur;
+        float* out = (!left && !right) ? dwte + (int64_t)cur * C
+                                       : ws + ((int64_t)c * 2 + (left ? 0 : 1)) * C;
+#pragma unroll
+        for (int ch = 0; ch < NCH; ch++) {
+            const int c4 = lane + 64 * ch;
+            if (c4 >= C4) continue;
+            float4 o = acc[ch];
+            if (!left && !right) {
+                const float4 w = pre[ch];
+                o = make_float4(w.x + o.x, w.y + o.y, w.z + o.z, w.w + o.w);
+            }
+            st4(out + 4 * c4, o);
+        }
+    };
+    for (int g = 0; g < cnt; g += 4) {
+        // the rows of four keys are loaded before any is added
+        uint32_t kk[4];
+        float4 r[4][NCH];
+#pragma unroll
+        for (int u = 0; u < 4; u++) {
+            kk[u] = (uint32_t)__shfl((int)kl, g + u, 64);
+            const bool live = g + u < cnt && (kk[u] >> pos_bits) < (uint32_t)V;
+            const E* row = dx + (int64_t)(kk[u] & pmask) * C;
+#pragma unroll
+            for (int ch = 0; ch < NCH; ch++) {
+                const int c4 = lane + 64 * ch;
+                r[u][ch] = live && c4 < C4 ? Act<E>::ld(row + 4 * c4)
+                                           : make_float4(0.f, 0.f, 0.f, 0.f);
+            }
+        }
+#pragma unroll
+        for (int u = 0; u < 4; u++) {
+            if (g + u >= cnt) break;
+            const uint32_t tok = kk[u] >> pos_bits;
+            if (tok != cur) {
+                flush(g + u);
+#pragma unroll
+                for (int ch = 0; ch < NCH; ch++) acc[ch] = make_float4(0.f, 0.f, 0.f, 0.f);
+                cur = tok;
+                start = g + u;
+                prefetch();
+            }
+#pragma unroll
+            for (int ch = 0; ch < NCH; ch++) {
+                acc[ch].x += r[u][ch].x;
+                acc[ch].y += r[u][ch].y;
+                acc[ch].z += r[u][ch].z;
+                acc[ch].w += r[u][ch].w;
             }
         }
     }
+    flush(cnt);
+}
+
+template <int NCH>
+__global__ __launch_bounds__(256) void encoder_bwd_span_kernel(float* __restrict__ dwte,
+                                                               const float* __restrict__ ws,
+                                                               const uint32_t* __restrict__ keys,
+                                                               int n, int C, int V,
+                                                               int pos_bits) {
+    const int c = blockIdx.x * 4 + (threadIdx.x >> 6);
+    const int lane = threadIdx.x & 63;
+    const int nc = (n + EB_CHUNK - 1) / EB_CHUNK;
+    if (c + 1 >= nc) return;  // no later chunk
+    const int i0 = c * EB_CHUNK, i1 = i0 + EB_CHUNK;
+    const uint32_t tok = keys[i1 - 1] >> pos_bits;
+    if (tok >= (uint32_t)V || (keys[i1] >> pos_bits) != tok) return;
+    // the run started before this chunk: its owner is an earlier chunk
+    if (i0 > 0 && (keys[i0] >> pos_bits) == tok && (keys[i0 - 1] >> pos_bits) == tok) return;
+    // the run's last chunk: the first later chunk not followed by another key of tok
+    int last = -1;
+    for (int base = c + 1; base < nc && last < 0; base += 64) {
+        const int cc = base + lane;
+        bool ends = true;
+        if (cc < nc) {
+            const int next = min(n, (cc + 1) * EB_CHUNK);  // first key after chunk cc
+            ends = next >= n || (keys[next] >> pos_bits) != tok;
+        }
+        const unsigned long long m = __ballot(ends);
+        if (m) last = base + __builtin_ctzll(m);
+    }
+    const int C4 = C >> 2;
+    float4 acc[NCH];
+#pragma unroll
+    for (int ch = 0; ch < NCH; ch++) {
+        const int c4 = lane + 64 * ch;
+        acc[ch] = c4 < C4 ? ld4(ws + ((int64_t)c * 2 + 1) * C + 4 * c4)
+                          : make_float4(0.f, 0.f, 0.f, 0.f);
+    }
+    for (int cc = c + 1; cc <= last; cc += 4) {
+        float4 r[4][NCH];
+#pragma unroll
+        for (int u = 0; u < 4; u++)
+#pragma unroll
+            for (int ch = 0; ch < NCH; ch++) {
+                const int c4 = lane + 64 * ch;
+                r[u][ch] = cc + u <= last && c4 < C4
+                               ? ld4(ws + ((int64_t)(cc + u) * 2) * C + 4 * c4)
+                               : make_float4(0.f, 0.f, 0.f, 0.f);
+            }
+#pragma unroll
+        for (int u = 0; u < 4; u++)
+#pragma unroll
+            for (int ch = 0; ch < NCH; ch++) {
+                acc[ch].x += r[u][ch].x;
+                acc[ch].y += r[u][ch].y;
+                acc[ch].z += r[u][ch].z;
+                acc[ch].w += r[u][ch].w;
+            }
+    }
     float* out = dwte + (int64_t)tok * C;
 #pragma unroll
-    for (int c = 0; c < NCH; c++) {
-        const int c4 = lane + 64 * c;
-        if (c4 < C4) {
-            float4 o = ld4(out + 4 * c4);
-            o.x += acc[c].x;
-            o.y += acc[c].y;
-            o.z += acc[c].z;
-            o.w += acc[c].w;
-            st4(out + 4 * c4, o);
-        }
+    for (int ch = 0; ch < NCH; ch++) {
+        const int c4 = lane + 64 * ch;
+        if (c4 >= C4) continue;
+        float4 o = ld4(out + 4 * c4);
+        o.x += acc[ch].x;
+        o.y += acc[ch].y;
+        o.z += acc[ch].z;
+        o.w += acc[ch].w;
+        st4(out + 4 * c4, o);
     }
 }
 
@@ -546,17 +677,26 @@ hipError_t encoder_sort(hipStream_t s, uint32_t* keys, const int32_t* tok, int n
 }
 
 template <class E>
-hipError_t encoder_backward_t(hipStream_t s, float* dwte, float* dwpe, const E* dx,
+hipError_t encoder_backward_t(hipStream_t s, float* dwte, float* dwpe, float* ws, const E* dx,
                               const uint32_t* keys, int B, int T_, int C, int V, int pos_bits) {
     const int n = B * T_;
-    dim3 grid((n + 3) / 4), block(256);
+    const int nc = (n + EB_CHUNK - 1) / EB_CHUNK;
+    const dim3 grid((nc + 3) / 4), block(256);
+#define EB_CASE(N)                                                                            \
+    case N:                                                                                   \
+        launch((encoder_bwd_chunk_kernel<N, E>), grid, block, 0, s, dwte, ws, dx, keys, n, C, \
+               V, pos_bits);                                                                  \
+        launch((encoder_bwd_span_kernel<N>), grid, block, 0, s, dwte, (const float*)ws, keys, \
+               n, C, V, pos_bits);                                                            \
+        break;
     switch ((C + 255) / 256) {
-        case 1: launch((encoder_bwd_wte_kernel<1, E>), grid, block, 0, s, dwte, dx, keys, n, C, V, pos_bits); break;
-        case 2: launch((encoder_bwd_wte_kernel<2, E>), grid, block, 0, s, dwte, dx, keys, n, C, V, pos_bits); break;
-        case 3: launch((encoder_bwd_wte_kernel<3, E>), grid, block, 0, s, dwte, dx, keys, n, C, V, pos_bits); break;
-        case 4: launch((encoder_bwd_wte_kernel<4, E>), grid, block, 0, s, dwte, dx, keys, n, C, V, pos_bits); break;
+        EB_CASE(1)
+        EB_CASE(2)
+        EB_CASE(3)
+        EB_CASE(4)
         default: return hipErrorInvalidValue;
     }
+#undef EB_CASE
     hipError_t e = hipGetLastError();
     if (e != hipSuccess || !dwpe) return e;  // no position table (rotary model)
     const int64_t nw = (int64_t)T_ * (C / 4);
@@ -565,13 +705,15 @@ hipError_t encoder_backward_t(hipStream_t s, float* dwte, float* dwpe, const E* 
     return hipGetLastError();
 }
 
-hipError_t encoder_backward(hipStream_t s, float* dwte, float* dwpe, const void* dx,
+hipError_t encoder_backward(hipStream_t s, float* dwte, float* dwpe, float* ws, const void* dx,
                             const uint32_t* keys, int B, int T, int C, int V, int pos_bits,
                             int dt) {
     if (B * T <= 0) return hipSuccess;
+    static_assert(EB_CHUNK == kEmbedChunk, "chunk of the embedding backward");
     return by_dt(dt, [&](auto e) {
         using E = decltype(e);
-        return encoder_backward_t<E>(s, dwte, dwpe, (const E*)dx, keys, B, T, C, V, pos_bits);
+        return encoder_backward_t<E>(s, dwte, dwpe, ws, (const E*)dx, keys, B, T, C, V,
+                                     pos_bits);
     });
 }
 

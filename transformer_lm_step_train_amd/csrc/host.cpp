@@ -169,6 +169,7 @@ void Layout::build(const gpt2_config* c, int cus, bool with_guards) {
     attn_d = take("att_rowdot", (size_t)M * NH * f);
     ln_part = take("ln_partials", gk::layernorm_partials_floats(M, C) * f);
     bias_part = take("bias_partials", gk::bias_partials_floats(M, 4 * C) * f);
+    embed_part = take("embed_partials", gk::embed_partials_floats(M, C) * f);
     // the largest split-K workspace over every matmul of the step
     gemm_ws_bytes = 0;
     auto need = [&](int op, int epi, int mm, int n, int k) {
@@ -201,21 +202,33 @@ constexpr char kCkptMagic[8] = {'G', 'P', 'T', '2', 'C', 'K', 'P', 'T'};
 void ckpt_header_make(CkptHeader* h, int precision, int64_t nparams, int64_t step) {
     std::memset(h, 0, sizeof *h);
     std::memcpy(h->magic, kCkptMagic, 8);
-    h->version = 1;
+    h->version = kCkptVersion;
     h->precision = (uint32_t)precision;
     h->nparams = nparams;
     h->step = step;
 }
 
 int ckpt_header_check(const CkptHeader* h, size_t got, int64_t nparams, const char* path) {
-    if (got != sizeof *h || std::memcmp(h->magic, kCkptMagic, 8) != 0 || h->version != 1)
-        return fail(GPT2_EINVAL, "%s is not a version-1 checkpoint", path);
+    if (got != sizeof *h || std::memcmp(h->magic, kCkptMagic, 8) != 0 ||
+        (h->version != 1 && h->version != 2))
+        return fail(GPT2_EINVAL, "%s is not a version-1 or -2 checkpoint", path);
     if (h->precision > (uint32_t)GPT2_F16_MIXED)
         return fail(GPT2_EINVAL, "%s: unknown precision %u", path, h->precision);
     if (h->step < 0) return fail(GPT2_EINVAL, "%s: negative step %lld", path, (long long)h->step);
     if (h->nparams != nparams)
         return fail(GPT2_EINVAL, "checkpoint holds %lld parameters, the model %lld",
                     (long long)h->nparams, (long long)nparams);
+    return GPT2_OK;
+}
+
+int ckpt_scale_check(const CkptScale* s, size_t got, uint32_t precision, const char* path) {
+    if (got != sizeof *s) return fail(GPT2_EINVAL, "%s: truncated loss-scale block", path);
+    if (s->zero != 0) return fail(GPT2_EINVAL, "%s: malformed loss-scale block", path);
+    if (precision == (uint32_t)GPT2_F16_MIXED &&
+        (!(s->scale >= 1.0f && s->scale < INFINITY) || s->good < 0 || s->growth_interval < 1 ||
+         s->good >= s->growth_interval))
+        return fail(GPT2_EINVAL, "%s: invalid loss-scale state (scale %g, %d of %d)", path,
+                    (double)s->scale, s->good, s->growth_interval);
     return GPT2_OK;
 }
 

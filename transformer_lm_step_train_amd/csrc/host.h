@@ -55,8 +55,8 @@ struct Layout {
     size_t params, grads, m, v, shadow;
     size_t encoded, ln1, ln1_mean, ln1_rstd, qkv, atty, lse, res2, ln2, ln2_mean, ln2_rstd, fch,
         fch_gelu, res3, lnf, lnf_mean, lnf_rstd, logits, losses;
-    size_t dres, dtmp, dqkv, dfch, attn_d, ln_part, bias_part, gemm_ws, keys, tokens, targets,
-        scalars, rope_cs;
+    size_t dres, dtmp, dqkv, dfch, attn_d, ln_part, bias_part, embed_part, gemm_ws, keys, tokens,
+        targets, scalars, rope_cs;
     size_t gemm_ws_bytes, total;
     // Every sub-buffer in allocation order: name, offset, bytes and (with
     // guards) the offset of its guard region.
@@ -72,16 +72,28 @@ struct Layout {
     void build(const gpt2_config* c, int cus, bool with_guards);
 };
 
-// Checkpoint file header (32 bytes, little-endian), then params, m and v.
+// Checkpoint file: a 32-byte header (little-endian); in version 2 the
+// 16-byte loss-scale state of the fp16 model follows; then params, m, v.
 struct CkptHeader {
     char magic[8];
     uint32_t version, precision;
     int64_t nparams, step;
 };
 static_assert(sizeof(CkptHeader) == 32, "checkpoint header is 32 bytes");
+struct CkptScale {
+    float scale;              // the loss scale S (1 for the other models)
+    int32_t good;             // clean updates in a row since S last changed
+    int32_t growth_interval;  // clean updates that double S (0 for the others)
+    uint32_t zero;
+};
+static_assert(sizeof(CkptScale) == 16, "checkpoint scale block is 16 bytes");
+constexpr uint32_t kCkptVersion = 2;
 void ckpt_header_make(CkptHeader* h, int precision, int64_t nparams, int64_t step);
-// GPT2_OK if `got` bytes were read and they hold a version-1 header for
-// nparams parameters; else GPT2_EINVAL naming path.
+// GPT2_OK if `got` bytes were read and they hold a version-1 or -2 header of
+// a known precision for nparams parameters; else GPT2_EINVAL naming path.
 int ckpt_header_check(const CkptHeader* h, size_t got, int64_t nparams, const char* path);
+// GPT2_OK if `got` bytes were read and they hold a scale block that a model of
+// the header's precision can resume from; else GPT2_EINVAL naming path.
+int ckpt_scale_check(const CkptScale* s, size_t got, uint32_t precision, const char* path);
 
 }  // namespace gh

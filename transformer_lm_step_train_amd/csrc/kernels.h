@@ -152,8 +152,10 @@ hipError_t encoder_forward(hipStream_t s, void* out, const int32_t* tok,
 hipError_t encoder_sort_prepare(int n_pow2);
 hipError_t encoder_sort(hipStream_t s, uint32_t* keys, const int32_t* tok,
                         int n, int V, int pos_bits, int n_pow2);
-// dwte[tok] += dx rows (summed in position order), dwpe[t] += sum_b dx.
-hipError_t encoder_backward(hipStream_t s, float* dwte, float* dwpe,
+// dwte[tok] += dx rows (chunks of sorted keys summed in position order, then
+// the chunks of each run in order), dwpe[t] += sum_b dx.  ws holds
+// embed_partials_floats(B*T, C) floats.
+hipError_t encoder_backward(hipStream_t s, float* dwte, float* dwpe, float* ws,
                             const void* dx, const uint32_t* sorted_keys,
                             int B, int T, int C, int V, int pos_bits, int dt);
 

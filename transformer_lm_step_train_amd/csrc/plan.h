@@ -58,4 +58,11 @@ size_t layernorm_partials_floats(int N, int C);
 constexpr int kBiasRows = 64;
 size_t bias_partials_floats(int M, int N);
 
+// Keys per chunk of the embedding backward, and its two partial rows per
+// chunk of M sorted keys.
+constexpr int kEmbedChunk = 16;
+inline size_t embed_partials_floats(int M, int C) {
+    return (size_t)2 * cdiv(M, kEmbedChunk) * C;
+}
+
 }  // namespace gk

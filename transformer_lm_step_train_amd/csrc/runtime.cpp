@@ -491,7 +491,8 @@ int backward_impl(gpt2_model* md) {
                                       C, h));
     }
     LAUNCH(md, GPT2_KC_OTHER, 0, es * M * C + 8.0 * M * C + 8.0 * T * C + 4.0 * M,
-           gk::encoder_backward(s, md->G(P_WTE), y.rope ? nullptr : md->G(P_WPE), dres,
+           gk::encoder_backward(s, md->G(P_WTE), y.rope ? nullptr : md->G(P_WPE),
+                                md->at<float>(y.embed_part), dres,
                                 md->at<uint32_t>(y.keys), B,
                                 T, C, V, y.pos_bits, h));
     return GPT2_OK;
@@ -673,9 +674,11 @@ int gpt2_copy_opt_state(gpt2_model* md, float* hm, float* hv) {
 
 // ---- checkpoint -----------------------------------------------------------
 //
-// File: a 32-byte header {"GPT2CKPT", version 1 (u32), precision (u32),
-// nparams (i64), step (i64)}, then params, m and v as nparams little-endian
-// fp32 each, in the arena order.  Streamed through one host buffer of at most
+// File: a 32-byte header {"GPT2CKPT", version 2 (u32), precision (u32),
+// nparams (i64), step (i64)}, the 16-byte loss-scale block {scale (f32),
+// clean updates (i32), growth interval (i32), 0 (u32)}, then params, m and v
+// as nparams little-endian fp32 each, in the arena order.  Version-1 files
+// (no scale block) still load.  Streamed through one host buffer of at most
 // 16M floats.
 
 namespace {
@@ -718,8 +721,15 @@ int gpt2_save_checkpoint(gpt2_model* md, const char* path, int64_t step) {
     if (!f) return fail(GPT2_EINVAL, "cannot open %s: %s", path, strerror(errno));
     gh::CkptHeader h;
     gh::ckpt_header_make(&h, md->cfg.precision, md->lay.nparams, step);
-    int rc = fwrite(&h, sizeof h, 1, f) == 1 ? ckpt_stream(md, f, true)
-                                             : fail(GPT2_EINVAL, "checkpoint write failed");
+    gh::CkptScale sc{1.0f, 0, 0, 0u};
+    if (md->lay.dt == DT_F16) {  // the dynamic loss-scale state is part of the training state
+        TRY(hip_check(hipMemcpy(&sc.scale, md->lscale(), 4, hipMemcpyDeviceToHost), "scale read"));
+        TRY(hip_check(hipMemcpy(&sc.good, md->lgood(), 4, hipMemcpyDeviceToHost), "scale read"));
+        sc.growth_interval = md->growth_interval;
+    }
+    int rc = fwrite(&h, sizeof h, 1, f) == 1 && fwrite(&sc, sizeof sc, 1, f) == 1
+                 ? ckpt_stream(md, f, true)
+                 : fail(GPT2_EINVAL, "checkpoint write failed");
     if (fclose(f) != 0 && rc == GPT2_OK) rc = fail(GPT2_EINVAL, "checkpoint close failed");
     return rc;
 }
@@ -729,8 +739,11 @@ int gpt2_load_checkpoint(gpt2_model* md, const char* path, int64_t* step) {
     FILE* f = fopen(path, "rb");
     if (!f) return fail(GPT2_EINVAL, "cannot open %s: %s", path, strerror(errno));
     gh::CkptHeader h{};
+    gh::CkptScale sc{1.0f, 0, 0, 0u};
     const size_t got = fread(&h, 1, sizeof h, f);
     int rc = gh::ckpt_header_check(&h, got, md->lay.nparams, path);
+    if (rc == GPT2_OK && h.version >= 2)
+        rc = gh::ckpt_scale_check(&sc, fread(&sc, 1, sizeof sc, f), h.precision, path);
     if (rc == GPT2_OK) rc = hip_check(hipStreamSynchronize(md->stream), "synchronize");
     if (rc == GPT2_OK) rc = ckpt_stream(md, f, false);
     if (rc == GPT2_OK && fgetc(f) != EOF) rc = fail(GPT2_EINVAL, "checkpoint has trailing bytes");
@@ -741,6 +754,15 @@ int gpt2_load_checkpoint(gpt2_model* md, const char* path, int64_t* step) {
                                   md->lay.nparams, md->lay.dt),
                       "16-bit weight copy"));
         TRY(hip_check(hipStreamSynchronize(md->stream), "synchronize"));
+    }
+    if (md->lay.dt == DT_F16 && h.version >= 2 && h.precision == (uint32_t)GPT2_F16_MIXED) {
+        // resume the saved loss-scale schedule (an fp32 or bf16 file leaves
+        // the fp16 model's current schedule as it is)
+        const int32_t st[3] = {sc.good, 0, 0};  // good, found, skipped
+        TRY(hip_check(hipMemcpy(md->lscale(), &sc.scale, 4, hipMemcpyHostToDevice),
+                      "scale write"));
+        TRY(hip_check(hipMemcpy(md->lgood(), st, 12, hipMemcpyHostToDevice), "scale write"));
+        md->growth_interval = sc.growth_interval;
     }
     if (step) *step = h.step;
     return GPT2_OK;
