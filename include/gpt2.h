@@ -215,8 +215,13 @@ GPT2_API int gpt2_sample(gpt2_model* model, int b, int t, float coin, int32_t* t
  * prompt (host, ids in [0, V)); for t = prompt_len .. n-1 it runs a forward
  * of tokens[0 .. t) (B = 1, T = t, no targets) and writes
  * gpt2_sample(0, t-1, coins[t - prompt_len]) to tokens[t].  coins holds
- * n - prompt_len uniforms in [0, 1).  Every step recomputes the whole prefix
- * (no key/value cache).  Requires 1 <= prompt_len
+ * n - prompt_len uniforms in [0, 1).  The first step runs the whole prompt;
+ * every later step runs only the newest position, reading the keys and
+ * values of the earlier positions from the activations the previous steps
+ * left (a key/value cache in the arena), so the logits equal those of a
+ * whole forward bit for bit.  Afterwards the activations are those of a
+ * forward of tokens[0 .. n-1), except att_lse (scratch here).  Requires
+ * 1 <= prompt_len
  * <= n <= seq_len of the config.  Errors as gpt2_forward / gpt2_sample; on
  * error tokens[prompt_len .. n) may be partly written. */
 GPT2_API int gpt2_generate(gpt2_model* model, int32_t* tokens, int prompt_len, int n,

@@ -160,3 +160,33 @@ def test_generate_bf16_valid_and_deterministic():
         o.close()
     assert np.array_equal(outs[0], outs[1])
     assert np.all((outs[0] >= 0) & (outs[0] < c["V"]))
+
+
+@pytest.mark.parametrize("name,prec,prompt_len", [("ragged", "fp32", 1), ("ragged", "bf16", 5),
+                                                  ("tiny_rope", "fp32", 3),
+                                                  ("small", "fp16", 130)])
+def test_cached_generation_equals_whole_forward(name, prec, prompt_len):
+    """gpt2_generate runs only the newest position after the prompt, with
+    the earlier positions' keys and values read from the activations: its
+    last logits row and every layer's activations of that row equal a whole
+    forward of the same tokens bit for bit (query blocks of 128 rows: the
+    small case crosses from the first block into the second and third)."""
+    g = gpt2()
+    c = synth.CONFIGS[name]
+    p = {"fp32": g.GPT2_FP32, "bf16": g.GPT2_BF16_MIXED, "fp16": g.GPT2_F16_MIXED}[prec]
+    n = c["maxT"]
+    rope = c.get("rope", False)
+    m = g.Model(c["L"], c["C"], c["NH"], c["V"], c["maxT"], 1, n, precision=p, rope=rope)
+    m.set_params(synth.init_params(c["L"], c["C"], c["V"], c["maxT"], rope=rope))
+    prompt = synth.token_stream(1, prompt_len, c["V"])[0][0]
+    toks = m.generate(prompt, n, synth.coins(n - prompt_len))
+    assert np.array_equal(toks[:prompt_len], prompt)
+    names = ("ln1", "qkv", "atty", "residual2", "fch_gelu", "residual3")
+    cached = {(k, l): m.activation(k, l).copy() for k in names for l in range(c["L"])}
+    cached_logits = m.activation("logits").copy()
+    m.forward(toks[None, :n - 1])
+    whole = {(k, l): m.activation(k, l) for k in names for l in range(c["L"])}
+    assert np.array_equal(cached_logits, m.activation("logits"))
+    for key in cached:
+        assert np.array_equal(cached[key], whole[key]), key
+    m.close()

@@ -111,7 +111,7 @@ template <int HS, class E>
 __global__ __launch_bounds__(256, 2) void attn_fwd_kernel(E* __restrict__ out,
                                                           float* __restrict__ lse,
                                                           const E* __restrict__ qkv, int T,
-                                                          int C, int NH, float qscale) {
+                                                          int C, int NH, float qscale, int qb0) {
     constexpr int LD = HS + 4, HALF = HS / 2, NDB = (HS + 31) / 32;
     constexpr int LDT = AT + 4;        // V^T row stride (keys)
     constexpr int VROWS = NDB * 32;    // V^T rows (head dims, padded to 32)
@@ -120,9 +120,10 @@ __global__ __launch_bounds__(256, 2) void attn_fwd_kernel(E* __restrict__ out,
 
     // Longest-first over the whole grid: all heads' last query blocks (the
     // most key tiles) are dispatched first, the first blocks fill the tail.
-    // Plain round-robin dispatch then gives every XCD the same mix.
+    // Plain round-robin dispatch then gives every XCD the same mix.  Query
+    // blocks before qb0 are not computed (their rows are already stored).
     const int nqb = (T + AQ - 1) / AQ;
-    const int nbh = gridDim.x / nqb;
+    const int nbh = gridDim.x / (nqb - qb0);
     const int bh = blockIdx.x % nbh;
     const int qb = nqb - 1 - blockIdx.x / nbh;
     if (VROWS > HS) {  // padding rows of V^T stay zero
@@ -531,11 +532,12 @@ __global__ __launch_bounds__(256, 2) void attn_bwd_dkdv_kernel(
 
 template <int HS, class E>
 hipError_t fwd_hs(hipStream_t s, E* out, float* lse, const E* qkv, int B, int T, int C,
-                  int NH) {
+                  int NH, int q_first) {
     const int nqb = (T + AQ - 1) / AQ;
+    const int qb0 = q_first / AQ;
     const float qscale = LOG2E / sqrtf((float)HS);
-    launch((attn_fwd_kernel<HS, E>), dim3(B * NH * nqb), dim3(256), 0, s, out, lse,
-                       qkv, T, C, NH, qscale);
+    launch((attn_fwd_kernel<HS, E>), dim3(B * NH * (nqb - qb0)), dim3(256), 0, s, out, lse,
+           qkv, T, C, NH, qscale, qb0);
     return hipGetLastError();
 }
 
@@ -554,11 +556,11 @@ hipError_t bwd_hs(hipStream_t s, E* dqkv, float* D, const E* dout, const E* qkv,
 
 template <class E>
 hipError_t forward_t(hipStream_t s, E* out, float* lse, const E* qkv, int B, int T, int C,
-                     int NH) {
+                     int NH, int q_first) {
     switch (C / NH) {
-        case 16: return fwd_hs<16, E>(s, out, lse, qkv, B, T, C, NH);
-        case 32: return fwd_hs<32, E>(s, out, lse, qkv, B, T, C, NH);
-        case 64: return fwd_hs<64, E>(s, out, lse, qkv, B, T, C, NH);
+        case 16: return fwd_hs<16, E>(s, out, lse, qkv, B, T, C, NH, q_first);
+        case 32: return fwd_hs<32, E>(s, out, lse, qkv, B, T, C, NH, q_first);
+        case 64: return fwd_hs<64, E>(s, out, lse, qkv, B, T, C, NH, q_first);
         default: return hipErrorInvalidValue;
     }
 }
@@ -577,12 +579,13 @@ hipError_t backward_t(hipStream_t s, E* dqkv, float* D, const E* dout, const E* 
 }  // namespace
 
 hipError_t attention_forward(hipStream_t s, void* out, float* lse, const void* qkv, int B, int T,
-                             int C, int NH, int dt) {
+                             int C, int NH, int dt, int q_first) {
     if (B <= 0 || T <= 0) return hipSuccess;
+    if (q_first < 0 || q_first >= T) return hipErrorInvalidValue;
     if (dt != DT_F32)
         return attention_forward_half(s, (uint16_t*)out, lse, (const uint16_t*)qkv, B, T, C, NH,
-                                      dt);
-    return forward_t<float>(s, (float*)out, lse, (const float*)qkv, B, T, C, NH);
+                                      dt, q_first);
+    return forward_t<float>(s, (float*)out, lse, (const float*)qkv, B, T, C, NH, q_first);
 }
 
 hipError_t attention_backward(hipStream_t s, void* dqkv, float* dpre, const void* dout,

@@ -153,13 +153,15 @@ template <int HS, class H>
 __global__ __launch_bounds__(256, 2) void attn16_fwd_kernel(uint16_t* __restrict__ out,
                                                             float* __restrict__ lse,
                                                             const uint16_t* __restrict__ qkv,
-                                                            int T, int C, int NH, float qscale) {
+                                                            int T, int C, int NH, float qscale,
+                                                            int qb0) {
     constexpr int NKS = HS / 16, NDB = (HS + 31) / 32, LDK = NDB * 32 + 8;
     __shared__ __attribute__((aligned(16))) uint16_t ks[2][RT * LDK];
     __shared__ __attribute__((aligned(16))) uint16_t vs[2][RT * LDK];
 
+    // query blocks before qb0 are not computed (their rows are already stored)
     const int nqb = (T + RQ - 1) / RQ;
-    const int nbh = gridDim.x / nqb;
+    const int nbh = gridDim.x / (nqb - qb0);
     const int bh = blockIdx.x % nbh;
     const int qb = nqb - 1 - blockIdx.x / nbh;  // longest first
     const int b = bh / NH, h = bh - b * NH;
@@ -504,22 +506,23 @@ hipError_t bwd16(hipStream_t s, uint16_t* dqkv, float* D, const uint16_t* dout,
 
 template <int HS, class H>
 hipError_t fwd16(hipStream_t s, uint16_t* out, float* lse, const uint16_t* qkv, int B, int T,
-                 int C, int NH) {
+                 int C, int NH, int q_first) {
     const int nqb = (T + RQ - 1) / RQ;
+    const int qb0 = q_first / RQ;
     const float qscale = L2E / sqrtf((float)HS);
-    launch((attn16_fwd_kernel<HS, H>), dim3(B * NH * nqb), dim3(256), 0, s, out, lse,
-                       qkv, T, C, NH, qscale);
+    launch((attn16_fwd_kernel<HS, H>), dim3(B * NH * (nqb - qb0)), dim3(256), 0, s, out, lse,
+           qkv, T, C, NH, qscale, qb0);
     return hipGetLastError();
 }
 
 
 template <class H>
 hipError_t fwd_h(hipStream_t s, uint16_t* out, float* lse, const uint16_t* qkv, int B, int T,
-                 int C, int NH) {
+                 int C, int NH, int q_first) {
     switch (C / NH) {
-        case 16: return fwd16<16, H>(s, out, lse, qkv, B, T, C, NH);
-        case 32: return fwd16<32, H>(s, out, lse, qkv, B, T, C, NH);
-        case 64: return fwd16<64, H>(s, out, lse, qkv, B, T, C, NH);
+        case 16: return fwd16<16, H>(s, out, lse, qkv, B, T, C, NH, q_first);
+        case 32: return fwd16<32, H>(s, out, lse, qkv, B, T, C, NH, q_first);
+        case 64: return fwd16<64, H>(s, out, lse, qkv, B, T, C, NH, q_first);
         default: return hipErrorInvalidValue;
     }
 }
@@ -539,10 +542,11 @@ hipError_t bwd_h(hipStream_t s, uint16_t* dqkv, float* D, const uint16_t* dout,
 }  // namespace
 
 hipError_t attention_forward_half(hipStream_t s, uint16_t* out, float* lse, const uint16_t* qkv,
-                                  int B, int T, int C, int NH, int dt) {
+                                  int B, int T, int C, int NH, int dt, int q_first) {
     if (B <= 0 || T <= 0) return hipSuccess;
-    return dt == DT_F16 ? fwd_h<HF16>(s, out, lse, qkv, B, T, C, NH)
-                        : fwd_h<HBF16>(s, out, lse, qkv, B, T, C, NH);
+    if (q_first < 0 || q_first >= T) return hipErrorInvalidValue;
+    return dt == DT_F16 ? fwd_h<HF16>(s, out, lse, qkv, B, T, C, NH, q_first)
+                        : fwd_h<HBF16>(s, out, lse, qkv, B, T, C, NH, q_first);
 }
 
 hipError_t attention_backward_half(hipStream_t s, uint16_t* dqkv, float* D,

@@ -87,15 +87,18 @@ hipError_t gemm(hipStream_t s, const GemmArgs& a, float* workspace,
 // scaled score row; backward reads dout and writes dqkv (B*T, 3C), using
 // dpre (B, NH, T) as scratch for rowsum(dout * out).
 // Activations are stored per dt (DT_F32, DT_BF16, DT_F16); lse and D fp32.
+// q_first: rows before it are left as they are (their keys and values are
+// read, their outputs not recomputed: whole 128-row blocks before it are
+// skipped, and rows of its own block are rewritten with the same values).
 hipError_t attention_forward(hipStream_t s, void* out, float* lse, const void* qkv, int B,
-                             int T, int C, int NH, int dt);
+                             int T, int C, int NH, int dt, int q_first = 0);
 hipError_t attention_backward(hipStream_t s, void* dqkv, float* dpre, const void* dout,
                               const void* qkv, const void* out, const float* lse, int B,
                               int T, int C, int NH, int dt);
 // Mixed-precision attention on the 16-bit matrix cores (all tensors bf16 or
 // fp16 bits per dt, lse and D fp32).
 hipError_t attention_forward_half(hipStream_t s, uint16_t* out, float* lse, const uint16_t* qkv,
-                                  int B, int T, int C, int NH, int dt);
+                                  int B, int T, int C, int NH, int dt, int q_first);
 hipError_t attention_backward_half(hipStream_t s, uint16_t* dqkv, float* D,
                                    const uint16_t* dout, const uint16_t* qkv,
                                    const uint16_t* out, const float* lse, int B, int T, int C,

@@ -268,35 +268,47 @@ int run_gemm(gpt2_model* md, const Mm& x) {
 // alone (evaluation: the logits stay, no backward state).
 enum FwdMode { FWD_INFER = 0, FWD_TRAIN = 1, FWD_EVAL = 2 };
 
+// Rows before r0 (only with B = 1 and no targets) are taken as already
+// computed for the same leading tokens by an earlier forward: every row-wise
+// kernel starts at row r0, and attention reads the keys and values of all T
+// rows from the qkv activations (a key/value cache) but computes only the
+// outputs from r0's query block on.  Each row's arithmetic is the same as in
+// a whole forward, so the results are identical.
 int forward_impl(gpt2_model* md, const int32_t* tok, const int32_t* tgt, int B, int T,
-                 int mode) {
+                 int mode, int r0 = 0) {
     const Layout& y = md->lay;
-    const int L = y.L, C = y.C, NH = y.NH, V = y.V, M = B * T;
+    const int L = y.L, C = y.C, NH = y.NH, V = y.V;
+    const int M = B * T - r0;  // rows computed
+    const size_t ro = (size_t)r0;
     const int h = y.dt;
     const size_t MC = (size_t)y.M * C;  // per-layer capacity stride, elements
     const double es = (double)y.es;
     hipStream_t s = md->stream;
-    void* enc = md->A(y.encoded);
+    void* enc = md->A(y.encoded, ro * C);
+    const int hsz = C / NH;
 
     LAUNCH(md, GPT2_KC_OTHER, 0, 4.0, gk::fill_zero(s, (float*)md->flag(), 1));
     LAUNCH(md, GPT2_KC_OTHER, 0, 8.0 * M * C + es * M * C + 4.0 * M,
-           gk::encoder_forward(s, enc, tok, md->P(P_WTE), y.rope ? nullptr : md->P(P_WPE), B, T, C,
-                               V, md->flag(), h));
+           gk::encoder_forward(s, enc, tok + ro, md->P(P_WTE),
+                               y.rope ? nullptr : md->P(P_WPE) + ro * C, B, T - r0, C, V,
+                               md->flag(), h));
     for (int l = 0; l < L; l++) {
-        const void* resid = l == 0 ? enc : (const void*)md->A(y.res3, (l - 1) * MC);
-        void* ln1 = md->A(y.ln1, l * MC);
-        float* ln1m = md->at<float>(y.ln1_mean) + (size_t)l * y.M;
-        float* ln1r = md->at<float>(y.ln1_rstd) + (size_t)l * y.M;
-        void* qkv = md->A(y.qkv, l * 3 * MC);
-        void* atty = md->A(y.atty, l * MC);
+        const void* resid = l == 0 ? enc : (const void*)md->A(y.res3, (l - 1) * MC + ro * C);
+        void* ln1 = md->A(y.ln1, l * MC + ro * C);
+        float* ln1m = md->at<float>(y.ln1_mean) + (size_t)l * y.M + ro;
+        float* ln1r = md->at<float>(y.ln1_rstd) + (size_t)l * y.M + ro;
+        void* qkv_l = md->A(y.qkv, l * 3 * MC);
+        void* qkv = md->A(y.qkv, l * 3 * MC + ro * 3 * C);
+        void* atty_l = md->A(y.atty, l * MC);
+        void* atty = md->A(y.atty, l * MC + ro * C);
         float* lse = md->at<float>(y.lse) + (size_t)l * y.M * NH;
-        void* res2 = md->A(y.res2, l * MC);
-        void* ln2 = md->A(y.ln2, l * MC);
-        float* ln2m = md->at<float>(y.ln2_mean) + (size_t)l * y.M;
-        float* ln2r = md->at<float>(y.ln2_rstd) + (size_t)l * y.M;
-        void* fch = md->A(y.fch, l * 4 * MC);
-        void* fchg = md->A(y.fch_gelu, l * 4 * MC);
-        void* res3 = md->A(y.res3, l * MC);
+        void* res2 = md->A(y.res2, l * MC + ro * C);
+        void* ln2 = md->A(y.ln2, l * MC + ro * C);
+        float* ln2m = md->at<float>(y.ln2_mean) + (size_t)l * y.M + ro;
+        float* ln2r = md->at<float>(y.ln2_rstd) + (size_t)l * y.M + ro;
+        void* fch = md->A(y.fch, l * 4 * MC + ro * 4 * C);
+        void* fchg = md->A(y.fch_gelu, l * 4 * MC + ro * 4 * C);
+        void* res3 = md->A(y.res3, l * MC + ro * C);
 
         LAUNCH(md, GPT2_KC_LAYERNORM, 0, es * 2.0 * M * C + 8.0 * M,
                gk::layernorm_forward(s, ln1, ln1m, ln1r, resid, md->P(P_LN1W) + l * C,
@@ -307,12 +319,14 @@ int forward_impl(gpt2_model* md, const int32_t* tok, const int32_t* tgt, int B, 
         TRY(run_gemm(md, a));
         if (y.rope)
             LAUNCH(md, GPT2_KC_OTHER, 0, es * 4.0 * M * C,
-                   gk::rope_apply(s, qkv, md->at<float>(y.rope_cs), B, T, C, NH, 1, h));
+                   gk::rope_apply(s, qkv, md->at<float>(y.rope_cs) + ro * hsz, B, T - r0, C, NH,
+                                  1, h));
         {
-            const double hs = C / NH;
-            const double flops = 4.0 * B * NH * hs * (double)T * (T + 1) / 2.0;
+            const double hs = hsz;
+            const double rows = (double)T * (T + 1) / 2.0 - (double)r0 * (r0 + 1) / 2.0;
+            const double flops = 4.0 * B * NH * hs * rows;
             LAUNCH(md, GPT2_KC_ATTENTION, flops, es * 4.0 * M * C + 4.0 * M * NH,
-                   gk::attention_forward(s, atty, lse, qkv, B, T, C, NH, h));
+                   gk::attention_forward(s, atty_l, lse, qkv_l, B, T, C, NH, h, r0));
         }
         a = mm(gk::GEMM_NT, gk::EPI_RESID, M, C, C, atty, C,
                (const char*)md->W(P_ATTPROJW) + (size_t)l * C * C * y.es, C, res2, C);
@@ -335,12 +349,13 @@ int forward_impl(gpt2_model* md, const int32_t* tok, const int32_t* tgt, int B, 
         a.ldaux = C;
         TRY(run_gemm(md, a));
     }
-    const void* last = md->A(y.res3, (L - 1) * MC);
-    void* lnf = md->A(y.lnf);
+    const void* last = md->A(y.res3, (L - 1) * MC + ro * C);
+    void* lnf = md->A(y.lnf, ro * C);
     LAUNCH(md, GPT2_KC_LAYERNORM, 0, es * 2.0 * M * C + 8.0 * M,
-           gk::layernorm_forward(s, lnf, md->at<float>(y.lnf_mean), md->at<float>(y.lnf_rstd),
-                                 last, md->P(P_LNFW), md->P(P_LNFB), M, C, h));
-    void* logits = md->A(y.logits);
+           gk::layernorm_forward(s, lnf, md->at<float>(y.lnf_mean) + ro,
+                                 md->at<float>(y.lnf_rstd) + ro, last, md->P(P_LNFW),
+                                 md->P(P_LNFB), M, C, h));
+    void* logits = md->A(y.logits, ro * y.Vp);
     TRY(run_gemm(md, mm(gk::GEMM_NT, gk::EPI_STORE, M, V, C, lnf, C, md->W(P_WTE), C, logits,
                         y.Vp)));
     const bool train = mode == FWD_TRAIN;
@@ -930,8 +945,13 @@ int gpt2_generate(gpt2_model* md, int32_t* tokens, int prompt_len, int n, const 
     if (prompt_len < 1 || n < prompt_len || n > md->lay.Tmax)
         return fail(GPT2_EINVAL, "prompt_len=%d n=%d outside 1 <= prompt_len <= n <= %d",
                     prompt_len, n, md->lay.Tmax);
+    // The prompt's forward, then one new position per drawn token: the rows
+    // of the earlier positions, kept in the activation arena, serve as the
+    // key/value cache.
     for (int t = prompt_len; t < n; t++) {
-        TRY(gpt2_forward(md, tokens, nullptr, 1, t, nullptr));
+        int32_t *dtok, *dtgt;
+        TRY(stage_ids(md, tokens, nullptr, 1, t, &dtok, &dtgt));
+        TRY(forward_impl(md, dtok, nullptr, 1, t, FWD_INFER, t == prompt_len ? 0 : t - 1));
         TRY(gpt2_sample(md, 0, t - 1, coins[t - prompt_len], tokens + t));
     }
     return GPT2_OK;
