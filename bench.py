@@ -55,9 +55,10 @@ def parse():
 
 
 def source_hash():
-    """SHA-256 of the fp32 matmul kernel's sources (kernel and its helpers)."""
+    """SHA-256 of the fp32 matmul kernel's sources (kernel, its helpers and
+    the split plans, which decide the tile order)."""
     h = hashlib.sha256()
-    for f in ("gemm.hip", "common.h"):
+    for f in ("gemm.hip", "common.h", "plan.cpp", "plan.h"):
         h.update(open(os.path.join(ROOT, "transformer_lm_step_train_amd", "csrc", f), "rb").read())
     return h.hexdigest()
 

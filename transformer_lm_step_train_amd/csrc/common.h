@@ -79,6 +79,24 @@ __device__ __forceinline__ int xcd_remap(int wg, int n) {
     return wg < (q << 3) ? (wg & 7) * q + (wg >> 3) : wg;
 }
 
+// Tile and K-split index of a split-K workgroup (grid: tiles x 1 x nz).
+// With nz a multiple of 8 each XCD takes whole K chunks: XCD x runs every
+// tile of chunks x, x + 8, ... in tile order, so the workgroups resident on
+// one XCD read the same A and B chunk panels through its L2.  Otherwise the
+// tiles of each chunk are spread by xcd_remap.  Bijective on both forms.
+__device__ __forceinline__ void split_remap(int bx, int bz, int tiles, int nz, int& tile,
+                                            int& kz) {
+    if (nz > 1 && (nz & 7) == 0) {
+        const int lin = bx + tiles * bz;  // dispatch order
+        const int j = lin >> 3;
+        kz = (lin & 7) + 8 * (j / tiles);
+        tile = j - (j / tiles) * tiles;
+    } else {
+        kz = bz;
+        tile = xcd_remap(bx, tiles);
+    }
+}
+
 // ---- 16-bit storage -------------------------------------------------------
 #include "dtype.h"
 

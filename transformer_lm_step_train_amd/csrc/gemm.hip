@@ -139,7 +139,7 @@ template <int EPI>
 __device__ __forceinline__ float4 epi_store(const GemmArgs& a, float* __restrict__ partial,
                                             int row, int col, float4 v) {
     if (EPI == EPI_PARTIAL) {
-        st4(partial + (int64_t)blockIdx.z * a.M * a.N + (int64_t)row * a.N + col, v);
+        st4(partial + (int64_t)row * a.N + col, v);
         return v;
     }
     float* c = a.C + (int64_t)row * a.ldc + col;
@@ -173,7 +173,7 @@ template <int EPI>
 __device__ __forceinline__ float epi_scalar(const GemmArgs& a, float* __restrict__ partial,
                                             int row, int col, float v) {
     if (EPI == EPI_PARTIAL) {
-        partial[(int64_t)blockIdx.z * a.M * a.N + (int64_t)row * a.N + col] = v;
+        partial[(int64_t)row * a.N + col] = v;
         return v;
     }
     const int64_t idx = (int64_t)row * a.ldc + col;
@@ -205,7 +205,8 @@ __global__ __launch_bounds__(NTHR, BK == 16 ? 3 : 2) void gemm_kernel(
     constexpr int SMEM = MAIN > EPIF ? MAIN : EPIF;
     __shared__ __attribute__((aligned(16))) float sm[SMEM];
 
-    const int tile = xcd_remap(blockIdx.x, tiles_m * tiles_n);
+    int tile, kz;
+    split_remap(blockIdx.x, blockIdx.z, tiles_m * tiles_n, gridDim.z, tile, kz);
     constexpr int GM = 8;
     const int per_group = GM * tiles_n;
     const int group = tile / per_group;
@@ -215,7 +216,9 @@ __global__ __launch_bounds__(NTHR, BK == 16 ? 3 : 2) void gemm_kernel(
     const int m0 = (first_m + in_g % gm) * BM;
     const int n0 = (in_g / gm) * BN;
 
-    const int k_begin = blockIdx.z * kchunk;
+    const int k_begin = kz * kchunk;
+    // this split's partial-sum slice (EPI_PARTIAL)
+    float* const part = EPI == EPI_PARTIAL ? partial + (int64_t)kz * a.M * a.N : nullptr;
     const int k_end = min(a.K, k_begin + kchunk);
 
     const int lane = threadIdx.x & 63, wave = threadIdx.x >> 6;
@@ -334,11 +337,11 @@ __global__ __launch_bounds__(NTHR, BK == 16 ? 3 : 2) void gemm_kernel(
             if (row >= a.M) continue;
             float4 o = make_float4(0.f, 0.f, 0.f, 0.f);
             if (col + 3 < a.N) {
-                o = epi_store<EPI>(a, partial, row, col, v);
+                o = epi_store<EPI>(a, part, row, col, v);
             } else {
-                if (col < a.N) o.x = epi_scalar<EPI>(a, partial, row, col, v.x);
-                if (col + 1 < a.N) o.y = epi_scalar<EPI>(a, partial, row, col + 1, v.y);
-                if (col + 2 < a.N) o.z = epi_scalar<EPI>(a, partial, row, col + 2, v.z);
+                if (col < a.N) o.x = epi_scalar<EPI>(a, part, row, col, v.x);
+                if (col + 1 < a.N) o.y = epi_scalar<EPI>(a, part, row, col + 1, v.y);
+                if (col + 2 < a.N) o.z = epi_scalar<EPI>(a, part, row, col + 2, v.z);
             }
             if (csum) {
                 cs.x += o.x;
