@@ -490,7 +490,8 @@ struct TileT32 {
 };
 
 // NT, or NN with the B operand read through the transposing loads.
-template <int OP, int EPI, class H>
+// NT, or NN with the B operand read through the transposing loads.
+template <int OP, int EPI, class H, int PF>
 __global__ __launch_bounds__(NTHR, 3) void gemm_bf16_k32_kernel(const GemmArgsH a, int tiles_m,
                                                                int tiles_n) {
     static_assert(OP == GEMM_NT || OP == GEMM_NN, "NT, or NN with the transposing reads");
@@ -524,8 +525,11 @@ __global__ __launch_bounds__(NTHR, 3) void gemm_bf16_k32_kernel(const GemmArgsH 
 #pragma unroll
             for (int e = 0; e < 16; e++) acc[i][j][e] = 0.f;
 
-    TA ta[2];
-    TB tb[2];
+    // PF register slots of global loads in flight: the loads of step kt + PF
+    // are issued while step kt computes
+    static_assert(PF == 2 || PF == 3, "prefetch depth");
+    TA ta[PF];
+    TB tb[PF];
     const int nfull = a.K / SBK;
     auto issue = [&](auto slotc, int kt) {
         constexpr int S = decltype(slotc)::value;
@@ -554,18 +558,23 @@ __global__ __launch_bounds__(NTHR, 3) void gemm_bf16_k32_kernel(const GemmArgsH 
     };
     using I0 = std::integral_constant<int, 0>;
     using I1 = std::integral_constant<int, 1>;
+    using I2 = std::integral_constant<int, 2 % PF>;
     if (nfull > 0) {
         issue(I0{}, 0);
         ta[0].store(smh);
         tb[0].store(smh + 2 * TA::ELEMS);
         issue(I1{}, 1);
+        if constexpr (PF == 3) issue(I2{}, 2);
     }
     __syncthreads();
+    // Step kt computes from LDS buffer kt & 1, issues step kt + PF's loads
+    // into the slot that held step kt, and stores step kt + 1 (slot
+    // (kt + 1) % PF) into the other buffer.
     auto step = [&](int kt, auto slotc) {
         constexpr int S = decltype(slotc)::value;
-        constexpr int NS = S ^ 1;
+        constexpr int NS = (S + 1) % PF;
         const int cur = kt & 1;
-        issue(slotc, kt + 2);
+        issue(slotc, kt + PF);
         compute(smh + cur * TA::ELEMS, smh + 2 * TA::ELEMS + cur * TB::ELEMS);
         // unconditional: no path reaches the next loads with this slot pending
         ta[NS].store(smh + (cur ^ 1) * TA::ELEMS);
@@ -573,11 +582,15 @@ __global__ __launch_bounds__(NTHR, 3) void gemm_bf16_k32_kernel(const GemmArgsH 
         __syncthreads();
     };
     int kt = 0;
-    for (; kt + 1 < nfull; kt += 2) {
+    for (; kt + PF <= nfull; kt += PF) {
         step(kt, I0{});
         step(kt + 1, I1{});
+        if constexpr (PF == 3) step(kt + 2, I2{});
     }
-    if (kt < nfull) step(kt, I0{});
+    if (kt < nfull) step(kt++, I0{});
+    if constexpr (PF == 3) {
+        if (kt < nfull) step(kt++, I1{});
+    }
     if (nfull * SBK < a.K) {  // partial last step, zero-padded
         const int kk = nfull * SBK;
         ta[0].template load<true>(a.A, a.lda, m0, a.M, kk, a.K);
@@ -979,16 +992,21 @@ template <int OP, int EPI, class H>
 hipError_t launch_h(hipStream_t s, const GemmArgsH& a, float* ws) {
     const int tm = cdiv(a.M, BM), tn = cdiv(a.N, BN);
     // 32-deep steps at three workgroups per CU: the forward products with a
-    // short reduction and the input gradients that take the transposing reads
-    if constexpr (OP == GEMM_NT) {
-        if (a.K < 2048) {
-            launch((gemm_bf16_k32_kernel<OP, EPI, H>), dim3(tm * tn), dim3(NTHR), 0, s, a, tm, tn);
-            return hipGetLastError();
-        }
-    }
-    if constexpr (OP == GEMM_NN) {
-        if (a.ldb % 8 == 0 && ((uintptr_t)a.B & 15) == 0) {
-            launch((gemm_bf16_k32_kernel<OP, EPI, H>), dim3(tm * tn), dim3(NTHR), 0, s, a, tm, tn);
+    // short reduction and the input gradients that take the transposing
+    // reads.  A very wide output (the LM-head forward, whose weight operand
+    // streams 77 MB from memory) keeps three steps of loads in flight:
+    // 687 against 622 TFLOP/s there, while at N = 2304 and 3072 the deeper
+    // prefetch was 13-24% slower (standalone sweep, bitwise-equal outputs).
+    if constexpr (OP == GEMM_NT || OP == GEMM_NN) {
+        const bool k32 = (OP == GEMM_NT && a.K < 2048) ||
+                         (OP == GEMM_NN && a.ldb % 8 == 0 && ((uintptr_t)a.B & 15) == 0);
+        if (k32) {
+            if (a.N >= kGemm16DeepPrefetchN)
+                launch((gemm_bf16_k32_kernel<OP, EPI, H, 3>), dim3(tm * tn), dim3(NTHR), 0, s, a,
+                       tm, tn);
+            else
+                launch((gemm_bf16_k32_kernel<OP, EPI, H, 2>), dim3(tm * tn), dim3(NTHR), 0, s, a,
+                       tm, tn);
             return hipGetLastError();
         }
     }

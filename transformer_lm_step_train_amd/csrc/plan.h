@@ -39,6 +39,9 @@ size_t gemm_workspace_bytes(int op, int epi, int M, int N, int K, int cus);
 // ---- 16-bit matmul -----------------------------------------------------------
 constexpr int kGemm16Step = 64;     // the reduction step of the split plan
 constexpr int kGemm16BigTile = 256;  // output tile of the large-tile kernel
+// Outputs at least this wide keep three reduction steps of loads in flight
+// in the 32-deep-step forward and input-gradient products (two otherwise).
+constexpr int kGemm16DeepPrefetchN = 16384;
 
 // Which kernel (the 256x256 one: `big`) and how many K splits.
 struct PlanH {
