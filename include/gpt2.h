@@ -78,6 +78,15 @@ typedef struct {
     int32_t precision;           /* GPT2_FP32, GPT2_BF16_MIXED, GPT2_F16_MIXED */
     int32_t rope;                /* 0: learned position table wpe (GPT-2);
                                     1: rotary position embedding instead */
+    int32_t attn_recompute;      /* 0: the fp32 attention backward keeps dS
+                                    in a workspace of batch_size * num_heads
+                                    * 4 * 128^2 * nb(nb+1)/2 bytes, nb =
+                                    ceil(seq_len / 128), when that is at most
+                                    4 GiB (453 MiB for the 124M model at B16
+                                    T1024), and computes dQ from it; 1: no
+                                    workspace, the dQ kernel recomputes the
+                                    scores (slower).  Results agree to
+                                    rounding; each is deterministic. */
 } gpt2_config;
 
 /* Optional device allocator.  alloc returns device memory of at least

@@ -49,6 +49,7 @@ static gpt2_config cfg(int L, int C, int NH, int V, int maxT, int B, int T, int 
     c.seq_len = T;
     c.precision = prec;
     c.rope = rope;
+    c.attn_recompute = 0;
     return c;
 }
 
@@ -66,6 +67,9 @@ static void test_configs() {
         cfg(2, 64, 4, 512, 64, 2, 64, 0, 2),  cfg(2, 64, 4, -1, 64, 2, 64),
         cfg(2, 64, 4, 512, 64, -3, 64),
     };
+    gpt2_config rc = cfg(2, 64, 4, 512, 64, 2, 64);
+    rc.attn_recompute = 2;
+    CHECK(gpt2_validate_config(&rc) == GPT2_EINVAL);
     for (const auto& c : bad) {
         CHECK(gpt2_validate_config(&c) == GPT2_EINVAL);
         CHECK(strlen(gpt2_last_error()) > 0);
@@ -114,6 +118,17 @@ static void check_layout(const gpt2_config& c, bool guards) {
     CHECK(y.params == 0 && y.grads >= y.nparams * 4 && y.m > y.grads && y.v > y.m);
     CHECK((y.shadow != 0) == (c.precision != GPT2_FP32));
     CHECK((y.rope_cs != 0) == (c.rope != 0));
+    // the dS workspace: fp32 models that keep dS and fit the cap
+    const int64_t ds_bytes = (int64_t)y.Bmax * y.NH * gk::attn_ds_stride(y.Tmax) * 4;
+    const bool keep = !y.half && c.attn_recompute == 0 && ds_bytes <= gk::kAttnDsMaxBytes;
+    CHECK((y.ds_stride != 0) == keep);
+    if (keep) {
+        CHECK(y.ds_stride == gk::attn_ds_stride(y.Tmax));
+        bool found = false;
+        for (const auto& r : y.regions)
+            if (r.off == y.attn_ds) found = r.bytes == (size_t)ds_bytes;
+        CHECK(found);
+    }
     CHECK(y.n_pow2 >= y.M && y.n_pow2 < 2 * y.M + 2);
     CHECK((1 << y.pos_bits) >= y.M);
     // the workspace covers every split plan of the step's products
@@ -154,6 +169,11 @@ static void test_layouts() {
                 check_layout(cfg(4, 256, 4, 8192, 256, 4, 256, prec, rope), guards);
                 check_layout(cfg(12, 768, 12, 50257, 1024, 16, 1024, prec, rope), guards);
                 check_layout(cfg(1, 16, 1, 1, 1, 1, 1, prec, rope), guards);
+                // dS workspace past its cap (B1 T32768, 4 heads: 8.6 GB)
+                check_layout(cfg(1, 64, 4, 512, 32768, 1, 32768, prec, rope), guards);
+                gpt2_config r = cfg(2, 96, 3, 1001, 80, 3, 77, prec, rope);
+                r.attn_recompute = 1;
+                check_layout(r, guards);
             }
     // the byte count the ABI reports is the layout's, with guards off
     gpt2_config c = cfg(12, 768, 12, 50257, 1024, 16, 1024);

@@ -36,19 +36,21 @@ def gpt2():
 class Pair:
     """A GPU model and an oracle model with identical weights."""
 
-    def __init__(self, name, B=None, T=None, alloc_B=None, alloc_T=None, params=None):
+    def __init__(self, name, B=None, T=None, alloc_B=None, alloc_T=None, params=None,
+                 attn_recompute=False):
         c = dict(synth.CONFIGS[name])
         self.c = c
         self.B = B or c["B"]
         self.T = T or c["T"]
-        print(f"[parity] config={name} B={self.B} T={self.T}", flush=True)
+        print(f"[parity] config={name} B={self.B} T={self.T} attn_recompute={attn_recompute}",
+              flush=True)
         rope = c.get("rope", False)
         if params is None:
             params = synth.init_params(c["L"], c["C"], c["V"], c["maxT"], rope=rope)
         self.p0 = params
         g = gpt2()
         self.gpu = g.Model(c["L"], c["C"], c["NH"], c["V"], c["maxT"], alloc_B or self.B,
-                           alloc_T or self.T, rope=rope)
+                           alloc_T or self.T, rope=rope, attn_recompute=attn_recompute)
         self.gpu.set_params(params)
         self.orc = OracleModel(c["L"], c["C"], c["NH"], c["V"], c["maxT"], self.B, self.T,
                                rope=rope)
@@ -145,6 +147,49 @@ def test_one_training_step(name):
     tok, tgt = synth.token_stream(P.B, P.T, P.c["V"])
     check_step(P, tok, tgt)
     P.close()
+
+
+@pytest.mark.parametrize("name", ["tiny", "ragged", "small", "ragged_rope"])
+def test_one_training_step_recomputing_attention(name):
+    """The attention backward without the dS workspace (its dQ kernel
+    recomputes the scores) against the oracle."""
+    P = Pair(name, attn_recompute=True)
+    tok, tgt = synth.token_stream(P.B, P.T, P.c["V"])
+    check_step(P, tok, tgt)
+    P.close()
+
+
+@pytest.mark.parametrize("name,B,T", [("ragged", None, None), ("small", None, None),
+                                      ("gpt2_124m_b4t64", None, None), ("tiny", 2, 300)])
+def test_attention_backward_paths_agree(name, B, T):
+    """The two attention backwards (dS kept, dS recomputed) compute the same
+    sums in different orders: their gradients agree to a few roundoffs, and
+    the dS path repeats bit for bit."""
+    c = synth.CONFIGS[name]
+    B, T = B or c["B"], T or c["T"]
+    g = gpt2()
+    params = synth.init_params(c["L"], c["C"], c["V"], max(c["maxT"], T))
+    tok, tgt = synth.token_stream(B, T, c["V"])
+    grads = {}
+    for rec in (False, True):
+        m = g.Model(c["L"], c["C"], c["NH"], c["V"], max(c["maxT"], T), B, T,
+                    attn_recompute=rec)
+        m.set_params(params)
+        runs = []
+        for _ in range(2):
+            m.forward(tok, tgt)
+            m.zero_grad()
+            m.backward()
+            runs.append(m.grads())
+        assert np.array_equal(runs[0], runs[1]), rec
+        grads[rec] = runs[0]
+        m.close()
+    sizes, _ = oracle.param_sizes(c["L"], c["C"], c["NH"], c["V"], max(c["maxT"], T))
+    G, R = split(grads[False], sizes), split(grads[True], sizes)
+    errs = {n: rel(G[n], R[n]) for n in oracle.PARAM_NAMES}
+    print(f"[parity] {name} B={B} T={T} dS kept vs recomputed:",
+          {k: f"{v:.1e}" for k, v in errs.items()}, flush=True)
+    assert all(v < 2e-5 for v in errs.values()), errs
 
 
 def test_weight_decay_step():

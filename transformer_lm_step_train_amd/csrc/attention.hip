@@ -22,7 +22,11 @@
 // dP = dout V^T;  dQ = dS K / sqrt(hs);  dK = dS^T Q / sqrt(hs);  dV = P^T dout.
 // dQ (with D) and (dK, dV) come from two kernels that each own their output
 // rows, so no output is accumulated with atomics and results are
-// deterministic.
+// deterministic.  With a dS workspace the order is: D (one row dot per
+// position and head), then the key/value kernel, which also stores dS^T,
+// then dQ = dS K as a plain product over the stored dS: 5 matmul-sized
+// passes instead of 7 (the dQ kernel no longer recomputes S and dP).
+// Without one, the dQ kernel recomputes S and dP and also writes D.
 //
 // Each workgroup is four waves owning 128 consecutive rows; the other operand
 // streams through LDS in 64-row tiles (V transposed in the forward, so one
@@ -37,6 +41,7 @@ namespace gk {
 namespace {
 
 constexpr int AQ = 128;  // rows owned per workgroup (four waves of 32)
+static_assert(AQ == kAttnBlock, "dS^T blocks are one workgroup's rows");
 constexpr int AT = 64;   // rows per staged tile
 constexpr float LOG2E = 1.4426950408889634f;
 constexpr float LN2 = 0.6931471805599453f;
@@ -386,11 +391,20 @@ __global__ __launch_bounds__(256, 2) void attn_bwd_dq_kernel(
     if (q < T) store_row<HS, NDB>(dqkv + ((int64_t)b * T + q) * ld + h * HS, dq, g, scale);
 }
 
-template <int HS, class E>
+// dS^T storage (the key/value kernel writes it, the dQ kernel reads it): per
+// (sequence, head), the 128 x 128 blocks on or below the diagonal, block
+// (key block kb, query block qb) at qb(qb+1)/2 + kb, each [key][query]
+// row-major.  Blocks of 32 keys x 32 queries that the mask empties are never
+// written and never read.
+__device__ __forceinline__ int64_t ds_block(int qb, int kb) {
+    return ((int64_t)(qb * (qb + 1) / 2 + kb)) * (AQ * AQ);
+}
+
+template <int HS, class E, bool STORE_DS>
 __global__ __launch_bounds__(256, 2) void attn_bwd_dkdv_kernel(
     E* __restrict__ dqkv, const E* __restrict__ dout, const E* __restrict__ qkv,
     const float* __restrict__ lse, const float* __restrict__ D, int T, int C, int NH,
-    float qscale, float scale) {
+    float qscale, float scale, float* __restrict__ dsT, int64_t ds_stride) {
     constexpr int LD = HS + 4, HALF = HS / 2, NDB = (HS + 31) / 32;
     __shared__ __attribute__((aligned(16))) float qs[2][AT * LD];
     __shared__ __attribute__((aligned(16))) float dos[2][AT * LD];
@@ -493,6 +507,14 @@ __global__ __launch_bounds__(256, 2) void attn_bwd_dkdv_kernel(
                 sc[e] = p;
                 dp[e] = p * (dp[e] - dsm[cur][ql]);
             }
+            if constexpr (STORE_DS) {  // this wave's 32 keys x 32 queries of dS^T
+                float* row = dsT + (int64_t)bh * ds_stride + ds_block(qt >> 1, kb0) +
+                             (wave * 32 + li) * AQ + (qt & 1) * AT + qh * 32 + 4 * g;
+#pragma unroll
+                for (int c = 0; c < 4; c++)
+                    st4(row + 8 * c, make_float4(dp[4 * c], dp[4 * c + 1], dp[4 * c + 2],
+                                                 dp[4 * c + 3]));
+            }
 #pragma unroll
             for (int half = 0; half < 2; half++) {
                 float da[8][NDB], qa[8][NDB];  // reads issued before the MFMAs
@@ -530,6 +552,93 @@ __global__ __launch_bounds__(256, 2) void attn_bwd_dkdv_kernel(
     }
 }
 
+// D_t = dout_t . out_t per position and head (one wave per position; the
+// HS/4 lanes of a head reduce their float4 partial dots).
+template <int HS, class E>
+__global__ __launch_bounds__(256) void attn_rowdot_kernel(float* __restrict__ D,
+                                                          const E* __restrict__ dout,
+                                                          const E* __restrict__ out, int M,
+                                                          int T, int C, int NH) {
+    constexpr int G = HS / 4;  // lanes per head
+    const int lane = threadIdx.x & 63;
+    const int r = blockIdx.x * 4 + (threadIdx.x >> 6);
+    if (r >= M) return;  // whole wave
+    const int b = r / T, t = r - b * T;
+    const E* dr = dout + (int64_t)r * C;
+    const E* orow = out + (int64_t)r * C;
+    for (int j0 = 0; j0 < C / 4; j0 += 64) {
+        const int j = j0 + lane;
+        float v = 0.f;
+        if (j < C / 4) {
+            const float4 x = Act<E>::ld(dr + 4 * j), y = Act<E>::ld(orow + 4 * j);
+            v = (x.x * y.x + x.y * y.y) + (x.z * y.z + x.w * y.w);
+        }
+#pragma unroll
+        for (int o = 1; o < G; o <<= 1) v += __shfl_xor(v, o, WAVE);
+        if (j < C / 4 && (lane & (G - 1)) == 0) D[((int64_t)b * NH + j / G) * T + t] = v;
+    }
+}
+
+// dQ = dS K / sqrt(hs) from the stored dS^T.  Each wave owns 32 queries and
+// runs over 32-key blocks up to its diagonal, loading its operands straight
+// from memory in MFMA order (a key row of K and a key row of dS^T are each
+// 128 contiguous bytes per half-wave), one block ahead.  No LDS, no barriers.
+template <int HS, class E>
+__global__ __launch_bounds__(256, 2) void attn_bwd_dq_ds_kernel(
+    E* __restrict__ dqkv, const float* __restrict__ dsT, int64_t ds_stride,
+    const E* __restrict__ qkv, int T, int C, int NH, float scale) {
+    constexpr int NDB = (HS + 31) / 32;
+    const int nqb = (T + AQ - 1) / AQ;
+    const int nbh = gridDim.x / nqb;
+    const int bh = blockIdx.x % nbh;
+    const int qb = nqb - 1 - blockIdx.x / nbh;  // longest first
+    const int b = bh / NH, h = bh - b * NH;
+    const int lane = threadIdx.x & 63, wave = threadIdx.x >> 6;
+    const int li = lane & 31, g = lane >> 5;
+    const int qw = qb * AQ + wave * 32;
+    if (qw >= T) return;  // whole wave
+    const int64_t ld = 3 * (int64_t)C;
+    const E* kbase = qkv + (int64_t)b * T * ld + C + h * HS;
+    const float* dsq = dsT + (int64_t)bh * ds_stride + (qw - qb * AQ) + li;
+    const int nblk = qw / 32 + 1;  // 32-key blocks up to the diagonal
+
+    float av[2][16], kv[2][16][NDB];
+    auto load = [&](int buf, int kblk) {
+        const int k0 = kblk * 32;
+        const float* blk = dsq + ds_block(qb, k0 / AQ) + (k0 % AQ) * AQ;
+#pragma unroll
+        for (int st = 0; st < 16; st++) {
+            const int kl = 2 * st + g, key = k0 + kl;
+            av[buf][st] = blk[kl * AQ];
+#pragma unroll
+            for (int d = 0; d < NDB; d++) {
+                const int dim = d * 32 + li;
+                kv[buf][st][d] = key < T && dim < HS ? Act<E>::ld1(kbase + (int64_t)key * ld + dim)
+                                                     : 0.f;
+            }
+        }
+    };
+    floatx16 dq[NDB];
+#pragma unroll
+    for (int d = 0; d < NDB; d++) zero16(dq[d]);
+    load(0, 0);
+    for (int kblk = 0; kblk < nblk; kblk += 2) {
+        if (kblk + 1 < nblk) load(1, kblk + 1);
+#pragma unroll
+        for (int st = 0; st < 16; st++)
+#pragma unroll
+            for (int d = 0; d < NDB; d++) dq[d] = mfma(kv[0][st][d], av[0][st], dq[d]);
+        if (kblk + 1 >= nblk) break;
+        if (kblk + 2 < nblk) load(0, kblk + 2);
+#pragma unroll
+        for (int st = 0; st < 16; st++)
+#pragma unroll
+            for (int d = 0; d < NDB; d++) dq[d] = mfma(kv[1][st][d], av[1][st], dq[d]);
+    }
+    const int q = qw + li;
+    if (q < T) store_row<HS, NDB>(dqkv + ((int64_t)b * T + q) * ld + h * HS, dq, g, scale);
+}
+
 template <int HS, class E>
 hipError_t fwd_hs(hipStream_t s, E* out, float* lse, const E* qkv, int B, int T, int C,
                   int NH, int q_first) {
@@ -543,14 +652,24 @@ hipError_t fwd_hs(hipStream_t s, E* out, float* lse, const E* qkv, int B, int T,
 
 template <int HS, class E>
 hipError_t bwd_hs(hipStream_t s, E* dqkv, float* D, const E* dout, const E* qkv, const E* out,
-                  const float* lse, int B, int T, int C, int NH) {
+                  const float* lse, int B, int T, int C, int NH, float* dsT, int64_t ds_stride) {
     const int nb = (T + AQ - 1) / AQ;
     const float scale = 1.0f / sqrtf((float)HS);
     const float qscale = LOG2E * scale;
+    if (dsT) {
+        const int M = B * T;
+        launch((attn_rowdot_kernel<HS, E>), dim3((M + 3) / 4), dim3(256), 0, s, D, dout, out, M,
+               T, C, NH);
+        launch((attn_bwd_dkdv_kernel<HS, E, true>), dim3(B * NH * nb), dim3(256), 0, s, dqkv,
+               dout, qkv, lse, (const float*)D, T, C, NH, qscale, scale, dsT, ds_stride);
+        launch((attn_bwd_dq_ds_kernel<HS, E>), dim3(B * NH * nb), dim3(256), 0, s, dqkv,
+               (const float*)dsT, ds_stride, qkv, T, C, NH, scale);
+        return hipGetLastError();
+    }
     launch((attn_bwd_dq_kernel<HS, E>), dim3(B * NH * nb), dim3(256), 0, s, dqkv, D,
                        dout, out, qkv, lse, T, C, NH, qscale, scale);
-    launch((attn_bwd_dkdv_kernel<HS, E>), dim3(B * NH * nb), dim3(256), 0, s, dqkv,
-                       dout, qkv, lse, D, T, C, NH, qscale, scale);
+    launch((attn_bwd_dkdv_kernel<HS, E, false>), dim3(B * NH * nb), dim3(256), 0, s, dqkv,
+                       dout, qkv, lse, D, T, C, NH, qscale, scale, nullptr, (int64_t)0);
     return hipGetLastError();
 }
 
@@ -567,11 +686,12 @@ hipError_t forward_t(hipStream_t s, E* out, float* lse, const E* qkv, int B, int
 
 template <class E>
 hipError_t backward_t(hipStream_t s, E* dqkv, float* D, const E* dout, const E* qkv,
-                      const E* out, const float* lse, int B, int T, int C, int NH) {
+                      const E* out, const float* lse, int B, int T, int C, int NH, float* dsT,
+                      int64_t ds_stride) {
     switch (C / NH) {
-        case 16: return bwd_hs<16, E>(s, dqkv, D, dout, qkv, out, lse, B, T, C, NH);
-        case 32: return bwd_hs<32, E>(s, dqkv, D, dout, qkv, out, lse, B, T, C, NH);
-        case 64: return bwd_hs<64, E>(s, dqkv, D, dout, qkv, out, lse, B, T, C, NH);
+        case 16: return bwd_hs<16, E>(s, dqkv, D, dout, qkv, out, lse, B, T, C, NH, dsT, ds_stride);
+        case 32: return bwd_hs<32, E>(s, dqkv, D, dout, qkv, out, lse, B, T, C, NH, dsT, ds_stride);
+        case 64: return bwd_hs<64, E>(s, dqkv, D, dout, qkv, out, lse, B, T, C, NH, dsT, ds_stride);
         default: return hipErrorInvalidValue;
     }
 }
@@ -590,14 +710,15 @@ hipError_t attention_forward(hipStream_t s, void* out, float* lse, const void* q
 
 hipError_t attention_backward(hipStream_t s, void* dqkv, float* dpre, const void* dout,
                               const void* qkv, const void* out, const float* lse, int B, int T,
-                              int C, int NH, int dt) {
+                              int C, int NH, int dt, float* ds_ws, int64_t ds_stride) {
     if (B <= 0 || T <= 0) return hipSuccess;
     if (dt != DT_F32)
         return attention_backward_half(s, (uint16_t*)dqkv, dpre, (const uint16_t*)dout,
                                        (const uint16_t*)qkv, (const uint16_t*)out, lse, B, T, C,
                                        NH, dt);
+    if (ds_ws && ds_stride < attn_ds_stride(T)) return hipErrorInvalidValue;
     return backward_t<float>(s, (float*)dqkv, dpre, (const float*)dout, (const float*)qkv,
-                             (const float*)out, lse, B, T, C, NH);
+                             (const float*)out, lse, B, T, C, NH, ds_ws, ds_stride);
 }
 
 }  // namespace gk

@@ -75,6 +75,8 @@ int check_config(const gpt2_config* c) {
         c->precision != GPT2_F16_MIXED)
         return fail(GPT2_EINVAL, "unknown precision %d", c->precision);
     if (c->rope != 0 && c->rope != 1) return fail(GPT2_EINVAL, "rope must be 0 or 1");
+    if (c->attn_recompute != 0 && c->attn_recompute != 1)
+        return fail(GPT2_EINVAL, "attn_recompute must be 0 or 1");
     return GPT2_OK;
 }
 
@@ -167,6 +169,13 @@ void Layout::build(const gpt2_config* c, int cus, bool with_guards) {
     dqkv = take("dqkv", 3 * MC * es);
     dfch = take("dfch", 4 * MC * es);
     attn_d = take("att_rowdot", (size_t)M * NH * f);
+    ds_stride = 0;
+    attn_ds = 0;
+    if (!half && !c->attn_recompute &&
+        (int64_t)Bmax * NH * gk::attn_ds_stride(Tmax) * (int64_t)f <= gk::kAttnDsMaxBytes) {
+        ds_stride = gk::attn_ds_stride(Tmax);
+        attn_ds = take("att_dsT", (size_t)Bmax * NH * ds_stride * f);
+    }
     ln_part = take("ln_partials", gk::layernorm_partials_floats(M, C) * f);
     bias_part = take("bias_partials", gk::bias_partials_floats(M, 4 * C) * f);
     embed_part = take("embed_partials", gk::embed_partials_floats(M, C) * f);

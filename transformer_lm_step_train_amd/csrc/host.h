@@ -55,8 +55,9 @@ struct Layout {
     size_t params, grads, m, v, shadow;
     size_t encoded, ln1, ln1_mean, ln1_rstd, qkv, atty, lse, res2, ln2, ln2_mean, ln2_rstd, fch,
         fch_gelu, res3, lnf, lnf_mean, lnf_rstd, logits, losses;
-    size_t dres, dtmp, dqkv, dfch, attn_d, ln_part, bias_part, embed_part, gemm_ws, keys, tokens,
-        targets, scalars, rope_cs;
+    size_t dres, dtmp, dqkv, dfch, attn_d, attn_ds, ln_part, bias_part, embed_part, gemm_ws, keys,
+        tokens, targets, scalars, rope_cs;
+    int64_t ds_stride;  // floats per (sequence, head) of attn_ds; 0: no dS workspace
     size_t gemm_ws_bytes, total;
     // Every sub-buffer in allocation order: name, offset, bytes and (with
     // guards) the offset of its guard region.

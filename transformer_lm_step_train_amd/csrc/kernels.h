@@ -92,9 +92,13 @@ hipError_t gemm(hipStream_t s, const GemmArgs& a, float* workspace,
 // skipped, and rows of its own block are rewritten with the same values).
 hipError_t attention_forward(hipStream_t s, void* out, float* lse, const void* qkv, int B,
                              int T, int C, int NH, int dt, int q_first = 0);
+// ds_ws (optional, fp32 models): dS workspace of ds_stride floats per
+// (sequence, head), ds_stride >= attn_ds_stride(T) (plan.h); with it the
+// backward keeps dS instead of recomputing the scores for dQ.
 hipError_t attention_backward(hipStream_t s, void* dqkv, float* dpre, const void* dout,
                               const void* qkv, const void* out, const float* lse, int B,
-                              int T, int C, int NH, int dt);
+                              int T, int C, int NH, int dt, float* ds_ws = nullptr,
+                              int64_t ds_stride = 0);
 // Mixed-precision attention on the 16-bit matrix cores (all tensors bf16 or
 // fp16 bits per dt, lse and D fp32).
 hipError_t attention_forward_half(hipStream_t s, uint16_t* out, float* lse, const uint16_t* qkv,

@@ -68,4 +68,14 @@ inline size_t embed_partials_floats(int M, int C) {
     return (size_t)2 * cdiv(M, kEmbedChunk) * C;
 }
 
+// The attention backward's dS^T workspace: per (sequence, head), the 128 x
+// 128 blocks on or below the diagonal for sequences of up to Tmax positions.
+// Kept only while the whole workspace stays within kAttnDsMaxBytes.
+constexpr int kAttnBlock = 128;
+constexpr int64_t kAttnDsMaxBytes = (int64_t)4 << 30;
+inline int64_t attn_ds_stride(int Tmax) {
+    const int64_t nb = cdiv(Tmax, kAttnBlock);
+    return nb * (nb + 1) / 2 * kAttnBlock * kAttnBlock;
+}
+
 }  // namespace gk

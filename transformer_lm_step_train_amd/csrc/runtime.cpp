@@ -483,9 +483,13 @@ int backward_impl(gpt2_model* md) {
         {
             const double hs = C / NH;
             const double flops = 8.0 * B * NH * hs * (double)T * (T + 1) / 2.0;
-            LAUNCH(md, GPT2_KC_ATTENTION, flops, es * 7.0 * M * C + 8.0 * M * NH,
+            const double nb32 = (T + 31) / 32;  // dS^T blocks written, then read
+            const double ds_bytes = y.ds_stride ? 8.0 * B * NH * nb32 * (nb32 + 1) / 2 * 1024 : 0;
+            LAUNCH(md, GPT2_KC_ATTENTION, flops, es * 7.0 * M * C + 8.0 * M * NH + ds_bytes,
                    gk::attention_backward(s, dqkv, md->at<float>(y.attn_d), dtmp, qkv, atty, lse,
-                                          B, T, C, NH, h));
+                                          B, T, C, NH, h,
+                                          y.ds_stride ? md->at<float>(y.attn_ds) : nullptr,
+                                          y.ds_stride));
         }
         if (y.rope)  // back through the rotation: dq, dk of the unrotated q, k
             LAUNCH(md, GPT2_KC_OTHER, 0, es * 4.0 * M * C,

@@ -38,7 +38,8 @@ _i64 = _c.c_int64
 class gpt2_config(_c.Structure):
     _fields_ = [("max_seq_len", _i32), ("vocab_size", _i32), ("num_layers", _i32),
                 ("num_heads", _i32), ("channels", _i32), ("batch_size", _i32),
-                ("seq_len", _i32), ("precision", _i32), ("rope", _i32)]
+                ("seq_len", _i32), ("precision", _i32), ("rope", _i32),
+                ("attn_recompute", _i32)]
 
 
 ALLOC_FN = _c.CFUNCTYPE(_vp, _c.c_size_t, _vp)
@@ -124,10 +125,11 @@ def _check(rc):
     return rc
 
 
-def make_config(L, C, NH, V, maxT, B, T, precision=GPT2_FP32, rope=0) -> gpt2_config:
+def make_config(L, C, NH, V, maxT, B, T, precision=GPT2_FP32, rope=0,
+                attn_recompute=0) -> gpt2_config:
     return gpt2_config(max_seq_len=maxT, vocab_size=V, num_layers=L, num_heads=NH,
                        channels=C, batch_size=B, seq_len=T, precision=precision,
-                       rope=int(rope))
+                       rope=int(rope), attn_recompute=int(attn_recompute))
 
 
 # ---- the C ABI, one function each ------------------------------------------
@@ -344,8 +346,9 @@ class Model:
     """One model handle.  With torch=True (default) device memory comes from
     torch's caching allocator and work runs on torch's current stream."""
 
-    def __init__(self, L, C, NH, V, maxT, B, T, precision=GPT2_FP32, torch=True, rope=False):
-        self.cfg = make_config(L, C, NH, V, maxT, B, T, precision, rope)
+    def __init__(self, L, C, NH, V, maxT, B, T, precision=GPT2_FP32, torch=True, rope=False,
+                 attn_recompute=False):
+        self.cfg = make_config(L, C, NH, V, maxT, B, T, precision, rope, attn_recompute)
         self.rope = bool(rope)
         self.L, self.C, self.NH, self.V, self.maxT, self.B, self.T = L, C, NH, V, maxT, B, T
         self._allocator = None
