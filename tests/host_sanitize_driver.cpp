@@ -119,11 +119,13 @@ static void check_layout(const gpt2_config& c, bool guards) {
     CHECK((y.shadow != 0) == (c.precision != GPT2_FP32));
     CHECK((y.rope_cs != 0) == (c.rope != 0));
     // the dS workspace: fp32 models that keep dS and fit the cap
-    const int64_t ds_bytes = (int64_t)y.Bmax * y.NH * gk::attn_ds_stride(y.Tmax) * 4;
-    const bool keep = !y.half && c.attn_recompute == 0 && ds_bytes <= gk::kAttnDsMaxBytes;
+    const int64_t ds_bytes = (int64_t)y.Bmax * y.NH * gk::attn_ds_stride(y.Tmax, y.C / y.NH) * 4;
+    const bool keep = !y.half && c.attn_recompute == 0 && ds_bytes < gk::kAttnDsMaxBytes;
     CHECK((y.ds_stride != 0) == keep);
     if (keep) {
-        CHECK(y.ds_stride == gk::attn_ds_stride(y.Tmax));
+        CHECK(y.ds_stride == gk::attn_ds_stride(y.Tmax, y.C / y.NH));
+        for (int T = 1; T <= y.Tmax; T += 37)  // a shorter run fits the same slice
+            CHECK(gk::attn_ds_stride(T, y.C / y.NH) <= y.ds_stride);
         bool found = false;
         for (const auto& r : y.regions)
             if (r.off == y.attn_ds) found = r.bytes == (size_t)ds_bytes;

@@ -391,11 +391,16 @@ __global__ __launch_bounds__(256, 2) void attn_bwd_dq_kernel(
     if (q < T) store_row<HS, NDB>(dqkv + ((int64_t)b * T + q) * ld + h * HS, dq, g, scale);
 }
 
-// dS^T storage (the key/value kernel writes it, the dQ kernel reads it): per
-// (sequence, head), the 128 x 128 blocks on or below the diagonal, block
-// (key block kb, query block qb) at qb(qb+1)/2 + kb, each [key][query]
-// row-major.  Blocks of 32 keys x 32 queries that the mask empties are never
-// written and never read.
+// The dS workspace (the key/value kernel writes it, the dQ kernel reads it),
+// per (sequence, head):
+//  - dS^T in the 128 x 128 blocks on or below the diagonal, block (key block
+//    kb, query block qb) at qb(qb+1)/2 + kb, each [key][query] row-major.
+//    The 32 x 32 tiles that the mask empties are never written and never
+//    read.  The writer stores float4 runs of queries; a reading lane (one
+//    query) loads one value per key, 128 contiguous bytes per half-wave.
+//  - then K in the dQ product's operand order, per 32-key block and 32 head
+//    dimensions (1024 floats): K[key 2 st + g][dim i] at (32 g + i) * 16 + st,
+//    so a lane loads its 16 values as four float4.
 __device__ __forceinline__ int64_t ds_block(int qb, int kb) {
     return ((int64_t)(qb * (qb + 1) / 2 + kb)) * (AQ * AQ);
 }
@@ -404,7 +409,7 @@ template <int HS, class E, bool STORE_DS>
 __global__ __launch_bounds__(256, 2) void attn_bwd_dkdv_kernel(
     E* __restrict__ dqkv, const E* __restrict__ dout, const E* __restrict__ qkv,
     const float* __restrict__ lse, const float* __restrict__ D, int T, int C, int NH,
-    float qscale, float scale, float* __restrict__ dsT, int64_t ds_stride) {
+    float qscale, float scale, float* __restrict__ dsT, int64_t ds_stride, int64_t kf_off) {
     constexpr int LD = HS + 4, HALF = HS / 2, NDB = (HS + 31) / 32;
     __shared__ __attribute__((aligned(16))) float qs[2][AT * LD];
     __shared__ __attribute__((aligned(16))) float dos[2][AT * LD];
@@ -425,12 +430,31 @@ __global__ __launch_bounds__(256, 2) void attn_bwd_dkdv_kernel(
     const int key = kw + li;
 
     float kr[HALF], vr[HALF];
+    // this (sequence, head)'s slice of the dS workspace, addressed by one
+    // lane offset plus wave-uniform ones (its size is under 2 GiB)
+    const __amdgpu_buffer_rsrc_t wsr =
+        buf_rsrc(dsT + (STORE_DS ? (int64_t)bh * ds_stride : 0),
+                 STORE_DS ? (uint32_t)(ds_stride * 4) : 0u);
+    const int lane_off = ((li & 1) * 512 + (li >> 1)) * 4;  // bytes: key 2 st + (li & 1), st = li / 2
+    // this wave's keys in the dQ product's operand order (keys past T zero)
+    const bool kfrag = STORE_DS && kw < T;
+    const int kf_so = (int)((kf_off + (int64_t)(kw / 32) * NDB * 1024) * 4);
 #pragma unroll
     for (int s = 0; s < HALF; s += 4) {
         float4 x = make_float4(0.f, 0.f, 0.f, 0.f), y = x;
         if (key < T) {
             x = Act<E>::ld(qbase + C + (int64_t)key * ld + g * HALF + s);
             y = Act<E>::ld(qbase + 2 * C + (int64_t)key * ld + g * HALF + s);
+        }
+        if (kfrag) {
+            const float xs[4] = {x.x, x.y, x.z, x.w};
+#pragma unroll
+            for (int c = 0; c < 4; c++) {
+                const int dim = g * HALF + s + c;
+                __builtin_amdgcn_raw_buffer_store_b32(
+                    __float_as_uint(xs[c]), wsr, lane_off + ((dim >> 5) * 1024 + (dim & 31) * 16) * 4,
+                    kf_so, 0);
+            }
         }
         kr[s] = x.x * qscale;  // the score scale folded into the key once
         kr[s + 1] = x.y * qscale;
@@ -508,12 +532,13 @@ __global__ __launch_bounds__(256, 2) void attn_bwd_dkdv_kernel(
                 dp[e] = p * (dp[e] - dsm[cur][ql]);
             }
             if constexpr (STORE_DS) {  // this wave's 32 keys x 32 queries of dS^T
-                float* row = dsT + (int64_t)bh * ds_stride + ds_block(qt >> 1, kb0) +
-                             (wave * 32 + li) * AQ + (qt & 1) * AT + qh * 32 + 4 * g;
+                const int so = (int)((ds_block(qt >> 1, kb0) + (wave * 32) * AQ) * 4);
+                const int vo = (li * AQ + (qt & 1) * AT + qh * 32 + 4 * g) * 4;
 #pragma unroll
                 for (int c = 0; c < 4; c++)
-                    st4(row + 8 * c, make_float4(dp[4 * c], dp[4 * c + 1], dp[4 * c + 2],
-                                                 dp[4 * c + 3]));
+                    BufAct<float>::st(wsr, vo + 32 * c, so,
+                                      make_float4(dp[4 * c], dp[4 * c + 1], dp[4 * c + 2],
+                                                  dp[4 * c + 3]));
             }
 #pragma unroll
             for (int half = 0; half < 2; half++) {
@@ -579,14 +604,15 @@ __global__ __launch_bounds__(256) void attn_rowdot_kernel(float* __restrict__ D,
     }
 }
 
-// dQ = dS K / sqrt(hs) from the stored dS^T.  Each wave owns 32 queries and
-// runs over 32-key blocks up to its diagonal, loading its operands straight
-// from memory in MFMA order (a key row of K and a key row of dS^T are each
-// 128 contiguous bytes per half-wave), one block ahead.  No LDS, no barriers.
-template <int HS, class E>
+// dQ = dS K / sqrt(hs) from the dS workspace.  Each wave owns 32 queries and
+// runs over 32-key blocks up to its diagonal, loading a block's operands
+// straight from the workspace in MFMA order (16 coalesced dS values and four
+// float4 of K per 32 head dimensions per lane), PF blocks ahead.  No LDS, no
+// barriers.
+template <int HS, class E, int PF>
 __global__ __launch_bounds__(256, 2) void attn_bwd_dq_ds_kernel(
-    E* __restrict__ dqkv, const float* __restrict__ dsT, int64_t ds_stride,
-    const E* __restrict__ qkv, int T, int C, int NH, float scale) {
+    E* __restrict__ dqkv, const float* __restrict__ dsT, int64_t ds_stride, int64_t kf_off, int T,
+    int C, int NH, float scale) {
     constexpr int NDB = (HS + 31) / 32;
     const int nqb = (T + AQ - 1) / AQ;
     const int nbh = gridDim.x / nqb;
@@ -598,42 +624,55 @@ __global__ __launch_bounds__(256, 2) void attn_bwd_dq_ds_kernel(
     const int qw = qb * AQ + wave * 32;
     if (qw >= T) return;  // whole wave
     const int64_t ld = 3 * (int64_t)C;
-    const E* kbase = qkv + (int64_t)b * T * ld + C + h * HS;
-    const float* dsq = dsT + (int64_t)bh * ds_stride + (qw - qb * AQ) + li;
+    // this (sequence, head)'s slice of the workspace (under 2 GiB)
+    const __amdgpu_buffer_rsrc_t wsr =
+        buf_rsrc(dsT + (int64_t)bh * ds_stride, (uint32_t)(ds_stride * 4));
+    const int kvo = (g * 32 + li) * 16 * 4;  // this lane's 16 key values of a block, bytes
+    const int dvo = (g * AQ + (qw - qb * AQ) + li) * 4;  // its query's column, key 2 st + g
+    const int ds_so = (int)(ds_block(qb, 0) * 4);
+    const int kf_so = (int)(kf_off * 4);
     const int nblk = qw / 32 + 1;  // 32-key blocks up to the diagonal
 
-    float av[2][16], kv[2][16][NDB];
-    auto load = [&](int buf, int kblk) {
-        const int k0 = kblk * 32;
-        const float* blk = dsq + ds_block(qb, k0 / AQ) + (k0 % AQ) * AQ;
+    float av[PF][16], kv[PF][NDB][16];
+    auto load = [&](int u, int kblk) {
+        const int a = ds_so + ((kblk >> 2) * (AQ * AQ) + (kblk & 3) * 32 * AQ) * 4;
 #pragma unroll
-        for (int st = 0; st < 16; st++) {
-            const int kl = 2 * st + g, key = k0 + kl;
-            av[buf][st] = blk[kl * AQ];
+        for (int st = 0; st < 16; st++)
+            av[u][st] = __uint_as_float(
+                __builtin_amdgcn_raw_buffer_load_b32(wsr, dvo, a + st * 2 * AQ * 4, BUF_NT));
 #pragma unroll
-            for (int d = 0; d < NDB; d++) {
-                const int dim = d * 32 + li;
-                kv[buf][st][d] = key < T && dim < HS ? Act<E>::ld1(kbase + (int64_t)key * ld + dim)
-                                                     : 0.f;
+        for (int d = 0; d < NDB; d++)
+#pragma unroll
+            for (int c = 0; c < 4; c++) {
+                // keys are read by every wave of the sequence: default cache policy
+                const u32x4_t k = __builtin_amdgcn_raw_buffer_load_b128(
+                    wsr, kvo + 16 * c, kf_so + (kblk * NDB + d) * 4096, 0);
+                float4 x = make_float4(__uint_as_float(k[0]), __uint_as_float(k[1]),
+                                       __uint_as_float(k[2]), __uint_as_float(k[3]));
+                if (HS < 32 && li >= HS) x = make_float4(0.f, 0.f, 0.f, 0.f);
+                kv[u][d][4 * c] = x.x;
+                kv[u][d][4 * c + 1] = x.y;
+                kv[u][d][4 * c + 2] = x.z;
+                kv[u][d][4 * c + 3] = x.w;
             }
-        }
     };
     floatx16 dq[NDB];
 #pragma unroll
     for (int d = 0; d < NDB; d++) zero16(dq[d]);
-    load(0, 0);
-    for (int kblk = 0; kblk < nblk; kblk += 2) {
-        if (kblk + 1 < nblk) load(1, kblk + 1);
 #pragma unroll
-        for (int st = 0; st < 16; st++)
+    for (int u = 0; u < PF; u++)
+        if (u < nblk) load(u, u);
+    for (int kblk = 0; kblk < nblk; kblk += PF) {
 #pragma unroll
-            for (int d = 0; d < NDB; d++) dq[d] = mfma(kv[0][st][d], av[0][st], dq[d]);
-        if (kblk + 1 >= nblk) break;
-        if (kblk + 2 < nblk) load(0, kblk + 2);
+        for (int u = 0; u < PF; u++) {
+            if (kblk + u < nblk) {
 #pragma unroll
-        for (int st = 0; st < 16; st++)
+                for (int st = 0; st < 16; st++)
 #pragma unroll
-            for (int d = 0; d < NDB; d++) dq[d] = mfma(kv[1][st][d], av[1][st], dq[d]);
+                    for (int d = 0; d < NDB; d++) dq[d] = mfma(kv[u][d][st], av[u][st], dq[d]);
+                if (kblk + u + PF < nblk) load(u, kblk + u + PF);
+            }
+        }
     }
     const int q = qw + li;
     if (q < T) store_row<HS, NDB>(dqkv + ((int64_t)b * T + q) * ld + h * HS, dq, g, scale);
@@ -661,15 +700,17 @@ hipError_t bwd_hs(hipStream_t s, E* dqkv, float* D, const E* dout, const E* qkv,
         launch((attn_rowdot_kernel<HS, E>), dim3((M + 3) / 4), dim3(256), 0, s, D, dout, out, M,
                T, C, NH);
         launch((attn_bwd_dkdv_kernel<HS, E, true>), dim3(B * NH * nb), dim3(256), 0, s, dqkv,
-               dout, qkv, lse, (const float*)D, T, C, NH, qscale, scale, dsT, ds_stride);
-        launch((attn_bwd_dq_ds_kernel<HS, E>), dim3(B * NH * nb), dim3(256), 0, s, dqkv,
-               (const float*)dsT, ds_stride, qkv, T, C, NH, scale);
+               dout, qkv, lse, (const float*)D, T, C, NH, qscale, scale, dsT, ds_stride,
+               attn_ds_blocks_floats(T));
+        launch((attn_bwd_dq_ds_kernel<HS, E, 3>), dim3(B * NH * nb), dim3(256), 0, s, dqkv,
+               (const float*)dsT, ds_stride, attn_ds_blocks_floats(T), T, C, NH, scale);
         return hipGetLastError();
     }
     launch((attn_bwd_dq_kernel<HS, E>), dim3(B * NH * nb), dim3(256), 0, s, dqkv, D,
                        dout, out, qkv, lse, T, C, NH, qscale, scale);
     launch((attn_bwd_dkdv_kernel<HS, E, false>), dim3(B * NH * nb), dim3(256), 0, s, dqkv,
-                       dout, qkv, lse, D, T, C, NH, qscale, scale, nullptr, (int64_t)0);
+                       dout, qkv, lse, D, T, C, NH, qscale, scale, nullptr, (int64_t)0,
+                       (int64_t)0);
     return hipGetLastError();
 }
 
@@ -716,7 +757,7 @@ hipError_t attention_backward(hipStream_t s, void* dqkv, float* dpre, const void
         return attention_backward_half(s, (uint16_t*)dqkv, dpre, (const uint16_t*)dout,
                                        (const uint16_t*)qkv, (const uint16_t*)out, lse, B, T, C,
                                        NH, dt);
-    if (ds_ws && ds_stride < attn_ds_stride(T)) return hipErrorInvalidValue;
+    if (ds_ws && (NH <= 0 || ds_stride < attn_ds_stride(T, C / NH))) return hipErrorInvalidValue;
     return backward_t<float>(s, (float*)dqkv, dpre, (const float*)dout, (const float*)qkv,
                              (const float*)out, lse, B, T, C, NH, ds_ws, ds_stride);
 }

@@ -172,8 +172,9 @@ void Layout::build(const gpt2_config* c, int cus, bool with_guards) {
     ds_stride = 0;
     attn_ds = 0;
     if (!half && !c->attn_recompute &&
-        (int64_t)Bmax * NH * gk::attn_ds_stride(Tmax) * (int64_t)f <= gk::kAttnDsMaxBytes) {
-        ds_stride = gk::attn_ds_stride(Tmax);
+        (int64_t)Bmax * NH * gk::attn_ds_stride(Tmax, C / NH) * (int64_t)f <
+            gk::kAttnDsMaxBytes) {
+        ds_stride = gk::attn_ds_stride(Tmax, C / NH);
         attn_ds = take("att_dsT", (size_t)Bmax * NH * ds_stride * f);
     }
     ln_part = take("ln_partials", gk::layernorm_partials_floats(M, C) * f);

@@ -93,7 +93,7 @@ hipError_t gemm(hipStream_t s, const GemmArgs& a, float* workspace,
 hipError_t attention_forward(hipStream_t s, void* out, float* lse, const void* qkv, int B,
                              int T, int C, int NH, int dt, int q_first = 0);
 // ds_ws (optional, fp32 models): dS workspace of ds_stride floats per
-// (sequence, head), ds_stride >= attn_ds_stride(T) (plan.h); with it the
+// (sequence, head), ds_stride >= attn_ds_stride(T, C / NH) (plan.h); with it the
 // backward keeps dS instead of recomputing the scores for dQ.
 hipError_t attention_backward(hipStream_t s, void* dqkv, float* dpre, const void* dout,
                               const void* qkv, const void* out, const float* lse, int B,

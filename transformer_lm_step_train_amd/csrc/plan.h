@@ -68,14 +68,20 @@ inline size_t embed_partials_floats(int M, int C) {
     return (size_t)2 * cdiv(M, kEmbedChunk) * C;
 }
 
-// The attention backward's dS^T workspace: per (sequence, head), the 128 x
-// 128 blocks on or below the diagonal for sequences of up to Tmax positions.
-// Kept only while the whole workspace stays within kAttnDsMaxBytes.
+// The attention backward's dS workspace, per (sequence, head) of T
+// positions and head size hs: the 128 x 128 blocks of dS^T on or below the
+// diagonal, then the keys in the dQ product's operand order (one 32-key
+// block per 1024 floats and 32 head dimensions).  Kept only while the whole
+// workspace stays under kAttnDsMaxBytes (so each (sequence, head) slice is
+// addressable with 32-bit byte offsets).
 constexpr int kAttnBlock = 128;
-constexpr int64_t kAttnDsMaxBytes = (int64_t)4 << 30;
-inline int64_t attn_ds_stride(int Tmax) {
-    const int64_t nb = cdiv(Tmax, kAttnBlock);
+constexpr int64_t kAttnDsMaxBytes = (int64_t)2 << 30;
+inline int64_t attn_ds_blocks_floats(int T) {
+    const int64_t nb = cdiv(T, kAttnBlock);
     return nb * (nb + 1) / 2 * kAttnBlock * kAttnBlock;
+}
+inline int64_t attn_ds_stride(int T, int hs) {
+    return attn_ds_blocks_floats(T) + (int64_t)cdiv(T, 32) * cdiv(hs, 32) * 1024;
 }
 
 }  // namespace gk
