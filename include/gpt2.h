@@ -79,14 +79,17 @@ typedef struct {
     int32_t rope;                /* 0: learned position table wpe (GPT-2);
                                     1: rotary position embedding instead */
     int32_t attn_recompute;      /* 0: the fp32 attention backward keeps dS
-                                    in a workspace of batch_size * num_heads
-                                    * 4 * 128^2 * nb(nb+1)/2 bytes, nb =
-                                    ceil(seq_len / 128), when that is at most
-                                    4 GiB (453 MiB for the 124M model at B16
-                                    T1024), and computes dQ from it; 1: no
-                                    workspace, the dQ kernel recomputes the
-                                    scores (slower).  Results agree to
-                                    rounding; each is deterministic. */
+                                    (and the keys in the dQ product's
+                                    operand order) in a workspace of
+                                    batch_size * num_heads * 4 * (128^2 *
+                                    nb(nb+1)/2 + 1024 * ceil(seq_len/32) *
+                                    ceil(hs/32)) bytes, nb = ceil(seq_len /
+                                    128), when that is under 2 GiB (480 MiB
+                                    for the 124M model at B16 T1024), and
+                                    computes dQ from it; 1: no workspace,
+                                    the dQ kernel recomputes the scores
+                                    (slower).  Results agree to rounding;
+                                    each is deterministic. */
 } gpt2_config;
 
 /* Optional device allocator.  alloc returns device memory of at least

@@ -141,7 +141,7 @@ def check_step(P, tok, tgt, lr=1e-4, wd=0.0):
 
 
 @pytest.mark.parametrize("name", ["tiny", "ragged", "small", "ragged80", "gpt2_124m_b4t64",
-                                  "tiny_rope", "ragged_rope"])
+                                  "tiny_rope", "ragged_rope", "wide_vocab"])
 def test_one_training_step(name):
     P = Pair(name)
     tok, tgt = synth.token_stream(P.B, P.T, P.c["V"])

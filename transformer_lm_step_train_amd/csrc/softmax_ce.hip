@@ -41,6 +41,9 @@ __global__ __launch_bounds__(NT) __attribute__((amdgpu_waves_per_eu(4))) void so
     __shared__ float shm[NW], shs[NW];
     const int64_t row = blockIdx.x;
     if (gscale) dscale *= *gscale;  // loss scaling of the fp16 model
+    // row-uniform values are kept in scalar registers (the row fills the
+    // vector registers)
+    dscale = __int_as_float(__builtin_amdgcn_readfirstlane(__float_as_int(dscale)));
     T* z = logits + row * ldv;
     const int V4 = ldv >> 2;
     const auto zr = buf_rsrc(z, (uint32_t)ldv * sizeof(T));
@@ -48,6 +51,8 @@ __global__ __launch_bounds__(NT) __attribute__((amdgpu_waves_per_eu(4))) void so
     const int vo = threadIdx.x * BufAct<T>::BYTES;
     const int tgt = targets[row];
     const bool bad = tgt < 0 || tgt >= V;
+    // the thread whose groups hold the target column reads its logit
+    const bool owner = !bad && threadIdx.x == (tgt >> 2) % NT;
     float4 v[NJ];
 #pragma unroll
     for (int j = 0; j < NJ; j++) {
@@ -57,8 +62,8 @@ __global__ __launch_bounds__(NT) __attribute__((amdgpu_waves_per_eu(4))) void so
         else
             v[j] = make_float4(-INFINITY, -INFINITY, -INFINITY, -INFINITY);
     }
-    float zt = 0.f;
-    if (threadIdx.x == 0 && !bad) zt = Act<T>::ld1(z + tgt);
+    const float zt = __int_as_float(
+        __builtin_amdgcn_readfirstlane(__float_as_int(bad ? 0.f : Act<T>::ld1(z + tgt))));
     float m = -INFINITY;
 #pragma unroll
     for (int j = 0; j < NJ; j++) {
@@ -93,35 +98,34 @@ __global__ __launch_bounds__(NT) __attribute__((amdgpu_waves_per_eu(4))) void so
         shs[wave] = sw;
     }
     __syncthreads();
-    float M = shm[0];
-#pragma unroll
-    for (int i = 1; i < NW; i++) M = fmaxf(M, shm[i]);
-    float S = 0.f;
-#pragma unroll
-    for (int i = 0; i < NW; i++)
-        S += shm[i] == -INFINITY ? 0.f : shs[i] * __builtin_amdgcn_exp2f((shm[i] - M) * LOG2E);
+    // every wave merges the NW pairs across its lanes (few registers while
+    // the row is held)
+    const float mi = lane < NW ? shm[lane] : -INFINITY;
+    const float M = wave_max(mi);
+    const float S = wave_sum(mi == -INFINITY ? 0.f : shs[lane < NW ? lane : 0] *
+                                                      __builtin_amdgcn_exp2f((mi - M) * LOG2E));
     const float lse = M + logf(S);
-    if (threadIdx.x == 0) {
-        losses[row] = bad ? 0.f : lse - zt;
-        if (bad) atomicOr(flag, 2);
+    if (owner) losses[row] = lse - zt;
+    if (bad && threadIdx.x == 0) {
+        losses[row] = 0.f;
+        atomicOr(flag, 2);
     }
     if constexpr (!GRAD) return;
     // exp(z - lse) = e * exp(m_t - lse); the padding columns give 0.
     const float f = bad || m == -INFINITY ? 0.f : __builtin_amdgcn_exp2f((m - lse) * LOG2E) * dscale;
-    // The target column: group jt of thread `owner`, component tc.
-    const int jt = bad ? -1 : (tgt >> 2) / NT, owner = (tgt >> 2) % NT, tc = tgt & 3;
-    const float hit = bad ? 0.f : dscale;
 #pragma unroll
     for (int j = 0; j < NJ; j++) {
-        float4 d = make_float4(v[j].x * f, v[j].y * f, v[j].z * f, v[j].w * f);
-        if (j == jt && threadIdx.x == owner) {
-            if (tc == 0) d.x -= hit;
-            if (tc == 1) d.y -= hit;
-            if (tc == 2) d.z -= hit;
-            if (tc == 3) d.w -= hit;
-        }
-        if (NT * (j + 1) <= V4 || threadIdx.x + NT * j < V4) BufAct<T>::st(zr, vo, JB * j, d);
+        v[j].x *= f;
+        v[j].y *= f;
+        v[j].z *= f;
+        v[j].w *= f;
+        if (NT * (j + 1) <= V4 || threadIdx.x + NT * j < V4) BufAct<T>::st(zr, vo, JB * j, v[j]);
+        __builtin_amdgcn_sched_barrier(0);  // one group at a time
     }
+    // The target column, stored again by the thread that wrote it: the same
+    // exponential (same operands and instructions as in its group) times f,
+    // minus the scaled one-hot.
+    if (owner) Act<T>::st1(z + tgt, __builtin_amdgcn_exp2f(fmaf(zt, LOG2E, -ms)) * f - dscale);
 }
 
 template <int NT, int NJ, class T>
@@ -150,7 +154,10 @@ hipError_t softmax_ce_t(hipStream_t s, T* logits, float* losses, const int32_t* 
     if (nj <= 8) return launch_ce<512, 8>(s, logits, losses, targets, N, V, ldv, dscale, gs, flag);
     if (nj <= 16) return launch_ce<512, 16>(s, logits, losses, targets, N, V, ldv, dscale, gs, flag);
     if (nj <= 25) return launch_ce<512, 25>(s, logits, losses, targets, N, V, ldv, dscale, gs, flag);
-    if (nj <= 32) return launch_ce<512, 32>(s, logits, losses, targets, N, V, ldv, dscale, gs, flag);
+    // rows past 51200 columns (up to 65536): one 1024-thread workgroup per
+    // compute unit, 16 groups per thread, so the row still fits in registers
+    if ((V4 + 1023) / 1024 <= 16)
+        return launch_ce<1024, 16>(s, logits, losses, targets, N, V, ldv, dscale, gs, flag);
     return hipErrorInvalidValue;
 }
 
