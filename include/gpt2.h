@@ -62,7 +62,7 @@ typedef struct gpt2_model gpt2_model; /* opaque */
 /* Model shape plus the largest batch the arenas are sized for.  Limits:
  * channels % num_heads == 0 with head size 16, 32 or 64; channels <= 1024;
  * num_layers <= 1024; seq_len <= max_seq_len <= 65536; batch_size*seq_len <=
- * 32768; vocab_size <= 65536.
+ * 32768; vocab_size <= 65536; rope and attn_recompute are 0 or 1.
  *
  * rope = 1 replaces the learned position table by a rotary position
  * embedding, the architectural extension the pages name (yinghuohong.cn,
