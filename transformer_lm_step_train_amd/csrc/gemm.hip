@@ -18,9 +18,10 @@
 // last step is loaded with zero padding after the loop.
 //
 // Operands whose reduction index is contiguous in HBM are stored in LDS as
-// [row][k] (BK+4 floats per row); operands whose free index is contiguous
-// are stored as [k][row] (132-float rows).  Both are written with float4.
-// At BK = 16 the workgroup needs 40 KB of LDS and at most 168 VGPRs, so
+// [row][k] (rows of BK floats, padded by 4 floats after every 256 bytes);
+// operands whose free index is contiguous are stored as [k][row] (132-float
+// rows).  Both are written with float4 and read without bank conflicts.
+// At BK = 16 the workgroup needs 35 KB of LDS and at most 168 VGPRs, so
 // three share a compute unit.
 //
 // The epilogue stages each wave's 64x64 block through LDS in two 32-row
@@ -53,9 +54,15 @@ struct Tile;
 
 template <int R, int NT, int BK>
 struct Tile<true, R, NT, BK> {
-    static constexpr int FM_LD = BK + 4;  // [row][k] row stride
+    // [row][k]: rows of BK floats in groups of G = 64 / BK rows (256 bytes,
+    // all 64 banks) followed by 4 floats of padding.  A 16-lane float4 store
+    // (G rows of whole steps) and a 16-lane fragment read (one float4 of 16
+    // consecutive rows) then both touch 16 distinct groups of four banks.
+    static constexpr int G = 64 / BK;
+    static_assert(64 % BK == 0 && R % G == 0, "whole row groups");
     static constexpr int KV = BK / 4;     // float4 per row per step
-    static constexpr int FLOATS = R * FM_LD;
+    static constexpr int FLOATS = R * BK + (R / G) * 4;
+    static __device__ __forceinline__ int off(int r) { return r * BK + (r / G) * 4; }
     static constexpr int PER = R * KV / NT;
     float4 v[PER];
     // Rows past the matrix read its last row instead (their products land
@@ -86,11 +93,11 @@ struct Tile<true, R, NT, BK> {
 #pragma unroll
         for (int i = 0; i < PER; i++) {
             const int idx = threadIdx.x + NT * i;
-            st4(s + (idx / KV) * FM_LD + (idx % KV) * 4, v[i]);
+            st4(s + off(idx / KV) + (idx % KV) * 4, v[i]);
         }
     }
     __device__ static __forceinline__ float4 frag(const float* s, int r, int g, int q) {
-        return ld4(s + r * FM_LD + (BK / 2) * g + 4 * q);
+        return ld4(s + off(r) + (BK / 2) * g + 4 * q);
     }
 };
 
