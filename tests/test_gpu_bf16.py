@@ -53,7 +53,7 @@ def pair(name):
 
 
 @pytest.mark.parametrize("name", ["tiny", "ragged", "ragged80", "gpt2_124m_b4t64",
-                                  "ragged_rope", "wide_vocab"])
+                                  "ragged_rope", "wide_vocab", "tiny_long"])
 def test_bf16_step(name):
     m, o, c = pair(name)
     tok, tgt = synth.token_stream(c["B"], c["T"], c["V"])

@@ -141,7 +141,7 @@ def check_step(P, tok, tgt, lr=1e-4, wd=0.0):
 
 
 @pytest.mark.parametrize("name", ["tiny", "ragged", "small", "ragged80", "gpt2_124m_b4t64",
-                                  "tiny_rope", "ragged_rope", "wide_vocab"])
+                                  "tiny_rope", "ragged_rope", "wide_vocab", "tiny_long"])
 def test_one_training_step(name):
     P = Pair(name)
     tok, tgt = synth.token_stream(P.B, P.T, P.c["V"])
@@ -149,7 +149,7 @@ def test_one_training_step(name):
     P.close()
 
 
-@pytest.mark.parametrize("name", ["tiny", "ragged", "small", "ragged_rope"])
+@pytest.mark.parametrize("name", ["tiny", "ragged", "small", "ragged_rope", "tiny_long"])
 def test_one_training_step_recomputing_attention(name):
     """The attention backward without the dS workspace (its dQ kernel
     recomputes the scores) against the oracle."""
