@@ -187,3 +187,54 @@ def test_bf16_batch_step(inputs, gpu16, orc):
     print("[full] bf16 grad rel:", {k: f"{v:.2e}" for k, v in errs.items()}, flush=True)
     assert all(v < BF16_GRAD_BOUND for v in errs.values()), errs
     assert np.all(np.isfinite(gpu16["params1"]))
+
+
+@pytest.mark.parametrize("prec", ["fp32", "bf16"])
+def test_max_batch_equals_its_halves(prec, monkeypatch):
+    """The largest batch the limits allow at T = 1024: B = 32, B*T = 32768
+    (the 32-key embedding sort, the weight gradients split over K = 32768,
+    a 960 MiB attention dS workspace), with guard words after every buffer.
+    Sequences never interact, so the batch loss is the mean of the two
+    16-sequence halves' losses and the batch gradient the mean of their
+    gradients; the halves run on a second model allocated for B = 16.
+    Tolerances: loss rel 1e-6 (same per-row losses, another summation
+    order), gradients rel 1e-4 fp32 / the bf16 bound (sums over K split
+    differently)."""
+    g = gpt2()
+    p = g.GPT2_FP32 if prec == "fp32" else g.GPT2_BF16_MIXED
+    monkeypatch.setenv("GPT2_GUARD_WORDS", "1")
+    params = synth.init_params(CFG["L"], CFG["C"], V, CFG["maxT"])
+    tok, tgt = synth.token_stream(2 * B, T, V)
+    print(f"[full] B=32 step, precision {prec}", flush=True)
+    m = g.Model(CFG["L"], CFG["C"], CFG["NH"], V, CFG["maxT"], 2 * B, T, precision=p)
+    m.set_params(params)
+    dtok = torch.tensor(tok, dtype=torch.int32, device="cuda")
+    dtgt = torch.tensor(tgt, dtype=torch.int32, device="cuda")
+    loss = m.forward_device(dtok, dtgt)
+    m.zero_grad()
+    m.backward()
+    G = m.grads().astype(np.float64)
+    m.check_guards()
+    m.close()
+    m = g.Model(CFG["L"], CFG["C"], CFG["NH"], V, CFG["maxT"], B, T, precision=p)
+    m.set_params(params)
+    hl, hg = [], np.zeros_like(G)
+    for h in range(2):
+        hl.append(m.forward_device(dtok[h * B:(h + 1) * B].contiguous(),
+                                   dtgt[h * B:(h + 1) * B].contiguous()))
+        m.zero_grad()
+        m.backward()
+        hg += m.grads()
+    m.check_guards()
+    m.close()
+    torch.cuda.synchronize()
+    lref = (hl[0] + hl[1]) / 2
+    print(f"[full] B=32 {prec} loss {loss:.7f}, halves {hl}", flush=True)
+    assert abs(loss - lref) / lref < 1e-6, (loss, hl)
+    sizes, _ = oracle.param_sizes(CFG["L"], CFG["C"], CFG["NH"], V, CFG["maxT"])
+    GG, RR = split(G, sizes), split(hg / 2, sizes)
+    errs = {n: rel(GG[n], RR[n]) for n in oracle.PARAM_NAMES}
+    print(f"[full] B=32 {prec} grad rel to the halves:", {k: f"{v:.1e}" for k, v in errs.items()},
+          flush=True)
+    bound = 1e-4 if prec == "fp32" else BF16_GRAD_BOUND
+    assert all(v < bound for v in errs.values()), errs
