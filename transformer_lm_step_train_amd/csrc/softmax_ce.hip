@@ -29,8 +29,8 @@ __device__ __forceinline__ float block_max(float v, float* sh) {
     return r;
 }
 
-template <int NT, int NJ, bool GRAD, class T>
-__global__ __launch_bounds__(NT) __attribute__((amdgpu_waves_per_eu(4))) void softmax_ce_kernel(T* __restrict__ logits,
+template <int NT, int NJ, bool GRAD, class T, int WPE = 4>
+__global__ __launch_bounds__(NT) __attribute__((amdgpu_waves_per_eu(WPE))) void softmax_ce_kernel(T* __restrict__ logits,
                                                         float* __restrict__ losses,
                                                         const int32_t* __restrict__ targets,
                                                         int V, int ldv, float dscale,
@@ -128,15 +128,15 @@ __global__ __launch_bounds__(NT) __attribute__((amdgpu_waves_per_eu(4))) void so
     if (owner) Act<T>::st1(z + tgt, __builtin_amdgcn_exp2f(fmaf(zt, LOG2E, -ms)) * f - dscale);
 }
 
-template <int NT, int NJ, class T>
+template <int NT, int NJ, class T, int WPE = 4>
 hipError_t launch_ce(hipStream_t s, T* logits, float* losses, const int32_t* targets, int N,
                      int V, int ldv, float dscale, const float* gscale, int* flag) {
     if (dscale != 0.f)
-        launch((softmax_ce_kernel<NT, NJ, true, T>), dim3(N), dim3(NT), 0, s, logits, losses,
+        launch((softmax_ce_kernel<NT, NJ, true, T, WPE>), dim3(N), dim3(NT), 0, s, logits, losses,
                targets, V, ldv, dscale, gscale, flag);
     else
-        launch((softmax_ce_kernel<NT, NJ, false, T>), dim3(N), dim3(NT), 0, s, logits, losses,
-               targets, V, ldv, dscale, gscale, flag);
+        launch((softmax_ce_kernel<NT, NJ, false, T, WPE>), dim3(N), dim3(NT), 0, s, logits,
+               losses, targets, V, ldv, dscale, gscale, flag);
     return hipGetLastError();
 }
 
@@ -153,6 +153,14 @@ hipError_t softmax_ce_t(hipStream_t s, T* logits, float* losses, const int32_t* 
     if (nj <= 4) return launch_ce<512, 4>(s, logits, losses, targets, N, V, ldv, dscale, gs, flag);
     if (nj <= 8) return launch_ce<512, 8>(s, logits, losses, targets, N, V, ldv, dscale, gs, flag);
     if (nj <= 16) return launch_ce<512, 16>(s, logits, losses, targets, N, V, ldv, dscale, gs, flag);
+    // 16-bit rows up to 53248 columns: 1024 threads of 13 groups and two rows
+    // per compute unit (8 waves per SIMD, 64 VGPRs: three of one group's
+    // exponentials spill to scratch once per row).  On GPT-2's 50304-wide
+    // rows 677 against 827 us in bf16 (standalone), where the 512-thread rows
+    // keep too few bytes in flight; in fp32 the gain is 3%, so fp32 keeps the
+    // spill-free 512-thread rows.
+    if (sizeof(T) == 2 && (V4 + 1023) / 1024 <= 13)
+        return launch_ce<1024, 13, T, 8>(s, logits, losses, targets, N, V, ldv, dscale, gs, flag);
     if (nj <= 25) return launch_ce<512, 25>(s, logits, losses, targets, N, V, ldv, dscale, gs, flag);
     // rows past 51200 columns (up to 65536): one 1024-thread workgroup per
     // compute unit, 16 groups per thread, so the row still fits in registers
