@@ -140,8 +140,10 @@ hipError_t launch_ce(hipStream_t s, T* logits, float* losses, const int32_t* tar
     return hipGetLastError();
 }
 
-// 512-thread workgroups, so that two rows share a compute unit and one
-// row's loads overlap the other's reduction and stores.
+// Two rows share a compute unit, so that one row's loads overlap the other's
+// reduction and stores: 512-thread workgroups, except the 16-bit rows of up
+// to 53248 columns (1024 threads) and rows past 51200 columns (1024 threads,
+// one row per compute unit).
 template <class T>
 hipError_t softmax_ce_t(hipStream_t s, T* logits, float* losses, const int32_t* targets, int N,
                         int V, int ldv, float dscale, const float* gs, int* flag) {
