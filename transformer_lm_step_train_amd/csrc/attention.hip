@@ -58,20 +58,22 @@ __device__ __forceinline__ void zero16(floatx16& x) {
 }
 
 // One 64-row tile of one head (HS floats per row), held in registers between
-// its global load and its LDS store.  Rows at or past T are zero.
+// its global load and its LDS store.
 template <int HS>
 struct TileRegs {
     static constexpr int C4 = HS / 4;
     static constexpr int PER = AT * C4 / 256;  // float4 per thread
     float4 v[PER];
+    // Rows past the sequence read its last row instead: every product they
+    // enter is masked (their scores are -inf, their probabilities and dS 0),
+    // so any finite values serve, and the loads need no branches.
     template <class E>
     __device__ __forceinline__ void load(const E* __restrict__ base, int64_t ld, int r0, int T) {
 #pragma unroll
         for (int i = 0; i < PER; i++) {
             const int idx = threadIdx.x + 256 * i;
             const int r = idx / C4, c = (idx - r * C4) * 4;
-            v[i] = r0 + r < T ? Act<E>::ld(base + (int64_t)(r0 + r) * ld + c)
-                              : make_float4(0.f, 0.f, 0.f, 0.f);
+            v[i] = Act<E>::ld(base + (int64_t)min(r0 + r, T - 1) * ld + c);
         }
     }
     __device__ __forceinline__ void store(float* sm) const {
@@ -138,7 +140,9 @@ __global__ __launch_bounds__(256, 2) void attn_fwd_kernel(E* __restrict__ out,
         }
     }
     const int b = bh / NH, h = bh - b * NH;
-    const int lane = threadIdx.x & 63, wave = threadIdx.x >> 6;
+    // the wave index in a scalar register, so that every per-wave offset
+    // is scalar (buffer offsets then need no per-lane loop)
+    const int lane = threadIdx.x & 63, wave = __builtin_amdgcn_readfirstlane(threadIdx.x >> 6);
     const int li = lane & 31, g = lane >> 5;
     const int64_t ld = 3 * (int64_t)C;
     const E* qbase = qkv + (int64_t)b * T * ld + h * HS;
@@ -275,7 +279,7 @@ __global__ __launch_bounds__(256, 2) void attn_bwd_dq_kernel(
     const int bh = blockIdx.x % nbh;
     const int qb = nqb - 1 - blockIdx.x / nbh;  // longest first
     const int b = bh / NH, h = bh - b * NH;
-    const int lane = threadIdx.x & 63, wave = threadIdx.x >> 6;
+    const int lane = threadIdx.x & 63, wave = __builtin_amdgcn_readfirstlane(threadIdx.x >> 6);
     const int li = lane & 31, g = lane >> 5;
     const int64_t ld = 3 * (int64_t)C;
     const E* qbase = qkv + (int64_t)b * T * ld + h * HS;
@@ -413,14 +417,14 @@ __global__ __launch_bounds__(256, 2) void attn_bwd_dkdv_kernel(
     constexpr int LD = HS + 4, HALF = HS / 2, NDB = (HS + 31) / 32;
     __shared__ __attribute__((aligned(16))) float qs[2][AT * LD];
     __shared__ __attribute__((aligned(16))) float dos[2][AT * LD];
-    __shared__ float lsm[2][AT], dsm[2][AT];
+    __shared__ __attribute__((aligned(16))) float lsm[2][AT], dsm[2][AT];
 
     const int nkb = (T + AQ - 1) / AQ;
     const int nbh = gridDim.x / nkb;
     const int bh = blockIdx.x % nbh;
     const int kb0 = blockIdx.x / nbh;  // lowest keys = most query tiles: first
     const int b = bh / NH, h = bh - b * NH;
-    const int lane = threadIdx.x & 63, wave = threadIdx.x >> 6;
+    const int lane = threadIdx.x & 63, wave = __builtin_amdgcn_readfirstlane(threadIdx.x >> 6);
     const int li = lane & 31, g = lane >> 5;
     const int64_t ld = 3 * (int64_t)C;
     const E* qbase = qkv + (int64_t)b * T * ld + h * HS;
@@ -474,15 +478,18 @@ __global__ __launch_bounds__(256, 2) void attn_bwd_dkdv_kernel(
     const int qt0 = (kb0 * AQ) / AT;
     const int nqt = (T + AT - 1) / AT;
     TileRegs<HS> qreg, dreg;
-    float sreg = 0.f;  // one lse (threads 0..63) or D (64..127) value per thread
+    float sreg = 0.f;  // one lse (wave 0) or D (the other waves) value per thread
+    // wave 0 loads the tile's lse, the other waves its D (waves 2 and 3
+    // redundantly); positions past the sequence read its last one (their
+    // probabilities are masked to 0).  The base-2 scaling waits for the LDS
+    // store, so the load stays in flight with the tile's.
     auto load_stats = [&](int qt) {
-        const int i = threadIdx.x & 63, t = qt * AT + i;
-        if (threadIdx.x < 64) sreg = t < T ? lse[srow + t] * LOG2E : 0.f;
-        else if (threadIdx.x < 128) sreg = t < T ? D[srow + t] : 0.f;
+        const int t = min(qt * AT + lane, T - 1);
+        sreg = (wave == 0 ? lse : D)[srow + t];
     };
     auto store_stats = [&](int buf) {
-        if (threadIdx.x < 64) lsm[buf][threadIdx.x] = sreg;
-        else if (threadIdx.x < 128) dsm[buf][threadIdx.x - 64] = sreg;
+        if (wave == 0) lsm[buf][lane] = sreg * LOG2E;
+        else if (wave == 1) dsm[buf][lane] = sreg;
     };
     qreg.load(qbase, ld, qt0 * AT, T);
     dreg.load(dobase, C, qt0 * AT, T);
@@ -494,43 +501,61 @@ __global__ __launch_bounds__(256, 2) void attn_bwd_dkdv_kernel(
     for (int qt = qt0; qt < nqt; qt++) {
         const int cur = (qt - qt0) & 1;
         if (qt + 1 < nqt) {
+            load_stats(qt + 1);  // first, so that its wait is not behind the dS stores
             qreg.load(qbase, ld, (qt + 1) * AT, T);
             dreg.load(dobase, C, (qt + 1) * AT, T);
-            load_stats(qt + 1);
         }
         const float* qsm = qs[cur];
         const float* dsmem = dos[cur];
 #pragma unroll
         for (int qh = 0; qh < 2; qh++) {
             const int qlo = qt * AT + qh * 32;
-            if (kw >= T || qlo + 31 < kw || qlo >= T) continue;  // empty under the mask
+            const bool run = kw < T && qlo + 31 >= kw && qlo < T;  // else empty under the mask
             floatx16 sc, dp;
             zero16(sc);
             zero16(dp);
-            const float* qrow = qsm + (qh * 32 + li) * LD + g * HALF;
-            const float* drow = dsmem + (qh * 32 + li) * LD + g * HALF;
+            if (run) {
+                const float* qrow = qsm + (qh * 32 + li) * LD + g * HALF;
+                const float* drow = dsmem + (qh * 32 + li) * LD + g * HALF;
 #pragma unroll
-            for (int s = 0; s < HALF; s += 4) {
-                const float4 qf = ld4(qrow + s);
-                const float4 df = ld4(drow + s);
-                sc = mfma(qf.x, kr[s], sc);
-                sc = mfma(qf.y, kr[s + 1], sc);
-                sc = mfma(qf.z, kr[s + 2], sc);
-                sc = mfma(qf.w, kr[s + 3], sc);
-                dp = mfma(df.x, vr[s], dp);
-                dp = mfma(df.y, vr[s + 1], dp);
-                dp = mfma(df.z, vr[s + 2], dp);
-                dp = mfma(df.w, vr[s + 3], dp);
-            }
+                for (int s = 0; s < HALF; s += 4) {
+                    const float4 qf = ld4(qrow + s);
+                    const float4 df = ld4(drow + s);
+                    sc = mfma(qf.x, kr[s], sc);
+                    sc = mfma(qf.y, kr[s + 1], sc);
+                    sc = mfma(qf.z, kr[s + 2], sc);
+                    sc = mfma(qf.w, kr[s + 3], sc);
+                    dp = mfma(df.x, vr[s], dp);
+                    dp = mfma(df.y, vr[s + 1], dp);
+                    dp = mfma(df.z, vr[s + 2], dp);
+                    dp = mfma(df.w, vr[s + 3], dp);
+                }
+                // steps e = 4c..4c+3 hold queries qh*32 + 8c + 4g + (0..3): one
+                // float4 of each statistic; the mask is a select, not a branch
 #pragma unroll
-            for (int e = 0; e < 16; e++) {
-                const int ql = qh * 32 + 8 * (e >> 2) + 4 * g + (e & 3);
-                const int qa = qt * AT + ql;
-                const bool live = (qa < T) & (key <= qa);
-                const float p = live ? exp2_fast(sc[e] - lsm[cur][ql]) : 0.f;
-                sc[e] = p;
-                dp[e] = p * (dp[e] - dsm[cur][ql]);
+                for (int c = 0; c < 4; c++) {
+                    const int ql = qh * 32 + 8 * c + 4 * g;
+                    const float4 l4 = ld4(&lsm[cur][ql]), d4 = ld4(&dsm[cur][ql]);
+                    const float lv[4] = {l4.x, l4.y, l4.z, l4.w}, dv4[4] = {d4.x, d4.y, d4.z, d4.w};
+#pragma unroll
+                    for (int j = 0; j < 4; j++) {
+                        const int e = 4 * c + j, qa = qt * AT + ql + j;
+                        const bool live = (qa < T) & (key <= qa);
+                        const float p = live ? exp2_fast(sc[e] - lv[j]) : 0.f;
+                        sc[e] = p;
+                        dp[e] = p * (dp[e] - dv4[j]);
+                    }
+                }
             }
+            if (qh == 0 && qt + 1 < nqt) {
+                // The next tile goes into the other buffer (free since the last
+                // barrier) before any dS store of this tile: waiting for its
+                // loads then never waits for those stores as well.
+                qreg.store(qs[cur ^ 1]);
+                dreg.store(dos[cur ^ 1]);
+                store_stats(cur ^ 1);
+            }
+            if (!run) continue;
             if constexpr (STORE_DS) {  // this wave's 32 keys x 32 queries of dS^T
                 const int so = (int)((ds_block(qt >> 1, kb0) + (wave * 32) * AQ) * 4);
                 const int vo = (li * AQ + (qt & 1) * AT + qh * 32 + 4 * g) * 4;
@@ -562,11 +587,6 @@ __global__ __launch_bounds__(256, 2) void attn_bwd_dkdv_kernel(
                         dk[d] = mfma(qa[i][d], dp[half * 8 + i], dk[d]);
                     }
             }
-        }
-        if (qt + 1 < nqt) {
-            qreg.store(qs[cur ^ 1]);
-            dreg.store(dos[cur ^ 1]);
-            store_stats(cur ^ 1);
         }
         __syncthreads();
     }
@@ -619,7 +639,7 @@ __global__ __launch_bounds__(256, 2) void attn_bwd_dq_ds_kernel(
     const int bh = blockIdx.x % nbh;
     const int qb = nqb - 1 - blockIdx.x / nbh;  // longest first
     const int b = bh / NH, h = bh - b * NH;
-    const int lane = threadIdx.x & 63, wave = threadIdx.x >> 6;
+    const int lane = threadIdx.x & 63, wave = __builtin_amdgcn_readfirstlane(threadIdx.x >> 6);
     const int li = lane & 31, g = lane >> 5;
     const int qw = qb * AQ + wave * 32;
     if (qw >= T) return;  // whole wave

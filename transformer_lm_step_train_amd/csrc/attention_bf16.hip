@@ -214,7 +214,7 @@ __global__ __launch_bounds__(256, 2) void attn16_fwd_kernel(uint16_t* __restrict
 #pragma unroll
                     for (int e = 0; e < 16; e++) {
                         const int key = k0 + kb * 32 + 8 * (e >> 2) + 4 * g + (e & 3);
-                        sc[kb][e] = (key > q) | (key >= T) ? -INFINITY : sc[kb][e];
+                        sc[kb][e] = ((key > q) | (key >= T)) ? -INFINITY : sc[kb][e];
                     }
             }
             float mt = -INFINITY;
@@ -383,14 +383,14 @@ __global__ __launch_bounds__(256, 3) void attn16_dkdv_kernel(
     constexpr int NKS = HS / 16, NDB = (HS + 31) / 32, LDK = NDB * 32 + 8;
     __shared__ __attribute__((aligned(16))) uint16_t qs[2][RT * LDK];
     __shared__ __attribute__((aligned(16))) uint16_t ds[2][RT * LDK];
-    __shared__ float lsm[2][RT], dsm[2][RT];
+    __shared__ __attribute__((aligned(16))) float lsm[2][RT], dsm[2][RT];
 
     const int nkb = (T + RQ - 1) / RQ;
     const int nbh = gridDim.x / nkb;
     const int bh = blockIdx.x % nbh;
     const int kb0 = blockIdx.x / nbh;  // lowest keys = most query tiles: first
     const int b = bh / NH, h = bh - b * NH;
-    const int lane = threadIdx.x & 63, wave = threadIdx.x >> 6;
+    const int lane = threadIdx.x & 63, wave = __builtin_amdgcn_readfirstlane(threadIdx.x >> 6);
     const int li = lane & 31, g = lane >> 5;
     const int64_t ld = 3 * (int64_t)C;
     const uint16_t* base = qkv + (int64_t)b * T * ld + h * HS;
@@ -419,15 +419,16 @@ __global__ __launch_bounds__(256, 3) void attn16_dkdv_kernel(
     const int qt0 = (kb0 * RQ) / RT;
     const int nqt = (T + RT - 1) / RT;
     Tile16<HS> qreg, dreg;
-    float sreg = 0.f;  // one lse (threads 0..63) or D (64..127) value per thread
-    auto load_stats = [&](int qt) {  // every thread loads (a fixed count per step)
-        const int t = min(qt * RT + (threadIdx.x & 63), T - 1);
-        const float x = (threadIdx.x < 64 ? lse : D)[srow + t];
-        sreg = threadIdx.x < 64 ? x * L2E : x;
+    float sreg = 0.f;  // one lse (wave 0) or D (the other waves) value per thread
+    // every thread loads (a fixed count per step); the base-2 scaling of lse
+    // waits for the LDS store, so the load stays in flight with the tile's
+    auto load_stats = [&](int qt) {
+        const int t = min(qt * RT + lane, T - 1);
+        sreg = (wave == 0 ? lse : D)[srow + t];
     };
     auto store_stats = [&](int buf) {
-        if (threadIdx.x < 64) lsm[buf][threadIdx.x] = sreg;
-        else if (threadIdx.x < 128) dsm[buf][threadIdx.x - 64] = sreg;
+        if (wave == 0) lsm[buf][lane] = sreg * L2E;
+        else if (wave == 1) dsm[buf][lane] = sreg;
     };
     qreg.load(base, ld, qt0 * RT, T);
     dreg.load(dobase, C, qt0 * RT, T);
@@ -439,9 +440,9 @@ __global__ __launch_bounds__(256, 3) void attn16_dkdv_kernel(
     for (int qt = qt0; qt < nqt; qt++) {
         const int cur = (qt - qt0) & 1;
         const int nxt = min(qt + 1, nqt - 1);
+        load_stats(nxt);
         qreg.load(base, ld, nxt * RT, T);
         dreg.load(dobase, C, nxt * RT, T);
-        load_stats(nxt);
 #pragma unroll
         for (int qh = 0; qh < 2; qh++) {
             const int qlo = qt * RT + qh * 32;
@@ -456,15 +457,22 @@ __global__ __launch_bounds__(256, 3) void attn16_dkdv_kernel(
                 sc = H::mma(rd(qr + 16 * j), kv[j], sc);
                 dp = H::mma(rd(dr + 16 * j), vv[j], dp);
             }
+            // steps e = 4c..4c+3 hold queries qh*32 + 8c + 4g + (0..3): one
+            // float4 of each statistic; the mask is a select, not a branch
 #pragma unroll
-            for (int e = 0; e < 16; e++) {
-                const int ql = qh * 32 + 8 * (e >> 2) + 4 * g + (e & 3);
-                const int qa = qt * RT + ql;
-                const bool live = (qa < T) & (key <= qa);
-                const float p =
-                    live ? __builtin_amdgcn_exp2f(fmaf(sc[e], qscale, -lsm[cur][ql])) : 0.f;
-                sc[e] = p;
-                dp[e] = p * (dp[e] - dsm[cur][ql]);
+            for (int c = 0; c < 4; c++) {
+                const int ql = qh * 32 + 8 * c + 4 * g;
+                const float4 l4 = *reinterpret_cast<const float4*>(&lsm[cur][ql]);
+                const float4 d4 = *reinterpret_cast<const float4*>(&dsm[cur][ql]);
+                const float lv[4] = {l4.x, l4.y, l4.z, l4.w}, dv4[4] = {d4.x, d4.y, d4.z, d4.w};
+#pragma unroll
+                for (int j = 0; j < 4; j++) {
+                    const int e = 4 * c + j, qa = qt * RT + ql + j;
+                    const bool live = (qa < T) & (key <= qa);
+                    const float p = live ? __builtin_amdgcn_exp2f(fmaf(sc[e], qscale, -lv[j])) : 0.f;
+                    sc[e] = p;
+                    dp[e] = p * (dp[e] - dv4[j]);
+                }
             }
 #pragma unroll
             for (int hh = 0; hh < 2; hh++) {
