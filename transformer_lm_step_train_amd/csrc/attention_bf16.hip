@@ -70,7 +70,12 @@ struct Tile16 {
     static constexpr int CH = HS / 8;             // 16-byte chunks per row
     static constexpr int N = RT * CH;             // chunks per tile
     static constexpr int PER = (N + 255) / 256;   // per thread
-    uint4 v[PER];
+    // A native vector, not the uint4 struct: a struct is copied as a memcpy,
+    // and the optimizer then forwards global -> registers -> LDS into one
+    // global-to-LDS copy at the LDS store, which issues the load there
+    // instead of a whole step ahead.
+    typedef unsigned int chunk_t __attribute__((ext_vector_type(4)));
+    chunk_t v[PER];
     __device__ __forceinline__ void load(const uint16_t* __restrict__ base, int64_t ld, int r0,
                                          int T) {
 #pragma unroll
@@ -78,7 +83,7 @@ struct Tile16 {
             const int idx = threadIdx.x + 256 * i;
             if (N % 256 == 0 || idx < N) {
                 const int r = min(r0 + idx / CH, T - 1), c = (idx % CH) * 8;
-                v[i] = *reinterpret_cast<const uint4*>(base + (int64_t)r * ld + c);
+                v[i] = *reinterpret_cast<const chunk_t*>(base + (int64_t)r * ld + c);
             }
         }
     }
@@ -89,7 +94,7 @@ struct Tile16 {
         for (int i = 0; i < PER; i++) {
             const int idx = threadIdx.x + 256 * i;
             if (N % 256 == 0 || idx < N)
-                *reinterpret_cast<uint4*>(sm + (idx / CH) * LD + (idx % CH) * 8) = v[i];
+                *reinterpret_cast<chunk_t*>(sm + (idx / CH) * LD + (idx % CH) * 8) = v[i];
         }
     }
 };
@@ -372,11 +377,12 @@ __global__ __launch_bounds__(256, 3) void attn16_dq_kernel(
 
 // dK and dV (lane owns a key).  Q and dout are staged as rows, read as 16
 // bytes for S = Q K^T and dP = dout V^T (queries down the accumulator) and
-// with the transposing reads for dK^T = Q^T dS and dV^T = dout^T P.  At 175
-// VGPRs it spills a few registers at three workgroups per compute unit and
-// still measured 5% faster than at two.
+// with the transposing reads for dK^T = Q^T dS and dV^T = dout^T P.  With
+// the next tile's loads issued a whole step ahead it needs 200 VGPRs, so two
+// workgroups share a compute unit (capped for three it spills, and the spill
+// reloads then wait for the prefetch).
 template <int HS, class H>
-__global__ __launch_bounds__(256, 3) void attn16_dkdv_kernel(
+__global__ __launch_bounds__(256, 2) void attn16_dkdv_kernel(
     uint16_t* __restrict__ dqkv, const uint16_t* __restrict__ dout,
     const uint16_t* __restrict__ qkv, const float* __restrict__ lse, const float* __restrict__ D,
     int T, int C, int NH, float qscale, float scale) {
