@@ -473,11 +473,22 @@ __global__ __launch_bounds__(256, 2) void attn16_dkdv_kernel(
                 const float lv[4] = {l4.x, l4.y, l4.z, l4.w}, dv4[4] = {d4.x, d4.y, d4.z, d4.w};
 #pragma unroll
                 for (int j = 0; j < 4; j++) {
-                    const int e = 4 * c + j, qa = qt * RT + ql + j;
-                    const bool live = (qa < T) & (key <= qa);
-                    const float p = live ? __builtin_amdgcn_exp2f(fmaf(sc[e], qscale, -lv[j])) : 0.f;
+                    const int e = 4 * c + j;
+                    const float p = __builtin_amdgcn_exp2f(fmaf(sc[e], qscale, -lv[j]));
                     sc[e] = p;
                     dp[e] = p * (dp[e] - dv4[j]);
+                }
+            }
+            // the mask (selects, so masked infinities do not survive) only on
+            // blocks that touch it: the diagonal and the sequence end (the
+            // same test for the whole wave)
+            if (qlo < kw + 31 || qlo + 31 >= T) {
+#pragma unroll
+                for (int e = 0; e < 16; e++) {
+                    const int qa = qt * RT + qh * 32 + 8 * (e >> 2) + 4 * g + (e & 3);
+                    const bool live = (qa < T) & (key <= qa);
+                    sc[e] = live ? sc[e] : 0.f;
+                    dp[e] = live ? dp[e] : 0.f;
                 }
             }
 #pragma unroll
