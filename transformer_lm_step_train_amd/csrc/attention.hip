@@ -531,7 +531,7 @@ __global__ __launch_bounds__(256, 2) void attn_bwd_dkdv_kernel(
                     dp = mfma(df.w, vr[s + 3], dp);
                 }
                 // steps e = 4c..4c+3 hold queries qh*32 + 8c + 4g + (0..3): one
-                // float4 of each statistic; the mask is a select, not a branch
+                // float4 of each statistic
 #pragma unroll
                 for (int c = 0; c < 4; c++) {
                     const int ql = qh * 32 + 8 * c + 4 * g;
@@ -539,11 +539,22 @@ __global__ __launch_bounds__(256, 2) void attn_bwd_dkdv_kernel(
                     const float lv[4] = {l4.x, l4.y, l4.z, l4.w}, dv4[4] = {d4.x, d4.y, d4.z, d4.w};
 #pragma unroll
                     for (int j = 0; j < 4; j++) {
-                        const int e = 4 * c + j, qa = qt * AT + ql + j;
-                        const bool live = (qa < T) & (key <= qa);
-                        const float p = live ? exp2_fast(sc[e] - lv[j]) : 0.f;
+                        const int e = 4 * c + j;
+                        const float p = exp2_fast(sc[e] - lv[j]);
                         sc[e] = p;
                         dp[e] = p * (dp[e] - dv4[j]);
+                    }
+                }
+                // the mask as selects (masked infinities do not survive), only
+                // on blocks that touch it: the diagonal and the sequence end
+                // (the same test for the whole wave)
+                if (qlo < kw + 31 || qlo + 31 >= T) {
+#pragma unroll
+                    for (int e = 0; e < 16; e++) {
+                        const int qa = qt * AT + qh * 32 + 8 * (e >> 2) + 4 * g + (e & 3);
+                        const bool live = (qa < T) & (key <= qa);
+                        sc[e] = live ? sc[e] : 0.f;
+                        dp[e] = live ? dp[e] : 0.f;
                     }
                 }
             }

@@ -575,15 +575,7 @@ __global__ __launch_bounds__(NTHR, 3) void gemm_bf16_k32_kernel(const GemmArgsH 
         constexpr int NS = (S + 1) % PF;
         const int cur = kt & 1;
         issue(slotc, kt + PF);
-        // With three slots (outputs of at least 16384 columns, whose weight
-        // streams from memory) the step keeps its written order: loads,
-        // products, then the LDS stores.  The compiler otherwise moves the
-        // stores to the top of the step and the loads to its end, which
-        // measured 4% slower there (and 6-13% faster on the two-slot shapes,
-        // which keep it).
-        if constexpr (PF == 3) __builtin_amdgcn_sched_barrier(0);
         compute(smh + cur * TA::ELEMS, smh + 2 * TA::ELEMS + cur * TB::ELEMS);
-        if constexpr (PF == 3) __builtin_amdgcn_sched_barrier(0);
         // unconditional: no path reaches the next loads with this slot pending
         ta[NS].store(smh + (cur ^ 1) * TA::ELEMS);
         tb[NS].store(smh + 2 * TA::ELEMS + (cur ^ 1) * TB::ELEMS);
