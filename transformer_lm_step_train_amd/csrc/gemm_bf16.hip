@@ -954,6 +954,210 @@ __global__ __launch_bounds__(NTHR, (Shape<MI, NI>::OCC)) void gemm_bf16_big_kern
     }
 }
 
+// ---- weight gradients with the stages loaded straight into LDS -----------
+//
+// The TN products (both operands contiguous in the free index) on the same
+// 256x256 tiles, 4x4 blocks per wave and transposing fragment reads as the
+// kernel above, but each 32-deep stage goes from memory to LDS with
+// global_load_lds_dwordx4 (lane l writes bytes 16l..16l+15 after the wave's
+// LDS base), so no registers hold a stage on its way and no LDS store
+// instructions are issued.  Four stages, loaded three steps ahead; one
+// barrier per step.  Such a load writes 1 KB of LDS contiguously, so the
+// [k][256] stage rows are not padded: their 16-byte chunks are permuted by
+// 2 (k & 3) instead, which spreads the four rows of a transposing read over
+// the banks as 16 elements of padding did.  The loads choose which chunk of
+// the row each lane fetches, so that the chunk lands at its permuted place.
+// Results are bitwise those of the kernel above (same k order).  Needs
+// whole stages (K and the split chunk multiples of 32), leading dimensions
+// that are multiples of 8 and 16-byte aligned operands.
+constexpr int LBK = 32;               // k per stage
+constexpr int LSTAGE = LBK * 256;     // bf16 elements per operand per stage
+
+// element offset of (k, r) in a [32][256] stage
+__device__ __forceinline__ int lds_off(int k, int r) {
+    return k * 256 + (((r >> 3) ^ ((k & 3) << 1)) << 3) + (r & 7);
+}
+
+// operand of rows rb..rb+31 (lane li = row rb + li), k = 16q + 8g .. +7
+__device__ __forceinline__ uint4 lds_frag(const uint16_t* s, int rb, int q, int lane) {
+    const int grp = lane >> 4, rr = lane & 15;
+    const int r = rb + 16 * (grp & 1) + 4 * (rr & 3);
+    const int k = 16 * q + 8 * (grp >> 1) + (rr >> 2);
+    const tr4_t lo = __builtin_amdgcn_ds_read_tr16_b64_v4i16((lds_tr4_ptr)(s + lds_off(k, r)));
+    const tr4_t hi = __builtin_amdgcn_ds_read_tr16_b64_v4i16((lds_tr4_ptr)(s + lds_off(k + 4, r)));
+    const uint2 a = __builtin_bit_cast(uint2, lo), b = __builtin_bit_cast(uint2, hi);
+    return make_uint4(a.x, a.y, b.x, b.y);
+}
+
+// s_waitcnt immediates (vmcnt in bits 3:0 and 15:14, the others at maximum)
+constexpr unsigned kVm0 = 0x0f70, kVm8 = 0x0f78, kVm16 = 0x4f70, kLgkm0 = 0xc07f;
+
+template <int EPI, class H>
+__global__ __launch_bounds__(NTHR, 1) void gemm_bf16_tn_lds_kernel(const GemmArgsH a, int tiles_m,
+                                                                  int tiles_n, int kchunk,
+                                                                  float* __restrict__ partial) {
+    using SH = Shape<4, 4>;
+    constexpr int MI = 4, NI = 4;
+    // Eight distinct arrays, so that the compiler can tell the stage being
+    // refilled from the stage being read (with one array it waits for every
+    // load in flight before each read).
+    __shared__ __attribute__((aligned(16))) uint16_t SA0[LSTAGE], SA1[LSTAGE], SA2[LSTAGE],
+        SA3[LSTAGE], SB0[LSTAGE], SB1[LSTAGE], SB2[LSTAGE], SB3[LSTAGE];
+
+    const int tile = xcd_remap(blockIdx.x, tiles_m * tiles_n);
+    constexpr int GM = 8;
+    const int per_group = GM * tiles_n;
+    const int group = tile / per_group;
+    const int first_m = group * GM;
+    const int gm = min(tiles_m - first_m, GM);
+    const int in_g = tile - group * per_group;
+    const int m0 = (first_m + in_g % gm) * 256;
+    const int n0 = (in_g / gm) * 256;
+
+    const int k_begin = blockIdx.z * kchunk;
+    const int k_end = min(a.K, k_begin + kchunk);
+    const int nsteps = (k_end - k_begin) / LBK;  // whole stages (checked by the host)
+
+    const int lane = threadIdx.x & 63;
+    const int wave = __builtin_amdgcn_readfirstlane(threadIdx.x >> 6);
+    const int wm = (wave >> 1) * SH::WM, wn = (wave & 1) * SH::WN;
+    const int li = lane & 31, g = lane >> 5;
+
+    // Load j = wave + 4i (i = 0..3) of a stage fills its rows 2j and 2j + 1:
+    // lane l writes physical chunk l % 32 of row k = 2j + l / 32, the place of
+    // logical chunk (l % 32) ^ 2 (k & 3), with k & 3 = (2 wave + l / 32) & 3
+    // for every i.  Columns past the matrix read its last whole run of 8
+    // (they reach only outputs that are never stored).
+    const int kl = lane >> 5;
+    const int chunk = (lane & 31) ^ (((2 * wave + kl) & 3) << 1);
+    int ra = m0 + 8 * chunk, rb = n0 + 8 * chunk;
+    ra = ra < a.M ? ra : ((a.M - 1) & ~7);
+    rb = rb < a.N ? rb : ((a.N - 1) & ~7);
+    const uint16_t* ga = a.A + (int64_t)(k_begin + kl) * a.lda + ra;
+    const uint16_t* gb = a.B + (int64_t)(k_begin + kl) * a.ldb + rb;
+    auto issue = [&](int t, uint16_t* sa, uint16_t* sb) {
+        const int64_t kk = (int64_t)t * LBK;
+#pragma unroll
+        for (int i = 0; i < 4; i++) {
+            const int j = wave + 4 * i;
+            __builtin_amdgcn_global_load_lds(
+                (const void __attribute__((address_space(1)))*)(ga + (kk + 2 * j) * a.lda),
+                (void __attribute__((address_space(3)))*)(sa + j * 512), 16, 0, 0);
+            __builtin_amdgcn_global_load_lds(
+                (const void __attribute__((address_space(1)))*)(gb + (kk + 2 * j) * a.ldb),
+                (void __attribute__((address_space(3)))*)(sb + j * 512), 16, 0, 0);
+        }
+    };
+
+    floatx16 acc[MI][NI];
+#pragma unroll
+    for (int i = 0; i < MI; i++)
+#pragma unroll
+        for (int j = 0; j < NI; j++)
+#pragma unroll
+            for (int e = 0; e < 16; e++) acc[i][j][e] = 0.f;
+    // one stage: the fragments of the second 16-deep sub-step are read before
+    // the MFMAs of the first
+    auto compute = [&](const uint16_t* sa, const uint16_t* sb) {
+        uint4 af[2][MI], bf[2][NI];
+#pragma unroll
+        for (int i = 0; i < MI; i++) af[0][i] = lds_frag(sa, wm + 32 * i, 0, lane);
+#pragma unroll
+        for (int j = 0; j < NI; j++) bf[0][j] = lds_frag(sb, wn + 32 * j, 0, lane);
+#pragma unroll
+        for (int q = 0; q < 2; q++) {
+            if (q == 0) {
+#pragma unroll
+                for (int i = 0; i < MI; i++) af[1][i] = lds_frag(sa, wm + 32 * i, 1, lane);
+#pragma unroll
+                for (int j = 0; j < NI; j++) bf[1][j] = lds_frag(sb, wn + 32 * j, 1, lane);
+            }
+#pragma unroll
+            for (int i = 0; i < MI; i++)
+#pragma unroll
+                for (int j = 0; j < NI; j++) acc[i][j] = H::mma(af[q][i], bf[q][j], acc[i][j]);
+        }
+    };
+    // Before step t: this wave's loads of step t have landed once at most
+    // the loads of the (up to two) later steps already issued are in flight
+    // (eight per step); after the barrier every wave's have, and every wave
+    // has finished step t - 1, so stage (t + 3) % 4 = (t - 1) % 4 is free.
+    // The raw barrier: __syncthreads() would also wait for the loads in
+    // flight.
+    auto sync = [&](int later) {
+        if (later >= 2) __builtin_amdgcn_s_waitcnt(kVm16);
+        else if (later == 1) __builtin_amdgcn_s_waitcnt(kVm8);
+        else __builtin_amdgcn_s_waitcnt(kVm0);
+        __builtin_amdgcn_s_waitcnt(kLgkm0);
+        __builtin_amdgcn_sched_barrier(0);
+        __builtin_amdgcn_s_barrier();
+        __builtin_amdgcn_sched_barrier(0);
+    };
+    if (nsteps > 0) issue(0, SA0, SB0);
+    if (nsteps > 1) issue(1, SA1, SB1);
+    if (nsteps > 2) issue(2, SA2, SB2);
+    int t = 0;
+    for (; t + 7 < nsteps; t += 4) {  // every step refills a stage: no branches
+        sync(2);
+        issue(t + 3, SA3, SB3);
+        compute(SA0, SB0);
+        sync(2);
+        issue(t + 4, SA0, SB0);
+        compute(SA1, SB1);
+        sync(2);
+        issue(t + 5, SA1, SB1);
+        compute(SA2, SB2);
+        sync(2);
+        issue(t + 6, SA2, SB2);
+        compute(SA3, SB3);
+    }
+    uint16_t* const sas[4] = {SA0, SA1, SA2, SA3};
+    uint16_t* const sbs[4] = {SB0, SB1, SB2, SB3};
+#pragma unroll
+    for (int u = 0; u < 8; u++) {  // the last steps (at most seven; t % 4 == 0)
+        if (t + u < nsteps) {
+            sync(min(nsteps - 1 - (t + u), 2));
+            if (t + u + 3 < nsteps) issue(t + u + 3, sas[(u + 3) & 3], sbs[(u + 3) & 3]);
+            compute(sas[u & 3], sbs[u & 3]);
+        }
+    }
+    __builtin_amdgcn_s_waitcnt(kLgkm0);
+    __builtin_amdgcn_sched_barrier(0);
+    __builtin_amdgcn_s_barrier();  // every wave is done with the stages
+    __builtin_amdgcn_sched_barrier(0);
+
+    // Epilogue as in the kernel above; each wave stages its 32 x 128 fp32
+    // strips (16 KB, unpadded) in its own A stage.
+    constexpr int ELD = SH::WN;
+    float* ws = reinterpret_cast<float*>(wave == 0 ? SA0 : wave == 1 ? SA1 : wave == 2 ? SA2 : SA3);
+#pragma unroll
+    for (int i = 0; i < MI; i++) {
+#pragma unroll
+        for (int j = 0; j < NI; j++)
+#pragma unroll
+            for (int e = 0; e < 16; e++)
+                ws[(8 * (e >> 2) + 4 * g + (e & 3)) * ELD + 32 * j + li] = acc[i][j][e];
+        __builtin_amdgcn_s_waitcnt(kLgkm0);  // the strip is in LDS
+        __builtin_amdgcn_wave_barrier();
+        constexpr int C4 = SH::WN / 4;
+#pragma unroll 4
+        for (int idx = lane; idx < 32 * C4; idx += 64) {
+            const int r = idx / C4, c4 = (idx % C4) * 4;
+            const float4 v = ld4(ws + r * ELD + c4);
+            const int row = m0 + wm + 32 * i + r, col = n0 + wn + c4;
+            if (row >= a.M) continue;
+            if (col + 3 < a.N) {
+                epi4<EPI, H>(a, partial, row, col, v);
+            } else {
+                if (col < a.N) epi1<EPI, H>(a, partial, row, col, v.x);
+                if (col + 1 < a.N) epi1<EPI, H>(a, partial, row, col + 1, v.y);
+                if (col + 2 < a.N) epi1<EPI, H>(a, partial, row, col + 2, v.z);
+            }
+        }
+        __builtin_amdgcn_wave_barrier();
+    }
+}
+
 template <int EPI, class H>
 __global__ __launch_bounds__(256) void splitk_reduce_bf16_kernel(const GemmArgsH a,
                                                                  const float* __restrict__ partial,
@@ -1020,6 +1224,15 @@ hipError_t launch_big(hipStream_t s, const GemmArgsH& a, int splits, float* ws) 
     const int tm = cdiv(a.M, 256), tn = cdiv(a.N, 256);
     const int chunk = splits > 1 ? gemm16_split_chunk(a.K, splits) : (a.K > 0 ? a.K : 1);
     const int nz = splits > 1 ? cdiv(a.K, chunk) : 1;
+    if constexpr (OP == GEMM_TN) {
+        // the stages straight into LDS when they are whole and aligned
+        if (a.K % LBK == 0 && chunk % LBK == 0 && a.lda % 8 == 0 && a.ldb % 8 == 0 &&
+            (((uintptr_t)a.A | (uintptr_t)a.B) & 15) == 0) {
+            launch((gemm_bf16_tn_lds_kernel<EPI, H>), dim3(tm * tn, 1, nz), dim3(NTHR), 0, s, a,
+                   tm, tn, chunk, ws);
+            return hipGetLastError();
+        }
+    }
     launch((gemm_bf16_big_kernel<OP, EPI, 4, 4, H>), dim3(tm * tn, 1, nz), dim3(NTHR), 0,
                        s, a, tm, tn, chunk, ws);
     return hipGetLastError();
