@@ -954,22 +954,29 @@ __global__ __launch_bounds__(NTHR, (Shape<MI, NI>::OCC)) void gemm_bf16_big_kern
     }
 }
 
-// ---- weight gradients with the stages loaded straight into LDS -----------
+// ---- 256x256 products with the stages loaded straight into LDS ----------
 //
-// The TN products (both operands contiguous in the free index) on the same
-// 256x256 tiles, 4x4 blocks per wave and transposing fragment reads as the
-// kernel above, but each 32-deep stage goes from memory to LDS with
+// The weight gradients (TN) and the long-K input gradient (NN, K = V) on the
+// same 256x256 tiles, 4x4 blocks per wave and fragment reads as the kernel
+// above, but each 32-deep stage goes from memory to LDS with
 // global_load_lds_dwordx4 (lane l writes bytes 16l..16l+15 after the wave's
 // LDS base), so no registers hold a stage on its way and no LDS store
-// instructions are issued.  Four stages, loaded three steps ahead; one
-// barrier per step.  Such a load writes 1 KB of LDS contiguously, so the
-// [k][256] stage rows are not padded: their 16-byte chunks are permuted by
-// 2 (k & 3) instead, which spreads the four rows of a transposing read over
-// the banks as 16 elements of padding did.  The loads choose which chunk of
-// the row each lane fetches, so that the chunk lands at its permuted place.
-// Results are bitwise those of the kernel above (same k order).  Needs
-// whole stages (K and the split chunk multiples of 32), leading dimensions
-// that are multiples of 8 and 16-byte aligned operands.
+// instructions are issued: at one wave per SIMD every instruction of the
+// wave is on its critical path.  Four stages, loaded three steps ahead; one
+// raw barrier per step.  Such a load writes 1 KB of LDS contiguously, so the
+// stage rows are not padded; their 16-byte chunks are permuted instead, and
+// each lane fetches the chunk that belongs at its place:
+//   - free index contiguous ([k][256]: both TN operands, the NN weight),
+//     chunk c of row k at c ^ 2 (k & 3), the bank spread of 16 elements of
+//     padding for the transposing reads;
+//   - reduction index contiguous ([256][32]: the NN A operand), chunk c of
+//     row r at c ^ ((r >> 2) & 3), so the 8 rows one 16-byte read serves at
+//     a time fall on distinct banks.
+// A partial last stage (K not a multiple of 32, the last split only) is
+// loaded through registers with zero padding into the same layout.  The
+// k order is that of the kernel above, so results are bitwise equal.
+// Needs split chunks that are multiples of 32, leading dimensions that are
+// multiples of 8 and 16-byte aligned operands.
 constexpr int LBK = 32;               // k per stage
 constexpr int LSTAGE = LBK * 256;     // bf16 elements per operand per stage
 
@@ -977,8 +984,13 @@ constexpr int LSTAGE = LBK * 256;     // bf16 elements per operand per stage
 __device__ __forceinline__ int lds_off(int k, int r) {
     return k * 256 + (((r >> 3) ^ ((k & 3) << 1)) << 3) + (r & 7);
 }
+// element offset of (r, k) in a [256][32] stage
+__device__ __forceinline__ int lds_off_kc(int r, int k) {
+    return r * LBK + (((k >> 3) ^ ((r >> 2) & 3)) << 3) + (k & 7);
+}
 
-// operand of rows rb..rb+31 (lane li = row rb + li), k = 16q + 8g .. +7
+// operand of rows rb..rb+31 (lane li = row rb + li), k = 16q + 8g .. +7,
+// from a [32][256] stage, with two transposing reads
 __device__ __forceinline__ uint4 lds_frag(const uint16_t* s, int rb, int q, int lane) {
     const int grp = lane >> 4, rr = lane & 15;
     const int r = rb + 16 * (grp & 1) + 4 * (rr & 3);
@@ -988,14 +1000,20 @@ __device__ __forceinline__ uint4 lds_frag(const uint16_t* s, int rb, int q, int 
     const uint2 a = __builtin_bit_cast(uint2, lo), b = __builtin_bit_cast(uint2, hi);
     return make_uint4(a.x, a.y, b.x, b.y);
 }
+// the same operand from a [256][32] stage: one 16-byte read
+__device__ __forceinline__ uint4 lds_frag_kc(const uint16_t* s, int rb, int q, int lane) {
+    return *reinterpret_cast<const uint4*>(s + lds_off_kc(rb + (lane & 31), 16 * q + 8 * (lane >> 5)));
+}
 
 // s_waitcnt immediates (vmcnt in bits 3:0 and 15:14, the others at maximum)
 constexpr unsigned kVm0 = 0x0f70, kVm8 = 0x0f78, kVm16 = 0x4f70, kLgkm0 = 0xc07f;
 
-template <int EPI, class H>
-__global__ __launch_bounds__(NTHR, 1) void gemm_bf16_tn_lds_kernel(const GemmArgsH a, int tiles_m,
-                                                                  int tiles_n, int kchunk,
-                                                                  float* __restrict__ partial) {
+template <int OP, int EPI, class H>
+__global__ __launch_bounds__(NTHR, 1) void gemm_bf16_lds_kernel(const GemmArgsH a, int tiles_m,
+                                                               int tiles_n, int kchunk,
+                                                               float* __restrict__ partial) {
+    static_assert(OP == GEMM_TN || OP == GEMM_NN, "TN or NN");
+    constexpr bool AKC = OP == GEMM_NN;  // A contiguous along k
     using SH = Shape<4, 4>;
     constexpr int MI = 4, NI = 4;
     // Eight distinct arrays, so that the compiler can tell the stage being
@@ -1016,35 +1034,56 @@ __global__ __launch_bounds__(NTHR, 1) void gemm_bf16_tn_lds_kernel(const GemmArg
 
     const int k_begin = blockIdx.z * kchunk;
     const int k_end = min(a.K, k_begin + kchunk);
-    const int nsteps = (k_end - k_begin) / LBK;  // whole stages (checked by the host)
+    const int nsteps = (k_end - k_begin) / LBK;  // whole stages; the rest is the tail
 
     const int lane = threadIdx.x & 63;
     const int wave = __builtin_amdgcn_readfirstlane(threadIdx.x >> 6);
     const int wm = (wave >> 1) * SH::WM, wn = (wave & 1) * SH::WN;
     const int li = lane & 31, g = lane >> 5;
 
-    // Load j = wave + 4i (i = 0..3) of a stage fills its rows 2j and 2j + 1:
-    // lane l writes physical chunk l % 32 of row k = 2j + l / 32, the place of
-    // logical chunk (l % 32) ^ 2 (k & 3), with k & 3 = (2 wave + l / 32) & 3
-    // for every i.  Columns past the matrix read its last whole run of 8
-    // (they reach only outputs that are never stored).
+    // Load j = wave + 4i (i = 0..3) of a stage fills 1 KB of it.
+    //   [32][256]: rows 2j and 2j + 1; lane l writes physical chunk l % 32 of
+    //   row k = 2j + l / 32, the place of logical chunk (l % 32) ^ 2 (k & 3),
+    //   with k & 3 = (2 wave + l / 32) & 3 for every i.  Columns past the
+    //   matrix read its last whole run of 8.
+    //   [256][32] (NN A): rows 16j .. 16j + 15; lane l writes physical chunk
+    //   l % 4 of row r = 16j + l / 4, the place of logical chunk
+    //   (l % 4) ^ ((r >> 2) & 3) = (l % 4) ^ ((l >> 4) & 3).  Rows past the
+    //   matrix read its last row.
+    // (Both only reach outputs that are never stored.)
     const int kl = lane >> 5;
-    const int chunk = (lane & 31) ^ (((2 * wave + kl) & 3) << 1);
-    int ra = m0 + 8 * chunk, rb = n0 + 8 * chunk;
-    ra = ra < a.M ? ra : ((a.M - 1) & ~7);
-    rb = rb < a.N ? rb : ((a.N - 1) & ~7);
-    const uint16_t* ga = a.A + (int64_t)(k_begin + kl) * a.lda + ra;
-    const uint16_t* gb = a.B + (int64_t)(k_begin + kl) * a.ldb + rb;
+    const int fchunk = (lane & 31) ^ (((2 * wave + kl) & 3) << 1);
+    int rbn = n0 + 8 * fchunk;
+    rbn = rbn < a.N ? rbn : ((a.N - 1) & ~7);
+    const uint16_t* gb = a.B + (int64_t)(k_begin + kl) * a.ldb + rbn;
+    const uint16_t* ga[4];
+    int64_t astep;  // elements per stage along the A pointer
+    if constexpr (AKC) {
+        const int kc = (lane & 3) ^ ((lane >> 4) & 3);
+#pragma unroll
+        for (int i = 0; i < 4; i++) {
+            const int r = min(m0 + 16 * (wave + 4 * i) + (lane >> 2), a.M - 1);
+            ga[i] = a.A + (int64_t)r * a.lda + k_begin + 8 * kc;
+        }
+        astep = LBK;
+    } else {
+        int ra = m0 + 8 * fchunk;
+        ra = ra < a.M ? ra : ((a.M - 1) & ~7);
+#pragma unroll
+        for (int i = 0; i < 4; i++)
+            ga[i] = a.A + (int64_t)(k_begin + kl + 2 * (wave + 4 * i)) * a.lda + ra;
+        astep = (int64_t)LBK * a.lda;
+    }
     auto issue = [&](int t, uint16_t* sa, uint16_t* sb) {
-        const int64_t kk = (int64_t)t * LBK;
 #pragma unroll
         for (int i = 0; i < 4; i++) {
             const int j = wave + 4 * i;
             __builtin_amdgcn_global_load_lds(
-                (const void __attribute__((address_space(1)))*)(ga + (kk + 2 * j) * a.lda),
+                (const void __attribute__((address_space(1)))*)(ga[i] + t * astep),
                 (void __attribute__((address_space(3)))*)(sa + j * 512), 16, 0, 0);
             __builtin_amdgcn_global_load_lds(
-                (const void __attribute__((address_space(1)))*)(gb + (kk + 2 * j) * a.ldb),
+                (const void __attribute__((address_space(1)))*)(gb + ((int64_t)t * LBK + 2 * j) *
+                                                                      a.ldb),
                 (void __attribute__((address_space(3)))*)(sb + j * 512), 16, 0, 0);
         }
     };
@@ -1056,19 +1095,23 @@ __global__ __launch_bounds__(NTHR, 1) void gemm_bf16_tn_lds_kernel(const GemmArg
         for (int j = 0; j < NI; j++)
 #pragma unroll
             for (int e = 0; e < 16; e++) acc[i][j][e] = 0.f;
+    auto fa = [&](const uint16_t* sa, int i, int q) {
+        if constexpr (AKC) return lds_frag_kc(sa, wm + 32 * i, q, lane);
+        else return lds_frag(sa, wm + 32 * i, q, lane);
+    };
     // one stage: the fragments of the second 16-deep sub-step are read before
     // the MFMAs of the first
     auto compute = [&](const uint16_t* sa, const uint16_t* sb) {
         uint4 af[2][MI], bf[2][NI];
 #pragma unroll
-        for (int i = 0; i < MI; i++) af[0][i] = lds_frag(sa, wm + 32 * i, 0, lane);
+        for (int i = 0; i < MI; i++) af[0][i] = fa(sa, i, 0);
 #pragma unroll
         for (int j = 0; j < NI; j++) bf[0][j] = lds_frag(sb, wn + 32 * j, 0, lane);
 #pragma unroll
         for (int q = 0; q < 2; q++) {
             if (q == 0) {
 #pragma unroll
-                for (int i = 0; i < MI; i++) af[1][i] = lds_frag(sa, wm + 32 * i, 1, lane);
+                for (int i = 0; i < MI; i++) af[1][i] = fa(sa, i, 1);
 #pragma unroll
                 for (int j = 0; j < NI; j++) bf[1][j] = lds_frag(sb, wn + 32 * j, 1, lane);
             }
@@ -1078,20 +1121,21 @@ __global__ __launch_bounds__(NTHR, 1) void gemm_bf16_tn_lds_kernel(const GemmArg
                 for (int j = 0; j < NI; j++) acc[i][j] = H::mma(af[q][i], bf[q][j], acc[i][j]);
         }
     };
+    auto barrier = [&]() {  // raw: __syncthreads() would also wait for the loads in flight
+        __builtin_amdgcn_sched_barrier(0);
+        __builtin_amdgcn_s_barrier();
+        __builtin_amdgcn_sched_barrier(0);
+    };
     // Before step t: this wave's loads of step t have landed once at most
     // the loads of the (up to two) later steps already issued are in flight
     // (eight per step); after the barrier every wave's have, and every wave
     // has finished step t - 1, so stage (t + 3) % 4 = (t - 1) % 4 is free.
-    // The raw barrier: __syncthreads() would also wait for the loads in
-    // flight.
     auto sync = [&](int later) {
         if (later >= 2) __builtin_amdgcn_s_waitcnt(kVm16);
         else if (later == 1) __builtin_amdgcn_s_waitcnt(kVm8);
         else __builtin_amdgcn_s_waitcnt(kVm0);
         __builtin_amdgcn_s_waitcnt(kLgkm0);
-        __builtin_amdgcn_sched_barrier(0);
-        __builtin_amdgcn_s_barrier();
-        __builtin_amdgcn_sched_barrier(0);
+        barrier();
     };
     if (nsteps > 0) issue(0, SA0, SB0);
     if (nsteps > 1) issue(1, SA1, SB1);
@@ -1122,9 +1166,50 @@ __global__ __launch_bounds__(NTHR, 1) void gemm_bf16_tn_lds_kernel(const GemmArg
         }
     }
     __builtin_amdgcn_s_waitcnt(kLgkm0);
-    __builtin_amdgcn_sched_barrier(0);
-    __builtin_amdgcn_s_barrier();  // every wave is done with the stages
-    __builtin_amdgcn_sched_barrier(0);
+    barrier();  // every wave is done with the stages
+    const int kt = k_begin + nsteps * LBK;
+    if (kt < k_end) {  // partial last stage through registers, zero past k_end
+#pragma unroll
+        for (int i = 0; i < 4; i++) {
+            const int idx = threadIdx.x + NTHR * i;
+            {  // B: [32][256], 8 consecutive columns of one k-row
+                const int k = idx >> 5, c = idx & 31;
+                int n = n0 + 8 * c;
+                n = n < a.N ? n : ((a.N - 1) & ~7);
+                uint4 v = make_uint4(0u, 0u, 0u, 0u);
+                if (kt + k < k_end)
+                    v = *reinterpret_cast<const uint4*>(a.B + (int64_t)(kt + k) * a.ldb + n);
+                *reinterpret_cast<uint4*>(SB0 + lds_off(k, 8 * c)) = v;
+            }
+            if constexpr (AKC) {  // A: [256][32], 8 consecutive k of one row
+                const int r = idx >> 2, c = idx & 3, k = kt + 8 * c;
+                const int row = min(m0 + r, a.M - 1);
+                const uint4 x = *reinterpret_cast<const uint4*>(
+                    a.A + (int64_t)row * a.lda + (k < k_end ? k : k_begin));
+                const uint32_t w[4] = {x.x, x.y, x.z, x.w};
+                uint32_t o[4];
+#pragma unroll
+                for (int j = 0; j < 4; j++) {
+                    const uint32_t lo = k + 2 * j < k_end ? (w[j] & 0xFFFFu) : 0u;
+                    const uint32_t hi = k + 2 * j + 1 < k_end ? (w[j] & 0xFFFF0000u) : 0u;
+                    o[j] = lo | hi;
+                }
+                *reinterpret_cast<uint4*>(SA0 + lds_off_kc(r, 8 * c)) =
+                    make_uint4(o[0], o[1], o[2], o[3]);
+            } else {  // A: [32][256] like B
+                const int k = idx >> 5, c = idx & 31;
+                int m = m0 + 8 * c;
+                m = m < a.M ? m : ((a.M - 1) & ~7);
+                uint4 v = make_uint4(0u, 0u, 0u, 0u);
+                if (kt + k < k_end)
+                    v = *reinterpret_cast<const uint4*>(a.A + (int64_t)(kt + k) * a.lda + m);
+                *reinterpret_cast<uint4*>(SA0 + lds_off(k, 8 * c)) = v;
+            }
+        }
+        __syncthreads();
+        compute(SA0, SB0);
+        __syncthreads();  // before the epilogue stages into SA0
+    }
 
     // Epilogue as in the kernel above; each wave stages its 32 x 128 fp32
     // strips (16 KB, unpadded) in its own A stage.
@@ -1224,14 +1309,13 @@ hipError_t launch_big(hipStream_t s, const GemmArgsH& a, int splits, float* ws) 
     const int tm = cdiv(a.M, 256), tn = cdiv(a.N, 256);
     const int chunk = splits > 1 ? gemm16_split_chunk(a.K, splits) : (a.K > 0 ? a.K : 1);
     const int nz = splits > 1 ? cdiv(a.K, chunk) : 1;
-    if constexpr (OP == GEMM_TN) {
-        // the stages straight into LDS when they are whole and aligned
-        if (a.K % LBK == 0 && chunk % LBK == 0 && a.lda % 8 == 0 && a.ldb % 8 == 0 &&
-            (((uintptr_t)a.A | (uintptr_t)a.B) & 15) == 0) {
-            launch((gemm_bf16_tn_lds_kernel<EPI, H>), dim3(tm * tn, 1, nz), dim3(NTHR), 0, s, a,
-                   tm, tn, chunk, ws);
-            return hipGetLastError();
-        }
+    // the stages straight into LDS when the split chunks are whole stages
+    // and the operands aligned
+    if (chunk % LBK == 0 && a.lda % 8 == 0 && a.ldb % 8 == 0 &&
+        (((uintptr_t)a.A | (uintptr_t)a.B) & 15) == 0) {
+        launch((gemm_bf16_lds_kernel<OP, EPI, H>), dim3(tm * tn, 1, nz), dim3(NTHR), 0, s, a, tm,
+               tn, chunk, ws);
+        return hipGetLastError();
     }
     launch((gemm_bf16_big_kernel<OP, EPI, 4, 4, H>), dim3(tm * tn, 1, nz), dim3(NTHR), 0,
                        s, a, tm, tn, chunk, ws);
