@@ -1243,6 +1243,206 @@ __global__ __launch_bounds__(NTHR, 1) void gemm_bf16_lds_kernel(const GemmArgsH 
     }
 }
 
+// ---- persistent 256x256 forward products, stages straight into LDS -------
+//
+// The NT products (both operands contiguous along k) with a short reduction:
+// one workgroup per compute unit walks its tiles (tile = the i-th virtual
+// workgroup blockIdx.x + i * gridDim.x, mapped as the other kernels map
+// their workgroups) as one stream of 32-deep steps, so the loads of a tile's
+// first stages overlap the previous tile's last steps and its epilogue.
+// Stages as in the kernel above ([256][32] rows, chunks permuted by
+// (r >> 2) mod 4, loaded three steps ahead); both operands are read with
+// 16-byte fragment reads.  The epilogue stages one 32x32 block per wave at a
+// time in a separate LDS area.  Needs K a multiple of 128 (every tile starts
+// on stage 0) and at least 256, leading dimensions that are multiples of 8
+// and 16-byte aligned operands.  The k order is that of the 128x128 kernels, so the
+// results are bitwise the same.
+template <int EPI, class H>
+__global__ __launch_bounds__(NTHR, 1) void gemm_bf16_nt_stream_kernel(const GemmArgsH a,
+                                                                     int tiles_m, int tiles_n) {
+    using SH = Shape<4, 4>;
+    constexpr int MI = 4, NI = 4;
+    constexpr int ELD = 36;  // epilogue staging row stride (floats)
+    __shared__ __attribute__((aligned(16))) uint16_t SA0[LSTAGE], SA1[LSTAGE], SA2[LSTAGE],
+        SA3[LSTAGE], SB0[LSTAGE], SB1[LSTAGE], SB2[LSTAGE], SB3[LSTAGE];
+    __shared__ __attribute__((aligned(16))) float EP[4 * 32 * ELD];
+
+    const int ntiles = tiles_m * tiles_n;
+    const int G = gridDim.x;
+    const int my_tiles = (ntiles - (int)blockIdx.x + G - 1) / G;  // >= 1: the grid has no more WGs than tiles
+    const int S = a.K / LBK;                                       // steps per tile, a multiple of 4
+
+    const int lane = threadIdx.x & 63;
+    const int wave = __builtin_amdgcn_readfirstlane(threadIdx.x >> 6);
+    const int wm = (wave >> 1) * SH::WM, wn = (wave & 1) * SH::WN;
+    const int li = lane & 31, g = lane >> 5;
+    const int kc = (lane & 3) ^ ((lane >> 4) & 3);  // the logical chunk this lane fetches
+
+    struct Ptrs {
+        const uint16_t* a[4];
+        const uint16_t* b[4];
+        int m0, n0;
+    };
+    // load j = wave + 4i of a stage fills rows 16j .. 16j + 15 (1 KB); rows
+    // past the matrix read its last row (only outputs never stored see them)
+    auto tile_ptrs = [&](int ti, Ptrs& p) {
+        const int tile = xcd_remap((int)blockIdx.x + ti * G, ntiles);
+        constexpr int GM = 8;
+        const int per_group = GM * tiles_n;
+        const int group = tile / per_group;
+        const int first_m = group * GM;
+        const int gm = min(tiles_m - first_m, GM);
+        const int in_g = tile - group * per_group;
+        p.m0 = (first_m + in_g % gm) * 256;
+        p.n0 = (in_g / gm) * 256;
+#pragma unroll
+        for (int i = 0; i < 4; i++) {
+            const int r = 16 * (wave + 4 * i) + (lane >> 2);
+            p.a[i] = a.A + (int64_t)min(p.m0 + r, a.M - 1) * a.lda + 8 * kc;
+            p.b[i] = a.B + (int64_t)min(p.n0 + r, a.N - 1) * a.ldb + 8 * kc;
+        }
+    };
+    auto issue = [&](const Ptrs& p, int ks, uint16_t* sa, uint16_t* sb) {
+#pragma unroll
+        for (int i = 0; i < 4; i++) {
+            const int j = wave + 4 * i;
+            __builtin_amdgcn_global_load_lds(
+                (const void __attribute__((address_space(1)))*)(p.a[i] + ks * LBK),
+                (void __attribute__((address_space(3)))*)(sa + j * 512), 16, 0, 0);
+            __builtin_amdgcn_global_load_lds(
+                (const void __attribute__((address_space(1)))*)(p.b[i] + ks * LBK),
+                (void __attribute__((address_space(3)))*)(sb + j * 512), 16, 0, 0);
+        }
+    };
+
+    floatx16 acc[MI][NI];
+    auto zero_acc = [&]() {
+#pragma unroll
+        for (int i = 0; i < MI; i++)
+#pragma unroll
+            for (int j = 0; j < NI; j++)
+#pragma unroll
+                for (int e = 0; e < 16; e++) acc[i][j][e] = 0.f;
+    };
+    auto compute = [&](const uint16_t* sa, const uint16_t* sb) {
+        uint4 af[2][MI], bf[2][NI];
+#pragma unroll
+        for (int i = 0; i < MI; i++) af[0][i] = lds_frag_kc(sa, wm + 32 * i, 0, lane);
+#pragma unroll
+        for (int j = 0; j < NI; j++) bf[0][j] = lds_frag_kc(sb, wn + 32 * j, 0, lane);
+#pragma unroll
+        for (int q = 0; q < 2; q++) {
+            if (q == 0) {
+#pragma unroll
+                for (int i = 0; i < MI; i++) af[1][i] = lds_frag_kc(sa, wm + 32 * i, 1, lane);
+#pragma unroll
+                for (int j = 0; j < NI; j++) bf[1][j] = lds_frag_kc(sb, wn + 32 * j, 1, lane);
+            }
+#pragma unroll
+            for (int i = 0; i < MI; i++)
+#pragma unroll
+                for (int j = 0; j < NI; j++) acc[i][j] = H::mma(af[q][i], bf[q][j], acc[i][j]);
+        }
+    };
+    auto barrier = [&]() {  // raw: __syncthreads() would also wait for the loads in flight
+        __builtin_amdgcn_sched_barrier(0);
+        __builtin_amdgcn_s_barrier();
+        __builtin_amdgcn_sched_barrier(0);
+    };
+    // Before step s: this wave's loads of step s have landed once at most the
+    // loads of the (up to two) later steps already issued are in flight
+    // (eight per step; epilogue stores issued after them only make the wait
+    // longer); after the barrier every wave's have, and every wave has
+    // finished step s - 1, whose stage the step refills.
+    auto sync = [&](int later) {
+        if (later >= 2) __builtin_amdgcn_s_waitcnt(kVm16);
+        else if (later == 1) __builtin_amdgcn_s_waitcnt(kVm8);
+        else __builtin_amdgcn_s_waitcnt(kVm0);
+        __builtin_amdgcn_s_waitcnt(kLgkm0);
+        barrier();
+    };
+    // Epilogue of one tile: each wave stages its 32x32 blocks one at a time
+    // and stores them along rows (4 columns per lane).
+    float* ep = EP + wave * 32 * ELD;
+    auto epilogue = [&](int m0, int n0) {
+#pragma unroll
+        for (int i = 0; i < MI; i++)
+#pragma unroll
+            for (int j = 0; j < NI; j++) {
+#pragma unroll
+                for (int e = 0; e < 16; e++)
+                    ep[(8 * (e >> 2) + 4 * g + (e & 3)) * ELD + li] = acc[i][j][e];
+                __builtin_amdgcn_s_waitcnt(kLgkm0);
+                __builtin_amdgcn_wave_barrier();
+#pragma unroll
+                for (int u = 0; u < 4; u++) {
+                    const int idx = lane + 64 * u, r = idx >> 3, c4 = (idx & 7) * 4;
+                    const float4 v = ld4(ep + r * ELD + c4);
+                    const int row = m0 + wm + 32 * i + r, col = n0 + wn + 32 * j + c4;
+                    if (row >= a.M) continue;
+                    if (col + 3 < a.N) {
+                        epi4<EPI, H>(a, nullptr, row, col, v);
+                    } else {
+                        if (col < a.N) epi1<EPI, H>(a, nullptr, row, col, v.x);
+                        if (col + 1 < a.N) epi1<EPI, H>(a, nullptr, row, col + 1, v.y);
+                        if (col + 2 < a.N) epi1<EPI, H>(a, nullptr, row, col + 2, v.z);
+                    }
+                }
+                __builtin_amdgcn_s_waitcnt(kLgkm0);
+                __builtin_amdgcn_wave_barrier();
+            }
+    };
+
+    Ptrs cur, nxt;
+    tile_ptrs(0, cur);
+    zero_acc();
+    issue(cur, 0, SA0, SB0);
+    issue(cur, 1, SA1, SB1);
+    issue(cur, 2, SA2, SB2);
+    // four steps whose refills all fall in this tile: no branches
+    auto body = [&](int ks) {
+        sync(2);
+        issue(cur, ks + 3, SA3, SB3);
+        compute(SA0, SB0);
+        sync(2);
+        issue(cur, ks + 4, SA0, SB0);
+        compute(SA1, SB1);
+        sync(2);
+        issue(cur, ks + 5, SA1, SB1);
+        compute(SA2, SB2);
+        sync(2);
+        issue(cur, ks + 6, SA2, SB2);
+        compute(SA3, SB3);
+    };
+    for (int ti = 0; ti < my_tiles; ti++) {
+        const bool more = ti + 1 < my_tiles;
+        if (more) tile_ptrs(ti + 1, nxt);
+        // The first four steps stay out of the loop: the previous tile's
+        // epilogue stores may still be in flight there, and with stores and
+        // loads both pending the compiler waits for everything before a
+        // stage read; peeled, it does so once per tile and not at the
+        // loop's head on every pass.
+        body(0);
+        for (int ks = 4; ks + 8 <= S; ks += 4) body(ks);
+        // the tile's last four steps refill with the next tile's first three
+        sync(2);
+        issue(cur, S - 1, SA3, SB3);
+        compute(SA0, SB0);
+        sync(2);
+        if (more) issue(nxt, 0, SA0, SB0);
+        compute(SA1, SB1);
+        sync(more ? 2 : 1);
+        if (more) issue(nxt, 1, SA1, SB1);
+        compute(SA2, SB2);
+        sync(more ? 2 : 0);
+        if (more) issue(nxt, 2, SA2, SB2);
+        compute(SA3, SB3);
+        epilogue(cur.m0, cur.n0);
+        zero_acc();
+        cur = nxt;
+    }
+}
+
 template <int EPI, class H>
 __global__ __launch_bounds__(256) void splitk_reduce_bf16_kernel(const GemmArgsH a,
                                                                  const float* __restrict__ partial,
@@ -1290,6 +1490,19 @@ hipError_t launch_h(hipStream_t s, const GemmArgsH& a, float* ws) {
         const bool k32 = (OP == GEMM_NT && a.K < 2048) ||
                          (OP == GEMM_NN && a.ldb % 8 == 0 && ((uintptr_t)a.B & 15) == 0);
         if (k32) {
+            // The LM-head forward (no bias) on the persistent 256x256 kernel:
+            // 1987 -> 1650 us standalone, bitwise equal.
+            if constexpr (OP == GEMM_NT && EPI == EPI_STORE) {
+                if (a.N >= kGemm16DeepPrefetchN && !a.bias && a.K % 128 == 0 && a.K >= 256 &&
+                    a.lda % 8 == 0 && a.ldb % 8 == 0 &&
+                    (((uintptr_t)a.A | (uintptr_t)a.B) & 15) == 0) {
+                    const int tm2 = cdiv(a.M, 256), tn2 = cdiv(a.N, 256);
+                    launch((gemm_bf16_nt_stream_kernel<EPI, H>),
+                           dim3(std::min(tm2 * tn2, device_cu_count())), dim3(NTHR), 0, s, a, tm2,
+                           tn2);
+                    return hipGetLastError();
+                }
+            }
             if (a.N >= kGemm16DeepPrefetchN)
                 launch((gemm_bf16_k32_kernel<OP, EPI, H, 3>), dim3(tm * tn), dim3(NTHR), 0, s, a,
                        tm, tn);
