@@ -244,6 +244,28 @@ __device__ __forceinline__ float epi1(const GemmArgsH& a, float* __restrict__ pa
     return v;
 }
 
+// The epilogues that read an input of the output's shape (the residual of
+// EPI_RESID, the GELU input of EPI_GELU_BWD) find it cold in HBM: it was
+// written long before, and its loads, a few in flight per lane, would stall
+// the epilogue.  Right after the main loop each thread of the 128x128
+// workgroup loads one value of its tile's rows instead, so that all the
+// tile's 128-byte lines (two per 256-byte row run) are requested at once
+// while the accumulators go through LDS; the epilogue's own loads then hit
+// in L2.  The value is consumed by an empty asm at the kernel's end so the
+// load stays.  Measured with caches flushed before each launch, the GELU'
+// input gradient went from 170 to 149 us and the attention projection from
+// 57 to 47 us, with bitwise-equal outputs.
+template <int EPI>
+__device__ __forceinline__ uint32_t touch_aux_tile(const GemmArgsH& a, int m0, int n0) {
+    static_assert(NTHR == 256 && BM == 128 && BN == 128, "two lines per row of the tile");
+    if constexpr (EPI == EPI_GELU_BWD || EPI == EPI_RESID) {
+        const int r = min(m0 + (int)(threadIdx.x >> 1), a.M - 1);
+        const int c = min(n0 + 64 * (int)(threadIdx.x & 1), a.N - 1);
+        return a.aux[(int64_t)r * a.ldaux + c];
+    }
+    return 0u;
+}
+
 template <int OP, int EPI, class H>
 __global__ __launch_bounds__(NTHR, 2) void gemm_bf16_kernel(const GemmArgsH a, int tiles_m,
                                                             int tiles_n, int kchunk,
@@ -345,6 +367,7 @@ __global__ __launch_bounds__(NTHR, 2) void gemm_bf16_kernel(const GemmArgsH a, i
         __syncthreads();
     }
 
+    const uint32_t aux_touch = touch_aux_tile<EPI>(a, m0, n0);
     // stage each wave's 64x64 fp32 block in LDS, then work along rows;
     // EPI_GELU_BWD column sums: a lane keeps columns 4*(lane & 15) .. +3
     const bool csum = EPI == EPI_GELU_BWD && a.colsum != nullptr;
@@ -402,6 +425,7 @@ __global__ __launch_bounds__(NTHR, 2) void gemm_bf16_kernel(const GemmArgsH a, i
             }
         }
     }
+    asm volatile("" ::"v"(aux_touch));
 }
 
 // ---- 32-deep reduction steps, three workgroups per CU --------------------
@@ -602,6 +626,7 @@ __global__ __launch_bounds__(NTHR, 3) void gemm_bf16_k32_kernel(const GemmArgsH 
         __syncthreads();
     }
 
+    const uint32_t aux_touch = touch_aux_tile<EPI>(a, m0, n0);
     // each wave's 64x64 block through LDS in two 32-row halves; EPI_GELU_BWD
     // column sums as in the 64-step kernel (same rows in the same order)
     const bool csum = EPI == EPI_GELU_BWD && a.colsum != nullptr;
@@ -659,6 +684,7 @@ __global__ __launch_bounds__(NTHR, 3) void gemm_bf16_k32_kernel(const GemmArgsH 
             }
         }
     }
+    asm volatile("" ::"v"(aux_touch));
 }
 
 // ---- large tiles for the weight-gradient and long-K products -------------
