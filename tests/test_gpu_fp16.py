@@ -52,7 +52,7 @@ def pair(name):
     return m, o, c, params
 
 
-@pytest.mark.parametrize("name", ["tiny", "ragged", "ragged80", "gpt2_124m_b4t64",
+@pytest.mark.parametrize("name", ["tiny", "ragged", "ragged80", "ragged704", "gpt2_124m_b4t64",
                                   "ragged_rope", "wide_vocab", "tiny_long"])
 def test_fp16_step(name):
     m, o, c, _ = pair(name)

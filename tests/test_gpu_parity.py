@@ -140,8 +140,9 @@ def check_step(P, tok, tgt, lr=1e-4, wd=0.0):
     return loss_g
 
 
-@pytest.mark.parametrize("name", ["tiny", "ragged", "small", "ragged80", "gpt2_124m_b4t64",
-                                  "tiny_rope", "ragged_rope", "wide_vocab", "tiny_long"])
+@pytest.mark.parametrize("name", ["tiny", "ragged", "small", "ragged80", "ragged704",
+                                  "gpt2_124m_b4t64", "tiny_rope", "ragged_rope", "wide_vocab",
+                                  "tiny_long"])
 def test_one_training_step(name):
     P = Pair(name)
     tok, tgt = synth.token_stream(P.B, P.T, P.c["V"])

@@ -153,6 +153,10 @@ CONFIGS = {
     "wide_vocab": dict(L=1, C=64, NH=4, V=60001, maxT=32, B=2, T=24, steps=1),
     # sequences past 1024 positions: nine 128-row query blocks, a ragged last
     "tiny_long": dict(L=2, C=64, NH=4, V=512, maxT=1152, B=1, T=1100, steps=1),
+    # width 704 (3C = 2112 and 4C = 2816 outputs, reductions of 2112 and 2816)
+    # with B*T = 231 rows: the 16-bit forward and input-gradient products of
+    # the wide layers on ragged row and column tiles
+    "ragged704": dict(L=1, C=704, NH=11, V=1001, maxT=80, B=3, T=77, steps=1),
 }
 
 ADAMW = dict(lr=1e-4, beta1=0.9, beta2=0.999, eps=1e-8, weight_decay=0.0)
