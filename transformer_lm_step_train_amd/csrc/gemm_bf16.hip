@@ -180,8 +180,8 @@ __device__ __forceinline__ void st4h(uint16_t* p, float4 v) {
 template <int EPI, class H>
 __device__ __forceinline__ float4 epi4(const GemmArgsH& a, float* __restrict__ partial, int row,
                                        int col, float4 v) {
-    if (EPI == EPI_PARTIAL) {
-        st4(partial + (int64_t)blockIdx.z * a.M * a.N + (int64_t)row * a.N + col, v);
+    if (EPI == EPI_PARTIAL) {  // partial: this split's M x N slice
+        st4(partial + (int64_t)row * a.N + col, v);
         return v;
     }
     const int64_t idx = (int64_t)row * a.ldc + col;
@@ -220,7 +220,7 @@ template <int EPI, class H>
 __device__ __forceinline__ float epi1(const GemmArgsH& a, float* __restrict__ partial, int row,
                                       int col, float v) {
     if (EPI == EPI_PARTIAL) {
-        partial[(int64_t)blockIdx.z * a.M * a.N + (int64_t)row * a.N + col] = v;
+        partial[(int64_t)row * a.N + col] = v;
         return v;
     }
     const int64_t idx = (int64_t)row * a.ldc + col;
@@ -291,6 +291,7 @@ __global__ __launch_bounds__(NTHR, 2) void gemm_bf16_kernel(const GemmArgsH a, i
     const int n0 = (in_g / gm) * BN;
 
     const int k_begin = blockIdx.z * kchunk;
+    float* const part = EPI == EPI_PARTIAL ? partial + (int64_t)blockIdx.z * a.M * a.N : nullptr;
     const int k_end = min(a.K, k_begin + kchunk);
 
     const int lane = threadIdx.x & 63, wave = threadIdx.x >> 6;
@@ -390,11 +391,11 @@ __global__ __launch_bounds__(NTHR, 2) void gemm_bf16_kernel(const GemmArgsH a, i
         if (row >= a.M) continue;
         float4 o = make_float4(0.f, 0.f, 0.f, 0.f);
         if (col + 3 < a.N) {
-            o = epi4<EPI, H>(a, partial, row, col, v);
+            o = epi4<EPI, H>(a, part, row, col, v);
         } else {
-            if (col < a.N) o.x = epi1<EPI, H>(a, partial, row, col, v.x);
-            if (col + 1 < a.N) o.y = epi1<EPI, H>(a, partial, row, col + 1, v.y);
-            if (col + 2 < a.N) o.z = epi1<EPI, H>(a, partial, row, col + 2, v.z);
+            if (col < a.N) o.x = epi1<EPI, H>(a, part, row, col, v.x);
+            if (col + 1 < a.N) o.y = epi1<EPI, H>(a, part, row, col + 1, v.y);
+            if (col + 2 < a.N) o.z = epi1<EPI, H>(a, part, row, col + 2, v.z);
         }
         if (csum) {
             cs.x += o.x;
@@ -837,6 +838,7 @@ __global__ __launch_bounds__(NTHR, (Shape<MI, NI>::OCC)) void gemm_bf16_big_kern
     const int n0 = (in_g / gm) * SH::BN;
 
     const int k_begin = blockIdx.z * kchunk;
+    float* const part = EPI == EPI_PARTIAL ? partial + (int64_t)blockIdx.z * a.M * a.N : nullptr;
     const int k_end = min(a.K, k_begin + kchunk);
     const int nfull = (k_end - k_begin) / BK;
 
@@ -969,11 +971,11 @@ __global__ __launch_bounds__(NTHR, (Shape<MI, NI>::OCC)) void gemm_bf16_big_kern
             const int row = m0 + wm + 32 * i + r, col = n0 + wn + c4;
             if (row >= a.M) continue;
             if (col + 3 < a.N) {
-                epi4<EPI, H>(a, partial, row, col, v);
+                epi4<EPI, H>(a, part, row, col, v);
             } else {
-                if (col < a.N) epi1<EPI, H>(a, partial, row, col, v.x);
-                if (col + 1 < a.N) epi1<EPI, H>(a, partial, row, col + 1, v.y);
-                if (col + 2 < a.N) epi1<EPI, H>(a, partial, row, col + 2, v.z);
+                if (col < a.N) epi1<EPI, H>(a, part, row, col, v.x);
+                if (col + 1 < a.N) epi1<EPI, H>(a, part, row, col + 1, v.y);
+                if (col + 2 < a.N) epi1<EPI, H>(a, part, row, col + 2, v.z);
             }
         }
         __builtin_amdgcn_wave_barrier();
@@ -1034,6 +1036,29 @@ __device__ __forceinline__ uint4 lds_frag_kc(const uint16_t* s, int rb, int q, i
 // s_waitcnt immediates (vmcnt in bits 3:0 and 15:14, the others at maximum)
 constexpr unsigned kVm0 = 0x0f70, kVm8 = 0x0f78, kVm16 = 0x4f70, kLgkm0 = 0xc07f;
 
+// Tile and K chunk of a split workgroup (grid: tiles x 1 x nz).  The hardware
+// hands workgroups to the 8 XCDs round-robin in dispatch order; here XCD x
+// takes one contiguous run of the chunk-major order (chunk, tile), so the
+// workgroups resident on one XCD are, for all but two chunks of the run, the
+// tiles of one chunk, and read that chunk's A and B rows through its L2 at
+// the same time.  Bijective for any nz (whole chunks per XCD need nz a
+// multiple of 8, which costs the 16-bit products a second round of
+// workgroups).
+__device__ __forceinline__ void chunk_major_remap(int bx, int bz, int tiles, int nz, int& tile,
+                                                  int& kz) {
+    if (nz <= 1) {
+        kz = 0;
+        tile = xcd_remap(bx, tiles);
+        return;
+    }
+    const int lin = bx + tiles * bz;  // dispatch order
+    const int total = tiles * nz;
+    const int x = lin & 7, base = total >> 3, extra = total & 7;
+    const int o = x * base + min(x, extra) + (lin >> 3);  // XCD y holds base + (y < extra)
+    kz = o / tiles;
+    tile = o - kz * tiles;
+}
+
 template <int OP, int EPI, class H>
 __global__ __launch_bounds__(NTHR, 1) void gemm_bf16_lds_kernel(const GemmArgsH a, int tiles_m,
                                                                int tiles_n, int kchunk,
@@ -1048,7 +1073,8 @@ __global__ __launch_bounds__(NTHR, 1) void gemm_bf16_lds_kernel(const GemmArgsH 
     __shared__ __attribute__((aligned(16))) uint16_t SA0[LSTAGE], SA1[LSTAGE], SA2[LSTAGE],
         SA3[LSTAGE], SB0[LSTAGE], SB1[LSTAGE], SB2[LSTAGE], SB3[LSTAGE];
 
-    const int tile = xcd_remap(blockIdx.x, tiles_m * tiles_n);
+    int tile, kz;
+    chunk_major_remap(blockIdx.x, blockIdx.z, tiles_m * tiles_n, gridDim.z, tile, kz);
     constexpr int GM = 8;
     const int per_group = GM * tiles_n;
     const int group = tile / per_group;
@@ -1058,7 +1084,8 @@ __global__ __launch_bounds__(NTHR, 1) void gemm_bf16_lds_kernel(const GemmArgsH 
     const int m0 = (first_m + in_g % gm) * 256;
     const int n0 = (in_g / gm) * 256;
 
-    const int k_begin = blockIdx.z * kchunk;
+    const int k_begin = kz * kchunk;
+    float* const part = EPI == EPI_PARTIAL ? partial + (int64_t)kz * a.M * a.N : nullptr;
     const int k_end = min(a.K, k_begin + kchunk);
     const int nsteps = (k_end - k_begin) / LBK;  // whole stages; the rest is the tail
 
@@ -1258,11 +1285,11 @@ __global__ __launch_bounds__(NTHR, 1) void gemm_bf16_lds_kernel(const GemmArgsH 
             const int row = m0 + wm + 32 * i + r, col = n0 + wn + c4;
             if (row >= a.M) continue;
             if (col + 3 < a.N) {
-                epi4<EPI, H>(a, partial, row, col, v);
+                epi4<EPI, H>(a, part, row, col, v);
             } else {
-                if (col < a.N) epi1<EPI, H>(a, partial, row, col, v.x);
-                if (col + 1 < a.N) epi1<EPI, H>(a, partial, row, col + 1, v.y);
-                if (col + 2 < a.N) epi1<EPI, H>(a, partial, row, col + 2, v.z);
+                if (col < a.N) epi1<EPI, H>(a, part, row, col, v.x);
+                if (col + 1 < a.N) epi1<EPI, H>(a, part, row, col + 1, v.y);
+                if (col + 2 < a.N) epi1<EPI, H>(a, part, row, col + 2, v.z);
             }
         }
         __builtin_amdgcn_wave_barrier();
