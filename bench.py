@@ -54,24 +54,30 @@ def parse():
     return a
 
 
-def source_hash():
-    """SHA-256 of the fp32 matmul kernel's sources (kernel, its helpers and
-    the split plans, which decide the tile order)."""
+def source_hash(precision="fp32"):
+    """SHA-256 of a matmul family's sources (kernels, their helpers and the
+    split plans, which decide the tile order): the fp32 or the 16-bit one."""
     h = hashlib.sha256()
-    for f in ("gemm.hip", "common.h", "plan.cpp", "plan.h"):
+    kern = "gemm.hip" if precision == "fp32" else "gemm_bf16.hip"
+    for f in (kern, "common.h", "plan.cpp", "plan.h"):
         h.update(open(os.path.join(ROOT, "transformer_lm_step_train_amd", "csrc", f), "rb").read())
     return h.hexdigest()
 
 
-def measured_traffic(half):
+TRAFFIC_FILES = {"fp32": "gemm_fp32_traffic.json", "bf16": "gemm_bf16_traffic.json"}
+
+
+def measured_traffic(precision):
     """HBM bytes per matmul launch from the committed rocprofv3 FETCH_SIZE /
-    WRITE_SIZE summary, or None if the matmul source has changed since the
-    counters were taken (or for the 16-bit models, which they do not cover)."""
-    path = os.path.join(ROOT, "profiles", "gemm_fp32_traffic.json")
-    if half or not os.path.exists(path):
+    WRITE_SIZE summary of this precision's step, or None if the matmul
+    sources have changed since the counters were taken (or for fp16, which
+    they do not cover)."""
+    name = TRAFFIC_FILES.get(precision)
+    path = os.path.join(ROOT, "profiles", name) if name else None
+    if not path or not os.path.exists(path):
         return None
     rec = json.load(open(path))
-    if source_hash() != rec.get("source_sha256"):
+    if source_hash(precision) != rec.get("source_sha256"):
         return None
     return round(rec["hbm_bytes_per_launch"])
 
@@ -254,7 +260,7 @@ def run_leg(precision, args, params, tok, tgt):
         achieved = (g["flops"] / n) / avg_s / 1e12 if avg_s > 0 else 0.0
         roofline = {"bound": "mfma", "achieved": round(achieved, 2),
                     "peak": peak, "unit": "TFLOP/s",
-                    "frac": round(achieved / peak, 4), "traffic": measured_traffic(half),
+                    "frac": round(achieved / peak, 4), "traffic": measured_traffic(precision),
                     "traffic_unit": "HBM bytes per launch (rocprofv3 FETCH_SIZE+WRITE_SIZE)",
                     "algorithmic_bytes_per_launch": round(g["bytes"] / n),
                     "kernel": "gemm (all %s MFMA matmul launches of the step)" % precision,
