@@ -4,9 +4,24 @@
 // C 语言实现", section "用C语言实现LLM": the matmul layer; the reduced-precision
 // extension is named by yinghuohong.cn, section "脚动完成每一个层前向/反向流传").
 //
-// Three kernels share the operand conventions of the fp32 one (NT forward,
+// The kernels share the operand conventions of the fp32 one (NT forward,
 // NN input gradient, TN weight gradient) and its fused epilogues; outputs
-// are bf16 activations or fp32 weight gradients (+=).
+// are bf16 activations or fp32 weight gradients (+=).  Which kernel takes a
+// product (launch_h and launch_big at the end of the file):
+//   - QKV and fc forwards, and input gradients with K >= 1536 or N >= 2048:
+//     gemm_bf16_t128_lds_kernel (128x128, stages loaded straight into LDS);
+//   - the LM-head forward: gemm_bf16_nt_stream_kernel (persistent 256x256);
+//   - the other forwards with K < 2048 and input gradients:
+//     gemm_bf16_k32_kernel (128x128, register-staged 32-deep steps);
+//   - forwards with K >= 2048 and operands the above cannot take:
+//     gemm_bf16_kernel (128x128, 64-deep steps);
+//   - weight gradients and the LM-head input gradient (K split):
+//     gemm_bf16_lds_kernel (256x256, stages straight into LDS), or
+//     gemm_bf16_big_kernel when the split chunks are not whole stages or
+//     the operands not 16-byte aligned; splitk_reduce_bf16_kernel sums the
+//     splits in order.
+// The kernels that can take the same product (with the same K split) add
+// the same k in the same order, so they give bitwise-equal results.
 //
 // The forward and input-gradient products use a 128x128 output tile per
 // 256-thread workgroup, 64x64 per wave (2x2 blocks of the 32x32 MFMA), and
